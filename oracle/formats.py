@@ -1,0 +1,171 @@
+"""Storage formats, written as plain bit loops (oracle side; test infrastructure).
+
+Plain packing (the weight format of the uniform and LUT variants)
+----------------------------------------------------------------
+The workloads store b-bit codes "packed 32/b per uint32 along K".  Reading
+taken: code ``c`` of a row goes to word ``c // (32/b)`` of that row, in bits
+``[b*(c % (32/b)), +b)`` -- the lowest k in the lowest bits.  A row occupies
+``ceil(cols*b/32)`` words; unused high bits of a row's last word are zero.
+Zero points use the same packing along the group axis.
+
+Tile-COO (outlier variant; FlashQuant abstract: "Tile-COO outlier encoding")
+---------------------------------------------------------------------------
+The page names the encoding but gives no fields.  Reading taken: tiles of
+128 x 128 weights, numbered row-tile-major then k-tile
+(``t = (r // 128) * ceil(K/128) + c // 128``); one uint32 per outlier with
+bits 0-7 = local column, bits 8-15 = local row, bits 16-31 = the fp16 bits of
+the value; records sorted by (tile, local row, local col); ``tile_ptr`` is
+the exclusive prefix sum of per-tile counts (length tiles + 1).
+
+Codebook code tiles (codebook variant)
+--------------------------------------
+uint8 codes ``[N, K/4]`` (one code per 4 consecutive k) are regrouped into
+tiles of 16 rows x 64 code columns (two 128-wide quant groups).  Inside a
+tile, byte ``16*l + i`` (l = 0..63, i = 0..15) holds the code of row
+``16*rt + i``, code column ``64*ct + l``.  Tiles are ordered row-tile-major,
+then column tile.  Rows and columns past the matrix hold code 0.
+"""
+from __future__ import annotations
+
+import numpy as np
+
+
+def words_per_row(cols: int, bits: int) -> int:
+    return (cols * bits + 31) // 32
+
+
+def pack_plain(codes: np.ndarray, bits: int) -> np.ndarray:
+    """[R, C] uint8 codes -> [R, ceil(C*b/32)] uint32, one bit at a time."""
+    codes = np.asarray(codes)
+    if codes.ndim != 2:
+        raise ValueError("codes must be 2-D")
+    if bits not in (2, 4, 8):
+        raise ValueError("bits must be 2, 4 or 8")
+    if codes.size and int(codes.max()) >= (1 << bits):
+        raise ValueError("code out of range")
+    R, C = codes.shape
+    per = 32 // bits
+    out = np.zeros((R, words_per_row(C, bits)), dtype=np.uint64)
+    c64 = codes.astype(np.uint64)
+    for c in range(C):
+        word = c // per
+        base = bits * (c % per)
+        for t in range(bits):
+            bit = (c64[:, c] >> np.uint64(t)) & np.uint64(1)
+            out[:, word] |= bit << np.uint64(base + t)
+    return out.astype(np.uint32)
+
+
+def unpack_plain(packed: np.ndarray, bits: int, cols: int) -> np.ndarray:
+    """Inverse of pack_plain, one bit at a time."""
+    packed = np.asarray(packed, dtype=np.uint32).astype(np.uint64)
+    R = packed.shape[0]
+    per = 32 // bits
+    out = np.zeros((R, cols), dtype=np.uint64)
+    for c in range(cols):
+        word = c // per
+        base = bits * (c % per)
+        for t in range(bits):
+            bit = (packed[:, word] >> np.uint64(base + t)) & np.uint64(1)
+            out[:, c] |= bit << np.uint64(t)
+    return out.astype(np.uint8)
+
+
+# ----------------------------------------------------------------------------
+# Tile-COO
+# ----------------------------------------------------------------------------
+TILE = 128
+
+
+def tilecoo_encode(N, K, rows, cols, vals_f16):
+    """COO triplets -> (tile_ptr uint32[T+1], tile_rec uint32[nnz])."""
+    rows = np.asarray(rows, dtype=np.int64)
+    cols = np.asarray(cols, dtype=np.int64)
+    vals = np.asarray(vals_f16, dtype=np.float16)
+    if not (rows.shape == cols.shape == vals.shape):
+        raise ValueError("length mismatch")
+    if rows.size and (rows.min() < 0 or rows.max() >= N or cols.min() < 0 or cols.max() >= K):
+        raise ValueError("coordinate out of range")
+    if len(set(zip(rows.tolist(), cols.tolist()))) != rows.size:
+        raise ValueError("duplicate coordinate")
+    if rows.size and not np.all(np.isfinite(vals.astype(np.float64))):
+        raise ValueError("non-finite outlier value")
+    KT = (K + TILE - 1) // TILE
+    NT = (N + TILE - 1) // TILE
+    entries = []
+    for r, c, v in zip(rows.tolist(), cols.tolist(), vals.view(np.uint16).tolist()):
+        t = (r // TILE) * KT + c // TILE
+        lr, lc = r % TILE, c % TILE
+        entries.append((t, lr, lc, (v << 16) | (lr << 8) | lc))
+    entries.sort()
+    counts = [0] * (NT * KT)
+    for t, _, _, _ in entries:
+        counts[t] += 1
+    ptr = [0]
+    for n in counts:
+        ptr.append(ptr[-1] + n)
+    return (np.array(ptr, dtype=np.uint32),
+            np.array([e[3] for e in entries], dtype=np.uint32))
+
+
+def tilecoo_decode(N, K, tile_ptr, tile_rec):
+    """(tile_ptr, tile_rec) -> (rows int64, cols int64, vals fp16) in record order."""
+    KT = (K + TILE - 1) // TILE
+    rows, cols, vals = [], [], []
+    for t in range(len(tile_ptr) - 1):
+        tr, tk = divmod(t, KT)
+        for i in range(int(tile_ptr[t]), int(tile_ptr[t + 1])):
+            rec = int(tile_rec[i])
+            rows.append(tr * TILE + ((rec >> 8) & 0xFF))
+            cols.append(tk * TILE + (rec & 0xFF))
+            vals.append(rec >> 16)
+    return (np.array(rows, dtype=np.int64), np.array(cols, dtype=np.int64),
+            np.array(vals, dtype=np.uint16).view(np.float16))
+
+
+# ----------------------------------------------------------------------------
+# codebook code tiles
+# ----------------------------------------------------------------------------
+CB_ROWS = 16  # rows per tile
+CB_COLS = 64  # code columns per tile (= two 128-wide quant groups at v = 4)
+
+
+def cb_tiled_bytes(N, KC):
+    nr = (N + CB_ROWS - 1) // CB_ROWS
+    nc = (KC + CB_COLS - 1) // CB_COLS
+    return nr * nc * CB_ROWS * CB_COLS
+
+
+def pack_codebook_tiles(codes: np.ndarray) -> np.ndarray:
+    """[N, KC] uint8 -> flat uint8 tiles; byte 16*l + i of tile (rt, ct) holds
+    code[16*rt + i, 64*ct + l]; out-of-range rows/columns hold 0."""
+    N, KC = codes.shape
+    NR = (N + CB_ROWS - 1) // CB_ROWS
+    NC = (KC + CB_COLS - 1) // CB_COLS
+    out = np.zeros(cb_tiled_bytes(N, KC), dtype=np.uint8)
+    for rt in range(NR):
+        for ct in range(NC):
+            base = (rt * NC + ct) * CB_ROWS * CB_COLS
+            for l in range(CB_COLS):
+                for i in range(CB_ROWS):
+                    r = rt * CB_ROWS + i
+                    c = ct * CB_COLS + l
+                    if r < N and c < KC:
+                        out[base + CB_ROWS * l + i] = codes[r, c]
+    return out
+
+
+def unpack_codebook_tiles(tiles: np.ndarray, N, KC) -> np.ndarray:
+    NR = (N + CB_ROWS - 1) // CB_ROWS
+    NC = (KC + CB_COLS - 1) // CB_COLS
+    out = np.zeros((N, KC), dtype=np.uint8)
+    for rt in range(NR):
+        for ct in range(NC):
+            base = (rt * NC + ct) * CB_ROWS * CB_COLS
+            for l in range(CB_COLS):
+                for i in range(CB_ROWS):
+                    r = rt * CB_ROWS + i
+                    c = ct * CB_COLS + l
+                    if r < N and c < KC:
+                        out[r, c] = tiles[base + CB_ROWS * l + i]
+    return out

@@ -1,0 +1,216 @@
+"""float64 reference results for every variant (oracle side; test infrastructure).
+
+Every function takes the *logical* inputs (one code per byte, fp16 values as
+numpy.float16), widens them exactly to float64 and returns ``(y_ref, A)``:
+
+    y_ref[m, n] = sum_k x[m, k] * w[n, k]        (float64)
+    A[m, n]     = sum_k |x[m, k] * w[n, k]|      (float64, the tolerance scale)
+
+Accept a result y when ``|y - y_ref| <= 2e-3 * A + 1e-6``.  All products of
+the inputs used here carry at most 11+8+11 significant bits, so each is exact
+in float64; the only float64 error is the summation, below 1e-12 * A for
+every shape in use.
+
+Sources (titles of the pages; sections as the pages name them):
+
+* Uniform group-wise asymmetric weights -- QFactory (ATC'25) review,
+  "Problem and motivation" (low-bit, group-wise asymmetric scale/zero
+  parameters) and "Experiments" (asymmetric W8/W4/W2, group 128x1).  The pages
+  print no dequantization formula; reading taken: w = s * (q - z) with an
+  integer zero point of the code's width.
+* Zero-point algebraic expansion -- same page, "Key observations",
+  observation 2 (paper sec. 4.3, Table 2): for one group it reduces to
+  sum s(q - z)x = s(sum q x - z sum x).
+* NF4-style lookup table -- "Fast NF4 Dequantization Kernels for Large
+  Language Model Inference", abstract and method: 4-bit codes index 16
+  normal-float levels, times a block-wise absmax scale (block 64 along K).
+* Outlier-aware decomposition -- FlashQuant abstract: a low-bit dense path plus
+  a high-precision sparse path sharing activations and outputs; the two add.
+* Codebook / Psumbook -- CodeGEMM notes, "Key design 1" (Psumbook
+  p_i^j = sum_k c_k^i x_k^j), "Overall framework" (build Psumbook -> read by
+  code -> accumulate) and "Key design 4" (per-group normalization scale).
+"""
+from __future__ import annotations
+
+import numpy as np
+
+_ROW_CHUNK = 2048  # rows of W materialised at once
+
+
+def _f64(a):
+    return np.asarray(a).astype(np.float64)
+
+
+def _gemv_rows(x64, wfun, N, rows=None):
+    """Apply y = x W^T and A = |x| |W|^T over row chunks of W built by wfun(lo, hi)
+    (or over the explicit row list `rows`)."""
+    M = x64.shape[0]
+    ax = np.abs(x64)
+    if rows is None:
+        y = np.empty((M, N))
+        A = np.empty((M, N))
+        for lo in range(0, N, _ROW_CHUNK):
+            hi = min(N, lo + _ROW_CHUNK)
+            w = wfun(np.arange(lo, hi))
+            y[:, lo:hi] = x64 @ w.T
+            A[:, lo:hi] = ax @ np.abs(w).T
+        return y, A
+    rows = np.asarray(rows, dtype=np.int64)
+    w = wfun(rows)
+    return x64 @ w.T, ax @ np.abs(w).T
+
+
+# ----------------------------------------------------------------------------
+# uniform W2 / W4 / W8
+# ----------------------------------------------------------------------------
+
+def dequant_uniform(codes, scales, zeros, g=128):
+    """w[n, k] = s[n, k // g] * (q[n, k] - z[n, k // g])."""
+    q = _f64(codes)
+    s = np.repeat(_f64(scales), g, axis=1)
+    z = np.repeat(_f64(zeros), g, axis=1)
+    return s * (q - z)
+
+
+def gemv_uniform(x, codes, scales, zeros, g=128, rows=None):
+    x64 = _f64(x)
+
+    def wfun(r):
+        return dequant_uniform(codes[r], scales[r], zeros[r], g)
+
+    return _gemv_rows(x64, wfun, codes.shape[0], rows)
+
+
+def gemv_uniform_identity(x, codes, scales, zeros, g=128):
+    """Same result through the group identity sum s(q-z)x = s(sum q x - z sum x)."""
+    x64 = _f64(x)
+    q = _f64(codes)
+    s = _f64(scales)
+    z = _f64(zeros)
+    N, K = q.shape
+    M = x64.shape[0]
+    y = np.zeros((M, N))
+    for G in range(K // g):
+        xg = x64[:, G * g:(G + 1) * g]            # [M, g]
+        qx = xg @ q[:, G * g:(G + 1) * g].T        # [M, N]  sum q x
+        sx = xg.sum(axis=1, keepdims=True)         # [M, 1]  sum x
+        y += s[:, G][None, :] * (qx - z[:, G][None, :] * sx)
+    return y
+
+
+# ----------------------------------------------------------------------------
+# LUT4 (NF4-style)
+# ----------------------------------------------------------------------------
+
+def dequant_lut4(codes, absmax, lut, block=64):
+    """w[n, k] = LUT[q[n, k]] * a[n, k // block]."""
+    L = _f64(lut)
+    return L[np.asarray(codes, dtype=np.int64)] * np.repeat(_f64(absmax), block, axis=1)
+
+
+def gemv_lut4(x, codes, absmax, lut, block=64, rows=None):
+    x64 = _f64(x)
+
+    def wfun(r):
+        return dequant_lut4(codes[r], absmax[r], lut, block)
+
+    return _gemv_rows(x64, wfun, codes.shape[0], rows)
+
+
+# ----------------------------------------------------------------------------
+# outlier-aware W4 (dense + sparse fp16)
+# ----------------------------------------------------------------------------
+
+def sparse_part(x, N, o_rows, o_cols, o_vals):
+    """S x^T for the COO outliers: y_s[m, r] += v * x[m, c]; also sum |v x|."""
+    x64 = _f64(x)
+    M = x64.shape[0]
+    v = _f64(o_vals)
+    ys = np.zeros((M, N))
+    As = np.zeros((M, N))
+    r = np.asarray(o_rows, dtype=np.int64)
+    c = np.asarray(o_cols, dtype=np.int64)
+    for m in range(M):
+        np.add.at(ys[m], r, v * x64[m, c])
+        np.add.at(As[m], r, np.abs(v * x64[m, c]))
+    return ys, As
+
+
+def gemv_outlier(x, codes, scales, zeros, o_rows, o_cols, o_vals, g=128, rows=None):
+    """Dense codes are used as given (codes at outlier positions are not altered);
+    the fp16 outliers are added on top."""
+    yd, Ad = gemv_uniform(x, codes, scales, zeros, g)
+    ys, As = sparse_part(x, codes.shape[0], o_rows, o_cols, o_vals)
+    y, A = yd + ys, Ad + As
+    if rows is not None:
+        rows = np.asarray(rows, dtype=np.int64)
+        return y[:, rows], A[:, rows]
+    return y, A
+
+
+# ----------------------------------------------------------------------------
+# codebook (m = 1 codebook, v-dim centroids, per-group scale)
+# ----------------------------------------------------------------------------
+
+def dequant_codebook(codes, codebook, scales, g=128):
+    """w[n, v*j + t] = s[n, (v*j + t) // g] * C[code[n, j], t]."""
+    C = _f64(codebook)
+    v = C.shape[1]
+    cents = C[np.asarray(codes, dtype=np.int64)]          # [N, KC, v]
+    N, KC = codes.shape
+    w = cents.reshape(N, KC * v)
+    return w * np.repeat(_f64(scales), g, axis=1)
+
+
+def gemv_codebook(x, codes, codebook, scales, g=128, rows=None):
+    x64 = _f64(x)
+
+    def wfun(r):
+        return dequant_codebook(codes[r], codebook, scales[r], g)
+
+    return _gemv_rows(x64, wfun, codes.shape[0], rows)
+
+
+def psumbook(x, codebook):
+    """P[m, j, c] = sum_t C[c, t] * x[m, v*j + t]  (one table per v-wide segment j)."""
+    x64 = _f64(x)
+    C = _f64(codebook)
+    M, K = x64.shape
+    v = C.shape[1]
+    xs = x64.reshape(M, K // v, v)                        # [M, J, v]
+    return xs @ C.T                                       # [M, J, ncent]
+
+
+def gemv_codebook_psumbook(x, codes, codebook, scales, g=128):
+    """Codebook-centric evaluation: build the Psumbook, read it by code,
+    accumulate per group, scale per group."""
+    P = psumbook(x, codebook)                             # [M, J, ncent]
+    M, J, _ = P.shape
+    v = np.asarray(codebook).shape[1]
+    per_g = g // v
+    codes = np.asarray(codes, dtype=np.int64)
+    N = codes.shape[0]
+    s = _f64(scales)
+    y = np.zeros((M, N))
+    jj = np.arange(J)
+    for m in range(M):
+        looked = P[m][jj[None, :], codes]                 # [N, J]
+        grp = looked.reshape(N, J // per_g, per_g).sum(axis=2)
+        y[m] = (grp * s).sum(axis=1)
+    return y
+
+
+# ----------------------------------------------------------------------------
+# acceptance
+# ----------------------------------------------------------------------------
+
+def within_tolerance(y, y_ref, A, rel=2e-3, abs_=1e-6):
+    """Boolean mask of |y - y_ref| <= rel*A + abs_ (y may be fp16 or float)."""
+    y64 = _f64(y)
+    return np.abs(y64 - y_ref) <= rel * A + abs_
+
+
+def worst_ratio(y, y_ref, A, rel=2e-3, abs_=1e-6):
+    """max over elements of |y - y_ref| / (rel*A + abs_) (<= 1 means pass)."""
+    y64 = _f64(y)
+    return float(np.max(np.abs(y64 - y_ref) / (rel * A + abs_))) if y64.size else 0.0

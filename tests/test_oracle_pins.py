@@ -1,0 +1,284 @@
+"""Pins for the float64 oracle against exact arithmetic, closed forms,
+identities and the facts the pages print (CPU only).
+
+Each pin is chosen so that a plausible slip in the oracle -- a dropped term,
+a sign, an off-by-one group index, a transposed operand -- fails at least one
+test here; ``test_planted_mistakes_are_caught`` checks exactly that.
+"""
+import json
+import os
+from fractions import Fraction
+
+import numpy as np
+import pytest
+
+import synth
+from oracle import exact, reference as ref
+
+
+def _tiny_uniform(seed, M, N, K, bits):
+    return synth.uniform_case(seed, M, N, K, bits)
+
+
+# ----------------------------------------------------------------------------
+# exact brute force on tiny shapes
+# ----------------------------------------------------------------------------
+@pytest.mark.parametrize("bits", [2, 4, 8])
+@pytest.mark.parametrize("M,N,K", [(1, 3, 128), (3, 5, 256)])
+def test_uniform_matches_exact(bits, M, N, K):
+    c = _tiny_uniform(100 + bits, M, N, K, bits)
+    y, A = ref.gemv_uniform(c["x"], c["codes"], c["scales"], c["zeros"])
+    ye = exact.to_f64(exact.gemv_uniform_exact(c["x"], c["codes"], c["scales"], c["zeros"]))
+    assert np.all(np.abs(y - ye) <= 1e-12 * A + 1e-300)
+    assert np.all(A > 0)
+
+
+def test_lut4_matches_exact():
+    c = synth.lut4_case(5, 2, 4, 256)
+    y, A = ref.gemv_lut4(c["x"], c["codes"], c["absmax"], c["lut"])
+    ye = exact.to_f64(exact.gemv_lut4_exact(c["x"], c["codes"], c["absmax"], c["lut"]))
+    assert np.all(np.abs(y - ye) <= 1e-12 * A)
+
+
+def test_codebook_matches_exact():
+    c = synth.codebook_case(6, 2, 3, 256)
+    y, A = ref.gemv_codebook(c["x"], c["codes"], c["codebook"], c["scales"])
+    ye = exact.to_f64(exact.gemv_codebook_exact(c["x"], c["codes"], c["codebook"], c["scales"]))
+    assert np.all(np.abs(y - ye) <= 1e-12 * A)
+
+
+def test_outlier_matches_exact():
+    c = synth.outlier_case(8, 2, 6, 256, frac=0.02)
+    y, A = ref.gemv_outlier(c["x"], c["codes"], c["scales"], c["zeros"],
+                            c["o_rows"], c["o_cols"], c["o_vals"])
+    yd = exact.gemv_uniform_exact(c["x"], c["codes"], c["scales"], c["zeros"])
+    ys = exact.sparse_exact(c["x"], 6, c["o_rows"], c["o_cols"], c["o_vals"])
+    ye = exact.to_f64([[a + b for a, b in zip(r1, r2)] for r1, r2 in zip(yd, ys)])
+    assert len(c["o_rows"]) == int(0.02 * 6 * 256)
+    assert np.all(np.abs(y - ye) <= 1e-12 * A)
+
+
+# ----------------------------------------------------------------------------
+# closed forms and identities
+# ----------------------------------------------------------------------------
+@pytest.mark.parametrize("bits", [2, 4, 8])
+def test_one_hot_x_gives_single_dequantized_weight(bits):
+    """x = e_k  =>  y[n] = s[n, k//128] * (q[n,k] - z[n, k//128]), every (q, z)."""
+    L = 1 << bits
+    qs, zs = np.meshgrid(np.arange(L), np.arange(L), indexing="ij")
+    N = L * L
+    K = 256
+    k = 131  # second group
+    codes = np.zeros((N, K), dtype=np.uint8)
+    codes[:, k] = qs.reshape(-1)
+    zeros = np.zeros((N, 2), dtype=np.uint8)
+    zeros[:, 1] = zs.reshape(-1)
+    zeros[:, 0] = (zs.reshape(-1) + 1) % L  # must not leak into the answer
+    scales = synth.f16(np.linspace(0.001, 0.02, N * 2)).reshape(N, 2)
+    x = np.zeros((1, K), dtype=np.float16)
+    x[0, k] = 1.0
+    y, A = ref.gemv_uniform(x, codes, scales, zeros)
+    want = scales[:, 1].astype(np.float64) * (qs.reshape(-1) - zs.reshape(-1))
+    assert np.array_equal(y[0], want)
+    assert np.array_equal(A[0], np.abs(want))
+
+
+def test_all_ones_x_closed_form():
+    c = _tiny_uniform(11, 1, 7, 384, 4)
+    x = np.ones((1, 384), dtype=np.float16)
+    y, _ = ref.gemv_uniform(x, c["codes"], c["scales"], c["zeros"])
+    for n in range(7):
+        want = 0.0
+        for G in range(3):
+            qsum = int(c["codes"][n, 128 * G:128 * (G + 1)].astype(np.int64).sum())
+            want += float(c["scales"][n, G]) * (qsum - 128 * int(c["zeros"][n, G]))
+        assert y[0, n] == pytest.approx(want, rel=1e-14, abs=1e-14)
+
+
+@pytest.mark.parametrize("bits", [2, 4, 8])
+def test_codes_equal_zero_points_give_zero(bits):
+    c = _tiny_uniform(12, 2, 9, 256, bits)
+    codes = np.repeat(c["zeros"], 128, axis=1)
+    y, A = ref.gemv_uniform(c["x"], codes, c["scales"], c["zeros"])
+    assert np.all(y == 0.0) and np.all(A == 0.0)
+
+
+def test_unit_scale_zero_offset_is_integer_matvec():
+    rng = np.random.default_rng(3)
+    N, K, M = 6, 256, 2
+    codes = rng.integers(0, 16, size=(N, K), dtype=np.uint8)
+    xi = rng.integers(-8, 9, size=(M, K))
+    x = xi.astype(np.float16)
+    y, _ = ref.gemv_uniform(x, codes, np.ones((N, 2), dtype=np.float16), np.zeros((N, 2), dtype=np.uint8))
+    want = xi.astype(object) @ codes.astype(object).T
+    assert np.array_equal(y.astype(np.int64), np.array(want, dtype=np.int64))
+
+
+def test_group_identity_matches_direct():
+    """QFactory zero-point expansion specialised to one group."""
+    c = _tiny_uniform(13, 3, 40, 512, 4)
+    y, A = ref.gemv_uniform(c["x"], c["codes"], c["scales"], c["zeros"])
+    yi = ref.gemv_uniform_identity(c["x"], c["codes"], c["scales"], c["zeros"])
+    sx = np.abs(c["x"].astype(np.float64)).sum(axis=1, keepdims=True)
+    assert np.all(np.abs(y - yi) <= 1e-12 * (A + 16 * 0.02 * sx))
+
+
+def test_zero_point_expansion_page_example(golden_dir):
+    with open(os.path.join(golden_dir, "page_facts.json")) as f:
+        fx = json.load(f)["zero_point_expansion"]
+    A = np.array(fx["A"], dtype=object)
+    B = np.array(fx["B"], dtype=object)
+    z1, z2 = fx["z1"], fx["z2"]
+    K = A.shape[1]
+    JA = np.ones(A.shape, dtype=object)
+    JB = np.ones(B.shape, dtype=object)
+    expanded = A @ B - z1 * (JA @ B) - z2 * (A @ JB) + z1 * z2 * K * np.ones((A.shape[0], B.shape[1]), dtype=object)
+    assert expanded.tolist() == fx["product"]
+    # and the oracle's dequantized product agrees with it: rows of B^T are weight rows
+    codes = np.array(B.T, dtype=np.uint8)          # [N=2, K=3] codes
+    x = np.array(A, dtype=np.float16)              # [M=2, K=3] activations; shift x by z1:
+    x = (x.astype(np.float64) - z1).astype(np.float16)
+    # pad K to one full group of 128 with zero activations and code == zero point
+    Kp = 128
+    xp = np.zeros((2, Kp), dtype=np.float16); xp[:, :3] = x
+    cp = np.full((2, Kp), z2, dtype=np.uint8); cp[:, :3] = codes
+    y, _ = ref.gemv_uniform(xp, cp, np.ones((2, 1), dtype=np.float16), np.full((2, 1), z2, dtype=np.uint8))
+    assert y.tolist() == fx["product"]
+
+
+def test_rows_are_independent():
+    c = _tiny_uniform(14, 4, 10, 256, 2)
+    y, A = ref.gemv_uniform(c["x"], c["codes"], c["scales"], c["zeros"])
+    for m in range(4):
+        y1, A1 = ref.gemv_uniform(c["x"][m:m + 1], c["codes"], c["scales"], c["zeros"])
+        assert np.array_equal(y1[0], y[m]) and np.array_equal(A1[0], A[m])
+    ys, As = ref.gemv_uniform(c["x"], c["codes"], c["scales"], c["zeros"], rows=[7, 2])
+    assert np.array_equal(ys, y[:, [7, 2]]) and np.array_equal(As, A[:, [7, 2]])
+
+
+def test_lut4_one_hot_and_reduction_to_uniform():
+    c = _tiny_uniform(15, 2, 8, 256, 4)
+    z0 = 6
+    lut = np.arange(16, dtype=np.float64) - z0
+    lut16 = lut.astype(np.float16)
+    absmax = np.repeat(c["scales"], 2, axis=1)    # same scale on both 64-blocks
+    yl, Al = ref.gemv_lut4(c["x"], c["codes"], absmax, lut16)
+    yu, Au = ref.gemv_uniform(c["x"], c["codes"], c["scales"], np.full_like(c["zeros"], z0))
+    assert np.allclose(yl, yu, rtol=0, atol=1e-12 * Au.max()) and np.allclose(Al, Au, rtol=1e-14)
+    # one-hot x picks LUT[q] * a for the block of k
+    lc = synth.lut4_case(16, 1, 16, 128)
+    codes = np.arange(16, dtype=np.uint8)[:, None].repeat(128, axis=1)
+    x = np.zeros((1, 128), dtype=np.float16); x[0, 70] = 1.0
+    y, _ = ref.gemv_lut4(x, codes, lc["absmax"], lc["lut"])
+    want = lc["lut"].astype(np.float64) * lc["absmax"][:, 1].astype(np.float64)
+    assert np.array_equal(y[0], want)
+
+
+def test_lut_levels_are_sorted_and_symmetric(golden_dir):
+    with open(os.path.join(golden_dir, "page_facts.json")) as f:
+        nf4 = json.load(f)["nf4_lut"]
+    L = synth.normal_quantile_levels(nf4["levels"]).astype(np.float64)
+    assert L.size == nf4["levels"] and L.size * 4 == nf4["shared_bytes_per_block"]  # fp32 LUT fits
+    assert np.all(np.diff(L) > 0) and L[-1] == 1.0 and L[0] == -1.0
+    assert np.allclose(L, -L[::-1])
+    assert 16 // 4 == nf4["fp16_over_code_bits"]
+
+
+def test_codebook_psumbook_equals_dequant_and_reduces_to_w2(golden_dir):
+    c = synth.codebook_case(17, 3, 12, 512)
+    y, A = ref.gemv_codebook(c["x"], c["codes"], c["codebook"], c["scales"])
+    yp = ref.gemv_codebook_psumbook(c["x"], c["codes"], c["codebook"], c["scales"])
+    assert np.all(np.abs(y - yp) <= 1e-12 * A)
+    P = ref.psumbook(c["x"], c["codebook"])
+    with open(os.path.join(golden_dir, "page_facts.json")) as f:
+        facts = json.load(f)
+    for e in facts["psumbook_entries_per_tile"]["cases"]:
+        assert (e["t_w"] // e["v"]) * (2 ** e["b"]) * e["m"] == e["entries"]
+    assert P.shape == (3, 512 // 4, 256)
+    rc = facts["codebook_read_cost"]["cases"][0]
+    assert rc["m"] * rc["rows"] * rc["K"] // rc["v"] * rc["batch"] == rc["reads"]
+    # reduction to W2: centroid c holds the four 2-bit fields of c minus z0
+    z0 = 1
+    C = np.array([[((cc >> (2 * t)) & 3) - z0 for t in range(4)] for cc in range(256)], dtype=np.float16)
+    yc, _ = ref.gemv_codebook(c["x"], c["codes"], C, c["scales"])
+    q2 = np.zeros((12, 512), dtype=np.uint8)
+    for t in range(4):
+        q2[:, t::4] = (c["codes"] >> (2 * t)) & 3
+    yu, Au = ref.gemv_uniform(c["x"], q2, c["scales"], np.full((12, 4), z0, dtype=np.uint8))
+    assert np.all(np.abs(yc - yu) <= 1e-12 * Au)
+    # one-hot x picks s * C[code][t]
+    x = np.zeros((1, 512), dtype=np.float16); x[0, 4 * 37 + 2] = 1.0
+    y1, _ = ref.gemv_codebook(x, c["codes"], c["codebook"], c["scales"])
+    want = c["scales"][:, 1].astype(np.float64) * c["codebook"][c["codes"][:, 37], 2].astype(np.float64)
+    assert np.array_equal(y1[0], want)
+
+
+def test_outlier_special_cases():
+    c = synth.outlier_case(18, 2, 16, 256, frac=0.03)
+    none = np.zeros(0, dtype=np.int32)
+    y0, A0 = ref.gemv_outlier(c["x"], c["codes"], c["scales"], c["zeros"], none, none,
+                              np.zeros(0, dtype=np.float16))
+    yu, Au = ref.gemv_uniform(c["x"], c["codes"], c["scales"], c["zeros"])
+    assert np.array_equal(y0, yu) and np.array_equal(A0, Au)
+    # zero scales leave a pure sparse product
+    s0 = np.zeros_like(c["scales"])
+    ys, _ = ref.gemv_outlier(c["x"], c["codes"], s0, c["zeros"], c["o_rows"], c["o_cols"], c["o_vals"])
+    ye = exact.to_f64(exact.sparse_exact(c["x"], 16, c["o_rows"], c["o_cols"], c["o_vals"]))
+    assert np.array_equal(ys, ye)
+    # a single outlier under one-hot x adds v to s(q - z)
+    x = np.zeros((1, 256), dtype=np.float16); x[0, 200] = 1.0
+    y1, _ = ref.gemv_outlier(x, c["codes"], c["scales"], c["zeros"], [3], [200],
+                             np.array([0.75], dtype=np.float16))
+    w = float(c["scales"][3, 1]) * (int(c["codes"][3, 200]) - int(c["zeros"][3, 1]))
+    assert y1[0, 3] == w + 0.75
+
+
+def test_kernel_rounding_budget_fits_tolerance():
+    """Emulate every rounding the reading permits (fp16 dequantized weight, fp32
+    partial sums in an arbitrary order, fp16 output) and check the tolerance
+    still holds with margin on a realistic shape: the reading is not too tight."""
+    c = synth.uniform_case(19, 2, 256, 4096, 4)
+    y_ref, A = ref.gemv_uniform(c["x"], c["codes"], c["scales"], c["zeros"])
+    w16 = ref.dequant_uniform(c["codes"], c["scales"], c["zeros"]).astype(np.float16).astype(np.float32)
+    prod = c["x"].astype(np.float32)[:, None, :] * w16[None, :, :]      # [M, N, K] fp32
+    acc = np.zeros(prod.shape[:2], dtype=np.float32)
+    for kk in range(0, 4096, 32):                                       # lane-split partials
+        acc = acc + prod[:, :, kk:kk + 32].sum(axis=2, dtype=np.float32)
+    y = acc.astype(np.float16)
+    assert ref.worst_ratio(y, y_ref, A) < 0.6
+
+
+# ----------------------------------------------------------------------------
+# planted mistakes: a wrong oracle must fail a pin
+# ----------------------------------------------------------------------------
+def _mut_sign(codes, scales, zeros, g=128):
+    return np.repeat(scales.astype(np.float64), g, 1) * (codes.astype(np.float64) + np.repeat(zeros.astype(np.float64), g, 1))
+
+
+def _mut_group_off(codes, scales, zeros, g=128):
+    s = np.roll(np.repeat(scales.astype(np.float64), g, 1), 1, axis=1)
+    return s * (codes.astype(np.float64) - np.repeat(zeros.astype(np.float64), g, 1))
+
+
+def _mut_dropped_zero(codes, scales, zeros, g=128):
+    return np.repeat(scales.astype(np.float64), g, 1) * codes.astype(np.float64)
+
+
+def _mut_transpose_groups(codes, scales, zeros, g=128):
+    # zero point indexed by row of the group instead of the group
+    z = np.repeat(zeros.astype(np.float64)[:, ::-1], g, 1)
+    return np.repeat(scales.astype(np.float64), g, 1) * (codes.astype(np.float64) - z)
+
+
+@pytest.mark.parametrize("mutant", [_mut_sign, _mut_group_off, _mut_dropped_zero, _mut_transpose_groups])
+def test_planted_mistakes_are_caught(monkeypatch, mutant):
+    monkeypatch.setattr(ref, "dequant_uniform", mutant)
+    failures = 0
+    for pin in (lambda: test_uniform_matches_exact(4, 3, 5, 256),
+                lambda: test_one_hot_x_gives_single_dequantized_weight(4),
+                lambda: test_codes_equal_zero_points_give_zero(4)):
+        try:
+            pin()
+        except AssertionError:
+            failures += 1
+    assert failures >= 1
