@@ -1,0 +1,160 @@
+"""Python binding of libqgemv.so (fused dequantize-and-multiply GEMV, MI355X).
+
+Argument marshalling only: every step of the computation runs in the HIP
+kernels of the library.  torch supplies device memory and the current stream.
+There is no fallback: if the library is missing, every call raises.
+
+The C ABI is declared in ``include/qgemv.h``; function names here mirror it.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libqgemv.so")
+
+OK, ERR_NULL, ERR_SHAPE, ERR_ALIGN, ERR_UNSUPPORTED, ERR_WORKSPACE, ERR_VALUE, ERR_HIP = range(8)
+PATH_AUTO, PATH_VALU, PATH_MFMA = 0, 1, 2
+LAYOUT_PLAIN, LAYOUT_DEVICE = 0, 1
+GROUP = 128
+
+_lib = None
+
+_vp = ctypes.c_void_p
+_i = ctypes.c_int
+_sz = ctypes.c_size_t
+_i64 = ctypes.c_int64
+
+# name -> (restype, argtypes); kept in step with include/qgemv.h
+_SIGS = {
+    "qgemv_version": (_i, []),
+    "qgemv_status_string": (ctypes.c_char_p, [_i]),
+    "qgemv_last_hip_error": (_i, []),
+    "qgemv_packed_words": (_sz, [_i, _i, _i]),
+    "qgemv_pack": (_i, [_i, _i, _i, _i, _vp, _vp, _vp]),
+    "qgemv_unpack": (_i, [_i, _i, _i, _i, _vp, _vp, _vp]),
+    "qgemv_w2a16": (_i, [_i, _i, _i, _vp, _vp, _vp, _vp, _vp, _vp]),
+    "qgemv_w4a16": (_i, [_i, _i, _i, _vp, _vp, _vp, _vp, _vp, _vp]),
+    "qgemv_w8a16": (_i, [_i, _i, _i, _vp, _vp, _vp, _vp, _vp, _vp]),
+    "qgemv_uniform": (_i, [_i, _i, _i, _i, _i, _vp, _vp, _vp, _vp, _vp, _vp]),
+}
+
+
+class QgemvError(RuntimeError):
+    def __init__(self, fn, status):
+        msg = lib().qgemv_status_string(status).decode()
+        if status == ERR_HIP:
+            msg += f" (hipError {lib().qgemv_last_hip_error()})"
+        super().__init__(f"{fn}: {msg} [{status}]")
+        self.status = status
+
+
+def lib():
+    """The loaded library (raises if it has not been built)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is not built: run `python -m gemm_unpack_bit_amd.build`")
+        L = ctypes.CDLL(LIB_PATH)
+        for name, (res, args) in _SIGS.items():
+            f = getattr(L, name)
+            f.restype = res
+            f.argtypes = args
+        _lib = L
+    return _lib
+
+
+def _check(fn, status):
+    if status != OK:
+        raise QgemvError(fn, status)
+
+
+# ----------------------------------------------------------------------------
+# torch marshalling
+# ----------------------------------------------------------------------------
+
+def _torch():
+    import torch
+
+    return torch
+
+
+def _ptr(t):
+    return _vp(t.data_ptr()) if t is not None else _vp(0)
+
+
+def _stream(t):
+    torch = _torch()
+    return _vp(torch.cuda.current_stream(t.device).cuda_stream)
+
+
+def _need(t, dtype, name):
+    torch = _torch()
+    if not isinstance(t, torch.Tensor) or not t.is_cuda:
+        raise TypeError(f"{name} must be a CUDA tensor")
+    if t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+
+
+def packed_words(bits, rows, cols):
+    return int(lib().qgemv_packed_words(bits, rows, cols))
+
+
+def pack(codes, bits, layout=LAYOUT_DEVICE):
+    """[R, C] uint8 codes (one per byte) -> [R, ceil(C*b/32)] int32 words."""
+    torch = _torch()
+    _need(codes, torch.uint8, "codes")
+    R, C = codes.shape
+    out = torch.empty((R, packed_words(bits, 1, C)), dtype=torch.int32, device=codes.device)
+    _check("qgemv_pack", lib().qgemv_pack(bits, layout, R, C, _ptr(codes), _ptr(out), _stream(codes)))
+    return out
+
+
+def unpack(packed, bits, cols, layout=LAYOUT_DEVICE):
+    torch = _torch()
+    _need(packed, torch.int32, "packed")
+    R = packed.shape[0]
+    out = torch.empty((R, cols), dtype=torch.uint8, device=packed.device)
+    _check("qgemv_unpack", lib().qgemv_unpack(bits, layout, R, cols, _ptr(packed), _ptr(out), _stream(packed)))
+    return out
+
+
+def pack_zeros(zeros, bits):
+    """[N, G] uint8 zero points -> plain-packed int32 words (the zero-point format)."""
+    return pack(zeros, bits, LAYOUT_PLAIN)
+
+
+def uniform(x, wq, scales, zeros, bits, path=PATH_AUTO, out=None):
+    """y = x . dequant(Wq)^T for group-wise asymmetric b-bit weights.
+
+    x [M, K] fp16; wq [N, K*b/32] int32 (device packed); scales [N, K/128] fp16;
+    zeros [N, ceil(K/128*b/32)] int32 (plain packed).  Returns y [M, N] fp16."""
+    torch = _torch()
+    _need(x, torch.float16, "x")
+    _need(wq, torch.int32, "wq")
+    _need(scales, torch.float16, "scales")
+    _need(zeros, torch.int32, "zeros")
+    M, K = x.shape
+    N = wq.shape[0]
+    if out is None:
+        out = torch.empty((M, N), dtype=torch.float16, device=x.device)
+    else:
+        _need(out, torch.float16, "out")
+    _check("qgemv_uniform", lib().qgemv_uniform(bits, path, M, N, K, _ptr(x), _ptr(wq), _ptr(scales),
+                                                _ptr(zeros), _ptr(out), _stream(x)))
+    return out
+
+
+def w2a16(x, wq, scales, zeros, out=None):
+    return uniform(x, wq, scales, zeros, 2, PATH_AUTO, out)
+
+
+def w4a16(x, wq, scales, zeros, out=None):
+    return uniform(x, wq, scales, zeros, 4, PATH_AUTO, out)
+
+
+def w8a16(x, wq, scales, zeros, out=None):
+    return uniform(x, wq, scales, zeros, 8, PATH_AUTO, out)

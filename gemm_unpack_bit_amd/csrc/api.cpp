@@ -1,0 +1,150 @@
+// C ABI of libqgemv.so: argument validation, dispatch and launch.
+// Host-only code (built with the host compiler); kernels live in the .hip files.
+#include "qgemv.h"
+
+#include <hip/hip_runtime.h>
+
+#include <cstdint>
+#include <cstdio>
+#include <cstdlib>
+
+#include "kernels.hpp"
+
+namespace {
+
+thread_local int g_last_hip_error = 0;
+
+int hip_status(hipError_t e) {
+  if (e == hipSuccess) return QGEMV_OK;
+  g_last_hip_error = (int)e;
+  return QGEMV_ERR_HIP;
+}
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+bool overlaps(const void* a, size_t na, const void* b, size_t nb) {
+  const uintptr_t x = reinterpret_cast<uintptr_t>(a), y = reinterpret_cast<uintptr_t>(b);
+  return x < y + nb && y < x + na;
+}
+
+bool valid_bits(int b) { return b == 2 || b == 4 || b == 8; }
+
+size_t plain_words(int bits, int rows, int cols) {
+  return (size_t)rows * (size_t)(((long)cols * bits + 31) / 32);
+}
+
+// Shape rules shared by the compute entry points.  Kernels address every
+// buffer with 32-bit byte offsets below 2^31 (buffer loads past the end read
+// zero), so each operand must stay under 2 GiB.
+int check_mnk(int M, int N, int K, int bits) {
+  if (M < 1 || M > QGEMV_MAX_M || N < 1 || K < QGEMV_GROUP || K % QGEMV_GROUP) return QGEMV_ERR_SHAPE;
+  const long lim = 1L << 31;
+  if ((long)N * K * bits / 8 >= lim || (long)M * K * 2 >= lim || (long)M * N * 2 >= lim) return QGEMV_ERR_SHAPE;
+  return QGEMV_OK;
+}
+
+// Tuning override of the VALU launch shape: QGEMV_VALU_CFG="ri,nv,wk,rb,u".
+// Read on every call (cheap) so a tuning sweep can change it between calls.
+qg::ValuCfg valu_cfg(int bits, int M, int N, int K) {
+  qg::ValuCfg c = qg::pick_valu(bits, M, N, K);
+  if (const char* e = std::getenv("QGEMV_VALU_CFG")) {
+    int ri, nv, wk, rb, u;
+    if (std::sscanf(e, "%d,%d,%d,%d,%d", &ri, &nv, &wk, &rb, &u) == 5) {
+      c.ri = ri;
+      c.nv = nv;
+      c.wk = wk;
+      c.rb = rb;
+      c.u = u;
+    }
+  }
+  return c;
+}
+
+}  // namespace
+
+extern "C" {
+
+int qgemv_version(void) { return 100; }
+
+const char* qgemv_status_string(int status) {
+  switch (status) {
+    case QGEMV_OK: return "ok";
+    case QGEMV_ERR_NULL: return "null pointer";
+    case QGEMV_ERR_SHAPE: return "unsupported shape";
+    case QGEMV_ERR_ALIGN: return "misaligned pointer";
+    case QGEMV_ERR_UNSUPPORTED: return "unsupported variant or path";
+    case QGEMV_ERR_WORKSPACE: return "workspace missing or too small";
+    case QGEMV_ERR_VALUE: return "invalid data or aliasing output";
+    case QGEMV_ERR_HIP: return "HIP runtime error";
+  }
+  return "unknown status";
+}
+
+int qgemv_last_hip_error(void) { return g_last_hip_error; }
+
+size_t qgemv_packed_words(int bits, int rows, int cols) {
+  if (!valid_bits(bits) || rows < 0 || cols < 0) return 0;
+  return plain_words(bits, rows, cols);
+}
+
+int qgemv_pack(int bits, int layout, int rows, int cols, const uint8_t* codes, uint32_t* packed,
+               qgemv_stream_t stream) {
+  if (!codes || !packed) return QGEMV_ERR_NULL;
+  if (!valid_bits(bits) || (layout != QGEMV_LAYOUT_PLAIN && layout != QGEMV_LAYOUT_DEVICE))
+    return QGEMV_ERR_UNSUPPORTED;
+  if (rows < 0 || cols < 0) return QGEMV_ERR_SHAPE;
+  if (overlaps(codes, (size_t)rows * cols, packed, plain_words(bits, rows, cols) * 4)) return QGEMV_ERR_VALUE;
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  int rc = hip_status(qg::launch_pack(bits, layout, rows, cols, codes, packed, s));
+  if (rc) return rc;
+  int bad = 0;
+  rc = hip_status(qg::pack_error_flag(&bad, s));
+  if (rc) return rc;
+  return bad ? QGEMV_ERR_VALUE : QGEMV_OK;
+}
+
+int qgemv_unpack(int bits, int layout, int rows, int cols, const uint32_t* packed, uint8_t* codes,
+                 qgemv_stream_t stream) {
+  if (!codes || !packed) return QGEMV_ERR_NULL;
+  if (!valid_bits(bits) || (layout != QGEMV_LAYOUT_PLAIN && layout != QGEMV_LAYOUT_DEVICE))
+    return QGEMV_ERR_UNSUPPORTED;
+  if (rows < 0 || cols < 0) return QGEMV_ERR_SHAPE;
+  if (overlaps(codes, (size_t)rows * cols, packed, plain_words(bits, rows, cols) * 4)) return QGEMV_ERR_VALUE;
+  return hip_status(
+      qg::launch_unpack(bits, layout, rows, cols, packed, codes, reinterpret_cast<hipStream_t>(stream)));
+}
+
+int qgemv_uniform(int bits, int path, int M, int N, int K, const uint16_t* x, const uint32_t* wq,
+                  const uint16_t* scales, const uint32_t* zeros, uint16_t* y, qgemv_stream_t stream) {
+  if (!x || !wq || !scales || !zeros || !y) return QGEMV_ERR_NULL;
+  if (!valid_bits(bits)) return QGEMV_ERR_UNSUPPORTED;
+  if (path != QGEMV_PATH_AUTO && path != QGEMV_PATH_VALU) return QGEMV_ERR_UNSUPPORTED;
+  int rc = check_mnk(M, N, K, bits);
+  if (rc) return rc;
+  if (!aligned16(x) || !aligned16(wq) || ((uintptr_t)scales & 1u) || ((uintptr_t)zeros & 3u) ||
+      ((uintptr_t)y & 1u))
+    return QGEMV_ERR_ALIGN;
+  const size_t ybytes = (size_t)M * N * 2;
+  const int G = K / QGEMV_GROUP;
+  if (overlaps(y, ybytes, x, (size_t)M * K * 2) || overlaps(y, ybytes, wq, plain_words(bits, N, K) * 4) ||
+      overlaps(y, ybytes, scales, (size_t)N * G * 2) || overlaps(y, ybytes, zeros, plain_words(bits, N, G) * 4))
+    return QGEMV_ERR_VALUE;
+  qg::UniformArgs a{bits, M, N, K, x, wq, scales, zeros, y};
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  return hip_status(qg::launch_gemv_valu(a, valu_cfg(bits, M, N, K), s));
+}
+
+int qgemv_w2a16(int M, int N, int K, const uint16_t* x, const uint32_t* wq, const uint16_t* scales,
+                const uint32_t* zeros, uint16_t* y, qgemv_stream_t stream) {
+  return qgemv_uniform(2, QGEMV_PATH_AUTO, M, N, K, x, wq, scales, zeros, y, stream);
+}
+int qgemv_w4a16(int M, int N, int K, const uint16_t* x, const uint32_t* wq, const uint16_t* scales,
+                const uint32_t* zeros, uint16_t* y, qgemv_stream_t stream) {
+  return qgemv_uniform(4, QGEMV_PATH_AUTO, M, N, K, x, wq, scales, zeros, y, stream);
+}
+int qgemv_w8a16(int M, int N, int K, const uint16_t* x, const uint32_t* wq, const uint16_t* scales,
+                const uint32_t* zeros, uint16_t* y, qgemv_stream_t stream) {
+  return qgemv_uniform(8, QGEMV_PATH_AUTO, M, N, K, x, wq, scales, zeros, y, stream);
+}
+
+}  // extern "C"

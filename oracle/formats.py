@@ -8,6 +8,15 @@ taken: code ``c`` of a row goes to word ``c // (32/b)`` of that row, in bits
 ``ceil(cols*b/32)`` words; unused high bits of a row's last word are zero.
 Zero points use the same packing along the group axis.
 
+Device packing (what the GEMV kernels read)
+-------------------------------------------
+Same words as the plain packing (word j of a row covers k in
+[j*P, (j+1)*P), P = 32/b), with the fields of each word permuted: field f
+holds k = j*P + 2f for f < P/2 and k = j*P + 2(f - P/2) + 1 for f >= P/2.
+Fields f and f + P/2 then hold two consecutive k, so a kernel that splits a
+word into its two 16-bit halves gets (k, k+1) pairs directly.  For b = 4 the
+fields of a word hold k offsets 0,2,4,6,1,3,5,7.
+
 Tile-COO (outlier variant; FlashQuant abstract: "Tile-COO outlier encoding")
 ---------------------------------------------------------------------------
 The page names the encoding but gives no fields.  Reading taken: tiles of
@@ -68,6 +77,50 @@ def unpack_plain(packed: np.ndarray, bits: int, cols: int) -> np.ndarray:
         for t in range(bits):
             bit = (packed[:, word] >> np.uint64(base + t)) & np.uint64(1)
             out[:, c] |= bit << np.uint64(t)
+    return out.astype(np.uint8)
+
+
+def device_field_k(bits: int, f: int) -> int:
+    """k offset (inside its word) of field f of a device-packed word."""
+    half = (32 // bits) // 2
+    return 2 * f if f < half else 2 * (f - half) + 1
+
+
+def pack_device(codes: np.ndarray, bits: int) -> np.ndarray:
+    """[R, C] uint8 codes -> device-packed [R, ceil(C*b/32)] uint32, bit by bit."""
+    codes = np.asarray(codes)
+    if codes.ndim != 2 or bits not in (2, 4, 8):
+        raise ValueError("bad codes or bits")
+    if codes.size and int(codes.max()) >= (1 << bits):
+        raise ValueError("code out of range")
+    R, C = codes.shape
+    per = 32 // bits
+    out = np.zeros((R, words_per_row(C, bits)), dtype=np.uint64)
+    c64 = codes.astype(np.uint64)
+    for j in range(out.shape[1]):
+        for f in range(per):
+            c = j * per + device_field_k(bits, f)
+            if c >= C:
+                continue
+            for t in range(bits):
+                bit = (c64[:, c] >> np.uint64(t)) & np.uint64(1)
+                out[:, j] |= bit << np.uint64(bits * f + t)
+    return out.astype(np.uint32)
+
+
+def unpack_device(packed: np.ndarray, bits: int, cols: int) -> np.ndarray:
+    packed = np.asarray(packed, dtype=np.uint32).astype(np.uint64)
+    R = packed.shape[0]
+    per = 32 // bits
+    out = np.zeros((R, cols), dtype=np.uint64)
+    for j in range(packed.shape[1]):
+        for f in range(per):
+            c = j * per + device_field_k(bits, f)
+            if c >= cols:
+                continue
+            for t in range(bits):
+                bit = (packed[:, j] >> np.uint64(bits * f + t)) & np.uint64(1)
+                out[:, c] |= bit << np.uint64(t)
     return out.astype(np.uint8)
 
 

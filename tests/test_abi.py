@@ -1,0 +1,88 @@
+"""The C-ABI library loads on a CPU-only host, exports every symbol the header
+declares, and its host-side logic (validation, status strings, sizes) works
+without touching a GPU."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import gemm_unpack_bit_amd as q
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def _declared():
+    names = set()
+    for f in os.listdir(os.path.join(ROOT, "include")):
+        if f.endswith(".h"):
+            src = open(os.path.join(ROOT, "include", f)).read()
+            src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+            names |= set(re.findall(r"\b(qgemv_\w+)\s*\(", src))
+    return names
+
+
+@pytest.fixture(scope="module")
+def L():
+    if not os.path.exists(q.LIB_PATH):
+        pytest.skip("library not built")
+    return q.lib()
+
+
+def test_every_declared_symbol_is_exported(L):
+    names = _declared()
+    assert len(names) >= 10
+    raw = ctypes.CDLL(q.LIB_PATH)
+    for n in sorted(names):
+        assert hasattr(raw, n), n
+    # and the binding's signature table covers exactly the header
+    assert set(q._SIGS) == names
+
+
+def test_host_queries(L):
+    assert L.qgemv_version() >= 100
+    for s in range(8):
+        assert L.qgemv_status_string(s)
+    assert L.qgemv_status_string(99) == b"unknown status"
+    assert L.qgemv_packed_words(4, 3, 4096) == 3 * 512
+    assert L.qgemv_packed_words(2, 5, 17) == 5 * 2
+    assert L.qgemv_packed_words(8, 2, 3) == 2
+    assert L.qgemv_packed_words(3, 2, 3) == 0
+    assert L.qgemv_last_hip_error() == 0
+
+
+FAKE = 0x1000  # 16-byte aligned, never dereferenced: every call below fails validation first
+
+
+def _uni(L, bits=4, path=0, M=1, N=64, K=256, x=FAKE, wq=FAKE * 2, s=FAKE * 3, z=FAKE * 4, y=FAKE * 64):
+    v = ctypes.c_void_p
+    return L.qgemv_uniform(bits, path, M, N, K, v(x), v(wq), v(s), v(z), v(y), v(0))
+
+
+def test_uniform_validation_without_gpu(L):
+    assert _uni(L, x=0) == q.ERR_NULL
+    assert _uni(L, y=0) == q.ERR_NULL
+    assert _uni(L, bits=3) == q.ERR_UNSUPPORTED
+    assert _uni(L, path=7) == q.ERR_UNSUPPORTED
+    assert _uni(L, M=0) == q.ERR_SHAPE
+    assert _uni(L, M=17) == q.ERR_SHAPE
+    assert _uni(L, N=0) == q.ERR_SHAPE
+    assert _uni(L, K=200) == q.ERR_SHAPE
+    assert _uni(L, K=0) == q.ERR_SHAPE
+    assert _uni(L, x=FAKE + 2) == q.ERR_ALIGN
+    assert _uni(L, wq=FAKE * 2 + 8) == q.ERR_ALIGN
+    assert _uni(L, y=FAKE * 2) == q.ERR_VALUE  # y overlaps wq
+    v = ctypes.c_void_p
+    assert L.qgemv_w4a16(1, 64, 256, v(0), v(FAKE), v(FAKE), v(FAKE), v(FAKE), v(0)) == q.ERR_NULL
+    assert L.qgemv_w2a16(0, 64, 256, v(FAKE), v(FAKE), v(FAKE), v(FAKE), v(FAKE), v(0)) == q.ERR_SHAPE
+    assert L.qgemv_w8a16(1, 64, 100, v(FAKE), v(FAKE), v(FAKE), v(FAKE), v(FAKE), v(0)) == q.ERR_SHAPE
+
+
+def test_pack_validation_without_gpu(L):
+    v = ctypes.c_void_p
+    assert L.qgemv_pack(4, 1, 2, 8, v(0), v(FAKE), v(0)) == q.ERR_NULL
+    assert L.qgemv_pack(5, 1, 2, 8, v(FAKE), v(FAKE * 16), v(0)) == q.ERR_UNSUPPORTED
+    assert L.qgemv_pack(4, 2, 2, 8, v(FAKE), v(FAKE * 16), v(0)) == q.ERR_UNSUPPORTED  # layout
+    assert L.qgemv_pack(4, 0, -1, 8, v(FAKE), v(FAKE * 16), v(0)) == q.ERR_SHAPE
+    assert L.qgemv_unpack(4, 1, 2, 8, v(FAKE), v(0), v(0)) == q.ERR_NULL
+    assert L.qgemv_pack(4, 1, 2, 8, v(FAKE), v(FAKE + 4), v(0)) == q.ERR_VALUE  # overlap

@@ -1,0 +1,173 @@
+"""GPU parity of the uniform W2/W4/W8 A16 path against the float64 oracle.
+
+Element-by-element checks use |y - y_ref| <= 2e-3 * A + 1e-6 (A = sum |x w|);
+packing and the exact special cases are checked bit for bit.
+"""
+import os
+
+import numpy as np
+import pytest
+
+import synth
+from oracle import formats, reference as ref
+from tests.gpu_util import assert_within, dev, host, sample_rows, say, torch, uniform_weights
+
+pytestmark = pytest.mark.gpu
+
+q = pytest.importorskip("gemm_unpack_bit_amd")
+PATHS = [q.PATH_AUTO, q.PATH_VALU]
+
+
+# ----------------------------------------------------------------------------
+# packing
+# ----------------------------------------------------------------------------
+@pytest.mark.parametrize("layout", [0, 1])
+@pytest.mark.parametrize("bits", [2, 4, 8])
+@pytest.mark.parametrize("R,C", [(1, 8), (3, 37), (16, 256), (33, 1000)])
+def test_pack_bit_exact_against_oracle(layout, bits, R, C):
+    say("pack", layout, bits, R, C)
+    codes = synth.codes(R * 1000 + C, 2, R * C, bits).reshape(R, C)
+    packed = q.pack(dev(codes), bits, layout)
+    want = (formats.pack_device if layout else formats.pack_plain)(codes, bits)
+    assert np.array_equal(host(packed).view(np.uint32), want)
+    assert np.array_equal(host(q.unpack(packed, bits, C, layout)), codes)
+
+
+def test_pack_rejects_out_of_range_code():
+    say("pack bad code")
+    codes = np.zeros((2, 64), dtype=np.uint8)
+    codes[1, 5] = 16
+    with pytest.raises(q.QgemvError) as e:
+        q.pack(dev(codes), 4)
+    assert e.value.status == q.ERR_VALUE
+    # the flag is cleared for the next call
+    codes[1, 5] = 15
+    q.pack(dev(codes), 4)
+
+
+# ----------------------------------------------------------------------------
+# small and ragged shapes: every element against the oracle
+# ----------------------------------------------------------------------------
+SMALL = [(1, 128), (7, 256), (100, 384), (128, 1024), (300, 2176), (67, 4096)]
+
+
+@pytest.mark.parametrize("path", PATHS)
+@pytest.mark.parametrize("bits", [2, 4, 8])
+@pytest.mark.parametrize("N,K", SMALL)
+@pytest.mark.parametrize("M", [1, 2, 3, 4, 5, 16])
+def test_uniform_small_shapes(path, bits, N, K, M):
+    say("uniform", path, bits, N, K, M)
+    c = synth.uniform_case(N * 7 + K + bits, M, N, K, bits)
+    wq = q.pack(dev(c["codes"]), bits)
+    zq = q.pack_zeros(dev(c["zeros"]), bits)
+    y = q.uniform(dev(c["x"]), wq, dev(c["scales"]), zq, bits, path)
+    y_ref, A = ref.gemv_uniform(c["x"], c["codes"], c["scales"], c["zeros"])
+    assert_within(host(y), y_ref, A, f"W{bits} M={M} N={N} K={K} path={path}")
+
+
+# ----------------------------------------------------------------------------
+# exact special cases
+# ----------------------------------------------------------------------------
+@pytest.mark.parametrize("path", PATHS)
+@pytest.mark.parametrize("bits", [2, 4, 8])
+def test_one_hot_x_is_bit_exact(path, bits):
+    """x = e_k gives y[n] = fp16(s * (q - z)) for every (q, z) pair."""
+    say("one-hot", path, bits)
+    L = 1 << bits
+    qs, zs = np.meshgrid(np.arange(L), np.arange(L), indexing="ij")
+    N = L * L
+    K = 512
+    for k in (0, 129, 511):
+        codes = synth.codes(k, 3, N * K, bits).reshape(N, K)
+        codes[:, k] = qs.reshape(-1)
+        zeros = synth.codes(k, 4, N * 4, bits).reshape(N, 4)
+        zeros[:, k // 128] = zs.reshape(-1)
+        scales = synth.f16(synth.uniform(k, 5, N * 4, 0.001, 0.02)).reshape(N, 4)
+        x = np.zeros((1, K), dtype=np.float16)
+        x[0, k] = 1.0
+        y = q.uniform(dev(x), q.pack(dev(codes), bits), dev(scales), q.pack_zeros(dev(zeros), bits), bits, path)
+        want = (scales[:, k // 128].astype(np.float64) * (qs.reshape(-1) - zs.reshape(-1))).astype(np.float16)
+        assert np.array_equal(host(y)[0].view(np.uint16), want.view(np.uint16))
+
+
+@pytest.mark.parametrize("bits", [2, 4, 8])
+def test_codes_equal_zero_points_give_exact_zero(bits):
+    say("q==z", bits)
+    c = synth.uniform_case(40 + bits, 4, 96, 1024, bits)
+    codes = np.repeat(c["zeros"], 128, axis=1)
+    y = q.uniform(dev(c["x"]), q.pack(dev(codes), bits), dev(c["scales"]), q.pack_zeros(dev(c["zeros"]), bits), bits)
+    assert np.all(host(y).astype(np.float64) == 0.0)
+
+
+def test_subnormal_and_large_activations():
+    say("subnormal/large x")
+    c = synth.uniform_case(50, 2, 64, 512, 4)
+    x = c["x"].astype(np.float64)
+    x[0] = x[0] * 2.0 ** -17          # mostly subnormal fp16 values
+    x[1] = x[1] * 3000.0              # large but finite
+    c["x"] = x.astype(np.float16)
+    y = q.uniform(dev(c["x"]), q.pack(dev(c["codes"]), 4), dev(c["scales"]), q.pack_zeros(dev(c["zeros"]), 4), 4)
+    y_ref, A = ref.gemv_uniform(c["x"], c["codes"], c["scales"], c["zeros"])
+    assert_within(host(y), y_ref, A, "subnormal/large x")
+
+
+@pytest.mark.parametrize("bits", [2, 4, 8])
+def test_output_fully_written_and_deterministic(bits):
+    say("poison/determinism", bits)
+    t = torch()
+    c = synth.uniform_case(60 + bits, 3, 1000, 2048, bits)
+    args = (dev(c["x"]), q.pack(dev(c["codes"]), bits), dev(c["scales"]), q.pack_zeros(dev(c["zeros"]), bits))
+    y1 = t.full((3, 1000), float("nan"), dtype=t.float16, device="cuda")
+    q.uniform(*args, bits, out=y1)
+    y2 = t.full((3, 1000), float("nan"), dtype=t.float16, device="cuda")
+    q.uniform(*args, bits, out=y2)
+    a, b = host(y1), host(y2)
+    assert not np.isnan(a.astype(np.float32)).any()
+    assert np.array_equal(a.view(np.uint16), b.view(np.uint16))
+
+
+def test_bad_arguments_raise():
+    say("bad args")
+    t = torch()
+    x = t.zeros((1, 256), dtype=t.float16, device="cuda")
+    wq = t.zeros((8, 32), dtype=t.int32, device="cuda")
+    s = t.zeros((8, 2), dtype=t.float16, device="cuda")
+    z = t.zeros((8, 1), dtype=t.int32, device="cuda")
+    with pytest.raises(q.QgemvError) as e:
+        q.uniform(x[:, :200].contiguous(), wq, s, z, 4)
+    assert e.value.status == q.ERR_SHAPE
+    with pytest.raises(q.QgemvError):
+        q.uniform(x, wq, s, z, 3)
+
+
+# ----------------------------------------------------------------------------
+# full workload sizes (sampled rows), in the launch configuration the bench uses
+# ----------------------------------------------------------------------------
+LLAMA8B = list(synth.LLAMA3_8B_LAYERS.items())
+LLAMA70B = list(synth.LLAMA_70B_LAYERS.items())
+
+
+def _full_check(seed, name, N, K, bits, M):
+    c, wq, s, zq = uniform_weights(seed, N, K, bits)
+    x = c["x"][:M]
+    say("full", name, N, K, bits, M)
+    y = host(q.uniform(dev(x), wq, s, zq, bits))
+    rows = sample_rows(N)
+    y_ref, A = ref.gemv_uniform(x, c["codes"], c["scales"], c["zeros"], rows=rows)
+    assert_within(y[:, rows], y_ref, A, f"{name} W{bits} M={M}")
+    assert np.isfinite(y.astype(np.float32)).all()
+
+
+@pytest.mark.parametrize("bits", [4, 8, 2])
+@pytest.mark.parametrize("idx", range(4))
+def test_llama8b_layers_m1(bits, idx):
+    name, (N, K) = LLAMA8B[idx]
+    _full_check(synth.seed_for(1, idx), name, N, K, bits, 1)
+
+
+@pytest.mark.parametrize("bits", [4, 2])
+@pytest.mark.parametrize("idx", range(4))
+def test_llama70b_layers_batches(bits, idx):
+    name, (N, K) = LLAMA70B[idx]
+    for M in (1, 2, 4, 8, 16):
+        _full_check(synth.seed_for(2, idx), name, N, K, bits, M)

@@ -43,6 +43,38 @@ def test_plain_packing_integer_form_and_roundtrip(bits):
         assert np.array_equal(formats.unpack_plain(packed, bits, cols), codes)
 
 
+def test_device_packing_golden_words(golden_dir):
+    for case in _golden(golden_dir, "plain_packing.json")["device_cases"]:
+        codes = np.array([case["codes"]], dtype=np.uint8)
+        packed = formats.pack_device(codes, case["bits"])
+        assert int(packed[0, 0]) == int(case["word"], 16), case
+
+
+@pytest.mark.parametrize("bits", [2, 4, 8])
+def test_device_packing_is_a_field_permutation_of_plain(bits):
+    rng = np.random.default_rng(10 + bits)
+    for cols in (256, 40):
+        codes = rng.integers(0, 1 << bits, size=(4, cols), dtype=np.uint8)
+        dev = formats.pack_device(codes, bits)
+        plain = formats.pack_plain(codes, bits)
+        assert dev.shape == plain.shape
+        assert np.array_equal(formats.unpack_device(dev, bits, cols), codes)
+        per = 32 // bits
+        # fields f and f + per/2 of every word hold consecutive k
+        for j in range(dev.shape[1]):
+            for f in range(per // 2):
+                k_lo = j * per + 2 * f
+                if k_lo + 1 < cols:
+                    lo = (int(dev[0, j]) >> (bits * f)) & ((1 << bits) - 1)
+                    hi = (int(dev[0, j]) >> (bits * (f + per // 2))) & ((1 << bits) - 1)
+                    assert (lo, hi) == (codes[0, k_lo], codes[0, k_lo + 1])
+        # same multiset of fields per word as the plain packing
+        for j in range(dev.shape[1]):
+            fd = sorted((int(dev[1, j]) >> (bits * f)) & ((1 << bits) - 1) for f in range(per))
+            fp = sorted((int(plain[1, j]) >> (bits * f)) & ((1 << bits) - 1) for f in range(per))
+            assert fd == fp
+
+
 def test_plain_packing_rejects_bad_codes():
     with pytest.raises(ValueError):
         formats.pack_plain(np.array([[4]], dtype=np.uint8), 2)
