@@ -1,0 +1,311 @@
+"""Benchmark: W4A16 g128 decode GEMV on Llama-3-8B-shaped linear layers, 1 GPU.
+
+One step = one decode pass (M = 1) through the four weight matrices of a
+Llama-3-8B decoder layer -- fused QKV (6144x4096), O (4096x4096), fused
+gate+up (28672x4096), down (4096x14336) -- each a W4A16 group-128 asymmetric
+GEMV through the C ABI (qgemv_w4a16).  Inputs are seeded synthetic tensors of
+those shapes (x ~ N(0,1), codes U{0..15}, scales U(0.001,0.02), zeros
+U{0..15}); R rotated copies of every weight tensor (R * bytes >= 1 GiB, above
+the 256 MB Infinity Cache and the 8 x 4 MB L2) make every call read its
+weights from HBM.
+
+Timing: W eager warm-up steps; then the GPU is kept busy by a device-side
+sleep while the host enqueues exactly K steps (4K kernel launches) between two
+HIP events on the launch stream, so the measured region holds GPU time only
+(the host finishes enqueueing before the sleep ends -- checked, else the run
+aborts).  Synchronized on both sides.  value = algorithmic bytes of the K steps
+/ elapsed time.
+
+Printed: ONE JSON line (rank 0).  Extra objects: "roofline" for the dominant
+kernel (gate+up, the largest matrix; average launch duration = a region of K
+back-to-back launches of that layer alone, timed the same way), "cpu_baseline"
+(the float64 CPU oracle on a bounded row sample, host cores), "layers"
+(per-layer us/call, same method).
+
+Profiling helpers (used under rocprofv3):
+  --only LAYER          run only that layer in every step
+  --copy-calibration    also time a device copy of known size (for scaling
+                        FETCH_SIZE / WRITE_SIZE counters)
+  --summarize-trace CSV print per-kernel, per-grid duration statistics of a
+                        rocprofv3 --kernel-trace CSV and exit
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+import synth  # noqa: E402
+
+PEAK_HBM_GBS = 8000.0
+METRIC = "W4A16 g128 decode GEMV µs/call and effective HBM GB/s (% of peak), 1 GPU"
+BITS, M, G = 4, 1, 128
+
+
+def alg_bytes(N, K, bits=BITS, m=M):
+    Gn = K // G
+    return N * K * bits // 8 + N * Gn * 2 + N * ((Gn * bits + 31) // 32) * 4 + m * K * 2 + m * N * 2
+
+
+def build_inputs(torch, q, dev):
+    layers = []
+    for idx, (name, (N, K)) in enumerate(synth.LLAMA3_8B_LAYERS.items()):
+        c = synth.uniform_case(synth.seed_for(1, idx), M, N, K, BITS)
+        wq = q.pack(torch.from_numpy(c["codes"]).to(dev), BITS)
+        zq = q.pack_zeros(torch.from_numpy(c["zeros"]).to(dev), BITS)
+        s = torch.from_numpy(c["scales"]).to(dev)
+        x = torch.from_numpy(c["x"]).to(dev)
+        layers.append(dict(name=name, N=N, K=K, x=x, wq=[wq], s=[s], z=[zq], host=c,
+                           y=torch.empty((M, N), dtype=torch.float16, device=dev),
+                           bytes=alg_bytes(N, K)))
+    step_bytes = sum(L["bytes"] for L in layers)
+    R = max(2, -(-(1 << 30) // step_bytes))
+    for L in layers:
+        for _ in range(R - 1):
+            L["wq"].append(L["wq"][0].clone())
+            L["s"].append(L["s"][0].clone())
+            L["z"].append(L["z"][0].clone())
+    torch.cuda.synchronize()
+    return layers, R, step_bytes
+
+
+def spot_check(q, layers):
+    """Sampled rows of every layer against the float64 oracle (a guard that the
+    timed kernels compute the right thing; the full parity suite is in tests/)."""
+    from oracle import reference as ref
+
+    for L in layers:
+        y = q.w4a16(L["x"], L["wq"][0], L["s"][0], L["z"][0]).cpu().numpy()
+        rows = np.linspace(0, L["N"] - 1, 16).astype(np.int64)
+        c = L["host"]
+        y_ref, A = ref.gemv_uniform(c["x"], c["codes"], c["scales"], c["zeros"], rows=rows)
+        ok = ref.within_tolerance(y[:, rows], y_ref, A)
+        if not ok.all():
+            raise SystemExit(f"bench: {L['name']} outside tolerance on sampled rows")
+
+
+class Timer:
+    """GPU-time regions of back-to-back launches: a device sleep keeps the
+    stream busy while the host enqueues the region, so the two events bracket
+    GPU execution only."""
+
+    def __init__(self, torch):
+        self.torch = torch
+        # calibrate the sleep primitive (cycles -> seconds) once
+        cyc = 10_000_000
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        e0.record()
+        torch.cuda._sleep(cyc)
+        e1.record()
+        torch.cuda.synchronize()
+        self.s_per_cycle = e0.elapsed_time(e1) * 1e-3 / cyc
+
+    host_bound = False
+
+    def region_us(self, fn, n, host_s_per_call):
+        torch = self.torch
+        sleep_s = max(0.005, 3.0 * n * host_s_per_call)
+        for attempt in range(4):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            torch.cuda.synchronize()
+            t0 = time.perf_counter()
+            torch.cuda._sleep(int(sleep_s / self.s_per_cycle))
+            e0.record()
+            for i in range(n):
+                fn(i)
+            e1.record()
+            host = time.perf_counter() - t0
+            torch.cuda.synchronize()
+            if host <= 0.8 * sleep_s:
+                return e0.elapsed_time(e1) * 1000.0
+            sleep_s = 2.0 * host  # the host was slower than estimated (e.g. under a profiler)
+        print(f"bench: warning: host enqueue ({host * 1e3:.1f} ms) did not stay ahead of the GPU",
+              file=sys.stderr)
+        Timer.host_bound = True
+        return e0.elapsed_time(e1) * 1000.0
+
+
+def host_cost(torch, fn, n=20):
+    """Host seconds per fn call (to size the covering sleep)."""
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(n):
+        fn(i)
+    dt = (time.perf_counter() - t0) / n
+    torch.cuda.synchronize()
+    return dt
+
+
+def summarize_trace(path):
+    """Per kernel name and grid: count, mean/median/p10/p90 duration (us)."""
+    import csv
+    from collections import defaultdict
+
+    d = defaultdict(list)
+    with open(path) as f:
+        for r in csv.DictReader(f):
+            key = (r["Kernel_Name"], int(r["Grid_Size_X"]), int(r["Workgroup_Size_X"]))
+            d[key].append((int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1000.0)
+    print(f"{'kernel':72s} {'grid':>8s} {'wg':>5s} {'n':>5s} {'mean':>8s} {'median':>8s} {'p10':>8s} {'p90':>8s}")
+    for (name, gx, wx), v in sorted(d.items(), key=lambda kv: -sum(kv[1])):
+        v.sort()
+        n = len(v)
+        print(f"{name[:72]:72s} {gx:8d} {wx:5d} {n:5d} {sum(v) / n:8.3f} {v[n // 2]:8.3f} "
+              f"{v[n // 10]:8.3f} {v[(9 * n) // 10]:8.3f}")
+
+
+def cpu_baseline(layers, budget_s=10.0):
+    """The float64 oracle (unpack -> dequantize -> matvec) on the first 1/8 of
+    the rows of every layer, repeated until `budget_s` of wall time."""
+    from oracle import reference as ref
+
+    try:
+        import threadpoolctl
+
+        info = threadpoolctl.threadpool_info()
+        blas_threads = max([i.get("num_threads", 1) for i in info] or [1])
+    except Exception:  # pragma: no cover
+        blas_threads = os.cpu_count() or 1
+    sample_bytes = 0
+    t0 = time.perf_counter()
+    reps = 0
+    while True:
+        for L in layers:
+            c = L["host"]
+            rows = np.arange(L["N"] // 8)
+            ref.gemv_uniform(c["x"], c["codes"], c["scales"], c["zeros"], rows=rows)
+            sample_bytes += alg_bytes(len(rows), L["K"])
+        reps += 1
+        el = time.perf_counter() - t0
+        if el >= budget_s:
+            break
+    return {
+        "value": round(sample_bytes / el / 1e9, 4),
+        "unit": "GB/s",
+        "cores": int(blas_threads),
+        "kind": "oracle",
+        "sample": f"float64 oracle (numpy) on rows [0, N/8) of each of the 4 layers, {reps} passes in "
+                  f"{el:.1f} s; extrapolated {el / reps * 8 * 1e6:.0f} us per full 4-layer step",
+    }
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=50)
+    ap.add_argument("--no-cpu", action="store_true", help="skip the cpu_baseline leg")
+    ap.add_argument("--only", default=None, help="run only this layer (profiling)")
+    ap.add_argument("--copy-calibration", action="store_true")
+    ap.add_argument("--summarize-trace", default=None)
+    args = ap.parse_args()
+    if args.summarize_trace:
+        summarize_trace(args.summarize_trace)
+        return
+    if args.gpus != 1:
+        print(f"bench.py: this build runs on one GPU; --gpus {args.gpus} is not supported "
+              "(the GEMV is measured on one GPU's share; see the sharding notes)", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    import gemm_unpack_bit_amd as q
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    dev = torch.device("cuda:0")
+    layers, R, step_bytes = build_inputs(torch, q, dev)
+    spot_check(q, layers)
+
+    run = [L for L in layers if args.only in (None, L["name"])]
+    if not run:
+        raise SystemExit(f"bench: no layer named {args.only}")
+    if args.only:
+        step_bytes = sum(L["bytes"] for L in run)
+
+    def step(i):
+        r = i % R
+        for L in run:
+            q.w4a16(L["x"], L["wq"][r], L["s"][r], L["z"][r], out=L["y"])
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+
+    timer = Timer(torch)
+    K = args.steps
+    total_us = timer.region_us(step, K, host_cost(torch, step))
+    ms_per_step = total_us / K / 1000.0
+    value = step_bytes * K / (total_us * 1e-6) / 1e9
+
+    if args.copy_calibration:
+        src = torch.empty(256 << 20, dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+
+    per_layer = {}
+    for L in run:
+        def one(i, L=L):
+            r = i % R
+            q.w4a16(L["x"], L["wq"][r], L["s"][r], L["z"][r], out=L["y"])
+
+        us = timer.region_us(one, K, host_cost(torch, one)) / K
+        per_layer[L["name"]] = {
+            "N": L["N"], "K": L["K"], "us_per_call": round(us, 3),
+            "GBps": round(L["bytes"] / us / 1e3, 1), "pct_peak": round(L["bytes"] / us / 1e3 / PEAK_HBM_GBS * 100, 1),
+            "bytes": L["bytes"],
+        }
+    dom = max(run, key=lambda L: L["bytes"])
+    dom_us = per_layer[dom["name"]]["us_per_call"]
+    achieved = dom["bytes"] / dom_us / 1e3
+
+    out = {
+        "metric": METRIC,
+        "value": round(value, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 6),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f16",
+        "data": "synthetic",
+        "config": {
+            "workload": "Llama-3-8B decoder-layer linear GEMVs (qkv 6144x4096, o 4096x4096, gate_up 28672x4096, "
+                        "down 4096x14336), W4A16 asymmetric g128, M=1, cache-cold rotated weights",
+            "batch_m": M, "bits": BITS, "group": G, "rotated_copies": R, "step_bytes": step_bytes,
+            "us_per_step": round(ms_per_step * 1000, 3), "pct_peak": round(value / PEAK_HBM_GBS * 100, 2),
+            "timing": "GPU-time region of back-to-back launches behind a device sleep"
+                      + (" (host-bound: numbers unreliable)" if Timer.host_bound else ""),
+        },
+        "roofline": {
+            "bound": "hbm",
+            "kernel": f"qgemv W4A16 GEMV gate_up {dom['N']}x{dom['K']} M=1",
+            "achieved": round(achieved, 1),
+            "peak": PEAK_HBM_GBS,
+            "unit": "GB/s",
+            "frac": round(achieved / PEAK_HBM_GBS, 4),
+            "traffic": None,
+            "us_per_launch": dom_us,
+            "bytes_per_launch": dom["bytes"],
+        },
+        "layers": per_layer,
+    }
+    if not args.no_cpu:
+        out["cpu_baseline"] = cpu_baseline(layers)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -31,7 +31,7 @@ _SIGS = {
     "qgemv_version": (_i, []),
     "qgemv_status_string": (ctypes.c_char_p, [_i]),
     "qgemv_last_hip_error": (_i, []),
-    "qgemv_packed_words": (_sz, [_i, _i, _i]),
+    "qgemv_packed_words": (_sz, [_i, _i, _i, _i]),
     "qgemv_pack": (_i, [_i, _i, _i, _i, _vp, _vp, _vp]),
     "qgemv_unpack": (_i, [_i, _i, _i, _i, _vp, _vp, _vp]),
     "qgemv_w2a16": (_i, [_i, _i, _i, _vp, _vp, _vp, _vp, _vp, _vp]),
@@ -99,24 +99,29 @@ def _need(t, dtype, name):
         raise ValueError(f"{name} must be contiguous")
 
 
-def packed_words(bits, rows, cols):
-    return int(lib().qgemv_packed_words(bits, rows, cols))
+def packed_words(bits, rows, cols, layout=LAYOUT_DEVICE):
+    return int(lib().qgemv_packed_words(bits, layout, rows, cols))
 
 
 def pack(codes, bits, layout=LAYOUT_DEVICE):
-    """[R, C] uint8 codes (one per byte) -> [R, ceil(C*b/32)] int32 words."""
+    """[R, C] uint8 codes (one per byte) -> int32 words: [R, ceil(C*b/32)] for the
+    plain layout, flat [packed_words] for the tiled device layout."""
     torch = _torch()
     _need(codes, torch.uint8, "codes")
     R, C = codes.shape
-    out = torch.empty((R, packed_words(bits, 1, C)), dtype=torch.int32, device=codes.device)
+    n = packed_words(bits, R, C, layout)
+    if n == 0 and R and C:
+        raise ValueError("bad bits/shape for this layout")
+    shape = (R, n // R if R else 0) if layout == LAYOUT_PLAIN else (n,)
+    out = torch.empty(shape, dtype=torch.int32, device=codes.device)
     _check("qgemv_pack", lib().qgemv_pack(bits, layout, R, C, _ptr(codes), _ptr(out), _stream(codes)))
     return out
 
 
-def unpack(packed, bits, cols, layout=LAYOUT_DEVICE):
+def unpack(packed, bits, rows, cols, layout=LAYOUT_DEVICE):
     torch = _torch()
     _need(packed, torch.int32, "packed")
-    R = packed.shape[0]
+    R = rows
     out = torch.empty((R, cols), dtype=torch.uint8, device=packed.device)
     _check("qgemv_unpack", lib().qgemv_unpack(bits, layout, R, cols, _ptr(packed), _ptr(out), _stream(packed)))
     return out
@@ -130,7 +135,7 @@ def pack_zeros(zeros, bits):
 def uniform(x, wq, scales, zeros, bits, path=PATH_AUTO, out=None):
     """y = x . dequant(Wq)^T for group-wise asymmetric b-bit weights.
 
-    x [M, K] fp16; wq [N, K*b/32] int32 (device packed); scales [N, K/128] fp16;
+    x [M, K] fp16; wq int32 words in the device layout; scales [N, K/128] fp16;
     zeros [N, ceil(K/128*b/32)] int32 (plain packed).  Returns y [M, N] fp16."""
     torch = _torch()
     _need(x, torch.float16, "x")
@@ -138,7 +143,10 @@ def uniform(x, wq, scales, zeros, bits, path=PATH_AUTO, out=None):
     _need(scales, torch.float16, "scales")
     _need(zeros, torch.int32, "zeros")
     M, K = x.shape
-    N = wq.shape[0]
+    N = scales.shape[0]
+    need = packed_words(bits, N, K)  # 0 for bits/K the library rejects itself
+    if need and wq.numel() != need:
+        raise ValueError("wq does not hold N x K device-layout codes")
     if out is None:
         out = torch.empty((M, N), dtype=torch.float16, device=x.device)
     else:

@@ -29,9 +29,7 @@ bool overlaps(const void* a, size_t na, const void* b, size_t nb) {
 
 bool valid_bits(int b) { return b == 2 || b == 4 || b == 8; }
 
-size_t plain_words(int bits, int rows, int cols) {
-  return (size_t)rows * (size_t)(((long)cols * bits + 31) / 32);
-}
+size_t words(int bits, int layout, int rows, int cols) { return qg::packed_words(bits, layout, rows, cols); }
 
 // Shape rules shared by the compute entry points.  Kernels address every
 // buffer with 32-bit byte offsets below 2^31 (buffer loads past the end read
@@ -39,25 +37,36 @@ size_t plain_words(int bits, int rows, int cols) {
 int check_mnk(int M, int N, int K, int bits) {
   if (M < 1 || M > QGEMV_MAX_M || N < 1 || K < QGEMV_GROUP || K % QGEMV_GROUP) return QGEMV_ERR_SHAPE;
   const long lim = 1L << 31;
-  if ((long)N * K * bits / 8 >= lim || (long)M * K * 2 >= lim || (long)M * N * 2 >= lim) return QGEMV_ERR_SHAPE;
+  if ((long)((N + 15) / 16) * 16 * K * bits / 8 >= lim || (long)M * K * 2 >= lim || (long)M * N * 2 >= lim)
+    return QGEMV_ERR_SHAPE;
   return QGEMV_OK;
 }
 
-// Tuning override of the VALU launch shape: QGEMV_VALU_CFG="ri,nv,wk,rb,u".
-// Read on every call (cheap) so a tuning sweep can change it between calls.
-qg::ValuCfg valu_cfg(int bits, int M, int N, int K) {
-  qg::ValuCfg c = qg::pick_valu(bits, M, N, K);
-  if (const char* e = std::getenv("QGEMV_VALU_CFG")) {
-    int ri, nv, wk, rb, u;
-    if (std::sscanf(e, "%d,%d,%d,%d,%d", &ri, &nv, &wk, &rb, &u) == 5) {
-      c.ri = ri;
-      c.nv = nv;
+// Tuning override of the launch shape: QGEMV_TILE_CFG="tpw,wk[,mt[,v]]"
+// (tile-rows per workgroup, waves per workgroup, batch rows per VALU
+// workgroup, pipeline variant).  Read on
+// every call (cheap) so a tuning sweep can change it between calls.
+qg::TileCfg tile_cfg(int bits, int M, int N, int K, bool mfma) {
+  qg::TileCfg c = qg::pick_tiles(bits, M, N, K, mfma);
+  if (const char* e = std::getenv("QGEMV_TILE_CFG")) {
+    int tpw, wk, mt, v;
+    const int n = std::sscanf(e, "%d,%d,%d,%d", &tpw, &wk, &mt, &v);
+    if (n >= 2) {
+      c.tpw = tpw;
       c.wk = wk;
-      c.rb = rb;
-      c.u = u;
     }
+    if (n >= 3 && !mfma) c.mt = mt;
+    if (n >= 4) c.v = v;
   }
   return c;
+}
+
+// Dot engine for QGEMV_PATH_AUTO: VALU for small batches, MFMA from the
+// measured crossover batch on.
+int auto_path(int bits, int M, int K) {
+  (void)bits;
+  (void)K;
+  return M <= 2 ? QGEMV_PATH_VALU : QGEMV_PATH_MFMA;
 }
 
 }  // namespace
@@ -82,9 +91,11 @@ const char* qgemv_status_string(int status) {
 
 int qgemv_last_hip_error(void) { return g_last_hip_error; }
 
-size_t qgemv_packed_words(int bits, int rows, int cols) {
+size_t qgemv_packed_words(int bits, int layout, int rows, int cols) {
   if (!valid_bits(bits) || rows < 0 || cols < 0) return 0;
-  return plain_words(bits, rows, cols);
+  if (layout == QGEMV_LAYOUT_DEVICE && cols % QGEMV_GROUP) return 0;
+  if (layout != QGEMV_LAYOUT_PLAIN && layout != QGEMV_LAYOUT_DEVICE) return 0;
+  return words(bits, layout, rows, cols);
 }
 
 int qgemv_pack(int bits, int layout, int rows, int cols, const uint8_t* codes, uint32_t* packed,
@@ -92,8 +103,8 @@ int qgemv_pack(int bits, int layout, int rows, int cols, const uint8_t* codes, u
   if (!codes || !packed) return QGEMV_ERR_NULL;
   if (!valid_bits(bits) || (layout != QGEMV_LAYOUT_PLAIN && layout != QGEMV_LAYOUT_DEVICE))
     return QGEMV_ERR_UNSUPPORTED;
-  if (rows < 0 || cols < 0) return QGEMV_ERR_SHAPE;
-  if (overlaps(codes, (size_t)rows * cols, packed, plain_words(bits, rows, cols) * 4)) return QGEMV_ERR_VALUE;
+  if (rows < 0 || cols < 0 || (layout == QGEMV_LAYOUT_DEVICE && cols % QGEMV_GROUP)) return QGEMV_ERR_SHAPE;
+  if (overlaps(codes, (size_t)rows * cols, packed, words(bits, layout, rows, cols) * 4)) return QGEMV_ERR_VALUE;
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
   int rc = hip_status(qg::launch_pack(bits, layout, rows, cols, codes, packed, s));
   if (rc) return rc;
@@ -108,8 +119,8 @@ int qgemv_unpack(int bits, int layout, int rows, int cols, const uint32_t* packe
   if (!codes || !packed) return QGEMV_ERR_NULL;
   if (!valid_bits(bits) || (layout != QGEMV_LAYOUT_PLAIN && layout != QGEMV_LAYOUT_DEVICE))
     return QGEMV_ERR_UNSUPPORTED;
-  if (rows < 0 || cols < 0) return QGEMV_ERR_SHAPE;
-  if (overlaps(codes, (size_t)rows * cols, packed, plain_words(bits, rows, cols) * 4)) return QGEMV_ERR_VALUE;
+  if (rows < 0 || cols < 0 || (layout == QGEMV_LAYOUT_DEVICE && cols % QGEMV_GROUP)) return QGEMV_ERR_SHAPE;
+  if (overlaps(codes, (size_t)rows * cols, packed, words(bits, layout, rows, cols) * 4)) return QGEMV_ERR_VALUE;
   return hip_status(
       qg::launch_unpack(bits, layout, rows, cols, packed, codes, reinterpret_cast<hipStream_t>(stream)));
 }
@@ -118,7 +129,8 @@ int qgemv_uniform(int bits, int path, int M, int N, int K, const uint16_t* x, co
                   const uint16_t* scales, const uint32_t* zeros, uint16_t* y, qgemv_stream_t stream) {
   if (!x || !wq || !scales || !zeros || !y) return QGEMV_ERR_NULL;
   if (!valid_bits(bits)) return QGEMV_ERR_UNSUPPORTED;
-  if (path != QGEMV_PATH_AUTO && path != QGEMV_PATH_VALU) return QGEMV_ERR_UNSUPPORTED;
+  if (path != QGEMV_PATH_AUTO && path != QGEMV_PATH_VALU && path != QGEMV_PATH_MFMA)
+    return QGEMV_ERR_UNSUPPORTED;
   int rc = check_mnk(M, N, K, bits);
   if (rc) return rc;
   if (!aligned16(x) || !aligned16(wq) || ((uintptr_t)scales & 1u) || ((uintptr_t)zeros & 3u) ||
@@ -126,12 +138,16 @@ int qgemv_uniform(int bits, int path, int M, int N, int K, const uint16_t* x, co
     return QGEMV_ERR_ALIGN;
   const size_t ybytes = (size_t)M * N * 2;
   const int G = K / QGEMV_GROUP;
-  if (overlaps(y, ybytes, x, (size_t)M * K * 2) || overlaps(y, ybytes, wq, plain_words(bits, N, K) * 4) ||
-      overlaps(y, ybytes, scales, (size_t)N * G * 2) || overlaps(y, ybytes, zeros, plain_words(bits, N, G) * 4))
+  if (overlaps(y, ybytes, x, (size_t)M * K * 2) ||
+      overlaps(y, ybytes, wq, words(bits, QGEMV_LAYOUT_DEVICE, N, K) * 4) ||
+      overlaps(y, ybytes, scales, (size_t)N * G * 2) ||
+      overlaps(y, ybytes, zeros, words(bits, QGEMV_LAYOUT_PLAIN, N, G) * 4))
     return QGEMV_ERR_VALUE;
   qg::UniformArgs a{bits, M, N, K, x, wq, scales, zeros, y};
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
-  return hip_status(qg::launch_gemv_valu(a, valu_cfg(bits, M, N, K), s));
+  if (path == QGEMV_PATH_AUTO) path = auto_path(bits, M, K);
+  const bool mfma = path == QGEMV_PATH_MFMA;
+  return hip_status(qg::launch_gemv_tiles(a, tile_cfg(bits, M, N, K, mfma), s));
 }
 
 int qgemv_w2a16(int M, int N, int K, const uint16_t* x, const uint32_t* wq, const uint16_t* scales,

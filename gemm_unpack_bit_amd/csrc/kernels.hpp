@@ -15,18 +15,22 @@ struct UniformArgs {
   uint16_t* y;
 };
 
-// VALU GEMV launch shape: MT = x rows per pass (1, 2 or 4); RI = weight rows
-// per wave-wide load (1, 2 or 4); NV = 16-byte code vectors per lane and row
-// (1 or 2); U = row groups per pipeline stage (2 or 4); WK = waves per
-// workgroup splitting K; RB = rows per workgroup (multiple of RI * U).
-struct ValuCfg {
-  int mt, ri, wk, rb, nv, u;
+// Launch shape of the tiled kernel: mfma selects the dot engine; mt = batch
+// rows per pass of the VALU engine (1 or 2; the MFMA engine takes all 16);
+// tpw = 16-row tile-rows per workgroup (2, 4, 8); wk = waves per workgroup,
+// which take the chunks of quant groups round-robin (1..8); v = pipeline
+// variant (0: 4-group chunks, 2 stage buffers; 1: 2-group chunks, 4 buffers;
+// tpw must be a multiple of the buffer count).
+struct TileCfg {
+  bool mfma;
+  int mt, tpw, wk, v;
 };
 
-ValuCfg pick_valu(int bits, int M, int N, int K);
-hipError_t launch_gemv_valu(const UniformArgs& a, const ValuCfg& c, hipStream_t s);
+TileCfg pick_tiles(int bits, int M, int N, int K, bool mfma);
+hipError_t launch_gemv_tiles(const UniformArgs& a, const TileCfg& c, hipStream_t s);
 
-// bit packing (layout: 0 plain, 1 device)
+// bit packing (layout: 0 plain, 1 device = tiled, see pack.hip)
+size_t packed_words(int bits, int layout, int rows, int cols);
 hipError_t launch_pack(int bits, int layout, int rows, int cols, const uint8_t* codes, uint32_t* packed,
                        hipStream_t s);
 hipError_t launch_unpack(int bits, int layout, int rows, int cols, const uint32_t* packed, uint8_t* codes,

@@ -69,8 +69,8 @@ typedef enum {
 /* Kernel family for the uniform entry points (qgemv_uniform). */
 typedef enum {
   QGEMV_PATH_AUTO = 0, /* measured dispatch by (bits, M, N, K)            */
-  QGEMV_PATH_VALU = 1, /* VALU GEMV: dot2 on packed fp16, DPP K-reduction */
-  QGEMV_PATH_MFMA = 2  /* MFMA skinny GEMM: dequant into matrix-core operands */
+  QGEMV_PATH_VALU = 1, /* VALU dot engine: v_dot2 on unpacked fp16 pairs   */
+  QGEMV_PATH_MFMA = 2  /* MFMA dot engine: unpacked pairs as matrix-core B */
 } qgemv_path;
 
 #define QGEMV_GROUP 128
@@ -85,30 +85,36 @@ const char *qgemv_status_string(int status);
 int qgemv_last_hip_error(void);
 
 /* ------------------------------------------------------------------------
- * Bit packing of b-bit codes (b in {2,4,8}).
+ * Bit packing of b-bit codes (b in {2,4,8}), P = 32/b codes per uint32.
  *
- * A [rows, cols] code matrix is stored row-major, each row in
- * ceil(cols*b/32) uint32 words; word j of a row holds the P = 32/b codes of
- * columns [j*P, (j+1)*P).  Two field orders inside a word:
+ *   QGEMV_LAYOUT_PLAIN   row-major, each row in ceil(cols*b/32) words; word j
+ *                        of a row holds columns [j*P, (j+1)*P), field f (bits
+ *                        [b*f, b*f+b)) holding column j*P + f.  The "32/b
+ *                        codes per uint32 along K" interchange format of the
+ *                        workloads; zero points use this layout.
+ *   QGEMV_LAYOUT_DEVICE  (cols % 128 == 0) tiles of 16 rows x 128 columns,
+ *                        rows padded with code 0 to a multiple of 16.  Tile
+ *                        (rt, g) starts at word (rt*G + g)*64*b, G = cols/128.
+ *                        Inside a tile, lane l in [0,64) holds row 16*rt + l%16
+ *                        and columns [128g + 32(l/16), +32) as b words: word i
+ *                        of lane l is tile word (i/4)*256 + l*min(b,4) + i%4 and
+ *                        covers columns 128g + 32(l/16) + P*i + [0,P), field f
+ *                        holding offset 2f (f < P/2) or 2(f - P/2) + 1
+ *                        (f >= P/2).  Every wave-wide load of a tile is then
+ *                        one contiguous block and the two 16-bit halves of a
+ *                        word are consecutive columns.  The weights of every
+ *                        compute entry point use this layout.
  *
- *   QGEMV_LAYOUT_PLAIN   field f (bits [b*f, b*f+b)) holds column j*P + f --
- *                        the "32/b codes per uint32 along K" interchange format
- *                        of the workloads; zero points use this layout.
- *   QGEMV_LAYOUT_DEVICE  field f holds column j*P + 2f for f < P/2 and
- *                        j*P + 2(f - P/2) + 1 for f >= P/2, so the two 16-bit
- *                        halves of a word carry consecutive columns (k, k+1);
- *                        the weights of every compute entry point use this.
- *
- * Both layouts have the same size; unused high fields of a row's last word
- * are zero.
+ * Unused fields (past cols, or padding rows) are zero.
  * ------------------------------------------------------------------------ */
 typedef enum { QGEMV_LAYOUT_PLAIN = 0, QGEMV_LAYOUT_DEVICE = 1 } qgemv_layout;
 
-/* Number of uint32 words of a packed [rows, cols] matrix (0 on bad args). */
-size_t qgemv_packed_words(int bits, int rows, int cols);
+/* Number of uint32 words of a packed [rows, cols] matrix in `layout`
+ * (0 on bad arguments, including cols % 128 != 0 for the device layout). */
+size_t qgemv_packed_words(int bits, int layout, int rows, int cols);
 
 /* codes [dev] uint8 [rows, cols], one code per byte (< 2^bits)
- * packed [dev] uint32 [qgemv_packed_words(bits, rows, cols)]
+ * packed [dev] uint32 [qgemv_packed_words(bits, layout, rows, cols)]
  * Offline prep: synchronizes `stream`; returns QGEMV_ERR_VALUE (packed
  * contents then unspecified) if any code is >= 2^bits. */
 int qgemv_pack(int bits, int layout, int rows, int cols, const uint8_t *codes, uint32_t *packed,
@@ -124,7 +130,8 @@ int qgemv_unpack(int bits, int layout, int rows, int cols, const uint32_t *packe
  *     w[n, k] = s[n, k/128] * (q[n, k] - z[n, k/128])
  *
  *   x      [dev] fp16   [M, K]
- *   wq     [dev] uint32 device-packed b-bit codes [N, K*b/32]
+ *   wq     [dev] uint32 device-layout b-bit codes
+ *                       [qgemv_packed_words(b, QGEMV_LAYOUT_DEVICE, N, K)]
  *   scales [dev] fp16   [N, K/128]
  *   zeros  [dev] uint32 plain-packed b-bit zero points [N, ceil((K/128)*b/32)]
  *   y      [dev] fp16   [M, N]
@@ -140,7 +147,15 @@ int qgemv_w8a16(int M, int N, int K, const uint16_t *x, const uint32_t *wq,
                 qgemv_stream_t stream);
 
 /* Same computation with an explicit bit width and kernel family (qgemv_path);
- * the w{2,4,8}a16 calls are qgemv_uniform(b, QGEMV_PATH_AUTO, ...). */
+ * the w{2,4,8}a16 calls are qgemv_uniform(b, QGEMV_PATH_AUTO, ...).
+ *
+ * Shapes: 1 <= M <= QGEMV_MAX_M, N >= 1, K a positive multiple of 128, each
+ * operand under 2 GiB (QGEMV_ERR_SHAPE otherwise).  x and wq 16-byte aligned,
+ * scales and y 2-byte, zeros 4-byte (QGEMV_ERR_ALIGN).  y must not overlap an
+ * input (QGEMV_ERR_VALUE).  Checks run in the order null, bits/path, shape,
+ * alignment, overlap; nothing is launched on an error.  Asynchronous on
+ * `stream`; the caller owns every buffer.  The result is deterministic: the
+ * same inputs give the same bits on every call. */
 int qgemv_uniform(int bits, int path, int M, int N, int K, const uint16_t *x,
                   const uint32_t *wq, const uint16_t *scales, const uint32_t *zeros,
                   uint16_t *y, qgemv_stream_t stream);

@@ -10,12 +10,20 @@ Zero points use the same packing along the group axis.
 
 Device packing (what the GEMV kernels read)
 -------------------------------------------
-Same words as the plain packing (word j of a row covers k in
-[j*P, (j+1)*P), P = 32/b), with the fields of each word permuted: field f
-holds k = j*P + 2f for f < P/2 and k = j*P + 2(f - P/2) + 1 for f >= P/2.
-Fields f and f + P/2 then hold two consecutive k, so a kernel that splits a
-word into its two 16-bit halves gets (k, k+1) pairs directly.  For b = 4 the
-fields of a word hold k offsets 0,2,4,6,1,3,5,7.
+Field order inside a word: a word covers P = 32/b consecutive k; field f holds
+k offset 2f for f < P/2 and 2(f - P/2) + 1 for f >= P/2, so fields f and
+f + P/2 hold two consecutive k and the two 16-bit halves of a word give (k, k+1)
+pairs directly.  For b = 4 the fields hold k offsets 0,2,4,6,1,3,5,7.
+``pack_device`` applies only this field order to the plain word sequence.
+
+Tile order (``pack_tiles``, the weight format of the compute entry points):
+the matrix is cut into tiles of 16 rows x 128 k (one quant group), padded with
+code 0 to a multiple of 16 rows.  Tile (rt, g) occupies 16*128*b/32 words from
+word (rt * G + g) * 64 * b (G = K / 128).  Inside a tile, "lane" l in [0, 64)
+owns row 16*rt + (l % 16) and the 32 codes k in [128 g + 32 (l // 16), +32),
+as b words in device field order (word i covers k offset (32/b)*i of that
+run); lane l's word i sits at tile word (i // 4) * 256 + l * min(b, 4) + i % 4.
+A wave-wide load of one word group per lane is then one contiguous block.
 
 Tile-COO (outlier variant; FlashQuant abstract: "Tile-COO outlier encoding")
 ---------------------------------------------------------------------------
@@ -122,6 +130,51 @@ def unpack_device(packed: np.ndarray, bits: int, cols: int) -> np.ndarray:
                 bit = (packed[:, j] >> np.uint64(bits * f + t)) & np.uint64(1)
                 out[:, c] |= bit << np.uint64(t)
     return out.astype(np.uint8)
+
+
+def tiles_words(bits: int, rows: int, cols: int) -> int:
+    return ((rows + 15) // 16) * 16 * cols * bits // 32
+
+
+def pack_tiles(codes: np.ndarray, bits: int) -> np.ndarray:
+    """[R, C] uint8 codes (C % 128 == 0) -> flat uint32 tile-order words."""
+    codes = np.asarray(codes)
+    R, C = codes.shape
+    if C % 128:
+        raise ValueError("cols must be a multiple of 128")
+    per = 32 // bits
+    G = C // 128
+    RT = (R + 15) // 16
+    pad = np.zeros((RT * 16, C), dtype=np.uint8)
+    pad[:R] = codes
+    rowwords = pack_device(pad, bits)             # [RT*16, C/per], field order applied
+    out = np.zeros(tiles_words(bits, R, C), dtype=np.uint32)
+    wpl = bits                                     # words per lane per tile
+    for rt in range(RT):
+        for g in range(G):
+            base = (rt * G + g) * 64 * bits
+            for l in range(64):
+                r = 16 * rt + (l % 16)
+                k0 = 128 * g + 32 * (l // 16)
+                for i in range(wpl):
+                    out[base + (i // 4) * 256 + l * min(bits, 4) + i % 4] = rowwords[r, (k0 + per * i) // per]
+    return out
+
+
+def unpack_tiles(words: np.ndarray, bits: int, rows: int, cols: int) -> np.ndarray:
+    per = 32 // bits
+    G = cols // 128
+    RT = (rows + 15) // 16
+    rowwords = np.zeros((RT * 16, cols // per), dtype=np.uint32)
+    for rt in range(RT):
+        for g in range(G):
+            base = (rt * G + g) * 64 * bits
+            for l in range(64):
+                r = 16 * rt + (l % 16)
+                k0 = 128 * g + 32 * (l // 16)
+                for i in range(bits):
+                    rowwords[r, (k0 + per * i) // per] = words[base + (i // 4) * 256 + l * min(bits, 4) + i % 4]
+    return unpack_device(rowwords, bits, cols)[:rows]
 
 
 # ----------------------------------------------------------------------------

@@ -44,10 +44,14 @@ def test_host_queries(L):
     for s in range(8):
         assert L.qgemv_status_string(s)
     assert L.qgemv_status_string(99) == b"unknown status"
-    assert L.qgemv_packed_words(4, 3, 4096) == 3 * 512
-    assert L.qgemv_packed_words(2, 5, 17) == 5 * 2
-    assert L.qgemv_packed_words(8, 2, 3) == 2
-    assert L.qgemv_packed_words(3, 2, 3) == 0
+    assert L.qgemv_packed_words(4, 0, 3, 4096) == 3 * 512
+    assert L.qgemv_packed_words(2, 0, 5, 17) == 5 * 2
+    assert L.qgemv_packed_words(8, 0, 2, 3) == 2
+    assert L.qgemv_packed_words(3, 0, 2, 3) == 0
+    assert L.qgemv_packed_words(4, 1, 20, 256) == 32 * 256 * 4 // 32   # rows padded to 16
+    assert L.qgemv_packed_words(2, 1, 16, 128) == 16 * 128 * 2 // 32
+    assert L.qgemv_packed_words(4, 1, 20, 100) == 0                   # cols % 128
+    assert L.qgemv_packed_words(4, 2, 20, 256) == 0                   # unknown layout
     assert L.qgemv_last_hip_error() == 0
 
 
@@ -80,9 +84,10 @@ def test_uniform_validation_without_gpu(L):
 
 def test_pack_validation_without_gpu(L):
     v = ctypes.c_void_p
-    assert L.qgemv_pack(4, 1, 2, 8, v(0), v(FAKE), v(0)) == q.ERR_NULL
-    assert L.qgemv_pack(5, 1, 2, 8, v(FAKE), v(FAKE * 16), v(0)) == q.ERR_UNSUPPORTED
-    assert L.qgemv_pack(4, 2, 2, 8, v(FAKE), v(FAKE * 16), v(0)) == q.ERR_UNSUPPORTED  # layout
+    assert L.qgemv_pack(4, 1, 2, 128, v(0), v(FAKE), v(0)) == q.ERR_NULL
+    assert L.qgemv_pack(5, 1, 2, 128, v(FAKE), v(FAKE * 16), v(0)) == q.ERR_UNSUPPORTED
+    assert L.qgemv_pack(4, 2, 2, 128, v(FAKE), v(FAKE * 16), v(0)) == q.ERR_UNSUPPORTED  # layout
     assert L.qgemv_pack(4, 0, -1, 8, v(FAKE), v(FAKE * 16), v(0)) == q.ERR_SHAPE
-    assert L.qgemv_unpack(4, 1, 2, 8, v(FAKE), v(0), v(0)) == q.ERR_NULL
-    assert L.qgemv_pack(4, 1, 2, 8, v(FAKE), v(FAKE + 4), v(0)) == q.ERR_VALUE  # overlap
+    assert L.qgemv_pack(4, 1, 2, 8, v(FAKE), v(FAKE * 16), v(0)) == q.ERR_SHAPE       # device needs cols % 128
+    assert L.qgemv_unpack(4, 1, 2, 128, v(FAKE), v(0), v(0)) == q.ERR_NULL
+    assert L.qgemv_pack(4, 0, 2, 8, v(FAKE), v(FAKE + 4), v(0)) == q.ERR_VALUE  # overlap

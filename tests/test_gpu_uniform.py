@@ -15,27 +15,37 @@ from tests.gpu_util import assert_within, dev, host, sample_rows, say, torch, un
 pytestmark = pytest.mark.gpu
 
 q = pytest.importorskip("gemm_unpack_bit_amd")
-PATHS = [q.PATH_AUTO, q.PATH_VALU]
+PATHS = [q.PATH_AUTO, q.PATH_VALU, q.PATH_MFMA]
 
 
 # ----------------------------------------------------------------------------
 # packing
 # ----------------------------------------------------------------------------
-@pytest.mark.parametrize("layout", [0, 1])
 @pytest.mark.parametrize("bits", [2, 4, 8])
 @pytest.mark.parametrize("R,C", [(1, 8), (3, 37), (16, 256), (33, 1000)])
-def test_pack_bit_exact_against_oracle(layout, bits, R, C):
-    say("pack", layout, bits, R, C)
+def test_plain_pack_bit_exact_against_oracle(bits, R, C):
+    say("pack plain", bits, R, C)
     codes = synth.codes(R * 1000 + C, 2, R * C, bits).reshape(R, C)
-    packed = q.pack(dev(codes), bits, layout)
-    want = (formats.pack_device if layout else formats.pack_plain)(codes, bits)
-    assert np.array_equal(host(packed).view(np.uint32), want)
-    assert np.array_equal(host(q.unpack(packed, bits, C, layout)), codes)
+    packed = q.pack(dev(codes), bits, q.LAYOUT_PLAIN)
+    assert np.array_equal(host(packed).view(np.uint32), formats.pack_plain(codes, bits))
+    assert np.array_equal(host(q.unpack(packed, bits, R, C, q.LAYOUT_PLAIN)), codes)
+
+
+@pytest.mark.parametrize("bits", [2, 4, 8])
+@pytest.mark.parametrize("R,C", [(1, 128), (16, 256), (33, 384), (100, 1024)])
+def test_device_pack_bit_exact_against_oracle(bits, R, C):
+    say("pack device", bits, R, C)
+    codes = synth.codes(R * 1000 + C, 2, R * C, bits).reshape(R, C)
+    packed = q.pack(dev(codes), bits)
+    assert np.array_equal(host(packed).view(np.uint32), formats.pack_tiles(codes, bits))
+    assert np.array_equal(host(q.unpack(packed, bits, R, C)), codes)
 
 
 def test_pack_rejects_out_of_range_code():
     say("pack bad code")
     codes = np.zeros((2, 64), dtype=np.uint8)
+    codes[1, 5] = 16
+    codes = np.zeros((2, 128), dtype=np.uint8)
     codes[1, 5] = 16
     with pytest.raises(q.QgemvError) as e:
         q.pack(dev(codes), 4)
@@ -130,7 +140,7 @@ def test_bad_arguments_raise():
     say("bad args")
     t = torch()
     x = t.zeros((1, 256), dtype=t.float16, device="cuda")
-    wq = t.zeros((8, 32), dtype=t.int32, device="cuda")
+    wq = t.zeros((16 * 32,), dtype=t.int32, device="cuda")
     s = t.zeros((8, 2), dtype=t.float16, device="cuda")
     z = t.zeros((8, 1), dtype=t.int32, device="cuda")
     with pytest.raises(q.QgemvError) as e:
@@ -147,22 +157,23 @@ LLAMA8B = list(synth.LLAMA3_8B_LAYERS.items())
 LLAMA70B = list(synth.LLAMA_70B_LAYERS.items())
 
 
-def _full_check(seed, name, N, K, bits, M):
+def _full_check(seed, name, N, K, bits, M, paths=(q.PATH_AUTO,)):
     c, wq, s, zq = uniform_weights(seed, N, K, bits)
     x = c["x"][:M]
-    say("full", name, N, K, bits, M)
-    y = host(q.uniform(dev(x), wq, s, zq, bits))
     rows = sample_rows(N)
     y_ref, A = ref.gemv_uniform(x, c["codes"], c["scales"], c["zeros"], rows=rows)
-    assert_within(y[:, rows], y_ref, A, f"{name} W{bits} M={M}")
-    assert np.isfinite(y.astype(np.float32)).all()
+    for path in paths:
+        say("full", name, N, K, bits, M, "path", path)
+        y = host(q.uniform(dev(x), wq, s, zq, bits, path))
+        assert_within(y[:, rows], y_ref, A, f"{name} W{bits} M={M} path={path}")
+        assert np.isfinite(y.astype(np.float32)).all()
 
 
 @pytest.mark.parametrize("bits", [4, 8, 2])
 @pytest.mark.parametrize("idx", range(4))
 def test_llama8b_layers_m1(bits, idx):
     name, (N, K) = LLAMA8B[idx]
-    _full_check(synth.seed_for(1, idx), name, N, K, bits, 1)
+    _full_check(synth.seed_for(1, idx), name, N, K, bits, 1, paths=(q.PATH_AUTO, q.PATH_MFMA))
 
 
 @pytest.mark.parametrize("bits", [4, 2])
@@ -170,4 +181,4 @@ def test_llama8b_layers_m1(bits, idx):
 def test_llama70b_layers_batches(bits, idx):
     name, (N, K) = LLAMA70B[idx]
     for M in (1, 2, 4, 8, 16):
-        _full_check(synth.seed_for(2, idx), name, N, K, bits, M)
+        _full_check(synth.seed_for(2, idx), name, N, K, bits, M, paths=(q.PATH_VALU, q.PATH_MFMA))

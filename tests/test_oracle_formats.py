@@ -75,6 +75,26 @@ def test_device_packing_is_a_field_permutation_of_plain(bits):
             assert fd == fp
 
 
+@pytest.mark.parametrize("bits", [2, 4, 8])
+def test_tile_order_positions_and_roundtrip(bits):
+    """Hand-derived positions of the tile order, then a round trip on a ragged shape."""
+    R, C = 20, 256                      # 2 row tiles (second padded), 2 groups
+    codes = ((np.arange(R)[:, None] * 5 + np.arange(C)[None, :] * 3) % (1 << bits)).astype(np.uint8)
+    words = formats.pack_tiles(codes, bits)
+    assert words.size == 32 * C * bits // 32
+    per = 32 // bits
+    # tile (rt=1, g=1), lane l = 16*kq + n: row 16 + n, k from 128 + 32*kq
+    for n, kq, i in [(0, 0, 0), (3, 2, bits - 1), (15, 3, bits // 2)]:
+        l = 16 * kq + n
+        w = int(words[(1 * 2 + 1) * 64 * bits + (i // 4) * 256 + l * min(bits, 4) + i % 4])
+        r, k = 16 + n, 128 + 32 * kq + per * i
+        for f in range(per):
+            kk = k + formats.device_field_k(bits, f)
+            want = codes[r, kk] if r < R else 0
+            assert (w >> (bits * f)) & ((1 << bits) - 1) == want, (n, kq, i, f)
+    assert np.array_equal(formats.unpack_tiles(words, bits, R, C), codes)
+
+
 def test_plain_packing_rejects_bad_codes():
     with pytest.raises(ValueError):
         formats.pack_plain(np.array([[4]], dtype=np.uint8), 2)
