@@ -20,7 +20,9 @@ Printed: ONE JSON line (rank 0).  Extra objects: "roofline" for the dominant
 kernel (gate+up, the largest matrix; average launch duration = a region of K
 back-to-back launches of that layer alone, timed the same way), "cpu_baseline"
 (the float64 CPU oracle on a bounded row sample, host cores), "layers"
-(per-layer us/call, same method).
+(per-layer us/call, same method).  roofline.traffic = HBM bytes per launch of
+that kernel from rocprofv3 FETCH_SIZE / WRITE_SIZE (scaled by a device copy of
+known size), read from profiles/; null when the kernel sources changed since.
 
 Profiling helpers (used under rocprofv3):
   --only LAYER          run only that layer in every step
@@ -162,6 +164,29 @@ def summarize_trace(path):
               f"{v[n // 10]:8.3f} {v[(9 * n) // 10]:8.3f}")
 
 
+# HBM traffic of the dominant kernel, from two rocprofv3 --pmc passes
+# (FETCH_SIZE, WRITE_SIZE) scaled by the same counters on a device copy of
+# known size; valid only for the kernel sources it was measured on.
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "gemv_w4a16_gate_up_28672x4096_m1_hbm_traffic.json")
+
+
+def measured_traffic():
+    import hashlib
+
+    try:
+        with open(TRAFFIC_FILE) as f:
+            rec = json.load(f)
+        h = hashlib.sha256()
+        for src in rec["kernel_sources"]:
+            with open(os.path.join(ROOT, src), "rb") as f:
+                h.update(f.read())
+    except (OSError, KeyError, ValueError):
+        return None
+    if h.hexdigest() != rec.get("kernel_src_sha256"):
+        return None  # the kernel changed since the counters were taken
+    return int(rec["traffic_bytes_per_launch"])
+
+
 def cpu_baseline(layers, budget_s=10.0):
     """The float64 oracle (unpack -> dequantize -> matvec) on the first 1/8 of
     the rows of every layer, repeated until `budget_s` of wall time."""
@@ -222,11 +247,11 @@ def main():
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     dev = torch.device("cuda:0")
     layers, R, step_bytes = build_inputs(torch, q, dev)
-    spot_check(q, layers)
 
     run = [L for L in layers if args.only in (None, L["name"])]
     if not run:
         raise SystemExit(f"bench: no layer named {args.only}")
+    spot_check(q, run)
     if args.only:
         step_bytes = sum(L["bytes"] for L in run)
 
@@ -296,7 +321,7 @@ def main():
             "peak": PEAK_HBM_GBS,
             "unit": "GB/s",
             "frac": round(achieved / PEAK_HBM_GBS, 4),
-            "traffic": None,
+            "traffic": measured_traffic() if dom["name"] == "gate_up" else None,
             "us_per_launch": dom_us,
             "bytes_per_launch": dom["bytes"],
         },

@@ -61,12 +61,13 @@ qg::TileCfg tile_cfg(int bits, int M, int N, int K, bool mfma) {
   return c;
 }
 
-// Dot engine for QGEMV_PATH_AUTO: VALU for small batches, MFMA from the
-// measured crossover batch on.
-int auto_path(int bits, int M, int K) {
+// Dot engine for QGEMV_PATH_AUTO, from the same sweeps: the VALU engine for
+// one activation row, and for two on narrow layers (N <= 4096); the MFMA
+// engine from there on, where one matrix-core pass serves all rows.
+int auto_path(int bits, int M, int N) {
   (void)bits;
-  (void)K;
-  return M <= 2 ? QGEMV_PATH_VALU : QGEMV_PATH_MFMA;
+  if (M <= 1 || (M == 2 && N <= 4096)) return QGEMV_PATH_VALU;
+  return QGEMV_PATH_MFMA;
 }
 
 }  // namespace
@@ -145,7 +146,7 @@ int qgemv_uniform(int bits, int path, int M, int N, int K, const uint16_t* x, co
     return QGEMV_ERR_VALUE;
   qg::UniformArgs a{bits, M, N, K, x, wq, scales, zeros, y};
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
-  if (path == QGEMV_PATH_AUTO) path = auto_path(bits, M, K);
+  if (path == QGEMV_PATH_AUTO) path = auto_path(bits, M, N);
   const bool mfma = path == QGEMV_PATH_MFMA;
   return hip_status(qg::launch_gemv_tiles(a, tile_cfg(bits, M, N, K, mfma), s));
 }

@@ -124,11 +124,17 @@ constexpr int ring_depth(int v) { return v == 1 || v == 2 ? 4 : 2; }
 // Occupancy target (waves per SIMD) the compiler must fit the registers in:
 // one-group chunks are sized for 5 (<= 96 VGPRs), the others for 3.
 constexpr int waves_per_simd(int ng) { return ng == 1 ? 5 : 3; }
+// Workgroup size bound: one-group chunks fit 16 waves (<= 128 VGPRs each).
+constexpr int max_threads(int ng) { return ng == 1 ? 1024 : 512; }
 
 // SAL: K/128 is a multiple of NG, so a chunk's NG scales of one row are one
 // aligned load and every chunk is whole.
-template <int BITS, bool MFMA, int MT, int NG, int D, int TPW, bool SAL>
-__global__ void __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(waves_per_simd(NG))))
+// XLDS (VALU engine): the workgroup stages its MT activation rows in LDS once
+// and every lane reads its 64-byte slice of a group from there.  The sixteen
+// lanes of a k-quarter share that slice, so loading it per lane through the
+// vector memory path would request 16x the bytes it uses.
+template <int BITS, bool MFMA, int MT, int NG, int D, int TPW, bool SAL, bool XLDS>
+__global__ void __launch_bounds__(max_threads(NG)) __attribute__((amdgpu_waves_per_eu(waves_per_simd(NG))))
 gemv_tiles_kernel(UniformArgs a) {
   using TR = Uni<BITS>;
   constexpr int PPD = TR::CPD / 2;
@@ -136,11 +142,13 @@ gemv_tiles_kernel(UniformArgs a) {
   constexpr uint32_t ZMASK = (1u << BITS) - 1u;
   constexpr uint32_t TB = 16u * 128u * BITS / 8;  // tile bytes
   constexpr int XR = MFMA ? 1 : MT;               // activation rows per lane
-  static_assert(TPW % D == 0, "a chunk's stages fill the ring evenly");
+  static_assert(TPW % D == 0 || (TPW == 1 && D == 2), "a chunk's stages fill the ring evenly");
   static_assert(ZPW % NG == 0, "a chunk's zero points share one word");
 
-  // per-wave partials: VALU [WK][TPW][MT][16] floats, MFMA [WK][TPW][64] float4
-  extern __shared__ float red[];
+  static_assert(!(MFMA && XLDS), "the MFMA engine's activation lanes are distinct");
+  // LDS: [staged activations: MT x K halves, XLDS only] then the per-wave
+  // partials: VALU [WK][TPW][MT][16] floats, MFMA [WK][TPW][64] float4
+  extern __shared__ __attribute__((aligned(16))) float smem[];
 
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -161,6 +169,11 @@ gemv_tiles_kernel(UniformArgs a) {
   const rsrc_t rz = make_rsrc(a.zeros, (uint32_t)N * zrow);
   const rsrc_t rs = make_rsrc(a.scales, (uint32_t)N * G * 2u);
   const rsrc_t rx = make_rsrc(a.x, (uint32_t)M * K * 2u);
+  // staged activation row stride in halves: K, then a zero pad that groups
+  // past K read instead (they add s = 0 times a finite value)
+  const int XK = K + 32;
+  float* red = XLDS ? smem + (size_t)MT * XK / 2 : smem;
+  const u4* xs = reinterpret_cast<const u4*>(smem);
 
   // activation row offsets of this lane (group 0, its k-quarter)
   uint32_t xoff[XR];
@@ -205,8 +218,12 @@ gemv_tiles_kernel(UniformArgs a) {
     st.z = bload4(rz, rv ? row * zrow : OOB, sz);
   };
 
-  u4 xr[NG][XR][4];
-  auto load_x = [&](int c) {
+  // activation buffers: one, or two when a single tile-row per workgroup
+  // leaves nothing else to overlap the next chunk's activation loads with
+  constexpr int XB = TPW < D ? 2 : 1;
+  u4 xr[XLDS ? 1 : XB][XLDS ? 1 : NG][XR][4];
+  auto load_x = [&](int c, int b) {
+    if constexpr (XLDS) return;
     const int gc0 = c * NG;
 #pragma unroll
     for (int j = 0; j < NG; ++j) {
@@ -215,7 +232,7 @@ gemv_tiles_kernel(UniformArgs a) {
 #pragma unroll
       for (int r = 0; r < XR; ++r)
 #pragma unroll
-        for (int v = 0; v < 4; ++v) xr[j][r][v] = bload16(rx, ok ? xoff[r] + 16u * v : OOB, sx);
+        for (int v = 0; v < 4; ++v) xr[XLDS ? 0 : b][XLDS ? 0 : j][r][v] = bload16(rx, ok ? xoff[r] + 16u * v : OOB, sx);
     }
   };
 
@@ -228,7 +245,7 @@ gemv_tiles_kernel(UniformArgs a) {
     for (int m = 0; m < MT; ++m) accv[t][m] = 0.f;
   }
 
-  auto compute = [&](int t, int c, const St& st) {
+  auto compute = [&](int t, int c, const St& st, int b) {
     const int gc0 = c * NG;
 #pragma unroll
     for (int j = 0; j < NG; ++j) {
@@ -241,7 +258,7 @@ gemv_tiles_kernel(UniformArgs a) {
         f4 dd = f4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int s = 0; s < 4; ++s)
-          dd = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(h8, xr[j][0][s]),
+          dd = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(h8, xr[b][XLDS ? 0 : j][0][s]),
                                                        cat4(p[4 * s], p[4 * s + 1], p[4 * s + 2], p[4 * s + 3]),
                                                        dd, 0, 0, 0);
 #pragma unroll
@@ -251,9 +268,13 @@ gemv_tiles_kernel(UniformArgs a) {
         for (int m = 0; m < MT; ++m) {
           float part = 0.f;
 #pragma unroll
-          for (int v = 0; v < 4; ++v)
+          for (int v = 0; v < 4; ++v) {
+            // x[m0 + m][128 (gc0 + j) + 32 kq + 8 v .. + 8], or the zero pad
+            const bool xin = (SAL && XB == 1) || gc0 + j < G;
+            const u4 xv = XLDS ? xs[(m * XK + (xin ? 128 * (gc0 + j) + 32 * kq : K)) / 8 + v] : xr[b][j][m][v];
 #pragma unroll
-            for (int e = 0; e < 4; ++e) part = dot2(p[4 * v + e], as_h2(xr[j][m][v][e]), part);
+            for (int e = 0; e < 4; ++e) part = dot2(p[4 * v + e], as_h2(xv[e]), part);
+          }
           accv[t][m] = fmaf(sc, part, accv[t][m]);
         }
       }
@@ -261,30 +282,74 @@ gemv_tiles_kernel(UniformArgs a) {
   };
 
   // chunks c = wave, wave + WK, ...; stages (t, c) in order through a ring of
-  // D register buffers, D - 1 stages in flight ahead of the one unpacked
+  // D register buffers, D - 1 stages in flight ahead of the one unpacked.
+  // The scheduling barriers keep the schedule as written: unpacking a stage
+  // early would hold its expanded pairs in registers and cost occupancy.
   St ring[D];
   int c = wave;
-  if (c < NC) {
+  auto stage_x = [&]() {
+    // activations of rows m0 .. m0 + MT - 1 into LDS, 16 distinct bytes per
+    // lane and load; rows >= M read zeros.  Four loads in flight per lane.
+    // (row stride XK; the 4 pad vectors of each row get zeros: their loads
+    // are out of range)
+    u4* xw = reinterpret_cast<u4*>(smem);
+    const int X8 = XK / 8, n16 = MT * X8;
+    for (int i0 = threadIdx.x; i0 < n16; i0 += 4 * blockDim.x) {
+      u4 v[4];
 #pragma unroll
-    for (int t = 0; t < D - 1; ++t) load_stage(t, c, ring[t]);
-    load_x(c);
-  }
-  for (; c < NC; c += WK) {
-#pragma unroll
-    for (int t = 0; t < TPW; ++t) {
-      const int ta = t + D - 1;  // stage to issue (slot of the stage unpacked last)
-      if (ta < TPW) {
-        load_stage(ta, c, ring[ta % D]);
-      } else {
-        load_stage(ta - TPW, c + WK, ring[ta % D]);  // next chunk (zeros past the last); same slot
+      for (int u = 0; u < 4; ++u) {
+        const int i = i0 + u * blockDim.x;
+        const int m = i / X8, k8 = i - m * X8;
+        v[u] = bload16(rx, i < n16 && m0 + m < M && k8 < K / 8 ? ((uint32_t)(m0 + m) * K + 8u * k8) * 2u : OOB);
       }
-      // keep the schedule as written: unpacking a stage early would hold its
-      // expanded pairs in registers and cost occupancy
+#pragma unroll
+      for (int u = 0; u < 4; ++u)
+        if (i0 + u * blockDim.x < n16) xw[i0 + u * blockDim.x] = v[u];
+    }
+    __syncthreads();
+  };
+  if constexpr (XB == 1) {
+    if (c < NC) {
+#pragma unroll
+      for (int t = 0; t < D - 1; ++t) load_stage(t, c, ring[t]);
+      load_x(c, 0);
+    }
+    if constexpr (XLDS) stage_x();
+    for (; c < NC; c += WK) {
+#pragma unroll
+      for (int t = 0; t < TPW; ++t) {
+        const int ta = t + D - 1;  // stage to issue (slot of the stage unpacked last)
+        if (ta < TPW) {
+          load_stage(ta, c, ring[ta % D]);
+        } else {
+          load_stage(ta - TPW, c + WK, ring[ta % D]);  // next chunk (zeros past the last); same slot
+        }
+        __builtin_amdgcn_sched_barrier(0);
+        compute(t, c, ring[t % D], 0);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+      load_x(c + WK, 0);
+    }
+  } else {
+    // one tile-row, two stages: chunks alternate between slot/buffer 0 and 1
+    // (a chunk past the last reads zeros and adds nothing)
+    if (c < NC) {
+      load_stage(0, c, ring[0]);
+      load_x(c, 0);
+    }
+    if constexpr (XLDS) stage_x();
+    for (; c < NC; c += 2 * WK) {
+      load_stage(0, c + WK, ring[1]);
+      load_x(c + WK, 1);
       __builtin_amdgcn_sched_barrier(0);
-      compute(t, c, ring[t % D]);
+      compute(0, c, ring[0], 0);
+      __builtin_amdgcn_sched_barrier(0);
+      load_stage(0, c + 2 * WK, ring[0]);
+      load_x(c + 2 * WK, 0);
+      __builtin_amdgcn_sched_barrier(0);
+      compute(0, c + WK, ring[1], 1);
       __builtin_amdgcn_sched_barrier(0);
     }
-    load_x(c + WK);
   }
 
   if constexpr (MFMA) {
@@ -325,23 +390,50 @@ constexpr size_t LDS_MAX = 64 * 1024;
 size_t tiles_lds_bytes(bool mfma, int mt, int tpw, int wk) {
   return mfma ? (size_t)wk * tpw * 64 * 16 : (size_t)wk * tpw * mt * 16 * 4;
 }
+// activation staging of the VALU engine: MT rows of K halves
+constexpr size_t XLDS_MAX = 64 * 1024 + 128;
+size_t xlds_bytes(bool mfma, int mt, int K) { return mfma ? 0 : (size_t)mt * (K + 32) * 2; }
 
 template <int BITS, bool MFMA, int MT, int V, int TPW>
 hipError_t launch_t(const UniformArgs& a, const TileCfg& c, hipStream_t s) {
   constexpr int NG = chunk_groups(BITS, MFMA, MT, V);
   constexpr int D = ring_depth(V);
-  if constexpr (TPW % D != 0) {
+  if constexpr (TPW % D != 0 && !(TPW == 1 && D == 2 && NG == 1)) {
     return hipErrorInvalidValue;
   } else {
     const int NT = (a.N + 15) / 16;
     const dim3 grid((NT + TPW - 1) / TPW, MFMA ? 1 : (a.M + MT - 1) / MT);
     const dim3 block(64 * c.wk);
-    const size_t lds = tiles_lds_bytes(MFMA, MT, TPW, c.wk);
-    if (lds > LDS_MAX) return hipErrorInvalidValue;
-    if ((a.K / 128) % NG == 0)
-      hipLaunchKernelGGL((gemv_tiles_kernel<BITS, MFMA, MT, NG, D, TPW, true>), grid, block, lds, s, a);
-    else
-      hipLaunchKernelGGL((gemv_tiles_kernel<BITS, MFMA, MT, NG, D, TPW, false>), grid, block, lds, s, a);
+    const size_t red = tiles_lds_bytes(MFMA, MT, TPW, c.wk);
+    if (red > LDS_MAX || 64 * c.wk > max_threads(NG)) return hipErrorInvalidValue;
+    const size_t xl = xlds_bytes(MFMA, MT, a.K);
+    const bool sal = (a.K / 128) % NG == 0;
+    if (!MFMA && xl <= XLDS_MAX) {
+      const size_t lds = xl + red;
+      if (lds > 64 * 1024) {
+        static bool raised = false;  // one-time opt-in above the default dynamic LDS limit
+        if (!raised) {
+          hipError_t e = hipFuncSetAttribute(
+              reinterpret_cast<const void*>(&gemv_tiles_kernel<BITS, MFMA, MT, NG, D, TPW, true, !MFMA>),
+              hipFuncAttributeMaxDynamicSharedMemorySize, (int)(XLDS_MAX + LDS_MAX));
+          if (e == hipSuccess)
+            e = hipFuncSetAttribute(
+                reinterpret_cast<const void*>(&gemv_tiles_kernel<BITS, MFMA, MT, NG, D, TPW, false, !MFMA>),
+                hipFuncAttributeMaxDynamicSharedMemorySize, (int)(XLDS_MAX + LDS_MAX));
+          if (e != hipSuccess) return e;
+          raised = true;
+        }
+      }
+      if (sal)
+        hipLaunchKernelGGL((gemv_tiles_kernel<BITS, MFMA, MT, NG, D, TPW, true, !MFMA>), grid, block, lds, s, a);
+      else
+        hipLaunchKernelGGL((gemv_tiles_kernel<BITS, MFMA, MT, NG, D, TPW, false, !MFMA>), grid, block, lds, s, a);
+    } else {
+      if (sal)
+        hipLaunchKernelGGL((gemv_tiles_kernel<BITS, MFMA, MT, NG, D, TPW, true, false>), grid, block, red, s, a);
+      else
+        hipLaunchKernelGGL((gemv_tiles_kernel<BITS, MFMA, MT, NG, D, TPW, false, false>), grid, block, red, s, a);
+    }
     return hipGetLastError();
   }
 }
@@ -349,6 +441,9 @@ hipError_t launch_t(const UniformArgs& a, const TileCfg& c, hipStream_t s) {
 template <int BITS, bool MFMA, int MT, int V>
 hipError_t launch_tpw(const UniformArgs& a, const TileCfg& c, hipStream_t s) {
   switch (c.tpw) {
+    case 1:
+      if constexpr (V == 3) return launch_t<BITS, MFMA, MT, V, 1>(a, c, s);
+      return hipErrorInvalidValue;
     case 2: return launch_t<BITS, MFMA, MT, V, 2>(a, c, s);
     case 4: return launch_t<BITS, MFMA, MT, V, 4>(a, c, s);
     case 8: return launch_t<BITS, MFMA, MT, V, 8>(a, c, s);
@@ -379,27 +474,46 @@ hipError_t launch_b(const UniformArgs& a, const TileCfg& c, hipStream_t s) {
 
 }  // namespace
 
+// Launch shape per engine and layer shape, from sweeps on MI355X over the
+// Llama-3-8B / 70B decode layers (cache-cold weights, W2/W4/W8, M = 1..16):
+//  * few tile-rows (NT <= 256, N <= 4096): one tile-row per workgroup and
+//    one-group chunks, so all 256 CUs get work;
+//  * otherwise two tile-rows per workgroup, four-group chunks; waves per
+//    workgroup shrink as the tile-row count grows (the grid already fills
+//    the chip); the MFMA engine takes more tile-rows per workgroup on the
+//    widest layers, where it reuses each activation fragment longer.
 TileCfg pick_tiles(int bits, int M, int N, int K, bool mfma) {
   TileCfg c;
   c.mfma = mfma;
   c.mt = mfma || M <= 1 ? 1 : 2;
-  c.v = 0;
-  const int ng = chunk_groups(bits, mfma, c.mt, c.v);
   const int G = K / 128;
-  const int nc = (G + ng - 1) / ng;
   const long nt = (N + 15) / 16;
-  const long mtiles = mfma ? 1 : (M + c.mt - 1) / c.mt;
-  // every chunk in flight at once (up to 8 waves), then as many tile-rows
-  // per workgroup as still leave >= 4096 waves
-  c.wk = nc < 8 ? nc : 8;
-  c.tpw = 8;
-  while (c.tpw > 2 && ((nt + c.tpw - 1) / c.tpw) * mtiles * c.wk < 4096) c.tpw /= 2;
-  while (c.tpw > 2 && tiles_lds_bytes(mfma, c.mt, c.tpw, c.wk) > LDS_MAX) c.tpw /= 2;
+  if (nt <= (bits == 8 && !mfma ? 640 : 256)) {
+    c.tpw = 1;
+    c.v = 3;
+    c.wk = !mfma && G >= 64 ? 16 : 8;
+  } else if (!mfma) {
+    c.tpw = 2;
+    c.v = 0;
+    c.wk = nt >= 2048 ? 4 : (nt >= 1024 ? 2 : 8);
+  } else if (nt >= 1536) {
+    const bool deep = M >= 8 && bits == 4;  // 2- and 8-bit stages leave no room for 8 tile-rows
+    c.tpw = deep ? 8 : 4;
+    c.v = deep ? 1 : 0;
+    c.wk = deep ? 8 : 4;
+  } else {
+    c.tpw = nt >= 640 ? 4 : 2;
+    c.v = 0;
+    c.wk = nt >= 640 ? 8 : 4;
+  }
+  // never more waves than chunks of groups
+  const int nc = (G + chunk_groups(bits, mfma, c.mt, c.v) - 1) / chunk_groups(bits, mfma, c.mt, c.v);
+  if (c.wk > nc) c.wk = nc < 1 ? 1 : nc;
   return c;
 }
 
 hipError_t launch_gemv_tiles(const UniformArgs& a, const TileCfg& c, hipStream_t s) {
-  if (c.wk < 1 || c.wk > 8) return hipErrorInvalidValue;
+  if (c.wk < 1 || c.wk > 16) return hipErrorInvalidValue;
   switch (a.bits) {
     case 2: return launch_b<2>(a, c, s);
     case 4: return launch_b<4>(a, c, s);

@@ -17,8 +17,9 @@ struct UniformArgs {
 
 // Launch shape of the tiled kernel: mfma selects the dot engine; mt = batch
 // rows per pass of the VALU engine (1 or 2; the MFMA engine takes all 16);
-// tpw = 16-row tile-rows per workgroup (2, 4, 8); wk = waves per workgroup,
-// which take the chunks of quant groups round-robin (1..8); v = pipeline
+// tpw = 16-row tile-rows per workgroup (1 [v = 3 only], 2, 4, 8); wk = waves per workgroup,
+// which take the chunks of quant groups round-robin (1..8, 16 for one-group
+// chunks); v = pipeline
 // variant (0: 4-group chunks, 2 stage buffers; 1: 2-group chunks, 4 buffers;
 // tpw must be a multiple of the buffer count).
 struct TileCfg {
