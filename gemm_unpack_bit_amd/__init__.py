@@ -38,6 +38,7 @@ _SIGS = {
     "qgemv_w4a16": (_i, [_i, _i, _i, _vp, _vp, _vp, _vp, _vp, _vp]),
     "qgemv_w8a16": (_i, [_i, _i, _i, _vp, _vp, _vp, _vp, _vp, _vp]),
     "qgemv_uniform": (_i, [_i, _i, _i, _i, _i, _vp, _vp, _vp, _vp, _vp, _vp]),
+    "qgemv_lut4": (_i, [_i, _i, _i, _vp, _vp, _vp, _vp, _vp, _vp]),
 }
 
 
@@ -166,3 +167,29 @@ def w4a16(x, wq, scales, zeros, out=None):
 
 def w8a16(x, wq, scales, zeros, out=None):
     return uniform(x, wq, scales, zeros, 8, PATH_AUTO, out)
+
+
+def lut4(x, wq, absmax, lut, out=None):
+    """y = x . (lut[q] * absmax)^T for 4-bit codes with a 16-entry fp16 table.
+
+    x [M, K] fp16; wq int32 4-bit codes in the device layout; absmax [N, K/64]
+    fp16 (one scale per 64 consecutive k); lut [16] fp16.  Returns y [M, N]."""
+    torch = _torch()
+    _need(x, torch.float16, "x")
+    _need(wq, torch.int32, "wq")
+    _need(absmax, torch.float16, "absmax")
+    _need(lut, torch.float16, "lut")
+    M, K = x.shape
+    N = absmax.shape[0]
+    need = packed_words(4, N, K)
+    if need and wq.numel() != need:
+        raise ValueError("wq does not hold N x K device-layout 4-bit codes")
+    if lut.numel() != 16:
+        raise ValueError("lut must hold 16 entries")
+    if out is None:
+        out = torch.empty((M, N), dtype=torch.float16, device=x.device)
+    else:
+        _need(out, torch.float16, "out")
+    _check("qgemv_lut4", lib().qgemv_lut4(M, N, K, _ptr(x), _ptr(wq), _ptr(absmax), _ptr(lut), _ptr(out),
+                                          _stream(x)))
+    return out

@@ -61,6 +61,22 @@ qg::TileCfg tile_cfg(int bits, int M, int N, int K, bool mfma) {
   return c;
 }
 
+// Tuning override of the LUT4 launch shape: QGEMV_LUT4_CFG="tpw,ng,wk[,mt]".
+qg::Lut4Cfg lut4_cfg(int M, int N, int K) {
+  qg::Lut4Cfg c = qg::pick_lut4(M, N, K);
+  if (const char* e = std::getenv("QGEMV_LUT4_CFG")) {
+    int tpw, ng, wk, mt;
+    const int n = std::sscanf(e, "%d,%d,%d,%d", &tpw, &ng, &wk, &mt);
+    if (n >= 3) {
+      c.tpw = tpw;
+      c.ng = ng;
+      c.wk = wk;
+    }
+    if (n == 4) c.mt = mt;
+  }
+  return c;
+}
+
 // Dot engine for QGEMV_PATH_AUTO, from the same sweeps: the VALU engine for
 // one activation row, and for two on narrow layers (N <= 4096); the MFMA
 // engine from there on, where one matrix-core pass serves all rows.
@@ -162,6 +178,24 @@ int qgemv_w4a16(int M, int N, int K, const uint16_t* x, const uint32_t* wq, cons
 int qgemv_w8a16(int M, int N, int K, const uint16_t* x, const uint32_t* wq, const uint16_t* scales,
                 const uint32_t* zeros, uint16_t* y, qgemv_stream_t stream) {
   return qgemv_uniform(8, QGEMV_PATH_AUTO, M, N, K, x, wq, scales, zeros, y, stream);
+}
+
+int qgemv_lut4(int M, int N, int K, const uint16_t* x, const uint32_t* wq, const uint16_t* absmax,
+               const uint16_t* lut, uint16_t* y, qgemv_stream_t stream) {
+  if (!x || !wq || !absmax || !lut || !y) return QGEMV_ERR_NULL;
+  int rc = check_mnk(M, N, K, 4);
+  if (rc) return rc;
+  if (K > QGEMV_LUT4_MAX_K || (size_t)K > qg::lut4_max_k(1)) return QGEMV_ERR_SHAPE;
+  if (!aligned16(x) || !aligned16(wq) || ((uintptr_t)absmax & 1u) || ((uintptr_t)lut & 1u) ||
+      ((uintptr_t)y & 1u))
+    return QGEMV_ERR_ALIGN;
+  const size_t ybytes = (size_t)M * N * 2;
+  if (overlaps(y, ybytes, x, (size_t)M * K * 2) ||
+      overlaps(y, ybytes, wq, words(4, QGEMV_LAYOUT_DEVICE, N, K) * 4) ||
+      overlaps(y, ybytes, absmax, (size_t)N * (K / QGEMV_LUT_BLOCK) * 2) || overlaps(y, ybytes, lut, 32))
+    return QGEMV_ERR_VALUE;
+  qg::Lut4Args a{M, N, K, x, wq, absmax, lut, y};
+  return hip_status(qg::launch_gemv_lut4(a, lut4_cfg(M, N, K), reinterpret_cast<hipStream_t>(stream)));
 }
 
 }  // extern "C"

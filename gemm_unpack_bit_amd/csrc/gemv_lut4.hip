@@ -1,0 +1,353 @@
+// Fused LUT-dequantize-and-multiply for 4-bit codes with a 16-entry fp16
+// lookup table (NF4-style) and a per-64-block fp16 scale, at decode batch
+// M <= 16, on gfx950:
+//
+//   y[m, n] = sum_k x[m, k] * LUT[q[n, k]] * a[n, k/64]
+//
+// The Fast NF4 Dequantization Kernels page: the 16-level table lives on chip
+// (shared memory, 64 bytes per block) instead of being re-read per element,
+// with simplified indexing; the 64-weight block scale is applied per block.
+//
+// Design (gfx950):
+//  * Codes use the same tiled device layout as the uniform W4 kernels (one
+//    16-row x 128-k tile per quant group, lane l = row l % 16, k-quarter
+//    l / 16), so the packer and the streaming are shared.  A lane's 32 k lie in
+//    one 64-block, so the block scale is one per lane and group.
+//  * Lookup: an LDS pair table holds, for every code byte b, the fp16 pair
+//    (LUT[b & 15], LUT[b >> 4]), replicated 64 times lane-major: entry b of copy
+//    c at byte (64 b + c) * 4.  Lane l always reads copy l, so every lookup is
+//    bank-conflict-free, and its address (b << 8) | (4 l) is one v_perm_b32 of
+//    the code word and 4 l.  One LDS read yields two dequantized weights.
+//  * In the device field order byte j of a code word holds the k offsets
+//    (0,2), (4,6), (1,3), (5,7) for j = 0..3.  The activations are staged in
+//    LDS with each 8-k run stored in that order, so a table pair meets its
+//    activation pair as loaded: per 8 weights, 4 v_perm + 4 ds_read_b32 +
+//    4 v_dot2 (one VALU instruction per weight).
+//  * Streaming, pipeline, work split and reduction follow the uniform kernel:
+//    branch-free non-temporal tile loads through a two-slot register ring,
+//    permlane quarter sums, LDS wave sums in fixed order (deterministic).
+#include "common.hpp"
+#include "kernels.hpp"
+
+namespace qg {
+namespace {
+
+constexpr int TABLE_COPIES = 64;
+constexpr uint32_t TABLE_BYTES = 256u * TABLE_COPIES * 4u;  // 64 KB
+
+// activation area: MT staged rows, and at least 1 KB (it first holds the 256
+// pair values the table copies are made from)
+__host__ __device__ constexpr size_t xarea_bytes(int mt, int K) {
+  return (size_t)mt * (K + 32) * 2 > 1024 ? (size_t)mt * (K + 32) * 2 : 1024;
+}
+
+__device__ __forceinline__ float quarter_sum4(float v) {
+  const uint32_t u = __float_as_uint(v);
+  const auto a = __builtin_amdgcn_permlane32_swap(u, u, false, false);
+  const float s = __uint_as_float(a[0]) + __uint_as_float(a[1]);
+  const uint32_t su = __float_as_uint(s);
+  const auto b = __builtin_amdgcn_permlane16_swap(su, su, false, false);
+  return __uint_as_float(b[0]) + __uint_as_float(b[1]);
+}
+
+// Block scales of NG consecutive groups of one row: the lane's 64-block is
+// (2 g + kq / 2); one aligned load when SAL.
+template <int NG>
+__device__ __forceinline__ void load_block_scales(rsrc_t r, uint32_t rowoff, uint32_t soff, int half,
+                                                  uint16_t* s) {
+  if constexpr (NG == 1) {
+    const uint32_t v = bload4(r, rowoff, soff);
+    s[0] = (uint16_t)(v >> (16 * half));
+  } else if constexpr (NG == 2) {
+    const u2 v = __builtin_bit_cast(u2, __builtin_amdgcn_raw_buffer_load_b64(r, rowoff, soff, 0));
+    s[0] = (uint16_t)(v[0] >> (16 * half));
+    s[1] = (uint16_t)(v[1] >> (16 * half));
+  } else {
+    static_assert(NG == 4, "NG in {1, 2, 4}");
+    const u4 v = bload16(r, rowoff, soff);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) s[j] = (uint16_t)(v[j] >> (16 * half));
+  }
+}
+
+// TPW tile-rows per workgroup (1, 2), NG groups per chunk, MT activation
+// rows per workgroup.  SAL: K/128 is a multiple of NG and the block scales are
+// 4*NG-byte aligned, so a chunk's scales are one load.
+template <int MT, int NG, int TPW, bool SAL>
+__global__ void __launch_bounds__(512) gemv_lut4_kernel(Lut4Args a) {
+  // LDS: [pair table 64 KB][activations MT x XK halves, 8-k runs permuted
+  // (xarea_bytes)][partials]
+  extern __shared__ __attribute__((aligned(16))) uint32_t lsm[];
+  char* const lds = reinterpret_cast<char*>(lsm);
+
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int WK = blockDim.x >> 6;
+  const int n = lane & 15;
+  const int kq = lane >> 4;
+  const int M = a.M, N = a.N, K = a.K;
+  const int G = K / 128;
+  const int KB = K / 64;  // block scales per row
+  const int NT = (N + 15) / 16;
+  const int NC = (G + NG - 1) / NG;
+  const int m0 = blockIdx.y * MT;
+  const int rt0 = blockIdx.x * TPW;
+  const int XK = K + 32;  // staged row stride (halves): K, then a zero pad
+  const uint32_t lane4 = 4u * lane;
+  float* const red = reinterpret_cast<float*>(lds + TABLE_BYTES + xarea_bytes(MT, K));
+
+  const rsrc_t rw = make_rsrc(a.wq, (uint32_t)NT * G * 1024u);
+  const rsrc_t ra = make_rsrc(a.absmax, (uint32_t)N * KB * 2u);
+  const rsrc_t rx = make_rsrc(a.x, (uint32_t)M * K * 2u);
+  const rsrc_t rl = make_rsrc(a.lut, 32u);
+
+  struct St {
+    u4 c[NG];
+    uint16_t s[NG];
+  };
+
+  // all loads unconditional: out-of-range tile-rows, groups and chunks read
+  // zeros (scale 0), so they add exactly 0
+  auto load_stage = [&](int t, int c, St& st) {
+    const int rt = rt0 + t;
+    const int gc0 = c * NG;
+    const bool tv = rt < NT;
+    const bool cv = gc0 < G;
+    const uint32_t row = (uint32_t)rt * 16u + n;
+    const bool rv = row < (uint32_t)N && cv;
+#pragma unroll
+    for (int j = 0; j < NG; ++j) {
+      const bool ok = tv && (SAL ? cv : gc0 + j < G);
+      const uint32_t sw = __builtin_amdgcn_readfirstlane(ok ? ((uint32_t)rt * G + gc0 + j) * 1024u : 0u);
+      st.c[j] = bload16<CPOL_NT>(rw, ok ? 16u * lane : OOB, sw);
+    }
+    const uint32_t ss = __builtin_amdgcn_readfirstlane(cv ? 4u * gc0 : 0u);
+    if constexpr (SAL) {
+      load_block_scales<NG>(ra, rv ? row * (uint32_t)KB * 2u : OOB, ss, kq >> 1, st.s);
+    } else {
+#pragma unroll
+      for (int j = 0; j < NG; ++j)
+        st.s[j] = bload2(ra, rv && gc0 + j < G ? (row * (uint32_t)KB + (kq >> 1)) * 2u : OOB, ss + 4u * j);
+    }
+  };
+
+  float acc[TPW][MT];
+#pragma unroll
+  for (int t = 0; t < TPW; ++t)
+#pragma unroll
+    for (int m = 0; m < MT; ++m) acc[t][m] = 0.f;
+
+  // With several tile-rows per workgroup a chunk's activation slices are read
+  // from LDS once into registers and reused for every tile-row; with one they
+  // are read per use.
+  constexpr bool XREG = TPW >= 2;
+  u4 xc[XREG ? NG : 1][XREG ? MT : 1][4];
+  auto xslice = [&](int c, int j, int m, int d) -> u4 {
+    const int gc0 = c * NG;
+    const bool xin = (SAL && TPW >= 2) || gc0 + j < G;
+    const uint32_t xk = xin ? 128u * (gc0 + j) + 32u * kq : (uint32_t)K;
+    return *reinterpret_cast<const u4*>(lds + TABLE_BYTES + ((uint32_t)m * XK + xk + 8u * d) * 2u);
+  };
+  auto load_xc = [&](int c) {
+    if constexpr (XREG) {
+#pragma unroll
+      for (int j = 0; j < NG; ++j)
+#pragma unroll
+        for (int m = 0; m < MT; ++m)
+#pragma unroll
+          for (int d = 0; d < 4; ++d) xc[j][m][d] = xslice(c, j, m, d);
+    }
+  };
+
+  auto compute = [&](int t, int c, const St& st) {
+#pragma unroll
+    for (int j = 0; j < NG; ++j) {
+      float part[MT];
+#pragma unroll
+      for (int m = 0; m < MT; ++m) part[m] = 0.f;
+#pragma unroll
+      for (int d = 0; d < 4; ++d) {
+        u4 xv[MT];
+#pragma unroll
+        for (int m = 0; m < MT; ++m) xv[m] = XREG ? xc[XREG ? j : 0][XREG ? m : 0][d] : xslice(c, j, m, d);
+        const uint32_t w = st.c[j][d];
+#pragma unroll
+        for (int jb = 0; jb < 4; ++jb) {
+          // (code byte jb << 8) | 4 lane: entry jb of this lane's table copy
+          const uint32_t addr = __builtin_amdgcn_perm(w, lane4, 0x0C0C0000u | ((4u + jb) << 8));
+          const h2 pr = as_h2(*reinterpret_cast<const uint32_t*>(lds + addr));
+#pragma unroll
+          for (int m = 0; m < MT; ++m) part[m] = dot2(pr, as_h2(xv[m][jb]), part[m]);
+        }
+      }
+      const float sc = h2f(st.s[j]);
+#pragma unroll
+      for (int m = 0; m < MT; ++m) acc[t][m] = fmaf(sc, part[m], acc[t][m]);
+    }
+  };
+
+  St ring[2];
+  int c = wave;
+  if (c < NC) load_stage(0, c, ring[0]);  // weights in flight while the tables fill
+
+  // pair table: 256 pair values, then 64 lane-major copies of each
+  {
+    uint32_t* pairs = reinterpret_cast<uint32_t*>(lds + TABLE_BYTES);  // scratch in the x area
+    for (int e = threadIdx.x; e < 256; e += blockDim.x) {
+      const uint32_t lo = bload2(rl, 2u * (e & 15));
+      const uint32_t hi = bload2(rl, 2u * (e >> 4));
+      pairs[e] = lo | (hi << 16);
+    }
+    __syncthreads();
+    for (int i = threadIdx.x; i < 256 * TABLE_COPIES; i += blockDim.x) lsm[i] = pairs[i / TABLE_COPIES];
+    __syncthreads();
+  }
+  // activations of rows m0 .. m0 + MT - 1; each 8-k run stored as
+  // (x0,x2),(x4,x6),(x1,x3),(x5,x7); the 4 pad runs per row read zeros
+  {
+    u4* xw = reinterpret_cast<u4*>(lds + TABLE_BYTES);
+    const int X8 = XK / 8, n16 = MT * X8;
+    for (int i0 = threadIdx.x; i0 < n16; i0 += 4 * blockDim.x) {
+      u4 v[4];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const int i = i0 + u * blockDim.x;
+        const int m = i / X8, k8 = i - m * X8;
+        v[u] = bload16(rx, i < n16 && m0 + m < M && k8 < K / 8 ? ((uint32_t)(m0 + m) * K + 8u * k8) * 2u : OOB);
+      }
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const u4 p = {__builtin_amdgcn_perm(v[u][1], v[u][0], 0x05040100u),
+                      __builtin_amdgcn_perm(v[u][3], v[u][2], 0x05040100u),
+                      __builtin_amdgcn_perm(v[u][1], v[u][0], 0x07060302u),
+                      __builtin_amdgcn_perm(v[u][3], v[u][2], 0x07060302u)};
+        if (i0 + u * blockDim.x < n16) xw[i0 + u * blockDim.x] = p;
+      }
+    }
+    __syncthreads();
+  }
+
+  if constexpr (TPW >= 2) {
+    for (; c < NC; c += WK) {
+      load_xc(c);
+#pragma unroll
+      for (int t = 0; t < TPW; ++t) {
+        if (t + 1 < TPW)
+          load_stage(t + 1, c, ring[(t + 1) & 1]);
+        else
+          load_stage(0, c + WK, ring[(t + 1) & 1]);  // next chunk (zeros past the last)
+        __builtin_amdgcn_sched_barrier(0);
+        compute(t, c, ring[t & 1]);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    }
+  } else {
+    // one tile-row: chunks alternate between the two slots
+    for (; c < NC; c += 2 * WK) {
+      load_stage(0, c + WK, ring[1]);
+      __builtin_amdgcn_sched_barrier(0);
+      compute(0, c, ring[0]);
+      __builtin_amdgcn_sched_barrier(0);
+      load_stage(0, c + 2 * WK, ring[0]);
+      __builtin_amdgcn_sched_barrier(0);
+      compute(0, c + WK, ring[1]);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  }
+
+#pragma unroll
+  for (int t = 0; t < TPW; ++t)
+#pragma unroll
+    for (int m = 0; m < MT; ++m) {
+      const float v = quarter_sum4(acc[t][m]);
+      if (lane < 16) red[((wave * TPW + t) * MT + m) * 16 + lane] = v;
+    }
+  __syncthreads();
+  for (int e = threadIdx.x; e < TPW * MT * 16; e += blockDim.x) {
+    const int r = e & 15, m = (e >> 4) % MT, t = (e >> 4) / MT;
+    float sum = 0.f;
+    for (int w = 0; w < WK; ++w) sum += red[((w * TPW + t) * MT + m) * 16 + r];
+    const int row = (rt0 + t) * 16 + r;
+    if (m0 + m < M && row < N) a.y[(size_t)(m0 + m) * N + row] = f2h(sum);
+  }
+}
+
+constexpr size_t LUT4_LDS_LIMIT = 160 * 1024;
+
+size_t lut4_lds_bytes(int mt, int tpw, int wk, int K) {
+  return TABLE_BYTES + xarea_bytes(mt, K) + (size_t)wk * tpw * mt * 16 * 4;
+}
+
+template <int MT, int NG, int TPW>
+hipError_t launch_l(const Lut4Args& a, const Lut4Cfg& c, hipStream_t s) {
+  const int NT = (a.N + 15) / 16;
+  const dim3 grid((NT + TPW - 1) / TPW, (a.M + MT - 1) / MT);
+  const dim3 block(64 * c.wk);
+  const size_t lds = lut4_lds_bytes(MT, TPW, c.wk, a.K);
+  if (lds > LUT4_LDS_LIMIT) return hipErrorInvalidValue;
+  const bool sal = (a.K / 128) % NG == 0 && reinterpret_cast<uintptr_t>(a.absmax) % (4 * NG) == 0;
+  static bool raised = false;  // every launch needs more than the default 64 KB of dynamic LDS
+  if (!raised) {
+    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&gemv_lut4_kernel<MT, NG, TPW, true>),
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)LUT4_LDS_LIMIT);
+    if (e == hipSuccess)
+      e = hipFuncSetAttribute(reinterpret_cast<const void*>(&gemv_lut4_kernel<MT, NG, TPW, false>),
+                              hipFuncAttributeMaxDynamicSharedMemorySize, (int)LUT4_LDS_LIMIT);
+    if (e != hipSuccess) return e;
+    raised = true;
+  }
+  if (sal)
+    hipLaunchKernelGGL((gemv_lut4_kernel<MT, NG, TPW, true>), grid, block, lds, s, a);
+  else
+    hipLaunchKernelGGL((gemv_lut4_kernel<MT, NG, TPW, false>), grid, block, lds, s, a);
+  return hipGetLastError();
+}
+
+template <int MT>
+hipError_t launch_lm(const Lut4Args& a, const Lut4Cfg& c, hipStream_t s) {
+  switch (c.tpw * 10 + c.ng) {
+    case 11: return launch_l<MT, 1, 1>(a, c, s);
+    case 24: return launch_l<MT, 4, 2>(a, c, s);
+  }
+  return hipErrorInvalidValue;
+}
+
+}  // namespace
+
+size_t lut4_max_k(int mt) {
+  // largest multiple of 128 whose staged rows and table fit with 8 waves x 2 tile-rows
+  size_t k = 0;
+  while (lut4_lds_bytes(mt, 2, 8, (int)(k + 128)) <= LUT4_LDS_LIMIT) k += 128;
+  return k;
+}
+
+Lut4Cfg pick_lut4(int M, int N, int K) {
+  Lut4Cfg c;
+  c.mt = M <= 1 ? 1 : 2;
+  if ((size_t)K > lut4_max_k(c.mt)) c.mt = 1;
+  const long nt = (N + 15) / 16;
+  const int G = K / 128;
+  // sweeps on MI355X (Llama-3-8B layers, M = 1, 2): one tile-row per
+  // workgroup only for the narrowest layers
+  if (nt <= 256) {
+    c.tpw = 1;
+    c.ng = 1;
+  } else {
+    c.tpw = 2;
+    c.ng = 4;
+  }
+  const int nc = (G + c.ng - 1) / c.ng;
+  c.wk = nc < 8 ? nc : 8;
+  return c;
+}
+
+hipError_t launch_gemv_lut4(const Lut4Args& a, const Lut4Cfg& c, hipStream_t s) {
+  if (c.wk < 1 || c.wk > 8) return hipErrorInvalidValue;
+  switch (c.mt) {
+    case 1: return launch_lm<1>(a, c, s);
+    case 2: return launch_lm<2>(a, c, s);
+  }
+  return hipErrorInvalidValue;
+}
+
+}  // namespace qg

@@ -30,6 +30,25 @@ struct TileCfg {
 TileCfg pick_tiles(int bits, int M, int N, int K, bool mfma);
 hipError_t launch_gemv_tiles(const UniformArgs& a, const TileCfg& c, hipStream_t s);
 
+// 4-bit codes (tiled device layout) with a 16-entry fp16 table and fp16
+// per-64-block scales: y = x . (LUT[q] * absmax)^T
+struct Lut4Args {
+  int M, N, K;
+  const uint16_t* x;
+  const uint32_t* wq;
+  const uint16_t* absmax;
+  const uint16_t* lut;
+  uint16_t* y;
+};
+// mt = activation rows per workgroup (1, 2); tpw = tile-rows per workgroup
+// (1 with ng = 1, or 2 with ng = 4); wk = waves per workgroup (1..8)
+struct Lut4Cfg {
+  int mt, tpw, ng, wk;
+};
+Lut4Cfg pick_lut4(int M, int N, int K);
+size_t lut4_max_k(int mt);  // largest K the LDS staging holds at mt rows
+hipError_t launch_gemv_lut4(const Lut4Args& a, const Lut4Cfg& c, hipStream_t s);
+
 // bit packing (layout: 0 plain, 1 device = tiled, see pack.hip)
 size_t packed_words(int bits, int layout, int rows, int cols);
 hipError_t launch_pack(int bits, int layout, int rows, int cols, const uint8_t* codes, uint32_t* packed,

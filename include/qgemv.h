@@ -76,6 +76,7 @@ typedef enum {
 #define QGEMV_GROUP 128
 #define QGEMV_LUT_BLOCK 64
 #define QGEMV_MAX_M 16
+#define QGEMV_LUT4_MAX_K 48000
 
 /* Library version (major*10000 + minor*100 + patch). */
 int qgemv_version(void);
@@ -159,6 +160,28 @@ int qgemv_w8a16(int M, int N, int K, const uint16_t *x, const uint32_t *wq,
 int qgemv_uniform(int bits, int path, int M, int N, int K, const uint16_t *x,
                   const uint32_t *wq, const uint16_t *scales, const uint32_t *zeros,
                   uint16_t *y, qgemv_stream_t stream);
+
+/* ------------------------------------------------------------------------
+ * LUT4: 4-bit codes with a 16-entry fp16 lookup table (NF4-style) and one
+ * fp16 scale per 64 consecutive k of a row (Fast NF4 Dequantization Kernels
+ * page: on-chip 16-level table, per-block scale):
+ *     w[n, k] = lut[q[n, k]] * absmax[n, k/64]
+ *
+ *   x      [dev] fp16   [M, K]
+ *   wq     [dev] uint32 4-bit codes in the device layout
+ *                       [qgemv_packed_words(4, QGEMV_LAYOUT_DEVICE, N, K)]
+ *   absmax [dev] fp16   [N, K/64]
+ *   lut    [dev] fp16   [16]; any values (the table is an input, not a format)
+ *   y      [dev] fp16   [M, N]
+ *
+ * Shapes as qgemv_uniform, plus K <= QGEMV_LUT4_MAX_K (the activation rows are
+ * staged on chip beside the table; QGEMV_ERR_SHAPE beyond).  x and wq 16-byte aligned,
+ * absmax, lut and y 2-byte aligned.  y must not overlap an input.  Asynchronous
+ * on `stream`, deterministic, no allocation.
+ * ------------------------------------------------------------------------ */
+int qgemv_lut4(int M, int N, int K, const uint16_t *x, const uint32_t *wq,
+               const uint16_t *absmax, const uint16_t *lut, uint16_t *y,
+               qgemv_stream_t stream);
 
 #ifdef __cplusplus
 }

@@ -91,3 +91,19 @@ def test_pack_validation_without_gpu(L):
     assert L.qgemv_pack(4, 1, 2, 8, v(FAKE), v(FAKE * 16), v(0)) == q.ERR_SHAPE       # device needs cols % 128
     assert L.qgemv_unpack(4, 1, 2, 128, v(FAKE), v(0), v(0)) == q.ERR_NULL
     assert L.qgemv_pack(4, 0, 2, 8, v(FAKE), v(FAKE + 4), v(0)) == q.ERR_VALUE  # overlap
+
+
+def _lut(L, M=1, N=64, K=256, x=FAKE, wq=FAKE * 2, a=FAKE * 3, lut=FAKE * 4, y=FAKE * 64):
+    v = ctypes.c_void_p
+    return L.qgemv_lut4(M, N, K, v(x), v(wq), v(a), v(lut), v(y), v(0))
+
+
+def test_lut4_validation_without_gpu(L):
+    assert _lut(L, lut=0) == q.ERR_NULL
+    assert _lut(L, a=0) == q.ERR_NULL
+    assert _lut(L, M=17) == q.ERR_SHAPE
+    assert _lut(L, K=192) == q.ERR_SHAPE        # the tiles are 128 wide
+    assert _lut(L, K=48128) == q.ERR_SHAPE      # beyond the on-chip activation staging
+    assert _lut(L, x=FAKE + 4) == q.ERR_ALIGN
+    assert _lut(L, a=FAKE * 3 + 1) == q.ERR_ALIGN
+    assert _lut(L, y=FAKE * 4) == q.ERR_VALUE    # y overlaps the table
