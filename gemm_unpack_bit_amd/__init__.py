@@ -39,6 +39,9 @@ _SIGS = {
     "qgemv_w8a16": (_i, [_i, _i, _i, _vp, _vp, _vp, _vp, _vp, _vp]),
     "qgemv_uniform": (_i, [_i, _i, _i, _i, _i, _vp, _vp, _vp, _vp, _vp, _vp]),
     "qgemv_lut4": (_i, [_i, _i, _i, _vp, _vp, _vp, _vp, _vp, _vp]),
+    "qgemv_outlier": (_i, [_i, _i, _i, _i, _vp, _vp, _vp, _vp, _vp, _vp, ctypes.c_int64, _vp, _vp]),
+    "qgemv_tilecoo_ptr_len": (_sz, [_i, _i]),
+    "qgemv_tilecoo_encode": (_i, [_i, _i, ctypes.c_int64, _vp, _vp, _vp, _vp, _vp]),
 }
 
 
@@ -192,4 +195,57 @@ def lut4(x, wq, absmax, lut, out=None):
         _need(out, torch.float16, "out")
     _check("qgemv_lut4", lib().qgemv_lut4(M, N, K, _ptr(x), _ptr(wq), _ptr(absmax), _ptr(lut), _ptr(out),
                                           _stream(x)))
+    return out
+
+
+def tilecoo_encode(N, K, rows, cols, vals):
+    """Host-side Tile-COO encoding of fp16 outliers (numpy in, numpy out).
+
+    rows, cols: integer coordinates; vals: fp16 values.  Returns (tile_ptr
+    uint32 [ceil(N/128) * ceil(K/128) + 1], tile_rec uint32 [nnz])."""
+    import numpy as np
+
+    rows = np.ascontiguousarray(rows, dtype=np.int32)
+    cols = np.ascontiguousarray(cols, dtype=np.int32)
+    vbits = np.ascontiguousarray(np.asarray(vals, dtype=np.float16).view(np.uint16))
+    nnz = rows.size
+    if cols.size != nnz or vbits.size != nnz:
+        raise ValueError("rows, cols and vals must have one entry per outlier")
+    n_ptr = int(lib().qgemv_tilecoo_ptr_len(N, K))
+    if n_ptr == 0:
+        raise ValueError("bad N or K")
+    ptr = np.zeros(n_ptr, dtype=np.uint32)
+    rec = np.zeros(max(nnz, 1), dtype=np.uint32)
+    p = lambda a: a.ctypes.data_as(ctypes.c_void_p)
+    _check("qgemv_tilecoo_encode", lib().qgemv_tilecoo_encode(N, K, nnz, p(rows), p(cols), p(vbits), p(ptr), p(rec)))
+    return ptr, rec[:nnz]
+
+
+def outlier(x, wq, scales, zeros, tile_ptr, tile_rec, path=PATH_AUTO, out=None):
+    """y = x . (W_dense + S)^T: the W4 uniform format plus fp16 Tile-COO outliers.
+
+    tile_ptr / tile_rec: device int32 (or uint32 viewed as int32) tensors from
+    tilecoo_encode.  Other arguments as uniform(..., bits=4)."""
+    torch = _torch()
+    _need(x, torch.float16, "x")
+    _need(wq, torch.int32, "wq")
+    _need(scales, torch.float16, "scales")
+    _need(zeros, torch.int32, "zeros")
+    _need(tile_ptr, torch.int32, "tile_ptr")
+    _need(tile_rec, torch.int32, "tile_rec")
+    M, K = x.shape
+    N = scales.shape[0]
+    need = packed_words(4, N, K)
+    if need and wq.numel() != need:
+        raise ValueError("wq does not hold N x K device-layout 4-bit codes")
+    if tile_ptr.numel() != int(lib().qgemv_tilecoo_ptr_len(N, K)):
+        raise ValueError("tile_ptr does not match N x K")
+    nnz = tile_rec.numel()
+    if out is None:
+        out = torch.empty((M, N), dtype=torch.float16, device=x.device)
+    else:
+        _need(out, torch.float16, "out")
+    rec_ptr = _ptr(tile_rec) if nnz else None
+    _check("qgemv_outlier", lib().qgemv_outlier(path, M, N, K, _ptr(x), _ptr(wq), _ptr(scales), _ptr(zeros),
+                                                _ptr(tile_ptr), rec_ptr, nnz, _ptr(out), _stream(x)))
     return out

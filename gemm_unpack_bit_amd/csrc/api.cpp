@@ -180,6 +180,33 @@ int qgemv_w8a16(int M, int N, int K, const uint16_t* x, const uint32_t* wq, cons
   return qgemv_uniform(8, QGEMV_PATH_AUTO, M, N, K, x, wq, scales, zeros, y, stream);
 }
 
+int qgemv_outlier(int path, int M, int N, int K, const uint16_t* x, const uint32_t* wq, const uint16_t* scales,
+                  const uint32_t* zeros, const uint32_t* tile_ptr, const uint32_t* tile_rec, int64_t nnz, uint16_t* y,
+                  qgemv_stream_t stream) {
+  if (!x || !wq || !scales || !zeros || !tile_ptr || !y || (nnz > 0 && !tile_rec)) return QGEMV_ERR_NULL;
+  if (path != QGEMV_PATH_AUTO && path != QGEMV_PATH_VALU && path != QGEMV_PATH_MFMA)
+    return QGEMV_ERR_UNSUPPORTED;
+  int rc = check_mnk(M, N, K, 4);
+  if (rc) return rc;
+  if (nnz < 0 || nnz > (int64_t)N * K || nnz * 4 >= (int64_t)1 << 31) return QGEMV_ERR_SHAPE;
+  if (!aligned16(x) || !aligned16(wq) || ((uintptr_t)scales & 1u) || ((uintptr_t)zeros & 3u) ||
+      ((uintptr_t)tile_ptr & 3u) || ((uintptr_t)tile_rec & 3u) || ((uintptr_t)y & 1u))
+    return QGEMV_ERR_ALIGN;
+  const size_t ybytes = (size_t)M * N * 2;
+  const int G = K / QGEMV_GROUP;
+  if (overlaps(y, ybytes, x, (size_t)M * K * 2) ||
+      overlaps(y, ybytes, wq, words(4, QGEMV_LAYOUT_DEVICE, N, K) * 4) ||
+      overlaps(y, ybytes, scales, (size_t)N * G * 2) ||
+      overlaps(y, ybytes, zeros, words(4, QGEMV_LAYOUT_PLAIN, N, G) * 4) ||
+      overlaps(y, ybytes, tile_ptr, qgemv_tilecoo_ptr_len(N, K) * 4) ||
+      (nnz > 0 && overlaps(y, ybytes, tile_rec, (size_t)nnz * 4)))
+    return QGEMV_ERR_VALUE;
+  qg::UniformArgs a{4, M, N, K, x, wq, scales, zeros, y, tile_ptr, tile_rec, (int)nnz};
+  if (path == QGEMV_PATH_AUTO) path = auto_path(4, M, N);
+  const bool mfma = path == QGEMV_PATH_MFMA;
+  return hip_status(qg::launch_gemv_outlier(a, qg::pick_outlier(M, N, K, mfma), reinterpret_cast<hipStream_t>(stream)));
+}
+
 int qgemv_lut4(int M, int N, int K, const uint16_t* x, const uint32_t* wq, const uint16_t* absmax,
                const uint16_t* lut, uint16_t* y, qgemv_stream_t stream) {
   if (!x || !wq || !absmax || !lut || !y) return QGEMV_ERR_NULL;

@@ -133,7 +133,9 @@ constexpr int max_threads(int ng) { return ng == 1 ? 1024 : 512; }
 // and every lane reads its 64-byte slice of a group from there.  The sixteen
 // lanes of a k-quarter share that slice, so loading it per lane through the
 // vector memory path would request 16x the bytes it uses.
-template <int BITS, bool MFMA, int MT, int NG, int D, int TPW, bool SAL, bool XLDS>
+// SP: also add the Tile-COO fp16 outliers of the workgroup's rows (outlier
+// variant): see sparse_prologue below.
+template <int BITS, bool MFMA, int MT, int NG, int D, int TPW, bool SAL, bool XLDS, bool SP>
 __global__ void __launch_bounds__(max_threads(NG)) __attribute__((amdgpu_waves_per_eu(waves_per_simd(NG))))
 gemv_tiles_kernel(UniformArgs a) {
   using TR = Uni<BITS>;
@@ -174,6 +176,29 @@ gemv_tiles_kernel(UniformArgs a) {
   const int XK = K + 32;
   float* red = XLDS ? smem + (size_t)MT * XK / 2 : smem;
   const u4* xs = reinterpret_cast<const u4*>(smem);
+
+  // outlier variant: LDS after the partials (see sparse_lds_bytes)
+  constexpr int MS = MFMA ? 16 : MT;  // batch rows a workgroup produces
+  constexpr int CH = MS == 1 ? 2048 : (MS == 2 ? 1024 : 256);  // records per staged chunk
+  constexpr int RW = 16 * TPW;        // weight rows of the workgroup
+  uint32_t* sptr = nullptr;  // [G + 1] tile_ptr of the workgroup's 128-row tile-row
+  uint32_t* srng = nullptr;  // [RW][G] (start | end << 16) of a row's records in a k-tile
+  float* spsum = nullptr;    // [MS][RW] sparse sums
+  uint32_t* recbuf = nullptr;  // [CH] staged records
+  float* prodbuf = nullptr;    // [MS][CH] products v * x
+  if constexpr (SP) {
+    const size_t redb = MFMA ? (size_t)WK * TPW * 64 * 16 : (size_t)WK * TPW * MT * 16 * 4;
+    char* b = reinterpret_cast<char*>(red) + redb;
+    sptr = reinterpret_cast<uint32_t*>(b);
+    b += ((size_t)(G + 1) * 4 + 15) / 16 * 16;
+    srng = reinterpret_cast<uint32_t*>(b);
+    b += (size_t)RW * G * 4;
+    spsum = reinterpret_cast<float*>(b);
+    b += (size_t)MS * RW * 4;
+    recbuf = reinterpret_cast<uint32_t*>(b);
+    b += (size_t)CH * 4;
+    prodbuf = reinterpret_cast<float*>(b);
+  }
 
   // activation row offsets of this lane (group 0, its k-quarter)
   uint32_t xoff[XR];
@@ -308,6 +333,93 @@ gemv_tiles_kernel(UniformArgs a) {
     }
     __syncthreads();
   };
+  // Outliers (FlashQuant abstract: fp16 sparse path fused with the low-bit
+  // dense one, sharing activations and outputs; Tile-COO records): the
+  // workgroup's rows lie in one 128-row tile-row of the Tile-COO encoding.
+  // Pass 1 marks, per row and k-tile, the run of that row's records (records
+  // are sorted by row inside a tile); pass 2 forms the exact products v * x
+  // and each output row sums its own in record order, so the result is
+  // deterministic.  Runs while the first weight stages are in flight.
+  auto sparse_prologue = [&]() {
+    if constexpr (SP) {
+      const int KT = G;
+      const uint32_t R = (uint32_t)rt0 / 8u;
+      const uint32_t lr0 = ((uint32_t)rt0 % 8u) * 16u;
+      const rsrc_t rp = make_rsrc(a.tile_ptr, ((uint32_t)((N + 127) / 128) * KT + 1u) * 4u);
+      const rsrc_t rr = make_rsrc(a.tile_rec, (uint32_t)a.nnz * 4u);
+      for (int i = threadIdx.x; i <= KT; i += blockDim.x) sptr[i] = bload4(rp, (R * KT + i) * 4u);
+      for (int i = threadIdx.x; i < RW * KT; i += blockDim.x) srng[i] = 0u;
+      for (int i = threadIdx.x; i < MS * RW; i += blockDim.x) spsum[i] = 0.f;
+      __syncthreads();
+      const uint32_t p0 = sptr[0], p1 = sptr[KT];
+      auto tile_of = [&](uint32_t i) {  // last k-tile whose records start at or before i
+        int lo = 0, hi = KT - 1;
+        while (lo < hi) {
+          const int mid = (lo + hi + 1) >> 1;
+          if (sptr[mid] <= i) lo = mid; else hi = mid - 1;
+        }
+        return lo;
+      };
+      for (uint32_t cs = p0; cs < p1; cs += CH) {  // pass 1
+        const uint32_t ce = min(p1, cs + (uint32_t)CH);
+        for (uint32_t i = cs + threadIdx.x; i < ce; i += blockDim.x) recbuf[i - cs] = bload4(rr, i * 4u);
+        __syncthreads();
+        for (uint32_t i = cs + threadIdx.x; i < ce; i += blockDim.x) {
+          const uint32_t rec = recbuf[i - cs];
+          const uint32_t lr = (rec >> 8) & 0xFFu;
+          if (lr - lr0 >= (uint32_t)RW) continue;  // another workgroup's row
+          const int kt = tile_of(i);
+          const uint32_t tb = sptr[kt], te = sptr[kt + 1];
+          uint16_t* rg = reinterpret_cast<uint16_t*>(srng) + 2 * ((lr - lr0) * KT + kt);
+          bool first = i == tb, last = i + 1 == te;
+          if (!first) {
+            const uint32_t pv = i - 1 >= cs ? recbuf[i - 1 - cs] : bload4(rr, (i - 1) * 4u);
+            first = ((pv >> 8) & 0xFFu) != lr;
+          }
+          if (!last) {
+            const uint32_t nx = i + 1 < ce ? recbuf[i + 1 - cs] : bload4(rr, (i + 1) * 4u);
+            last = ((nx >> 8) & 0xFFu) != lr;
+          }
+          if (first) rg[0] = (uint16_t)(i - tb);
+          if (last) rg[1] = (uint16_t)(i + 1 - tb);
+        }
+        __syncthreads();
+      }
+      for (uint32_t cs = p0; cs < p1; cs += CH) {  // pass 2
+        const uint32_t ce = min(p1, cs + (uint32_t)CH);
+        for (uint32_t i = cs + threadIdx.x; i < ce; i += blockDim.x) {
+          const uint32_t rec = bload4(rr, i * 4u);
+          const uint32_t lr = (rec >> 8) & 0xFFu;
+          if (lr - lr0 >= (uint32_t)RW) continue;
+          const uint32_t col = (uint32_t)tile_of(i) * 128u + (rec & 0xFFu);
+          const float v = h2f((uint16_t)(rec >> 16));
+#pragma unroll
+          for (int m = 0; m < MS; ++m) {
+            float xv;
+            if constexpr (XLDS) {
+              xv = (float)reinterpret_cast<const _Float16*>(smem)[(size_t)m * XK + col];
+            } else {
+              xv = m0 + m < M ? h2f(bload2(rx, ((uint32_t)(m0 + m) * K + col) * 2u)) : 0.f;
+            }
+            prodbuf[m * CH + (i - cs)] = v * xv;  // exact: a product of two fp16 values
+          }
+        }
+        __syncthreads();
+        for (int e = threadIdx.x; e < MS * RW; e += blockDim.x) {
+          const int m = e / RW, rl = e - m * RW;
+          float sum = spsum[e];
+          for (int kt = 0; kt < KT; ++kt) {
+            const uint32_t rg = srng[rl * KT + kt];
+            const uint32_t b = sptr[kt] + (rg & 0xFFFFu), en = sptr[kt] + (rg >> 16);
+            for (uint32_t i = max(b, cs); i < min(en, ce); ++i) sum += prodbuf[m * CH + (i - cs)];
+          }
+          spsum[e] = sum;
+        }
+        __syncthreads();
+      }
+    }
+  };
+
   if constexpr (XB == 1) {
     if (c < NC) {
 #pragma unroll
@@ -315,6 +427,7 @@ gemv_tiles_kernel(UniformArgs a) {
       load_x(c, 0);
     }
     if constexpr (XLDS) stage_x();
+    sparse_prologue();
     for (; c < NC; c += WK) {
 #pragma unroll
       for (int t = 0; t < TPW; ++t) {
@@ -338,6 +451,7 @@ gemv_tiles_kernel(UniformArgs a) {
       load_x(c, 0);
     }
     if constexpr (XLDS) stage_x();
+    sparse_prologue();
     for (; c < NC; c += 2 * WK) {
       load_stage(0, c + WK, ring[1]);
       load_x(c + WK, 1);
@@ -364,6 +478,7 @@ gemv_tiles_kernel(UniformArgs a) {
       float sum = 0.f;
       for (int w = 0; w < WK; ++w) sum += r4[(w * TPW + t) * 64 + l][i];
       const int row = (rt0 + t) * 16 + r;
+      if constexpr (SP) sum += spsum[m * RW + t * 16 + r];
       if (m < M && row < N) a.y[(size_t)m * N + row] = f2h(sum);
     }
   } else {
@@ -380,6 +495,7 @@ gemv_tiles_kernel(UniformArgs a) {
       float sum = 0.f;
       for (int w = 0; w < WK; ++w) sum += red[((w * TPW + t) * MT + m) * 16 + r];
       const int row = (rt0 + t) * 16 + r;
+      if constexpr (SP) sum += spsum[m * RW + t * 16 + r];
       if (m0 + m < M && row < N) a.y[(size_t)(m0 + m) * N + row] = f2h(sum);
     }
   }
@@ -394,7 +510,33 @@ size_t tiles_lds_bytes(bool mfma, int mt, int tpw, int wk) {
 constexpr size_t XLDS_MAX = 64 * 1024 + 128;
 size_t xlds_bytes(bool mfma, int mt, int K) { return mfma ? 0 : (size_t)mt * (K + 32) * 2; }
 
-template <int BITS, bool MFMA, int MT, int V, int TPW>
+// LDS of the outlier variant beyond the dense kernel's (mirrors the kernel's
+// layout: tile pointers, run table, sparse sums, record and product chunks)
+size_t sparse_lds_bytes(bool mfma, int mt, int tpw, int K) {
+  const size_t G = K / 128, ms = mfma ? 16 : mt, rw = 16 * tpw;
+  const size_t ch = ms == 1 ? 2048 : (ms == 2 ? 1024 : 256);
+  return (4 * (G + 1) + 15) / 16 * 16 + 4 * rw * G + 4 * ms * rw + 4 * ch + 4 * ch * ms;
+}
+
+constexpr size_t LDS_ALL = 160 * 1024;  // gfx950 LDS per workgroup
+
+template <int BITS, bool MFMA, int MT, int NG, int D, int TPW, bool SAL, bool XLDS, bool SP>
+hipError_t launch_k(const UniformArgs& a, dim3 grid, dim3 block, size_t lds, hipStream_t s) {
+  auto kern = &gemv_tiles_kernel<BITS, MFMA, MT, NG, D, TPW, SAL, XLDS, SP>;
+  if (lds > 64 * 1024) {
+    static bool raised = false;  // one-time opt-in above the default dynamic LDS limit
+    if (!raised) {
+      hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
+                                         hipFuncAttributeMaxDynamicSharedMemorySize, (int)LDS_ALL);
+      if (e != hipSuccess) return e;
+      raised = true;
+    }
+  }
+  hipLaunchKernelGGL(kern, grid, block, lds, s, a);
+  return hipGetLastError();
+}
+
+template <int BITS, bool MFMA, int MT, int V, int TPW, bool SP = false>
 hipError_t launch_t(const UniformArgs& a, const TileCfg& c, hipStream_t s) {
   constexpr int NG = chunk_groups(BITS, MFMA, MT, V);
   constexpr int D = ring_depth(V);
@@ -407,34 +549,17 @@ hipError_t launch_t(const UniformArgs& a, const TileCfg& c, hipStream_t s) {
     const size_t red = tiles_lds_bytes(MFMA, MT, TPW, c.wk);
     if (red > LDS_MAX || 64 * c.wk > max_threads(NG)) return hipErrorInvalidValue;
     const size_t xl = xlds_bytes(MFMA, MT, a.K);
-    const bool sal = (a.K / 128) % NG == 0;
-    if (!MFMA && xl <= XLDS_MAX) {
-      const size_t lds = xl + red;
-      if (lds > 64 * 1024) {
-        static bool raised = false;  // one-time opt-in above the default dynamic LDS limit
-        if (!raised) {
-          hipError_t e = hipFuncSetAttribute(
-              reinterpret_cast<const void*>(&gemv_tiles_kernel<BITS, MFMA, MT, NG, D, TPW, true, !MFMA>),
-              hipFuncAttributeMaxDynamicSharedMemorySize, (int)(XLDS_MAX + LDS_MAX));
-          if (e == hipSuccess)
-            e = hipFuncSetAttribute(
-                reinterpret_cast<const void*>(&gemv_tiles_kernel<BITS, MFMA, MT, NG, D, TPW, false, !MFMA>),
-                hipFuncAttributeMaxDynamicSharedMemorySize, (int)(XLDS_MAX + LDS_MAX));
-          if (e != hipSuccess) return e;
-          raised = true;
-        }
-      }
-      if (sal)
-        hipLaunchKernelGGL((gemv_tiles_kernel<BITS, MFMA, MT, NG, D, TPW, true, !MFMA>), grid, block, lds, s, a);
-      else
-        hipLaunchKernelGGL((gemv_tiles_kernel<BITS, MFMA, MT, NG, D, TPW, false, !MFMA>), grid, block, lds, s, a);
-    } else {
-      if (sal)
-        hipLaunchKernelGGL((gemv_tiles_kernel<BITS, MFMA, MT, NG, D, TPW, true, false>), grid, block, red, s, a);
-      else
-        hipLaunchKernelGGL((gemv_tiles_kernel<BITS, MFMA, MT, NG, D, TPW, false, false>), grid, block, red, s, a);
+    const bool xlds = !MFMA && xl <= XLDS_MAX;
+    const size_t lds = (xlds ? xl : 0) + red + (SP ? sparse_lds_bytes(MFMA, MT, TPW, a.K) : 0);
+    if (lds > LDS_ALL) return hipErrorInvalidValue;
+    // chunk scales in one load: whole chunks and a 2*NG-byte aligned base
+    const bool sal = (a.K / 128) % NG == 0 && reinterpret_cast<uintptr_t>(a.scales) % (2 * NG) == 0;
+    if (xlds) {
+      return sal ? launch_k<BITS, MFMA, MT, NG, D, TPW, true, !MFMA, SP>(a, grid, block, lds, s)
+                 : launch_k<BITS, MFMA, MT, NG, D, TPW, false, !MFMA, SP>(a, grid, block, lds, s);
     }
-    return hipGetLastError();
+    return sal ? launch_k<BITS, MFMA, MT, NG, D, TPW, true, false, SP>(a, grid, block, lds, s)
+               : launch_k<BITS, MFMA, MT, NG, D, TPW, false, false, SP>(a, grid, block, lds, s);
   }
 }
 
@@ -510,6 +635,36 @@ TileCfg pick_tiles(int bits, int M, int N, int K, bool mfma) {
   const int nc = (G + chunk_groups(bits, mfma, c.mt, c.v) - 1) / chunk_groups(bits, mfma, c.mt, c.v);
   if (c.wk > nc) c.wk = nc < 1 ? 1 : nc;
   return c;
+}
+
+// Outlier variant: the uniform W4 dense shapes, restricted to the one- and
+// two-tile-row forms (whose workgroups cover at most 32 rows of a 128-row
+// Tile-COO tile-row).
+TileCfg pick_outlier(int M, int N, int K, bool mfma) {
+  TileCfg c = pick_tiles(4, M, N, K, mfma);
+  if (c.tpw != 1) {
+    c.tpw = 2;
+    c.v = 0;
+    const int nc = (K / 128 + chunk_groups(4, mfma, c.mt, 0) - 1) / chunk_groups(4, mfma, c.mt, 0);
+    if (c.wk > nc) c.wk = nc;
+  }
+  return c;
+}
+
+hipError_t launch_gemv_outlier(const UniformArgs& a, const TileCfg& c, hipStream_t s) {
+  if (a.bits != 4 || c.wk < 1 || c.wk > 16) return hipErrorInvalidValue;
+  const int key = c.tpw * 10 + c.v;
+  if (c.mfma) {
+    if (key == 13) return launch_t<4, true, 1, 3, 1, true>(a, c, s);
+    if (key == 20) return launch_t<4, true, 1, 0, 2, true>(a, c, s);
+  } else if (c.mt == 1) {
+    if (key == 13) return launch_t<4, false, 1, 3, 1, true>(a, c, s);
+    if (key == 20) return launch_t<4, false, 1, 0, 2, true>(a, c, s);
+  } else if (c.mt == 2) {
+    if (key == 13) return launch_t<4, false, 2, 3, 1, true>(a, c, s);
+    if (key == 20) return launch_t<4, false, 2, 0, 2, true>(a, c, s);
+  }
+  return hipErrorInvalidValue;
 }
 
 hipError_t launch_gemv_tiles(const UniformArgs& a, const TileCfg& c, hipStream_t s) {

@@ -13,6 +13,10 @@ struct UniformArgs {
   const uint16_t* scales;
   const uint32_t* zeros;
   uint16_t* y;
+  // outlier variant only (nullptr / 0 otherwise): Tile-COO fp16 outliers
+  const uint32_t* tile_ptr;
+  const uint32_t* tile_rec;
+  int nnz;
 };
 
 // Launch shape of the tiled kernel: mfma selects the dot engine; mt = batch
@@ -29,6 +33,9 @@ struct TileCfg {
 
 TileCfg pick_tiles(int bits, int M, int N, int K, bool mfma);
 hipError_t launch_gemv_tiles(const UniformArgs& a, const TileCfg& c, hipStream_t s);
+// W4 dense + Tile-COO sparse in one kernel (tpw 1 with v 3, or tpw 2 with v 0)
+TileCfg pick_outlier(int M, int N, int K, bool mfma);
+hipError_t launch_gemv_outlier(const UniformArgs& a, const TileCfg& c, hipStream_t s);
 
 // 4-bit codes (tiled device layout) with a 16-entry fp16 table and fp16
 // per-64-block scales: y = x . (LUT[q] * absmax)^T

@@ -183,6 +183,46 @@ int qgemv_lut4(int M, int N, int K, const uint16_t *x, const uint32_t *wq,
                const uint16_t *absmax, const uint16_t *lut, uint16_t *y,
                qgemv_stream_t stream);
 
+/* ------------------------------------------------------------------------
+ * Outlier-aware W4A16 (FlashQuant abstract: a low-bit dense path and a
+ * high-precision sparse path sharing activations and outputs in one kernel,
+ * outliers in Tile-COO):
+ *     y = x . (W_dense + S)^T
+ * W_dense is the uniform 4-bit format of qgemv_w4a16 (its codes are used as
+ * given, also at outlier positions); S holds fp16 outliers at unique
+ * positions, encoded by qgemv_tilecoo_encode:
+ *
+ *   tile_ptr [dev] uint32 [qgemv_tilecoo_ptr_len(N, K)]: 128 x 128 tiles in
+ *                  row-tile-major order (tile (r/128) * ceil(K/128) + c/128),
+ *                  exclusive prefix sum of record counts; tile_ptr[last] = nnz
+ *   tile_rec [dev] uint32 [nnz]: (fp16 value bits << 16) | (row % 128) << 8 |
+ *                  (col % 128), sorted by (row, col) inside a tile; may be
+ *                  NULL when nnz == 0
+ *   nnz            number of records (0 <= nnz <= N*K, nnz*4 < 2^31)
+ *
+ * Other arguments, shapes and errors as qgemv_uniform (W4, `path` selects the
+ * dense engine); tile_ptr and tile_rec 4-byte aligned.  Records are read as
+ * given (their validity is the encoder's job).  Asynchronous, deterministic,
+ * no allocation.
+ * ------------------------------------------------------------------------ */
+int qgemv_outlier(int path, int M, int N, int K, const uint16_t *x, const uint32_t *wq,
+                  const uint16_t *scales, const uint32_t *zeros, const uint32_t *tile_ptr,
+                  const uint32_t *tile_rec, int64_t nnz, uint16_t *y, qgemv_stream_t stream);
+
+/* Entries of tile_ptr for an N x K weight: ceil(N/128) * ceil(K/128) + 1
+ * (0 on bad arguments). */
+size_t qgemv_tilecoo_ptr_len(int N, int K);
+
+/* Host-side Tile-COO encoder (offline prep; HOST pointers, synchronous).
+ *   rows, cols [host] int32 [nnz]: outlier coordinates, 0 <= row < N, 0 <= col < K
+ *   val_bits   [host] uint16 [nnz]: fp16 bit patterns of the values
+ *   tile_ptr   [host] uint32 [qgemv_tilecoo_ptr_len(N, K)]   (written)
+ *   tile_rec   [host] uint32 [nnz]                            (written)
+ * Returns QGEMV_ERR_VALUE for a coordinate out of range, a repeated position
+ * or an inf/NaN value, QGEMV_ERR_SHAPE for bad N, K or nnz. */
+int qgemv_tilecoo_encode(int N, int K, int64_t nnz, const int32_t *rows, const int32_t *cols,
+                         const uint16_t *val_bits, uint32_t *tile_ptr, uint32_t *tile_rec);
+
 #ifdef __cplusplus
 }
 #endif

@@ -1,0 +1,116 @@
+"""GPU parity of the fused outlier-aware W4A16 variant (dense uniform W4 +
+fp16 Tile-COO outliers in one kernel) against the float64 oracle."""
+import numpy as np
+import pytest
+
+import synth
+from oracle import reference as ref
+from tests.gpu_util import assert_within, dev, host, sample_rows, say, torch
+
+pytestmark = pytest.mark.gpu
+
+q = pytest.importorskip("gemm_unpack_bit_amd")
+PATHS = [q.PATH_AUTO, q.PATH_VALU, q.PATH_MFMA]
+
+
+def _upload(c, N, K):
+    wq = q.pack(dev(c["codes"]), 4)
+    zq = q.pack_zeros(dev(c["zeros"]), 4)
+    ptr, rec = q.tilecoo_encode(N, K, c["o_rows"], c["o_cols"], c["o_vals"])
+    return wq, dev(c["scales"]), zq, dev(ptr.view(np.int32)), dev(rec.view(np.int32))
+
+
+@pytest.mark.parametrize("path", PATHS)
+@pytest.mark.parametrize("N,K,frac", [(16, 128, 0.05), (100, 384, 0.02), (256, 1024, 0.01), (300, 2176, 0.005),
+                                      (1000, 640, 0.01)])
+@pytest.mark.parametrize("M", [1, 2, 5, 16])
+def test_outlier_small_shapes(path, N, K, frac, M):
+    say("outlier", path, N, K, frac, M)
+    c = synth.outlier_case(N * 3 + K, M, N, K, frac=frac)
+    wq, s, zq, tp, tr = _upload(c, N, K)
+    y = host(q.outlier(dev(c["x"]), wq, s, zq, tp, tr, path))
+    y_ref, A = ref.gemv_outlier(c["x"], c["codes"], c["scales"], c["zeros"], c["o_rows"], c["o_cols"], c["o_vals"])
+    assert_within(y, y_ref, A, f"outlier M={M} N={N} K={K} path={path}")
+
+
+@pytest.mark.parametrize("path", [q.PATH_VALU, q.PATH_MFMA])
+def test_no_outliers_equals_dense_bitwise(path):
+    """nnz = 0: the same dense kernel path, so y equals qgemv_uniform bit for bit."""
+    say("outlier nnz=0", path)
+    N, K, M = 4096, 4096, 1 if path == q.PATH_VALU else 4
+    c = synth.uniform_case(3, M, N, K, 4)
+    wq = q.pack(dev(c["codes"]), 4)
+    zq = q.pack_zeros(dev(c["zeros"]), 4)
+    s, x = dev(c["scales"]), dev(c["x"])
+    ptr, rec = q.tilecoo_encode(N, K, [], [], [])
+    t = torch()
+    y = host(q.outlier(x, wq, s, zq, dev(ptr.view(np.int32)), t.zeros(0, dtype=t.int32, device="cuda"), path))
+    yd = host(q.uniform(x, wq, s, zq, 4, path))
+    assert np.array_equal(y.view(np.uint16), yd.view(np.uint16))
+
+
+def test_zero_scales_give_pure_sparse_product():
+    """s = 0: the dense part vanishes and y = S x exactly up to fp32 summation."""
+    say("outlier spmv")
+    N, K = 384, 1024
+    c = synth.outlier_case(11, 2, N, K, frac=0.02)
+    c["scales"][:] = 0
+    wq, s, zq, tp, tr = _upload(c, N, K)
+    y = host(q.outlier(dev(c["x"]), wq, s, zq, tp, tr))
+    ys, As = ref.sparse_part(c["x"], N, c["o_rows"], c["o_cols"], c["o_vals"])
+    assert_within(y, ys, As, "outlier pure sparse")
+
+
+def test_single_outlier_one_hot_exact():
+    """One outlier at (r, k) and x = e_k: y[r] = fp16(s (q - z) + v) exactly here
+    (both terms are exact in fp32 and their sum is exact for these values)."""
+    say("outlier one-hot")
+    N, K = 256, 512
+    c = synth.uniform_case(5, 1, N, K, 4)
+    r, k = 37, 300
+    c["o_rows"], c["o_cols"] = np.array([r]), np.array([k])
+    c["o_vals"] = np.array([0.5], dtype=np.float16)
+    c["scales"][:] = np.float16(0.015625)
+    wq, s, zq, tp, tr = _upload(c, N, K)
+    x = np.zeros((1, K), dtype=np.float16)
+    x[0, k] = 2.0
+    y = host(q.outlier(dev(x), wq, s, zq, tp, tr))
+    y_ref, _ = ref.gemv_outlier(x, c["codes"], c["scales"], c["zeros"], c["o_rows"], c["o_cols"], c["o_vals"])
+    assert np.array_equal(y.view(np.uint16), synth.f16(y_ref).view(np.uint16))
+
+
+def test_outlier_deterministic():
+    say("outlier determinism")
+    N, K = 4096, 4096
+    c = synth.outlier_case(21, 1, N, K)
+    wq, s, zq, tp, tr = _upload(c, N, K)
+    x = dev(c["x"])
+    y1 = host(q.outlier(x, wq, s, zq, tp, tr))
+    y2 = host(q.outlier(x, wq, s, zq, tp, tr))
+    assert np.array_equal(y1.view(np.uint16), y2.view(np.uint16))
+
+
+@pytest.mark.parametrize("M", [1, 4, 16])
+def test_outlier_4096_config(M):
+    """The 4096 x 4096 workload: 0.5% unique outliers ~ N(0, 0.2), every row checked."""
+    say("outlier 4096", M)
+    N = K = 4096
+    c = synth.outlier_case(synth.seed_for(4, 0), M, N, K)
+    wq, s, zq, tp, tr = _upload(c, N, K)
+    y = host(q.outlier(dev(c["x"]), wq, s, zq, tp, tr))
+    y_ref, A = ref.gemv_outlier(c["x"], c["codes"], c["scales"], c["zeros"], c["o_rows"], c["o_cols"], c["o_vals"])
+    assert_within(y, y_ref, A, f"outlier 4096 M={M}")
+
+
+def test_outlier_dense_tiles():
+    """Many outliers in one tile (a tile run longer than a staged chunk)."""
+    say("outlier dense tile")
+    N, K = 128, 256
+    c = synth.uniform_case(8, 1, N, K, 4)
+    rr, cc = np.meshgrid(np.arange(128), np.arange(128), indexing="ij")
+    c["o_rows"], c["o_cols"] = rr.ravel(), cc.ravel() + 128
+    c["o_vals"] = synth.f16(synth.normal(8, synth.S_OVAL, 128 * 128, 0.2))
+    wq, s, zq, tp, tr = _upload(c, N, K)
+    y = host(q.outlier(dev(c["x"]), wq, s, zq, tp, tr))
+    y_ref, A = ref.gemv_outlier(c["x"], c["codes"], c["scales"], c["zeros"], c["o_rows"], c["o_cols"], c["o_vals"])
+    assert_within(y, y_ref, A, "outlier dense tile")
