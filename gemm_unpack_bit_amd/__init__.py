@@ -41,6 +41,8 @@ _SIGS = {
     "qgemv_lut4": (_i, [_i, _i, _i, _vp, _vp, _vp, _vp, _vp, _vp]),
     "qgemv_outlier": (_i, [_i, _i, _i, _i, _vp, _vp, _vp, _vp, _vp, _vp, ctypes.c_int64, _vp, _vp]),
     "qgemv_tilecoo_ptr_len": (_sz, [_i, _i]),
+    "qgemv_codebook": (_i, [_i, _i, _i, _vp, _vp, _vp, _vp, _vp, _vp, _sz, _vp]),
+    "qgemv_codebook_workspace_bytes": (_sz, [_i, _i, _i]),
     "qgemv_tilecoo_encode": (_i, [_i, _i, ctypes.c_int64, _vp, _vp, _vp, _vp, _vp]),
 }
 
@@ -248,4 +250,42 @@ def outlier(x, wq, scales, zeros, tile_ptr, tile_rec, path=PATH_AUTO, out=None):
     rec_ptr = _ptr(tile_rec) if nnz else None
     _check("qgemv_outlier", lib().qgemv_outlier(path, M, N, K, _ptr(x), _ptr(wq), _ptr(scales), _ptr(zeros),
                                                 _ptr(tile_ptr), rec_ptr, nnz, _ptr(out), _stream(x)))
+    return out
+
+
+def codebook_workspace_bytes(M, N, K):
+    return int(lib().qgemv_codebook_workspace_bytes(M, N, K))
+
+
+def codebook(x, codes, cb, scales, ws=None, out=None):
+    """y = x . dequant(codes)^T for a 256 x 4 fp16 codebook (8-bit codes, one
+    per 4 consecutive k) with one fp16 scale per 128 k.
+
+    codes: int32 words of the [N, K/4] uint8 code matrix packed with
+    pack(codes, 8) (device layout); cb [256, 4] fp16; scales [N, K/128] fp16;
+    ws: optional zero-filled workspace (uint8/int32 tensor) of
+    codebook_workspace_bytes(M, N, K) bytes, reused across calls."""
+    torch = _torch()
+    _need(x, torch.float16, "x")
+    _need(codes, torch.int32, "codes")
+    _need(cb, torch.float16, "codebook")
+    _need(scales, torch.float16, "scales")
+    M, K = x.shape
+    N = scales.shape[0]
+    need = packed_words(8, N, K // 4) if K % 512 == 0 else 0
+    if need and codes.numel() != need:
+        raise ValueError("codes do not hold the N x K/4 device-layout code matrix")
+    if cb.numel() != 1024:
+        raise ValueError("codebook must be 256 x 4")
+    if out is None:
+        out = torch.empty((M, N), dtype=torch.float16, device=x.device)
+    else:
+        _need(out, torch.float16, "out")
+    ws_ptr, ws_bytes = (None, 0)
+    if ws is not None:
+        if not ws.is_cuda or not ws.is_contiguous():
+            raise ValueError("ws must be a contiguous CUDA tensor")
+        ws_ptr, ws_bytes = _ptr(ws), ws.numel() * ws.element_size()
+    _check("qgemv_codebook", lib().qgemv_codebook(M, N, K, _ptr(x), _ptr(codes), _ptr(cb), _ptr(scales), _ptr(out),
+                                                  ws_ptr, ws_bytes, _stream(x)))
     return out

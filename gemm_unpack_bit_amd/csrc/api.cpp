@@ -207,6 +207,44 @@ int qgemv_outlier(int path, int M, int N, int K, const uint16_t* x, const uint32
   return hip_status(qg::launch_gemv_outlier(a, qg::pick_outlier(M, N, K, mfma), reinterpret_cast<hipStream_t>(stream)));
 }
 
+size_t qgemv_codebook_workspace_bytes(int M, int N, int K) {
+  if (M < 1 || M > QGEMV_MAX_M || N < 1 || K < 512 || K % 512) return 0;
+  return qg::codebook_ws_bytes(qg::pick_codebook(M, N, K), M, N);
+}
+
+int qgemv_codebook(int M, int N, int K, const uint16_t* x, const uint32_t* codes, const uint16_t* codebook,
+                   const uint16_t* scales, uint16_t* y, void* ws, size_t ws_bytes, qgemv_stream_t stream) {
+  if (!x || !codes || !codebook || !scales || !y) return QGEMV_ERR_NULL;
+  if (M < 1 || M > QGEMV_MAX_M || N < 1 || K < 512 || K % 512) return QGEMV_ERR_SHAPE;
+  const long lim = 1L << 31;
+  if ((long)((N + 15) / 16) * 16 * (K / 4) >= lim || (long)M * K * 2 >= lim || (long)M * N * 2 >= lim)
+    return QGEMV_ERR_SHAPE;
+  if (!aligned16(x) || !aligned16(codes) || ((uintptr_t)codebook & 3u) || ((uintptr_t)scales & 1u) ||
+      ((uintptr_t)y & 1u) || ((uintptr_t)ws & 3u))
+    return QGEMV_ERR_ALIGN;
+  const size_t ybytes = (size_t)M * N * 2;
+  if (overlaps(y, ybytes, x, (size_t)M * K * 2) ||
+      overlaps(y, ybytes, codes, words(8, QGEMV_LAYOUT_DEVICE, N, K / 4) * 4) ||
+      overlaps(y, ybytes, codebook, 256 * 4 * 2) || overlaps(y, ybytes, scales, (size_t)N * (K / 128) * 2) ||
+      (ws && overlaps(y, ybytes, ws, ws_bytes)))
+    return QGEMV_ERR_VALUE;
+  qg::CodebookCfg c = qg::pick_codebook(M, N, K);
+  if (const char* e = std::getenv("QGEMV_CODEBOOK_CFG")) {  // tuning override "tpw,wk,ks"
+    int tpw, wk, ks;
+    if (std::sscanf(e, "%d,%d,%d", &tpw, &wk, &ks) == 3) {
+      c.tpw = tpw;
+      c.wk = wk;
+      c.ks = ks;
+    }
+  }
+  const size_t need = qg::codebook_ws_bytes(c, M, N);
+  if (need > 0 && (!ws || ws_bytes < need)) c.ks = 1;  // no room to split K: one pass per row block
+  float* wsf = reinterpret_cast<float*>(ws);
+  uint32_t* cnt = c.ks > 1 ? reinterpret_cast<uint32_t*>(wsf + (size_t)c.ks * M * N) : nullptr;
+  qg::CodebookArgs a{M, N, K, x, codes, codebook, scales, y, c.ks > 1 ? wsf : nullptr, cnt};
+  return hip_status(qg::launch_gemv_codebook(a, c, reinterpret_cast<hipStream_t>(stream)));
+}
+
 int qgemv_lut4(int M, int N, int K, const uint16_t* x, const uint32_t* wq, const uint16_t* absmax,
                const uint16_t* lut, uint16_t* y, qgemv_stream_t stream) {
   if (!x || !wq || !absmax || !lut || !y) return QGEMV_ERR_NULL;

@@ -56,6 +56,27 @@ Lut4Cfg pick_lut4(int M, int N, int K);
 size_t lut4_max_k(int mt);  // largest K the LDS staging holds at mt rows
 hipError_t launch_gemv_lut4(const Lut4Args& a, const Lut4Cfg& c, hipStream_t s);
 
+// Codebook (m = 1, v = 4, b = 8, g = 128) with a Psumbook: codes [N, K/4]
+// uint8 in the tiled 8-bit device layout, codebook fp16 [256][4], scales fp16
+// [N, K/128]; ws/cnt: the K-split workspace (partials, then counters)
+struct CodebookArgs {
+  int M, N, K;
+  const uint16_t* x;
+  const uint32_t* codes;
+  const uint16_t* codebook;
+  const uint16_t* scales;
+  uint16_t* y;
+  float* ws;
+  uint32_t* cnt;
+};
+// tpw = row-tiles per wave (1, 2, 4), wk = waves (1..16), ks = K splits
+struct CodebookCfg {
+  int tpw, wk, ks;
+};
+CodebookCfg pick_codebook(int M, int N, int K);
+size_t codebook_ws_bytes(const CodebookCfg& c, int M, int N);
+hipError_t launch_gemv_codebook(const CodebookArgs& a, const CodebookCfg& c, hipStream_t s);
+
 // bit packing (layout: 0 plain, 1 device = tiled, see pack.hip)
 size_t packed_words(int bits, int layout, int rows, int cols);
 hipError_t launch_pack(int bits, int layout, int rows, int cols, const uint8_t* codes, uint32_t* packed,

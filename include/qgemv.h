@@ -209,6 +209,39 @@ int qgemv_outlier(int path, int M, int N, int K, const uint16_t *x, const uint32
                   const uint16_t *scales, const uint32_t *zeros, const uint32_t *tile_ptr,
                   const uint32_t *tile_rec, int64_t nnz, uint16_t *y, qgemv_stream_t stream);
 
+/* ------------------------------------------------------------------------
+ * Codebook GEMV with a Psumbook (CodeGEMM paper notes: m = 1 codebook of 256
+ * centroids of v = 4 dims, b = 8-bit codes, one scale per g = 128 k):
+ *     w[n, 4j + t] = scales[n, (4j + t)/128] * codebook[codes[n, j]][t]
+ * computed by building, per 512-k range, the partial sums of every centroid
+ * with every 4-wide activation segment on chip and accumulating by lookup.
+ *
+ *   x        [dev] fp16   [M, K]
+ *   codes    [dev] uint32 the [N, K/4] uint8 code matrix packed with
+ *                         qgemv_pack(8, QGEMV_LAYOUT_DEVICE, N, K/4, ...)
+ *   codebook [dev] fp16   [256][4]
+ *   scales   [dev] fp16   [N, K/128]
+ *   y        [dev] fp16   [M, N]
+ *   ws       [dev] optional workspace of qgemv_codebook_workspace_bytes(M, N, K)
+ *                  bytes, ZERO-FILLED before its first use (every call leaves it
+ *                  zero-filled again).  With it the library splits K across
+ *                  workgroups and adds the parts in a fixed order; with NULL or
+ *                  a smaller ws it runs one pass per row block (same result
+ *                  within the tolerance, usually slower).  Calls that share a
+ *                  workspace must not overlap in time.
+ *
+ * Shapes: 1 <= M <= 16, N >= 1, K a positive multiple of 512 (QGEMV_ERR_SHAPE).
+ * x, codes 16-byte aligned, codebook and ws 4-byte, scales and y 2-byte
+ * (QGEMV_ERR_ALIGN).  y must not overlap an input or ws (QGEMV_ERR_VALUE).
+ * Asynchronous, deterministic for a given workspace size.
+ * ------------------------------------------------------------------------ */
+int qgemv_codebook(int M, int N, int K, const uint16_t *x, const uint32_t *codes,
+                   const uint16_t *codebook, const uint16_t *scales, uint16_t *y, void *ws,
+                   size_t ws_bytes, qgemv_stream_t stream);
+/* Workspace bytes qgemv_codebook uses to split K for this shape (0 if it
+ * never splits, or on bad arguments). */
+size_t qgemv_codebook_workspace_bytes(int M, int N, int K);
+
 /* Entries of tile_ptr for an N x K weight: ceil(N/128) * ceil(K/128) + 1
  * (0 on bad arguments). */
 size_t qgemv_tilecoo_ptr_len(int N, int K);

@@ -107,3 +107,20 @@ def test_lut4_validation_without_gpu(L):
     assert _lut(L, x=FAKE + 4) == q.ERR_ALIGN
     assert _lut(L, a=FAKE * 3 + 1) == q.ERR_ALIGN
     assert _lut(L, y=FAKE * 4) == q.ERR_VALUE    # y overlaps the table
+
+
+def _cb(L, M=1, N=64, K=512, x=FAKE, codes=FAKE * 2, cbk=FAKE * 3, s=FAKE * 4, y=FAKE * 64, ws=0, wsb=0):
+    v = ctypes.c_void_p
+    return L.qgemv_codebook(M, N, K, v(x), v(codes), v(cbk), v(s), v(y), v(ws), wsb, v(0))
+
+
+def test_codebook_validation_without_gpu(L):
+    assert _cb(L, codes=0) == q.ERR_NULL
+    assert _cb(L, K=384) == q.ERR_SHAPE          # K must be a multiple of 512
+    assert _cb(L, M=0) == q.ERR_SHAPE
+    assert _cb(L, x=FAKE + 8) == q.ERR_ALIGN
+    assert _cb(L, cbk=FAKE * 3 + 2) == q.ERR_ALIGN
+    assert _cb(L, y=FAKE * 3) == q.ERR_VALUE      # y overlaps the codebook
+    assert L.qgemv_codebook_workspace_bytes(1, 64, 384) == 0
+    n = L.qgemv_codebook_workspace_bytes(1, 57344, 8192)
+    assert n >= 4 * 57344                          # K split: at least one fp32 partial per row

@@ -1,0 +1,78 @@
+"""GPU parity of the codebook (Psumbook) variant against the float64 oracle:
+m = 1 codebook of 256 centroids x 4 dims, 8-bit codes, one scale per 128 k."""
+import numpy as np
+import pytest
+
+import synth
+from oracle import reference as ref
+from tests.gpu_util import assert_within, dev, host, sample_rows, say, torch
+
+pytestmark = pytest.mark.gpu
+
+q = pytest.importorskip("gemm_unpack_bit_amd")
+
+
+def _upload(c):
+    return q.pack(dev(c["codes"]), 8), dev(c["codebook"]), dev(c["scales"])
+
+
+def _ws(M, N, K):
+    t = torch()
+    n = q.codebook_workspace_bytes(M, N, K)
+    return t.zeros(max(n, 4), dtype=t.uint8, device="cuda") if n else None
+
+
+@pytest.mark.parametrize("use_ws", [False, True])
+@pytest.mark.parametrize("N,K", [(16, 512), (100, 1024), (300, 2048), (70, 1536), (1000, 4096)])
+@pytest.mark.parametrize("M", [1, 2, 4, 16])
+def test_codebook_small_shapes(use_ws, N, K, M):
+    say("codebook", use_ws, N, K, M)
+    c = synth.codebook_case(N * 5 + K, M, N, K)
+    codes, cb, s = _upload(c)
+    y = host(q.codebook(dev(c["x"]), codes, cb, s, ws=_ws(M, N, K) if use_ws else None))
+    y_ref, A = ref.gemv_codebook(c["x"], c["codes"], c["codebook"], c["scales"])
+    assert_within(y, y_ref, A, f"codebook M={M} N={N} K={K} ws={use_ws}")
+
+
+def test_codebook_one_hot_is_exact():
+    """x = e_k: y[n] = fp16(s * C[code][k % 4]) exactly."""
+    say("codebook one-hot")
+    N, K = 64, 1024
+    c = synth.codebook_case(3, 1, N, K)
+    codes, cb, s = _upload(c)
+    w = ref.dequant_codebook(c["codes"], c["codebook"], c["scales"])
+    for k in (0, 1, 2, 3, 127, 128, 515, 1023):
+        x = np.zeros((1, K), dtype=np.float16)
+        x[0, k] = 1.0
+        y = host(q.codebook(dev(x), codes, cb, s))
+        assert np.array_equal(y[0].view(np.uint16), synth.f16(w[:, k]).view(np.uint16)), k
+
+
+def test_codebook_deterministic_and_workspace_reusable():
+    say("codebook determinism")
+    M, N, K = 1, 8192, 8192
+    c = synth.codebook_case(7, M, N, K)
+    codes, cb, s = _upload(c)
+    x = dev(c["x"])
+    ws = _ws(M, N, K)
+    y1 = host(q.codebook(x, codes, cb, s, ws=ws))
+    y2 = host(q.codebook(x, codes, cb, s, ws=ws))
+    assert np.array_equal(y1.view(np.uint16), y2.view(np.uint16))
+    rows = sample_rows(N)
+    y_ref, A = ref.gemv_codebook(c["x"], c["codes"], c["codebook"], c["scales"], rows=rows)
+    assert_within(y1[:, rows], y_ref, A, "codebook 8192 ws reuse")
+
+
+@pytest.mark.parametrize("idx", range(4))
+def test_codebook_70b_layers(idx):
+    name, (N, K) = list(synth.LLAMA_70B_LAYERS.items())[idx]
+    say("codebook full", name, N, K)
+    c = synth.codebook_case(synth.seed_for(5, idx), 4, N, K)
+    codes, cb, s = _upload(c)
+    rows = sample_rows(N)
+    for M in (1, 4):
+        x = c["x"][:M]
+        y = host(q.codebook(dev(x), codes, cb, s, ws=_ws(M, N, K)))
+        y_ref, A = ref.gemv_codebook(x, c["codes"], c["codebook"], c["scales"], rows=rows)
+        assert_within(y[:, rows], y_ref, A, f"codebook {name} M={M}")
+        assert np.isfinite(y.astype(np.float32)).all()
