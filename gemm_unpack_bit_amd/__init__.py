@@ -16,7 +16,7 @@ LIB_PATH = os.path.join(_PKG, "libqgemv.so")
 
 OK, ERR_NULL, ERR_SHAPE, ERR_ALIGN, ERR_UNSUPPORTED, ERR_WORKSPACE, ERR_VALUE, ERR_HIP = range(8)
 PATH_AUTO, PATH_VALU, PATH_MFMA = 0, 1, 2
-LAYOUT_PLAIN, LAYOUT_DEVICE = 0, 1
+LAYOUT_PLAIN, LAYOUT_DEVICE, LAYOUT_ROWS64 = 0, 1, 2
 GROUP = 128
 
 _lib = None
@@ -262,7 +262,7 @@ def codebook(x, codes, cb, scales, ws=None, out=None):
     per 4 consecutive k) with one fp16 scale per 128 k.
 
     codes: int32 words of the [N, K/4] uint8 code matrix packed with
-    pack(codes, 8) (device layout); cb [256, 4] fp16; scales [N, K/128] fp16;
+    pack(codes, 8, LAYOUT_ROWS64); cb [256, 4] fp16; scales [N, K/128] fp16;
     ws: optional zero-filled workspace (uint8/int32 tensor) of
     codebook_workspace_bytes(M, N, K) bytes, reused across calls."""
     torch = _torch()
@@ -272,9 +272,9 @@ def codebook(x, codes, cb, scales, ws=None, out=None):
     _need(scales, torch.float16, "scales")
     M, K = x.shape
     N = scales.shape[0]
-    need = packed_words(8, N, K // 4) if K % 512 == 0 else 0
+    need = packed_words(8, N, K // 4, LAYOUT_ROWS64) if K % 512 == 0 else 0
     if need and codes.numel() != need:
-        raise ValueError("codes do not hold the N x K/4 device-layout code matrix")
+        raise ValueError("codes do not hold the N x K/4 code matrix in the 64-row layout")
     if cb.numel() != 1024:
         raise ValueError("codebook must be 256 x 4")
     if out is None:

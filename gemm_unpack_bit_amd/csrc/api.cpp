@@ -111,14 +111,15 @@ int qgemv_last_hip_error(void) { return g_last_hip_error; }
 size_t qgemv_packed_words(int bits, int layout, int rows, int cols) {
   if (!valid_bits(bits) || rows < 0 || cols < 0) return 0;
   if (layout == QGEMV_LAYOUT_DEVICE && cols % QGEMV_GROUP) return 0;
-  if (layout != QGEMV_LAYOUT_PLAIN && layout != QGEMV_LAYOUT_DEVICE) return 0;
+  if (layout != QGEMV_LAYOUT_PLAIN && layout != QGEMV_LAYOUT_DEVICE && layout != QGEMV_LAYOUT_ROWS64) return 0;
   return words(bits, layout, rows, cols);
 }
 
 int qgemv_pack(int bits, int layout, int rows, int cols, const uint8_t* codes, uint32_t* packed,
                qgemv_stream_t stream) {
   if (!codes || !packed) return QGEMV_ERR_NULL;
-  if (!valid_bits(bits) || (layout != QGEMV_LAYOUT_PLAIN && layout != QGEMV_LAYOUT_DEVICE))
+  if (!valid_bits(bits) || (layout != QGEMV_LAYOUT_PLAIN && layout != QGEMV_LAYOUT_DEVICE &&
+                            !(layout == QGEMV_LAYOUT_ROWS64 && bits == 8)))
     return QGEMV_ERR_UNSUPPORTED;
   if (rows < 0 || cols < 0 || (layout == QGEMV_LAYOUT_DEVICE && cols % QGEMV_GROUP)) return QGEMV_ERR_SHAPE;
   if (overlaps(codes, (size_t)rows * cols, packed, words(bits, layout, rows, cols) * 4)) return QGEMV_ERR_VALUE;
@@ -134,7 +135,8 @@ int qgemv_pack(int bits, int layout, int rows, int cols, const uint8_t* codes, u
 int qgemv_unpack(int bits, int layout, int rows, int cols, const uint32_t* packed, uint8_t* codes,
                  qgemv_stream_t stream) {
   if (!codes || !packed) return QGEMV_ERR_NULL;
-  if (!valid_bits(bits) || (layout != QGEMV_LAYOUT_PLAIN && layout != QGEMV_LAYOUT_DEVICE))
+  if (!valid_bits(bits) || (layout != QGEMV_LAYOUT_PLAIN && layout != QGEMV_LAYOUT_DEVICE &&
+                            !(layout == QGEMV_LAYOUT_ROWS64 && bits == 8)))
     return QGEMV_ERR_UNSUPPORTED;
   if (rows < 0 || cols < 0 || (layout == QGEMV_LAYOUT_DEVICE && cols % QGEMV_GROUP)) return QGEMV_ERR_SHAPE;
   if (overlaps(codes, (size_t)rows * cols, packed, words(bits, layout, rows, cols) * 4)) return QGEMV_ERR_VALUE;
@@ -217,30 +219,34 @@ int qgemv_codebook(int M, int N, int K, const uint16_t* x, const uint32_t* codes
   if (!x || !codes || !codebook || !scales || !y) return QGEMV_ERR_NULL;
   if (M < 1 || M > QGEMV_MAX_M || N < 1 || K < 512 || K % 512) return QGEMV_ERR_SHAPE;
   const long lim = 1L << 31;
-  if ((long)((N + 15) / 16) * 16 * (K / 4) >= lim || (long)M * K * 2 >= lim || (long)M * N * 2 >= lim)
+  if ((long)((N + 63) / 64) * 64 * (K / 4) >= lim || (long)M * K * 2 >= lim || (long)M * N * 2 >= lim)
     return QGEMV_ERR_SHAPE;
   if (!aligned16(x) || !aligned16(codes) || ((uintptr_t)codebook & 3u) || ((uintptr_t)scales & 1u) ||
       ((uintptr_t)y & 1u) || ((uintptr_t)ws & 3u))
     return QGEMV_ERR_ALIGN;
   const size_t ybytes = (size_t)M * N * 2;
   if (overlaps(y, ybytes, x, (size_t)M * K * 2) ||
-      overlaps(y, ybytes, codes, words(8, QGEMV_LAYOUT_DEVICE, N, K / 4) * 4) ||
+      overlaps(y, ybytes, codes, words(8, QGEMV_LAYOUT_ROWS64, N, K / 4) * 4) ||
       overlaps(y, ybytes, codebook, 256 * 4 * 2) || overlaps(y, ybytes, scales, (size_t)N * (K / 128) * 2) ||
       (ws && overlaps(y, ybytes, ws, ws_bytes)))
     return QGEMV_ERR_VALUE;
   qg::CodebookCfg c = qg::pick_codebook(M, N, K);
-  if (const char* e = std::getenv("QGEMV_CODEBOOK_CFG")) {  // tuning override "tpw,wk,ks"
-    int tpw, wk, ks;
-    if (std::sscanf(e, "%d,%d,%d", &tpw, &wk, &ks) == 3) {
-      c.tpw = tpw;
+  if (const char* e = std::getenv("QGEMV_CODEBOOK_CFG")) {  // tuning override "wk,ks"
+    int wk, ks;
+    if (std::sscanf(e, "%d,%d", &wk, &ks) == 2) {
       c.wk = wk;
       c.ks = ks;
     }
   }
   const size_t need = qg::codebook_ws_bytes(c, M, N);
-  if (need > 0 && (!ws || ws_bytes < need)) c.ks = 1;  // no room to split K: one pass per row block
+  // no room to split K (or more counters than the area holds): one pass per row block
+  if (need > 0 && (!ws || ws_bytes < need || (size_t)M * qg::codebook_row_blocks(c, N) > qg::CB_COUNTERS))
+    c.ks = 1;
   float* wsf = reinterpret_cast<float*>(ws);
-  uint32_t* cnt = c.ks > 1 ? reinterpret_cast<uint32_t*>(wsf + (size_t)c.ks * M * N) : nullptr;
+  // counters: the last CB_COUNTERS words of the caller's buffer
+  uint32_t* cnt = c.ks > 1 ? reinterpret_cast<uint32_t*>(reinterpret_cast<char*>(ws) + (ws_bytes & ~(size_t)3) -
+                                                          qg::CB_COUNTERS * 4)
+                           : nullptr;
   qg::CodebookArgs a{M, N, K, x, codes, codebook, scales, y, c.ks > 1 ? wsf : nullptr, cnt};
   return hip_status(qg::launch_gemv_codebook(a, c, reinterpret_cast<hipStream_t>(stream)));
 }

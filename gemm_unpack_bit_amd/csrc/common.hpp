@@ -10,6 +10,7 @@ typedef _Float16 h2 __attribute__((ext_vector_type(2)));
 typedef _Float16 h4 __attribute__((ext_vector_type(4)));
 typedef _Float16 h8 __attribute__((ext_vector_type(8)));
 typedef float f4 __attribute__((ext_vector_type(4)));
+typedef float f16v __attribute__((ext_vector_type(16)));
 typedef uint32_t u2 __attribute__((ext_vector_type(2)));
 typedef uint32_t u4 __attribute__((ext_vector_type(4)));
 
@@ -73,6 +74,17 @@ __device__ __forceinline__ uint32_t magic1024x2() {
   uint32_t v;
   asm("v_mov_b32 %0, 0x64006400" : "=v"(v));
   return v;
+}
+
+// Workgroup barrier that orders LDS only: each wave waits for its own LDS
+// operations (lgkmcnt 0) and meets the others at s_barrier, while its global
+// loads stay in flight.  __syncthreads() would also wait for every vector
+// memory load (prefetches included), draining a software pipeline.
+__device__ __forceinline__ void lds_barrier() {
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+  __builtin_amdgcn_s_waitcnt(0xC07F);  // vmcnt 63, expcnt 7, lgkmcnt 0
+  __builtin_amdgcn_s_barrier();
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
 }
 
 // Raw buffer resource over [base, base + bytes): loads at byte offsets >= bytes

@@ -57,7 +57,7 @@ size_t lut4_max_k(int mt);  // largest K the LDS staging holds at mt rows
 hipError_t launch_gemv_lut4(const Lut4Args& a, const Lut4Cfg& c, hipStream_t s);
 
 // Codebook (m = 1, v = 4, b = 8, g = 128) with a Psumbook: codes [N, K/4]
-// uint8 in the tiled 8-bit device layout, codebook fp16 [256][4], scales fp16
+// uint8 in the 64-row layout (layout 2), codebook fp16 [256][4], scales fp16
 // [N, K/128]; ws/cnt: the K-split workspace (partials, then counters)
 struct CodebookArgs {
   int M, N, K;
@@ -69,12 +69,14 @@ struct CodebookArgs {
   float* ws;
   uint32_t* cnt;
 };
-// tpw = row-tiles per wave (1, 2, 4), wk = waves (1..16), ks = K splits
+// wk = waves = 64-row blocks per workgroup (4, 8, 16), ks = K splits
 struct CodebookCfg {
-  int tpw, wk, ks;
+  int wk, ks;
 };
 CodebookCfg pick_codebook(int M, int N, int K);
+constexpr size_t CB_COUNTERS = 4096;  // counters at the end of a codebook workspace
 size_t codebook_ws_bytes(const CodebookCfg& c, int M, int N);
+size_t codebook_row_blocks(const CodebookCfg& c, int N);
 hipError_t launch_gemv_codebook(const CodebookArgs& a, const CodebookCfg& c, hipStream_t s);
 
 // bit packing (layout: 0 plain, 1 device = tiled, see pack.hip)

@@ -11,6 +11,12 @@
 // (i/4)*256 + l*min(b,4) + i%4 and covers columns 128*g + 32*(l/16) + P*i +
 // [0, P) with field f holding offset 2f (f < P/2) or 2(f - P/2) + 1
 // (f >= P/2): the two 16-bit halves of a word carry consecutive columns.
+//
+// Row-block layout (layout 2, 8-bit codes only; the codebook variant's code
+// format): tiles of 64 rows x 16 columns (1 KB), tile (rb, cb) at byte
+// (rb * ceil(cols/16) + cb) * 1024, byte 16 l + i holding column 16 cb + i of
+// row 64 rb + l.  A wave-wide 16-byte load of one tile gives lane l 16
+// consecutive codes of its own row.  Rows and columns past the matrix are 0.
 #include "common.hpp"
 #include "kernels.hpp"
 
@@ -73,6 +79,35 @@ __global__ void pack_kernel(const uint8_t* __restrict__ codes, uint32_t* __restr
   packed[idx] = word;
 }
 
+__global__ void pack_rows64_kernel(const uint8_t* __restrict__ codes, uint32_t* __restrict__ packed, int rows,
+                                   int cols, size_t nwords) {
+  const size_t idx = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (idx >= nwords) return;
+  const int ncb = (cols + 15) / 16;
+  const size_t tile = idx / 256;
+  const int within = (int)(idx % 256);
+  const int l = within / 4, d = within % 4;
+  const int r = (int)(tile / ncb) * 64 + l;
+  const int c0 = (int)(tile % ncb) * 16 + 4 * d;
+  uint32_t word = 0;
+  if (r < rows) {
+#pragma unroll
+    for (int f = 0; f < 4; ++f)
+      if (c0 + f < cols) word |= (uint32_t)codes[(size_t)r * cols + c0 + f] << (8 * f);
+  }
+  packed[idx] = word;
+}
+
+__global__ void unpack_rows64_kernel(const uint32_t* __restrict__ packed, uint8_t* __restrict__ codes, int rows,
+                                     int cols) {
+  const size_t idx = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (idx >= (size_t)rows * cols) return;
+  const int r = (int)(idx / cols), c = (int)(idx % cols);
+  const int ncb = (cols + 15) / 16;
+  const size_t byte = ((size_t)(r / 64) * ncb + c / 16) * 1024 + 16 * (r % 64) + c % 16;
+  codes[idx] = (uint8_t)(packed[byte / 4] >> (8 * (byte % 4)));
+}
+
 template <int BITS, bool TILED>
 __global__ void unpack_kernel(const uint32_t* __restrict__ packed, uint8_t* __restrict__ codes, int rows,
                               int cols) {
@@ -130,6 +165,7 @@ hipError_t unpack_l(int bits, int rows, int cols, const uint32_t* packed, uint8_
 }  // namespace
 
 size_t packed_words(int bits, int layout, int rows, int cols) {
+  if (layout == 2) return bits == 8 ? (size_t)((rows + 63) / 64) * 64 * (size_t)((cols + 15) / 16) * 4 : 0;
   if (layout) return (size_t)((rows + 15) / 16) * 16 * (size_t)cols * bits / 32;
   return (size_t)rows * (size_t)(((long)cols * bits + 31) / 32);
 }
@@ -137,12 +173,24 @@ size_t packed_words(int bits, int layout, int rows, int cols) {
 hipError_t launch_pack(int bits, int layout, int rows, int cols, const uint8_t* codes, uint32_t* packed,
                        hipStream_t s) {
   const size_t n = packed_words(bits, layout, rows, cols);
+  if (layout == 2) {  // 8-bit codes: every byte value is a valid code
+    hipLaunchKernelGGL(clear_flag_kernel, dim3(1), dim3(1), 0, s);
+    if (n) hipLaunchKernelGGL(pack_rows64_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, codes, packed,
+                              rows, cols, n);
+    return hipGetLastError();
+  }
   return layout ? pack_l<true>(bits, rows, cols, codes, packed, n, s)
                 : pack_l<false>(bits, rows, cols, codes, packed, n, s);
 }
 
 hipError_t launch_unpack(int bits, int layout, int rows, int cols, const uint32_t* packed, uint8_t* codes,
                          hipStream_t s) {
+  if (layout == 2) {
+    const size_t n = (size_t)rows * cols;
+    if (n) hipLaunchKernelGGL(unpack_rows64_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, packed, codes,
+                              rows, cols);
+    return hipGetLastError();
+  }
   return layout ? unpack_l<true>(bits, rows, cols, packed, codes, s)
                 : unpack_l<false>(bits, rows, cols, packed, codes, s);
 }

@@ -106,9 +106,17 @@ int qgemv_last_hip_error(void);
  *                        word are consecutive columns.  The weights of every
  *                        compute entry point use this layout.
  *
+ *   QGEMV_LAYOUT_ROWS64  (b = 8 only) tiles of 64 rows x 16 columns, 1 KB each,
+ *                        rows padded to a multiple of 64 and columns to a
+ *                        multiple of 16; tile (rb, cb) starts at byte
+ *                        (rb*ceil(cols/16) + cb)*1024 and its byte 16l + i
+ *                        holds column 16cb + i of row 64rb + l.  A wave-wide
+ *                        16-byte load gives every lane 16 codes of its own row.
+ *                        The code format of qgemv_codebook.
+ *
  * Unused fields (past cols, or padding rows) are zero.
  * ------------------------------------------------------------------------ */
-typedef enum { QGEMV_LAYOUT_PLAIN = 0, QGEMV_LAYOUT_DEVICE = 1 } qgemv_layout;
+typedef enum { QGEMV_LAYOUT_PLAIN = 0, QGEMV_LAYOUT_DEVICE = 1, QGEMV_LAYOUT_ROWS64 = 2 } qgemv_layout;
 
 /* Number of uint32 words of a packed [rows, cols] matrix in `layout`
  * (0 on bad arguments, including cols % 128 != 0 for the device layout). */
@@ -218,13 +226,17 @@ int qgemv_outlier(int path, int M, int N, int K, const uint16_t *x, const uint32
  *
  *   x        [dev] fp16   [M, K]
  *   codes    [dev] uint32 the [N, K/4] uint8 code matrix packed with
- *                         qgemv_pack(8, QGEMV_LAYOUT_DEVICE, N, K/4, ...)
+ *                         qgemv_pack(8, QGEMV_LAYOUT_ROWS64, N, K/4, ...)
  *   codebook [dev] fp16   [256][4]
  *   scales   [dev] fp16   [N, K/128]
  *   y        [dev] fp16   [M, N]
- *   ws       [dev] optional workspace of qgemv_codebook_workspace_bytes(M, N, K)
- *                  bytes, ZERO-FILLED before its first use (every call leaves it
- *                  zero-filled again).  With it the library splits K across
+ *   ws       [dev] optional workspace of at least
+ *                  qgemv_codebook_workspace_bytes(M, N, K) bytes.  Its last
+ *                  16 KB hold counters that must be ZERO before the first call
+ *                  (every call leaves them zero); the rest is scratch.  One
+ *                  buffer may serve several shapes if it is passed with the
+ *                  same ws_bytes every time and is as large as the largest
+ *                  requirement.  With it the library splits K across
  *                  workgroups and adds the parts in a fixed order; with NULL or
  *                  a smaller ws it runs one pass per row block (same result
  *                  within the tolerance, usually slower).  Calls that share a

@@ -37,10 +37,11 @@ the exclusive prefix sum of per-tile counts (length tiles + 1).
 Codebook code tiles (codebook variant)
 --------------------------------------
 uint8 codes ``[N, K/4]`` (one code per 4 consecutive k) are regrouped into
-tiles of 16 rows x 64 code columns (two 128-wide quant groups).  Inside a
-tile, byte ``16*l + i`` (l = 0..63, i = 0..15) holds the code of row
-``16*rt + i``, code column ``64*ct + l``.  Tiles are ordered row-tile-major,
-then column tile.  Rows and columns past the matrix hold code 0.
+tiles of 64 rows x 16 code columns (1 KB).  Inside a tile, byte ``16*l + i``
+(l = 0..63, i = 0..15) holds the code of row ``64*rt + l``, code column
+``16*ct + i``.  Tiles are ordered row-tile-major, then column tile.  Rows and
+columns past the matrix hold code 0.  (The device layout is the
+implementation's choice; no page defines one.)
 """
 from __future__ import annotations
 
@@ -232,8 +233,8 @@ def tilecoo_decode(N, K, tile_ptr, tile_rec):
 # ----------------------------------------------------------------------------
 # codebook code tiles
 # ----------------------------------------------------------------------------
-CB_ROWS = 16  # rows per tile
-CB_COLS = 64  # code columns per tile (= two 128-wide quant groups at v = 4)
+CB_ROWS = 64  # rows per tile
+CB_COLS = 16  # code columns per tile
 
 
 def cb_tiled_bytes(N, KC):
@@ -244,7 +245,7 @@ def cb_tiled_bytes(N, KC):
 
 def pack_codebook_tiles(codes: np.ndarray) -> np.ndarray:
     """[N, KC] uint8 -> flat uint8 tiles; byte 16*l + i of tile (rt, ct) holds
-    code[16*rt + i, 64*ct + l]; out-of-range rows/columns hold 0."""
+    code[64*rt + l, 16*ct + i]; out-of-range rows/columns hold 0."""
     N, KC = codes.shape
     NR = (N + CB_ROWS - 1) // CB_ROWS
     NC = (KC + CB_COLS - 1) // CB_COLS
@@ -252,12 +253,12 @@ def pack_codebook_tiles(codes: np.ndarray) -> np.ndarray:
     for rt in range(NR):
         for ct in range(NC):
             base = (rt * NC + ct) * CB_ROWS * CB_COLS
-            for l in range(CB_COLS):
-                for i in range(CB_ROWS):
-                    r = rt * CB_ROWS + i
-                    c = ct * CB_COLS + l
+            for l in range(CB_ROWS):
+                for i in range(CB_COLS):
+                    r = rt * CB_ROWS + l
+                    c = ct * CB_COLS + i
                     if r < N and c < KC:
-                        out[base + CB_ROWS * l + i] = codes[r, c]
+                        out[base + CB_COLS * l + i] = codes[r, c]
     return out
 
 
@@ -268,10 +269,10 @@ def unpack_codebook_tiles(tiles: np.ndarray, N, KC) -> np.ndarray:
     for rt in range(NR):
         for ct in range(NC):
             base = (rt * NC + ct) * CB_ROWS * CB_COLS
-            for l in range(CB_COLS):
-                for i in range(CB_ROWS):
-                    r = rt * CB_ROWS + i
-                    c = ct * CB_COLS + l
+            for l in range(CB_ROWS):
+                for i in range(CB_COLS):
+                    r = rt * CB_ROWS + l
+                    c = ct * CB_COLS + i
                     if r < N and c < KC:
-                        out[r, c] = tiles[base + CB_ROWS * l + i]
+                        out[r, c] = tiles[base + CB_COLS * l + i]
     return out

@@ -4,7 +4,7 @@ import numpy as np
 import pytest
 
 import synth
-from oracle import reference as ref
+from oracle import formats, reference as ref
 from tests.gpu_util import assert_within, dev, host, sample_rows, say, torch
 
 pytestmark = pytest.mark.gpu
@@ -13,7 +13,16 @@ q = pytest.importorskip("gemm_unpack_bit_amd")
 
 
 def _upload(c):
-    return q.pack(dev(c["codes"]), 8), dev(c["codebook"]), dev(c["scales"])
+    return q.pack(dev(c["codes"]), 8, q.LAYOUT_ROWS64), dev(c["codebook"]), dev(c["scales"])
+
+
+@pytest.mark.parametrize("R,C", [(1, 16), (64, 128), (70, 40), (200, 2048)])
+def test_rows64_pack_bit_exact_against_oracle(R, C):
+    say("pack rows64", R, C)
+    codes = synth.codes(R + C, 2, R * C, 8).reshape(R, C)
+    packed = q.pack(dev(codes), 8, q.LAYOUT_ROWS64)
+    assert np.array_equal(host(packed).view(np.uint8), formats.pack_codebook_tiles(codes))
+    assert np.array_equal(host(q.unpack(packed, 8, R, C, q.LAYOUT_ROWS64)), codes)
 
 
 def _ws(M, N, K):
@@ -76,3 +85,22 @@ def test_codebook_70b_layers(idx):
         y_ref, A = ref.gemv_codebook(x, c["codes"], c["codebook"], c["scales"], rows=rows)
         assert_within(y[:, rows], y_ref, A, f"codebook {name} M={M}")
         assert np.isfinite(y.astype(np.float32)).all()
+
+
+def test_one_workspace_serves_several_shapes():
+    """A single zero-filled workspace, passed with the same size every time,
+    serves layers of different shapes called in any order."""
+    say("codebook shared workspace")
+    t = torch()
+    shapes = [(1, 8192, 8192), (1, 10240, 8192), (4, 8192, 8192)]
+    size = max(q.codebook_workspace_bytes(M, N, K) for M, N, K in shapes)
+    ws = t.zeros(size, dtype=t.uint8, device="cuda")
+    cases = []
+    for i, (M, N, K) in enumerate(shapes):
+        c = synth.codebook_case(40 + i, M, N, K)
+        cases.append((c, _upload(c), sample_rows(N)))
+    for rnd in range(2):
+        for (M, N, K), (c, (codes, cb, s), rows) in zip(shapes, cases):
+            y = host(q.codebook(dev(c["x"]), codes, cb, s, ws=ws))
+            y_ref, A = ref.gemv_codebook(c["x"], c["codes"], c["codebook"], c["scales"], rows=rows)
+            assert_within(y[:, rows], y_ref, A, f"shared ws round {rnd} M={M} N={N}")

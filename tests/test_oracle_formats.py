@@ -143,16 +143,18 @@ def test_tilecoo_roundtrip_and_errors():
 
 
 def test_codebook_tiles_positions_and_roundtrip():
-    N, KC = 20, 96  # ragged in both directions
+    N, KC = 70, 40  # ragged in both directions
     codes = ((np.arange(N)[:, None] * 7 + np.arange(KC)[None, :] * 3) % 256).astype(np.uint8)
     tiles = formats.pack_codebook_tiles(codes)
-    assert tiles.size == 2 * 2 * 1024
-    # tile (rt=1, ct=1) byte 16*l + i  <->  code[16 + i, 64 + l]
-    base = (1 * 2 + 1) * 1024
-    assert tiles[base + 16 * 5 + 3] == codes[19, 69]
-    assert tiles[base + 16 * 31 + 0] == codes[16, 95]
-    assert tiles[base + 16 * 32 + 0] == 0          # column 96 is past KC
-    assert tiles[base + 16 * 0 + 4] == 0           # row 20 is past N
+    assert tiles.size == 2 * 3 * 1024
+    # tile (rt=1, ct=2) byte 16*l + i  <->  code[64 + l, 32 + i]
+    base = (1 * 3 + 2) * 1024
+    assert tiles[base + 16 * 5 + 3] == codes[69, 35]
+    assert tiles[base + 16 * 0 + 7] == codes[64, 39]
+    assert tiles[base + 16 * 0 + 8] == 0           # column 40 is past KC
+    assert tiles[base + 16 * 6 + 0] == 0           # row 70 is past N
+    # tile (rt=0, ct=0) byte 16*l + i  <->  code[l, i]
+    assert tiles[16 * 63 + 15] == codes[63, 15]
     assert np.array_equal(formats.unpack_codebook_tiles(tiles, N, KC), codes)
 
 
