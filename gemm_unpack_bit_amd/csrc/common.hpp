@@ -80,6 +80,20 @@ __device__ __forceinline__ uint32_t magic1024x2() {
 // operations (lgkmcnt 0) and meets the others at s_barrier, while its global
 // loads stay in flight.  __syncthreads() would also wait for every vector
 // memory load (prefetches included), draining a software pipeline.
+// at(0) + at(1) + ... + at(n - 1), added in that order (n <= 16), with every
+// read issued before the first add: a loop that adds as it reads waits one
+// LDS round trip per term.
+template <typename F>
+__device__ __forceinline__ float ordered_sum16(int n, F&& at) {
+  float v[16];
+#pragma unroll
+  for (int w = 0; w < 16; ++w) v[w] = at(w < n ? w : n - 1);
+  float s = 0.f;
+#pragma unroll
+  for (int w = 0; w < 16; ++w) s = w < n ? s + v[w] : s;
+  return s;
+}
+
 __device__ __forceinline__ void lds_barrier() {
   __atomic_signal_fence(__ATOMIC_SEQ_CST);
   __builtin_amdgcn_s_waitcnt(0xC07F);  // vmcnt 63, expcnt 7, lgkmcnt 0

@@ -265,8 +265,7 @@ __global__ void __launch_bounds__(512) gemv_lut4_kernel(Lut4Args a) {
   __syncthreads();
   for (int e = threadIdx.x; e < TPW * MT * 16; e += blockDim.x) {
     const int r = e & 15, m = (e >> 4) % MT, t = (e >> 4) / MT;
-    float sum = 0.f;
-    for (int w = 0; w < WK; ++w) sum += red[((w * TPW + t) * MT + m) * 16 + r];
+    const float sum = ordered_sum16(WK, [&](int w) { return red[((w * TPW + t) * MT + m) * 16 + r]; });
     const int row = (rt0 + t) * 16 + r;
     if (m0 + m < M && row < N) a.y[(size_t)(m0 + m) * N + row] = f2h(sum);
   }

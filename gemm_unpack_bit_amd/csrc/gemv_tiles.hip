@@ -112,7 +112,11 @@ __device__ __forceinline__ void load_scales(rsrc_t r, uint32_t off, uint32_t sof
 //   V = 0: 64 activation VGPRs per lane (16 per group and batch row), D = 2;
 //   V = 1: half the chunk (32 VGPRs), D = 4;
 //   V = 2: one group per chunk (16 VGPRs per batch row), D = 4;
-//   V = 3: one group per chunk, D = 2.
+//   V = 3: one group per chunk, D = 2;
+//   V = 4, 5: one group per chunk, one tile-row per workgroup, D = 4 / 8
+//   chunks in flight (VALU engine with staged activations only): a small
+//   layer gives each wave only a few chunks, and all of them are issued at
+//   once instead of one memory round trip per chunk.
 // Fewer VGPRs buy occupancy (more waves per SIMD to overlap one wave's unpack
 // with another's loads); more groups per chunk buy longer contiguous stages.
 constexpr int chunk_groups(int bits, bool mfma, int mt, int v) {
@@ -120,7 +124,7 @@ constexpr int chunk_groups(int bits, bool mfma, int mt, int v) {
   if (v >= 2) return 1;
   return v && base > 1 ? base / 2 : base;
 }
-constexpr int ring_depth(int v) { return v == 1 || v == 2 ? 4 : 2; }
+constexpr int ring_depth(int v) { return v == 5 ? 8 : (v == 1 || v == 2 || v == 4 ? 4 : 2); }
 // Occupancy target (waves per SIMD) the compiler must fit the registers in:
 // one-group chunks are sized for 5 (<= 96 VGPRs), the others for 3.
 constexpr int waves_per_simd(int ng) { return ng == 1 ? 5 : 3; }
@@ -129,13 +133,20 @@ constexpr int max_threads(int ng) { return ng == 1 ? 1024 : 512; }
 
 // SAL: K/128 is a multiple of NG, so a chunk's NG scales of one row are one
 // aligned load and every chunk is whole.
-// XLDS (VALU engine): the workgroup stages its MT activation rows in LDS once
-// and every lane reads its 64-byte slice of a group from there.  The sixteen
-// lanes of a k-quarter share that slice, so loading it per lane through the
-// vector memory path would request 16x the bytes it uses.
+// XLDS: the workgroup stages its activation rows in LDS once (VALU: its MT
+// rows; MFMA: all M rows) and every lane reads its 64-byte slice of a group
+// from there.  The sixteen lanes of a k-quarter share that slice (VALU), so
+// loading it per lane through the vector memory path would request 16x the
+// bytes it uses.  MFMA lanes of batch rows past M read row M - 1 instead of
+// zeros: those rows of the product are never stored.
 // SP: also add the Tile-COO fp16 outliers of the workgroup's rows (outlier
 // variant): see sparse_prologue below.
-template <int BITS, bool MFMA, int MT, int NG, int D, int TPW, bool SAL, bool XLDS, bool SP>
+// PLDS (one tile-row of one-group chunks): the workgroup's 16 rows of scales
+// and of packed zero points are two contiguous blocks; they are staged in LDS
+// with coalesced 16-byte loads, so a chunk costs one weight load per lane
+// instead of three (per-lane scale and zero loads touch 16 rows' cache lines
+// for every 1 KB of codes).
+template <int BITS, bool MFMA, int MT, int NG, int D, int TPW, bool SAL, bool XLDS, bool SP, bool PLDS>
 __global__ void __launch_bounds__(max_threads(NG)) __attribute__((amdgpu_waves_per_eu(waves_per_simd(NG))))
 gemv_tiles_kernel(UniformArgs a) {
   using TR = Uni<BITS>;
@@ -144,12 +155,16 @@ gemv_tiles_kernel(UniformArgs a) {
   constexpr uint32_t ZMASK = (1u << BITS) - 1u;
   constexpr uint32_t TB = 16u * 128u * BITS / 8;  // tile bytes
   constexpr int XR = MFMA ? 1 : MT;               // activation rows per lane
-  static_assert(TPW % D == 0 || (TPW == 1 && D == 2), "a chunk's stages fill the ring evenly");
+  // DEEP: one tile-row and a ring of D > 2 one-group chunks
+  constexpr bool DEEP = TPW == 1 && D > 2;
+  static_assert(TPW % D == 0 || (TPW == 1 && D == 2) || DEEP, "a chunk's stages fill the ring evenly");
+  static_assert(!DEEP || (XLDS && NG == 1), "the deep chunk ring keeps no activations in registers");
   static_assert(ZPW % NG == 0, "a chunk's zero points share one word");
 
-  static_assert(!(MFMA && XLDS), "the MFMA engine's activation lanes are distinct");
-  // LDS: [staged activations: MT x K halves, XLDS only] then the per-wave
-  // partials: VALU [WK][TPW][MT][16] floats, MFMA [WK][TPW][64] float4
+  static_assert(!PLDS || (TPW == 1 && NG == 1), "staged quant params: one tile-row, one-group chunks");
+  // LDS: [staged activations: XM x K halves, XLDS only] [staged scales and
+  // zero points of the tile-row, PLDS only] then the per-wave partials: VALU
+  // [WK][TPW][MT][16] floats, MFMA [WK][TPW][64] float4
   extern __shared__ __attribute__((aligned(16))) float smem[];
 
   const int lane = threadIdx.x & 63;
@@ -174,7 +189,13 @@ gemv_tiles_kernel(UniformArgs a) {
   // staged activation row stride in halves: K, then a zero pad that groups
   // past K read instead (they add s = 0 times a finite value)
   const int XK = K + 32;
-  float* red = XLDS ? smem + (size_t)MT * XK / 2 : smem;
+  const int XM = MFMA ? min(M, 16) : MT;  // staged activation rows
+  char* const pbase = reinterpret_cast<char*>(smem) + (XLDS ? (size_t)XM * XK * 2 : 0);
+  const uint32_t psb = PLDS ? (32u * G + 15u) & ~15u : 0u;  // 16 rows x G scales, 16-byte padded
+  const uint32_t pzb = PLDS ? 16u * zrow : 0u;                // 16 rows of packed zero points
+  const uint16_t* ps = reinterpret_cast<const uint16_t*>(pbase);
+  const uint32_t* pz = reinterpret_cast<const uint32_t*>(pbase + psb);
+  float* red = reinterpret_cast<float*>(pbase + psb + pzb);
   const u4* xs = reinterpret_cast<const u4*>(smem);
 
   // outlier variant: LDS after the partials (see sparse_lds_bytes)
@@ -232,6 +253,7 @@ gemv_tiles_kernel(UniformArgs a) {
       const uint32_t sw = __builtin_amdgcn_readfirstlane(ok ? ((uint32_t)rt * G + gc0 + j) * TB : 0u);
       st.c[j].load(rw, ok ? lw : OOB, sw);
     }
+    if constexpr (PLDS) return;  // quant params come from LDS
     const uint32_t ss = __builtin_amdgcn_readfirstlane(cv ? 2u * gc0 : 0u);
     if constexpr (SAL) {
       load_scales<NG>(rs, srow, ss, st.s);
@@ -274,16 +296,31 @@ gemv_tiles_kernel(UniformArgs a) {
     const int gc0 = c * NG;
 #pragma unroll
     for (int j = 0; j < NG; ++j) {
-      const typename TR::Z zz = TR::zc((st.z >> (BITS * ((gc0 + j) % ZPW))) & ZMASK);
+      uint32_t zw = st.z;
+      uint16_t sj = st.s[j];
+      if constexpr (PLDS) {  // (a chunk past the last: scale 0, zero point 0)
+        // unconditional reads at a clamped group, then a select: a read under
+        // a condition would become a branch inside the pipelined loop
+        const bool gin = gc0 + j < G;
+        const int g = min(gc0 + j, G - 1);
+        const uint16_t sv = ps[n * G + g];
+        const uint32_t zv = pz[n * (int)(zrow / 4) + g / ZPW];
+        sj = gin ? sv : (uint16_t)0;
+        zw = gin ? zv : 0u;
+      }
+      const typename TR::Z zz = TR::zc((zw >> (BITS * ((gc0 + j) % ZPW))) & ZMASK);
       h2 p[16];  // (q - z) pairs of the lane's 32 consecutive k
 #pragma unroll
       for (int d = 0; d < BITS; ++d) TR::deq(st.c[j].w[d], mg, zz, p + d * PPD);
-      const float sc = h2f(st.s[j]);
+      const float sc = h2f(sj);
       if constexpr (MFMA) {
         f4 dd = f4{0.f, 0.f, 0.f, 0.f};
+        // A operand: batch row n (row XM - 1 for n >= XM), the lane's k slice
+        const bool xin = (SAL && XB == 1) || gc0 + j < G;
+        const int xa = (min(n, XM - 1) * XK + (xin ? 128 * (gc0 + j) + 32 * kq : K)) / 8;
 #pragma unroll
         for (int s = 0; s < 4; ++s)
-          dd = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(h8, xr[b][XLDS ? 0 : j][0][s]),
+          dd = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(h8, XLDS ? xs[xa + s] : xr[b][j][0][s]),
                                                        cat4(p[4 * s], p[4 * s + 1], p[4 * s + 2], p[4 * s + 3]),
                                                        dd, 0, 0, 0);
 #pragma unroll
@@ -312,26 +349,56 @@ gemv_tiles_kernel(UniformArgs a) {
   // early would hold its expanded pairs in registers and cost occupancy.
   St ring[D];
   int c = wave;
-  auto stage_x = [&]() {
-    // activations of rows m0 .. m0 + MT - 1 into LDS, 16 distinct bytes per
-    // lane and load; rows >= M read zeros.  Four loads in flight per lane.
-    // (row stride XK; the 4 pad vectors of each row get zeros: their loads
-    // are out of range)
-    u4* xw = reinterpret_cast<u4*>(smem);
-    const int X8 = XK / 8, n16 = MT * X8;
-    for (int i0 = threadIdx.x; i0 < n16; i0 += 4 * blockDim.x) {
-      u4 v[4];
+  // Activations of rows m0 .. m0 + MT - 1 into LDS, 16 distinct bytes per
+  // lane and load; rows >= M read zeros.  Four loads in flight per lane.
+  // (row stride XK; the 4 pad vectors of each row get zeros: their loads are
+  // out of range.)  The first pass is issued before the weight prefetch and
+  // written after it, so waiting for the activations never waits for the
+  // weights behind them (loads complete in order); the barrier waits for LDS
+  // traffic only, leaving the weight stages in flight.
+  const int X8 = XK / 8, n16 = XM * X8;
+  auto x_pass = [&](int i0, u4* v) {
 #pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        const int i = i0 + u * blockDim.x;
-        const int m = i / X8, k8 = i - m * X8;
-        v[u] = bload16(rx, i < n16 && m0 + m < M && k8 < K / 8 ? ((uint32_t)(m0 + m) * K + 8u * k8) * 2u : OOB);
-      }
+    for (int u = 0; u < 4; ++u) {
+      const int i = i0 + u * blockDim.x;
+      const int m = i / X8, k8 = i - m * X8;
+      v[u] = bload16(rx, i < n16 && m0 + m < M && k8 < K / 8 ? ((uint32_t)(m0 + m) * K + 8u * k8) * 2u : OOB);
+    }
+  };
+  u4 xfirst[XLDS ? 4 : 1];
+  // quant params of the tile-row: scale vectors [0, psb / 16), then zero
+  // point vectors; rows past N read zeros
+  const int np16 = (int)((psb + pzb) / 16);
+  auto p_pass = [&](int i) -> u4 {
+    const uint32_t sv = psb / 16u;
+    return (uint32_t)i < sv ? bload16(rs, (uint32_t)rt0 * 32u * G + 16u * i)
+                            : bload16(rz, i < np16 ? (uint32_t)rt0 * 16u * zrow + 16u * (i - sv) : OOB);
+  };
+  u4 pfirst;
+  auto stage_x_issue = [&]() {
+    if constexpr (XLDS) x_pass(threadIdx.x, xfirst);
+    if constexpr (PLDS) pfirst = p_pass(threadIdx.x);
+  };
+  auto stage_x = [&]() {
+    if constexpr (XLDS) {
+      u4* xw = reinterpret_cast<u4*>(smem);
 #pragma unroll
       for (int u = 0; u < 4; ++u)
-        if (i0 + u * blockDim.x < n16) xw[i0 + u * blockDim.x] = v[u];
+        if (threadIdx.x + u * blockDim.x < n16) xw[threadIdx.x + u * blockDim.x] = xfirst[u];
+      for (int i0 = threadIdx.x + 4 * blockDim.x; i0 < n16; i0 += 4 * blockDim.x) {
+        u4 v[4];
+        x_pass(i0, v);
+#pragma unroll
+        for (int u = 0; u < 4; ++u)
+          if (i0 + u * blockDim.x < n16) xw[i0 + u * blockDim.x] = v[u];
+      }
     }
-    __syncthreads();
+    if constexpr (PLDS) {
+      u4* pw = reinterpret_cast<u4*>(pbase);
+      if ((int)threadIdx.x < np16) pw[threadIdx.x] = pfirst;
+      for (int i = threadIdx.x + blockDim.x; i < np16; i += blockDim.x) pw[i] = p_pass(i);
+    }
+    lds_barrier();
   };
   // Outliers (FlashQuant abstract: fp16 sparse path fused with the low-bit
   // dense one, sharing activations and outputs; Tile-COO records): the
@@ -395,11 +462,13 @@ gemv_tiles_kernel(UniformArgs a) {
           const float v = h2f((uint16_t)(rec >> 16));
 #pragma unroll
           for (int m = 0; m < MS; ++m) {
-            float xv;
-            if constexpr (XLDS) {
-              xv = (float)reinterpret_cast<const _Float16*>(smem)[(size_t)m * XK + col];
-            } else {
-              xv = m0 + m < M ? h2f(bload2(rx, ((uint32_t)(m0 + m) * K + col) * 2u)) : 0.f;
+            float xv = 0.f;  // (batch rows past M: not staged, never stored)
+            if (m0 + m < M) {
+              if constexpr (XLDS) {
+                xv = (float)reinterpret_cast<const _Float16*>(smem)[(size_t)m * XK + col];
+              } else {
+                xv = h2f(bload2(rx, ((uint32_t)(m0 + m) * K + col) * 2u));
+              }
             }
             prodbuf[m * CH + (i - cs)] = v * xv;  // exact: a product of two fp16 values
           }
@@ -420,12 +489,12 @@ gemv_tiles_kernel(UniformArgs a) {
     }
   };
 
+  stage_x_issue();
+  // (a wave with no chunk at all, c >= NC, reads zeros: no branch here)
   if constexpr (XB == 1) {
-    if (c < NC) {
 #pragma unroll
-      for (int t = 0; t < D - 1; ++t) load_stage(t, c, ring[t]);
-      load_x(c, 0);
-    }
+    for (int t = 0; t < D - 1; ++t) load_stage(t, c, ring[t]);
+    load_x(c, 0);
     if constexpr (XLDS) stage_x();
     sparse_prologue();
     for (; c < NC; c += WK) {
@@ -443,14 +512,28 @@ gemv_tiles_kernel(UniformArgs a) {
       }
       load_x(c + WK, 0);
     }
+  } else if constexpr (DEEP) {
+    // one tile-row, D chunks in flight: chunk c + i WK sits in slot i % D
+    // (chunks past the last read zeros and add nothing)
+#pragma unroll
+    for (int i = 0; i < D - 1; ++i) load_stage(0, c + i * WK, ring[i]);
+    stage_x();
+    sparse_prologue();
+    for (; c < NC; c += D * WK) {
+#pragma unroll
+      for (int i = 0; i < D; ++i) {
+        load_stage(0, c + (i + D - 1) * WK, ring[(i + D - 1) % D]);
+        __builtin_amdgcn_sched_barrier(0);
+        compute(0, c + i * WK, ring[i], 0);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    }
   } else {
     // one tile-row, two stages: chunks alternate between slot/buffer 0 and 1
     // (a chunk past the last reads zeros and adds nothing)
-    if (c < NC) {
-      load_stage(0, c, ring[0]);
-      load_x(c, 0);
-    }
-    if constexpr (XLDS) stage_x();
+    load_stage(0, c, ring[0]);
+    load_x(c, 0);
+    if constexpr (XLDS || PLDS) stage_x();
     sparse_prologue();
     for (; c < NC; c += 2 * WK) {
       load_stage(0, c + WK, ring[1]);
@@ -475,8 +558,7 @@ gemv_tiles_kernel(UniformArgs a) {
     for (int e = threadIdx.x; e < TPW * 256; e += blockDim.x) {
       const int r = e & 15, m = (e >> 4) & 15, t = e >> 8;
       const int l = 16 * (m >> 2) + r, i = m & 3;
-      float sum = 0.f;
-      for (int w = 0; w < WK; ++w) sum += r4[(w * TPW + t) * 64 + l][i];
+      float sum = ordered_sum16(WK, [&](int w) { return r4[(w * TPW + t) * 64 + l][i]; });
       const int row = (rt0 + t) * 16 + r;
       if constexpr (SP) sum += spsum[m * RW + t * 16 + r];
       if (m < M && row < N) a.y[(size_t)m * N + row] = f2h(sum);
@@ -492,8 +574,7 @@ gemv_tiles_kernel(UniformArgs a) {
     __syncthreads();
     for (int e = threadIdx.x; e < TPW * MT * 16; e += blockDim.x) {
       const int r = e & 15, m = (e >> 4) % MT, t = (e >> 4) / MT;
-      float sum = 0.f;
-      for (int w = 0; w < WK; ++w) sum += red[((w * TPW + t) * MT + m) * 16 + r];
+      float sum = ordered_sum16(WK, [&](int w) { return red[((w * TPW + t) * MT + m) * 16 + r]; });
       const int row = (rt0 + t) * 16 + r;
       if constexpr (SP) sum += spsum[m * RW + t * 16 + r];
       if (m0 + m < M && row < N) a.y[(size_t)(m0 + m) * N + row] = f2h(sum);
@@ -506,9 +587,9 @@ constexpr size_t LDS_MAX = 64 * 1024;
 size_t tiles_lds_bytes(bool mfma, int mt, int tpw, int wk) {
   return mfma ? (size_t)wk * tpw * 64 * 16 : (size_t)wk * tpw * mt * 16 * 4;
 }
-// activation staging of the VALU engine: MT rows of K halves
+// activation staging: MT rows (VALU) or all M rows (MFMA) of K + 32 halves
 constexpr size_t XLDS_MAX = 64 * 1024 + 128;
-size_t xlds_bytes(bool mfma, int mt, int K) { return mfma ? 0 : (size_t)mt * (K + 32) * 2; }
+size_t xlds_bytes(bool mfma, int mt, int M, int K) { return (size_t)(mfma ? (M < 16 ? M : 16) : mt) * (K + 32) * 2; }
 
 // LDS of the outlier variant beyond the dense kernel's (mirrors the kernel's
 // layout: tile pointers, run table, sparse sums, record and product chunks)
@@ -520,9 +601,9 @@ size_t sparse_lds_bytes(bool mfma, int mt, int tpw, int K) {
 
 constexpr size_t LDS_ALL = 160 * 1024;  // gfx950 LDS per workgroup
 
-template <int BITS, bool MFMA, int MT, int NG, int D, int TPW, bool SAL, bool XLDS, bool SP>
+template <int BITS, bool MFMA, int MT, int NG, int D, int TPW, bool SAL, bool XLDS, bool SP, bool PLDS>
 hipError_t launch_k(const UniformArgs& a, dim3 grid, dim3 block, size_t lds, hipStream_t s) {
-  auto kern = &gemv_tiles_kernel<BITS, MFMA, MT, NG, D, TPW, SAL, XLDS, SP>;
+  auto kern = &gemv_tiles_kernel<BITS, MFMA, MT, NG, D, TPW, SAL, XLDS, SP, PLDS>;
   if (lds > 64 * 1024) {
     static bool raised = false;  // one-time opt-in above the default dynamic LDS limit
     if (!raised) {
@@ -536,11 +617,32 @@ hipError_t launch_k(const UniformArgs& a, dim3 grid, dim3 block, size_t lds, hip
   return hipGetLastError();
 }
 
+// staged quant params of one tile-row (PLDS): 16 rows of G fp16 scales,
+// 16-byte padded, then 16 rows of packed zero points
+size_t params_lds_bytes(int bits, int K) {
+  const size_t G = K / 128;
+  return (32 * G + 15) / 16 * 16 + 16 * 4 * ((G * bits + 31) / 32);
+}
+
+template <int BITS, bool MFMA, int MT, int NG, int D, int TPW, bool XL, bool SP>
+hipError_t launch_p(const UniformArgs& a, bool sal, bool plds, dim3 grid, dim3 block, size_t lds, hipStream_t s) {
+  if constexpr (TPW == 1 && NG == 1) {
+    // one-group chunks: a group's scale is always one whole, aligned load
+    if (!sal) return hipErrorInvalidValue;
+    return plds ? launch_k<BITS, MFMA, MT, NG, D, TPW, true, XL, SP, true>(a, grid, block, lds, s)
+                : launch_k<BITS, MFMA, MT, NG, D, TPW, true, XL, SP, false>(a, grid, block, lds, s);
+  } else {
+    return sal ? launch_k<BITS, MFMA, MT, NG, D, TPW, true, XL, SP, false>(a, grid, block, lds, s)
+               : launch_k<BITS, MFMA, MT, NG, D, TPW, false, XL, SP, false>(a, grid, block, lds, s);
+  }
+}
+
 template <int BITS, bool MFMA, int MT, int V, int TPW, bool SP = false>
 hipError_t launch_t(const UniformArgs& a, const TileCfg& c, hipStream_t s) {
   constexpr int NG = chunk_groups(BITS, MFMA, MT, V);
   constexpr int D = ring_depth(V);
-  if constexpr (TPW % D != 0 && !(TPW == 1 && D == 2 && NG == 1)) {
+  constexpr bool DEEP = TPW == 1 && D > 2;
+  if constexpr (TPW % D != 0 && !(TPW == 1 && D == 2 && NG == 1) && !(DEEP && !MFMA && NG == 1)) {
     return hipErrorInvalidValue;
   } else {
     const int NT = (a.N + 15) / 16;
@@ -548,18 +650,26 @@ hipError_t launch_t(const UniformArgs& a, const TileCfg& c, hipStream_t s) {
     const dim3 block(64 * c.wk);
     const size_t red = tiles_lds_bytes(MFMA, MT, TPW, c.wk);
     if (red > LDS_MAX || 64 * c.wk > max_threads(NG)) return hipErrorInvalidValue;
-    const size_t xl = xlds_bytes(MFMA, MT, a.K);
-    const bool xlds = !MFMA && xl <= XLDS_MAX;
-    const size_t lds = (xlds ? xl : 0) + red + (SP ? sparse_lds_bytes(MFMA, MT, TPW, a.K) : 0);
+    const size_t xl = xlds_bytes(MFMA, MT, a.M, a.K);
+    const bool xlds = xl <= XLDS_MAX;
+    // (the buffer bounds check drops a 16-byte load that straddles the end of
+    // an array, so both arrays must end on a 16-byte boundary: N % 8 == 0 does)
+    const size_t G = a.K / 128, zbytes = (size_t)a.N * 4 * ((G * BITS + 31) / 32);
+    const bool plds = TPW == 1 && NG == 1 && reinterpret_cast<uintptr_t>(a.scales) % 16 == 0 &&
+                      reinterpret_cast<uintptr_t>(a.zeros) % 16 == 0 && (size_t)a.N * G * 2 % 16 == 0 &&
+                      zbytes % 16 == 0;
+    const size_t lds = (xlds ? xl : 0) + (plds ? params_lds_bytes(BITS, a.K) : 0) + red +
+                       (SP ? sparse_lds_bytes(MFMA, MT, TPW, a.K) : 0);
     if (lds > LDS_ALL) return hipErrorInvalidValue;
     // chunk scales in one load: whole chunks and a 2*NG-byte aligned base
     const bool sal = (a.K / 128) % NG == 0 && reinterpret_cast<uintptr_t>(a.scales) % (2 * NG) == 0;
-    if (xlds) {
-      return sal ? launch_k<BITS, MFMA, MT, NG, D, TPW, true, !MFMA, SP>(a, grid, block, lds, s)
-                 : launch_k<BITS, MFMA, MT, NG, D, TPW, false, !MFMA, SP>(a, grid, block, lds, s);
+    if constexpr (DEEP) {
+      if (!xlds) return hipErrorInvalidValue;  // the deep ring reads activations from LDS only
+      return launch_p<BITS, MFMA, MT, NG, D, TPW, true, SP>(a, sal, plds, grid, block, lds, s);
+    } else {
+      if (xlds) return launch_p<BITS, MFMA, MT, NG, D, TPW, true, SP>(a, sal, plds, grid, block, lds, s);
+      return launch_p<BITS, MFMA, MT, NG, D, TPW, false, SP>(a, sal, plds, grid, block, lds, s);
     }
-    return sal ? launch_k<BITS, MFMA, MT, NG, D, TPW, true, false, SP>(a, grid, block, lds, s)
-               : launch_k<BITS, MFMA, MT, NG, D, TPW, false, false, SP>(a, grid, block, lds, s);
   }
 }
 
@@ -567,13 +677,20 @@ template <int BITS, bool MFMA, int MT, int V>
 hipError_t launch_tpw(const UniformArgs& a, const TileCfg& c, hipStream_t s) {
   switch (c.tpw) {
     case 1:
-      if constexpr (V == 3) return launch_t<BITS, MFMA, MT, V, 1>(a, c, s);
+      // (the 8-deep ring holds 8-bit stages only by spilling)
+      if constexpr (V == 3 || ((V == 4 || (V == 5 && BITS < 8)) && !MFMA)) return launch_t<BITS, MFMA, MT, V, 1>(a, c, s);
       return hipErrorInvalidValue;
-    case 2: return launch_t<BITS, MFMA, MT, V, 2>(a, c, s);
-    case 4: return launch_t<BITS, MFMA, MT, V, 4>(a, c, s);
-    case 8: return launch_t<BITS, MFMA, MT, V, 8>(a, c, s);
   }
-  return hipErrorInvalidValue;
+  if constexpr (V >= 4) {
+    return hipErrorInvalidValue;  // the deep rings exist for one tile-row only
+  } else {
+    switch (c.tpw) {
+      case 2: return launch_t<BITS, MFMA, MT, V, 2>(a, c, s);
+      case 4: return launch_t<BITS, MFMA, MT, V, 4>(a, c, s);
+      case 8: return launch_t<BITS, MFMA, MT, V, 8>(a, c, s);
+    }
+    return hipErrorInvalidValue;
+  }
 }
 
 template <int BITS, bool MFMA, int MT>
@@ -583,6 +700,8 @@ hipError_t launch_v(const UniformArgs& a, const TileCfg& c, hipStream_t s) {
     case 1: return launch_tpw<BITS, MFMA, MT, 1>(a, c, s);
     case 2: return launch_tpw<BITS, MFMA, MT, 2>(a, c, s);
     case 3: return launch_tpw<BITS, MFMA, MT, 3>(a, c, s);
+    case 4: return launch_tpw<BITS, MFMA, MT, 4>(a, c, s);
+    case 5: return launch_tpw<BITS, MFMA, MT, 5>(a, c, s);
   }
   return hipErrorInvalidValue;
 }

@@ -76,6 +76,42 @@ def test_uniform_small_shapes(path, bits, N, K, M):
 
 
 # ----------------------------------------------------------------------------
+# every launch shape the kernel accepts (forced through QGEMV_TILE_CFG), on a
+# ragged shape: whole and partial chunks, tile-rows past N, K/128 odd and even
+# ----------------------------------------------------------------------------
+LAUNCH_CASES = [(q.PATH_VALU, 1), (q.PATH_VALU, 2), (q.PATH_MFMA, 5)]
+
+
+@pytest.mark.parametrize("bits", [2, 4, 8])
+@pytest.mark.parametrize("N,K", [(300, 2176), (200, 2048)])
+@pytest.mark.parametrize("path,M", LAUNCH_CASES)
+def test_every_launch_shape(monkeypatch, bits, N, K, path, M):
+    say("launch shapes", bits, N, K, path, M)
+    c = synth.uniform_case(N + K + bits, M, N, K, bits)
+    wq = q.pack(dev(c["codes"]), bits)
+    zq = q.pack_zeros(dev(c["zeros"]), bits)
+    x, s = dev(c["x"]), dev(c["scales"])
+    y_ref, A = ref.gemv_uniform(c["x"], c["codes"], c["scales"], c["zeros"])
+    ran = []
+    for tpw in (1, 2, 4, 8):
+        for wk in (1, 4, 16):
+            for mt in ((1, 2) if path == q.PATH_VALU else (1,)):
+                for v in range(6):
+                    cfg = f"{tpw},{wk},{mt},{v}"
+                    monkeypatch.setenv("QGEMV_TILE_CFG", cfg)
+                    try:
+                        y = q.uniform(x, wq, s, zq, bits, path)
+                    except q.QgemvError:
+                        continue  # a shape this kernel does not take
+                    assert_within(host(y), y_ref, A, f"W{bits} M={M} N={N} K={K} path={path} cfg={cfg}")
+                    ran.append(cfg)
+    assert len(ran) >= 12, ran
+    if path == q.PATH_VALU:
+        # the deep chunk rings (one tile-row, 4 or 8 one-group chunks in flight)
+        assert any(r.startswith("1,") and r.endswith(",4") for r in ran), ran
+
+
+# ----------------------------------------------------------------------------
 # exact special cases
 # ----------------------------------------------------------------------------
 @pytest.mark.parametrize("path", PATHS)
