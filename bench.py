@@ -20,16 +20,23 @@ Printed: ONE JSON line (rank 0).  Extra objects: "roofline" for the dominant
 kernel (gate+up, the largest matrix; average launch duration = a region of K
 back-to-back launches of that layer alone, timed the same way), "cpu_baseline"
 (the float64 CPU oracle on a bounded row sample, host cores), "layers"
-(per-layer us/call, same method).  roofline.traffic = HBM bytes per launch of
+(per-layer us/call, same method), "variants" (W2, W8, W4 at M = 4 and 16,
+LUT4, outliers, codebook on the same four layers: per-layer launch time and
+algorithmic bytes, sampled rows checked against the oracle first; not part of
+`value`).  roofline.traffic = HBM bytes per launch of
 that kernel from rocprofv3 FETCH_SIZE / WRITE_SIZE (scaled by a device copy of
 known size), read from profiles/; null when the kernel sources changed since.
 
 Profiling helpers (used under rocprofv3):
-  --only LAYER          run only that layer in every step
+  --only LAYER          run only that layer in every step (skips the variants)
+  --no-variants         skip the other variants' measurements
   --copy-calibration    also time a device copy of known size (for scaling
                         FETCH_SIZE / WRITE_SIZE counters)
   --summarize-trace CSV print per-kernel, per-grid duration statistics of a
                         rocprofv3 --kernel-trace CSV and exit
+  --traffic-from FETCH_CSV WRITE_CSV
+                        write the gate_up traffic record (profiles/) from the
+                        two counter passes' CSVs and exit
 """
 from __future__ import annotations
 
@@ -151,10 +158,13 @@ def summarize_trace(path):
     import csv
     from collections import defaultdict
 
+    import re
+
     d = defaultdict(list)
     with open(path) as f:
         for r in csv.DictReader(f):
-            key = (r["Kernel_Name"], int(r["Grid_Size_X"]), int(r["Workgroup_Size_X"]))
+            name = re.sub(r"^void qg::\(anonymous namespace\)::", "", r["Kernel_Name"]).split("(")[0]
+            key = (name.replace(" ", ""), int(r["Grid_Size_X"]), int(r["Workgroup_Size_X"]))
             d[key].append((int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1000.0)
     print(f"{'kernel':72s} {'grid':>8s} {'wg':>5s} {'n':>5s} {'mean':>8s} {'median':>8s} {'p10':>8s} {'p90':>8s}")
     for (name, gx, wx), v in sorted(d.items(), key=lambda kv: -sum(kv[1])):
@@ -170,21 +180,172 @@ def summarize_trace(path):
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "gemv_w4a16_gate_up_28672x4096_m1_hbm_traffic.json")
 
 
-def measured_traffic():
+KERNEL_SOURCES = ["gemm_unpack_bit_amd/csrc/gemv_tiles.hip", "gemm_unpack_bit_amd/csrc/dequant.hpp",
+                  "gemm_unpack_bit_amd/csrc/common.hpp", "gemm_unpack_bit_amd/csrc/kernels.hpp",
+                  "gemm_unpack_bit_amd/csrc/api.cpp"]
+
+
+def sources_sha256(paths):
     import hashlib
 
+    h = hashlib.sha256()
+    for src in paths:
+        with open(os.path.join(ROOT, src), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
+
+
+def traffic_from(fetch_csv, write_csv):
+    """The traffic record from two rocprofv3 --pmc runs of
+    `bench.py --only gate_up --copy-calibration` (FETCH_SIZE, then WRITE_SIZE):
+    the GEMV's KiB per dispatch, each scaled by what the same counter reads for
+    the 256 MiB calibration copy, stamped with the current kernel sources'
+    SHA-256.  Written to TRAFFIC_FILE and printed."""
+    import csv
+
+    copy_bytes = 256 << 20
+
+    def read(path, counter):
+        gemv, copy, names = [], [], set()
+        for r in csv.DictReader(open(path)):
+            if r["Counter_Name"] != counter:
+                continue
+            v = float(r["Counter_Value"])
+            if "gemv_tiles_kernel" in r["Kernel_Name"]:
+                gemv.append(v)
+                names.add((r["Kernel_Name"], r["Grid_Size"], r["Workgroup_Size"]))
+            elif "copyBuffer" in r["Kernel_Name"]:
+                copy.append(v)
+        if not gemv or not copy or len(names) != 1:
+            raise SystemExit(f"traffic: expected one GEMV kernel and the calibration copy in {path}")
+        return sum(gemv) / len(gemv), max(copy), len(gemv), names.pop()
+
+    f_kib, f_copy, n, (kname, grid, wg) = read(fetch_csv, "FETCH_SIZE")
+    w_kib, w_copy, _, _ = read(write_csv, "WRITE_SIZE")
+    ff, wf = copy_bytes / 1024 / f_copy, copy_bytes / 1024 / w_copy
+    import re
+
+    m = re.search(r"gemv_tiles_kernel<[^>]*>", kname)
+    kshort = m.group(0).replace(" ", "") if m else kname
+    N, K = synth.LLAMA3_8B_LAYERS["gate_up"]
+    rec = {
+        "kernel": f"{kshort} (gate_up {N}x{K}, W4A16 g128, M=1, grid {grid} threads x {wg}/wg)",
+        "kernel_sources": KERNEL_SOURCES,
+        "kernel_src_sha256": sources_sha256(KERNEL_SOURCES),
+        "fetch_size_kib_per_dispatch": round(f_kib, 3),
+        "write_size_kib_per_dispatch": round(w_kib, 3),
+        "dispatches": n,
+        "copy_bytes": copy_bytes,
+        "copy_fetch_kib": round(f_copy, 3),
+        "copy_write_kib": round(w_copy, 3),
+        "fetch_factor": round(ff, 5),
+        "write_factor": round(wf, 5),
+        "traffic_bytes_per_launch": int(round((f_kib * ff + w_kib * wf) * 1024)),
+        "algorithmic_bytes_per_launch": alg_bytes(N, K),
+    }
+    with open(TRAFFIC_FILE, "w") as f:
+        json.dump(rec, f, indent=1)
+    print(json.dumps(rec, indent=1))
+
+
+def measured_traffic():
     try:
         with open(TRAFFIC_FILE) as f:
             rec = json.load(f)
-        h = hashlib.sha256()
-        for src in rec["kernel_sources"]:
-            with open(os.path.join(ROOT, src), "rb") as f:
-                h.update(f.read())
+        digest = sources_sha256(rec["kernel_sources"])
     except (OSError, KeyError, ValueError):
         return None
-    if h.hexdigest() != rec.get("kernel_src_sha256"):
+    if digest != rec.get("kernel_src_sha256"):
         return None  # the kernel changed since the counters were taken
     return int(rec["traffic_bytes_per_launch"])
+
+
+# ---------------------------------------------------------------------------
+# the other variants on the same four layers (reported beside the headline,
+# not part of `value`): each layer's cache-cold launch time, algorithmic bytes
+# per launch, sampled rows checked against the oracle first
+# ---------------------------------------------------------------------------
+VARIANTS = {
+    "w2a16_m1": dict(kind="uniform", bits=2, m=1),
+    "w8a16_m1": dict(kind="uniform", bits=8, m=1),
+    "w4a16_m4": dict(kind="uniform", bits=4, m=4),
+    "w4a16_m16": dict(kind="uniform", bits=4, m=16),
+    "lut4_m1": dict(kind="lut4", bits=4, m=1),
+    "outlier_m1": dict(kind="outlier", bits=4, m=1),
+    "codebook_m1": dict(kind="codebook", bits=2, m=1),
+}
+
+
+def variant_layer(torch, q, dev, kind, bits, m, idx, N, K):
+    """Host case, device inputs (one copy), launch function and algorithmic bytes."""
+    from oracle import reference as ref
+
+    seed = synth.seed_for(2, 16 * idx + bits + 4 * m)
+    up = lambda a: torch.from_numpy(np.ascontiguousarray(a)).to(dev)
+    y = torch.empty((m, N), dtype=torch.float16, device=dev)
+    io = 2 * m * K + 2 * m * N
+    if kind == "uniform":
+        c = synth.uniform_case(seed, m, N, K, bits)
+        t = dict(x=up(c["x"]), wq=q.pack(up(c["codes"]), bits), s=up(c["scales"]),
+                 z=q.pack_zeros(up(c["zeros"]), bits))
+        call = lambda t: q.uniform(t["x"], t["wq"], t["s"], t["z"], bits, out=y)
+        oracle = lambda rows: ref.gemv_uniform(c["x"], c["codes"], c["scales"], c["zeros"], rows=rows)
+        nbytes = alg_bytes(N, K, bits, m)
+    elif kind == "lut4":
+        c = synth.lut4_case(seed, m, N, K)
+        t = dict(x=up(c["x"]), wq=q.pack(up(c["codes"]), 4), a=up(c["absmax"]), lut=up(c["lut"]))
+        call = lambda t: q.lut4(t["x"], t["wq"], t["a"], t["lut"], out=y)
+        oracle = lambda rows: ref.gemv_lut4(c["x"], c["codes"], c["absmax"], c["lut"], rows=rows)
+        nbytes = N * K // 2 + N * (K // 64) * 2 + 32 + io
+    elif kind == "outlier":
+        c = synth.outlier_case(seed, m, N, K)
+        ptr, rec = q.tilecoo_encode(N, K, c["o_rows"], c["o_cols"], c["o_vals"])
+        t = dict(x=up(c["x"]), wq=q.pack(up(c["codes"]), 4), s=up(c["scales"]),
+                 z=q.pack_zeros(up(c["zeros"]), 4), p=up(ptr.view(np.int32)), r=up(rec.view(np.int32)))
+        call = lambda t: q.outlier(t["x"], t["wq"], t["s"], t["z"], t["p"], t["r"], out=y)
+        oracle = lambda rows: ref.gemv_outlier(c["x"], c["codes"], c["scales"], c["zeros"], c["o_rows"],
+                                               c["o_cols"], c["o_vals"], rows=rows)
+        nbytes = alg_bytes(N, K, 4, m) + 4 * rec.size + 4 * ptr.size
+    else:
+        c = synth.codebook_case(seed, m, N, K)
+        ws = torch.zeros(max(q.codebook_workspace_bytes(m, N, K), 4) // 4, dtype=torch.int32, device=dev)
+        t = dict(x=up(c["x"]), codes=q.pack(up(c["codes"]), 8, q.LAYOUT_ROWS64), cb=up(c["codebook"]),
+                 s=up(c["scales"]))
+        call = lambda t: q.codebook(t["x"], t["codes"], t["cb"], t["s"], ws=ws, out=y)
+        oracle = lambda rows: ref.gemv_codebook(c["x"], c["codes"], c["codebook"], c["scales"], rows=rows)
+        nbytes = N * K // 4 + N * (K // 128) * 2 + 256 * 4 * 2 + io
+    return t, call, oracle, y, nbytes
+
+
+def measure_variants(torch, q, dev, timer, n):
+    from oracle import reference as ref
+
+    out = {}
+    for vname, v in VARIANTS.items():
+        layers, total_us, total_bytes = {}, 0.0, 0
+        for idx, (name, (N, K)) in enumerate(synth.LLAMA3_8B_LAYERS.items()):
+            t, call, oracle, y, nbytes = variant_layer(torch, q, dev, v["kind"], v["bits"], v["m"], idx, N, K)
+            call(t)
+            rows = np.linspace(0, N - 1, 8).astype(np.int64)
+            y_ref, A = oracle(rows)
+            if not ref.within_tolerance(y.cpu().numpy()[:, rows], y_ref, A).all():
+                raise SystemExit(f"bench: variant {vname} {name} outside tolerance on sampled rows")
+            R = max(2, -(-(1 << 30) // nbytes))
+            copies = [t] + [{k: (a.clone() if k not in ("x", "lut", "cb") else a) for k, a in t.items()}
+                            for _ in range(R - 1)]
+            fn = lambda i: call(copies[i % R])
+            for i in range(8):
+                fn(i)
+            us = timer.region_us(fn, n, host_cost(torch, fn)) / n
+            layers[name] = {"us_per_call": round(us, 3), "GBps": round(nbytes / us / 1e3, 1),
+                            "pct_peak": round(nbytes / us / 1e3 / PEAK_HBM_GBS * 100, 1), "bytes": nbytes}
+            total_us += us
+            total_bytes += nbytes
+            del copies, t
+            torch.cuda.empty_cache()
+        out[vname] = {"m": v["m"], "layers": layers, "us_per_step": round(total_us, 3),
+                      "GBps": round(total_bytes / total_us / 1e3, 1)}
+    return out
 
 
 def cpu_baseline(layers, budget_s=10.0):
@@ -228,12 +389,17 @@ def main():
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=50)
     ap.add_argument("--no-cpu", action="store_true", help="skip the cpu_baseline leg")
+    ap.add_argument("--no-variants", action="store_true", help="skip the other variants' measurements")
     ap.add_argument("--only", default=None, help="run only this layer (profiling)")
     ap.add_argument("--copy-calibration", action="store_true")
     ap.add_argument("--summarize-trace", default=None)
+    ap.add_argument("--traffic-from", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"), default=None)
     args = ap.parse_args()
     if args.summarize_trace:
         summarize_trace(args.summarize_trace)
+        return
+    if args.traffic_from:
+        traffic_from(*args.traffic_from)
         return
     if args.gpus != 1:
         print(f"bench.py: this build runs on one GPU; --gpus {args.gpus} is not supported "
@@ -327,6 +493,8 @@ def main():
         },
         "layers": per_layer,
     }
+    if not (args.no_variants or args.only):
+        out["variants"] = measure_variants(torch, q, dev, timer, max(20, min(K, 100)))
     if not args.no_cpu:
         out["cpu_baseline"] = cpu_baseline(layers)
     print(json.dumps(out), flush=True)

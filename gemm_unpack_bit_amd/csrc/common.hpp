@@ -80,18 +80,42 @@ __device__ __forceinline__ uint32_t magic1024x2() {
 // operations (lgkmcnt 0) and meets the others at s_barrier, while its global
 // loads stay in flight.  __syncthreads() would also wait for every vector
 // memory load (prefetches included), draining a software pipeline.
-// at(0) + at(1) + ... + at(n - 1), added in that order (n <= 16), with every
-// read issued before the first add: a loop that adds as it reads waits one
-// LDS round trip per term.
+// Sum of the values held by lanes n, n + 16, n + 32, n + 48 of a wave,
+// returned in all four lanes, in the fixed order (q0 + q2) + (q1 + q3)
+// (gfx950 permlane swaps; every lane of the wave must take part).
+__device__ __forceinline__ float quarter_sum(float v) {
+  const uint32_t u = __float_as_uint(v);
+  const auto a = __builtin_amdgcn_permlane32_swap(u, u, false, false);
+  const float s = __uint_as_float(a[0]) + __uint_as_float(a[1]);
+  const uint32_t su = __float_as_uint(s);
+  const auto b = __builtin_amdgcn_permlane16_swap(su, su, false, false);
+  return __uint_as_float(b[0]) + __uint_as_float(b[1]);
+}
+
+// Sum over waves w < WK (WK <= 16) of per-wave partials red[w * OUT + o],
+// OUT a multiple of 16, after a barrier.  Output o is summed by the four lanes
+// l, l + 16, l + 32, l + 48 of one wave -- lane quarter q takes waves q, q + 4,
+// q + 8, q + 12, all reads issued together -- then across the quarters: a
+// fixed order, so the result is deterministic.  store(o, sum) runs once per
+// output, in lane l < 16 of the wave that summed it.
 template <typename F>
-__device__ __forceinline__ float ordered_sum16(int n, F&& at) {
-  float v[16];
+__device__ __forceinline__ void reduce_waves(const float* red, int OUT, int WK, F&& store) {
+  const int lane = threadIdx.x & 63, q = lane >> 4;
+  const int nw = blockDim.x >> 6;
+  for (int o0 = (threadIdx.x >> 6) * 16; o0 < OUT; o0 += nw * 16) {  // wave-uniform
+    const int o = o0 + (lane & 15);
+    float v[4];
 #pragma unroll
-  for (int w = 0; w < 16; ++w) v[w] = at(w < n ? w : n - 1);
-  float s = 0.f;
+    for (int i = 0; i < 4; ++i) {
+      const int w = q + 4 * i;
+      v[i] = red[(w < WK ? w : 0) * OUT + o];
+    }
+    float sum = 0.f;
 #pragma unroll
-  for (int w = 0; w < 16; ++w) s = w < n ? s + v[w] : s;
-  return s;
+    for (int i = 0; i < 4; ++i) sum = q + 4 * i < WK ? sum + v[i] : sum;
+    sum = quarter_sum(sum);
+    if (q == 0) store(o, sum);
+  }
 }
 
 __device__ __forceinline__ void lds_barrier() {

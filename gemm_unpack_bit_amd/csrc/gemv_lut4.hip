@@ -41,15 +41,6 @@ __host__ __device__ constexpr size_t xarea_bytes(int mt, int K) {
   return (size_t)mt * (K + 32) * 2 > 1024 ? (size_t)mt * (K + 32) * 2 : 1024;
 }
 
-__device__ __forceinline__ float quarter_sum4(float v) {
-  const uint32_t u = __float_as_uint(v);
-  const auto a = __builtin_amdgcn_permlane32_swap(u, u, false, false);
-  const float s = __uint_as_float(a[0]) + __uint_as_float(a[1]);
-  const uint32_t su = __float_as_uint(s);
-  const auto b = __builtin_amdgcn_permlane16_swap(su, su, false, false);
-  return __uint_as_float(b[0]) + __uint_as_float(b[1]);
-}
-
 // Block scales of NG consecutive groups of one row: the lane's 64-block is
 // (2 g + kq / 2); one aligned load when SAL.
 template <int NG>
@@ -259,16 +250,15 @@ __global__ void __launch_bounds__(512) gemv_lut4_kernel(Lut4Args a) {
   for (int t = 0; t < TPW; ++t)
 #pragma unroll
     for (int m = 0; m < MT; ++m) {
-      const float v = quarter_sum4(acc[t][m]);
+      const float v = quarter_sum(acc[t][m]);
       if (lane < 16) red[((wave * TPW + t) * MT + m) * 16 + lane] = v;
     }
   __syncthreads();
-  for (int e = threadIdx.x; e < TPW * MT * 16; e += blockDim.x) {
+  reduce_waves(red, TPW * MT * 16, WK, [&](int e, float sum) {
     const int r = e & 15, m = (e >> 4) % MT, t = (e >> 4) / MT;
-    const float sum = ordered_sum16(WK, [&](int w) { return red[((w * TPW + t) * MT + m) * 16 + r]; });
     const int row = (rt0 + t) * 16 + r;
     if (m0 + m < M && row < N) a.y[(size_t)(m0 + m) * N + row] = f2h(sum);
-  }
+  });
 }
 
 constexpr size_t LUT4_LDS_LIMIT = 160 * 1024;

@@ -48,18 +48,6 @@ __device__ __forceinline__ h8 cat4(h2 a, h2 b, h2 c, h2 d) {
   return __builtin_bit_cast(h8, u4{as_u32(a), as_u32(b), as_u32(c), as_u32(d)});
 }
 
-// Sum of the values held by lanes n, n + 16, n + 32, n + 48 (the four
-// k-quarters of tile row n), returned in all four lanes, in the fixed order
-// (q0 + q2) + (q1 + q3).
-__device__ __forceinline__ float quarter_sum(float v) {
-  const uint32_t u = __float_as_uint(v);
-  const auto a = __builtin_amdgcn_permlane32_swap(u, u, false, false);
-  const float s = __uint_as_float(a[0]) + __uint_as_float(a[1]);
-  const uint32_t su = __float_as_uint(s);
-  const auto b = __builtin_amdgcn_permlane16_swap(su, su, false, false);
-  return __uint_as_float(b[0]) + __uint_as_float(b[1]);
-}
-
 // One lane's codes of one tile: 32 codes = b words, in <= 2 loads.
 template <int BITS>
 struct LaneCodes {
@@ -558,7 +546,8 @@ gemv_tiles_kernel(UniformArgs a) {
     for (int e = threadIdx.x; e < TPW * 256; e += blockDim.x) {
       const int r = e & 15, m = (e >> 4) & 15, t = e >> 8;
       const int l = 16 * (m >> 2) + r, i = m & 3;
-      float sum = ordered_sum16(WK, [&](int w) { return r4[(w * TPW + t) * 64 + l][i]; });
+      float sum = 0.f;
+      for (int w = 0; w < WK; ++w) sum += r4[(w * TPW + t) * 64 + l][i];
       const int row = (rt0 + t) * 16 + r;
       if constexpr (SP) sum += spsum[m * RW + t * 16 + r];
       if (m < M && row < N) a.y[(size_t)m * N + row] = f2h(sum);
@@ -572,13 +561,12 @@ gemv_tiles_kernel(UniformArgs a) {
         if (lane < 16) red[((wave * TPW + t) * MT + m) * 16 + lane] = v;
       }
     __syncthreads();
-    for (int e = threadIdx.x; e < TPW * MT * 16; e += blockDim.x) {
+    reduce_waves(red, TPW * MT * 16, WK, [&](int e, float sum) {
       const int r = e & 15, m = (e >> 4) % MT, t = (e >> 4) / MT;
-      float sum = ordered_sum16(WK, [&](int w) { return red[((w * TPW + t) * MT + m) * 16 + r]; });
       const int row = (rt0 + t) * 16 + r;
       if constexpr (SP) sum += spsum[m * RW + t * 16 + r];
       if (m0 + m < M && row < N) a.y[(size_t)(m0 + m) * N + row] = f2h(sum);
-    }
+    });
   }
 }
 
@@ -718,40 +706,58 @@ hipError_t launch_b(const UniformArgs& a, const TileCfg& c, hipStream_t s) {
 
 }  // namespace
 
-// Launch shape per engine and layer shape, from sweeps on MI355X over the
-// Llama-3-8B / 70B decode layers (cache-cold weights, W2/W4/W8, M = 1..16):
-//  * few tile-rows (NT <= 256, N <= 4096): one tile-row per workgroup and
-//    one-group chunks, so all 256 CUs get work;
-//  * otherwise two tile-rows per workgroup, four-group chunks; waves per
-//    workgroup shrink as the tile-row count grows (the grid already fills
-//    the chip); the MFMA engine takes more tile-rows per workgroup on the
-//    widest layers, where it reuses each activation fragment longer.
+// Launch shape per engine and layer shape, fitted to full sweeps on MI355X
+// over the Llama-3-8B / 70B decode layers (cache-cold weights, W2/W4/W8,
+// M = 1..16; within 2% of the per-shape best in total):
+//  * VALU (batch 1): one tile-row per workgroup with staged quant params and
+//    one-group chunks -- 16 waves for long K, 4 when the grid is already wide,
+//    a 4-deep chunk ring for the shortest K -- except the widest layers and
+//    4-bit layers of 384-512 tile-rows, which take two tile-rows and
+//    four-group chunks;
+//  * MFMA (batch >= 2): one tile-row for narrow layers; more tile-rows per
+//    workgroup as the batch and the width grow (longer reuse of each staged
+//    activation fragment), 8 tile-rows with half chunks for the widest 4-bit
+//    layers at M >= 8.
 TileCfg pick_tiles(int bits, int M, int N, int K, bool mfma) {
   TileCfg c;
   c.mfma = mfma;
   c.mt = mfma || M <= 1 ? 1 : 2;
   const int G = K / 128;
   const long nt = (N + 15) / 16;
-  if (nt <= (bits == 8 && !mfma ? 640 : 256)) {
-    c.tpw = 1;
-    c.v = 3;
-    c.wk = !mfma && G >= 64 ? 16 : 8;
-  } else if (!mfma) {
-    c.tpw = 2;
-    c.v = 0;
-    c.wk = nt >= 2048 ? 4 : (nt >= 1024 ? 2 : 8);
-  } else if (nt >= 1536) {
-    const bool deep = M >= 8 && bits == 4;  // 2- and 8-bit stages leave no room for 8 tile-rows
-    c.tpw = deep ? 8 : 4;
-    c.v = deep ? 1 : 0;
-    c.wk = deep ? 8 : 4;
+  auto set = [&](int tpw, int wk, int v) {
+    c.tpw = tpw;
+    c.wk = wk;
+    c.v = v;
+  };
+  if (!mfma) {
+    if (nt >= 2048 || (bits == 4 && G <= 32 && nt > 256 && nt <= 512)) {
+      set(2, 8, 0);
+    } else {
+      const int wk = G >= 96 ? 16 : (nt >= 1024 ? 4 : 8);
+      set(1, wk, wk <= 8 && (nt <= 256 || nt >= 1024) ? 4 : 3);
+    }
+  } else if (M >= 8 && nt >= 1536 && bits != 2) {
+    if (bits == 4) set(8, 8, 1);        // half chunks keep 8 tile-rows of stages in registers
+    else if (M >= 9) set(8, 8, 0);
+    else set(4, 4, 0);
+  } else if (M <= 2) {
+    if (nt >= 2048 || (nt > 256 && G >= 128)) set(2, 8, 0);
+    else if (nt <= 256) set(1, 16, 3);
+    else set(1, nt >= 1024 ? 4 : 8, 3);
+  } else if (M <= 4) {
+    if (nt >= 1536) set(4, nt >= 2048 ? 4 : 8, 0);
+    else if (nt <= 256) set(1, G >= 96 ? 8 : 16, 3);
+    else if (G >= 128) set(2, 8, 0);
+    else set(1, 8, 3);
   } else {
-    c.tpw = nt >= 640 ? 4 : 2;
-    c.v = 0;
-    c.wk = nt >= 640 ? 8 : 4;
+    if (nt <= 256) set(1, M <= 8 ? 8 : 4, 3);
+    else if (nt >= 1536) set(4, 4, 0);
+    else if (nt >= 640) set(4, 8, 0);
+    else set(2, M <= 8 ? 8 : 4, 0);
   }
   // never more waves than chunks of groups
-  const int nc = (G + chunk_groups(bits, mfma, c.mt, c.v) - 1) / chunk_groups(bits, mfma, c.mt, c.v);
+  const int ng = chunk_groups(bits, mfma, c.mt, c.v);
+  const int nc = (G + ng - 1) / ng;
   if (c.wk > nc) c.wk = nc < 1 ? 1 : nc;
   return c;
 }
@@ -761,7 +767,9 @@ TileCfg pick_tiles(int bits, int M, int N, int K, bool mfma) {
 // Tile-COO tile-row).
 TileCfg pick_outlier(int M, int N, int K, bool mfma) {
   TileCfg c = pick_tiles(4, M, N, K, mfma);
-  if (c.tpw != 1) {
+  if (c.tpw == 1) {
+    c.v = 3;
+  } else {
     c.tpw = 2;
     c.v = 0;
     const int nc = (K / 128 + chunk_groups(4, mfma, c.mt, 0) - 1) / chunk_groups(4, mfma, c.mt, 0);
