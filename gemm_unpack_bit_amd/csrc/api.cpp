@@ -207,7 +207,19 @@ int qgemv_outlier(int path, int M, int N, int K, const uint16_t* x, const uint32
   qg::UniformArgs a{4, M, N, K, x, wq, scales, zeros, y, tile_ptr, tile_rec, (int)nnz};
   if (path == QGEMV_PATH_AUTO) path = auto_path(4, M, N);
   const bool mfma = path == QGEMV_PATH_MFMA;
-  return hip_status(qg::launch_gemv_outlier(a, qg::pick_outlier(M, N, K, mfma), reinterpret_cast<hipStream_t>(stream)));
+  qg::TileCfg c = qg::pick_outlier(M, N, K, mfma);
+  if (const char* e = std::getenv("QGEMV_OUTLIER_CFG")) {  // tuning override "tpw,wk[,mt[,v]]"
+    int tpw, wk, mt, v;
+    const int n = std::sscanf(e, "%d,%d,%d,%d", &tpw, &wk, &mt, &v);
+    if (n >= 2) {
+      c.v = tpw != 1 ? 0 : (c.tpw == 1 ? c.v : 3);  // (a one-tile-row pick keeps its ring)
+      c.tpw = tpw;
+      c.wk = wk;
+    }
+    if (n >= 3 && !mfma) c.mt = mt;
+    if (n >= 4) c.v = v;
+  }
+  return hip_status(qg::launch_gemv_outlier(a, c, reinterpret_cast<hipStream_t>(stream)));
 }
 
 size_t qgemv_codebook_workspace_bytes(int M, int N, int K) {

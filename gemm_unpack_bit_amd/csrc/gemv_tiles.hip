@@ -128,7 +128,7 @@ constexpr int max_threads(int ng) { return ng == 1 ? 1024 : 512; }
 // bytes it uses.  MFMA lanes of batch rows past M read row M - 1 instead of
 // zeros: those rows of the product are never stored.
 // SP: also add the Tile-COO fp16 outliers of the workgroup's rows (outlier
-// variant): see sparse_prologue below.
+// variant): see sparse_compute below.
 // PLDS (one tile-row of one-group chunks): the workgroup's 16 rows of scales
 // and of packed zero points are two contiguous blocks; they are staged in LDS
 // with coalesced 16-byte loads, so a chunk costs one weight load per lane
@@ -186,27 +186,20 @@ gemv_tiles_kernel(UniformArgs a) {
   float* red = reinterpret_cast<float*>(pbase + psb + pzb);
   const u4* xs = reinterpret_cast<const u4*>(smem);
 
-  // outlier variant: LDS after the partials (see sparse_lds_bytes)
-  constexpr int MS = MFMA ? 16 : MT;  // batch rows a workgroup produces
-  constexpr int CH = MS == 1 ? 2048 : (MS == 2 ? 1024 : 256);  // records per staged chunk
-  constexpr int RW = 16 * TPW;        // weight rows of the workgroup
-  uint32_t* sptr = nullptr;  // [G + 1] tile_ptr of the workgroup's 128-row tile-row
-  uint32_t* srng = nullptr;  // [RW][G] (start | end << 16) of a row's records in a k-tile
-  float* spsum = nullptr;    // [MS][RW] sparse sums
-  uint32_t* recbuf = nullptr;  // [CH] staged records
-  float* prodbuf = nullptr;    // [MS][CH] products v * x
+  // outlier variant (SP): LDS after the partials (see sparse_lds_bytes), per
+  // wave: MFMA, a 16 x 128 fp16 scratch tile, lane-major (lane l's 32 k of
+  // its row at halves 32 l .. 32 l + 31); VALU, run sums [MAXT][MT][64] fp32;
+  // then the first 64 records of MAXT tiles, loaded straight into LDS
+  constexpr int MAXT = 8;
+  constexpr int SPW0 = MFMA ? 4096 : MAXT * MT * 256;
+  constexpr int SPW = SPW0 + MAXT * 256;  // bytes per wave
+  _Float16* sscr = nullptr;
+  float* ssum = nullptr;
   if constexpr (SP) {
     const size_t redb = MFMA ? (size_t)WK * TPW * 64 * 16 : (size_t)WK * TPW * MT * 16 * 4;
-    char* b = reinterpret_cast<char*>(red) + redb;
-    sptr = reinterpret_cast<uint32_t*>(b);
-    b += ((size_t)(G + 1) * 4 + 15) / 16 * 16;
-    srng = reinterpret_cast<uint32_t*>(b);
-    b += (size_t)RW * G * 4;
-    spsum = reinterpret_cast<float*>(b);
-    b += (size_t)MS * RW * 4;
-    recbuf = reinterpret_cast<uint32_t*>(b);
-    b += (size_t)CH * 4;
-    prodbuf = reinterpret_cast<float*>(b);
+    char* b = reinterpret_cast<char*>(red) + redb + (size_t)wave * SPW;
+    sscr = reinterpret_cast<_Float16*>(b);
+    ssum = reinterpret_cast<float*>(b);
   }
 
   // activation row offsets of this lane (group 0, its k-quarter)
@@ -363,9 +356,27 @@ gemv_tiles_kernel(UniformArgs a) {
                             : bload16(rz, i < np16 ? (uint32_t)rt0 * 16u * zrow + 16u * (i - sv) : OOB);
   };
   u4 pfirst;
+  // Outlier variant: slot s of a wave's tiles, in order: chunk s / (TPW NG),
+  // tile-row, group; its global Tile-COO tile index (tiles past the last
+  // group or tile-row hold nothing)
+  const rsrc_t rtp = make_rsrc(a.tile_ptr, ((uint32_t)NT * G + 1u) * 4u);
+  auto tile_of = [&](int s, int& g, int& t) -> uint32_t {
+    constexpr int per = TPW * NG;
+    t = (s % per) / NG;
+    g = (wave + WK * (s / per)) * NG + s % NG;
+    return (uint32_t)(rt0 + t) * G + min(g, G - 1);
+  };
+  // lane 2 s (2 s + 1) loads the start (end) pointer of slot s, s < MAXT: one
+  // load, issued with the activations
+  uint32_t pfetch = 0;
   auto stage_x_issue = [&]() {
     if constexpr (XLDS) x_pass(threadIdx.x, xfirst);
     if constexpr (PLDS) pfirst = p_pass(threadIdx.x);
+    if constexpr (SP) {
+      int g, t;
+      const uint32_t T = tile_of(lane >> 1, g, t) + (lane & 1);
+      pfetch = bload4(rtp, lane < 2 * MAXT ? 4u * T : OOB);
+    }
   };
   auto stage_x = [&]() {
     if constexpr (XLDS) {
@@ -386,93 +397,224 @@ gemv_tiles_kernel(UniformArgs a) {
       if ((int)threadIdx.x < np16) pw[threadIdx.x] = pfirst;
       for (int i = threadIdx.x + blockDim.x; i < np16; i += blockDim.x) pw[i] = p_pass(i);
     }
+    if constexpr (SP) {
+      u4* z = reinterpret_cast<u4*>(sscr);
+#pragma unroll
+      for (int u = 0; u < SPW / 1024; ++u) z[lane + 64 * u] = u4{0u, 0u, 0u, 0u};
+    }
     lds_barrier();
   };
-  // Outliers (FlashQuant abstract: fp16 sparse path fused with the low-bit
-  // dense one, sharing activations and outputs; Tile-COO records): the
-  // workgroup's rows lie in one 128-row tile-row of the Tile-COO encoding.
-  // Pass 1 marks, per row and k-tile, the run of that row's records (records
-  // are sorted by row inside a tile); pass 2 forms the exact products v * x
-  // and each output row sums its own in record order, so the result is
-  // deterministic.  Runs while the first weight stages are in flight.
-  auto sparse_prologue = [&]() {
+  // Outliers (FlashQuant abstract: an fp16 sparse path fused with the
+  // low-bit dense one, sharing activations and outputs; Tile-COO records).
+  // A Tile-COO tile is the 16 x 128 tile of the dense layout, so a wave's
+  // outliers are those of the tiles of its own chunks.  Each wave loads the
+  // tile pointers of its first MAXT tiles with the activations and, right
+  // after the staging barrier, the first 64 records of each straight into LDS
+  // (they arrive during the dense loop).  After the dense loop the records
+  // meet the activations (VALU: per-lane run sums, below; MFMA: scattered
+  // into the wave's zeroed 16 x 128 fp16 scratch in the lane layout of the
+  // dense tile and multiplied like dequantized weights but unscaled, 4 more
+  // matrix-core steps per tile, then cleared).  Every product is exact and
+  // the order of the sums is fixed, so the result is deterministic.  Record
+  // fields are masked into the tile, so malformed records stay in bounds.
+  uint32_t* lrec = reinterpret_cast<uint32_t*>(reinterpret_cast<char*>(ssum) + SPW0);
+  auto slot_ok = [&](int g, int t) { return g < G && rt0 + t < NT; };
+  // start and count of slot s, from the pointers lanes 2 s and 2 s + 1 loaded
+  auto slot_ptr = [&](int s, uint32_t& p0, uint32_t& cnt) {
+    int g, t;
+    (void)tile_of(s, g, t);
+    p0 = __builtin_amdgcn_readlane(pfetch, 2 * s);
+    const uint32_t p1 = __builtin_amdgcn_readlane(pfetch, 2 * s + 1);
+    cnt = slot_ok(g, t) ? min(p1 - p0, 2048u) : 0u;  // (a tile holds at most 2048)
+  };
+  const rsrc_t rrec = make_rsrc(a.tile_rec, (uint32_t)a.nnz * 4u);
+  auto sparse_issue = [&]() {
     if constexpr (SP) {
-      const int KT = G;
-      const uint32_t R = (uint32_t)rt0 / 8u;
-      const uint32_t lr0 = ((uint32_t)rt0 % 8u) * 16u;
-      const rsrc_t rp = make_rsrc(a.tile_ptr, ((uint32_t)((N + 127) / 128) * KT + 1u) * 4u);
-      const rsrc_t rr = make_rsrc(a.tile_rec, (uint32_t)a.nnz * 4u);
-      for (int i = threadIdx.x; i <= KT; i += blockDim.x) sptr[i] = bload4(rp, (R * KT + i) * 4u);
-      for (int i = threadIdx.x; i < RW * KT; i += blockDim.x) srng[i] = 0u;
-      for (int i = threadIdx.x; i < MS * RW; i += blockDim.x) spsum[i] = 0.f;
-      __syncthreads();
-      const uint32_t p0 = sptr[0], p1 = sptr[KT];
-      auto tile_of = [&](uint32_t i) {  // last k-tile whose records start at or before i
-        int lo = 0, hi = KT - 1;
-        while (lo < hi) {
-          const int mid = (lo + hi + 1) >> 1;
-          if (sptr[mid] <= i) lo = mid; else hi = mid - 1;
-        }
-        return lo;
-      };
-      for (uint32_t cs = p0; cs < p1; cs += CH) {  // pass 1
-        const uint32_t ce = min(p1, cs + (uint32_t)CH);
-        for (uint32_t i = cs + threadIdx.x; i < ce; i += blockDim.x) recbuf[i - cs] = bload4(rr, i * 4u);
-        __syncthreads();
-        for (uint32_t i = cs + threadIdx.x; i < ce; i += blockDim.x) {
-          const uint32_t rec = recbuf[i - cs];
-          const uint32_t lr = (rec >> 8) & 0xFFu;
-          if (lr - lr0 >= (uint32_t)RW) continue;  // another workgroup's row
-          const int kt = tile_of(i);
-          const uint32_t tb = sptr[kt], te = sptr[kt + 1];
-          uint16_t* rg = reinterpret_cast<uint16_t*>(srng) + 2 * ((lr - lr0) * KT + kt);
-          bool first = i == tb, last = i + 1 == te;
-          if (!first) {
-            const uint32_t pv = i - 1 >= cs ? recbuf[i - 1 - cs] : bload4(rr, (i - 1) * 4u);
-            first = ((pv >> 8) & 0xFFu) != lr;
-          }
-          if (!last) {
-            const uint32_t nx = i + 1 < ce ? recbuf[i + 1 - cs] : bload4(rr, (i + 1) * 4u);
-            last = ((nx >> 8) & 0xFFu) != lr;
-          }
-          if (first) rg[0] = (uint16_t)(i - tb);
-          if (last) rg[1] = (uint16_t)(i + 1 - tb);
-        }
-        __syncthreads();
-      }
-      for (uint32_t cs = p0; cs < p1; cs += CH) {  // pass 2
-        const uint32_t ce = min(p1, cs + (uint32_t)CH);
-        for (uint32_t i = cs + threadIdx.x; i < ce; i += blockDim.x) {
-          const uint32_t rec = bload4(rr, i * 4u);
-          const uint32_t lr = (rec >> 8) & 0xFFu;
-          if (lr - lr0 >= (uint32_t)RW) continue;
-          const uint32_t col = (uint32_t)tile_of(i) * 128u + (rec & 0xFFu);
-          const float v = h2f((uint16_t)(rec >> 16));
 #pragma unroll
-          for (int m = 0; m < MS; ++m) {
-            float xv = 0.f;  // (batch rows past M: not staged, never stored)
-            if (m0 + m < M) {
-              if constexpr (XLDS) {
-                xv = (float)reinterpret_cast<const _Float16*>(smem)[(size_t)m * XK + col];
-              } else {
-                xv = h2f(bload2(rx, ((uint32_t)(m0 + m) * K + col) * 2u));
-              }
-            }
-            prodbuf[m * CH + (i - cs)] = v * xv;  // exact: a product of two fp16 values
+      for (int s = 0; s < MAXT; ++s) {
+        uint32_t p0, cnt;
+        slot_ptr(s, p0, cnt);
+        // (direct to LDS: no registers held across the dense loop)
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rrec, lrec + 64 * s, 4, (uint32_t)lane < cnt ? (p0 + lane) * 4u : OOB,
+                                                 0, 0, 0);
+      }
+    }
+  };
+  auto bperm = [&](uint32_t v, int src) -> uint32_t {
+    return (uint32_t)__builtin_amdgcn_ds_bpermute(src << 2, (int)v);
+  };
+  // Lanes of a wave exchange data through its LDS scratch; LDS operations of
+  // one wave complete in order, but without a fence the compiler may assume no
+  // other lane wrote what this lane reads (and forward its own earlier store).
+  auto wave_fence = [] { __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront"); };
+  auto sparse_tile = [&](uint32_t p0, uint32_t cnt, int g, int t, uint32_t rec0, bool have0) {
+    if (cnt == 0) return;
+    auto place = [&](uint32_t rec) { return ((((rec >> 8) & 15u) + 16u * ((rec >> 5) & 3u)) << 5) | (rec & 31u); };
+    for (uint32_t b = 0; b < cnt; b += 64) {  // scatter
+      const uint32_t rec = b == 0 && have0 ? rec0 : bload4(rrec, b + lane < cnt ? (p0 + b + lane) * 4u : OOB);
+      if (b + lane < cnt) sscr[place(rec)] = __builtin_bit_cast(_Float16, (uint16_t)(rec >> 16));
+    }
+    wave_fence();  // (the records were scattered by other lanes)
+    const u4* sl = reinterpret_cast<const u4*>(sscr) + 4 * lane;
+    u4 sv[4];
+#pragma unroll
+    for (int v = 0; v < 4; ++v) sv[v] = sl[v];
+    if constexpr (MFMA) {
+      f4 dd = f4{0.f, 0.f, 0.f, 0.f};
+      const int xa = (min(n, XM - 1) * XK + 128 * g + 32 * kq) / 8;
+#pragma unroll
+      for (int v = 0; v < 4; ++v) {
+        const u4 xv = XLDS ? xs[xa + v] : bload16(rx, xoff[0] == OOB ? OOB : xoff[0] + 256u * g + 16u * v);
+        dd = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(h8, xv), __builtin_bit_cast(h8, sv[v]), dd, 0, 0,
+                                                     0);
+      }
+#pragma unroll
+      for (int tt = 0; tt < TPW; ++tt)
+        if (tt == t)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) accm[tt][i] += dd[i];
+    } else {
+#pragma unroll
+      for (int m = 0; m < MT; ++m) {
+        float part = 0.f;
+#pragma unroll
+        for (int v = 0; v < 4; ++v) {
+          const u4 xv = XLDS ? xs[(m * XK + 128 * g + 32 * kq) / 8 + v]
+                             : bload16(rx, xoff[m] == OOB ? OOB : xoff[m] + 256u * g + 16u * v);
+#pragma unroll
+          for (int e = 0; e < 4; ++e) part = dot2(as_h2(sv[v][e]), as_h2(xv[e]), part);
+        }
+#pragma unroll
+        for (int tt = 0; tt < TPW; ++tt)
+          if (tt == t) accv[tt][m] += part;
+      }
+    }
+    for (uint32_t b = 0; b < cnt; b += 64) {  // clear what was written
+      const uint32_t rec = b == 0 && have0 ? rec0 : bload4(rrec, b + lane < cnt ? (p0 + b + lane) * 4u : OOB);
+      if (b + lane < cnt) sscr[place(rec)] = (_Float16)0.0f;
+    }
+    wave_fence();
+  };
+  // VALU engine: the records of a tile (up to 64, this lane's when `valid`)
+  // go to the lane that holds their row and k-quarter, T = row + 16 (col /
+  // 32).  Records are sorted by (row, col), so those of one target are
+  // consecutive: the last lane of each run adds the run's exact products in
+  // record order (ds_bpermute from the lanes before it) and writes the sum to
+  // the target's entry of sums slot `sl`; each lane then adds its entries in
+  // slot order and zeroes them.  Deterministic.
+  const _Float16* xh = reinterpret_cast<const _Float16*>(smem);
+  auto run_sums = [&](uint32_t rec, bool valid, int g, int sl) {
+    const uint32_t lc = rec & 127u;
+    const uint32_t T = valid ? ((rec >> 8) & 15u) + 16u * (lc >> 5) : 64u + lane;  // (distinct dummies)
+    const float v = h2f((uint16_t)(rec >> 16));
+    float prod[MT], acc[MT];
+#pragma unroll
+    for (int m = 0; m < MT; ++m) {
+      float xv;
+      if constexpr (XLDS) xv = (float)xh[m * XK + 128 * g + (int)lc];
+      else xv = h2f(bload2(rx, m0 + m < M ? ((uint32_t)(m0 + m) * K + 128u * g + lc) * 2u : OOB));
+      prod[m] = valid ? v * xv : 0.f;  // exact: a product of two fp16 values
+      acc[m] = prod[m];
+    }
+    // (every cross-lane read is made by the whole wave, outside any condition:
+    // a lane masked off in a branch does not supply its value)
+    const uint32_t Tn = bperm(T, min(lane + 1, 63));
+    const uint32_t Tp = bperm(T, max(lane - 1, 0));
+    const bool last = valid && (lane == 63 || Tn != T);
+    // add the products of the earlier lanes of the run, nearest first
+    bool cont = lane >= 1 && Tp == T;
+    for (int k = 1; __builtin_amdgcn_ballot_w64(cont) != 0; ++k) {  // (runs are short)
+#pragma unroll
+      for (int m = 0; m < MT; ++m) {
+        const float q = __uint_as_float(bperm(__float_as_uint(prod[m]), max(lane - k, 0)));
+        acc[m] = cont ? acc[m] + q : acc[m];
+      }
+      const uint32_t Tk = bperm(T, max(lane - k - 1, 0));
+      cont = cont && lane >= k + 1 && Tk == T;
+    }
+    if (last)
+#pragma unroll
+      for (int m = 0; m < MT; ++m) ssum[(sl * MT + m) * 64 + T] = acc[m];
+  };
+  // (callers fence before: other lanes wrote these entries; and after: other
+  // lanes write them next)
+  auto add_sums = [&](int sl, int t) {
+#pragma unroll
+    for (int m = 0; m < MT; ++m) {
+      float* e = ssum + (sl * MT + m) * 64 + lane;
+      const float v = *e;
+      *e = 0.f;
+#pragma unroll
+      for (int tt = 0; tt < TPW; ++tt)
+        if (tt == t) accv[tt][m] += v;
+    }
+  };
+  // a tile the fast path does not cover: 64 records at a time through slot 0
+  auto sparse_slow = [&](uint32_t p0, uint32_t cnt, int g, int t) {
+    for (uint32_t b = 0; b < cnt; b += 64) {
+      const bool valid = b + lane < cnt;
+      const uint32_t rec = bload4(rrec, valid ? (p0 + b + lane) * 4u : OOB);
+      run_sums(rec, valid, g, 0);
+      wave_fence();
+      add_sums(0, t);
+      wave_fence();
+    }
+  };
+  auto sparse_compute = [&]() {
+    if constexpr (SP) {
+      __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): the records are in LDS (issued long before)
+      const int nci = NC > wave ? (NC - wave + WK - 1) / WK : 0;  // this wave's chunks
+      const int ntl = nci * TPW * NG;
+      if constexpr (MFMA) {
+#pragma unroll
+        for (int s = 0; s < MAXT; ++s) {
+          int g, t;
+          (void)tile_of(s, g, t);
+          uint32_t p0, cnt;
+          slot_ptr(s, p0, cnt);
+          if (s < ntl) sparse_tile(p0, cnt, g, t, lrec[64 * s + lane], true);
+        }
+      } else {
+        // prefetched tiles of 1..64 records: all slots at once (empty ones skipped)
+        uint32_t used = 0;  // wave-uniform slot mask
+#pragma unroll
+        for (int s = 0; s < MAXT; ++s) {
+          int g, t;
+          (void)tile_of(s, g, t);
+          uint32_t p0, cnt;
+          slot_ptr(s, p0, cnt);
+          if (s < ntl && cnt - 1u < 64u) {
+            run_sums(lrec[64 * s + lane], (uint32_t)lane < cnt, g, s);
+            used |= 1u << s;
           }
         }
-        __syncthreads();
-        for (int e = threadIdx.x; e < MS * RW; e += blockDim.x) {
-          const int m = e / RW, rl = e - m * RW;
-          float sum = spsum[e];
-          for (int kt = 0; kt < KT; ++kt) {
-            const uint32_t rg = srng[rl * KT + kt];
-            const uint32_t b = sptr[kt] + (rg & 0xFFFFu), en = sptr[kt] + (rg >> 16);
-            for (uint32_t i = max(b, cs); i < min(en, ce); ++i) sum += prodbuf[m * CH + (i - cs)];
+        if (used) {
+          wave_fence();
+#pragma unroll
+          for (int s = 0; s < MAXT; ++s) {
+            int g, t;
+            (void)tile_of(s, g, t);
+            if (used & (1u << s)) add_sums(s, t);
           }
-          spsum[e] = sum;
+          wave_fence();
         }
-        __syncthreads();
+#pragma unroll
+        for (int s = 0; s < MAXT; ++s) {
+          int g, t;
+          (void)tile_of(s, g, t);
+          uint32_t p0, cnt;
+          slot_ptr(s, p0, cnt);
+          if (s < ntl && cnt > 64u) sparse_slow(p0, cnt, g, t);
+        }
+      }
+      for (int s = MAXT; s < ntl; ++s) {  // tiles past the prefetched ones
+        int g, t;
+        const uint32_t T = tile_of(s, g, t);
+        if (!slot_ok(g, t)) continue;
+        const uint32_t p0 = __builtin_amdgcn_readfirstlane(bload4(rtp, 4u * T));
+        const uint32_t p1 = __builtin_amdgcn_readfirstlane(bload4(rtp, 4u * T + 4u));
+        if constexpr (MFMA) sparse_tile(p0, min(p1 - p0, 2048u), g, t, 0u, false);
+        else sparse_slow(p0, min(p1 - p0, 2048u), g, t);
       }
     }
   };
@@ -483,8 +625,8 @@ gemv_tiles_kernel(UniformArgs a) {
 #pragma unroll
     for (int t = 0; t < D - 1; ++t) load_stage(t, c, ring[t]);
     load_x(c, 0);
-    if constexpr (XLDS) stage_x();
-    sparse_prologue();
+    if constexpr (XLDS || SP) stage_x();
+    sparse_issue();
     for (; c < NC; c += WK) {
 #pragma unroll
       for (int t = 0; t < TPW; ++t) {
@@ -506,7 +648,7 @@ gemv_tiles_kernel(UniformArgs a) {
 #pragma unroll
     for (int i = 0; i < D - 1; ++i) load_stage(0, c + i * WK, ring[i]);
     stage_x();
-    sparse_prologue();
+    sparse_issue();
     for (; c < NC; c += D * WK) {
 #pragma unroll
       for (int i = 0; i < D; ++i) {
@@ -521,8 +663,8 @@ gemv_tiles_kernel(UniformArgs a) {
     // (a chunk past the last reads zeros and adds nothing)
     load_stage(0, c, ring[0]);
     load_x(c, 0);
-    if constexpr (XLDS || PLDS) stage_x();
-    sparse_prologue();
+    if constexpr (XLDS || PLDS || SP) stage_x();
+    sparse_issue();
     for (; c < NC; c += 2 * WK) {
       load_stage(0, c + WK, ring[1]);
       load_x(c + WK, 1);
@@ -537,6 +679,8 @@ gemv_tiles_kernel(UniformArgs a) {
     }
   }
 
+  sparse_compute();
+
   if constexpr (MFMA) {
     // lane l holds result rows m = 4 (l / 16) + i of weight row l % 16
     f4* r4 = reinterpret_cast<f4*>(red);
@@ -549,7 +693,6 @@ gemv_tiles_kernel(UniformArgs a) {
       float sum = 0.f;
       for (int w = 0; w < WK; ++w) sum += r4[(w * TPW + t) * 64 + l][i];
       const int row = (rt0 + t) * 16 + r;
-      if constexpr (SP) sum += spsum[m * RW + t * 16 + r];
       if (m < M && row < N) a.y[(size_t)m * N + row] = f2h(sum);
     }
   } else {
@@ -564,7 +707,6 @@ gemv_tiles_kernel(UniformArgs a) {
     reduce_waves(red, TPW * MT * 16, WK, [&](int e, float sum) {
       const int r = e & 15, m = (e >> 4) % MT, t = (e >> 4) / MT;
       const int row = (rt0 + t) * 16 + r;
-      if constexpr (SP) sum += spsum[m * RW + t * 16 + r];
       if (m0 + m < M && row < N) a.y[(size_t)(m0 + m) * N + row] = f2h(sum);
     });
   }
@@ -579,13 +721,10 @@ size_t tiles_lds_bytes(bool mfma, int mt, int tpw, int wk) {
 constexpr size_t XLDS_MAX = 64 * 1024 + 128;
 size_t xlds_bytes(bool mfma, int mt, int M, int K) { return (size_t)(mfma ? (M < 16 ? M : 16) : mt) * (K + 32) * 2; }
 
-// LDS of the outlier variant beyond the dense kernel's (mirrors the kernel's
-// layout: tile pointers, run table, sparse sums, record and product chunks)
-size_t sparse_lds_bytes(bool mfma, int mt, int tpw, int K) {
-  const size_t G = K / 128, ms = mfma ? 16 : mt, rw = 16 * tpw;
-  const size_t ch = ms == 1 ? 2048 : (ms == 2 ? 1024 : 256);
-  return (4 * (G + 1) + 15) / 16 * 16 + 4 * rw * G + 4 * ms * rw + 4 * ch + 4 * ch * ms;
-}
+// LDS of the outlier variant beyond the dense kernel's, per wave: MFMA, a
+// 16 x 128 fp16 scratch tile; VALU, 8 slots of run sums for MT x 64 lanes;
+// then 8 x 64 prefetched records
+size_t sparse_lds_bytes(bool mfma, int mt, int wk) { return (size_t)wk * ((mfma ? 4096 : 8 * mt * 256) + 8 * 256); }
 
 constexpr size_t LDS_ALL = 160 * 1024;  // gfx950 LDS per workgroup
 
@@ -647,7 +786,7 @@ hipError_t launch_t(const UniformArgs& a, const TileCfg& c, hipStream_t s) {
                       reinterpret_cast<uintptr_t>(a.zeros) % 16 == 0 && (size_t)a.N * G * 2 % 16 == 0 &&
                       zbytes % 16 == 0;
     const size_t lds = (xlds ? xl : 0) + (plds ? params_lds_bytes(BITS, a.K) : 0) + red +
-                       (SP ? sparse_lds_bytes(MFMA, MT, TPW, a.K) : 0);
+                       (SP ? sparse_lds_bytes(MFMA, MT, c.wk) : 0);
     if (lds > LDS_ALL) return hipErrorInvalidValue;
     // chunk scales in one load: whole chunks and a 2*NG-byte aligned base
     const bool sal = (a.K / 128) % NG == 0 && reinterpret_cast<uintptr_t>(a.scales) % (2 * NG) == 0;
@@ -762,13 +901,13 @@ TileCfg pick_tiles(int bits, int M, int N, int K, bool mfma) {
   return c;
 }
 
-// Outlier variant: the uniform W4 dense shapes, restricted to the one- and
-// two-tile-row forms (whose workgroups cover at most 32 rows of a 128-row
-// Tile-COO tile-row).
+// Outlier variant: the uniform W4 dense shapes, restricted to the one-tile-row
+// forms (2- and 4-deep rings, the latter VALU only) and two tile-rows with
+// four-group chunks.
 TileCfg pick_outlier(int M, int N, int K, bool mfma) {
   TileCfg c = pick_tiles(4, M, N, K, mfma);
   if (c.tpw == 1) {
-    c.v = 3;
+    if (mfma || c.v != 4) c.v = 3;
   } else {
     c.tpw = 2;
     c.v = 0;
@@ -786,9 +925,11 @@ hipError_t launch_gemv_outlier(const UniformArgs& a, const TileCfg& c, hipStream
     if (key == 20) return launch_t<4, true, 1, 0, 2, true>(a, c, s);
   } else if (c.mt == 1) {
     if (key == 13) return launch_t<4, false, 1, 3, 1, true>(a, c, s);
+    if (key == 14) return launch_t<4, false, 1, 4, 1, true>(a, c, s);
     if (key == 20) return launch_t<4, false, 1, 0, 2, true>(a, c, s);
   } else if (c.mt == 2) {
     if (key == 13) return launch_t<4, false, 2, 3, 1, true>(a, c, s);
+    if (key == 14) return launch_t<4, false, 2, 4, 1, true>(a, c, s);
     if (key == 20) return launch_t<4, false, 2, 0, 2, true>(a, c, s);
   }
   return hipErrorInvalidValue;

@@ -2,8 +2,9 @@
 // outliers kept in high precision and encoded per tile, "Tile-COO", so the
 // sparse path works tile by tile beside the dense one).
 //
-// Format (128 x 128 tiles over the N x K weight):
-//   tile t = (row / 128) * KT + col / 128, KT = ceil(K / 128), row-tile-major;
+// Format (16 x 128 tiles over the N x K weight: the tile of the dense layout,
+// 16 rows of one quant group):
+//   tile t = (row / 16) * KT + col / 128, KT = ceil(K / 128), row-tile-major;
 //   tile_ptr[t] .. tile_ptr[t + 1] (exclusive prefix sum) index tile_rec;
 //   record = (fp16 value bits << 16) | (local_row << 8) | local_col, sorted by
 //   (local_row, local_col) inside a tile.
@@ -15,7 +16,7 @@
 
 namespace {
 
-constexpr int TILE = 128;
+constexpr int TILE_R = 16, TILE_C = 128;
 
 }  // namespace
 
@@ -23,14 +24,14 @@ extern "C" {
 
 size_t qgemv_tilecoo_ptr_len(int N, int K) {
   if (N < 1 || K < 1) return 0;
-  return (size_t)((N + TILE - 1) / TILE) * (size_t)((K + TILE - 1) / TILE) + 1;
+  return (size_t)((N + TILE_R - 1) / TILE_R) * (size_t)((K + TILE_C - 1) / TILE_C) + 1;
 }
 
 int qgemv_tilecoo_encode(int N, int K, int64_t nnz, const int32_t* rows, const int32_t* cols,
                          const uint16_t* val_bits, uint32_t* tile_ptr, uint32_t* tile_rec) {
   if (N < 1 || K < 1 || nnz < 0 || nnz > (int64_t)N * K || nnz > 0x7fffffff) return QGEMV_ERR_SHAPE;
   if (!tile_ptr || (nnz > 0 && (!rows || !cols || !val_bits || !tile_rec))) return QGEMV_ERR_NULL;
-  const int KT = (K + TILE - 1) / TILE;
+  const int KT = (K + TILE_C - 1) / TILE_C;
   const size_t T = qgemv_tilecoo_ptr_len(N, K) - 1;
   // sort key: tile, local row, local col (unique per position)
   std::vector<uint64_t> key((size_t)nnz);
@@ -38,8 +39,8 @@ int qgemv_tilecoo_encode(int N, int K, int64_t nnz, const int32_t* rows, const i
     const int32_t r = rows[i], c = cols[i];
     if (r < 0 || r >= N || c < 0 || c >= K) return QGEMV_ERR_VALUE;
     if ((val_bits[i] & 0x7C00u) == 0x7C00u) return QGEMV_ERR_VALUE;  // inf or NaN
-    const uint64_t t = (uint64_t)(r / TILE) * KT + (uint64_t)(c / TILE);
-    key[i] = (t << 48) | ((uint64_t)(r % TILE) << 40) | ((uint64_t)(c % TILE) << 32) | (uint64_t)i;
+    const uint64_t t = (uint64_t)(r / TILE_R) * KT + (uint64_t)(c / TILE_C);
+    key[i] = (t << 48) | ((uint64_t)(r % TILE_R) << 40) | ((uint64_t)(c % TILE_C) << 32) | (uint64_t)i;
   }
   std::sort(key.begin(), key.end());
   for (int64_t i = 1; i < nnz; ++i)

@@ -200,18 +200,20 @@ int qgemv_lut4(int M, int N, int K, const uint16_t *x, const uint32_t *wq,
  * given, also at outlier positions); S holds fp16 outliers at unique
  * positions, encoded by qgemv_tilecoo_encode:
  *
- *   tile_ptr [dev] uint32 [qgemv_tilecoo_ptr_len(N, K)]: 128 x 128 tiles in
- *                  row-tile-major order (tile (r/128) * ceil(K/128) + c/128),
- *                  exclusive prefix sum of record counts; tile_ptr[last] = nnz
- *   tile_rec [dev] uint32 [nnz]: (fp16 value bits << 16) | (row % 128) << 8 |
+ *   tile_ptr [dev] uint32 [qgemv_tilecoo_ptr_len(N, K)]: 16 x 128 tiles (the
+ *                  tile of the dense layout) in row-tile-major order (tile
+ *                  (r/16) * ceil(K/128) + c/128), exclusive prefix sum of
+ *                  record counts; tile_ptr[last] = nnz
+ *   tile_rec [dev] uint32 [nnz]: (fp16 value bits << 16) | (row % 16) << 8 |
  *                  (col % 128), sorted by (row, col) inside a tile; may be
  *                  NULL when nnz == 0
  *   nnz            number of records (0 <= nnz <= N*K, nnz*4 < 2^31)
  *
  * Other arguments, shapes and errors as qgemv_uniform (W4, `path` selects the
  * dense engine); tile_ptr and tile_rec 4-byte aligned.  Records are read as
- * given (their validity is the encoder's job).  Asynchronous, deterministic,
- * no allocation.
+ * given (their validity is the encoder's job; malformed ones give wrong
+ * values, never an out-of-bounds access).  Asynchronous, deterministic, no
+ * allocation.
  * ------------------------------------------------------------------------ */
 int qgemv_outlier(int path, int M, int N, int K, const uint16_t *x, const uint32_t *wq,
                   const uint16_t *scales, const uint32_t *zeros, const uint32_t *tile_ptr,
@@ -254,7 +256,7 @@ int qgemv_codebook(int M, int N, int K, const uint16_t *x, const uint32_t *codes
  * never splits, or on bad arguments). */
 size_t qgemv_codebook_workspace_bytes(int M, int N, int K);
 
-/* Entries of tile_ptr for an N x K weight: ceil(N/128) * ceil(K/128) + 1
+/* Entries of tile_ptr for an N x K weight: ceil(N/16) * ceil(K/128) + 1
  * (0 on bad arguments). */
 size_t qgemv_tilecoo_ptr_len(int N, int K);
 

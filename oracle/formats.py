@@ -28,11 +28,12 @@ A wave-wide load of one word group per lane is then one contiguous block.
 Tile-COO (outlier variant; FlashQuant abstract: "Tile-COO outlier encoding")
 ---------------------------------------------------------------------------
 The page names the encoding but gives no fields.  Reading taken: tiles of
-128 x 128 weights, numbered row-tile-major then k-tile
-(``t = (r // 128) * ceil(K/128) + c // 128``); one uint32 per outlier with
-bits 0-7 = local column, bits 8-15 = local row, bits 16-31 = the fp16 bits of
-the value; records sorted by (tile, local row, local col); ``tile_ptr`` is
-the exclusive prefix sum of per-tile counts (length tiles + 1).
+16 rows x 128 k -- the tile of the dense layout, one quant group of 16 rows --
+numbered row-tile-major then k-tile (``t = (r // 16) * ceil(K/128) + c // 128``);
+one uint32 per outlier with bits 0-7 = local column, bits 8-15 = local row,
+bits 16-31 = the fp16 bits of the value; records sorted by (tile, local row,
+local col); ``tile_ptr`` is the exclusive prefix sum of per-tile counts
+(length tiles + 1).
 
 Codebook code tiles (codebook variant)
 --------------------------------------
@@ -181,7 +182,7 @@ def unpack_tiles(words: np.ndarray, bits: int, rows: int, cols: int) -> np.ndarr
 # ----------------------------------------------------------------------------
 # Tile-COO
 # ----------------------------------------------------------------------------
-TILE = 128
+TILE_R, TILE_C = 16, 128
 
 
 def tilecoo_encode(N, K, rows, cols, vals_f16):
@@ -197,12 +198,12 @@ def tilecoo_encode(N, K, rows, cols, vals_f16):
         raise ValueError("duplicate coordinate")
     if rows.size and not np.all(np.isfinite(vals.astype(np.float64))):
         raise ValueError("non-finite outlier value")
-    KT = (K + TILE - 1) // TILE
-    NT = (N + TILE - 1) // TILE
+    KT = (K + TILE_C - 1) // TILE_C
+    NT = (N + TILE_R - 1) // TILE_R
     entries = []
     for r, c, v in zip(rows.tolist(), cols.tolist(), vals.view(np.uint16).tolist()):
-        t = (r // TILE) * KT + c // TILE
-        lr, lc = r % TILE, c % TILE
+        t = (r // TILE_R) * KT + c // TILE_C
+        lr, lc = r % TILE_R, c % TILE_C
         entries.append((t, lr, lc, (v << 16) | (lr << 8) | lc))
     entries.sort()
     counts = [0] * (NT * KT)
@@ -217,14 +218,14 @@ def tilecoo_encode(N, K, rows, cols, vals_f16):
 
 def tilecoo_decode(N, K, tile_ptr, tile_rec):
     """(tile_ptr, tile_rec) -> (rows int64, cols int64, vals fp16) in record order."""
-    KT = (K + TILE - 1) // TILE
+    KT = (K + TILE_C - 1) // TILE_C
     rows, cols, vals = [], [], []
     for t in range(len(tile_ptr) - 1):
         tr, tk = divmod(t, KT)
         for i in range(int(tile_ptr[t]), int(tile_ptr[t + 1])):
             rec = int(tile_rec[i])
-            rows.append(tr * TILE + ((rec >> 8) & 0xFF))
-            cols.append(tk * TILE + (rec & 0xFF))
+            rows.append(tr * TILE_R + ((rec >> 8) & 0xFF))
+            cols.append(tk * TILE_C + (rec & 0xFF))
             vals.append(rec >> 16)
     return (np.array(rows, dtype=np.int64), np.array(cols, dtype=np.int64),
             np.array(vals, dtype=np.uint16).view(np.float16))

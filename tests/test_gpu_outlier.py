@@ -114,3 +114,36 @@ def test_outlier_dense_tiles():
     y = host(q.outlier(dev(c["x"]), wq, s, zq, tp, tr))
     y_ref, A = ref.gemv_outlier(c["x"], c["codes"], c["scales"], c["zeros"], c["o_rows"], c["o_cols"], c["o_vals"])
     assert_within(y, y_ref, A, "outlier dense tile")
+
+
+@pytest.mark.parametrize("path,M", [(q.PATH_VALU, 1), (q.PATH_VALU, 2), (q.PATH_MFMA, 5)])
+@pytest.mark.parametrize("N,K", [(300, 2176), (64, 4096)])
+def test_outlier_every_launch_shape(monkeypatch, path, M, N, K):
+    """Every launch shape the outlier kernel takes, forced through
+    QGEMV_OUTLIER_CFG: few waves give a wave more tiles than it prefetches
+    records for; ragged N puts outliers in a partial tile-row."""
+    say("outlier launch shapes", path, M, N, K)
+    c = synth.outlier_case(N + K + M, M, N, K, frac=0.01)
+    extra = [(N - 1, 5), (N - 1, K - 1), (0, K - 1)]  # last row and last column
+    have = set(zip(c["o_rows"].tolist(), c["o_cols"].tolist()))
+    add = [rc for rc in extra if rc not in have]
+    if add:
+        c["o_rows"] = np.concatenate([c["o_rows"], np.array([r for r, _ in add], dtype=np.int32)])
+        c["o_cols"] = np.concatenate([c["o_cols"], np.array([k for _, k in add], dtype=np.int32)])
+        c["o_vals"] = np.concatenate([c["o_vals"], np.full(len(add), 0.75, dtype=np.float16)])
+    wq, s, zq, tp, tr = _upload(c, N, K)
+    x = dev(c["x"])
+    y_ref, A = ref.gemv_outlier(c["x"], c["codes"], c["scales"], c["zeros"], c["o_rows"], c["o_cols"], c["o_vals"])
+    ran = []
+    for tpw, v in ((1, 3), (1, 4), (2, 0)):
+        for wk in (1, 2, 4, 8, 16):
+            for mt in ((1, 2) if path == q.PATH_VALU else (1,)):
+                cfg = f"{tpw},{wk},{mt},{v}"
+                monkeypatch.setenv("QGEMV_OUTLIER_CFG", cfg)
+                try:
+                    y = host(q.outlier(x, wq, s, zq, tp, tr, path))
+                except q.QgemvError:
+                    continue
+                assert_within(y, y_ref, A, f"outlier M={M} N={N} K={K} path={path} cfg={cfg}")
+                ran.append(cfg)
+    assert len(ran) >= 8, ran

@@ -103,20 +103,23 @@ def test_plain_packing_rejects_bad_codes():
 
 
 def test_tilecoo_hand_example():
-    # N=200 (2 row tiles, the second ragged), K=256 (2 k tiles)
+    # N=200 (13 row tiles of 16, the last ragged), K=256 (2 k tiles): 26 tiles
     rows = [130, 0, 5, 5, 199]
     cols = [255, 3, 200, 1, 0]
     vals = np.array([1.5, -2.0, 0.25, 3.0, -0.125], dtype=np.float16)
     ptr, rec = formats.tilecoo_encode(200, 256, rows, cols, vals)
-    # tiles: t0=(0,0): (0,3),(5,1)  t1=(0,1): (5,200)  t2=(1,0): (199,0)  t3=(1,1): (130,255)
-    assert ptr.tolist() == [0, 2, 3, 4, 5]
+    # tiles (row tile, k tile) -> t = 2 rt + kt:
+    #   t0 = (0,0): (0,3), (5,1)   t1 = (0,1): (5,200)
+    #   t17 = (8,1): (130,255)     t24 = (12,0): (199,0)
+    want_ptr = [0, 2] + [3] * 16 + [4] * 7 + [5] * 2
+    assert len(want_ptr) == 27 and ptr.tolist() == want_ptr
     vb = vals.view(np.uint16)
     want = [
         (int(vb[1]) << 16) | (0 << 8) | 3,
         (int(vb[3]) << 16) | (5 << 8) | 1,
         (int(vb[2]) << 16) | (5 << 8) | (200 - 128),
-        (int(vb[4]) << 16) | ((199 - 128) << 8) | 0,
         (int(vb[0]) << 16) | ((130 - 128) << 8) | (255 - 128),
+        (int(vb[4]) << 16) | ((199 - 192) << 8) | 0,
     ]
     assert rec.tolist() == want
     r2, c2, v2 = formats.tilecoo_decode(200, 256, ptr, rec)
@@ -127,7 +130,7 @@ def test_tilecoo_hand_example():
 def test_tilecoo_roundtrip_and_errors():
     case = synth.outlier_case(7, 1, 384, 512, frac=0.01)
     ptr, rec = formats.tilecoo_encode(384, 512, case["o_rows"], case["o_cols"], case["o_vals"])
-    assert len(ptr) == 3 * 4 + 1 and int(ptr[-1]) == len(case["o_rows"])
+    assert len(ptr) == 24 * 4 + 1 and int(ptr[-1]) == len(case["o_rows"])
     assert np.all(np.diff(ptr.astype(np.int64)) >= 0)
     r, c, v = formats.tilecoo_decode(384, 512, ptr, rec)
     a = sorted(zip(r.tolist(), c.tolist(), v.view(np.uint16).tolist()))

@@ -32,7 +32,7 @@ def test_encoder_matches_oracle(N, K, frac):
 
 def test_encoder_empty_and_unsorted_input():
     ptr, rec = q.tilecoo_encode(256, 256, [], [], [])
-    assert ptr.tolist() == [0, 0, 0, 0, 0] and rec.size == 0
+    assert ptr.tolist() == [0] * (16 * 2 + 1) and rec.size == 0  # 16 row tiles x 2 k tiles
     rows, cols = [5, 1, 200, 1], [300, 7, 2, 3]
     vals = np.array([1.5, -2, 0.25, 3], dtype=np.float16)
     ptr, rec = q.tilecoo_encode(256, 384, rows, cols, vals)
