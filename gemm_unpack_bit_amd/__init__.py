@@ -263,8 +263,9 @@ def codebook(x, codes, cb, scales, ws=None, out=None):
 
     codes: int32 words of the [N, K/4] uint8 code matrix packed with
     pack(codes, 8, LAYOUT_ROWS64); cb [256, 4] fp16; scales [N, K/128] fp16;
-    ws: optional zero-filled workspace (uint8/int32 tensor) of
-    codebook_workspace_bytes(M, N, K) bytes, reused across calls."""
+    ws: optional scratch workspace (a uint8/int32 tensor, contents not
+    needed) of codebook_workspace_bytes(M, N, K) bytes, reusable across
+    calls on one stream; with it K is split across workgroups."""
     torch = _torch()
     _need(x, torch.float16, "x")
     _need(codes, torch.int32, "codes")

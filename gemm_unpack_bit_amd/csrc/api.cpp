@@ -224,7 +224,7 @@ int qgemv_outlier(int path, int M, int N, int K, const uint16_t* x, const uint32
 
 size_t qgemv_codebook_workspace_bytes(int M, int N, int K) {
   if (M < 1 || M > QGEMV_MAX_M || N < 1 || K < 512 || K % 512) return 0;
-  return qg::codebook_ws_bytes(qg::pick_codebook(M, N, K), M, N);
+  return qg::codebook_ws_bytes(qg::pick_codebook(M, N, K), M, N, K);
 }
 
 int qgemv_codebook(int M, int N, int K, const uint16_t* x, const uint32_t* codes, const uint16_t* codebook,
@@ -243,24 +243,30 @@ int qgemv_codebook(int M, int N, int K, const uint16_t* x, const uint32_t* codes
       overlaps(y, ybytes, codebook, 256 * 4 * 2) || overlaps(y, ybytes, scales, (size_t)N * (K / 128) * 2) ||
       (ws && overlaps(y, ybytes, ws, ws_bytes)))
     return QGEMV_ERR_VALUE;
+  if (ws && (overlaps(ws, ws_bytes, x, (size_t)M * K * 2) ||
+             overlaps(ws, ws_bytes, codes, words(8, QGEMV_LAYOUT_ROWS64, N, K / 4) * 4) ||
+             overlaps(ws, ws_bytes, codebook, 256 * 4 * 2) || overlaps(ws, ws_bytes, scales, (size_t)N * (K / 128) * 2)))
+    return QGEMV_ERR_VALUE;
   qg::CodebookCfg c = qg::pick_codebook(M, N, K);
-  if (const char* e = std::getenv("QGEMV_CODEBOOK_CFG")) {  // tuning override "wk,ks"
-    int wk, ks;
-    if (std::sscanf(e, "%d,%d", &wk, &ks) == 2) {
+  // tuning override: "1,wk,pp,r" (stationary) or "0,wk,ks" (sequential)
+  if (const char* e = std::getenv("QGEMV_CODEBOOK_CFG")) {
+    int kind, wk, p1, p2 = 0;
+    if (std::sscanf(e, "%d,%d,%d,%d", &kind, &wk, &p1, &p2) >= 3) {
       c.wk = wk;
-      c.ks = ks;
+      if (kind == 1) {
+        c.pp = p1;
+        c.r = p2;
+        c.ks = 1;
+      } else {
+        c.pp = 0;
+        c.r = 0;
+        c.ks = p1;
+      }
     }
   }
-  const size_t need = qg::codebook_ws_bytes(c, M, N);
-  // no room to split K (or more counters than the area holds): one pass per row block
-  if (need > 0 && (!ws || ws_bytes < need || (size_t)M * qg::codebook_row_blocks(c, N) > qg::CB_COUNTERS))
-    c.ks = 1;
-  float* wsf = reinterpret_cast<float*>(ws);
-  // counters: the last CB_COUNTERS words of the caller's buffer
-  uint32_t* cnt = c.ks > 1 ? reinterpret_cast<uint32_t*>(reinterpret_cast<char*>(ws) + (ws_bytes & ~(size_t)3) -
-                                                          qg::CB_COUNTERS * 4)
-                           : nullptr;
-  qg::CodebookArgs a{M, N, K, x, codes, codebook, scales, y, c.ks > 1 ? wsf : nullptr, cnt};
+  const size_t need = qg::codebook_ws_bytes(c, M, N, K);
+  if (need > 0 && (!ws || ws_bytes < need)) c = qg::codebook_fallback();  // no room for partial sums
+  qg::CodebookArgs a{M, N, K, x, codes, codebook, scales, y, reinterpret_cast<float*>(ws)};
   return hip_status(qg::launch_gemv_codebook(a, c, reinterpret_cast<hipStream_t>(stream)));
 }
 

@@ -14,57 +14,67 @@
 //  * Codes are an [N, K/4] uint8 matrix in the 64-row layout
 //    (qgemv_pack(8, QGEMV_LAYOUT_ROWS64, N, K/4)): a 1 KB tile holds 16
 //    consecutive codes of 64 rows, lane l of a wave-wide 16-byte load getting
-//    its own row's 16 codes.  A "quad" of 4 quant groups (128 segments, 512 k)
-//    is 8 consecutive tiles of a row block, 8 KB contiguous.
-//  * Psumbook of a quad in LDS, segment-major: fp16 P[s][c] at byte
-//    512 s + 2 c (64 KB).  All lanes of a wave look up the same segment s at
-//    once, so s is the instruction's immediate offset and the lane address is
-//    2 * code; the bank follows the (random) code, not the segment.  Two
-//    lookups are summed into the fp32 partial by one v_dot2 against (1, 1).
-//    Each lane owns one weight row, so no cross-lane reduction is needed.
+//    its own row's 16 codes.  A "pair" of 2 quant groups (64 segments, 256 k)
+//    is 4 consecutive tiles of a row block, 4 KB contiguous.
+//  * Psumbook of a pair in LDS, segment-major: fp16 P[s][c] at byte
+//    520 s + 2 c (33 KB, so 4 workgroups share a CU and keep its LDS busy
+//    while one of them waits at a barrier).  All lanes of a wave look up the
+//    same segment s at once, so s is the instruction's immediate offset and
+//    the lane address is 2 * code; the bank follows the (random) code, not the
+//    segment.  Two lookups are summed into the fp32 partial by one v_dot2
+//    against (1, 1).  Each lane owns one weight row, so no cross-lane
+//    reduction is needed.  The random 64-lane lookups are the bound: the LDS
+//    serves one about every 3 to 4 clocks per CU.
 //  * Build on the matrix cores: one v_mfma_f32_32x32x8_f16 gives P for 32
-//    segments x 32 centroids (A = activation segments, B = codebook rows, the
-//    v = 4 dims padded to 8 with zeros); 32 of them per quad, spread over the
-//    waves of the workgroup.
+//    centroids x 32 segments (A = codebook rows, B = activation segments, the
+//    v = 4 dims padded to 8 with zeros); 16 of them per pair, spread over the
+//    waves of the workgroup.  Each lane then holds 4 consecutive centroids of
+//    one segment per register quartet and writes them with one 8-byte store;
+//    the segment rows are 520 bytes apart (256 fp16 + 8 bytes of padding), so
+//    the 32 segments of a store land in distinct banks.  Each wave keeps the
+//    codebook rows it multiplies in registers for the whole kernel.
 //  * Work split: a workgroup holds WK waves, one 64-row block each, and a K
-//    range of whole quads; one build serves 64 * WK rows.  The K ranges of a
-//    row block are reduced in a fixed order by the last of their workgroups
-//    to finish (a counter per row block in the caller's workspace), so the
-//    result is deterministic.  Batch rows are grid z.
-//  * Per quad: build / LDS barrier / lookups, with the next quad's codes,
-//    scales and activation segments in flight meanwhile.  The barriers wait
-//    for LDS traffic only, so those prefetches stay outstanding across them.
+//    range of whole pairs; one build serves 64 * WK rows.  With K split, each
+//    range writes fp32 partial sums to the caller's workspace and a second,
+//    small kernel adds the ranges of every output in K order, so the result
+//    is deterministic and no workgroup waits on another.  Batch rows are
+//    grid z.
+//  * Per pair: LDS barrier / build / LDS barrier / lookups, with the next
+//    pair's codes, scales and activation segments in flight meanwhile.  The
+//    barriers wait for LDS traffic only, so those prefetches stay outstanding
+//    across them.
+#include <algorithm>
+
 #include "common.hpp"
 #include "kernels.hpp"
 
 namespace qg {
 namespace {
 
-constexpr uint32_t PSUM_BYTES = 128u * 256u * 2u;  // 128 segments x 256 centroids x fp16
-constexpr uint32_t CB_BYTES = 256u * 4u * 2u;      // the codebook, staged
+constexpr uint32_t PSTRIDE = 520u;              // bytes per segment row: 256 fp16 + 8 of padding
+constexpr uint32_t PSUM_BYTES = 64u * PSTRIDE;  // the Psumbook of one pair
 
 typedef _Float16 h4v __attribute__((ext_vector_type(4)));
 
-// SAL: the scales base is 8-byte aligned, so a quad's 4 scales of a row are
-// one load (K is a multiple of 512, so every row's quad starts 8-aligned too).
-template <bool SAL>
-__global__ void __launch_bounds__(1024) gemv_codebook_kernel(CodebookArgs a) {
-  // LDS: [Psumbook 64 KB][codebook 2 KB][flag]
-  extern __shared__ __attribute__((aligned(16))) uint32_t lsm[];
+// NSB: activation segment blocks each wave multiplies per pair (2 / min(WK, 2)).
+// SAL: the scales base is 4-byte aligned, so a pair's 2 scales of a row are
+// one load (K is a multiple of 512, so every row's pair starts 4-aligned too).
+template <int NSB, bool SAL>
+__global__ void __launch_bounds__(NSB == 1 ? 1024 : 64) gemv_codebook_seq_kernel(CodebookArgs a) {
+  __shared__ __attribute__((aligned(16))) uint32_t lsm[PSUM_BYTES / 4];
   char* const lds = reinterpret_cast<char*>(lsm);
-  uint32_t* const flag = reinterpret_cast<uint32_t*>(lds + PSUM_BYTES + CB_BYTES);
 
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int WK = blockDim.x >> 6;
   const int M = a.M, N = a.N, K = a.K;
   const int G = K / 128;   // quant groups
-  const int QN = K / 512;  // quads
+  const int HN = K / 256;  // pairs
   const int NCB = K / 64;  // 16-code tiles per row block
   const int NB = (N + 63) / 64;
   const int m = blockIdx.z;
   const int ks = blockIdx.y, KS = gridDim.y;
-  const int q0 = (QN * ks) / KS, q1 = (QN * (ks + 1)) / KS;
+  const int h0 = (HN * ks) / KS, h1 = (HN * (ks + 1)) / KS;
   const int rb = blockIdx.x * WK + wave;  // this wave's 64-row block
   const uint32_t row = (uint32_t)rb * 64u + lane;
   const bool rv = rb < NB && row < (uint32_t)N;
@@ -74,89 +84,111 @@ __global__ void __launch_bounds__(1024) gemv_codebook_kernel(CodebookArgs a) {
   const rsrc_t rx = make_rsrc(a.x, (uint32_t)M * K * 2u);
 
   struct St {
-    u4 c[8];        // 8 tiles x 16 codes of this lane's row
-    uint16_t s[4];  // the quad's 4 group scales of this row
+    u4 c[4];        // 4 tiles x 16 codes of this lane's row
+    uint16_t s[2];  // the pair's 2 group scales of this row
   };
   // Loads are unconditional, with every choice in the offsets: a wave past
   // the last row block reads zero codes, a row past N zero scales.  The
-  // prefetch past the K range re-reads the range's last quad (never used),
-  // so that the quad index only ever moves the wave-uniform offsets.
+  // prefetch past the K range re-reads the range's last pair (never used),
+  // so that the pair index only ever moves the wave-uniform offsets.
   const uint32_t vcode = rb < NB ? 16u * lane : OOB;
   const uint32_t vscale = rv ? row * (uint32_t)G * 2u : OOB;
-  auto load_stage = [&](int q, St& st) {
-    const uint32_t qc = (uint32_t)min(q, q1 - 1);
-    const uint32_t sw = __builtin_amdgcn_readfirstlane(((uint32_t)min(rb, NB - 1) * NCB + 8u * qc) * 1024u);
+  auto load_stage = [&](int h, St& st) {
+    const uint32_t hc = (uint32_t)min(h, h1 - 1);
+    const uint32_t sw = __builtin_amdgcn_readfirstlane(((uint32_t)min(rb, NB - 1) * NCB + 4u * hc) * 1024u);
 #pragma unroll
-    for (int i = 0; i < 8; ++i) st.c[i] = bload16<CPOL_NT>(rc, vcode + 1024u * i, sw);
+    for (int i = 0; i < 4; ++i) st.c[i] = bload16<CPOL_NT>(rc, vcode + 1024u * i, sw);
     if constexpr (SAL) {
-      const u2 v = __builtin_bit_cast(u2, __builtin_amdgcn_raw_buffer_load_b64(rs, vscale, 8u * qc, 0));
-#pragma unroll
-      for (int g = 0; g < 4; ++g) st.s[g] = (uint16_t)(v[g / 2] >> (16 * (g % 2)));
+      const uint32_t v = bload4(rs, vscale, 4u * hc);
+      st.s[0] = (uint16_t)v;
+      st.s[1] = (uint16_t)(v >> 16);
     } else {
 #pragma unroll
-      for (int g = 0; g < 4; ++g) st.s[g] = bload2(rs, vscale, 8u * qc + 2u * g);
+      for (int g = 0; g < 2; ++g) st.s[g] = bload2(rs, vscale, 4u * hc + 2u * g);
     }
   };
 
-  // build assignment: wave w computes blocks p = w, w + WK, ... (p < 32) of 32
-  // segments (sb = p % 4) x 32 centroids (cb = p / 4); WK % 4 == 0 keeps sb
-  // fixed per wave, so each wave needs one activation operand per quad
-  const int sbw = wave & 3;
+  // Build assignment: the 16 MFMA blocks of a pair are 2 segment blocks (sb)
+  // x 8 centroid blocks (cb).  With W2 = min(WK, 2) and WC = max(WK / 2, 1),
+  // wave w takes sb = w % 2 + j W2 (j < NSB) and cb = w / 2 + c WC
+  // (c < 8 / WC): 16 / WK blocks, each block exactly once.
+  const int W2 = WK < 2 ? WK : 2;
+  const int WC = WK < 2 ? 1 : WK / 2;
+  const int NCW = 8 / WC;  // centroid blocks per wave
   const int li = lane & 31;
   const bool klo = lane < 32;  // lanes holding dims 0..3 (the others: the zero padding)
-  const uint32_t vx = klo ? ((uint32_t)m * K + 4u * (32u * sbw + li)) * 2u : OOB;
-  auto load_xseg = [&](int q) -> u2 {  // segment 32 sb + l % 32 of quad q: 4 halves
-    const uint32_t qc = (uint32_t)min(q, q1 - 1);
-    return __builtin_bit_cast(u2, __builtin_amdgcn_raw_buffer_load_b64(rx, vx, 1024u * qc, 0));
+
+  // A operands: codebook rows 32 cb + l % 32 of this wave's centroid blocks
+  h4v ca[8];
+  {
+    const rsrc_t rcb = make_rsrc(a.codebook, 256u * 8u);
+#pragma unroll
+    for (int c = 0; c < 8; ++c) {
+      const uint32_t cb = (uint32_t)((wave >> 1) + c * WC);
+      const uint32_t v = klo && c < NCW ? (32u * cb + li) * 8u : OOB;
+      ca[c] = __builtin_bit_cast(h4v, __builtin_amdgcn_raw_buffer_load_b64(rcb, v, 0, 0));
+    }
+  }
+  // B operands: segment 32 sb + l % 32 of pair h, 4 halves
+  uint32_t vx[NSB];
+#pragma unroll
+  for (int j = 0; j < NSB; ++j) vx[j] = klo ? ((uint32_t)m * K + 4u * (32u * ((wave & 1) + j * W2) + li)) * 2u : OOB;
+  struct Xs {
+    u2 v[NSB];
   };
+  auto load_xs = [&](int h, Xs& xs) {
+    const uint32_t hc = (uint32_t)min(h, h1 - 1);
+#pragma unroll
+    for (int j = 0; j < NSB; ++j)
+      xs.v[j] = __builtin_bit_cast(u2, __builtin_amdgcn_raw_buffer_load_b64(rx, vx[j], 512u * hc, 0));
+  };
+  // this lane's store address within a segment block: segment l % 32, the
+  // 4-centroid quartet 4 (l / 32) of each 8-centroid group
+  const uint32_t pw = (uint32_t)li * PSTRIDE + 8u * (uint32_t)(lane >> 5);
 
   St ring[2];
-  load_stage(q0, ring[0]);
-  u2 xseg = load_xseg(q0);
+  Xs xr[2];
+  load_stage(h0, ring[0]);
+  load_xs(h0, xr[0]);
 
-  // codebook into LDS once (read by the build as B operands)
-  {
-    const rsrc_t rcb = make_rsrc(a.codebook, CB_BYTES);
-    for (int i = threadIdx.x; i < 512; i += blockDim.x) lsm[(PSUM_BYTES / 4) + i] = bload4(rcb, 4u * i);
-  }
-  const u2* cbv = reinterpret_cast<const u2*>(lds + PSUM_BYTES);
-  _Float16* const P16 = reinterpret_cast<_Float16*>(lds);
   const h2 ones = {(_Float16)1.0f, (_Float16)1.0f};
   float acc = 0.f;
 
-  auto step = [&](int q, const St& st, St& nxt) {
-    load_stage(q + 1, nxt);  // next quad (past the range: a harmless re-read)
-    const u2 xnext = load_xseg(q + 1);
-    lds_barrier();  // every wave is done reading the previous quad's P (and the codebook is staged)
-    for (int p = wave; p < 32; p += WK) {
-      const int cb = p >> 2;
-      const u2 cv = cbv[32 * cb + li];
-      const u2 cc = {klo ? cv.x : 0u, klo ? cv.y : 0u};
-      const f16v d = __builtin_amdgcn_mfma_f32_32x32x8f16(__builtin_bit_cast(h4v, xseg), __builtin_bit_cast(h4v, cc),
-                                                          f16v{}, 0, 0, 0);
-      // lane l, register r: P[32 sb + 8 (r / 4) + 4 (l / 32) + r % 4][32 cb + l % 32]
+  auto step = [&](int h, const St& st, St& nxt, const Xs& xs, Xs& xn) {
+    load_stage(h + 1, nxt);  // next pair (past the range: a harmless re-read)
+    load_xs(h + 1, xn);
+    lds_barrier();  // every wave is done reading the previous pair's P
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int s = 32 * sbw + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
-        P16[s * 256 + 32 * cb + li] = (_Float16)d[r];
+    for (int j = 0; j < NSB; ++j) {
+      const uint32_t sb = (uint32_t)((wave & 1) + j * W2);
+#pragma unroll
+      for (int c = 0; c < 8; ++c) {
+        if (c >= NCW) break;
+        const uint32_t cb = (uint32_t)((wave >> 1) + c * WC);
+        const f16v d = __builtin_amdgcn_mfma_f32_32x32x8f16(ca[c], __builtin_bit_cast(h4v, xs.v[j]), f16v{}, 0, 0, 0);
+        // lane l, register 4 g + i: P[32 sb + l % 32][32 cb + 8 g + 4 (l / 32) + i]
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          const h4v hv = {(_Float16)d[4 * g], (_Float16)d[4 * g + 1], (_Float16)d[4 * g + 2], (_Float16)d[4 * g + 3]};
+          *reinterpret_cast<u2*>(lds + pw + sb * (32u * PSTRIDE) + 64u * cb + 16u * g) = __builtin_bit_cast(u2, hv);
+        }
       }
     }
-    xseg = xnext;
-    lds_barrier();  // P of this quad complete
+    lds_barrier();  // P of this pair complete
 #pragma unroll
-    for (int g = 0; g < 4; ++g) {
+    for (int g = 0; g < 2; ++g) {
       float part = 0.f;
 #pragma unroll
-      for (int h = 0; h < 2; ++h) {  // tile 2g + h: segments 32g + 16h + 0..15
+      for (int t = 0; t < 2; ++t) {  // tile 2g + t: segments 32g + 16t + 0..15
 #pragma unroll
-        for (int d = 0; d < 4; ++d) {  // word d: segments 32g + 16h + 4d + 0..3
-          const uint32_t w = st.c[2 * g + h][d];
-          const uint32_t s0 = 32u * g + 16u * h + 4u * d;
+        for (int d = 0; d < 4; ++d) {  // word d: segments 32g + 16t + 4d + 0..3
+          const uint32_t w = st.c[2 * g + t][d];
+          const uint32_t s0 = 32u * g + 16u * t + 4u * d;
           h2 pa, pb;
 #pragma unroll
           for (int b = 0; b < 4; ++b) {
-            const uint32_t code2 = ((w >> (8 * b)) & 0xFFu) << 1;
-            const _Float16 v = *reinterpret_cast<const _Float16*>(lds + code2 + 512u * (s0 + b));
+            const uint32_t code2 = __builtin_amdgcn_ubfe(w, 8 * b, 8) << 1;
+            const _Float16 v = *reinterpret_cast<const _Float16*>(lds + code2 + PSTRIDE * (s0 + b));
             if (b < 2)
               pa[b] = v;
             else
@@ -169,90 +201,306 @@ __global__ void __launch_bounds__(1024) gemv_codebook_kernel(CodebookArgs a) {
       acc = fmaf(h2f(st.s[g]), part, acc);
     }
   };
-  // two quads per iteration so the stage buffers are named statically
-  for (int q = q0; q < q1; q += 2) {
-    step(q, ring[0], ring[1]);
-    if (q + 1 < q1) step(q + 1, ring[1], ring[0]);
+  // two pairs per iteration so the stage buffers are named statically
+  for (int h = h0; h < h1; h += 2) {
+    step(h, ring[0], ring[1], xr[0], xr[1]);
+    if (h + 1 < h1) step(h + 1, ring[1], ring[0], xr[1], xr[0]);
   }
 
-  if (KS == 1) {
-    if (rv) a.y[(size_t)m * N + row] = f2h(acc);
-    return;
-  }
-  // K split: partial sums to the workspace; the last workgroup of the row
-  // block adds them in K order
-  if (rv) a.ws[((size_t)ks * M + m) * N + row] = acc;
-  __threadfence();
-  __syncthreads();
-  if (threadIdx.x == 0) {
-    uint32_t* cnt = a.cnt + (size_t)m * gridDim.x + blockIdx.x;
-    const uint32_t old = atomicAdd(cnt, 1u);
-    const bool last = old == (uint32_t)KS - 1u;
-    if (last) *cnt = 0u;  // ready for the next call
-    *flag = last;
-  }
-  __syncthreads();
-  if (*flag) {
-    __threadfence();
-    if (rv) {
-      float sum = 0.f;
-      for (int k = 0; k < KS; ++k) sum += __builtin_nontemporal_load(&a.ws[((size_t)k * M + m) * N + row]);
-      a.y[(size_t)m * N + row] = f2h(sum);
+  if (!rv) return;
+  if (KS == 1)
+    a.y[(size_t)m * N + row] = f2h(acc);
+  else  // K split: this range's partial sum, added up by the reduce kernel
+    a.ws[((size_t)ks * M + m) * N + row] = acc;
+}
+
+// Stationary kernel: a workgroup owns one K part of PP pairs (SEG = 64 PP
+// segments) and one batch row, builds that part's Psumbook once, and streams
+// row blocks through it: wave w of row slice r takes row blocks
+// r WK + w + i R WK.  There is no barrier after the build, so every wave
+// runs at its own pace and the lookups of the 16 waves on a CU keep the LDS
+// busy.  Each part writes fp32 partial sums; the reduce kernel adds them.
+//
+// Grid: one dimension of 8 * ceil(R * KP / 8) * M workgroups.  Workgroup b
+// takes batch row m = (b / 8) % M and unit u = (b / (8 M)) * 8 + b % 8
+// (row slice u % R, K part u / R), so the M workgroups that read the same
+// codes get ids b, b + 8, ..., which are dispatched together and to the same
+// XCD (ids are dealt to the 8 XCDs in turn), and share its L2.  (Running the
+// K parts of a row slice together instead, so that neighbours read adjacent
+// 4 KB runs, measured slower.)
+template <int PP, bool SAL>
+__global__ void __launch_bounds__(PP == 4 ? 512 : 1024) gemv_codebook_stat_kernel(CodebookArgs a, int R) {
+  constexpr uint32_t SEG = 64u * PP;
+  constexpr uint32_t PBYTES = SEG * PSTRIDE;
+  // LDS: [Psumbook SEG x 520 B][codebook 256 x 8 B][activation segments SEG x 8 B]
+  __shared__ __attribute__((aligned(16))) uint32_t lsm[(PBYTES + 2048u + SEG * 8u) / 4];
+  char* const lds = reinterpret_cast<char*>(lsm);
+  u2* const stg = reinterpret_cast<u2*>(lds + PBYTES);  // codebook rows, then the segments
+
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int WK = blockDim.x >> 6;
+  const int M = a.M, N = a.N, K = a.K;
+  const int G = K / 128;   // quant groups
+  const int NCB = K / 64;  // 16-code tiles per row block
+  const int NB = (N + 63) / 64;
+  const int KP = K / (256 * PP);
+  const uint32_t b = blockIdx.x;
+  const int m = (int)((b >> 3) % (uint32_t)M);
+  const uint32_t u = (b / (8u * (uint32_t)M)) * 8u + (b & 7u);
+  if (u >= (uint32_t)R * (uint32_t)KP) return;  // padding: the whole workgroup
+  const int r = (int)(u % (uint32_t)R), kp = (int)(u / (uint32_t)R);
+
+  const int RS = R * WK;
+  const int rb0 = r * WK + wave;
+  const int cnt = rb0 < NB ? (NB - 1 - rb0) / RS + 1 : 0;  // this wave's row blocks
+
+  const rsrc_t rc = make_rsrc(a.codes, (uint32_t)NB * NCB * 1024u);
+  const rsrc_t rs = make_rsrc(a.scales, (uint32_t)N * G * 2u);
+
+  struct St {
+    u4 c[4 * PP];     // 4 PP tiles x 16 codes of this lane's row
+    uint32_t s[PP];   // the part's 2 PP group scales of this row, two per word
+  };
+  // Unconditional loads, every choice in the offsets: past this wave's last
+  // row block (and for a row past N) the offsets are out of range, so the
+  // loads return zeros without touching memory.
+  auto load_stage = [&](int i, St& st) {
+    const bool bv = i < cnt;
+    const int rb = rb0 + i * RS;
+    const uint32_t sw =
+        __builtin_amdgcn_readfirstlane(((uint32_t)(bv ? rb : 0) * NCB + 4u * PP * (uint32_t)kp) * 1024u);
+    const uint32_t vc = bv ? 16u * lane : OOB;
+#pragma unroll
+    for (int j = 0; j < 4 * PP; ++j) st.c[j] = bload16<CPOL_NT>(rc, vc + 1024u * j, sw);
+    const uint32_t row = (uint32_t)rb * 64u + lane;
+    const uint32_t vs = bv && row < (uint32_t)N ? (row * (uint32_t)G + 2u * PP * (uint32_t)kp) * 2u : OOB;
+#pragma unroll
+    for (int j = 0; j < PP; ++j) {
+      if constexpr (SAL)
+        st.s[j] = bload4(rs, vs + 4u * j);
+      else
+        st.s[j] = (uint32_t)bload2(rs, vs + 4u * j) | ((uint32_t)bload2(rs, vs + 4u * j + 2u) << 16);
+    }
+  };
+
+  // The codebook and this part's activation segments (256 + SEG 8-byte
+  // entries, at most 8 per thread) are loaded first: a wave's loads return in
+  // order, so the build then waits for these only, not for the code prefetch
+  // issued after them.
+  u2 sv[8];
+  {
+    const rsrc_t rcb = make_rsrc(a.codebook, 2048u);
+    const rsrc_t rx = make_rsrc(a.x, (uint32_t)M * K * 2u);
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const int i = threadIdx.x + j * (int)blockDim.x;
+      const uint32_t xo = ((uint32_t)m * K + 4u * (SEG * (uint32_t)kp + (uint32_t)(i - 256))) * 2u;
+      sv[j] = i < 256 ? __builtin_bit_cast(u2, __builtin_amdgcn_raw_buffer_load_b64(rcb, 8u * i, 0, 0))
+                      : __builtin_bit_cast(u2, __builtin_amdgcn_raw_buffer_load_b64(
+                                                   rx, i < 256 + (int)SEG ? xo : OOB, 0, 0));
     }
   }
+  // D row blocks of codes per wave: D - 1 in flight during the lookups of one
+  constexpr int D = PP == 1 ? 4 : (PP == 2 ? 3 : 2);
+  St ring[D];
+#pragma unroll
+  for (int k = 0; k + 1 < D; ++k) load_stage(k, ring[k]);  // in flight during the build
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    const int i = threadIdx.x + j * (int)blockDim.x;
+    if (i < 256 + (int)SEG) stg[i] = sv[j];
+  }
+  __syncthreads();
+  // Build: 2 PP segment blocks x 8 centroid blocks, one v_mfma_f32_32x32x8_f16
+  // each (A = codebook rows, B = activation segments, dims 4..7 zero)
+  {
+    const int li = lane & 31;
+    const bool klo = lane < 32;
+    const uint32_t pw = (uint32_t)li * PSTRIDE + 8u * (uint32_t)(lane >> 5);
+    for (int p = wave; p < 16 * PP; p += WK) {
+      const uint32_t sb = (uint32_t)(p % (2 * PP)), cb = (uint32_t)(p / (2 * PP));
+      const u2 av = stg[32u * cb + li], bv = stg[256u + 32u * sb + li];
+      const u2 A = {klo ? av.x : 0u, klo ? av.y : 0u}, B = {klo ? bv.x : 0u, klo ? bv.y : 0u};
+      const f16v d = __builtin_amdgcn_mfma_f32_32x32x8f16(__builtin_bit_cast(h4v, A), __builtin_bit_cast(h4v, B), f16v{},
+                                                          0, 0, 0);
+      // lane l, register 4 g + i: P[32 sb + l % 32][32 cb + 8 g + 4 (l / 32) + i]
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const h4v hv = {(_Float16)d[4 * g], (_Float16)d[4 * g + 1], (_Float16)d[4 * g + 2], (_Float16)d[4 * g + 3]};
+        *reinterpret_cast<u2*>(lds + pw + sb * (32u * PSTRIDE) + 64u * cb + 16u * g) = __builtin_bit_cast(u2, hv);
+      }
+    }
+  }
+  __syncthreads();
+
+  const h2 ones = {(_Float16)1.0f, (_Float16)1.0f};
+  auto step = [&](int i, const St& st, St& nxt) {
+    load_stage(i + D - 1, nxt);  // a later row block (past the last: a harmless re-read)
+    float acc = 0.f;
+#pragma unroll
+    for (int g = 0; g < 2 * PP; ++g) {
+      float part = 0.f;
+#pragma unroll
+      for (int t = 0; t < 2; ++t) {  // tile 2g + t: segments 32g + 16t + 0..15
+#pragma unroll
+        for (int d = 0; d < 4; ++d) {  // word d: segments 32g + 16t + 4d + 0..3
+          const uint32_t w = st.c[2 * g + t][d];
+          const uint32_t s0 = 32u * g + 16u * t + 4u * d;
+          h2 pa, pb;
+#pragma unroll
+          for (int bb = 0; bb < 4; ++bb) {
+            const uint32_t code2 = __builtin_amdgcn_ubfe(w, 8 * bb, 8) << 1;
+            const _Float16 v = *reinterpret_cast<const _Float16*>(lds + code2 + PSTRIDE * (s0 + bb));
+            if (bb < 2)
+              pa[bb] = v;
+            else
+              pb[bb - 2] = v;
+          }
+          part = dot2(pa, ones, part);
+          part = dot2(pb, ones, part);
+        }
+      }
+      acc = fmaf(h2f((uint16_t)(st.s[g / 2] >> (16 * (g % 2)))), part, acc);
+    }
+    const uint32_t row = (uint32_t)(rb0 + i * RS) * 64u + lane;
+    if (row < (uint32_t)N) {
+      if (KP == 1)
+        a.y[(size_t)m * N + row] = f2h(acc);
+      else
+        a.ws[((size_t)kp * M + m) * N + row] = acc;
+    }
+  };
+  // D row blocks per iteration so the stage buffers are named statically
+  for (int i = 0; i < cnt; i += D) {
+#pragma unroll
+    for (int k = 0; k < D; ++k)
+      if (i + k < cnt) step(i + k, ring[k], ring[(k + D - 1) % D]);
+  }
+}
+
+// y[i] = fp16(sum over k < KS of ws[k * MN + i]).  A workgroup takes 64
+// outputs; wave j adds parts j, j + 8, j + 16, ... (loads issued 8 at a time,
+// each a 256-byte row), and wave 0 adds the 8 wave sums in order: a fixed
+// order for every output, so the result is deterministic.
+__global__ void __launch_bounds__(512) codebook_reduce_kernel(const float* __restrict__ ws, uint16_t* __restrict__ y,
+                                                              int MN, int KS) {
+  __shared__ float part[8][64];
+  const int lane = threadIdx.x & 63, j = threadIdx.x >> 6;
+  const int i = blockIdx.x * 64 + lane;
+  float sum = 0.f;
+  if (i < MN) {
+    int k = j;
+    for (; k + 56 < KS; k += 64) {
+      float v[8];
+#pragma unroll
+      for (int t = 0; t < 8; ++t) v[t] = __builtin_nontemporal_load(&ws[(size_t)(k + 8 * t) * MN + i]);
+#pragma unroll
+      for (int t = 0; t < 8; ++t) sum += v[t];
+    }
+    for (; k < KS; k += 8) sum += __builtin_nontemporal_load(&ws[(size_t)k * MN + i]);
+  }
+  part[j][lane] = sum;
+  __syncthreads();
+  if (j == 0 && i < MN) {
+    float t = part[0][lane];
+#pragma unroll
+    for (int w = 1; w < 8; ++w) t += part[w][lane];
+    y[i] = f2h(t);
+  }
+}
+
+template <int NSB>
+void* seq_kernel_ptr(bool sal) {
+  return sal ? reinterpret_cast<void*>(&gemv_codebook_seq_kernel<NSB, true>)
+             : reinterpret_cast<void*>(&gemv_codebook_seq_kernel<NSB, false>);
+}
+
+template <int PP>
+void* stat_kernel_ptr(bool sal) {
+  return sal ? reinterpret_cast<void*>(&gemv_codebook_stat_kernel<PP, true>)
+             : reinterpret_cast<void*>(&gemv_codebook_stat_kernel<PP, false>);
 }
 
 }  // namespace
 
-// Workspace: KS x M x N fp32 partial sums from the start, and a fixed area of
-// CB_COUNTERS counters (one per batch row and row block) at the very end of
-// the caller's buffer, so that shapes sharing one workspace never write their
-// partial sums over each other's counters.  The counters must be zero before
-// first use; every call leaves them zero.
-size_t codebook_ws_bytes(const CodebookCfg& c, int M, int N) {
-  if (c.ks <= 1) return 0;
-  return (size_t)c.ks * M * N * 4 + CB_COUNTERS * 4;
+// K parts a launch writes partial sums for (1: none, y directly)
+static int codebook_parts(const CodebookCfg& c, int K) { return c.pp > 0 ? K / (256 * c.pp) : c.ks; }
+
+// Workspace: parts x M x N fp32 partial sums; scratch, no initial contents.
+size_t codebook_ws_bytes(const CodebookCfg& c, int M, int N, int K) {
+  const int parts = codebook_parts(c, K);
+  return parts > 1 ? (size_t)parts * M * N * 4 : 0;
 }
 
-size_t codebook_row_blocks(const CodebookCfg& c, int N) {
-  const int NB = (N + 63) / 64;
-  return (NB + c.wk - 1) / c.wk;
-}
-
-// Measured on MI355X (70B-class layers, M = 1 and 4): the best launches fill
-// the 256 CUs with about one workgroup each.  Take the fewest waves per
-// workgroup (the cheapest barriers) whose row blocks x batch rows fit in 256
-// workgroups, then split K (whole quads) while the grid still fits.
+// Fitted to sweeps on MI355X (8B- and 70B-shaped layers, M = 1 and 4).
+//  * The stationary kernel wins where there are many rows to stream through
+//    each Psumbook: N >= 10240 at M = 1, and at M >= 2 any layer of 32M
+//    weights or more (its M workgroups then share each code read through
+//    L2).  About 256 workgroups, two pairs per part once K >= 8192.
+//  * Elsewhere (fewer rows, or K long against N) the sequential kernel, with
+//    K split in whole pairs until the grid holds about 384 workgroups.
 CodebookCfg pick_codebook(int M, int N, int K) {
   CodebookCfg c;
-  c.wk = 16;
-  for (int wk = 4; wk <= 16; wk *= 2) {
-    c.wk = wk;
-    if ((long)codebook_row_blocks(c, N) * M <= 256) break;
+  c.wk = 4;
+  const long NB = (N + 63) / 64;
+  const long rg = (NB + c.wk - 1) / c.wk;  // row groups of one workgroup
+  const long HN = K / 256;
+  const bool stat = M == 1 ? N >= 10240 : (long)N * K >= (32L << 20);
+  if (stat) {
+    c.pp = K >= 8192 && HN % 2 == 0 ? 2 : 1;
+    c.ks = 1;
+    const long KP = HN / c.pp;
+    c.r = (int)std::max(1L, std::min(rg, (256 + KP * M - 1) / (KP * M)));
+  } else {
+    c.pp = 0;
+    c.r = 0;
+    c.ks = 1;
+    while (c.ks * 2 <= HN && rg * M * c.ks < 384) c.ks *= 2;
   }
-  const long wgs = (long)codebook_row_blocks(c, N) * M;
-  const int QN = K / 512;
+  return c;
+}
+
+CodebookCfg codebook_fallback() {
+  CodebookCfg c;
+  c.wk = 4;
+  c.pp = 0;
+  c.r = 0;
   c.ks = 1;
-  while (c.ks * 2 <= QN && wgs * c.ks * 2 <= 256) c.ks *= 2;
   return c;
 }
 
 hipError_t launch_gemv_codebook(const CodebookArgs& a, const CodebookCfg& c, hipStream_t s) {
-  // the Psumbook build gives each wave a fixed segment block: wk % 4 == 0
-  if (c.wk < 4 || c.wk > 16 || c.wk % 4 || c.ks < 1 || c.ks > a.K / 512) return hipErrorInvalidValue;
-  const dim3 grid((unsigned)codebook_row_blocks(c, a.N), c.ks, a.M);
-  const dim3 block(64 * c.wk);
-  const size_t lds = PSUM_BYTES + CB_BYTES + 16;
-  const bool sal = reinterpret_cast<uintptr_t>(a.scales) % 8 == 0;
-  auto kern = sal ? &gemv_codebook_kernel<true> : &gemv_codebook_kernel<false>;
-  static bool raised[2] = {false, false};
-  if (!raised[sal]) {
-    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
-                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+  if (c.wk != 1 && c.wk != 2 && c.wk != 4 && c.wk != 8 && c.wk != 16) return hipErrorInvalidValue;
+  const int parts = codebook_parts(c, a.K);
+  const bool sal = reinterpret_cast<uintptr_t>(a.scales) % 4 == 0;
+  if (c.pp > 0) {
+    // four pairs: 133 KB of Psumbook, one workgroup per CU, at most 8 waves
+    if ((c.pp != 1 && c.pp != 2 && c.pp != 4) || (c.pp == 4 && c.wk > 8) || (a.K / 256) % c.pp || c.r < 1 ||
+        c.r > (1 << 20))
+      return hipErrorInvalidValue;
+    if (parts > 1 && !a.ws) return hipErrorInvalidValue;
+    const long units = (long)c.r * parts;
+    const long blocks = (units + 7) / 8 * 8 * a.M;
+    if (blocks >= (1L << 31)) return hipErrorInvalidValue;
+    void* const kern = c.pp == 1 ? stat_kernel_ptr<1>(sal) : c.pp == 2 ? stat_kernel_ptr<2>(sal) : stat_kernel_ptr<4>(sal);
+    int r = c.r;
+    void* args[] = {const_cast<CodebookArgs*>(&a), &r};
+    hipError_t e = hipLaunchKernel(kern, dim3((unsigned)blocks), dim3(64 * c.wk), args, 0, s);
     if (e != hipSuccess) return e;
-    raised[sal] = true;
+  } else {
+    if (c.ks < 1 || c.ks > a.K / 256 || (c.ks > 1 && !a.ws)) return hipErrorInvalidValue;
+    const int NB = (a.N + 63) / 64;
+    const dim3 grid((unsigned)((NB + c.wk - 1) / c.wk), c.ks, a.M);
+    void* const kern = c.wk == 1 ? seq_kernel_ptr<2>(sal) : seq_kernel_ptr<1>(sal);
+    void* args[] = {const_cast<CodebookArgs*>(&a)};
+    hipError_t e = hipLaunchKernel(kern, grid, dim3(64 * c.wk), args, 0, s);
+    if (e != hipSuccess) return e;
   }
-  hipLaunchKernelGGL(kern, grid, block, lds, s, a);
+  if (parts > 1) {
+    const int MN = a.M * a.N;
+    hipLaunchKernelGGL(codebook_reduce_kernel, dim3((MN + 63) / 64), dim3(512), 0, s, a.ws, a.y, MN, parts);
+  }
   return hipGetLastError();
 }
 

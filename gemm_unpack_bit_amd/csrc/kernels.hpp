@@ -58,7 +58,7 @@ hipError_t launch_gemv_lut4(const Lut4Args& a, const Lut4Cfg& c, hipStream_t s);
 
 // Codebook (m = 1, v = 4, b = 8, g = 128) with a Psumbook: codes [N, K/4]
 // uint8 in the 64-row layout (layout 2), codebook fp16 [256][4], scales fp16
-// [N, K/128]; ws/cnt: the K-split workspace (partials, then counters)
+// [N, K/128]; ws: the K-split partial sums (KS x M x N fp32)
 struct CodebookArgs {
   int M, N, K;
   const uint16_t* x;
@@ -67,16 +67,17 @@ struct CodebookArgs {
   const uint16_t* scales;
   uint16_t* y;
   float* ws;
-  uint32_t* cnt;
 };
-// wk = waves = 64-row blocks per workgroup (4, 8, 16), ks = K splits
+// A codebook launch.  pp > 0 (1, 2, 4): the stationary kernel, one K part of pp pairs
+// (256 k each) per workgroup and r row slices; pp == 0: the sequential kernel,
+// ks K ranges per row block (ks == 1 needs no workspace).  wk = waves per
+// workgroup (1, 2, 4, 8, 16).
 struct CodebookCfg {
-  int wk, ks;
+  int wk, pp, r, ks;
 };
 CodebookCfg pick_codebook(int M, int N, int K);
-constexpr size_t CB_COUNTERS = 4096;  // counters at the end of a codebook workspace
-size_t codebook_ws_bytes(const CodebookCfg& c, int M, int N);
-size_t codebook_row_blocks(const CodebookCfg& c, int N);
+CodebookCfg codebook_fallback();
+size_t codebook_ws_bytes(const CodebookCfg& c, int M, int N, int K);
 hipError_t launch_gemv_codebook(const CodebookArgs& a, const CodebookCfg& c, hipStream_t s);
 
 // bit packing (layout: 0 plain, 1 device = tiled, see pack.hip)

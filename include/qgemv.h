@@ -233,21 +233,21 @@ int qgemv_outlier(int path, int M, int N, int K, const uint16_t *x, const uint32
  *   scales   [dev] fp16   [N, K/128]
  *   y        [dev] fp16   [M, N]
  *   ws       [dev] optional workspace of at least
- *                  qgemv_codebook_workspace_bytes(M, N, K) bytes.  Its last
- *                  16 KB hold counters that must be ZERO before the first call
- *                  (every call leaves them zero); the rest is scratch.  One
- *                  buffer may serve several shapes if it is passed with the
- *                  same ws_bytes every time and is as large as the largest
- *                  requirement.  With it the library splits K across
- *                  workgroups and adds the parts in a fixed order; with NULL or
- *                  a smaller ws it runs one pass per row block (same result
- *                  within the tolerance, usually slower).  Calls that share a
- *                  workspace must not overlap in time.
+ *                  qgemv_codebook_workspace_bytes(M, N, K) bytes of scratch
+ *                  (no initial contents needed) for fp32 partial sums.  With
+ *                  it every workgroup builds the Psumbook of one K part once
+ *                  and streams many weight rows through it; a second kernel on
+ *                  the same stream adds the parts of every output in a fixed
+ *                  order.  With NULL or a smaller ws each workgroup walks the
+ *                  whole K for its rows, building one Psumbook per 256 k (same
+ *                  result within the tolerance, slower).  One buffer may serve
+ *                  several shapes; calls that share a workspace must not
+ *                  overlap in time.
  *
  * Shapes: 1 <= M <= 16, N >= 1, K a positive multiple of 512 (QGEMV_ERR_SHAPE).
  * x, codes 16-byte aligned, codebook and ws 4-byte, scales and y 2-byte
- * (QGEMV_ERR_ALIGN).  y must not overlap an input or ws (QGEMV_ERR_VALUE).
- * Asynchronous, deterministic for a given workspace size.
+ * (QGEMV_ERR_ALIGN).  Neither y nor ws may overlap an input, nor each other
+ * (QGEMV_ERR_VALUE).  Asynchronous, deterministic for a given workspace size.
  * ------------------------------------------------------------------------ */
 int qgemv_codebook(int M, int N, int K, const uint16_t *x, const uint32_t *codes,
                    const uint16_t *codebook, const uint16_t *scales, uint16_t *y, void *ws,

@@ -121,6 +121,7 @@ def test_codebook_validation_without_gpu(L):
     assert _cb(L, x=FAKE + 8) == q.ERR_ALIGN
     assert _cb(L, cbk=FAKE * 3 + 2) == q.ERR_ALIGN
     assert _cb(L, y=FAKE * 3) == q.ERR_VALUE      # y overlaps the codebook
+    assert _cb(L, ws=FAKE * 4, wsb=64) == q.ERR_VALUE  # the workspace overlaps the scales
     assert L.qgemv_codebook_workspace_bytes(1, 64, 384) == 0
     n = L.qgemv_codebook_workspace_bytes(1, 8192, 28672)
     assert n >= 2 * 4 * 8192                       # few rows, long K: split, one fp32 partial per row and split

@@ -43,6 +43,28 @@ def test_codebook_small_shapes(use_ws, N, K, M):
     assert_within(y, y_ref, A, f"codebook M={M} N={N} K={K} ws={use_ws}")
 
 
+@pytest.mark.parametrize("M,N,K", [(1, 300, 3584), (3, 200, 2048), (16, 70, 1536), (2, 1000, 512)])
+def test_codebook_every_launch_shape(monkeypatch, M, N, K):
+    """Both kernels at every workgroup size (1..16 waves, so every split of
+    the build): the stationary one with one, two and four pairs per workgroup and
+    1 to all row slices, the sequential one with K splits up to one 256-k pair
+    per range; each against the oracle."""
+    say("codebook launch shapes", M, N, K)
+    c = synth.codebook_case(N + K + M, M, N, K)
+    codes, cb, s = _upload(c)
+    x = dev(c["x"])
+    y_ref, A = ref.gemv_codebook(c["x"], c["codes"], c["codebook"], c["scales"])
+    ws = torch().zeros(K // 256 * M * N * 4, dtype=torch().uint8, device="cuda")
+    NB = (N + 63) // 64
+    cfgs = [f"0,{wk},{ks}" for wk in (1, 2, 4, 8, 16) for ks in sorted({1, 2, 3, K // 256})]
+    cfgs += [f"1,{wk},{pp},{r}" for wk in (1, 2, 4, 8, 16) for pp in (1, 2, 4) for r in sorted({1, 2, 3, NB})
+             if (K // 256) % pp == 0 and not (pp == 4 and wk > 8)]
+    for cfg in cfgs:
+        monkeypatch.setenv("QGEMV_CODEBOOK_CFG", cfg)
+        y = host(q.codebook(x, codes, cb, s, ws=ws))
+        assert_within(y, y_ref, A, f"codebook M={M} N={N} K={K} cfg={cfg}")
+
+
 def test_codebook_one_hot_is_exact():
     """x = e_k: y[n] = fp16(s * C[code][k % 4]) exactly."""
     say("codebook one-hot")
