@@ -163,7 +163,7 @@ def summarize_trace(path):
     d = defaultdict(list)
     with open(path) as f:
         for r in csv.DictReader(f):
-            name = re.sub(r"^void qg::\(anonymous namespace\)::", "", r["Kernel_Name"]).split("(")[0]
+            name = re.sub(r"^(void )?qg::\(anonymous namespace\)::", "", r["Kernel_Name"]).split("(")[0]
             key = (name.replace(" ", ""), int(r["Grid_Size_X"]), int(r["Workgroup_Size_X"]))
             d[key].append((int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1000.0)
     print(f"{'kernel':72s} {'grid':>8s} {'wg':>5s} {'n':>5s} {'mean':>8s} {'median':>8s} {'p10':>8s} {'p90':>8s}")
