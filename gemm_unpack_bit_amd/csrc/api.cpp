@@ -61,18 +61,19 @@ qg::TileCfg tile_cfg(int bits, int M, int N, int K, bool mfma) {
   return c;
 }
 
-// Tuning override of the LUT4 launch shape: QGEMV_LUT4_CFG="tpw,ng,wk[,mt]".
+// Tuning override of the LUT4 launch shape: QGEMV_LUT4_CFG="tpw,ng,wk[,mt[,d]]".
 qg::Lut4Cfg lut4_cfg(int M, int N, int K) {
   qg::Lut4Cfg c = qg::pick_lut4(M, N, K);
   if (const char* e = std::getenv("QGEMV_LUT4_CFG")) {
-    int tpw, ng, wk, mt;
-    const int n = std::sscanf(e, "%d,%d,%d,%d", &tpw, &ng, &wk, &mt);
+    int tpw, ng, wk, mt, d;
+    const int n = std::sscanf(e, "%d,%d,%d,%d,%d", &tpw, &ng, &wk, &mt, &d);
     if (n >= 3) {
       c.tpw = tpw;
       c.ng = ng;
       c.wk = wk;
     }
-    if (n == 4) c.mt = mt;
+    if (n >= 4) c.mt = mt;
+    if (n >= 5) c.d = d;
   }
   return c;
 }

@@ -23,9 +23,16 @@
 //    LDS with each 8-k run stored in that order, so a table pair meets its
 //    activation pair as loaded: per 8 weights, 4 v_perm + 4 ds_read_b32 +
 //    4 v_dot2 (one VALU instruction per weight).
+//  * Persistent workgroups: the 64 KB table allows two workgroups per CU, and
+//    building it costs as much as streaming a few tile-rows, so the grid
+//    holds only the resident workgroups; each builds its table and stages the
+//    activations once, then walks row groups, issuing the next group's first
+//    chunks before reducing the current one (the barriers wait for LDS only).
 //  * Streaming, pipeline, work split and reduction follow the uniform kernel:
-//    branch-free non-temporal tile loads through a two-slot register ring,
+//    branch-free non-temporal tile loads through a D-slot register ring,
 //    permlane quarter sums, LDS wave sums in fixed order (deterministic).
+#include <algorithm>
+
 #include "common.hpp"
 #include "kernels.hpp"
 
@@ -62,10 +69,11 @@ __device__ __forceinline__ void load_block_scales(rsrc_t r, uint32_t rowoff, uin
 }
 
 // TPW tile-rows per workgroup (1, 2), NG groups per chunk, MT activation
-// rows per workgroup.  SAL: K/128 is a multiple of NG and the block scales are
+// rows per workgroup; with one tile-row, D chunks per wave in a ring (D - 1
+// loads ahead).  SAL: K/128 is a multiple of NG and the block scales are
 // 4*NG-byte aligned, so a chunk's scales are one load.
-template <int MT, int NG, int TPW, bool SAL>
-__global__ void __launch_bounds__(512) gemv_lut4_kernel(Lut4Args a) {
+template <int MT, int NG, int TPW, int D, bool SAL>
+__global__ void __launch_bounds__(512, MT == 1 ? 4 : 2) gemv_lut4_kernel(Lut4Args a) {
   // LDS: [pair table 64 KB][activations MT x XK halves, 8-k runs permuted
   // (xarea_bytes)][partials]
   extern __shared__ __attribute__((aligned(16))) uint32_t lsm[];
@@ -82,7 +90,8 @@ __global__ void __launch_bounds__(512) gemv_lut4_kernel(Lut4Args a) {
   const int NT = (N + 15) / 16;
   const int NC = (G + NG - 1) / NG;
   const int m0 = blockIdx.y * MT;
-  const int rt0 = blockIdx.x * TPW;
+  const int NRG = (NT + TPW - 1) / TPW;  // row groups (TPW tile-rows each)
+  int rt0 = blockIdx.x * TPW;             // the current row group's first tile-row
   const int XK = K + 32;  // staged row stride (halves): K, then a zero pad
   const uint32_t lane4 = 4u * lane;
   float* const red = reinterpret_cast<float*>(lds + TABLE_BYTES + xarea_bytes(MT, K));
@@ -123,10 +132,6 @@ __global__ void __launch_bounds__(512) gemv_lut4_kernel(Lut4Args a) {
   };
 
   float acc[TPW][MT];
-#pragma unroll
-  for (int t = 0; t < TPW; ++t)
-#pragma unroll
-    for (int m = 0; m < MT; ++m) acc[t][m] = 0.f;
 
   // With several tile-rows per workgroup a chunk's activation slices are read
   // from LDS once into registers and reused for every tile-row; with one they
@@ -177,9 +182,18 @@ __global__ void __launch_bounds__(512) gemv_lut4_kernel(Lut4Args a) {
     }
   };
 
-  St ring[2];
-  int c = wave;
-  if (c < NC) load_stage(0, c, ring[0]);  // weights in flight while the tables fill
+  constexpr int R = TPW >= 2 ? 2 : D;
+  St ring[R];
+  // the first chunks of row group rt0 (zeros past the last chunk or row)
+  auto prologue = [&]() {
+    if constexpr (TPW >= 2) {
+      load_stage(0, wave, ring[0]);
+    } else {
+#pragma unroll
+      for (int k = 0; k + 1 < R; ++k) load_stage(0, wave + k * WK, ring[k]);
+    }
+  };
+  prologue();  // weights in flight while the tables fill
 
   // pair table: 256 pair values, then 64 lane-major copies of each
   {
@@ -218,6 +232,15 @@ __global__ void __launch_bounds__(512) gemv_lut4_kernel(Lut4Args a) {
     __syncthreads();
   }
 
+  // Persistent: the table and the staged activations serve every row group
+  // rg = blockIdx.x, blockIdx.x + gridDim.x, ...  The next group's first
+  // chunks are issued before this group's reduction.
+  for (int rg = blockIdx.x; rg < NRG; rg += gridDim.x) {
+#pragma unroll
+  for (int t = 0; t < TPW; ++t)
+#pragma unroll
+    for (int m = 0; m < MT; ++m) acc[t][m] = 0.f;
+  int c = wave;
   if constexpr (TPW >= 2) {
     for (; c < NC; c += WK) {
       load_xc(c);
@@ -233,18 +256,23 @@ __global__ void __launch_bounds__(512) gemv_lut4_kernel(Lut4Args a) {
       }
     }
   } else {
-    // one tile-row: chunks alternate between the two slots
-    for (; c < NC; c += 2 * WK) {
-      load_stage(0, c + WK, ring[1]);
-      __builtin_amdgcn_sched_barrier(0);
-      compute(0, c, ring[0]);
-      __builtin_amdgcn_sched_barrier(0);
-      load_stage(0, c + 2 * WK, ring[0]);
-      __builtin_amdgcn_sched_barrier(0);
-      compute(0, c + WK, ring[1]);
-      __builtin_amdgcn_sched_barrier(0);
+    // one tile-row: chunks c = wave + i WK through the R-slot ring; the loads
+    // stay unconditional (zeros past the last chunk), only the compute is
+    // skipped there
+    for (; c < NC; c += R * WK) {
+#pragma unroll
+      for (int k = 0; k < R; ++k) {
+        load_stage(0, c + (k + R - 1) * WK, ring[(k + R - 1) % R]);
+        __builtin_amdgcn_sched_barrier(0);
+        if (c + k * WK < NC) compute(0, c + k * WK, ring[k]);
+        __builtin_amdgcn_sched_barrier(0);
+      }
     }
   }
+
+  const int rtc = rt0;
+  rt0 = (rg + (int)gridDim.x) * TPW;
+  prologue();  // past the last group: rows out of range, zeros
 
 #pragma unroll
   for (int t = 0; t < TPW; ++t)
@@ -253,12 +281,14 @@ __global__ void __launch_bounds__(512) gemv_lut4_kernel(Lut4Args a) {
       const float v = quarter_sum(acc[t][m]);
       if (lane < 16) red[((wave * TPW + t) * MT + m) * 16 + lane] = v;
     }
-  __syncthreads();
+  lds_barrier();  // LDS only: the next group's loads stay in flight
   reduce_waves(red, TPW * MT * 16, WK, [&](int e, float sum) {
     const int r = e & 15, m = (e >> 4) % MT, t = (e >> 4) / MT;
-    const int row = (rt0 + t) * 16 + r;
+    const int row = (rtc + t) * 16 + r;
     if (m0 + m < M && row < N) a.y[(size_t)(m0 + m) * N + row] = f2h(sum);
   });
+  lds_barrier();  // the partial area is written again by the next group
+  }
 }
 
 constexpr size_t LUT4_LDS_LIMIT = 160 * 1024;
@@ -267,36 +297,63 @@ size_t lut4_lds_bytes(int mt, int tpw, int wk, int K) {
   return TABLE_BYTES + xarea_bytes(mt, K) + (size_t)wk * tpw * mt * 16 * 4;
 }
 
-template <int MT, int NG, int TPW>
+template <int MT, int NG, int TPW, int D>
 hipError_t launch_l(const Lut4Args& a, const Lut4Cfg& c, hipStream_t s) {
   const int NT = (a.N + 15) / 16;
-  const dim3 grid((NT + TPW - 1) / TPW, (a.M + MT - 1) / MT);
+  const int NRG = (NT + TPW - 1) / TPW;
+  const int MY = (a.M + MT - 1) / MT;
   const dim3 block(64 * c.wk);
   const size_t lds = lut4_lds_bytes(MT, TPW, c.wk, a.K);
   if (lds > LUT4_LDS_LIMIT) return hipErrorInvalidValue;
   const bool sal = (a.K / 128) % NG == 0 && reinterpret_cast<uintptr_t>(a.absmax) % (4 * NG) == 0;
   static bool raised = false;  // every launch needs more than the default 64 KB of dynamic LDS
   if (!raised) {
-    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&gemv_lut4_kernel<MT, NG, TPW, true>),
+    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&gemv_lut4_kernel<MT, NG, TPW, D, true>),
                                        hipFuncAttributeMaxDynamicSharedMemorySize, (int)LUT4_LDS_LIMIT);
     if (e == hipSuccess)
-      e = hipFuncSetAttribute(reinterpret_cast<const void*>(&gemv_lut4_kernel<MT, NG, TPW, false>),
+      e = hipFuncSetAttribute(reinterpret_cast<const void*>(&gemv_lut4_kernel<MT, NG, TPW, D, false>),
                               hipFuncAttributeMaxDynamicSharedMemorySize, (int)LUT4_LDS_LIMIT);
     if (e != hipSuccess) return e;
     raised = true;
   }
+  // persistent grid: no more workgroups than are resident at once (each
+  // builds its table once and walks row groups).  Residency per CU is asked
+  // once per (alignment, waves, LDS size) and remembered.
+  static int occ[2][9];
+  static size_t occ_lds[2][9];
+  int dev = 0, cus = 0;
+  hipError_t e0 = hipGetDevice(&dev);
+  if (e0 == hipSuccess) e0 = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+  if (e0 == hipSuccess && occ_lds[sal][c.wk] != lds) {
+    int per_cu = 0;
+    e0 = hipOccupancyMaxActiveBlocksPerMultiprocessor(
+        &per_cu, sal ? reinterpret_cast<const void*>(&gemv_lut4_kernel<MT, NG, TPW, D, true>)
+                     : reinterpret_cast<const void*>(&gemv_lut4_kernel<MT, NG, TPW, D, false>),
+        (int)block.x, lds);
+    if (e0 == hipSuccess) {
+      occ[sal][c.wk] = std::max(per_cu, 1);
+      occ_lds[sal][c.wk] = lds;
+    }
+  }
+  if (e0 != hipSuccess) return e0;
+  const long slots = std::max(1L, (long)cus * occ[sal][c.wk] / MY);
+  const dim3 grid((unsigned)std::min<long>(NRG, slots), MY);
   if (sal)
-    hipLaunchKernelGGL((gemv_lut4_kernel<MT, NG, TPW, true>), grid, block, lds, s, a);
+    hipLaunchKernelGGL((gemv_lut4_kernel<MT, NG, TPW, D, true>), grid, block, lds, s, a);
   else
-    hipLaunchKernelGGL((gemv_lut4_kernel<MT, NG, TPW, false>), grid, block, lds, s, a);
+    hipLaunchKernelGGL((gemv_lut4_kernel<MT, NG, TPW, D, false>), grid, block, lds, s, a);
   return hipGetLastError();
 }
 
 template <int MT>
 hipError_t launch_lm(const Lut4Args& a, const Lut4Cfg& c, hipStream_t s) {
-  switch (c.tpw * 10 + c.ng) {
-    case 11: return launch_l<MT, 1, 1>(a, c, s);
-    case 24: return launch_l<MT, 4, 2>(a, c, s);
+  switch (c.tpw * 100 + c.ng * 10 + (c.tpw >= 2 ? 2 : c.d)) {
+    case 112: return launch_l<MT, 1, 1, 2>(a, c, s);
+    case 114: return launch_l<MT, 1, 1, 4>(a, c, s);
+    case 118: return launch_l<MT, 1, 1, 8>(a, c, s);
+    case 122: return launch_l<MT, 2, 1, 2>(a, c, s);
+    case 124: return launch_l<MT, 2, 1, 4>(a, c, s);
+    case 242: return launch_l<MT, 4, 2, 2>(a, c, s);
   }
   return hipErrorInvalidValue;
 }
@@ -314,19 +371,15 @@ Lut4Cfg pick_lut4(int M, int N, int K) {
   Lut4Cfg c;
   c.mt = M <= 1 ? 1 : 2;
   if ((size_t)K > lut4_max_k(c.mt)) c.mt = 1;
-  const long nt = (N + 15) / 16;
   const int G = K / 128;
-  // sweeps on MI355X (Llama-3-8B layers, M = 1, 2): one tile-row per
-  // workgroup only for the narrowest layers
-  if (nt <= 256) {
-    c.tpw = 1;
-    c.ng = 1;
-  } else {
-    c.tpw = 2;
-    c.ng = 4;
-  }
-  const int nc = (G + c.ng - 1) / c.ng;
-  c.wk = nc < 8 ? nc : 8;
+  (void)N;
+  // sweeps on MI355X (Llama-3-8B and 70B layers, M = 1, 2) with the
+  // persistent grid: one tile-row per row group, one-group chunks and 8
+  // waves everywhere; a 4-slot ring once K > 4096
+  c.tpw = 1;
+  c.ng = 1;
+  c.d = K > 4096 ? 4 : 2;
+  c.wk = G < 8 ? G : 8;
   return c;
 }
 

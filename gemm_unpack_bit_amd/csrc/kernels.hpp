@@ -49,8 +49,10 @@ struct Lut4Args {
 };
 // mt = activation rows per workgroup (1, 2); tpw = tile-rows per workgroup
 // (1 with ng = 1, or 2 with ng = 4); wk = waves per workgroup (1..8)
+// LUT4 launch: mt activation rows, tpw tile-rows per workgroup (1, 2), ng
+// groups per chunk, wk waves, d chunks per wave in flight-ring (tpw 1 only)
 struct Lut4Cfg {
-  int mt, tpw, ng, wk;
+  int mt, tpw, ng, wk, d;
 };
 Lut4Cfg pick_lut4(int M, int N, int K);
 size_t lut4_max_k(int mt);  // largest K the LDS staging holds at mt rows

@@ -32,6 +32,25 @@ def test_lut4_small_shapes(N, K, M):
     assert_within(host(y), y_ref, A, f"lut4 M={M} N={N} K={K}")
 
 
+@pytest.mark.parametrize("M,N,K", [(1, 300, 2176), (2, 200, 2048), (3, 64, 512), (16, 40, 1152)])
+def test_lut4_every_launch_shape(monkeypatch, M, N, K):
+    """Every launch shape: one tile-row per workgroup with 1- and 2-group
+    chunks through 2-, 4- and 8-slot rings, two tile-rows with 4-group
+    chunks, 1 to 8 waves, one and two staged activation rows."""
+    say("lut4 launch shapes", M, N, K)
+    c = synth.lut4_case(N + K + M, M, N, K)
+    wq, a, lut = _upload(c)
+    x = dev(c["x"])
+    y_ref, A = ref.gemv_lut4(c["x"], c["codes"], c["absmax"], c["lut"])
+    cfgs = [(1, ng, wk, mt, d) for ng in (1, 2) for wk in (1, 3, 8) for mt in (1, 2) for d in (2, 4, 8)
+            if not (ng == 2 and d == 8)]
+    cfgs += [(2, 4, wk, mt, 2) for wk in (1, 3, 8) for mt in (1, 2)]
+    for cfg in cfgs:
+        monkeypatch.setenv("QGEMV_LUT4_CFG", ",".join(map(str, cfg)))
+        y = host(q.lut4(x, wq, a, lut))
+        assert_within(y, y_ref, A, f"lut4 M={M} N={N} K={K} cfg={cfg}")
+
+
 def test_lut4_one_hot_is_exact():
     """x = e_k: y[n] = fp16(lut[q] * a) exactly (a single product, rounded once)."""
     say("lut4 one-hot")
