@@ -21,9 +21,9 @@ kernel (gate+up, the largest matrix; average launch duration = a region of K
 back-to-back launches of that layer alone, timed the same way), "cpu_baseline"
 (the float64 CPU oracle on a bounded row sample, host cores), "layers"
 (per-layer us/call, same method), "variants" (W2, W8, W4 at M = 4 and 16,
-LUT4, outliers, codebook on the same four layers: per-layer launch time and
-algorithmic bytes, sampled rows checked against the oracle first; not part of
-`value`).  roofline.traffic = HBM bytes per launch of
+LUT4, outliers, codebook on the same four layers, and the codebook on the
+70B-shaped layers at M = 1 and 4: per-layer launch time and algorithmic
+bytes, sampled rows checked against the oracle first; not part of `value`).  roofline.traffic = HBM bytes per launch of
 that kernel from rocprofv3 FETCH_SIZE / WRITE_SIZE (scaled by a device copy of
 known size), read from profiles/; null when the kernel sources changed since.
 
@@ -261,7 +261,8 @@ def measured_traffic():
 
 
 # ---------------------------------------------------------------------------
-# the other variants on the same four layers (reported beside the headline,
+# the other variants on the same four layers, and the codebook on the 70B
+# layers (reported beside the headline,
 # not part of `value`): each layer's cache-cold launch time, algorithmic bytes
 # per launch, sampled rows checked against the oracle first
 # ---------------------------------------------------------------------------
@@ -273,6 +274,9 @@ VARIANTS = {
     "lut4_m1": dict(kind="lut4", bits=4, m=1),
     "outlier_m1": dict(kind="outlier", bits=4, m=1),
     "codebook_m1": dict(kind="codebook", bits=2, m=1),
+    # the codebook workload's own shapes: the 70B layers at M = 1 and 4
+    "codebook_70b_m1": dict(kind="codebook", bits=2, m=1, layers="70b"),
+    "codebook_70b_m4": dict(kind="codebook", bits=2, m=4, layers="70b"),
 }
 
 
@@ -323,7 +327,8 @@ def measure_variants(torch, q, dev, timer, n):
     out = {}
     for vname, v in VARIANTS.items():
         layers, total_us, total_bytes = {}, 0.0, 0
-        for idx, (name, (N, K)) in enumerate(synth.LLAMA3_8B_LAYERS.items()):
+        shapes = synth.LLAMA_70B_LAYERS if v.get("layers") == "70b" else synth.LLAMA3_8B_LAYERS
+        for idx, (name, (N, K)) in enumerate(shapes.items()):
             t, call, oracle, y, nbytes = variant_layer(torch, q, dev, v["kind"], v["bits"], v["m"], idx, N, K)
             call(t)
             rows = np.linspace(0, N - 1, 8).astype(np.int64)
