@@ -249,19 +249,21 @@ int qgemv_codebook(int M, int N, int K, const uint16_t* x, const uint32_t* codes
              overlaps(ws, ws_bytes, codebook, 256 * 4 * 2) || overlaps(ws, ws_bytes, scales, (size_t)N * (K / 128) * 2)))
     return QGEMV_ERR_VALUE;
   qg::CodebookCfg c = qg::pick_codebook(M, N, K);
-  // tuning override: "1,wk,pp,r" (stationary) or "0,wk,ks" (sequential)
+  // tuning override: "1,wk,pp,r[,mb]" (stationary) or "0,wk,ks" (sequential)
   if (const char* e = std::getenv("QGEMV_CODEBOOK_CFG")) {
-    int kind, wk, p1, p2 = 0;
-    if (std::sscanf(e, "%d,%d,%d,%d", &kind, &wk, &p1, &p2) >= 3) {
+    int kind, wk, p1, p2 = 0, p3 = 1;
+    if (std::sscanf(e, "%d,%d,%d,%d,%d", &kind, &wk, &p1, &p2, &p3) >= 3) {
       c.wk = wk;
       if (kind == 1) {
         c.pp = p1;
         c.r = p2;
         c.ks = 1;
+        c.mb = p3;
       } else {
         c.pp = 0;
         c.r = 0;
         c.ks = p1;
+        c.mb = 1;
       }
     }
   }

@@ -379,6 +379,199 @@ __global__ void __launch_bounds__(PP == 4 ? 512 : 1024) gemv_codebook_stat_kerne
   }
 }
 
+// Batched stationary kernel (M >= 2): as the stationary kernel, but one
+// Psumbook serves MB batch rows: entry (s, c) holds the MB rows' partial sums
+// as consecutive fp16 (2 MB bytes), so one 4- or 8-byte LDS read per code
+// serves every row of the batch block, and the lookups no longer scale with
+// M.  Each row's value is added to its fp32 partial by one v_dot2 against a
+// unit pair.  Segment rows are 512 MB + 16 bytes apart: the build's 16-byte
+// stores of 32 segments spread over the banks.  Batch rows past M read zero
+// activations and are not stored.
+template <int MB, int PP, bool SAL>
+__global__ void __launch_bounds__(512) gemv_codebook_statb_kernel(CodebookArgs a, int R) {
+  constexpr uint32_t SEG = 64u * PP;
+  constexpr uint32_t EB = 2u * MB;              // bytes per entry
+  constexpr uint32_t BS = 256u * EB + 16u;      // bytes per segment row
+  constexpr uint32_t PBYTES = SEG * BS;
+  constexpr uint32_t SB = 65535u / BS + 1u;     // segments whose offsets fit the 16-bit immediate
+  // LDS: [Psumbook SEG x BS][codebook 256 x 8 B][activation segments MB x SEG x 8 B]
+  __shared__ __attribute__((aligned(16))) uint32_t lsm[(PBYTES + 2048u + MB * SEG * 8u) / 4];
+  char* const lds = reinterpret_cast<char*>(lsm);
+  u2* const stg = reinterpret_cast<u2*>(lds + PBYTES);
+
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int WK = blockDim.x >> 6;
+  const int M = a.M, N = a.N, K = a.K;
+  const int G = K / 128;
+  const int NCB = K / 64;
+  const int NB = (N + 63) / 64;
+  const int KP = K / (256 * PP);
+  const int MBLK = (M + MB - 1) / MB;
+  const uint32_t b = blockIdx.x;
+  const int mb = (int)((b >> 3) % (uint32_t)MBLK);
+  const uint32_t u = (b / (8u * (uint32_t)MBLK)) * 8u + (b & 7u);
+  if (u >= (uint32_t)R * (uint32_t)KP) return;  // padding: the whole workgroup
+  const int r = (int)(u % (uint32_t)R), kp = (int)(u / (uint32_t)R);
+  const int m0 = mb * MB;
+
+  const int RS = R * WK;
+  const int rb0 = r * WK + wave;
+  const int cnt = rb0 < NB ? (NB - 1 - rb0) / RS + 1 : 0;
+
+  const rsrc_t rc = make_rsrc(a.codes, (uint32_t)NB * NCB * 1024u);
+  const rsrc_t rs = make_rsrc(a.scales, (uint32_t)N * G * 2u);
+
+  struct St {
+    u4 c[4 * PP];
+    uint32_t s[PP];
+  };
+  auto load_stage = [&](int i, St& st) {
+    const bool bv = i < cnt;
+    const int rb = rb0 + i * RS;
+    const uint32_t sw =
+        __builtin_amdgcn_readfirstlane(((uint32_t)(bv ? rb : 0) * NCB + 4u * PP * (uint32_t)kp) * 1024u);
+    const uint32_t vc = bv ? 16u * lane : OOB;
+#pragma unroll
+    for (int j = 0; j < 4 * PP; ++j) st.c[j] = bload16<CPOL_NT>(rc, vc + 1024u * j, sw);
+    const uint32_t row = (uint32_t)rb * 64u + lane;
+    const uint32_t vs = bv && row < (uint32_t)N ? (row * (uint32_t)G + 2u * PP * (uint32_t)kp) * 2u : OOB;
+#pragma unroll
+    for (int j = 0; j < PP; ++j) {
+      if constexpr (SAL)
+        st.s[j] = bload4(rs, vs + 4u * j);
+      else
+        st.s[j] = (uint32_t)bload2(rs, vs + 4u * j) | ((uint32_t)bload2(rs, vs + 4u * j + 2u) << 16);
+    }
+  };
+
+  // codebook rows and the MB rows' activation segments first (loads return in
+  // order, so the build waits for these only), then the code prefetch
+  constexpr int NST = (256 + MB * (int)SEG + 63) / 64;  // staged entries per thread at 64 threads
+  u2 sv[NST];
+  {
+    const rsrc_t rcb = make_rsrc(a.codebook, 2048u);
+    const rsrc_t rx = make_rsrc(a.x, (uint32_t)M * K * 2u);
+#pragma unroll
+    for (int j = 0; j < NST; ++j) {
+      const int i = threadIdx.x + j * (int)blockDim.x;
+      const int e = i - 256, m = e / (int)SEG, sg = e - m * (int)SEG;
+      const bool xv = i >= 256 && i < 256 + MB * (int)SEG && m0 + m < M;
+      const uint32_t xo = xv ? ((uint32_t)(m0 + m) * K + 4u * (SEG * (uint32_t)kp + (uint32_t)sg)) * 2u : OOB;
+      sv[j] = i < 256 ? __builtin_bit_cast(u2, __builtin_amdgcn_raw_buffer_load_b64(rcb, 8u * i, 0, 0))
+                      : __builtin_bit_cast(u2, __builtin_amdgcn_raw_buffer_load_b64(rx, xo, 0, 0));
+    }
+  }
+  constexpr int D = PP == 1 ? 4 : 3;
+  St ring[D];
+#pragma unroll
+  for (int k = 0; k + 1 < D; ++k) load_stage(k, ring[k]);
+#pragma unroll
+  for (int j = 0; j < NST; ++j) {
+    const int i = threadIdx.x + j * (int)blockDim.x;
+    if (i < 256 + MB * (int)SEG) stg[i] = sv[j];
+  }
+  __syncthreads();
+  // Build: 2 PP segment blocks x 8 centroid blocks, MB v_mfma_f32_32x32x8_f16
+  // each (one per batch row); lane l then holds, per register quartet g, 4
+  // consecutive centroids x MB rows = 8 MB contiguous bytes of one segment
+  {
+    const int li = lane & 31;
+    const bool klo = lane < 32;
+    const uint32_t pw = (uint32_t)li * BS + 4u * EB * (uint32_t)(lane >> 5);
+    for (int p = wave; p < 16 * PP; p += WK) {
+      const uint32_t sb = (uint32_t)(p % (2 * PP)), cb = (uint32_t)(p / (2 * PP));
+      const u2 av = stg[32u * cb + li];
+      const u2 A = {klo ? av.x : 0u, klo ? av.y : 0u};
+      f16v d[MB];
+#pragma unroll
+      for (int m = 0; m < MB; ++m) {
+        const u2 bv = stg[256u + (uint32_t)m * SEG + 32u * sb + li];
+        const u2 B = {klo ? bv.x : 0u, klo ? bv.y : 0u};
+        d[m] = __builtin_amdgcn_mfma_f32_32x32x8f16(__builtin_bit_cast(h4v, A), __builtin_bit_cast(h4v, B), f16v{}, 0,
+                                                    0, 0);
+      }
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        char* const dst = lds + pw + sb * (32u * BS) + (32u * cb + 8u * g) * EB;
+        // centroid i of the quartet, row m: half i MB + m
+        _Float16 hv[4 * MB];
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+#pragma unroll
+          for (int m = 0; m < MB; ++m) hv[i * MB + m] = (_Float16)d[m][4 * g + i];
+#pragma unroll
+        for (int q = 0; q < MB / 2; ++q) {
+          u4 v;
+#pragma unroll
+          for (int w = 0; w < 4; ++w)
+            v[w] = (uint32_t)__builtin_bit_cast(uint16_t, hv[8 * q + 2 * w]) |
+                   ((uint32_t)__builtin_bit_cast(uint16_t, hv[8 * q + 2 * w + 1]) << 16);
+          *reinterpret_cast<u4*>(dst + 16u * q) = v;
+        }
+      }
+    }
+  }
+  __syncthreads();
+
+  const h2 e0 = {(_Float16)1.0f, (_Float16)0.0f}, e1 = {(_Float16)0.0f, (_Float16)1.0f};
+  auto step = [&](int i, const St& st, St& nxt) {
+    load_stage(i + D - 1, nxt);
+    float acc[MB];
+#pragma unroll
+    for (int m = 0; m < MB; ++m) acc[m] = 0.f;
+#pragma unroll
+    for (int g = 0; g < 2 * PP; ++g) {
+      float part[MB];
+#pragma unroll
+      for (int m = 0; m < MB; ++m) part[m] = 0.f;
+#pragma unroll
+      for (int t = 0; t < 2; ++t) {
+#pragma unroll
+        for (int dw = 0; dw < 4; ++dw) {
+          const uint32_t w = st.c[2 * g + t][dw];
+#pragma unroll
+          for (int bb = 0; bb < 4; ++bb) {
+            const uint32_t sg = 32u * g + 16u * t + 4u * dw + bb;
+            const uint32_t addr = __builtin_amdgcn_ubfe(w, 8 * bb, 8) * EB + (sg / SB) * (SB * BS);
+            const char* const src = lds + addr + BS * (sg % SB);
+            if constexpr (MB == 2) {
+              const h2 v = as_h2(*reinterpret_cast<const uint32_t*>(src));
+              part[0] = dot2(v, e0, part[0]);
+              part[1] = dot2(v, e1, part[1]);
+            } else {
+              const u2 v = *reinterpret_cast<const u2*>(src);
+              part[0] = dot2(as_h2(v.x), e0, part[0]);
+              part[1] = dot2(as_h2(v.x), e1, part[1]);
+              part[2] = dot2(as_h2(v.y), e0, part[2]);
+              part[3] = dot2(as_h2(v.y), e1, part[3]);
+            }
+          }
+        }
+      }
+      const float sc = h2f((uint16_t)(st.s[g / 2] >> (16 * (g % 2))));
+#pragma unroll
+      for (int m = 0; m < MB; ++m) acc[m] = fmaf(sc, part[m], acc[m]);
+    }
+    const uint32_t row = (uint32_t)(rb0 + i * RS) * 64u + lane;
+    if (row < (uint32_t)N) {
+#pragma unroll
+      for (int m = 0; m < MB; ++m) {
+        if (m0 + m >= M) break;
+        if (KP == 1)
+          a.y[(size_t)(m0 + m) * N + row] = f2h(acc[m]);
+        else
+          a.ws[((size_t)kp * M + m0 + m) * N + row] = acc[m];
+      }
+    }
+  };
+  for (int i = 0; i < cnt; i += D) {
+#pragma unroll
+    for (int k = 0; k < D; ++k)
+      if (i + k < cnt) step(i + k, ring[k], ring[(k + D - 1) % D]);
+  }
+}
+
 // y[i] = fp16(sum over k < KS of ws[k * MN + i]).  A workgroup takes 64
 // outputs; wave j adds parts j, j + 8, j + 16, ... (loads issued 8 at a time,
 // each a 256-byte row), and wave 0 adds the 8 wave sums in order: a fixed
@@ -416,6 +609,12 @@ void* seq_kernel_ptr(bool sal) {
              : reinterpret_cast<void*>(&gemv_codebook_seq_kernel<NSB, false>);
 }
 
+template <int MB, int PP>
+void* statb_kernel_ptr(bool sal) {
+  return sal ? reinterpret_cast<void*>(&gemv_codebook_statb_kernel<MB, PP, true>)
+             : reinterpret_cast<void*>(&gemv_codebook_statb_kernel<MB, PP, false>);
+}
+
 template <int PP>
 void* stat_kernel_ptr(bool sal) {
   return sal ? reinterpret_cast<void*>(&gemv_codebook_stat_kernel<PP, true>)
@@ -433,26 +632,39 @@ size_t codebook_ws_bytes(const CodebookCfg& c, int M, int N, int K) {
   return parts > 1 ? (size_t)parts * M * N * 4 : 0;
 }
 
-// Fitted to sweeps on MI355X (8B- and 70B-shaped layers, M = 1 and 4).
+// Fitted to sweeps on MI355X (8B- and 70B-shaped layers, M = 1, 2 and 4).
 //  * The stationary kernel wins where there are many rows to stream through
-//    each Psumbook: N >= 10240 at M = 1, and at M >= 2 any layer of 32M
-//    weights or more (its M workgroups then share each code read through
-//    L2).  About 256 workgroups, two pairs per part once K >= 8192.
+//    each Psumbook: N >= 10240 at M = 1 (two pairs per part once K >= 8192,
+//    about 256 workgroups), and at M >= 2 any layer of 32M weights or more.
+//  * At M >= 2 its Psumbook entries hold a block of batch rows (2 at M = 2
+//    or N < 8192, else 4), so one lookup serves the whole block: one pair per
+//    part, 8 waves with 4-row entries (4 with 2-row ones), about 256
+//    workgroups in all.  70B gate+up at M = 4: 98 -> 52 us.
 //  * Elsewhere (fewer rows, or K long against N) the sequential kernel, with
 //    K split in whole pairs until the grid holds about 384 workgroups.
 CodebookCfg pick_codebook(int M, int N, int K) {
   CodebookCfg c;
   c.wk = 4;
+  c.mb = 1;
   const long NB = (N + 63) / 64;
-  const long rg = (NB + c.wk - 1) / c.wk;  // row groups of one workgroup
   const long HN = K / 256;
   const bool stat = M == 1 ? N >= 10240 : (long)N * K >= (32L << 20);
-  if (stat) {
+  if (stat && M >= 2) {
+    c.mb = M == 2 || N < 8192 ? 2 : 4;
+    c.wk = c.mb == 4 ? 8 : 4;
+    c.pp = 1;
+    c.ks = 1;
+    const long rg = (NB + c.wk - 1) / c.wk;
+    const long units = HN * ((M + c.mb - 1) / c.mb);  // workgroups per row slice
+    c.r = (int)std::max(1L, std::min(rg, (256 + units / 2) / units));
+  } else if (stat) {
     c.pp = K >= 8192 && HN % 2 == 0 ? 2 : 1;
     c.ks = 1;
+    const long rg = (NB + c.wk - 1) / c.wk;
     const long KP = HN / c.pp;
-    c.r = (int)std::max(1L, std::min(rg, (256 + KP * M - 1) / (KP * M)));
+    c.r = (int)std::max(1L, std::min(rg, (256 + KP - 1) / KP));
   } else {
+    const long rg = (NB + c.wk - 1) / c.wk;
     c.pp = 0;
     c.r = 0;
     c.ks = 1;
@@ -464,6 +676,7 @@ CodebookCfg pick_codebook(int M, int N, int K) {
 CodebookCfg codebook_fallback() {
   CodebookCfg c;
   c.wk = 4;
+  c.mb = 1;
   c.pp = 0;
   c.r = 0;
   c.ks = 1;
@@ -475,15 +688,21 @@ hipError_t launch_gemv_codebook(const CodebookArgs& a, const CodebookCfg& c, hip
   const int parts = codebook_parts(c, a.K);
   const bool sal = reinterpret_cast<uintptr_t>(a.scales) % 4 == 0;
   if (c.pp > 0) {
-    // four pairs: 133 KB of Psumbook, one workgroup per CU, at most 8 waves
-    if ((c.pp != 1 && c.pp != 2 && c.pp != 4) || (c.pp == 4 && c.wk > 8) || (a.K / 256) % c.pp || c.r < 1 ||
-        c.r > (1 << 20))
+    // four pairs, or two pairs of 2-row entries, or one pair of 4-row entries:
+    // about 133 KB of Psumbook, one workgroup per CU, at most 8 waves
+    const bool big = c.pp * c.mb >= 4 || c.mb > 1;  // (the batched kernels: at most 8 waves)
+    if ((c.pp != 1 && c.pp != 2 && c.pp != 4) || (c.mb != 1 && c.mb != 2 && c.mb != 4) || c.pp * c.mb > 4 ||
+        (big && c.wk > 8) || (a.K / 256) % c.pp || c.r < 1 || c.r > (1 << 20))
       return hipErrorInvalidValue;
     if (parts > 1 && !a.ws) return hipErrorInvalidValue;
     const long units = (long)c.r * parts;
-    const long blocks = (units + 7) / 8 * 8 * a.M;
+    const long blocks = (units + 7) / 8 * 8 * ((a.M + c.mb - 1) / c.mb);
     if (blocks >= (1L << 31)) return hipErrorInvalidValue;
-    void* const kern = c.pp == 1 ? stat_kernel_ptr<1>(sal) : c.pp == 2 ? stat_kernel_ptr<2>(sal) : stat_kernel_ptr<4>(sal);
+    void* const kern = c.mb == 4   ? statb_kernel_ptr<4, 1>(sal)
+                       : c.mb == 2 ? (c.pp == 1 ? statb_kernel_ptr<2, 1>(sal) : statb_kernel_ptr<2, 2>(sal))
+                       : c.pp == 1 ? stat_kernel_ptr<1>(sal)
+                       : c.pp == 2 ? stat_kernel_ptr<2>(sal)
+                                   : stat_kernel_ptr<4>(sal);
     int r = c.r;
     void* args[] = {const_cast<CodebookArgs*>(&a), &r};
     hipError_t e = hipLaunchKernel(kern, dim3((unsigned)blocks), dim3(64 * c.wk), args, 0, s);

@@ -71,11 +71,12 @@ struct CodebookArgs {
   float* ws;
 };
 // A codebook launch.  pp > 0 (1, 2, 4): the stationary kernel, one K part of pp pairs
-// (256 k each) per workgroup and r row slices; pp == 0: the sequential kernel,
-// ks K ranges per row block (ks == 1 needs no workspace).  wk = waves per
+// (256 k each) per workgroup and r row slices, its Psumbook entries holding mb
+// batch rows (1, 2, 4; pp * mb <= 4); pp == 0: the sequential kernel, ks K
+// ranges per row block (ks == 1 needs no workspace).  wk = waves per
 // workgroup (1, 2, 4, 8, 16).
 struct CodebookCfg {
-  int wk, pp, r, ks;
+  int wk, pp, r, ks, mb;
 };
 CodebookCfg pick_codebook(int M, int N, int K);
 CodebookCfg codebook_fallback();

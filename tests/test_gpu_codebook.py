@@ -46,7 +46,8 @@ def test_codebook_small_shapes(use_ws, N, K, M):
 @pytest.mark.parametrize("M,N,K", [(1, 300, 3584), (3, 200, 2048), (16, 70, 1536), (2, 1000, 512)])
 def test_codebook_every_launch_shape(monkeypatch, M, N, K):
     """Both kernels at every workgroup size (1..16 waves, so every split of
-    the build): the stationary one with one, two and four pairs per workgroup and
+    the build): the stationary one with one, two and four pairs per workgroup,
+    Psumbook entries of 1, 2 and 4 batch rows, and
     1 to all row slices, the sequential one with K splits up to one 256-k pair
     per range; each against the oracle."""
     say("codebook launch shapes", M, N, K)
@@ -59,6 +60,9 @@ def test_codebook_every_launch_shape(monkeypatch, M, N, K):
     cfgs = [f"0,{wk},{ks}" for wk in (1, 2, 4, 8, 16) for ks in sorted({1, 2, 3, K // 256})]
     cfgs += [f"1,{wk},{pp},{r}" for wk in (1, 2, 4, 8, 16) for pp in (1, 2, 4) for r in sorted({1, 2, 3, NB})
              if (K // 256) % pp == 0 and not (pp == 4 and wk > 8)]
+    # batched Psumbook entries: 2 or 4 batch rows per lookup
+    cfgs += [f"1,{wk},{pp},{r},{mb}" for wk in (1, 2, 4, 8) for mb in (2, 4) for pp in (1, 2) for r in sorted({1, 3, NB})
+             if (K // 256) % pp == 0 and pp * mb <= 4]
     for cfg in cfgs:
         monkeypatch.setenv("QGEMV_CODEBOOK_CFG", cfg)
         y = host(q.codebook(x, codes, cb, s, ws=ws))
