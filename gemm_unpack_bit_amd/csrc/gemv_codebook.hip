@@ -33,16 +33,19 @@
 //    the segment rows are 520 bytes apart (256 fp16 + 8 bytes of padding), so
 //    the 32 segments of a store land in distinct banks.  Each wave keeps the
 //    codebook rows it multiplies in registers for the whole kernel.
-//  * Work split: a workgroup holds WK waves, one 64-row block each, and a K
-//    range of whole pairs; one build serves 64 * WK rows.  With K split, each
-//    range writes fp32 partial sums to the caller's workspace and a second,
-//    small kernel adds the ranges of every output in K order, so the result
-//    is deterministic and no workgroup waits on another.  Batch rows are
-//    grid z.
-//  * Per pair: LDS barrier / build / LDS barrier / lookups, with the next
-//    pair's codes, scales and activation segments in flight meanwhile.  The
-//    barriers wait for LDS traffic only, so those prefetches stay outstanding
-//    across them.
+//  * Three kernels share this design.  The stationary kernel gives each
+//    workgroup one K part (1, 2 or 4 pairs) and streams many row blocks
+//    through its Psumbook, built once, with no barrier after the build.  The
+//    batched stationary kernel (M >= 2) stores the partial sums of 2 or 4
+//    batch rows in each Psumbook entry, so one lookup serves them all.  The
+//    sequential kernel gives each workgroup WK row blocks and a K range, and
+//    per pair runs LDS barrier / build / LDS barrier / lookups, with the next
+//    pair's codes, scales and activation segments in flight meanwhile (the
+//    barriers wait for LDS traffic only); it serves small layers and calls
+//    without a workspace.
+//  * K parts write fp32 partial sums to the caller's workspace and a second,
+//    small kernel adds the parts of every output in a fixed order, so the
+//    result is deterministic and no workgroup waits on another.
 #include <algorithm>
 
 #include "common.hpp"
