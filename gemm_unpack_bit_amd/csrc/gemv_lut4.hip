@@ -193,33 +193,47 @@ __global__ void __launch_bounds__(512, MT == 1 ? 4 : 2) gemv_lut4_kernel(Lut4Arg
       for (int k = 0; k + 1 < R; ++k) load_stage(0, wave + k * WK, ring[k]);
     }
   };
+  // Start-up loads, in the order they are needed: the table entries, then the
+  // first pass of activations, then the weight prefetch.  A wave's loads
+  // return in order, so building the table waits for the 32-byte table only,
+  // and staging the activations never waits for the weights behind them.
+  uint32_t tlo[4], thi[4];  // table values of entries e = threadIdx.x + j blockDim.x
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int e = threadIdx.x + j * (int)blockDim.x;
+    tlo[j] = bload2(rl, e < 256 ? 2u * (e & 15) : OOB);
+    thi[j] = bload2(rl, e < 256 ? 2u * (e >> 4) : OOB);
+  }
+  const int X8 = XK / 8, n16 = MT * X8;
+  auto x_pass = [&](int i0, u4* v) {
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int i = i0 + u * blockDim.x;
+      const int m = i / X8, k8 = i - m * X8;
+      v[u] = bload16(rx, i < n16 && m0 + m < M && k8 < K / 8 ? ((uint32_t)(m0 + m) * K + 8u * k8) * 2u : OOB);
+    }
+  };
+  u4 xfirst[4];
+  x_pass(threadIdx.x, xfirst);
   prologue();  // weights in flight while the tables fill
 
   // pair table: 256 pair values, then 64 lane-major copies of each
   {
     uint32_t* pairs = reinterpret_cast<uint32_t*>(lds + TABLE_BYTES);  // scratch in the x area
-    for (int e = threadIdx.x; e < 256; e += blockDim.x) {
-      const uint32_t lo = bload2(rl, 2u * (e & 15));
-      const uint32_t hi = bload2(rl, 2u * (e >> 4));
-      pairs[e] = lo | (hi << 16);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int e = threadIdx.x + j * (int)blockDim.x;
+      if (e < 256) pairs[e] = tlo[j] | (thi[j] << 16);
     }
-    __syncthreads();
+    lds_barrier();
     for (int i = threadIdx.x; i < 256 * TABLE_COPIES; i += blockDim.x) lsm[i] = pairs[i / TABLE_COPIES];
-    __syncthreads();
+    lds_barrier();  // (LDS only: the weight prefetch stays in flight)
   }
   // activations of rows m0 .. m0 + MT - 1; each 8-k run stored as
   // (x0,x2),(x4,x6),(x1,x3),(x5,x7); the 4 pad runs per row read zeros
   {
     u4* xw = reinterpret_cast<u4*>(lds + TABLE_BYTES);
-    const int X8 = XK / 8, n16 = MT * X8;
-    for (int i0 = threadIdx.x; i0 < n16; i0 += 4 * blockDim.x) {
-      u4 v[4];
-#pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        const int i = i0 + u * blockDim.x;
-        const int m = i / X8, k8 = i - m * X8;
-        v[u] = bload16(rx, i < n16 && m0 + m < M && k8 < K / 8 ? ((uint32_t)(m0 + m) * K + 8u * k8) * 2u : OOB);
-      }
+    auto put = [&](int i0, const u4* v) {
 #pragma unroll
       for (int u = 0; u < 4; ++u) {
         const u4 p = {__builtin_amdgcn_perm(v[u][1], v[u][0], 0x05040100u),
@@ -228,8 +242,14 @@ __global__ void __launch_bounds__(512, MT == 1 ? 4 : 2) gemv_lut4_kernel(Lut4Arg
                       __builtin_amdgcn_perm(v[u][3], v[u][2], 0x07060302u)};
         if (i0 + u * blockDim.x < n16) xw[i0 + u * blockDim.x] = p;
       }
+    };
+    put(threadIdx.x, xfirst);
+    for (int i0 = threadIdx.x + 4 * blockDim.x; i0 < n16; i0 += 4 * blockDim.x) {
+      u4 v[4];
+      x_pass(i0, v);
+      put(i0, v);
     }
-    __syncthreads();
+    lds_barrier();
   }
 
   // Persistent: the table and the staged activations serve every row group
