@@ -62,6 +62,12 @@ def sparse_exact(x, N, rows, cols, vals):
     return y
 
 
+def gemv_dense_exact(x, w):
+    M, K = x.shape
+    return [[sum((_fr(x[m, k]) * _fr(w[n, k]) for k in range(K)), Fraction(0)) for n in range(w.shape[0])]
+            for m in range(M)]
+
+
 def to_f64(mat) -> np.ndarray:
     return np.array([[float(v) for v in row] for row in mat], dtype=np.float64)
 

@@ -60,6 +60,15 @@ def _gemv_rows(x64, wfun, N, rows=None):
     return x64 @ w.T, ax @ np.abs(w).T
 
 
+def gemv_dense(x, w, rows=None):
+    """y = x W^T for an fp16 weight W [N, K] used as given: the matrix product
+    that follows an eager dequantization (Fast NF4 Dequantization Kernels page,
+    method: the dequantized fp16 weight goes back to global memory for a
+    separate product)."""
+    w = np.asarray(w)
+    return _gemv_rows(_f64(x), lambda r: _f64(w[r]), w.shape[0], rows)
+
+
 # ----------------------------------------------------------------------------
 # uniform W2 / W4 / W8
 # ----------------------------------------------------------------------------
@@ -134,6 +143,16 @@ def sparse_part(x, N, o_rows, o_cols, o_vals):
         np.add.at(ys[m], r, v * x64[m, c])
         np.add.at(As[m], r, np.abs(v * x64[m, c]))
     return ys, As
+
+
+def add_sparse(y_prior, x, o_rows, o_cols, o_vals):
+    """y_prior + S x^T: the separate sparse kernel of the unfused outlier
+    pattern adds into the output the dense kernel already wrote (FlashQuant
+    abstract: the two paths share activations and outputs).  The tolerance
+    scale is |y_prior| + sum |v x|."""
+    yp = _f64(y_prior)
+    ys, As = sparse_part(x, yp.shape[1], o_rows, o_cols, o_vals)
+    return yp + ys, np.abs(yp) + As
 
 
 def gemv_outlier(x, codes, scales, zeros, o_rows, o_cols, o_vals, g=128, rows=None):

@@ -32,7 +32,7 @@ _M1 = np.uint64(0xBF58476D1CE4E5B9)
 _M2 = np.uint64(0x94D049BB133111EB)
 
 # sub-stream identifiers (fixed, so that every consumer draws the same bytes)
-S_X, S_CODES, S_SCALES, S_ZEROS, S_OPOS, S_OVAL, S_CB, S_LUT = range(1, 9)
+S_X, S_CODES, S_SCALES, S_ZEROS, S_OPOS, S_OVAL, S_CB, S_LUT, S_W, S_Y = range(1, 11)
 
 
 def _mix64(z: np.ndarray) -> np.ndarray:
@@ -115,6 +115,17 @@ def uniform_case(seed, M, N, K, bits, g=128, s_lo=0.001, s_hi=0.02):
         zeros=codes(seed, S_ZEROS, N * G, bits).reshape(N, G),
         bits=bits,
     )
+
+
+def dense_case(seed, M, N, K, std=0.02):
+    """fp16 weight [N, K] ~ N(0, std) (the magnitude of a dequantized weight)
+    and activations x ~ N(0, 1): the input of a plain fp16 GEMV."""
+    return dict(x=activations(seed, M, K), w=f16(normal(seed, S_W, N * K, std)).reshape(N, K))
+
+
+def output_prior(seed, M, N, std=1.0) -> np.ndarray:
+    """An fp16 [M, N] output already written by a dense kernel, ~ N(0, std)."""
+    return f16(normal(seed, S_Y, M * N, std)).reshape(M, N)
 
 
 def normal_quantile_levels(n=16) -> np.ndarray:

@@ -282,3 +282,97 @@ def test_planted_mistakes_are_caught(monkeypatch, mutant):
         except AssertionError:
             failures += 1
     assert failures >= 1
+
+
+# ----------------------------------------------------------------------------
+# unfused baselines: the plain fp16 product and the additive sparse step
+# ----------------------------------------------------------------------------
+def test_dense_gemv_worked_example():
+    """By hand: x = (1, 2, -1, 0.5, 0, ...), W rows (2, -1, 3, 4, 0, ...) and
+    (0.25, 0.5, 0, -2, 0, ...): y = (2 - 2 - 3 + 2, 0.25 + 1 + 0 - 1) = (-1, 0.25),
+    A = (2 + 2 + 3 + 2, 0.25 + 1 + 0 + 1) = (9, 2.25)."""
+    K = 128
+    x = np.zeros((1, K), np.float16)
+    x[0, :4] = [1, 2, -1, 0.5]
+    w = np.zeros((2, K), np.float16)
+    w[0, :4] = [2, -1, 3, 4]
+    w[1, :4] = [0.25, 0.5, 0, -2]
+    y, A = ref.gemv_dense(x, w)
+    assert y.tolist() == [[-1.0, 0.25]] and A.tolist() == [[9.0, 2.25]]
+
+
+def test_dense_gemv_selects_columns():
+    """A 0/1 weight with its one 1 of row n at column (5n + 3) mod K copies that
+    column of x (a transposed, reversed or shifted operand fails)."""
+    M, N, K = 3, 40, 128
+    x = synth.activations(21, M, K)
+    w = np.zeros((N, K), dtype=np.float16)
+    cols = (5 * np.arange(N) + 3) % K
+    w[np.arange(N), cols] = 1.0
+    y, A = ref.gemv_dense(x, w)
+    assert np.array_equal(y, x.astype(np.float64)[:, cols])
+    assert np.array_equal(A, np.abs(y))
+
+
+def test_dense_gemv_matches_exact_and_reduces_to_uniform():
+    """Exact brute force on a tiny random case; and the eager chain's
+    definition: the plain product over the dequantized weight is the uniform
+    GEMV (pinned above), on all rows and on a row subset."""
+    c = synth.dense_case(22, 2, 5, 128)
+    y, A = ref.gemv_dense(c["x"], c["w"])
+    ye = exact.to_f64(exact.gemv_dense_exact(c["x"], c["w"]))
+    assert np.allclose(y, ye, rtol=0, atol=1e-12 * A.max())
+    u = synth.uniform_case(23, 2, 24, 256, 4)
+    w = ref.dequant_uniform(u["codes"], u["scales"], u["zeros"])
+    yd, Ad = ref.gemv_dense(u["x"], w)
+    yu, Au = ref.gemv_uniform(u["x"], u["codes"], u["scales"], u["zeros"])
+    assert np.allclose(yd, yu, rtol=0, atol=1e-12 * Au.max()) and np.allclose(Ad, Au, rtol=1e-12)
+    rows = [0, 7, 23]
+    yr, Ar = ref.gemv_dense(u["x"], w, rows=rows)
+    assert np.array_equal(yr, yd[:, rows]) and np.array_equal(Ar, Ad[:, rows])
+
+
+def test_add_sparse_worked_example_and_special_cases():
+    """By hand: x[1] = 2, x[200] = -1; prior y = (1, 1, 1, -0.5); outliers
+    (row 2, col 1, 0.5), (2, 200, 0.25), (0, 200, 1.5):
+    y = (1 - 1.5, 1, 1 + 1 - 0.25, -0.5), A = (1 + 1.5, 1, 1 + 1 + 0.25, 0.5)."""
+    K = 256
+    x = np.zeros((1, K), np.float16)
+    x[0, 1], x[0, 200] = 2.0, -1.0
+    yp = np.array([[1.0, 1.0, 1.0, -0.5]], np.float16)
+    y, A = ref.add_sparse(yp, x, [2, 2, 0], [1, 200, 200], np.array([0.5, 0.25, 1.5], np.float16))
+    assert y.tolist() == [[-0.5, 1.0, 1.75, -0.5]] and A.tolist() == [[2.5, 1.0, 2.25, 0.5]]
+    none = np.zeros(0, np.int32)
+    y0, _ = ref.add_sparse(yp, x, none, none, np.zeros(0, np.float16))
+    assert np.array_equal(y0, yp.astype(np.float64))
+    c = synth.outlier_case(24, 2, 32, 256, frac=0.03)
+    ys, _ = ref.add_sparse(np.zeros((2, 32), np.float16), c["x"], c["o_rows"], c["o_cols"], c["o_vals"])
+    assert np.array_equal(ys, exact.to_f64(exact.sparse_exact(c["x"], 32, c["o_rows"], c["o_cols"], c["o_vals"])))
+
+
+def _dense_mut_reversed_k(x, w, rows=None):
+    w = np.asarray(w)
+    return ref._gemv_rows(ref._f64(x), lambda r: ref._f64(w[r])[:, ::-1], w.shape[0], rows)
+
+
+def _dense_mut_signed_A(x, w, rows=None):
+    x64, w64 = ref._f64(x), ref._f64(w)
+    y = x64 @ w64.T
+    return y, np.abs(y)
+
+
+def _dense_mut_row_shift(x, w, rows=None):
+    w = np.asarray(w)
+    return ref._gemv_rows(ref._f64(x), lambda r: ref._f64(w[(r + 1) % w.shape[0]]), w.shape[0], rows)
+
+
+@pytest.mark.parametrize("mutant", [_dense_mut_reversed_k, _dense_mut_signed_A, _dense_mut_row_shift])
+def test_planted_dense_mistakes_are_caught(monkeypatch, mutant):
+    monkeypatch.setattr(ref, "gemv_dense", mutant)
+    failures = 0
+    for pin in (test_dense_gemv_worked_example, test_dense_gemv_selects_columns):
+        try:
+            pin()
+        except AssertionError:
+            failures += 1
+    assert failures >= 1
