@@ -277,18 +277,67 @@ VARIANTS = {
     # the codebook workload's own shapes: the 70B layers at M = 1 and 4
     "codebook_70b_m1": dict(kind="codebook", bits=2, m=1, layers="70b"),
     "codebook_70b_m4": dict(kind="codebook", bits=2, m=4, layers="70b"),
+    # unfused baselines: what fusion buys.  fp16 weights (no quantization),
+    # eager dequantization + dense GEMV, and the dense W4 kernel + separate SpMV
+    "f16_dense_m1": dict(kind="dense", bits=16, m=1),
+    "eager_w4a16_m1": dict(kind="eager", bits=4, m=1),
+    "eager_lut4_m1": dict(kind="eager_lut4", bits=4, m=1),
+    "outlier_unfused_m1": dict(kind="outlier_unfused", bits=4, m=1),
 }
 
 
 def variant_layer(torch, q, dev, kind, bits, m, idx, N, K):
-    """Host case, device inputs (one copy), launch function and algorithmic bytes."""
+    """Host case, device inputs (one copy), launch function, algorithmic bytes
+    and, for the two-kernel baselines, each kernel alone with its bytes."""
     from oracle import reference as ref
 
     seed = synth.seed_for(2, 16 * idx + bits + 4 * m)
     up = lambda a: torch.from_numpy(np.ascontiguousarray(a)).to(dev)
     y = torch.empty((m, N), dtype=torch.float16, device=dev)
     io = 2 * m * K + 2 * m * N
-    if kind == "uniform":
+    parts = None
+    if kind == "dense":
+        c = synth.dense_case(seed, m, N, K)
+        t = dict(x=up(c["x"]), w=up(c["w"]))
+        call = lambda t: q.gemv_f16(t["x"], t["w"], out=y)
+        oracle = lambda rows: ref.gemv_dense(c["x"], c["w"], rows=rows)
+        nbytes = 2 * N * K + io
+    elif kind == "eager":
+        c = synth.uniform_case(seed, m, N, K, bits)
+        t = dict(x=up(c["x"]), wq=q.pack(up(c["codes"]), bits), s=up(c["scales"]),
+                 z=q.pack_zeros(up(c["zeros"]), bits), w=torch.empty((N, K), dtype=torch.float16, device=dev))
+        deq = lambda t: q.dequant(t["wq"], t["s"], t["z"], bits, K, out=t["w"])
+        mv = lambda t: q.gemv_f16(t["x"], t["w"], out=y)
+        call = lambda t: (deq(t), mv(t))
+        oracle = lambda rows: ref.gemv_uniform(c["x"], c["codes"], c["scales"], c["zeros"], rows=rows)
+        b_deq = alg_bytes(N, K, bits, 0) + 2 * N * K
+        parts = {"dequant": (deq, b_deq), "gemv_f16": (mv, 2 * N * K + io)}
+        nbytes = b_deq + 2 * N * K + io
+    elif kind == "eager_lut4":
+        c = synth.lut4_case(seed, m, N, K)
+        t = dict(x=up(c["x"]), wq=q.pack(up(c["codes"]), 4), a=up(c["absmax"]), lut=up(c["lut"]),
+                 w=torch.empty((N, K), dtype=torch.float16, device=dev))
+        deq = lambda t: q.dequant_lut4(t["wq"], t["a"], t["lut"], K, out=t["w"])
+        mv = lambda t: q.gemv_f16(t["x"], t["w"], out=y)
+        call = lambda t: (deq(t), mv(t))
+        oracle = lambda rows: ref.gemv_lut4(c["x"], c["codes"], c["absmax"], c["lut"], rows=rows)
+        b_deq = N * K // 2 + N * (K // 64) * 2 + 32 + 2 * N * K
+        parts = {"dequant_lut4": (deq, b_deq), "gemv_f16": (mv, 2 * N * K + io)}
+        nbytes = b_deq + 2 * N * K + io
+    elif kind == "outlier_unfused":
+        c = synth.outlier_case(seed, m, N, K)
+        ptr, rec = q.tilecoo_encode(N, K, c["o_rows"], c["o_cols"], c["o_vals"])
+        t = dict(x=up(c["x"]), wq=q.pack(up(c["codes"]), 4), s=up(c["scales"]),
+                 z=q.pack_zeros(up(c["zeros"]), 4), p=up(ptr.view(np.int32)), r=up(rec.view(np.int32)))
+        dense = lambda t: q.w4a16(t["x"], t["wq"], t["s"], t["z"], out=y)
+        sp = lambda t: q.spmv_tilecoo(t["x"], t["p"], t["r"], y)
+        call = lambda t: (dense(t), sp(t))
+        oracle = lambda rows: ref.gemv_outlier(c["x"], c["codes"], c["scales"], c["zeros"], c["o_rows"],
+                                               c["o_cols"], c["o_vals"], rows=rows)
+        b_sp = 4 * rec.size + 4 * ptr.size + 2 * m * K + 4 * m * N
+        parts = {"w4a16": (dense, alg_bytes(N, K, 4, m)), "spmv_tilecoo": (sp, b_sp)}
+        nbytes = alg_bytes(N, K, 4, m) + 4 * rec.size + 4 * ptr.size
+    elif kind == "uniform":
         c = synth.uniform_case(seed, m, N, K, bits)
         t = dict(x=up(c["x"]), wq=q.pack(up(c["codes"]), bits), s=up(c["scales"]),
                  z=q.pack_zeros(up(c["zeros"]), bits))
@@ -318,7 +367,7 @@ def variant_layer(torch, q, dev, kind, bits, m, idx, N, K):
         call = lambda t: q.codebook(t["x"], t["codes"], t["cb"], t["s"], ws=ws, out=y)
         oracle = lambda rows: ref.gemv_codebook(c["x"], c["codes"], c["codebook"], c["scales"], rows=rows)
         nbytes = N * K // 4 + N * (K // 128) * 2 + 256 * 4 * 2 + io
-    return t, call, oracle, y, nbytes
+    return t, call, oracle, y, nbytes, parts
 
 
 def measure_variants(torch, q, dev, timer, n):
@@ -329,7 +378,8 @@ def measure_variants(torch, q, dev, timer, n):
         layers, total_us, total_bytes = {}, 0.0, 0
         shapes = synth.LLAMA_70B_LAYERS if v.get("layers") == "70b" else synth.LLAMA3_8B_LAYERS
         for idx, (name, (N, K)) in enumerate(shapes.items()):
-            t, call, oracle, y, nbytes = variant_layer(torch, q, dev, v["kind"], v["bits"], v["m"], idx, N, K)
+            t, call, oracle, y, nbytes, parts = variant_layer(torch, q, dev, v["kind"], v["bits"], v["m"], idx,
+                                                              N, K)
             call(t)
             rows = np.linspace(0, N - 1, 8).astype(np.int64)
             y_ref, A = oracle(rows)
@@ -344,6 +394,11 @@ def measure_variants(torch, q, dev, timer, n):
             us = timer.region_us(fn, n, host_cost(torch, fn)) / n
             layers[name] = {"us_per_call": round(us, 3), "GBps": round(nbytes / us / 1e3, 1),
                             "pct_peak": round(nbytes / us / 1e3 / PEAK_HBM_GBS * 100, 1), "bytes": nbytes}
+            for pname, (pcall, pbytes) in (parts or {}).items():  # each kernel of the sequence alone
+                pfn = lambda i, pcall=pcall: pcall(copies[i % R])
+                pus = timer.region_us(pfn, n, host_cost(torch, pfn)) / n
+                layers[name][pname] = {"us_per_call": round(pus, 3), "GBps": round(pbytes / pus / 1e3, 1),
+                                       "bytes": pbytes}
             total_us += us
             total_bytes += nbytes
             del copies, t

@@ -44,6 +44,10 @@ _SIGS = {
     "qgemv_codebook": (_i, [_i, _i, _i, _vp, _vp, _vp, _vp, _vp, _vp, _sz, _vp]),
     "qgemv_codebook_workspace_bytes": (_sz, [_i, _i, _i]),
     "qgemv_tilecoo_encode": (_i, [_i, _i, ctypes.c_int64, _vp, _vp, _vp, _vp, _vp]),
+    "qgemv_dequant": (_i, [_i, _i, _i, _vp, _vp, _vp, _vp, _vp]),
+    "qgemv_dequant_lut4": (_i, [_i, _i, _vp, _vp, _vp, _vp, _vp]),
+    "qgemv_gemv_f16": (_i, [_i, _i, _i, _vp, _vp, _vp, _vp]),
+    "qgemv_spmv_tilecoo": (_i, [_i, _i, _i, _vp, _vp, _vp, ctypes.c_int64, _vp, _vp]),
 }
 
 
@@ -290,3 +294,88 @@ def codebook(x, codes, cb, scales, ws=None, out=None):
     _check("qgemv_codebook", lib().qgemv_codebook(M, N, K, _ptr(x), _ptr(codes), _ptr(cb), _ptr(scales), _ptr(out),
                                                   ws_ptr, ws_bytes, _stream(x)))
     return out
+
+
+# ---------------------------------------------------------------------------
+# unfused baselines (eager dequantization + dense GEMV; separate SpMV)
+# ---------------------------------------------------------------------------
+
+def _out_w(N, K, like, out):
+    torch = _torch()
+    if out is None:
+        return torch.empty((N, K), dtype=torch.float16, device=like.device)
+    _need(out, torch.float16, "out")
+    if tuple(out.shape) != (N, K):
+        raise ValueError("out must be [N, K]")
+    return out
+
+
+def dequant(wq, scales, zeros, bits, K, out=None):
+    """Eager dequantization: fp16 W [N, K] row-major, w = s * (q - z), each
+    weight the exact product rounded once.  Arguments as `uniform`."""
+    torch = _torch()
+    _need(wq, torch.int32, "wq")
+    _need(scales, torch.float16, "scales")
+    _need(zeros, torch.int32, "zeros")
+    N = scales.shape[0]
+    need = packed_words(bits, N, K)
+    if need and wq.numel() != need:
+        raise ValueError("wq does not hold N x K device-layout codes")
+    out = _out_w(N, K, wq, out)
+    _check("qgemv_dequant", lib().qgemv_dequant(bits, N, K, _ptr(wq), _ptr(scales), _ptr(zeros), _ptr(out),
+                                                _stream(wq)))
+    return out
+
+
+def dequant_lut4(wq, absmax, lut, K, out=None):
+    """Eager dequantization of 4-bit table codes: w = lut[q] * absmax[n, k/64]."""
+    torch = _torch()
+    _need(wq, torch.int32, "wq")
+    _need(absmax, torch.float16, "absmax")
+    _need(lut, torch.float16, "lut")
+    N = absmax.shape[0]
+    need = packed_words(4, N, K)
+    if need and wq.numel() != need:
+        raise ValueError("wq does not hold N x K device-layout 4-bit codes")
+    if lut.numel() != 16:
+        raise ValueError("lut must hold 16 entries")
+    out = _out_w(N, K, wq, out)
+    _check("qgemv_dequant_lut4", lib().qgemv_dequant_lut4(N, K, _ptr(wq), _ptr(absmax), _ptr(lut), _ptr(out),
+                                                          _stream(wq)))
+    return out
+
+
+def gemv_f16(x, w, out=None):
+    """Dense fp16 GEMV y = x . w^T (w [N, K] row-major), fp32 accumulation."""
+    torch = _torch()
+    _need(x, torch.float16, "x")
+    _need(w, torch.float16, "w")
+    M, K = x.shape
+    N = w.shape[0]
+    if w.shape[1] != K:
+        raise ValueError("w must be [N, K]")
+    if out is None:
+        out = torch.empty((M, N), dtype=torch.float16, device=x.device)
+    else:
+        _need(out, torch.float16, "out")
+    _check("qgemv_gemv_f16", lib().qgemv_gemv_f16(M, N, K, _ptr(x), _ptr(w), _ptr(out), _stream(x)))
+    return out
+
+
+def spmv_tilecoo(x, tile_ptr, tile_rec, y):
+    """y += x . S^T for Tile-COO outliers (in place on y [M, N]; returns y)."""
+    torch = _torch()
+    _need(x, torch.float16, "x")
+    _need(tile_ptr, torch.int32, "tile_ptr")
+    _need(y, torch.float16, "y")
+    M, K = x.shape
+    N = y.shape[1]
+    if tile_rec is not None:
+        _need(tile_rec, torch.int32, "tile_rec")
+    nnz = 0 if tile_rec is None else tile_rec.numel()
+    if tile_ptr.numel() != int(lib().qgemv_tilecoo_ptr_len(N, K)):
+        raise ValueError("tile_ptr does not match N x K")
+    _check("qgemv_spmv_tilecoo", lib().qgemv_spmv_tilecoo(M, N, K, _ptr(x), _ptr(tile_ptr),
+                                                          _ptr(tile_rec if nnz else None), nnz, _ptr(y),
+                                                          _stream(x)))
+    return y

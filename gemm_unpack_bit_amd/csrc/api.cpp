@@ -291,4 +291,86 @@ int qgemv_lut4(int M, int N, int K, const uint16_t* x, const uint32_t* wq, const
   return hip_status(qg::launch_gemv_lut4(a, lut4_cfg(M, N, K), reinterpret_cast<hipStream_t>(stream)));
 }
 
+// ---- unfused baselines ----
+
+namespace {
+int check_nk(int N, int K) {
+  if (N < 1 || K < QGEMV_GROUP || K % QGEMV_GROUP) return QGEMV_ERR_SHAPE;
+  if ((long)N * K * 2 >= 1L << 31 || (long)((N + 15) / 16) * 16 * K >= 1L << 31) return QGEMV_ERR_SHAPE;
+  return QGEMV_OK;
+}
+}  // namespace
+
+int qgemv_dequant(int bits, int N, int K, const uint32_t* wq, const uint16_t* scales, const uint32_t* zeros,
+                  uint16_t* w, qgemv_stream_t stream) {
+  if (!wq || !scales || !zeros || !w) return QGEMV_ERR_NULL;
+  if (!valid_bits(bits)) return QGEMV_ERR_UNSUPPORTED;
+  int rc = check_nk(N, K);
+  if (rc) return rc;
+  if (!aligned16(wq) || !aligned16(w) || ((uintptr_t)scales & 1u) || ((uintptr_t)zeros & 3u))
+    return QGEMV_ERR_ALIGN;
+  const size_t wbytes = (size_t)N * K * 2;
+  const int G = K / QGEMV_GROUP;
+  if (overlaps(w, wbytes, wq, words(bits, QGEMV_LAYOUT_DEVICE, N, K) * 4) ||
+      overlaps(w, wbytes, scales, (size_t)N * G * 2) ||
+      overlaps(w, wbytes, zeros, words(bits, QGEMV_LAYOUT_PLAIN, N, G) * 4))
+    return QGEMV_ERR_VALUE;
+  qg::DequantArgs a{bits, N, K, wq, scales, zeros, nullptr, nullptr, w};
+  return hip_status(qg::launch_dequant_uniform(a, reinterpret_cast<hipStream_t>(stream)));
+}
+
+int qgemv_dequant_lut4(int N, int K, const uint32_t* wq, const uint16_t* absmax, const uint16_t* lut, uint16_t* w,
+                       qgemv_stream_t stream) {
+  if (!wq || !absmax || !lut || !w) return QGEMV_ERR_NULL;
+  int rc = check_nk(N, K);
+  if (rc) return rc;
+  if (!aligned16(wq) || !aligned16(w) || ((uintptr_t)absmax & 1u) || ((uintptr_t)lut & 1u))
+    return QGEMV_ERR_ALIGN;
+  const size_t wbytes = (size_t)N * K * 2;
+  if (overlaps(w, wbytes, wq, words(4, QGEMV_LAYOUT_DEVICE, N, K) * 4) ||
+      overlaps(w, wbytes, absmax, (size_t)N * (K / QGEMV_LUT_BLOCK) * 2) || overlaps(w, wbytes, lut, 32))
+    return QGEMV_ERR_VALUE;
+  qg::DequantArgs a{4, N, K, wq, nullptr, nullptr, absmax, lut, w};
+  return hip_status(qg::launch_dequant_lut4(a, reinterpret_cast<hipStream_t>(stream)));
+}
+
+int qgemv_gemv_f16(int M, int N, int K, const uint16_t* x, const uint16_t* w, uint16_t* y,
+                   qgemv_stream_t stream) {
+  if (!x || !w || !y) return QGEMV_ERR_NULL;
+  if (M < 1 || M > QGEMV_MAX_M) return QGEMV_ERR_SHAPE;
+  int rc = check_nk(N, K);
+  if (rc) return rc;
+  if ((long)M * K * 2 >= 1L << 31) return QGEMV_ERR_SHAPE;
+  if (!aligned16(x) || !aligned16(w) || ((uintptr_t)y & 1u)) return QGEMV_ERR_ALIGN;
+  const size_t ybytes = (size_t)M * N * 2;
+  if (overlaps(y, ybytes, x, (size_t)M * K * 2) || overlaps(y, ybytes, w, (size_t)N * K * 2))
+    return QGEMV_ERR_VALUE;
+  qg::DenseCfg c = qg::pick_dense(M, N, K);
+  if (const char* e = std::getenv("QGEMV_DENSE_CFG")) {  // tuning override "tpw,s,wk"
+    int tpw, st, wk;
+    if (std::sscanf(e, "%d,%d,%d", &tpw, &st, &wk) == 3) c = {tpw, st, wk};
+  }
+  qg::DenseArgs a{M, N, K, x, w, y};
+  return hip_status(qg::launch_gemv_f16(a, c, reinterpret_cast<hipStream_t>(stream)));
+}
+
+int qgemv_spmv_tilecoo(int M, int N, int K, const uint16_t* x, const uint32_t* tile_ptr, const uint32_t* tile_rec,
+                       int64_t nnz, uint16_t* y, qgemv_stream_t stream) {
+  if (!x || !tile_ptr || !y || (nnz > 0 && !tile_rec)) return QGEMV_ERR_NULL;
+  if (M < 1 || M > QGEMV_MAX_M || N < 1 || K < QGEMV_GROUP || K % QGEMV_GROUP || K > QGEMV_SPMV_MAX_K)
+    return QGEMV_ERR_SHAPE;
+  // x is read at k up to 255 past a tile's start, within the buffer's bounds check
+  if ((long)M * K * 2 + 512 >= 1L << 31 || (long)M * N * 2 >= 1L << 31) return QGEMV_ERR_SHAPE;
+  if (nnz < 0 || nnz > (int64_t)N * K || nnz * 4 >= (int64_t)1 << 31) return QGEMV_ERR_SHAPE;
+  if (!aligned16(x) || ((uintptr_t)tile_ptr & 3u) || ((uintptr_t)tile_rec & 3u) || ((uintptr_t)y & 1u))
+    return QGEMV_ERR_ALIGN;
+  const size_t ybytes = (size_t)M * N * 2;
+  if (overlaps(y, ybytes, x, (size_t)M * K * 2) || overlaps(y, ybytes, tile_ptr, qgemv_tilecoo_ptr_len(N, K) * 4) ||
+      (nnz > 0 && overlaps(y, ybytes, tile_rec, (size_t)nnz * 4)))
+    return QGEMV_ERR_VALUE;
+  if (nnz == 0) return QGEMV_OK;  // nothing to add
+  qg::SpmvArgs a{M, N, K, x, tile_ptr, tile_rec, (int)nnz, y};
+  return hip_status(qg::launch_spmv_tilecoo(a, reinterpret_cast<hipStream_t>(stream)));
+}
+
 }  // extern "C"

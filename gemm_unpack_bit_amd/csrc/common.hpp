@@ -76,10 +76,6 @@ __device__ __forceinline__ uint32_t magic1024x2() {
   return v;
 }
 
-// Workgroup barrier that orders LDS only: each wave waits for its own LDS
-// operations (lgkmcnt 0) and meets the others at s_barrier, while its global
-// loads stay in flight.  __syncthreads() would also wait for every vector
-// memory load (prefetches included), draining a software pipeline.
 // Sum of the values held by lanes n, n + 16, n + 32, n + 48 of a wave,
 // returned in all four lanes, in the fixed order (q0 + q2) + (q1 + q3)
 // (gfx950 permlane swaps; every lane of the wave must take part).
@@ -118,6 +114,10 @@ __device__ __forceinline__ void reduce_waves(const float* red, int OUT, int WK, 
   }
 }
 
+// Workgroup barrier that orders LDS only: each wave waits for its own LDS
+// operations (lgkmcnt 0) and meets the others at s_barrier, while its global
+// loads stay in flight.  __syncthreads() would also wait for every vector
+// memory load (prefetches included), draining a software pipeline.
 __device__ __forceinline__ void lds_barrier() {
   __atomic_signal_fence(__ATOMIC_SEQ_CST);
   __builtin_amdgcn_s_waitcnt(0xC07F);  // vmcnt 63, expcnt 7, lgkmcnt 0

@@ -47,10 +47,9 @@ struct Lut4Args {
   const uint16_t* lut;
   uint16_t* y;
 };
-// mt = activation rows per workgroup (1, 2); tpw = tile-rows per workgroup
-// (1 with ng = 1, or 2 with ng = 4); wk = waves per workgroup (1..8)
-// LUT4 launch: mt activation rows, tpw tile-rows per workgroup (1, 2), ng
-// groups per chunk, wk waves, d chunks per wave in flight-ring (tpw 1 only)
+// LUT4 launch: mt activation rows per workgroup (1, 2), tpw tile-rows per
+// workgroup (1 with ng = 1, or 2 with ng = 4), ng groups per chunk, wk waves
+// (1..8), d chunks in each wave's ring (tpw 1 only)
 struct Lut4Cfg {
   int mt, tpw, ng, wk, d;
 };
@@ -82,6 +81,46 @@ CodebookCfg pick_codebook(int M, int N, int K);
 CodebookCfg codebook_fallback();
 size_t codebook_ws_bytes(const CodebookCfg& c, int M, int N, int K);
 hipError_t launch_gemv_codebook(const CodebookArgs& a, const CodebookCfg& c, hipStream_t s);
+
+// Unfused baselines (unfused.hip): eager dequantization to fp16 W [N, K]
+// row-major (uniform b-bit: bits, wq, scales, zeros; LUT4: wq, absmax, lut),
+// a dense fp16 GEMV over it, and a Tile-COO SpMV that adds x . S^T into y.
+struct DequantArgs {
+  int bits, N, K;
+  const uint32_t* wq;
+  const uint16_t* scales;
+  const uint32_t* zeros;
+  const uint16_t* absmax;
+  const uint16_t* lut;
+  uint16_t* w;
+};
+hipError_t launch_dequant_uniform(const DequantArgs& a, hipStream_t s);
+hipError_t launch_dequant_lut4(const DequantArgs& a, hipStream_t s);
+
+struct DenseArgs {
+  int M, N, K;
+  const uint16_t* x;
+  const uint16_t* w;
+  uint16_t* y;
+};
+// tpw row tiles of 16 per workgroup, s MFMA k-steps (32 k each) per chunk,
+// wk waves: (1, 8), (1, 4), (2, 4) or (4, 4) with wk 1..8
+struct DenseCfg {
+  int tpw, s, wk;
+};
+DenseCfg pick_dense(int M, int N, int K);
+hipError_t launch_gemv_f16(const DenseArgs& a, const DenseCfg& c, hipStream_t s);
+
+struct SpmvArgs {
+  int M, N, K;
+  const uint16_t* x;
+  const uint32_t* tile_ptr;
+  const uint32_t* tile_rec;
+  int nnz;
+  uint16_t* y;
+};
+size_t spmv_lds_bytes(int K);
+hipError_t launch_spmv_tilecoo(const SpmvArgs& a, hipStream_t s);
 
 // bit packing (layout: 0 plain, 1 device = tiled, see pack.hip)
 size_t packed_words(int bits, int layout, int rows, int cols);

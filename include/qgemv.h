@@ -77,6 +77,7 @@ typedef enum {
 #define QGEMV_LUT_BLOCK 64
 #define QGEMV_MAX_M 16
 #define QGEMV_LUT4_MAX_K 48000
+#define QGEMV_SPMV_MAX_K 1048576
 
 /* Library version (major*10000 + minor*100 + patch). */
 int qgemv_version(void);
@@ -255,6 +256,56 @@ int qgemv_codebook(int M, int N, int K, const uint16_t *x, const uint32_t *codes
 /* Workspace bytes qgemv_codebook uses to split K for this shape (0 if it
  * never splits, or on bad arguments). */
 size_t qgemv_codebook_workspace_bytes(int M, int N, int K);
+
+/* ------------------------------------------------------------------------
+ * Unfused baselines: the kernel sequences that the fused entry points above
+ * replace, for measuring what fusion buys.  Same results within the
+ * tolerance; more HBM traffic and one more launch.
+ *
+ * Eager dequantization (Fast NF4 Dequantization Kernels page, method: codes
+ * read from global memory, dequantized on chip, fp16 weights written back
+ * for a separate matrix product; QFactory review, "Problem and motivation":
+ * eager per-element dequantization), writing w [dev] fp16 [N, K] row-major:
+ *
+ *   qgemv_dequant       w[n, k] = s[n, k/128] * (q[n, k] - z[n, k/128]);
+ *                       bits in {2, 4, 8}, wq / scales / zeros as qgemv_uniform
+ *   qgemv_dequant_lut4  w[n, k] = lut[q[n, k]] * absmax[n, k/64];
+ *                       wq / absmax / lut as qgemv_lut4
+ *
+ * Each weight is the exact product rounded once to fp16 (nearest even).
+ * N >= 1, K a positive multiple of 128, N*K*2 < 2^31 (QGEMV_ERR_SHAPE); wq
+ * and w 16-byte aligned, scales / absmax / lut 2-byte, zeros 4-byte
+ * (QGEMV_ERR_ALIGN); w may not overlap an input (QGEMV_ERR_VALUE).
+ * ------------------------------------------------------------------------ */
+int qgemv_dequant(int bits, int N, int K, const uint32_t *wq, const uint16_t *scales,
+                  const uint32_t *zeros, uint16_t *w, qgemv_stream_t stream);
+int qgemv_dequant_lut4(int N, int K, const uint32_t *wq, const uint16_t *absmax,
+                       const uint16_t *lut, uint16_t *w, qgemv_stream_t stream);
+
+/* Dense fp16 GEMV over a dequantized (or any fp16) weight, the second kernel
+ * of the eager pattern:
+ *     y[m, n] = sum_k x[m, k] * w[n, k]     (fp32 accumulation, fp16 out)
+ *   x [dev] fp16 [M, K], w [dev] fp16 [N, K] row-major, y [dev] fp16 [M, N].
+ * 1 <= M <= 16, N >= 1, K a positive multiple of 128, N*K*2 < 2^31
+ * (QGEMV_ERR_SHAPE); x and w 16-byte aligned, y 2-byte (QGEMV_ERR_ALIGN);
+ * y may not overlap an input (QGEMV_ERR_VALUE).  Asynchronous, deterministic. */
+int qgemv_gemv_f16(int M, int N, int K, const uint16_t *x, const uint16_t *w, uint16_t *y,
+                   qgemv_stream_t stream);
+
+/* Separate sparse kernel of the unfused outlier pattern (FlashQuant abstract:
+ * the dense and the sparse path in two kernels sharing activations and
+ * outputs).  Adds the Tile-COO outliers (format of qgemv_outlier) into y:
+ *     y[m, n] = fp16(y[m, n] + sum over records (n, k, v) of v * x[m, k])
+ * with the sum in fp32 in a fixed order; y is read and written (typically the
+ * output of qgemv_w4a16 on the same stream).  Rows without outliers keep
+ * their bits.  1 <= M <= 16, N >= 1, K a positive multiple of 128 and at most
+ * QGEMV_SPMV_MAX_K, 0 <= nnz <= N*K, nnz*4 < 2^31 (QGEMV_ERR_SHAPE); x 16-byte
+ * aligned, tile_ptr and tile_rec 4-byte, y 2-byte (QGEMV_ERR_ALIGN); y may not
+ * overlap an input (QGEMV_ERR_VALUE).  Records are read as given (malformed
+ * ones give wrong values, never an out-of-bounds access).  Asynchronous,
+ * deterministic, no allocation. */
+int qgemv_spmv_tilecoo(int M, int N, int K, const uint16_t *x, const uint32_t *tile_ptr,
+                       const uint32_t *tile_rec, int64_t nnz, uint16_t *y, qgemv_stream_t stream);
 
 /* Entries of tile_ptr for an N x K weight: ceil(N/16) * ceil(K/128) + 1
  * (0 on bad arguments). */

@@ -125,3 +125,39 @@ def test_codebook_validation_without_gpu(L):
     assert L.qgemv_codebook_workspace_bytes(1, 64, 384) == 0
     n = L.qgemv_codebook_workspace_bytes(1, 8192, 28672)
     assert n >= 2 * 4 * 8192                       # few rows, long K: split, one fp32 partial per row and split
+
+
+def test_unfused_validation_without_gpu(L):
+    v = ctypes.c_void_p
+    dq = lambda bits=4, N=64, K=256, wq=FAKE, s=FAKE * 2, z=FAKE * 3, w=FAKE * 64: L.qgemv_dequant(
+        bits, N, K, v(wq), v(s), v(z), v(w), v(0))
+    assert dq(wq=0) == q.ERR_NULL
+    assert dq(bits=3) == q.ERR_UNSUPPORTED
+    assert dq(K=200) == q.ERR_SHAPE
+    assert dq(N=0) == q.ERR_SHAPE
+    assert dq(N=1 << 20, K=1 << 10) == q.ERR_SHAPE      # fp16 W of 2 GiB
+    assert dq(w=FAKE * 64 + 8) == q.ERR_ALIGN
+    assert dq(s=FAKE * 2 + 1) == q.ERR_ALIGN
+    assert dq(w=FAKE * 2) == q.ERR_VALUE                 # W overlaps the scales
+    dl = lambda N=64, K=256, wq=FAKE, a=FAKE * 2, lut=FAKE * 3, w=FAKE * 64: L.qgemv_dequant_lut4(
+        N, K, v(wq), v(a), v(lut), v(w), v(0))
+    assert dl(lut=0) == q.ERR_NULL
+    assert dl(K=64) == q.ERR_SHAPE
+    assert dl(wq=FAKE + 4) == q.ERR_ALIGN
+    assert dl(w=FAKE * 3) == q.ERR_VALUE                 # W overlaps the table
+    gf = lambda M=1, N=64, K=256, x=FAKE, w=FAKE * 2, y=FAKE * 1024: L.qgemv_gemv_f16(
+        M, N, K, v(x), v(w), v(y), v(0))
+    assert gf(w=0) == q.ERR_NULL
+    assert gf(M=17) == q.ERR_SHAPE
+    assert gf(K=100) == q.ERR_SHAPE
+    assert gf(x=FAKE + 2) == q.ERR_ALIGN
+    assert gf(y=FAKE * 2 + 32) == q.ERR_VALUE            # y inside W
+    sp = lambda M=1, N=64, K=256, x=FAKE, p=FAKE * 2, r=FAKE * 3, nnz=10, y=FAKE * 64: L.qgemv_spmv_tilecoo(
+        M, N, K, v(x), v(p), v(r), nnz, v(y), v(0))
+    assert sp(r=0) == q.ERR_NULL
+    assert sp(K=2 * 1048576) == q.ERR_SHAPE              # beyond the on-chip tile_ptr staging
+    assert sp(nnz=-1) == q.ERR_SHAPE
+    assert sp(nnz=64 * 256 + 1) == q.ERR_SHAPE
+    assert sp(p=FAKE * 2 + 2) == q.ERR_ALIGN
+    assert sp(y=FAKE * 3) == q.ERR_VALUE                 # y overlaps the records
+    assert sp(r=0, nnz=0) == q.OK                        # nothing to add: no launch
