@@ -10,6 +10,7 @@
 //   (local_row, local_col) inside a tile.
 #include <algorithm>
 #include <cstdint>
+#include <utility>
 #include <vector>
 
 #include "qgemv.h"
@@ -33,25 +34,26 @@ int qgemv_tilecoo_encode(int N, int K, int64_t nnz, const int32_t* rows, const i
   if (!tile_ptr || (nnz > 0 && (!rows || !cols || !val_bits || !tile_rec))) return QGEMV_ERR_NULL;
   const int KT = (K + TILE_C - 1) / TILE_C;
   const size_t T = qgemv_tilecoo_ptr_len(N, K) - 1;
-  // sort key: tile, local row, local col (unique per position)
-  std::vector<uint64_t> key((size_t)nnz);
+  // sort key per outlier: (tile, local row, local col), unique per position,
+  // paired with the outlier's index (tile indices may need more than 16 bits,
+  // so the key does not share a word with the index)
+  std::vector<std::pair<uint64_t, uint32_t>> key((size_t)nnz);
   for (int64_t i = 0; i < nnz; ++i) {
     const int32_t r = rows[i], c = cols[i];
     if (r < 0 || r >= N || c < 0 || c >= K) return QGEMV_ERR_VALUE;
     if ((val_bits[i] & 0x7C00u) == 0x7C00u) return QGEMV_ERR_VALUE;  // inf or NaN
     const uint64_t t = (uint64_t)(r / TILE_R) * KT + (uint64_t)(c / TILE_C);
-    key[i] = (t << 48) | ((uint64_t)(r % TILE_R) << 40) | ((uint64_t)(c % TILE_C) << 32) | (uint64_t)i;
+    key[i] = {(t << 11) | ((uint64_t)(r % TILE_R) << 7) | (uint64_t)(c % TILE_C), (uint32_t)i};
   }
   std::sort(key.begin(), key.end());
   for (int64_t i = 1; i < nnz; ++i)
-    if ((key[i] >> 32) == (key[i - 1] >> 32)) return QGEMV_ERR_VALUE;  // duplicate position
+    if (key[i].first == key[i - 1].first) return QGEMV_ERR_VALUE;  // duplicate position
   std::fill(tile_ptr, tile_ptr + T + 1, 0u);
-  for (int64_t i = 0; i < nnz; ++i) tile_ptr[(key[i] >> 48) + 1] += 1;
+  for (int64_t i = 0; i < nnz; ++i) tile_ptr[(key[i].first >> 11) + 1] += 1;
   for (size_t t = 0; t < T; ++t) tile_ptr[t + 1] += tile_ptr[t];
   for (int64_t i = 0; i < nnz; ++i) {
-    const uint64_t k = key[i];
-    const uint32_t src = (uint32_t)(k & 0xffffffffu);
-    tile_rec[i] = ((uint32_t)val_bits[src] << 16) | (uint32_t)(((k >> 40) & 0xff) << 8) | (uint32_t)((k >> 32) & 0xff);
+    const uint64_t k = key[i].first;
+    tile_rec[i] = ((uint32_t)val_bits[key[i].second] << 16) | (uint32_t)(((k >> 7) & 15u) << 8) | (uint32_t)(k & 127u);
   }
   return QGEMV_OK;
 }

@@ -13,7 +13,9 @@ if not os.path.exists(q.LIB_PATH):
     pytest.skip("library not built", allow_module_level=True)
 
 
-@pytest.mark.parametrize("N,K,frac", [(128, 128, 0.01), (300, 384, 0.005), (4096, 4096, 0.005), (129, 1000, 0.02)])
+# (4800, 30720): 72,000 tiles, past 16 bits of tile index
+@pytest.mark.parametrize("N,K,frac", [(128, 128, 0.01), (300, 384, 0.005), (4096, 4096, 0.005), (129, 1000, 0.02),
+                                      (4800, 30720, 0.0005)])
 def test_encoder_matches_oracle(N, K, frac):
     nnz = int(frac * N * K)
     pos = synth.unique_positions(N + K, synth.S_OPOS, N * K, nnz)
