@@ -197,18 +197,27 @@ gemv_tiles_kernel(UniformArgs a) {
 
   // outlier variant (SP): LDS after the partials (see sparse_lds_bytes), per
   // wave: MFMA, a 16 x 128 fp16 scratch tile, lane-major (lane l's 32 k of
-  // its row at halves 32 l .. 32 l + 31); VALU, run sums [MAXT][MT][64] fp32;
-  // then the first 64 records of MAXT tiles, loaded straight into LDS
+  // its row at halves 32 l .. 32 l + 31), then the first 64 records of MAXT
+  // tiles, loaded straight into LDS; VALU, VPB 64-record batches loaded
+  // straight into LDS, a batch's rows [64] and products [MT][64]; after the
+  // waves' slots (VALU) the workgroup's tile pointers [TPW G + 1]
   constexpr int MAXT = 8;
-  constexpr int SPW0 = MFMA ? 4096 : MAXT * MT * 256;
-  constexpr int SPW = SPW0 + MAXT * 256;  // bytes per wave
+  constexpr int VPB = 4;
+  constexpr int SPW0 = MFMA ? 4096 : 256 * VPB + 256;
+  constexpr int SPW = MFMA ? SPW0 + MAXT * 256 : SPW0 + MT * 256;  // bytes per wave
   _Float16* sscr = nullptr;
-  float* ssum = nullptr;
+  uint32_t* vrec = nullptr;  // VALU: [VPB][64] prefetched records
+  uint32_t* vrow = nullptr;  // VALU: [64] row keys of a batch
+  float* vprod = nullptr;    // VALU: [MT][64] products of a batch
+  uint32_t* vptr = nullptr;  // VALU: the workgroup's tile pointers
   if constexpr (SP) {
     const size_t redb = MFMA ? (size_t)WK * TPW * 64 * 16 : (size_t)WK * TPW * MT * 16 * 4;
     char* b = reinterpret_cast<char*>(red) + redb + (size_t)wave * SPW;
     sscr = reinterpret_cast<_Float16*>(b);
-    ssum = reinterpret_cast<float*>(b);
+    vrec = reinterpret_cast<uint32_t*>(b);
+    vrow = reinterpret_cast<uint32_t*>(b + 256 * VPB);
+    vprod = reinterpret_cast<float*>(b + 256 * VPB + 256);
+    vptr = reinterpret_cast<uint32_t*>(reinterpret_cast<char*>(red) + redb + (size_t)WK * SPW);
   }
 
   // activation row offsets of this lane (group 0, its k-quarter)
@@ -409,13 +418,26 @@ gemv_tiles_kernel(UniformArgs a) {
   // lane 2 s (2 s + 1) loads the start (end) pointer of slot s, s < MAXT: one
   // load, issued with the activations
   uint32_t pfetch = 0;
+  // VALU: the tile pointers of the workgroup's tile-rows (nvt tiles, nvt + 1
+  // entries), thread i loading entries i, i + blockDim, ... (at most SPP per
+  // thread here; more in stage_x)
+  constexpr int SPP = 2;
+  const int nvt = (min(TPW, NT - rt0)) * G;
+  uint32_t pv[SPP];
   auto stage_x_issue = [&]() {
     if constexpr (XLDS) x_pass(threadIdx.x, xfirst);
     if constexpr (PLDS) pfirst = p_pass(threadIdx.x);
-    if constexpr (SP) {
+    if constexpr (SP && MFMA) {
       int g, t;
       const uint32_t T = tile_of(lane >> 1, g, t) + (lane & 1);
       pfetch = bload4(rtp, lane < 2 * MAXT ? 4u * T : OOB);
+    }
+    if constexpr (SP && !MFMA) {
+#pragma unroll
+      for (int u = 0; u < SPP; ++u) {
+        const int i = threadIdx.x + u * blockDim.x;
+        pv[u] = bload4(rtp, i <= nvt ? ((uint32_t)rt0 * G + i) * 4u : OOB);
+      }
     }
   };
   auto stage_x = [&]() {
@@ -437,10 +459,19 @@ gemv_tiles_kernel(UniformArgs a) {
       if ((int)threadIdx.x < np16) pw[threadIdx.x] = pfirst;
       for (int i = threadIdx.x + blockDim.x; i < np16; i += blockDim.x) pw[i] = p_pass(i);
     }
-    if constexpr (SP) {
+    if constexpr (SP && MFMA) {
       u4* z = reinterpret_cast<u4*>(sscr);
 #pragma unroll
       for (int u = 0; u < SPW / 1024; ++u) z[lane + 64 * u] = u4{0u, 0u, 0u, 0u};
+    }
+    if constexpr (SP && !MFMA) {
+#pragma unroll
+      for (int u = 0; u < SPP; ++u) {
+        const int i = threadIdx.x + u * blockDim.x;
+        if (i <= nvt) vptr[i] = pv[u];
+      }
+      for (int i = threadIdx.x + SPP * blockDim.x; i <= nvt; i += blockDim.x)
+        vptr[i] = bload4(rtp, ((uint32_t)rt0 * G + i) * 4u);
     }
     lds_barrier();
     if constexpr (IDENT) {
@@ -467,18 +498,23 @@ gemv_tiles_kernel(UniformArgs a) {
   };
   // Outliers (FlashQuant abstract: an fp16 sparse path fused with the
   // low-bit dense one, sharing activations and outputs; Tile-COO records).
-  // A Tile-COO tile is the 16 x 128 tile of the dense layout, so a wave's
-  // outliers are those of the tiles of its own chunks.  Each wave loads the
-  // tile pointers of its first MAXT tiles with the activations and, right
-  // after the staging barrier, the first 64 records of each straight into LDS
-  // (they arrive during the dense loop).  After the dense loop the records
-  // meet the activations (VALU: per-lane run sums, below; MFMA: scattered
-  // into the wave's zeroed 16 x 128 fp16 scratch in the lane layout of the
-  // dense tile and multiplied like dequantized weights but unscaled, 4 more
-  // matrix-core steps per tile, then cleared).  Every product is exact and
-  // the order of the sums is fixed, so the result is deterministic.  Record
-  // fields are masked into the tile, so malformed records stay in bounds.
-  uint32_t* lrec = reinterpret_cast<uint32_t*>(reinterpret_cast<char*>(ssum) + SPW0);
+  // A Tile-COO tile is the 16 x 128 tile of the dense layout.
+  //  * VALU engine: the workgroup's records are one contiguous range (its
+  //    tile-rows' tiles are consecutive).  The tile pointers are staged with
+  //    the activations; right after the staging barrier each wave's first two
+  //    64-record batches go straight into LDS (they arrive during the dense
+  //    loop).  After the loop the waves walk their batches (sparse_batch) and
+  //    add the sums of their rows' records into their dense partials, which
+  //    the fixed-order reduction then adds like any other partial.
+  //  * MFMA engine: a wave's outliers are those of the tiles of its own
+  //    chunks; the first 64 records of its first MAXT tiles are prefetched to
+  //    LDS, then scattered into the wave's zeroed 16 x 128 fp16 scratch in the
+  //    lane layout of the dense tile and multiplied like dequantized weights
+  //    but unscaled (4 more matrix-core steps per tile), then cleared.
+  // Every product is exact and the order of the sums is fixed, so the result
+  // is deterministic.  Record fields are masked into the tile, so malformed
+  // records stay in bounds.
+  uint32_t* lrec = reinterpret_cast<uint32_t*>(reinterpret_cast<char*>(sscr) + SPW0);  // (MFMA)
   auto slot_ok = [&](int g, int t) { return g < G && rt0 + t < NT; };
   // start and count of slot s, from the pointers lanes 2 s and 2 s + 1 loaded
   auto slot_ptr = [&](int s, uint32_t& p0, uint32_t& cnt) {
@@ -489,8 +525,23 @@ gemv_tiles_kernel(UniformArgs a) {
     cnt = slot_ok(g, t) ? min(p1 - p0, 2048u) : 0u;  // (a tile holds at most 2048)
   };
   const rsrc_t rrec = make_rsrc(a.tile_rec, (uint32_t)a.nnz * 4u);
+  // VALU: the workgroup's records [vbeg, vend), one contiguous range; wave w
+  // takes the 64-record batches w, w + WK, ...; its first VPB go straight to
+  // LDS here, issued behind the first weight stages
+  uint32_t vbeg = 0, vend = 0;
   auto sparse_issue = [&]() {
-    if constexpr (SP) {
+    if constexpr (SP && !MFMA) {
+      vbeg = __builtin_amdgcn_readfirstlane(vptr[0]);
+      vend = __builtin_amdgcn_readfirstlane(vptr[nvt]);
+      // (a tile holds at most 2048 records: malformed pointers stay bounded)
+      vend = vend < vbeg ? vbeg : min(vend, vbeg + 2048u * (uint32_t)nvt);
+#pragma unroll
+      for (int i = 0; i < VPB; ++i) {
+        const uint32_t r = vbeg + 64u * (wave + WK * i) + lane;
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rrec, vrec + 64 * i, 4, r < vend ? r * 4u : OOB, 0, 0, 0);
+      }
+    }
+    if constexpr (SP && MFMA) {
 #pragma unroll
       for (int s = 0; s < MAXT; ++s) {
         uint32_t p0, cnt;
@@ -500,9 +551,6 @@ gemv_tiles_kernel(UniformArgs a) {
                                                  0, 0, 0);
       }
     }
-  };
-  auto bperm = [&](uint32_t v, int src) -> uint32_t {
-    return (uint32_t)__builtin_amdgcn_ds_bpermute(src << 2, (int)v);
   };
   // Lanes of a wave exchange data through its LDS scratch; LDS operations of
   // one wave complete in order, but without a fence the compiler may assume no
@@ -520,7 +568,7 @@ gemv_tiles_kernel(UniformArgs a) {
     u4 sv[4];
 #pragma unroll
     for (int v = 0; v < 4; ++v) sv[v] = sl[v];
-    if constexpr (MFMA) {
+    {
       f4 dd = f4{0.f, 0.f, 0.f, 0.f};
       const int xa = (min(n, XM - 1) * XK + 128 * g + 32 * kq) / 8;
 #pragma unroll
@@ -534,21 +582,6 @@ gemv_tiles_kernel(UniformArgs a) {
         if (tt == t)
 #pragma unroll
           for (int i = 0; i < 4; ++i) accm[tt][i] += dd[i];
-    } else {
-#pragma unroll
-      for (int m = 0; m < MT; ++m) {
-        float part = 0.f;
-#pragma unroll
-        for (int v = 0; v < 4; ++v) {
-          const u4 xv = XLDS ? xs[(m * XK + 128 * g + 32 * kq) / 8 + v]
-                             : bload16(rx, xoff[m] == OOB ? OOB : xoff[m] + 256u * g + 16u * v);
-#pragma unroll
-          for (int e = 0; e < 4; ++e) part = dot2(as_h2(sv[v][e]), as_h2(xv[e]), part);
-        }
-#pragma unroll
-        for (int tt = 0; tt < TPW; ++tt)
-          if (tt == t) accv[tt][m] += part;
-      }
     }
     for (uint32_t b = 0; b < cnt; b += 64) {  // clear what was written
       const uint32_t rec = b == 0 && have0 ? rec0 : bload4(rrec, b + lane < cnt ? (p0 + b + lane) * 4u : OOB);
@@ -556,117 +589,86 @@ gemv_tiles_kernel(UniformArgs a) {
     }
     wave_fence();
   };
-  // VALU engine: the records of a tile (up to 64, this lane's when `valid`)
-  // go to the lane that holds their row and k-quarter, T = row + 16 (col /
-  // 32).  Records are sorted by (row, col), so those of one target are
-  // consecutive: the last lane of each run adds the run's exact products in
-  // record order (ds_bpermute from the lanes before it) and writes the sum to
-  // the target's entry of sums slot `sl`; each lane then adds its entries in
-  // slot order and zeroes them.  Deterministic.
+  // VALU engine: a batch of 64 records.  Lane i takes record i: its tile is
+  // the last one whose range starts at or before it (binary search over the
+  // staged pointers), its product v x[m][k] is exact, and its row key
+  // (tile-row t, row r) = 16 t + r goes to the wave's slot with the products.
+  // Lane (r, quarter p) then adds, in record order, the products of the
+  // batch's quarter p whose row is r: so the records of a row reach the lanes
+  // of that row, whose partials the reduction below adds across quarters and
+  // waves in a fixed order.  Deterministic; record fields are masked into the
+  // tile-row, so malformed records stay in bounds.
   const _Float16* xh = reinterpret_cast<const _Float16*>(smem);
-  auto run_sums = [&](uint32_t rec, bool valid, int g, int sl) {
-    const uint32_t lc = rec & 127u;
-    const uint32_t T = valid ? ((rec >> 8) & 15u) + 16u * (lc >> 5) : 64u + lane;  // (distinct dummies)
+  float sacc[TPW][MT];
+  auto sparse_batch = [&](uint32_t rec, uint32_t idx) {
+    const bool ok = idx < vend;
+    int j = 0;
+    for (int st = 1 << (31 - __builtin_clz(nvt)); st > 0; st >>= 1)
+      if (j + st < nvt && vptr[j + st] <= idx) j += st;
+    const int t = TPW == 1 ? 0 : (j >= G ? 1 : 0);
+    const uint32_t col = 128u * (uint32_t)(j - t * G) + (rec & 127u);
     const float v = h2f((uint16_t)(rec >> 16));
-    float prod[MT], acc[MT];
 #pragma unroll
     for (int m = 0; m < MT; ++m) {
       float xv;
-      if constexpr (XLDS) xv = (float)xh[m * XK + 128 * g + (int)lc];
-      else xv = h2f(bload2(rx, m0 + m < M ? ((uint32_t)(m0 + m) * K + 128u * g + lc) * 2u : OOB));
-      prod[m] = valid ? v * xv : 0.f;  // exact: a product of two fp16 values
-      acc[m] = prod[m];
+      if constexpr (XLDS) xv = (float)xh[m * XK + col];
+      else xv = h2f(bload2(rx, ok && m0 + m < M ? ((uint32_t)(m0 + m) * K + col) * 2u : OOB));
+      vprod[m * 64 + lane] = ok ? v * xv : 0.f;
     }
-    // (every cross-lane read is made by the whole wave, outside any condition:
-    // a lane masked off in a branch does not supply its value)
-    const uint32_t Tn = bperm(T, min(lane + 1, 63));
-    const uint32_t Tp = bperm(T, max(lane - 1, 0));
-    const bool last = valid && (lane == 63 || Tn != T);
-    // add the products of the earlier lanes of the run, nearest first
-    bool cont = lane >= 1 && Tp == T;
-    for (int k = 1; __builtin_amdgcn_ballot_w64(cont) != 0; ++k) {  // (runs are short)
+    vrow[lane] = ok ? ((rec >> 8) & 15u) + 16u * t : 0xFFFFu;
+    wave_fence();  // (other lanes read these)
+    // the quarter's 16 keys and products, read together (16-byte reads that
+    // every lane of the quarter shares), then added where the row matches
+    u4 kv[4];
+    u4 pv4[MT][4];
 #pragma unroll
-      for (int m = 0; m < MT; ++m) {
-        const float q = __uint_as_float(bperm(__float_as_uint(prod[m]), max(lane - k, 0)));
-        acc[m] = cont ? acc[m] + q : acc[m];
+    for (int v = 0; v < 4; ++v) {
+      kv[v] = reinterpret_cast<const u4*>(vrow)[4 * kq + v];
+#pragma unroll
+      for (int m = 0; m < MT; ++m) pv4[m][v] = reinterpret_cast<const u4*>(vprod + m * 64)[4 * kq + v];
+    }
+#pragma unroll
+    for (int e0 = 0; e0 < 16; ++e0) {
+      const uint32_t key = kv[e0 >> 2][e0 & 3];
+#pragma unroll
+      for (int tt = 0; tt < TPW; ++tt) {
+        const bool hit = key == (uint32_t)(n + 16 * tt);
+#pragma unroll
+        for (int m = 0; m < MT; ++m) sacc[tt][m] += hit ? __uint_as_float(pv4[m][e0 >> 2][e0 & 3]) : 0.f;
       }
-      const uint32_t Tk = bperm(T, max(lane - k - 1, 0));
-      cont = cont && lane >= k + 1 && Tk == T;
     }
-    if (last)
-#pragma unroll
-      for (int m = 0; m < MT; ++m) ssum[(sl * MT + m) * 64 + T] = acc[m];
-  };
-  // (callers fence before: other lanes wrote these entries; and after: other
-  // lanes write them next)
-  auto add_sums = [&](int sl, int t) {
-#pragma unroll
-    for (int m = 0; m < MT; ++m) {
-      float* e = ssum + (sl * MT + m) * 64 + lane;
-      const float v = *e;
-      *e = 0.f;
-#pragma unroll
-      for (int tt = 0; tt < TPW; ++tt)
-        if (tt == t) accv[tt][m] += v;
-    }
-  };
-  // a tile the fast path does not cover: 64 records at a time through slot 0
-  auto sparse_slow = [&](uint32_t p0, uint32_t cnt, int g, int t) {
-    for (uint32_t b = 0; b < cnt; b += 64) {
-      const bool valid = b + lane < cnt;
-      const uint32_t rec = bload4(rrec, valid ? (p0 + b + lane) * 4u : OOB);
-      run_sums(rec, valid, g, 0);
-      wave_fence();
-      add_sums(0, t);
-      wave_fence();
-    }
+    wave_fence();  // (the slot is rewritten by the next batch)
   };
   auto sparse_compute = [&]() {
-    if constexpr (SP) {
+    if constexpr (SP && !MFMA) {
+      __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): the batches are in LDS (issued long before)
+#pragma unroll
+      for (int t = 0; t < TPW; ++t)
+#pragma unroll
+        for (int m = 0; m < MT; ++m) sacc[t][m] = 0.f;
+      for (int i = 0;; ++i) {  // wave-uniform
+        const uint32_t b0 = vbeg + 64u * (wave + WK * i);
+        if (b0 >= vend) break;
+        const uint32_t idx = b0 + lane;
+        const uint32_t rec = i < VPB ? vrec[64 * i + lane] : bload4(rrec, idx < vend ? idx * 4u : OOB);
+        sparse_batch(rec, idx);
+      }
+#pragma unroll
+      for (int t = 0; t < TPW; ++t)
+#pragma unroll
+        for (int m = 0; m < MT; ++m) accv[t][m] += sacc[t][m];
+    }
+    if constexpr (SP && MFMA) {
       __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): the records are in LDS (issued long before)
       const int nci = NC > wave ? (NC - wave + WK - 1) / WK : 0;  // this wave's chunks
       const int ntl = nci * TPW * NG;
-      if constexpr (MFMA) {
 #pragma unroll
-        for (int s = 0; s < MAXT; ++s) {
-          int g, t;
-          (void)tile_of(s, g, t);
-          uint32_t p0, cnt;
-          slot_ptr(s, p0, cnt);
-          if (s < ntl) sparse_tile(p0, cnt, g, t, lrec[64 * s + lane], true);
-        }
-      } else {
-        // prefetched tiles of 1..64 records: all slots at once (empty ones skipped)
-        uint32_t used = 0;  // wave-uniform slot mask
-#pragma unroll
-        for (int s = 0; s < MAXT; ++s) {
-          int g, t;
-          (void)tile_of(s, g, t);
-          uint32_t p0, cnt;
-          slot_ptr(s, p0, cnt);
-          if (s < ntl && cnt - 1u < 64u) {
-            run_sums(lrec[64 * s + lane], (uint32_t)lane < cnt, g, s);
-            used |= 1u << s;
-          }
-        }
-        if (used) {
-          wave_fence();
-#pragma unroll
-          for (int s = 0; s < MAXT; ++s) {
-            int g, t;
-            (void)tile_of(s, g, t);
-            if (used & (1u << s)) add_sums(s, t);
-          }
-          wave_fence();
-        }
-#pragma unroll
-        for (int s = 0; s < MAXT; ++s) {
-          int g, t;
-          (void)tile_of(s, g, t);
-          uint32_t p0, cnt;
-          slot_ptr(s, p0, cnt);
-          if (s < ntl && cnt > 64u) sparse_slow(p0, cnt, g, t);
-        }
+      for (int s = 0; s < MAXT; ++s) {
+        int g, t;
+        (void)tile_of(s, g, t);
+        uint32_t p0, cnt;
+        slot_ptr(s, p0, cnt);
+        if (s < ntl) sparse_tile(p0, cnt, g, t, lrec[64 * s + lane], true);
       }
       for (int s = MAXT; s < ntl; ++s) {  // tiles past the prefetched ones
         int g, t;
@@ -674,8 +676,7 @@ gemv_tiles_kernel(UniformArgs a) {
         if (!slot_ok(g, t)) continue;
         const uint32_t p0 = __builtin_amdgcn_readfirstlane(bload4(rtp, 4u * T));
         const uint32_t p1 = __builtin_amdgcn_readfirstlane(bload4(rtp, 4u * T + 4u));
-        if constexpr (MFMA) sparse_tile(p0, min(p1 - p0, 2048u), g, t, 0u, false);
-        else sparse_slow(p0, min(p1 - p0, 2048u), g, t);
+        sparse_tile(p0, min(p1 - p0, 2048u), g, t, 0u, false);
       }
     }
   };
@@ -782,10 +783,14 @@ size_t tiles_lds_bytes(bool mfma, int mt, int tpw, int wk) {
 constexpr size_t XLDS_MAX = 64 * 1024 + 128;
 size_t xlds_bytes(bool mfma, int mt, int M, int K) { return (size_t)(mfma ? (M < 16 ? M : 16) : mt) * (K + 32) * 2; }
 
-// LDS of the outlier variant beyond the dense kernel's, per wave: MFMA, a
-// 16 x 128 fp16 scratch tile; VALU, 8 slots of run sums for MT x 64 lanes;
-// then 8 x 64 prefetched records
-size_t sparse_lds_bytes(bool mfma, int mt, int wk) { return (size_t)wk * ((mfma ? 4096 : 8 * mt * 256) + 8 * 256); }
+// LDS of the outlier variant beyond the dense kernel's: MFMA, per wave a
+// 16 x 128 fp16 scratch tile and 8 x 64 prefetched records; VALU, per wave
+// four 64-record batches, a batch's row keys and MT x 64 products, then the
+// workgroup's tpw G + 1 tile pointers
+size_t sparse_lds_bytes(bool mfma, int mt, int wk, int tpw, int K) {
+  if (mfma) return (size_t)wk * (4096 + 8 * 256);
+  return (size_t)wk * (256 * 4 + 256 + 256 * mt) + ((size_t)tpw * (K / 128) + 1) * 4;
+}
 
 constexpr size_t LDS_ALL = 160 * 1024;  // gfx950 LDS per workgroup
 
@@ -848,7 +853,7 @@ hipError_t launch_t(const UniformArgs& a, const TileCfg& c, hipStream_t s) {
                       reinterpret_cast<uintptr_t>(a.zeros) % 16 == 0 && (size_t)a.N * G * 2 % 16 == 0 &&
                       zbytes % 16 == 0;
     const size_t lds = (xlds ? xl : 0) + (plds ? params_lds_bytes(BITS, a.K) : 0) + red +
-                       (SP ? sparse_lds_bytes(MFMA, MT, c.wk) : 0);
+                       (SP ? sparse_lds_bytes(MFMA, MT, c.wk, TPW, a.K) : 0);
     if (lds > LDS_ALL) return hipErrorInvalidValue;
     // chunk scales in one load: whole chunks and a 2*NG-byte aligned base
     const bool sal = (a.K / 128) % NG == 0 && reinterpret_cast<uintptr_t>(a.scales) % (2 * NG) == 0;
@@ -963,13 +968,32 @@ TileCfg pick_tiles(int bits, int M, int N, int K, bool mfma) {
   return c;
 }
 
-// Outlier variant: the uniform W4 dense shapes, restricted to the one-tile-row
-// forms (2- and 4-deep rings, the latter VALU only) and two tile-rows with
+// Outlier variant.  VALU (sweeps of the 8B and 70B layers at M = 1): one
+// tile-row of one-group chunks -- 16 waves for long K, 4 on wide layers,
+// else 8, with the 4-deep ring on layers of at most 256 tile-rows and the
+// 2-deep one elsewhere -- except from 2048 tile-rows on, where two tile-rows
+// with four-group chunks and 4 waves win.  MFMA: the uniform W4 shapes,
+// restricted to one tile-row with the 2-deep ring and two tile-rows with
 // four-group chunks.
 TileCfg pick_outlier(int M, int N, int K, bool mfma) {
   TileCfg c = pick_tiles(4, M, N, K, mfma);
-  if (c.tpw == 1) {
-    if (mfma || c.v != 4) c.v = 3;
+  if (!mfma) {
+    const long nt = (N + 15) / 16;
+    const int G = K / 128;
+    if (nt >= 2048) {
+      c.tpw = 2;
+      c.v = 0;
+      c.wk = 4;
+      const int nc = (G + chunk_groups(4, false, c.mt, 0) - 1) / chunk_groups(4, false, c.mt, 0);
+      if (c.wk > nc) c.wk = nc;
+    } else {
+      c.tpw = 1;
+      c.wk = G >= 96 ? 16 : (nt >= 1024 ? 4 : 8);
+      c.v = nt <= 256 && c.wk <= 8 ? 4 : 3;
+      if (c.wk > G) c.wk = G;
+    }
+  } else if (c.tpw == 1) {
+    c.v = 3;
   } else {
     c.tpw = 2;
     c.v = 0;

@@ -268,7 +268,8 @@ __global__ void __launch_bounds__(64 * SP_WAVES) spmv_tilecoo_kernel(SpmvArgs a)
   const rsrc_t ry = make_rsrc(a.y, (uint32_t)M * a.N * 2u);
   const uint16_t yprior = bload2(ry, eo ? ((uint32_t)em * a.N + en) * 2u : OOB);
   __syncthreads();
-  const uint32_t beg = ptr[0], end = ptr[G];
+  const uint32_t beg = ptr[0];
+  const uint32_t end = min(ptr[G], beg + 2048u * (uint32_t)G);  // (a tile holds at most 2048 records)
   if (beg >= end) return;  // no outliers in this tile-row: y untouched
   const rsrc_t rr = make_rsrc(a.tile_rec, (uint32_t)a.nnz * 4u);
   const rsrc_t rx = make_rsrc(a.x, (uint32_t)M * a.K * 2u);
