@@ -196,24 +196,21 @@ gemv_tiles_kernel(UniformArgs a) {
   const u4* xs = reinterpret_cast<const u4*>(smem);
 
   // outlier variant (SP): LDS after the partials (see sparse_lds_bytes), per
-  // wave: MFMA, a 16 x 128 fp16 scratch tile, lane-major (lane l's 32 k of
-  // its row at halves 32 l .. 32 l + 31), then the first 64 records of MAXT
-  // tiles, loaded straight into LDS; VALU, VPB 64-record batches loaded
-  // straight into LDS, a batch's rows [64] and products [MT][64]; after the
-  // waves' slots (VALU) the workgroup's tile pointers [TPW G + 1]
-  constexpr int MAXT = 8;
+  // wave: VPB 64-record batches loaded straight into LDS, a batch's row keys
+  // [64] and its products [PR][64] (VALU: the MT batch rows; MFMA: the M
+  // batch rows rounded up to 4, at most PM = 16); after the waves' slots, the
+  // workgroup's tile pointers [TPW G + 1]
   constexpr int VPB = 4;
-  constexpr int SPW0 = MFMA ? 4096 : 256 * VPB + 256;
-  constexpr int SPW = MFMA ? SPW0 + MAXT * 256 : SPW0 + MT * 256;  // bytes per wave
-  _Float16* sscr = nullptr;
-  uint32_t* vrec = nullptr;  // VALU: [VPB][64] prefetched records
-  uint32_t* vrow = nullptr;  // VALU: [64] row keys of a batch
-  float* vprod = nullptr;    // VALU: [MT][64] products of a batch
-  uint32_t* vptr = nullptr;  // VALU: the workgroup's tile pointers
+  constexpr int PM = MFMA ? 16 : MT;
+  const int PR = MFMA ? min((M + 3) & ~3, 16) : MT;
+  const int SPW = 256 * VPB + 256 + PR * 256;  // bytes per wave
+  uint32_t* vrec = nullptr;  // [VPB][64] prefetched records
+  uint32_t* vrow = nullptr;  // [64] row keys of a batch
+  float* vprod = nullptr;    // [PM][64] products of a batch
+  uint32_t* vptr = nullptr;  // the workgroup's tile pointers
   if constexpr (SP) {
     const size_t redb = MFMA ? (size_t)WK * TPW * 64 * 16 : (size_t)WK * TPW * MT * 16 * 4;
     char* b = reinterpret_cast<char*>(red) + redb + (size_t)wave * SPW;
-    sscr = reinterpret_cast<_Float16*>(b);
     vrec = reinterpret_cast<uint32_t*>(b);
     vrow = reinterpret_cast<uint32_t*>(b + 256 * VPB);
     vprod = reinterpret_cast<float*>(b + 256 * VPB + 256);
@@ -405,34 +402,17 @@ gemv_tiles_kernel(UniformArgs a) {
                             : bload16(rz, i < np16 ? (uint32_t)rt0 * 16u * zrow + 16u * (i - sv) : OOB);
   };
   u4 pfirst;
-  // Outlier variant: slot s of a wave's tiles, in order: chunk s / (TPW NG),
-  // tile-row, group; its global Tile-COO tile index (tiles past the last
-  // group or tile-row hold nothing)
+  // Outlier variant: the tile pointers of the workgroup's tile-rows (nvt
+  // tiles, nvt + 1 entries), thread i loading entries i, i + blockDim, ...
+  // (at most SPP per thread here; more in stage_x)
   const rsrc_t rtp = make_rsrc(a.tile_ptr, ((uint32_t)NT * G + 1u) * 4u);
-  auto tile_of = [&](int s, int& g, int& t) -> uint32_t {
-    constexpr int per = TPW * NG;
-    t = (s % per) / NG;
-    g = (wave + WK * (s / per)) * NG + s % NG;
-    return (uint32_t)(rt0 + t) * G + min(g, G - 1);
-  };
-  // lane 2 s (2 s + 1) loads the start (end) pointer of slot s, s < MAXT: one
-  // load, issued with the activations
-  uint32_t pfetch = 0;
-  // VALU: the tile pointers of the workgroup's tile-rows (nvt tiles, nvt + 1
-  // entries), thread i loading entries i, i + blockDim, ... (at most SPP per
-  // thread here; more in stage_x)
   constexpr int SPP = 2;
   const int nvt = (min(TPW, NT - rt0)) * G;
   uint32_t pv[SPP];
   auto stage_x_issue = [&]() {
     if constexpr (XLDS) x_pass(threadIdx.x, xfirst);
     if constexpr (PLDS) pfirst = p_pass(threadIdx.x);
-    if constexpr (SP && MFMA) {
-      int g, t;
-      const uint32_t T = tile_of(lane >> 1, g, t) + (lane & 1);
-      pfetch = bload4(rtp, lane < 2 * MAXT ? 4u * T : OOB);
-    }
-    if constexpr (SP && !MFMA) {
+    if constexpr (SP) {
 #pragma unroll
       for (int u = 0; u < SPP; ++u) {
         const int i = threadIdx.x + u * blockDim.x;
@@ -459,12 +439,7 @@ gemv_tiles_kernel(UniformArgs a) {
       if ((int)threadIdx.x < np16) pw[threadIdx.x] = pfirst;
       for (int i = threadIdx.x + blockDim.x; i < np16; i += blockDim.x) pw[i] = p_pass(i);
     }
-    if constexpr (SP && MFMA) {
-      u4* z = reinterpret_cast<u4*>(sscr);
-#pragma unroll
-      for (int u = 0; u < SPW / 1024; ++u) z[lane + 64 * u] = u4{0u, 0u, 0u, 0u};
-    }
-    if constexpr (SP && !MFMA) {
+    if constexpr (SP) {
 #pragma unroll
       for (int u = 0; u < SPP; ++u) {
         const int i = threadIdx.x + u * blockDim.x;
@@ -498,39 +473,22 @@ gemv_tiles_kernel(UniformArgs a) {
   };
   // Outliers (FlashQuant abstract: an fp16 sparse path fused with the
   // low-bit dense one, sharing activations and outputs; Tile-COO records).
-  // A Tile-COO tile is the 16 x 128 tile of the dense layout.
-  //  * VALU engine: the workgroup's records are one contiguous range (its
-  //    tile-rows' tiles are consecutive).  The tile pointers are staged with
-  //    the activations; right after the staging barrier each wave's first two
-  //    64-record batches go straight into LDS (they arrive during the dense
-  //    loop).  After the loop the waves walk their batches (sparse_batch) and
-  //    add the sums of their rows' records into their dense partials, which
-  //    the fixed-order reduction then adds like any other partial.
-  //  * MFMA engine: a wave's outliers are those of the tiles of its own
-  //    chunks; the first 64 records of its first MAXT tiles are prefetched to
-  //    LDS, then scattered into the wave's zeroed 16 x 128 fp16 scratch in the
-  //    lane layout of the dense tile and multiplied like dequantized weights
-  //    but unscaled (4 more matrix-core steps per tile), then cleared.
-  // Every product is exact and the order of the sums is fixed, so the result
-  // is deterministic.  Record fields are masked into the tile, so malformed
-  // records stay in bounds.
-  uint32_t* lrec = reinterpret_cast<uint32_t*>(reinterpret_cast<char*>(sscr) + SPW0);  // (MFMA)
-  auto slot_ok = [&](int g, int t) { return g < G && rt0 + t < NT; };
-  // start and count of slot s, from the pointers lanes 2 s and 2 s + 1 loaded
-  auto slot_ptr = [&](int s, uint32_t& p0, uint32_t& cnt) {
-    int g, t;
-    (void)tile_of(s, g, t);
-    p0 = __builtin_amdgcn_readlane(pfetch, 2 * s);
-    const uint32_t p1 = __builtin_amdgcn_readlane(pfetch, 2 * s + 1);
-    cnt = slot_ok(g, t) ? min(p1 - p0, 2048u) : 0u;  // (a tile holds at most 2048)
-  };
+  // A Tile-COO tile is the 16 x 128 tile of the dense layout, so the records
+  // of a workgroup's tile-rows are one contiguous range [vbeg, vend).  The
+  // tile pointers are staged with the activations; right after the staging
+  // barrier each wave's first VPB 64-record batches (batches w, w + WK, ...)
+  // go straight into LDS, issued behind the first weight stages, and arrive
+  // during the dense loop.  After the loop each wave walks its batches
+  // (sparse_batch) and adds the sums of its lanes' records into its dense
+  // partials, which the fixed-order reduction then adds like any other
+  // partial.  Every product is exact and the order of the sums is fixed, so
+  // the result is deterministic.  Record fields are masked into the
+  // tile-row and a tile's count is bounded, so malformed records stay in
+  // bounds.
   const rsrc_t rrec = make_rsrc(a.tile_rec, (uint32_t)a.nnz * 4u);
-  // VALU: the workgroup's records [vbeg, vend), one contiguous range; wave w
-  // takes the 64-record batches w, w + WK, ...; its first VPB go straight to
-  // LDS here, issued behind the first weight stages
   uint32_t vbeg = 0, vend = 0;
   auto sparse_issue = [&]() {
-    if constexpr (SP && !MFMA) {
+    if constexpr (SP) {
       vbeg = __builtin_amdgcn_readfirstlane(vptr[0]);
       vend = __builtin_amdgcn_readfirstlane(vptr[nvt]);
       // (a tile holds at most 2048 records: malformed pointers stay bounded)
@@ -541,65 +499,23 @@ gemv_tiles_kernel(UniformArgs a) {
         __builtin_amdgcn_raw_ptr_buffer_load_lds(rrec, vrec + 64 * i, 4, r < vend ? r * 4u : OOB, 0, 0, 0);
       }
     }
-    if constexpr (SP && MFMA) {
-#pragma unroll
-      for (int s = 0; s < MAXT; ++s) {
-        uint32_t p0, cnt;
-        slot_ptr(s, p0, cnt);
-        // (direct to LDS: no registers held across the dense loop)
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(rrec, lrec + 64 * s, 4, (uint32_t)lane < cnt ? (p0 + lane) * 4u : OOB,
-                                                 0, 0, 0);
-      }
-    }
   };
-  // Lanes of a wave exchange data through its LDS scratch; LDS operations of
+  // Lanes of a wave exchange data through its LDS slot; LDS operations of
   // one wave complete in order, but without a fence the compiler may assume no
   // other lane wrote what this lane reads (and forward its own earlier store).
   auto wave_fence = [] { __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront"); };
-  auto sparse_tile = [&](uint32_t p0, uint32_t cnt, int g, int t, uint32_t rec0, bool have0) {
-    if (cnt == 0) return;
-    auto place = [&](uint32_t rec) { return ((((rec >> 8) & 15u) + 16u * ((rec >> 5) & 3u)) << 5) | (rec & 31u); };
-    for (uint32_t b = 0; b < cnt; b += 64) {  // scatter
-      const uint32_t rec = b == 0 && have0 ? rec0 : bload4(rrec, b + lane < cnt ? (p0 + b + lane) * 4u : OOB);
-      if (b + lane < cnt) sscr[place(rec)] = __builtin_bit_cast(_Float16, (uint16_t)(rec >> 16));
-    }
-    wave_fence();  // (the records were scattered by other lanes)
-    const u4* sl = reinterpret_cast<const u4*>(sscr) + 4 * lane;
-    u4 sv[4];
-#pragma unroll
-    for (int v = 0; v < 4; ++v) sv[v] = sl[v];
-    {
-      f4 dd = f4{0.f, 0.f, 0.f, 0.f};
-      const int xa = (min(n, XM - 1) * XK + 128 * g + 32 * kq) / 8;
-#pragma unroll
-      for (int v = 0; v < 4; ++v) {
-        const u4 xv = XLDS ? xs[xa + v] : bload16(rx, xoff[0] == OOB ? OOB : xoff[0] + 256u * g + 16u * v);
-        dd = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(h8, xv), __builtin_bit_cast(h8, sv[v]), dd, 0, 0,
-                                                     0);
-      }
-#pragma unroll
-      for (int tt = 0; tt < TPW; ++tt)
-        if (tt == t)
-#pragma unroll
-          for (int i = 0; i < 4; ++i) accm[tt][i] += dd[i];
-    }
-    for (uint32_t b = 0; b < cnt; b += 64) {  // clear what was written
-      const uint32_t rec = b == 0 && have0 ? rec0 : bload4(rrec, b + lane < cnt ? (p0 + b + lane) * 4u : OOB);
-      if (b + lane < cnt) sscr[place(rec)] = (_Float16)0.0f;
-    }
-    wave_fence();
-  };
-  // VALU engine: a batch of 64 records.  Lane i takes record i: its tile is
-  // the last one whose range starts at or before it (binary search over the
-  // staged pointers), its product v x[m][k] is exact, and its row key
-  // (tile-row t, row r) = 16 t + r goes to the wave's slot with the products.
-  // Lane (r, quarter p) then adds, in record order, the products of the
-  // batch's quarter p whose row is r: so the records of a row reach the lanes
-  // of that row, whose partials the reduction below adds across quarters and
-  // waves in a fixed order.  Deterministic; record fields are masked into the
-  // tile-row, so malformed records stay in bounds.
+  // A batch of 64 records.  Lane i takes record i: its tile is the last one
+  // whose range starts at or before it (binary search over the staged
+  // pointers); its products v x[m][k] (exact) for the batch rows and its row
+  // key (tile-row t, row r) = 16 t + r go to the wave's slot.  Lane (r,
+  // quarter p) then adds, in record order, the products of the batch's
+  // quarter p whose row is r, for every batch row (VALU: its MT rows; MFMA:
+  // the rows m < M, four at a time).  The quarters are added in a fixed order
+  // at the end (VALU: by the reduction; MFMA: one quarter sum per row, added
+  // by the lanes that hold that row of the matrix-core result).
   const _Float16* xh = reinterpret_cast<const _Float16*>(smem);
-  float sacc[TPW][MT];
+  constexpr int SR = MFMA ? 16 : MT;  // batch rows a lane sums
+  float sacc[TPW][SR];
   auto sparse_batch = [&](uint32_t rec, uint32_t idx) {
     const bool ok = idx < vend;
     int j = 0;
@@ -609,43 +525,56 @@ gemv_tiles_kernel(UniformArgs a) {
     const uint32_t col = 128u * (uint32_t)(j - t * G) + (rec & 127u);
     const float v = h2f((uint16_t)(rec >> 16));
 #pragma unroll
-    for (int m = 0; m < MT; ++m) {
-      float xv;
-      if constexpr (XLDS) xv = (float)xh[m * XK + col];
-      else xv = h2f(bload2(rx, ok && m0 + m < M ? ((uint32_t)(m0 + m) * K + col) * 2u : OOB));
-      vprod[m * 64 + lane] = ok ? v * xv : 0.f;
+    for (int m = 0; m < PM; ++m) {
+      if (m < PR) {  // (wave-uniform: the rows of the slot)
+        const int xm = MFMA ? m : m0 + m;  // batch row (rows past M add nothing)
+        float xv = 0.f;
+        if (xm < M) {
+          if constexpr (XLDS) xv = (float)xh[m * XK + col];  // (staged rows: the batch rows from m0)
+          else xv = h2f(bload2(rx, ok ? ((uint32_t)xm * K + col) * 2u : OOB));
+        }
+        vprod[m * 64 + lane] = ok ? v * xv : 0.f;
+      }
     }
     vrow[lane] = ok ? ((rec >> 8) & 15u) + 16u * t : 0xFFFFu;
     wave_fence();  // (other lanes read these)
-    // the quarter's 16 keys and products, read together (16-byte reads that
-    // every lane of the quarter shares), then added where the row matches
+    // the quarter's 16 keys, and its products four rows at a time, read with
+    // 16-byte reads that every lane of the quarter shares, then added
+    // branch-free where the row matches
     u4 kv[4];
-    u4 pv4[MT][4];
 #pragma unroll
-    for (int v = 0; v < 4; ++v) {
-      kv[v] = reinterpret_cast<const u4*>(vrow)[4 * kq + v];
+    for (int v4 = 0; v4 < 4; ++v4) kv[v4] = reinterpret_cast<const u4*>(vrow)[4 * kq + v4];
 #pragma unroll
-      for (int m = 0; m < MT; ++m) pv4[m][v] = reinterpret_cast<const u4*>(vprod + m * 64)[4 * kq + v];
-    }
+    for (int g4 = 0; g4 < SR; g4 += 4) {
+      constexpr int RG = SR < 4 ? SR : 4;
+      if (g4 < PR) {  // (wave-uniform)
 #pragma unroll
-    for (int e0 = 0; e0 < 16; ++e0) {
-      const uint32_t key = kv[e0 >> 2][e0 & 3];
+        for (int v4 = 0; v4 < 4; ++v4) {  // four records at a time
+          u4 pv[RG];
 #pragma unroll
-      for (int tt = 0; tt < TPW; ++tt) {
-        const bool hit = key == (uint32_t)(n + 16 * tt);
+          for (int i = 0; i < RG; ++i) pv[i] = reinterpret_cast<const u4*>(vprod + (g4 + i) * 64)[4 * kq + v4];
 #pragma unroll
-        for (int m = 0; m < MT; ++m) sacc[tt][m] += hit ? __uint_as_float(pv4[m][e0 >> 2][e0 & 3]) : 0.f;
+          for (int e = 0; e < 4; ++e) {
+            const uint32_t key = kv[v4][e];
+#pragma unroll
+            for (int tt = 0; tt < TPW; ++tt) {
+              const bool hit = key == (uint32_t)(n + 16 * tt);
+#pragma unroll
+              for (int i = 0; i < RG; ++i) sacc[tt][g4 + i] += hit ? __uint_as_float(pv[i][e]) : 0.f;
+            }
+          }
+        }
       }
     }
     wave_fence();  // (the slot is rewritten by the next batch)
   };
   auto sparse_compute = [&]() {
-    if constexpr (SP && !MFMA) {
+    if constexpr (SP) {
       __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): the batches are in LDS (issued long before)
 #pragma unroll
       for (int t = 0; t < TPW; ++t)
 #pragma unroll
-        for (int m = 0; m < MT; ++m) sacc[t][m] = 0.f;
+        for (int i = 0; i < SR; ++i) sacc[t][i] = 0.f;
       for (int i = 0;; ++i) {  // wave-uniform
         const uint32_t b0 = vbeg + 64u * (wave + WK * i);
         if (b0 >= vend) break;
@@ -656,28 +585,17 @@ gemv_tiles_kernel(UniformArgs a) {
 #pragma unroll
       for (int t = 0; t < TPW; ++t)
 #pragma unroll
-        for (int m = 0; m < MT; ++m) accv[t][m] += sacc[t][m];
-    }
-    if constexpr (SP && MFMA) {
-      __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): the records are in LDS (issued long before)
-      const int nci = NC > wave ? (NC - wave + WK - 1) / WK : 0;  // this wave's chunks
-      const int ntl = nci * TPW * NG;
-#pragma unroll
-      for (int s = 0; s < MAXT; ++s) {
-        int g, t;
-        (void)tile_of(s, g, t);
-        uint32_t p0, cnt;
-        slot_ptr(s, p0, cnt);
-        if (s < ntl) sparse_tile(p0, cnt, g, t, lrec[64 * s + lane], true);
-      }
-      for (int s = MAXT; s < ntl; ++s) {  // tiles past the prefetched ones
-        int g, t;
-        const uint32_t T = tile_of(s, g, t);
-        if (!slot_ok(g, t)) continue;
-        const uint32_t p0 = __builtin_amdgcn_readfirstlane(bload4(rtp, 4u * T));
-        const uint32_t p1 = __builtin_amdgcn_readfirstlane(bload4(rtp, 4u * T + 4u));
-        sparse_tile(p0, min(p1 - p0, 2048u), g, t, 0u, false);
-      }
+        for (int i = 0; i < SR; ++i) {
+          if constexpr (MFMA) {
+            // lane (r, p) holds result rows 4 p .. 4 p + 3 of weight row r
+            if (i < M) {  // (wave-uniform)
+              const float sm = quarter_sum(sacc[t][i]);
+              accm[t][i & 3] += kq == (i >> 2) ? sm : 0.f;
+            }
+          } else {
+            accv[t][i] += sacc[t][i];
+          }
+        }
     }
   };
 
@@ -783,13 +701,13 @@ size_t tiles_lds_bytes(bool mfma, int mt, int tpw, int wk) {
 constexpr size_t XLDS_MAX = 64 * 1024 + 128;
 size_t xlds_bytes(bool mfma, int mt, int M, int K) { return (size_t)(mfma ? (M < 16 ? M : 16) : mt) * (K + 32) * 2; }
 
-// LDS of the outlier variant beyond the dense kernel's: MFMA, per wave a
-// 16 x 128 fp16 scratch tile and 8 x 64 prefetched records; VALU, per wave
-// four 64-record batches, a batch's row keys and MT x 64 products, then the
-// workgroup's tpw G + 1 tile pointers
-size_t sparse_lds_bytes(bool mfma, int mt, int wk, int tpw, int K) {
-  if (mfma) return (size_t)wk * (4096 + 8 * 256);
-  return (size_t)wk * (256 * 4 + 256 + 256 * mt) + ((size_t)tpw * (K / 128) + 1) * 4;
+// LDS of the outlier variant beyond the dense kernel's: per wave four
+// 64-record batches, a batch's row keys and its products (MT batch rows, or
+// on the MFMA engine the M rows rounded up to 4), then the workgroup's
+// tpw G + 1 tile pointers
+size_t sparse_lds_bytes(bool mfma, int mt, int wk, int tpw, int K, int M) {
+  const int pr = mfma ? (((M + 3) & ~3) < 16 ? ((M + 3) & ~3) : 16) : mt;
+  return (size_t)wk * (256 * 4 + 256 + 256 * pr) + ((size_t)tpw * (K / 128) + 1) * 4;
 }
 
 constexpr size_t LDS_ALL = 160 * 1024;  // gfx950 LDS per workgroup
@@ -853,7 +771,7 @@ hipError_t launch_t(const UniformArgs& a, const TileCfg& c, hipStream_t s) {
                       reinterpret_cast<uintptr_t>(a.zeros) % 16 == 0 && (size_t)a.N * G * 2 % 16 == 0 &&
                       zbytes % 16 == 0;
     const size_t lds = (xlds ? xl : 0) + (plds ? params_lds_bytes(BITS, a.K) : 0) + red +
-                       (SP ? sparse_lds_bytes(MFMA, MT, c.wk, TPW, a.K) : 0);
+                       (SP ? sparse_lds_bytes(MFMA, MT, c.wk, TPW, a.K, a.M) : 0);
     if (lds > LDS_ALL) return hipErrorInvalidValue;
     // chunk scales in one load: whole chunks and a 2*NG-byte aligned base
     const bool sal = (a.K / 128) % NG == 0 && reinterpret_cast<uintptr_t>(a.scales) % (2 * NG) == 0;
@@ -1000,6 +918,16 @@ TileCfg pick_outlier(int M, int N, int K, bool mfma) {
     const int nc = (K / 128 + chunk_groups(4, mfma, c.mt, 0) - 1) / chunk_groups(4, mfma, c.mt, 0);
     if (c.wk > nc) c.wk = nc;
   }
+  // halve the waves until the launch's LDS fits (staged activations and
+  // quant params, partials, the sparse phase's slots): long K with batch
+  // rows staged leaves less room for per-wave scratch
+  const size_t G = K / 128;
+  size_t xl = xlds_bytes(mfma, c.mt, M, K) + (!mfma ? (size_t)c.mt * (G + 1) * 32 : 0);
+  if (xl > XLDS_MAX) xl = 0;
+  const size_t fixed = xl + params_lds_bytes(4, K);
+  while (c.wk > 1 && fixed + tiles_lds_bytes(mfma, c.mt, c.tpw, c.wk) +
+                             sparse_lds_bytes(mfma, c.mt, c.wk, c.tpw, K, M) > LDS_ALL)
+    c.wk = (c.wk + 1) / 2;
   return c;
 }
 

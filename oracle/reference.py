@@ -158,13 +158,12 @@ def add_sparse(y_prior, x, o_rows, o_cols, o_vals):
 def gemv_outlier(x, codes, scales, zeros, o_rows, o_cols, o_vals, g=128, rows=None):
     """Dense codes are used as given (codes at outlier positions are not altered);
     the fp16 outliers are added on top."""
-    yd, Ad = gemv_uniform(x, codes, scales, zeros, g)
+    yd, Ad = gemv_uniform(x, codes, scales, zeros, g, rows=rows)
     ys, As = sparse_part(x, codes.shape[0], o_rows, o_cols, o_vals)
-    y, A = yd + ys, Ad + As
     if rows is not None:
         rows = np.asarray(rows, dtype=np.int64)
-        return y[:, rows], A[:, rows]
-    return y, A
+        ys, As = ys[:, rows], As[:, rows]
+    return yd + ys, Ad + As
 
 
 # ----------------------------------------------------------------------------

@@ -147,3 +147,18 @@ def test_outlier_every_launch_shape(monkeypatch, path, M, N, K):
                 assert_within(y, y_ref, A, f"outlier M={M} N={N} K={K} path={path} cfg={cfg}")
                 ran.append(cfg)
     assert len(ran) >= 8, ran
+
+
+# -- the decoder-layer shapes at every batch size (sampled rows): long K with
+# staged batch rows must still fit the launch's LDS
+@pytest.mark.parametrize("N,K,M", [(4096, 14336, 2), (4096, 14336, 4), (4096, 14336, 16), (6144, 4096, 2),
+                                   (28672, 4096, 4), (8192, 28672, 2)])
+def test_outlier_layer_shapes_batched(N, K, M):
+    say("outlier layer", N, K, M)
+    c = synth.outlier_case(61 + M, M, N, K)
+    wq, s, zq, tp, tr = _upload(c, N, K)
+    y = host(q.outlier(dev(c["x"]), wq, s, zq, tp, tr))
+    rows = sample_rows(N)
+    y_ref, A = ref.gemv_outlier(c["x"], c["codes"], c["scales"], c["zeros"], c["o_rows"], c["o_cols"], c["o_vals"],
+                                rows=rows)
+    assert_within(y[:, rows], y_ref, A, f"outlier M={M} N={N} K={K}")
