@@ -53,6 +53,23 @@ def gemv_codebook_exact(x, codes, codebook, scales, g=128):
     return out
 
 
+def gemv_codebook_additive_exact(x, codes, codebooks, scales, g):
+    M, K = x.shape
+    m, N, _ = codes.shape
+    v = codebooks.shape[2]
+    out = []
+    for mm in range(M):
+        row = []
+        for n in range(N):
+            acc = Fraction(0)
+            for k in range(K):
+                c = sum((_fr(codebooks[i, int(codes[i, n, k // v]), k % v]) for i in range(m)), Fraction(0))
+                acc += _fr(x[mm, k]) * _fr(scales[n, k // g]) * c
+            row.append(acc)
+        out.append(row)
+    return out
+
+
 def sparse_exact(x, N, rows, cols, vals):
     M = x.shape[0]
     y = [[Fraction(0)] * N for _ in range(M)]

@@ -189,6 +189,32 @@ def gemv_codebook(x, codes, codebook, scales, g=128, rows=None):
     return _gemv_rows(x64, wfun, codes.shape[0], rows)
 
 
+def dequant_codebook_additive(codes, codebooks, scales, g):
+    """m additive codebooks (CodeGEMM notes, "Key design 3": one kernel for any
+    number of codebooks m, vector length v, code bits b and group g; the
+    codebooks of a segment add up, as in the AQLM-style multi-codebook
+    configurations the notes compare against):
+    w[n, v*j + t] = s[n, (v*j + t) // g] * sum_i C_i[code_i[n, j], t]."""
+    Cs = _f64(codebooks)                                   # [m, 256, v]
+    codes = np.asarray(codes, dtype=np.int64)              # [m, N, KC]
+    m, N, KC = codes.shape
+    v = Cs.shape[2]
+    cents = np.zeros((N, KC, v))
+    for i in range(m):
+        cents += Cs[i][codes[i]]
+    return cents.reshape(N, KC * v) * np.repeat(_f64(scales), g, axis=1)
+
+
+def gemv_codebook_additive(x, codes, codebooks, scales, g, rows=None):
+    x64 = _f64(x)
+    codes = np.asarray(codes)
+
+    def wfun(r):
+        return dequant_codebook_additive(codes[:, r], codebooks, scales[r], g)
+
+    return _gemv_rows(x64, wfun, codes.shape[1], rows)
+
+
 def psumbook(x, codebook):
     """P[m, j, c] = sum_t C[c, t] * x[m, v*j + t]  (one table per v-wide segment j)."""
     x64 = _f64(x)

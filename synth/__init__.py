@@ -193,3 +193,15 @@ LLAMA_70B_LAYERS = {
     "gate_up": (57344, 8192),
     "down": (8192, 28672),
 }
+
+
+def codebook_additive_case(seed, M, N, K, ncb, v, g, c_std=0.02, s_lo=0.5, s_hi=2.0):
+    """ncb additive codebooks of 256 centroids of v dims: codes [ncb, N, K/v]
+    uniform 8-bit, centroids [ncb, 256, v] ~ N(0, c_std), per-g scales."""
+    assert K % g == 0 and g % v == 0
+    return dict(
+        x=activations(seed, M, K),
+        codes=codes(seed, S_CODES, ncb * N * (K // v), 8).reshape(ncb, N, K // v),
+        codebooks=f16(normal(seed, S_CB, ncb * 256 * v, c_std)).reshape(ncb, 256, v),
+        scales=f16(uniform(seed, S_SCALES, N * (K // g), s_lo, s_hi)).reshape(N, K // g),
+    )

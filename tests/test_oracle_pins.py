@@ -376,3 +376,59 @@ def test_planted_dense_mistakes_are_caught(monkeypatch, mutant):
         except AssertionError:
             failures += 1
     assert failures >= 1
+
+
+# ----------------------------------------------------------------------------
+# additive codebooks (m codebooks, vector length v, group g)
+# ----------------------------------------------------------------------------
+@pytest.mark.parametrize("m,v,g", [(1, 4, 32), (2, 8, 64), (3, 16, 32)])
+def test_codebook_additive_matches_exact(m, v, g):
+    c = synth.codebook_additive_case(25 + m, 2, 3, 128, m, v, g)
+    y, A = ref.gemv_codebook_additive(c["x"], c["codes"], c["codebooks"], c["scales"], g)
+    ye = exact.to_f64(exact.gemv_codebook_additive_exact(c["x"], c["codes"], c["codebooks"], c["scales"], g))
+    assert np.allclose(y, ye, rtol=0, atol=1e-12 * A.max())
+
+
+def test_codebook_additive_reduces_to_single_codebook():
+    """m = 1 is the single-codebook format (pinned above), and a codebook of
+    zeros adds nothing."""
+    c = synth.codebook_additive_case(26, 2, 20, 512, 1, 4, 128)
+    y1, A1 = ref.gemv_codebook_additive(c["x"], c["codes"], c["codebooks"], c["scales"], 128)
+    ys, As = ref.gemv_codebook(c["x"], c["codes"][0], c["codebooks"][0], c["scales"], 128)
+    assert np.array_equal(y1, ys) and np.array_equal(A1, As)
+    c2 = synth.codebook_additive_case(27, 1, 20, 512, 2, 8, 64)
+    cbs = c2["codebooks"].copy()
+    cbs[1] = 0
+    y2, _ = ref.gemv_codebook_additive(c2["x"], c2["codes"], cbs, c2["scales"], 64)
+    ys2, _ = ref.gemv_codebook(c2["x"], c2["codes"][0], c2["codebooks"][0], c2["scales"], 64)
+    assert np.allclose(y2, ys2, rtol=0, atol=1e-13)
+
+
+def test_codebook_additive_one_hot_worked_example():
+    """One-hot x at k = 37 (segment 2, dim 5 for v = 16; group 1 for g = 32):
+    y[n] = s[n, 1] * (C_0[code_0[n, 2], 5] + C_1[code_1[n, 2], 5] + C_2[code_2[n, 2], 5])."""
+    c = synth.codebook_additive_case(28, 1, 5, 128, 3, 16, 32)
+    x = np.zeros((1, 128), np.float16)
+    x[0, 37] = 1.0
+    y, _ = ref.gemv_codebook_additive(x, c["codes"], c["codebooks"], c["scales"], 32)
+    for n in range(5):
+        w = float(c["scales"][n, 1]) * sum(float(c["codebooks"][i, int(c["codes"][i, n, 2]), 5]) for i in range(3))
+        assert y[0, n] == pytest.approx(w, rel=1e-15, abs=0)
+
+
+def _cb_mut_wrong_group(codes, codebooks, scales, g):
+    return _orig_additive(codes, codebooks, np.roll(scales, 1, axis=1), g)
+
+
+def _cb_mut_first_codebook_only(codes, codebooks, scales, g):
+    return _orig_additive(codes[:1], codebooks[:1], scales, g)
+
+
+_orig_additive = ref.dequant_codebook_additive
+
+
+@pytest.mark.parametrize("mutant", [_cb_mut_wrong_group, _cb_mut_first_codebook_only])
+def test_planted_codebook_mistakes_are_caught(monkeypatch, mutant):
+    monkeypatch.setattr(ref, "dequant_codebook_additive", mutant)
+    with pytest.raises(AssertionError):
+        test_codebook_additive_one_hot_worked_example()
