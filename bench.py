@@ -277,6 +277,10 @@ VARIANTS = {
     # the codebook workload's own shapes: the 70B layers at M = 1 and 4
     "codebook_70b_m1": dict(kind="codebook", bits=2, m=1, layers="70b"),
     "codebook_70b_m4": dict(kind="codebook", bits=2, m=4, layers="70b"),
+    # the general codebook kernel on two ~2-bit formats of the family the
+    # CodeGEMM notes compare: (m, v, g) = (3, 16, 32) and (2, 8, 64)
+    "codebook_m3v16g32_m1": dict(kind="codebook_gen", bits=2, m=1, cb=(3, 16, 32)),
+    "codebook_m2v8g64_m1": dict(kind="codebook_gen", bits=2, m=1, cb=(2, 8, 64)),
     # unfused baselines: what fusion buys.  fp16 weights (no quantization),
     # eager dequantization + dense GEMV, and the dense W4 kernel + separate SpMV
     "f16_dense_m1": dict(kind="dense", bits=16, m=1),
@@ -286,7 +290,7 @@ VARIANTS = {
 }
 
 
-def variant_layer(torch, q, dev, kind, bits, m, idx, N, K):
+def variant_layer(torch, q, dev, kind, bits, m, idx, N, K, cb=None):
     """Host case, device inputs (one copy), launch function, algorithmic bytes
     and, for the two-kernel baselines, each kernel alone with its bytes."""
     from oracle import reference as ref
@@ -302,6 +306,17 @@ def variant_layer(torch, q, dev, kind, bits, m, idx, N, K):
         call = lambda t: q.gemv_f16(t["x"], t["w"], out=y)
         oracle = lambda rows: ref.gemv_dense(c["x"], c["w"], rows=rows)
         nbytes = 2 * N * K + io
+    elif kind == "codebook_gen":
+        ncb, v, g = cb
+        c = synth.codebook_additive_case(seed, m, N, K, ncb, v, g)
+        ws = torch.zeros(max(q.codebook_gen_workspace_bytes(m, N, K, ncb, v, g), 4) // 4, dtype=torch.int32,
+                         device=dev)
+        t = dict(x=up(c["x"]), codes=q.pack_codebook_planes(up(c["codes"])), cb=up(c["codebooks"]),
+                 s=up(c["scales"]))
+        call = lambda t: q.codebook_gen(t["x"], t["codes"], t["cb"], t["s"], g, ws=ws, out=y)
+        oracle = lambda rows: ref.gemv_codebook_additive(c["x"], c["codes"], c["codebooks"], c["scales"], g,
+                                                         rows=rows)
+        nbytes = ncb * N * K // v + N * (K // g) * 2 + ncb * 256 * v * 2 + io
     elif kind == "eager":
         c = synth.uniform_case(seed, m, N, K, bits)
         t = dict(x=up(c["x"]), wq=q.pack(up(c["codes"]), bits), s=up(c["scales"]),
@@ -379,7 +394,7 @@ def measure_variants(torch, q, dev, timer, n):
         shapes = synth.LLAMA_70B_LAYERS if v.get("layers") == "70b" else synth.LLAMA3_8B_LAYERS
         for idx, (name, (N, K)) in enumerate(shapes.items()):
             t, call, oracle, y, nbytes, parts = variant_layer(torch, q, dev, v["kind"], v["bits"], v["m"], idx,
-                                                              N, K)
+                                                              N, K, v.get("cb"))
             call(t)
             rows = np.linspace(0, N - 1, 8).astype(np.int64)
             y_ref, A = oracle(rows)

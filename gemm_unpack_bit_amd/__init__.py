@@ -44,6 +44,8 @@ _SIGS = {
     "qgemv_codebook": (_i, [_i, _i, _i, _vp, _vp, _vp, _vp, _vp, _vp, _sz, _vp]),
     "qgemv_codebook_workspace_bytes": (_sz, [_i, _i, _i]),
     "qgemv_tilecoo_encode": (_i, [_i, _i, ctypes.c_int64, _vp, _vp, _vp, _vp, _vp]),
+    "qgemv_codebook_gen": (_i, [_i, _i, _i, _i, _i, _i, _vp, _vp, _vp, _vp, _vp, _vp, _sz, _vp]),
+    "qgemv_codebook_gen_workspace_bytes": (_sz, [_i, _i, _i, _i, _i, _i]),
     "qgemv_dequant": (_i, [_i, _i, _i, _vp, _vp, _vp, _vp, _vp]),
     "qgemv_dequant_lut4": (_i, [_i, _i, _vp, _vp, _vp, _vp, _vp]),
     "qgemv_gemv_f16": (_i, [_i, _i, _i, _vp, _vp, _vp, _vp]),
@@ -379,3 +381,51 @@ def spmv_tilecoo(x, tile_ptr, tile_rec, y):
                                                           _ptr(tile_rec if nnz else None), nnz, _ptr(y),
                                                           _stream(x)))
     return y
+
+
+# ---------------------------------------------------------------------------
+# general codebook GEMV (m additive codebooks, vector length v, group g)
+# ---------------------------------------------------------------------------
+
+def pack_codebook_planes(codes):
+    """[ncb, N, K/v] uint8 codes -> int32 words: the ncb planes, each packed in
+    the 64-row layout, one after the other (the qgemv_codebook_gen format)."""
+    torch = _torch()
+    _need(codes, torch.uint8, "codes")
+    return torch.cat([pack(codes[i].contiguous(), 8, LAYOUT_ROWS64) for i in range(codes.shape[0])])
+
+
+def codebook_gen_workspace_bytes(M, N, K, ncb, v, group):
+    return int(lib().qgemv_codebook_gen_workspace_bytes(M, N, K, ncb, v, group))
+
+
+def codebook_gen(x, codes, codebooks, scales, group, ws=None, out=None):
+    """y = x . W^T with w[n, v j + t] = scales[n, (v j + t)/group] * sum_i codebooks[i][codes_i[n, j]][t].
+
+    codes: int32 words from pack_codebook_planes; codebooks [ncb, 256, v] fp16;
+    scales [N, K/group] fp16; ws: optional device scratch of
+    codebook_gen_workspace_bytes(...) bytes."""
+    torch = _torch()
+    _need(x, torch.float16, "x")
+    _need(codes, torch.int32, "codes")
+    _need(codebooks, torch.float16, "codebooks")
+    _need(scales, torch.float16, "scales")
+    M, K = x.shape
+    N = scales.shape[0]
+    ncb, nc, v = codebooks.shape
+    if nc != 256:
+        raise ValueError("codebooks must be [ncb, 256, v]")
+    need = packed_words(8, N, K // v, LAYOUT_ROWS64) * ncb if v and K % v == 0 else 0
+    if need and codes.numel() != need:
+        raise ValueError("codes do not hold ncb planes of N x K/v codes")
+    if ws is not None and (not ws.is_cuda or not ws.is_contiguous()):
+        raise ValueError("ws must be a contiguous CUDA tensor")
+    if out is None:
+        out = torch.empty((M, N), dtype=torch.float16, device=x.device)
+    else:
+        _need(out, torch.float16, "out")
+    wsb = ws.numel() * ws.element_size() if ws is not None else 0
+    _check("qgemv_codebook_gen", lib().qgemv_codebook_gen(M, N, K, ncb, v, group, _ptr(x), _ptr(codes),
+                                                          _ptr(codebooks), _ptr(scales), _ptr(out), _ptr(ws),
+                                                          wsb, _stream(x)))
+    return out

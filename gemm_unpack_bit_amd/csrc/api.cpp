@@ -273,6 +273,50 @@ int qgemv_codebook(int M, int N, int K, const uint16_t* x, const uint32_t* codes
   return hip_status(qg::launch_gemv_codebook(a, c, reinterpret_cast<hipStream_t>(stream)));
 }
 
+namespace {
+bool gen_format_ok(int ncb, int v, int group) {
+  return (v == 4 || v == 8 || v == 16) && ncb >= 1 && ncb <= v / 4 && (group == 32 || group == 64 || group == 128);
+}
+}  // namespace
+
+size_t qgemv_codebook_gen_workspace_bytes(int M, int N, int K, int ncb, int v, int group) {
+  if (!gen_format_ok(ncb, v, group) || M < 1 || M > QGEMV_MAX_M || N < 1 || K < 256 || K % 256) return 0;
+  return qg::codebook_gen_ws_bytes(M, N, K);
+}
+
+int qgemv_codebook_gen(int M, int N, int K, int ncb, int v, int group, const uint16_t* x, const uint32_t* codes,
+                       const uint16_t* codebooks, const uint16_t* scales, uint16_t* y, void* ws, size_t ws_bytes,
+                       qgemv_stream_t stream) {
+  if (!x || !codes || !codebooks || !scales || !y) return QGEMV_ERR_NULL;
+  if (!gen_format_ok(ncb, v, group)) return QGEMV_ERR_UNSUPPORTED;
+  if (M < 1 || M > QGEMV_MAX_M || N < 1 || K < 256 || K % 256) return QGEMV_ERR_SHAPE;
+  const size_t plane = words(8, QGEMV_LAYOUT_ROWS64, N, K / v) * 4;
+  const long lim = 1L << 31;
+  if ((long)(plane * ncb) >= lim || (long)M * K * 2 >= lim || (long)M * N * 2 >= lim ||
+      (long)N * (K / group) * 2 >= lim)
+    return QGEMV_ERR_SHAPE;
+  if (!aligned16(codes) || ((uintptr_t)x & 7u) || ((uintptr_t)codebooks & 7u) || ((uintptr_t)scales & 1u) ||
+      ((uintptr_t)y & 1u) || ((uintptr_t)ws & 3u))
+    return QGEMV_ERR_ALIGN;
+  const size_t ybytes = (size_t)M * N * 2, cbytes = (size_t)ncb * 256 * v * 2;
+  const size_t xbytes = (size_t)M * K * 2, sbytes = (size_t)N * (K / group) * 2;
+  if (overlaps(y, ybytes, x, xbytes) || overlaps(y, ybytes, codes, plane * ncb) ||
+      overlaps(y, ybytes, codebooks, cbytes) || overlaps(y, ybytes, scales, sbytes) ||
+      (ws && overlaps(y, ybytes, ws, ws_bytes)))
+    return QGEMV_ERR_VALUE;
+  if (ws && (overlaps(ws, ws_bytes, x, xbytes) || overlaps(ws, ws_bytes, codes, plane * ncb) ||
+             overlaps(ws, ws_bytes, codebooks, cbytes) || overlaps(ws, ws_bytes, scales, sbytes)))
+    return QGEMV_ERR_VALUE;
+  int ks = qg::codebook_gen_ks(M, N, K);
+  if (const char* e = std::getenv("QGEMV_CODEBOOK_GEN_KS")) {  // tuning override: K parts
+    const int k = std::atoi(e);
+    if (k >= 1) ks = k < K / 256 ? k : K / 256;
+  }
+  if (ks > 1 && (!ws || ws_bytes < (size_t)ks * M * N * 4)) ks = 1;  // no room for partial sums
+  qg::CodebookGenArgs a{M, N, K, ncb, v, group, x, codes, codebooks, scales, y, reinterpret_cast<float*>(ws)};
+  return hip_status(qg::launch_gemv_codebook_gen(a, ks, reinterpret_cast<hipStream_t>(stream)));
+}
+
 int qgemv_lut4(int M, int N, int K, const uint16_t* x, const uint32_t* wq, const uint16_t* absmax,
                const uint16_t* lut, uint16_t* y, qgemv_stream_t stream) {
   if (!x || !wq || !absmax || !lut || !y) return QGEMV_ERR_NULL;

@@ -579,6 +579,177 @@ __global__ void __launch_bounds__(512) gemv_codebook_statb_kernel(CodebookArgs a
 // outputs; wave j adds parts j, j + 8, j + 16, ... (loads issued 8 at a time,
 // each a 256-byte row), and wave 0 adds the 8 wave sums in order: a fixed
 // order for every output, so the result is deterministic.
+// General codebook kernel (CodeGEMM notes, key design 3: one kernel for any
+// number of codebooks m, vector length v, code bits b and group size g):
+// NCB additive codebooks of 256 centroids of V dims (V = 4, 8, 16), 8-bit
+// codes, one scale per g k (g = 32, 64, 128), and at most 2 code bits per
+// weight (NCB * 256 / V <= 64), so the Psumbook rows of a 256-k chunk -- row
+// i * S + s for codebook i and segment s, S = 256 / V -- fit the same
+// 64-row table as the single-codebook kernels.
+//   w[n, V j + t] = s[n, (V j + t) / g] * sum_i C_i[code_i[n, j]][t]
+//   P_i[j][c]    = sum_t C_i[c][t] * x[m, V j + t]
+//   y[m, n]      = sum_groups s[n, group] * sum_{j in group} sum_i P_i[j][code_i[n, j]]
+// Codes are NCB planes, each an [N, K/V] uint8 matrix in the 64-row layout.
+// A workgroup of 4 waves owns 4 row blocks and a K range.  Per chunk:
+// LDS barrier, the build on the matrix cores (v_mfma_f32_32x32x8_f16, A =
+// codebook rows with their dims in 8-wide steps, zero-padded for V = 4, B =
+// activation segments; tasks (codebook, centroid block, segment block) dealt
+// to the waves in turn), LDS barrier, then each lane looks up its own row's
+// codes, pairs of segments summed by one v_dot2, a group partial scaled once.
+// The next chunk's codes, scales and activation segments are in flight
+// meanwhile.  K parts (KS > 1) go through the workspace and the reduce kernel.
+template <int V, int NCB>
+__global__ void __launch_bounds__(256) gemv_codebook_gen_kernel(CodebookGenArgs a) {
+  constexpr int S = 256 / V;           // segments per chunk and codebook
+  constexpr int NT = S / 16;           // 16-code tiles per chunk and plane
+  constexpr int SB = (S + 31) / 32;    // 32-segment blocks
+  constexpr int NST = V <= 8 ? 1 : 2;  // 8-dim MFMA steps
+  constexpr int T = NCB * 8 * SB;      // build tasks per chunk
+  constexpr int TW = (T + 3) / 4;      // tasks per wave
+  static_assert(NCB * S <= 64, "a chunk's Psumbook rows fit the table");
+  __shared__ __attribute__((aligned(16))) uint32_t lsm[PSUM_BYTES / 4];
+  char* const lds = reinterpret_cast<char*>(lsm);
+
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int M = a.M, N = a.N, K = a.K, GS = a.group;
+  const int HN = K / 256;  // chunks
+  const int NB = (N + 63) / 64;
+  const int CPR = K / V / 16;  // code tiles per row block and plane
+  const uint32_t PLANE = (uint32_t)NB * CPR * 1024u;
+  const int GPR = K / GS;   // scale groups per row
+  const int NG = 256 / GS;  // scale groups per chunk
+  const int m = blockIdx.z;
+  const int ks = blockIdx.y, KS = gridDim.y;
+  const int h0 = (HN * ks) / KS, h1 = (HN * (ks + 1)) / KS;
+  const int rb = blockIdx.x * 4 + wave;  // this wave's 64-row block
+  const uint32_t row = (uint32_t)rb * 64u + lane;
+  const bool rv = rb < NB && row < (uint32_t)N;
+  const int li = lane & 31, hi = lane >> 5;
+
+  const rsrc_t rc = make_rsrc(a.codes, PLANE * NCB);
+  const rsrc_t rs = make_rsrc(a.scales, (uint32_t)N * GPR * 2u);
+  const rsrc_t rx = make_rsrc(a.x, (uint32_t)M * K * 2u);
+
+  // A operands, kept for the whole kernel: task u = wave + 4 j is codebook
+  // u / (8 SB), centroid block (u / SB) % 8, segment block u % SB; lane l
+  // holds centroid 32 cb + l % 32, dims 8 step + 4 (l / 32) .. + 3
+  h4v ca[TW][NST];
+  {
+    const rsrc_t rcb = make_rsrc(a.codebooks, NCB * 256u * V * 2u);
+#pragma unroll
+    for (int j = 0; j < TW; ++j) {
+      const int u = wave + 4 * j, ci = u / (8 * SB), cb = (u / SB) % 8;
+#pragma unroll
+      for (int st = 0; st < NST; ++st) {
+        const int d0 = 8 * st + 4 * hi;
+        const bool ok = u < T && d0 < V;
+        ca[j][st] = __builtin_bit_cast(
+            h4v, __builtin_amdgcn_raw_buffer_load_b64(rcb, ok ? (uint32_t)(((ci * 256 + 32 * cb + li) * V + d0) * 2) : OOB,
+                                                      0, 0));
+      }
+    }
+  }
+  struct St {
+    u4 c[NCB * NT];  // this lane's row's codes of the chunk, per plane
+    uint16_t s[8];   // the chunk's scales of this row
+    u2 xb[TW][NST];  // B operands of this wave's tasks
+  };
+  const uint32_t vcode = rb < NB ? 16u * lane : OOB;
+  const uint32_t vscale = rv ? row * (uint32_t)GPR * 2u : OOB;
+  auto load_stage = [&](int h, St& st) {
+    const uint32_t hc = (uint32_t)min(h, h1 - 1);  // (past the range: a harmless re-read)
+#pragma unroll
+    for (int i = 0; i < NCB; ++i)
+#pragma unroll
+      for (int t = 0; t < NT; ++t) {
+        const uint32_t so = __builtin_amdgcn_readfirstlane(
+            (uint32_t)i * PLANE + ((uint32_t)min(rb, NB - 1) * CPR + hc * NT + t) * 1024u);
+        st.c[i * NT + t] = bload16<CPOL_NT>(rc, vcode, so);
+      }
+#pragma unroll
+    for (int gg = 0; gg < 8; ++gg)
+      if (gg < NG) st.s[gg] = bload2(rs, vscale, (hc * NG + gg) * 2u);
+#pragma unroll
+    for (int j = 0; j < TW; ++j) {
+      const int u = wave + 4 * j, seg = 32 * (u % SB) + li;
+#pragma unroll
+      for (int st2 = 0; st2 < NST; ++st2) {
+        const int d0 = 8 * st2 + 4 * hi;
+        const bool ok = u < T && seg < S && d0 < V;
+        st.xb[j][st2] = __builtin_bit_cast(
+            u2, __builtin_amdgcn_raw_buffer_load_b64(
+                    rx, ok ? ((uint32_t)m * K + 256u * hc + (uint32_t)(V * seg + d0)) * 2u : OOB, 0, 0));
+      }
+    }
+  };
+
+  const h2 ones = {(_Float16)1.0f, (_Float16)1.0f};
+  float acc = 0.f;
+  auto step = [&](int h, const St& st, St& nxt) {
+    load_stage(h + 1, nxt);
+    lds_barrier();  // every wave is done reading the previous chunk's P
+#pragma unroll
+    for (int j = 0; j < TW; ++j) {
+      const int u = wave + 4 * j;
+      if (u < T) {  // (wave-uniform)
+        const int ci = u / (8 * SB), cb = (u / SB) % 8, seg = 32 * (u % SB) + li;
+        f16v d = f16v{};
+#pragma unroll
+        for (int st2 = 0; st2 < NST; ++st2)
+          d = __builtin_amdgcn_mfma_f32_32x32x8f16(ca[j][st2], __builtin_bit_cast(h4v, st.xb[j][st2]), d, 0, 0, 0);
+        // lane l, register 4 g + r: P_ci[seg][32 cb + 8 g + 4 (l / 32) + r]
+        if (seg < S) {
+          char* const base = lds + (uint32_t)(ci * S + seg) * PSTRIDE + 2u * (32u * cb + 4u * hi);
+#pragma unroll
+          for (int g = 0; g < 4; ++g) {
+            const h4v hv = {(_Float16)d[4 * g], (_Float16)d[4 * g + 1], (_Float16)d[4 * g + 2], (_Float16)d[4 * g + 3]};
+            *reinterpret_cast<u2*>(base + 16u * g) = __builtin_bit_cast(u2, hv);
+          }
+        }
+      }
+    }
+    lds_barrier();  // P of this chunk complete
+    // lookups: segments in pairs (a group holds at least 2 segments, an even
+    // number), the group partial scaled once
+    float part = 0.f;
+#pragma unroll
+    for (int sp = 0; sp < S; sp += 2) {
+#pragma unroll
+      for (int i = 0; i < NCB; ++i) {
+        h2 pv;
+#pragma unroll
+        for (int e = 0; e < 2; ++e) {
+          const int sg = sp + e;
+          const uint32_t w = st.c[i * NT + sg / 16][(sg % 16) / 4];
+          const uint32_t code2 = __builtin_amdgcn_ubfe(w, 8 * (sg % 4), 8) << 1;
+          pv[e] = *reinterpret_cast<const _Float16*>(lds + code2 + PSTRIDE * (uint32_t)(i * S + sg));
+        }
+        part = dot2(pv, ones, part);
+      }
+      if (((sp + 2) * V) % GS == 0) {  // (wave-uniform) end of a scale group
+        const int gi = (sp * V) / GS;
+        uint16_t sc = st.s[0];
+#pragma unroll
+        for (int gg = 1; gg < 8; ++gg) sc = gg == gi ? st.s[gg] : sc;  // (no dynamic register index)
+        acc = fmaf(h2f(sc), part, acc);
+        part = 0.f;
+      }
+    }
+  };
+  St ring[2];
+  load_stage(h0, ring[0]);
+  for (int h = h0; h < h1; h += 2) {  // two chunks per iteration so the stages are named statically
+    step(h, ring[0], ring[1]);
+    if (h + 1 < h1) step(h + 1, ring[1], ring[0]);
+  }
+  if (!rv) return;
+  if (KS == 1)
+    a.y[(size_t)m * N + row] = f2h(acc);
+  else  // K split: this range's partial sum, added up by the reduce kernel
+    a.ws[((size_t)ks * M + m) * N + row] = acc;
+}
+
 __global__ void __launch_bounds__(512) codebook_reduce_kernel(const float* __restrict__ ws, uint16_t* __restrict__ y,
                                                               int MN, int KS) {
   __shared__ float part[8][64];
@@ -722,6 +893,50 @@ hipError_t launch_gemv_codebook(const CodebookArgs& a, const CodebookCfg& c, hip
   if (parts > 1) {
     const int MN = a.M * a.N;
     hipLaunchKernelGGL(codebook_reduce_kernel, dim3((MN + 63) / 64), dim3(512), 0, s, a.ws, a.y, MN, parts);
+  }
+  return hipGetLastError();
+}
+
+// General codebook kernel: K parts such that the grid has about 512
+// workgroups (each walks at least one 256-k chunk).
+int codebook_gen_ks(int M, int N, int K) {
+  const int wgs = ((N + 63) / 64 + 3) / 4 * M;
+  int ks = (512 + wgs - 1) / wgs;
+  if (ks > K / 256) ks = K / 256;
+  return ks < 1 ? 1 : ks;
+}
+
+size_t codebook_gen_ws_bytes(int M, int N, int K) {
+  const int ks = codebook_gen_ks(M, N, K);
+  return ks > 1 ? (size_t)ks * M * N * 4 : 0;
+}
+
+template <int V, int NCB>
+void* gen_kernel_ptr() {
+  return reinterpret_cast<void*>(&gemv_codebook_gen_kernel<V, NCB>);
+}
+
+hipError_t launch_gemv_codebook_gen(const CodebookGenArgs& a, int ks, hipStream_t s) {
+  void* kern = nullptr;
+  switch (a.v * 10 + a.ncb) {
+    case 41: kern = gen_kernel_ptr<4, 1>(); break;
+    case 81: kern = gen_kernel_ptr<8, 1>(); break;
+    case 82: kern = gen_kernel_ptr<8, 2>(); break;
+    case 161: kern = gen_kernel_ptr<16, 1>(); break;
+    case 162: kern = gen_kernel_ptr<16, 2>(); break;
+    case 163: kern = gen_kernel_ptr<16, 3>(); break;
+    case 164: kern = gen_kernel_ptr<16, 4>(); break;
+    default: return hipErrorInvalidValue;
+  }
+  if (ks < 1 || ks > a.K / 256 || (ks > 1 && !a.ws)) return hipErrorInvalidValue;
+  const int NB = (a.N + 63) / 64;
+  const dim3 grid((unsigned)((NB + 3) / 4), ks, a.M);
+  void* args[] = {const_cast<CodebookGenArgs*>(&a)};
+  hipError_t e = hipLaunchKernel(kern, grid, dim3(256), args, 0, s);
+  if (e != hipSuccess) return e;
+  if (ks > 1) {
+    const int MN = a.M * a.N;
+    hipLaunchKernelGGL(codebook_reduce_kernel, dim3((MN + 63) / 64), dim3(512), 0, s, a.ws, a.y, MN, ks);
   }
   return hipGetLastError();
 }

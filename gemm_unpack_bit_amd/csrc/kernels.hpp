@@ -82,6 +82,23 @@ CodebookCfg codebook_fallback();
 size_t codebook_ws_bytes(const CodebookCfg& c, int M, int N, int K);
 hipError_t launch_gemv_codebook(const CodebookArgs& a, const CodebookCfg& c, hipStream_t s);
 
+// General codebook kernel: ncb additive codebooks [ncb][256][v] fp16 (v = 4,
+// 8, 16; ncb <= v / 4), codes as ncb planes of [N, K/v] uint8 in the 64-row
+// layout, scales fp16 [N, K/group] (group = 32, 64, 128); ws: the K parts'
+// fp32 partial sums (ks x M x N) when ks > 1
+struct CodebookGenArgs {
+  int M, N, K, ncb, v, group;
+  const uint16_t* x;
+  const uint32_t* codes;
+  const uint16_t* codebooks;
+  const uint16_t* scales;
+  uint16_t* y;
+  float* ws;
+};
+int codebook_gen_ks(int M, int N, int K);
+size_t codebook_gen_ws_bytes(int M, int N, int K);
+hipError_t launch_gemv_codebook_gen(const CodebookGenArgs& a, int ks, hipStream_t s);
+
 // Unfused baselines (unfused.hip): eager dequantization to fp16 W [N, K]
 // row-major (uniform b-bit: bits, wq, scales, zeros; LUT4: wq, absmax, lut),
 // a dense fp16 GEMV over it, and a Tile-COO SpMV that adds x . S^T into y.

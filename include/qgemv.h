@@ -258,6 +258,44 @@ int qgemv_codebook(int M, int N, int K, const uint16_t *x, const uint32_t *codes
 size_t qgemv_codebook_workspace_bytes(int M, int N, int K);
 
 /* ------------------------------------------------------------------------
+ * General codebook GEMV (CodeGEMM paper notes, key design 3: one kernel for
+ * any number of codebooks m, vector length v, code bits b and group size g),
+ * with m additive codebooks:
+ *     w[n, v*j + t] = scales[n, (v*j + t)/group] * sum_i codebooks[i][codes_i[n, j]][t]
+ * computed through one Psumbook per codebook (as qgemv_codebook).
+ *
+ *   ncb        m, the number of codebooks: 1 <= ncb <= v/4 (at most 2 code
+ *              bits per weight)
+ *   v          vector length: 4, 8 or 16
+ *   group      scale group along K: 32, 64 or 128
+ *   x          [dev] fp16   [M, K]
+ *   codes      [dev] uint32 ncb planes one after the other, plane i being
+ *                          codebook i's [N, K/v] uint8 codes packed with
+ *                          qgemv_pack(8, QGEMV_LAYOUT_ROWS64, N, K/v)
+ *   codebooks  [dev] fp16   [ncb][256][v]
+ *   scales     [dev] fp16   [N, K/group]
+ *   y          [dev] fp16   [M, N] (written)
+ *   ws         [dev] optional scratch of
+ *                  qgemv_codebook_gen_workspace_bytes(M, N, K, ncb, v, group)
+ *                  bytes for the fp32 partial sums of K parts (added by a
+ *                  second kernel in a fixed order); NULL or smaller: one K
+ *                  range per workgroup (same result within the tolerance,
+ *                  slower).  Calls that share a workspace must not overlap.
+ *
+ * Shapes: 1 <= M <= 16, N >= 1, K a positive multiple of 256
+ * (QGEMV_ERR_SHAPE); other ncb / v / group: QGEMV_ERR_UNSUPPORTED.  codes
+ * 16-byte aligned, x and codebooks 8-byte, ws 4-byte, scales and y 2-byte
+ * (QGEMV_ERR_ALIGN).  Neither y nor ws may overlap an input, nor each other
+ * (QGEMV_ERR_VALUE).  Asynchronous, deterministic for a given workspace size.
+ * ------------------------------------------------------------------------ */
+int qgemv_codebook_gen(int M, int N, int K, int ncb, int v, int group, const uint16_t *x,
+                       const uint32_t *codes, const uint16_t *codebooks, const uint16_t *scales,
+                       uint16_t *y, void *ws, size_t ws_bytes, qgemv_stream_t stream);
+/* Workspace bytes qgemv_codebook_gen uses to split K (0 if it never splits,
+ * or on bad arguments). */
+size_t qgemv_codebook_gen_workspace_bytes(int M, int N, int K, int ncb, int v, int group);
+
+/* ------------------------------------------------------------------------
  * Unfused baselines: the kernel sequences that the fused entry points above
  * replace, for measuring what fusion buys.  Same results within the
  * tolerance; more HBM traffic and one more launch.

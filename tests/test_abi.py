@@ -161,3 +161,24 @@ def test_unfused_validation_without_gpu(L):
     assert sp(p=FAKE * 2 + 2) == q.ERR_ALIGN
     assert sp(y=FAKE * 3) == q.ERR_VALUE                 # y overlaps the records
     assert sp(r=0, nnz=0) == q.OK                        # nothing to add: no launch
+
+
+def test_codebook_gen_validation_without_gpu(L):
+    v_ = ctypes.c_void_p
+
+    def cg(M=1, N=64, K=512, ncb=1, v=4, g=128, x=FAKE, codes=FAKE * 2, cbk=FAKE * 3, s=FAKE * 4, y=FAKE * 64,
+           ws=0, wsb=0):
+        return L.qgemv_codebook_gen(M, N, K, ncb, v, g, v_(x), v_(codes), v_(cbk), v_(s), v_(y), v_(ws), wsb, v_(0))
+
+    assert cg(codes=0) == q.ERR_NULL
+    assert cg(v=6) == q.ERR_UNSUPPORTED
+    assert cg(ncb=2, v=4) == q.ERR_UNSUPPORTED      # more than 2 code bits per weight
+    assert cg(g=16) == q.ERR_UNSUPPORTED
+    assert cg(K=384) == q.ERR_SHAPE                 # K must be a multiple of 256
+    assert cg(M=17) == q.ERR_SHAPE
+    assert cg(x=FAKE + 4) == q.ERR_ALIGN
+    assert cg(codes=FAKE * 2 + 8) == q.ERR_ALIGN
+    assert cg(y=FAKE * 3) == q.ERR_VALUE            # y overlaps the codebooks
+    assert cg(ws=FAKE * 4, wsb=64) == q.ERR_VALUE   # the workspace overlaps the scales
+    assert L.qgemv_codebook_gen_workspace_bytes(1, 64, 512, 2, 4, 128) == 0
+    assert L.qgemv_codebook_gen_workspace_bytes(1, 4096, 4096, 3, 16, 32) >= 4 * 4096
