@@ -308,11 +308,13 @@ int qgemv_codebook_gen(int M, int N, int K, int ncb, int v, int group, const uin
              overlaps(ws, ws_bytes, codebooks, cbytes) || overlaps(ws, ws_bytes, scales, sbytes)))
     return QGEMV_ERR_VALUE;
   int ks = qg::codebook_gen_ks(M, N, K);
-  if (const char* e = std::getenv("QGEMV_CODEBOOK_GEN_KS")) {  // tuning override: K parts
+  if (const char* e = std::getenv("QGEMV_CODEBOOK_GEN_KS")) {  // tuning override: K parts, or -wk (stationary)
     const int k = std::atoi(e);
     if (k >= 1) ks = k < K / 256 ? k : K / 256;
+    if (k <= -1 && k >= -4) ks = k;
   }
-  if (ks > 1 && (!ws || ws_bytes < (size_t)ks * M * N * 4)) ks = 1;  // no room for partial sums
+  const size_t need = ks < 0 ? (size_t)(K / 256) * M * N * 4 : (ks > 1 ? (size_t)ks * M * N * 4 : 0);
+  if (need > 0 && (!ws || ws_bytes < need)) ks = 1;  // no room for partial sums: one K range per workgroup
   qg::CodebookGenArgs a{M, N, K, ncb, v, group, x, codes, codebooks, scales, y, reinterpret_cast<float*>(ws)};
   return hip_status(qg::launch_gemv_codebook_gen(a, ks, reinterpret_cast<hipStream_t>(stream)));
 }

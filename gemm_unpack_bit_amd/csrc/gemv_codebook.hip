@@ -750,6 +750,130 @@ __global__ void __launch_bounds__(256) gemv_codebook_gen_kernel(CodebookGenArgs 
     a.ws[((size_t)ks * M + m) * N + row] = acc;
 }
 
+// Stationary form of the general kernel: a workgroup of WK waves owns one
+// 256-k chunk h and one batch row, builds the chunk's Psumbooks once, and
+// streams row blocks through them (wave w of row slice r takes row blocks
+// r WK + w + i R WK, the next one in flight) with no barrier after the build; each row's partial sum
+// for the chunk goes to the workspace, and the reduce kernel adds the chunks
+// in a fixed order.  Grid: R x K/256 x M workgroups.
+template <int V, int NCB>
+__global__ void __launch_bounds__(256) gemv_codebook_gen_stat_kernel(CodebookGenArgs a, int R) {
+  constexpr int S = 256 / V;
+  constexpr int NT = S / 16;
+  constexpr int SB = (S + 31) / 32;
+  constexpr int NST = V <= 8 ? 1 : 2;
+  constexpr int T = NCB * 8 * SB;
+  static_assert(NCB * S <= 64, "a chunk's Psumbook rows fit the table");
+  __shared__ __attribute__((aligned(16))) uint32_t lsm[PSUM_BYTES / 4];
+  char* const lds = reinterpret_cast<char*>(lsm);
+
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int WK = blockDim.x >> 6;
+  const int M = a.M, N = a.N, K = a.K, GS = a.group;
+  const int NB = (N + 63) / 64;
+  const int CPR = K / V / 16;
+  const uint32_t PLANE = (uint32_t)NB * CPR * 1024u;
+  const int GPR = K / GS, NG = 256 / GS;
+  const int r = blockIdx.x, h = blockIdx.y, m = blockIdx.z;
+  const int li = lane & 31, hi = lane >> 5;
+  const rsrc_t rc = make_rsrc(a.codes, PLANE * NCB);
+  const rsrc_t rs = make_rsrc(a.scales, (uint32_t)N * GPR * 2u);
+  const rsrc_t rx = make_rsrc(a.x, (uint32_t)M * K * 2u);
+
+  // the row blocks this wave streams, each with its codes and scales
+  struct St {
+    u4 c[NCB * NT];
+    uint16_t s[8];
+  };
+  auto load_rows = [&](int rb, St& st) {
+    const bool bv = rb < NB;  // (past the last block: zeros, never used)
+    const uint32_t vcode = bv ? 16u * lane : OOB;
+    const uint32_t row = (uint32_t)rb * 64u + lane;
+    const uint32_t vscale = bv && row < (uint32_t)N ? row * (uint32_t)GPR * 2u : OOB;
+#pragma unroll
+    for (int i = 0; i < NCB; ++i)
+#pragma unroll
+      for (int t = 0; t < NT; ++t) {
+        const uint32_t so = __builtin_amdgcn_readfirstlane(
+            (uint32_t)i * PLANE + ((uint32_t)min(rb, NB - 1) * CPR + (uint32_t)h * NT + t) * 1024u);
+        st.c[i * NT + t] = bload16<CPOL_NT>(rc, vcode, so);
+      }
+#pragma unroll
+    for (int gg = 0; gg < 8; ++gg)
+      if (gg < NG) st.s[gg] = bload2(rs, vscale, ((uint32_t)h * NG + gg) * 2u);
+  };
+  const int step_rb = R * WK;
+  int rb = r * WK + wave;
+  St ring[2];
+  // the activation segments and codebook rows of the build are issued first:
+  // a wave's loads return in order
+  {
+    const rsrc_t rcb = make_rsrc(a.codebooks, NCB * 256u * V * 2u);
+    for (int u = wave; u < T; u += WK) {  // (wave-uniform)
+      const int ci = u / (8 * SB), cb = (u / SB) % 8, seg = 32 * (u % SB) + li;
+      f16v d = f16v{};
+#pragma unroll
+      for (int st = 0; st < NST; ++st) {
+        const int d0 = 8 * st + 4 * hi;
+        const h4v av = __builtin_bit_cast(
+            h4v, __builtin_amdgcn_raw_buffer_load_b64(
+                     rcb, d0 < V ? (uint32_t)(((ci * 256 + 32 * cb + li) * V + d0) * 2) : OOB, 0, 0));
+        const h4v bv = __builtin_bit_cast(
+            h4v, __builtin_amdgcn_raw_buffer_load_b64(
+                     rx, seg < S && d0 < V ? ((uint32_t)m * K + 256u * h + (uint32_t)(V * seg + d0)) * 2u : OOB, 0,
+                     0));
+        d = __builtin_amdgcn_mfma_f32_32x32x8f16(av, bv, d, 0, 0, 0);
+      }
+      if (seg < S) {
+        char* const base = lds + (uint32_t)(ci * S + seg) * PSTRIDE + 2u * (32u * cb + 4u * hi);
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          const h4v hv = {(_Float16)d[4 * g], (_Float16)d[4 * g + 1], (_Float16)d[4 * g + 2], (_Float16)d[4 * g + 3]};
+          *reinterpret_cast<u2*>(base + 16u * g) = __builtin_bit_cast(u2, hv);
+        }
+      }
+    }
+  }
+  load_rows(rb, ring[0]);
+  __syncthreads();  // the Psumbooks are complete
+
+  const h2 ones = {(_Float16)1.0f, (_Float16)1.0f};
+  auto lookups = [&](int rbk, const St& st, St& nxt) {
+    load_rows(rbk + step_rb, nxt);
+    float acc = 0.f, part = 0.f;
+#pragma unroll
+    for (int sp = 0; sp < S; sp += 2) {
+#pragma unroll
+      for (int i = 0; i < NCB; ++i) {
+        h2 pv;
+#pragma unroll
+        for (int e = 0; e < 2; ++e) {
+          const int sg = sp + e;
+          const uint32_t w = st.c[i * NT + sg / 16][(sg % 16) / 4];
+          const uint32_t code2 = __builtin_amdgcn_ubfe(w, 8 * (sg % 4), 8) << 1;
+          pv[e] = *reinterpret_cast<const _Float16*>(lds + code2 + PSTRIDE * (uint32_t)(i * S + sg));
+        }
+        part = dot2(pv, ones, part);
+      }
+      if (((sp + 2) * V) % GS == 0) {  // (wave-uniform) end of a scale group
+        const int gi = (sp * V) / GS;
+        uint16_t sc = st.s[0];
+#pragma unroll
+        for (int gg = 1; gg < 8; ++gg) sc = gg == gi ? st.s[gg] : sc;  // (no dynamic register index)
+        acc = fmaf(h2f(sc), part, acc);
+        part = 0.f;
+      }
+    }
+    const uint32_t row = (uint32_t)rbk * 64u + lane;
+    if (row < (uint32_t)N) a.ws[((size_t)h * M + m) * N + row] = acc;
+  };
+  for (; rb < NB; rb += 2 * step_rb) {  // two row blocks per iteration so the stages are named statically
+    lookups(rb, ring[0], ring[1]);
+    if (rb + step_rb < NB) lookups(rb + step_rb, ring[1], ring[0]);
+  }
+}
+
 __global__ void __launch_bounds__(512) codebook_reduce_kernel(const float* __restrict__ ws, uint16_t* __restrict__ y,
                                                               int MN, int KS) {
   __shared__ float part[8][64];
@@ -897,9 +1021,13 @@ hipError_t launch_gemv_codebook(const CodebookArgs& a, const CodebookCfg& c, hip
   return hipGetLastError();
 }
 
-// General codebook kernel: K parts such that the grid has about 512
-// workgroups (each walks at least one 256-k chunk).
+// General codebook kernel dispatch (sweeps of the 8B layers at M = 1 for
+// (m, v, g) = (1, 4, 128), (3, 16, 32), (2, 8, 64)): the stationary form
+// with 4 waves up to K = 8192 (returned as -4), else the sequential form
+// with K parts such that the grid has about 512 workgroups (each walks at
+// least one 256-k chunk).
 int codebook_gen_ks(int M, int N, int K) {
+  if (K <= 8192 && K >= 512) return -4;
   const int wgs = ((N + 63) / 64 + 3) / 4 * M;
   int ks = (512 + wgs - 1) / wgs;
   if (ks > K / 256) ks = K / 256;
@@ -907,8 +1035,8 @@ int codebook_gen_ks(int M, int N, int K) {
 }
 
 size_t codebook_gen_ws_bytes(int M, int N, int K) {
-  const int ks = codebook_gen_ks(M, N, K);
-  return ks > 1 ? (size_t)ks * M * N * 4 : 0;
+  // room for the stationary form's one partial per 256-k chunk (the most parts)
+  return K / 256 > 1 ? (size_t)(K / 256) * M * N * 4 : 0;
 }
 
 template <int V, int NCB>
@@ -916,17 +1044,42 @@ void* gen_kernel_ptr() {
   return reinterpret_cast<void*>(&gemv_codebook_gen_kernel<V, NCB>);
 }
 
+template <int V, int NCB>
+void* gen_stat_kernel_ptr() {
+  return reinterpret_cast<void*>(&gemv_codebook_gen_stat_kernel<V, NCB>);
+}
+
+// stationary form: R row slices per chunk, about 256 workgroups
+int codebook_gen_stat_r(int M, int N, int K, int wk) {
+  const int rmax = ((N + 63) / 64 + wk - 1) / wk;
+  int r = (256 + (K / 256) * M - 1) / ((K / 256) * M);
+  return r < 1 ? 1 : (r > rmax ? rmax : r);
+}
+
 hipError_t launch_gemv_codebook_gen(const CodebookGenArgs& a, int ks, hipStream_t s) {
   void* kern = nullptr;
+  const bool stat = ks < 0;  // stationary: one K part per 256-k chunk
   switch (a.v * 10 + a.ncb) {
-    case 41: kern = gen_kernel_ptr<4, 1>(); break;
-    case 81: kern = gen_kernel_ptr<8, 1>(); break;
-    case 82: kern = gen_kernel_ptr<8, 2>(); break;
-    case 161: kern = gen_kernel_ptr<16, 1>(); break;
-    case 162: kern = gen_kernel_ptr<16, 2>(); break;
-    case 163: kern = gen_kernel_ptr<16, 3>(); break;
-    case 164: kern = gen_kernel_ptr<16, 4>(); break;
+    case 41: kern = stat ? gen_stat_kernel_ptr<4, 1>() : gen_kernel_ptr<4, 1>(); break;
+    case 81: kern = stat ? gen_stat_kernel_ptr<8, 1>() : gen_kernel_ptr<8, 1>(); break;
+    case 82: kern = stat ? gen_stat_kernel_ptr<8, 2>() : gen_kernel_ptr<8, 2>(); break;
+    case 161: kern = stat ? gen_stat_kernel_ptr<16, 1>() : gen_kernel_ptr<16, 1>(); break;
+    case 162: kern = stat ? gen_stat_kernel_ptr<16, 2>() : gen_kernel_ptr<16, 2>(); break;
+    case 163: kern = stat ? gen_stat_kernel_ptr<16, 3>() : gen_kernel_ptr<16, 3>(); break;
+    case 164: kern = stat ? gen_stat_kernel_ptr<16, 4>() : gen_kernel_ptr<16, 4>(); break;
     default: return hipErrorInvalidValue;
+  }
+  if (stat) {
+    if (!a.ws) return hipErrorInvalidValue;
+    const int wk = -ks, HN = a.K / 256;
+    if (wk < 1 || wk > 4) return hipErrorInvalidValue;
+    int R = codebook_gen_stat_r(a.M, a.N, a.K, wk);
+    void* args[] = {const_cast<CodebookGenArgs*>(&a), &R};
+    hipError_t e = hipLaunchKernel(kern, dim3(R, HN, a.M), dim3(64 * wk), args, 0, s);
+    if (e != hipSuccess) return e;
+    const int MN = a.M * a.N;
+    hipLaunchKernelGGL(codebook_reduce_kernel, dim3((MN + 63) / 64), dim3(512), 0, s, a.ws, a.y, MN, HN);
+    return hipGetLastError();
   }
   if (ks < 1 || ks > a.K / 256 || (ks > 1 && !a.ws)) return hipErrorInvalidValue;
   const int NB = (a.N + 63) / 64;

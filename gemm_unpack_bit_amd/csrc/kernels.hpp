@@ -97,6 +97,8 @@ struct CodebookGenArgs {
 };
 int codebook_gen_ks(int M, int N, int K);
 size_t codebook_gen_ws_bytes(int M, int N, int K);
+// ks >= 1: the sequential form with ks K parts; ks = -wk: the stationary
+// form with wk (1..4) waves per workgroup (one K part per 256-k chunk)
 hipError_t launch_gemv_codebook_gen(const CodebookGenArgs& a, int ks, hipStream_t s);
 
 // Unfused baselines (unfused.hip): eager dequantization to fp16 W [N, K]

@@ -88,3 +88,17 @@ def test_codebook_gen_full_size_gate_up(m, v, g):
     rows = sample_rows(N)
     y_ref, A = ref.gemv_codebook_additive(c["x"], c["codes"], c["codebooks"], c["scales"], g, rows=rows)
     assert_within(y[:, rows], y_ref, A, f"codebook gen full m={m} v={v} g={g}")
+
+
+@pytest.mark.parametrize("m,v,g", FORMATS)
+@pytest.mark.parametrize("wk", ["-1", "-2", "-4"])
+def test_codebook_gen_stationary_form(m, v, g, wk, monkeypatch):
+    """The stationary form (one K part per 256-k chunk, rows streamed through
+    each chunk's Psumbooks) at every workgroup size, on ragged rows."""
+    N, K, M = 777, 2048, 2
+    say("codebook gen stationary", m, v, g, wk)
+    c = synth.codebook_additive_case(47 + m + v, M, N, K, m, v, g)
+    monkeypatch.setenv("QGEMV_CODEBOOK_GEN_KS", wk)
+    y = _run(c, g)
+    y_ref, A = ref.gemv_codebook_additive(c["x"], c["codes"], c["codebooks"], c["scales"], g)
+    assert_within(y, y_ref, A, f"codebook gen stationary m={m} v={v} g={g} wk={wk}")
