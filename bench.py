@@ -281,6 +281,8 @@ VARIANTS = {
     # CodeGEMM notes compare: (m, v, g) = (3, 16, 32) and (2, 8, 64)
     "codebook_m3v16g32_m1": dict(kind="codebook_gen", bits=2, m=1, cb=(3, 16, 32)),
     "codebook_m2v8g64_m1": dict(kind="codebook_gen", bits=2, m=1, cb=(2, 8, 64)),
+    # prefill: the GEMM path at M = 512 (compute-bound; TFLOP/s reported)
+    "w4a16_prefill_m512": dict(kind="gemm", bits=4, m=512),
     # unfused baselines: what fusion buys.  fp16 weights (no quantization),
     # eager dequantization + dense GEMV, and the dense W4 kernel + separate SpMV
     "f16_dense_m1": dict(kind="dense", bits=16, m=1),
@@ -352,6 +354,13 @@ def variant_layer(torch, q, dev, kind, bits, m, idx, N, K, cb=None):
         b_sp = 4 * rec.size + 4 * ptr.size + 2 * m * K + 4 * m * N
         parts = {"w4a16": (dense, alg_bytes(N, K, 4, m)), "spmv_tilecoo": (sp, b_sp)}
         nbytes = alg_bytes(N, K, 4, m) + 4 * rec.size + 4 * ptr.size
+    elif kind == "gemm":
+        c = synth.uniform_case(seed, m, N, K, bits)
+        t = dict(x=up(c["x"]), wq=q.pack(up(c["codes"]), bits), s=up(c["scales"]),
+                 z=q.pack_zeros(up(c["zeros"]), bits))
+        call = lambda t: q.gemm_uniform(t["x"], t["wq"], t["s"], t["z"], bits, out=y)
+        oracle = lambda rows: ref.gemv_uniform(c["x"], c["codes"], c["scales"], c["zeros"], rows=rows)
+        nbytes = alg_bytes(N, K, bits, m)
     elif kind == "uniform":
         c = synth.uniform_case(seed, m, N, K, bits)
         t = dict(x=up(c["x"]), wq=q.pack(up(c["codes"]), bits), s=up(c["scales"]),
@@ -409,6 +418,8 @@ def measure_variants(torch, q, dev, timer, n):
             us = timer.region_us(fn, n, host_cost(torch, fn)) / n
             layers[name] = {"us_per_call": round(us, 3), "GBps": round(nbytes / us / 1e3, 1),
                             "pct_peak": round(nbytes / us / 1e3 / PEAK_HBM_GBS * 100, 1), "bytes": nbytes}
+            if v["kind"] == "gemm":  # compute-bound: fp16 matrix-core peak 2.5 PFLOP/s
+                layers[name]["TFLOPs"] = round(2.0 * v["m"] * N * K / us / 1e6, 1)
             for pname, (pcall, pbytes) in (parts or {}).items():  # each kernel of the sequence alone
                 pfn = lambda i, pcall=pcall: pcall(copies[i % R])
                 pus = timer.region_us(pfn, n, host_cost(torch, pfn)) / n

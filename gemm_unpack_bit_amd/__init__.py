@@ -44,6 +44,7 @@ _SIGS = {
     "qgemv_codebook": (_i, [_i, _i, _i, _vp, _vp, _vp, _vp, _vp, _vp, _sz, _vp]),
     "qgemv_codebook_workspace_bytes": (_sz, [_i, _i, _i]),
     "qgemv_tilecoo_encode": (_i, [_i, _i, ctypes.c_int64, _vp, _vp, _vp, _vp, _vp]),
+    "qgemv_gemm_uniform": (_i, [_i, _i, _i, _i, _vp, _vp, _vp, _vp, _vp, _vp]),
     "qgemv_codebook_gen": (_i, [_i, _i, _i, _i, _i, _i, _vp, _vp, _vp, _vp, _vp, _vp, _sz, _vp]),
     "qgemv_codebook_gen_workspace_bytes": (_sz, [_i, _i, _i, _i, _i, _i]),
     "qgemv_dequant": (_i, [_i, _i, _i, _vp, _vp, _vp, _vp, _vp]),
@@ -428,4 +429,26 @@ def codebook_gen(x, codes, codebooks, scales, group, ws=None, out=None):
     _check("qgemv_codebook_gen", lib().qgemv_codebook_gen(M, N, K, ncb, v, group, _ptr(x), _ptr(codes),
                                                           _ptr(codebooks), _ptr(scales), _ptr(out), _ptr(ws),
                                                           wsb, _stream(x)))
+    return out
+
+
+def gemm_uniform(x, wq, scales, zeros, bits, out=None):
+    """Prefill-size y = x . dequant(Wq)^T for any M (matrix cores); arguments
+    as `uniform`, x [M, K] with M unbounded."""
+    torch = _torch()
+    _need(x, torch.float16, "x")
+    _need(wq, torch.int32, "wq")
+    _need(scales, torch.float16, "scales")
+    _need(zeros, torch.int32, "zeros")
+    M, K = x.shape
+    N = scales.shape[0]
+    need = packed_words(bits, N, K)
+    if need and wq.numel() != need:
+        raise ValueError("wq does not hold N x K device-layout codes")
+    if out is None:
+        out = torch.empty((M, N), dtype=torch.float16, device=x.device)
+    else:
+        _need(out, torch.float16, "out")
+    _check("qgemv_gemm_uniform", lib().qgemv_gemm_uniform(bits, M, N, K, _ptr(x), _ptr(wq), _ptr(scales),
+                                                          _ptr(zeros), _ptr(out), _stream(x)))
     return out

@@ -14,6 +14,10 @@ namespace {
 
 thread_local int g_last_hip_error = 0;
 
+// qgemv_gemm_uniform: batches of at most this many rows run as 16-row slices
+// of the decode kernel
+constexpr int QGEMV_GEMM_SLICE_MAX_M = 64;
+
 int hip_status(hipError_t e) {
   if (e == hipSuccess) return QGEMV_OK;
   g_last_hip_error = (int)e;
@@ -169,6 +173,44 @@ int qgemv_uniform(int bits, int path, int M, int N, int K, const uint16_t* x, co
   if (path == QGEMV_PATH_AUTO) path = auto_path(bits, M, N);
   const bool mfma = path == QGEMV_PATH_MFMA;
   return hip_status(qg::launch_gemv_tiles(a, tile_cfg(bits, M, N, K, mfma), s));
+}
+
+int qgemv_gemm_uniform(int bits, int M, int N, int K, const uint16_t* x, const uint32_t* wq, const uint16_t* scales,
+                       const uint32_t* zeros, uint16_t* y, qgemv_stream_t stream) {
+  if (!x || !wq || !scales || !zeros || !y) return QGEMV_ERR_NULL;
+  if (!valid_bits(bits)) return QGEMV_ERR_UNSUPPORTED;
+  if (M < 1 || (M + 63) / 64 > 65535) return QGEMV_ERR_SHAPE;
+  int rc = check_mnk(1, N, K, bits);
+  if (rc) return rc;
+  const long lim = 1L << 31;
+  if ((long)M * K * 2 >= lim || (long)M * N * 2 >= lim) return QGEMV_ERR_SHAPE;
+  if (!aligned16(x) || !aligned16(wq) || ((uintptr_t)scales & 1u) || ((uintptr_t)zeros & 3u) ||
+      ((uintptr_t)y & 1u))
+    return QGEMV_ERR_ALIGN;
+  const size_t ybytes = (size_t)M * N * 2;
+  const int G = K / QGEMV_GROUP;
+  if (overlaps(y, ybytes, x, (size_t)M * K * 2) ||
+      overlaps(y, ybytes, wq, words(bits, QGEMV_LAYOUT_DEVICE, N, K) * 4) ||
+      overlaps(y, ybytes, scales, (size_t)N * G * 2) ||
+      overlaps(y, ybytes, zeros, words(bits, QGEMV_LAYOUT_PLAIN, N, G) * 4))
+    return QGEMV_ERR_VALUE;
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  // Batch-size policy (sweeps of the 8B layers, W4): up to 64 rows, the
+  // decode kernel on each 16-row slice (it streams the weights once per
+  // slice, but its grid fills the chip: 101 vs 287 us per step at M = 32);
+  // from 65 rows on, the GEMM (faster from about M = 128).
+  const char* force = std::getenv("QGEMV_GEMM_KERNEL");  // tuning override: "1" = the GEMM at any M
+  if (M <= QGEMV_GEMM_SLICE_MAX_M && !(force && force[0] == '1')) {
+    for (int m0 = 0; m0 < M; m0 += QGEMV_MAX_M) {
+      const int mm = M - m0 < QGEMV_MAX_M ? M - m0 : QGEMV_MAX_M;
+      qg::UniformArgs a{bits, mm, N, K, x + (size_t)m0 * K, wq, scales, zeros, y + (size_t)m0 * N};
+      rc = hip_status(qg::launch_gemv_tiles(a, tile_cfg(bits, mm, N, K, mm > 1), s));
+      if (rc) return rc;
+    }
+    return QGEMV_OK;
+  }
+  qg::UniformArgs a{bits, M, N, K, x, wq, scales, zeros, y};
+  return hip_status(qg::launch_gemm_tiles(a, s));
 }
 
 int qgemv_w2a16(int M, int N, int K, const uint16_t* x, const uint32_t* wq, const uint16_t* scales,

@@ -1,0 +1,196 @@
+// Prefill-size GEMM over the packed uniform weights: Y = X . dequant(Wq)^T
+// for any M (the decode GEMV kernels take M <= 16), on the matrix cores.
+//
+// The pages' decode kernels turn compute-bound as the batch grows (QFactory
+// review, "Key observations": larger batches shift the kernel from memory-
+// to compute-bound; ADAngel review: batch growth turns kernels
+// compute-bound).  Here the weights stay in their tiled device layout: a
+// lane's 32 consecutive k of one row in one quant group are exactly the B
+// operand of v_mfma_f32_16x16x32_f16 (as in the decode MFMA engine), so a
+// wave dequantizes its B fragments in registers straight from global memory
+// and exactly ((q - z) in fp16).  The activations of a 64-row block are
+// staged in LDS one quant group (128 k) at a time, double-buffered, and
+// shared by the workgroup.
+//
+// Block: 64 activation rows x 64 weight rows (4 tile-rows), 4 waves; wave w
+// computes rows 32 (w & 1) .. + 32 and tile-rows 2 (w >> 1) .. + 2 as 2 x 2
+// MFMA tiles.  Per group each wave runs 16 MFMAs into a group partial and
+// adds it times the lane's row scale (one rounding per group, as the decode
+// kernels).  Deterministic.
+#include "common.hpp"
+#include "dequant.hpp"
+#include "kernels.hpp"
+
+namespace qg {
+namespace {
+
+constexpr int XROW = 136;  // staged activation row: 128 halves + 8 of padding (bank spread)
+
+template <int BITS>
+__global__ void __launch_bounds__(256) gemm_tiles_kernel(UniformArgs a) {
+  using TR = Uni<BITS>;
+  constexpr int PPD = TR::CPD / 2;
+  constexpr int ZPW = 32 / BITS;
+  constexpr uint32_t TB = 16u * 128u * BITS / 8;  // tile bytes
+  __shared__ __attribute__((aligned(16))) _Float16 xs[2][64 * XROW];
+
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int n = lane & 15, kq = lane >> 4;
+  const int M = a.M, N = a.N, K = a.K;
+  const int G = K / 128;
+  const int NT = (N + 15) / 16;
+  const uint32_t zrow = 4u * ((G * BITS + 31) / 32);
+  const int m0 = blockIdx.y * 64;
+  const int rt0 = blockIdx.x * 4 + 2 * (wave >> 1);  // this wave's first tile-row
+  const int mw = 32 * (wave & 1);                    // this wave's first row of the block
+  const uint32_t mg = magic1024x2();
+
+  const rsrc_t rw = make_rsrc(a.wq, (uint32_t)NT * G * TB);
+  const rsrc_t rz = make_rsrc(a.zeros, (uint32_t)N * zrow);
+  const rsrc_t rs = make_rsrc(a.scales, (uint32_t)N * G * 2u);
+  const rsrc_t rx = make_rsrc(a.x, (uint32_t)M * K * 2u);
+
+  // activation staging: thread t moves 16-byte pieces t, t + 256, ... of the
+  // block's 64 x 128 tile of group g (rows past M read zeros)
+  auto x_load = [&](int g, u4 (&v)[4]) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int idx = threadIdx.x + 256 * i, r = idx >> 4, c8 = idx & 15;
+      v[i] = bload16(rx, m0 + r < M ? ((uint32_t)(m0 + r) * K + 128u * g + 8u * c8) * 2u : OOB);
+    }
+  };
+  auto x_store = [&](int b, const u4 (&v)[4]) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int idx = threadIdx.x + 256 * i, r = idx >> 4, c8 = idx & 15;
+      *reinterpret_cast<u4*>(&xs[b][r * XROW + 8 * c8]) = v[i];
+    }
+  };
+  // weights of the wave's 2 tile-rows in group g: codes, scale and zero point
+  struct Wst {
+    uint32_t w[2][BITS];
+    uint16_t s[2];
+    uint32_t z[2];
+  };
+  auto w_load = [&](int g, Wst& st) {
+#pragma unroll
+    for (int t = 0; t < 2; ++t) {
+      const int rt = rt0 + t;
+      const bool tv = rt < NT;
+      const uint32_t tb = ((uint32_t)rt * G + g) * TB;
+      if constexpr (BITS == 2) {
+        const u2 v = __builtin_bit_cast(
+            u2, __builtin_amdgcn_raw_buffer_load_b64(rw, tv ? tb + 8u * lane : OOB, 0, CPOL_NT));
+        st.w[t][0] = v.x;
+        st.w[t][1] = v.y;
+      } else {
+#pragma unroll
+        for (int h = 0; h < BITS / 4; ++h) {
+          const u4 v = bload16<CPOL_NT>(rw, tv ? tb + 1024u * h + 16u * lane : OOB);
+#pragma unroll
+          for (int e = 0; e < 4; ++e) st.w[t][4 * h + e] = v[e];
+        }
+      }
+      const int row = 16 * rt + n;
+      const bool rv = tv && row < N;
+      st.s[t] = bload2(rs, rv ? ((uint32_t)row * G + g) * 2u : OOB);
+      st.z[t] = bload4(rz, rv ? (uint32_t)row * zrow + 4u * (uint32_t)(g / ZPW) : OOB);
+    }
+  };
+
+  f4 acc[2][2];
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int t = 0; t < 2; ++t) acc[i][t] = f4{0.f, 0.f, 0.f, 0.f};
+
+  // Pipeline, distance 2: group g is computed from LDS buffer g % 2 while
+  // group g + 1 waits in registers (stored to the other buffer after the
+  // compute) and group g + 2 is being loaded; the barrier waits for LDS
+  // traffic only, so those loads stay in flight across it.
+  u4 xv[2][4];
+  Wst wst[3];
+  x_load(0, xv[0]);
+  w_load(0, wst[0]);
+  x_load(1, xv[1]);  // (with one group: other data in bounds, never used)
+  w_load(1, wst[1]);
+  x_store(0, xv[0]);
+  __syncthreads();
+
+  auto step = [&](int g, int b, u4 (&xnext)[4], u4 (&xlater)[4], const Wst& cur, Wst& later) {
+    if (g + 2 < G) {  // (workgroup-uniform)
+      x_load(g + 2, xlater);
+      w_load(g + 2, later);
+    }
+    // B fragments: the (q - z) pairs of the lane's 32 k of each tile-row
+    h2 p[2][16];
+#pragma unroll
+    for (int t = 0; t < 2; ++t) {
+      const typename TR::Z zz = TR::zc((cur.z[t] >> (BITS * (g % ZPW))) & ((1u << BITS) - 1u));
+#pragma unroll
+      for (int d = 0; d < BITS; ++d) TR::deq(cur.w[t][d], mg, zz, p[t] + d * PPD);
+    }
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      // A fragments: block row mw + 16 i + n, k 32 kq + 8 s .. + 7 of the group
+      const _Float16* xr = &xs[b][(mw + 16 * i + n) * XROW + 32 * kq];
+      f4 dd[2] = {f4{0.f, 0.f, 0.f, 0.f}, f4{0.f, 0.f, 0.f, 0.f}};
+#pragma unroll
+      for (int s = 0; s < 4; ++s) {
+        const h8 av = __builtin_bit_cast(h8, *reinterpret_cast<const u4*>(xr + 8 * s));
+#pragma unroll
+        for (int t = 0; t < 2; ++t) {
+          const u4 bv = {as_u32(p[t][4 * s]), as_u32(p[t][4 * s + 1]), as_u32(p[t][4 * s + 2]), as_u32(p[t][4 * s + 3])};
+          dd[t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(av, __builtin_bit_cast(h8, bv), dd[t], 0, 0, 0);
+        }
+      }
+#pragma unroll
+      for (int t = 0; t < 2; ++t) {
+        const float sc = h2f(cur.s[t]);  // lane l: weight row l % 16 of tile-row t
+#pragma unroll
+        for (int r = 0; r < 4; ++r) acc[i][t][r] = fmaf(sc, dd[t][r], acc[i][t][r]);
+      }
+    }
+    if (g + 1 < G) x_store(b ^ 1, xnext);
+    lds_barrier();  // group g + 1 staged; every wave is done with buffer b
+  };
+  // six groups per iteration so the register stages are named statically
+  for (int g = 0; g < G; g += 6) {
+    step(g, 0, xv[1], xv[0], wst[0], wst[2]);
+    if (g + 1 < G) step(g + 1, 1, xv[0], xv[1], wst[1], wst[0]);
+    if (g + 2 < G) step(g + 2, 0, xv[1], xv[0], wst[2], wst[1]);
+    if (g + 3 < G) step(g + 3, 1, xv[0], xv[1], wst[0], wst[2]);
+    if (g + 4 < G) step(g + 4, 0, xv[1], xv[0], wst[1], wst[0]);
+    if (g + 5 < G) step(g + 5, 1, xv[0], xv[1], wst[2], wst[1]);
+  }
+
+  // lane l holds D[row 4 (l / 16) + r][weight row l % 16] of each 16 x 16 tile
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int t = 0; t < 2; ++t) {
+      const int col = 16 * (rt0 + t) + n;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int row = m0 + mw + 16 * i + 4 * kq + r;
+        if (row < M && col < N) a.y[(size_t)row * N + col] = f2h(acc[i][t][r]);
+      }
+    }
+}
+
+}  // namespace
+
+hipError_t launch_gemm_tiles(const UniformArgs& a, hipStream_t s) {
+  const int NT = (a.N + 15) / 16;
+  const dim3 grid((NT + 3) / 4, (a.M + 63) / 64), block(256);
+  switch (a.bits) {
+    case 2: hipLaunchKernelGGL(gemm_tiles_kernel<2>, grid, block, 0, s, a); break;
+    case 4: hipLaunchKernelGGL(gemm_tiles_kernel<4>, grid, block, 0, s, a); break;
+    case 8: hipLaunchKernelGGL(gemm_tiles_kernel<8>, grid, block, 0, s, a); break;
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
+}  // namespace qg

@@ -296,6 +296,22 @@ int qgemv_codebook_gen(int M, int N, int K, int ncb, int v, int group, const uin
 size_t qgemv_codebook_gen_workspace_bytes(int M, int N, int K, int ncb, int v, int group);
 
 /* ------------------------------------------------------------------------
+ * Prefill-size GEMM of the uniform format (any M), the compute-bound regime
+ * the decode kernels give way to as the batch grows (QFactory review, "Key
+ * observations"; ADAngel review: batch growth turns kernels compute-bound):
+ *     y = x . (s * (q - z))^T        x [dev] fp16 [M, K], y [dev] fp16 [M, N]
+ * Other arguments as qgemv_uniform (bits 2, 4, 8; the same packed weights).
+ * M >= 1 with M*K*2 and M*N*2 below 2^31, N >= 1, K a positive multiple of
+ * 128 (QGEMV_ERR_SHAPE); alignment and overlap rules as qgemv_uniform.
+ * Up to 64 rows: the decode kernel on each 16-row slice of x; beyond: a
+ * GEMM on the matrix cores, 64 x 64 output blocks, fp32 accumulation with
+ * one scale per group.  Asynchronous, deterministic.
+ * ------------------------------------------------------------------------ */
+int qgemv_gemm_uniform(int bits, int M, int N, int K, const uint16_t *x, const uint32_t *wq,
+                       const uint16_t *scales, const uint32_t *zeros, uint16_t *y,
+                       qgemv_stream_t stream);
+
+/* ------------------------------------------------------------------------
  * Unfused baselines: the kernel sequences that the fused entry points above
  * replace, for measuring what fusion buys.  Same results within the
  * tolerance; more HBM traffic and one more launch.

@@ -182,3 +182,15 @@ def test_codebook_gen_validation_without_gpu(L):
     assert cg(ws=FAKE * 4, wsb=64) == q.ERR_VALUE   # the workspace overlaps the scales
     assert L.qgemv_codebook_gen_workspace_bytes(1, 64, 512, 2, 4, 128) == 0
     assert L.qgemv_codebook_gen_workspace_bytes(1, 4096, 4096, 3, 16, 32) >= 4 * 4096
+
+
+def test_gemm_validation_without_gpu(L):
+    v = ctypes.c_void_p
+    gm = lambda bits=4, M=100, N=64, K=256, x=FAKE, wq=FAKE * 2, s=FAKE * 3, z=FAKE * 4, y=FAKE * 1024: \
+        L.qgemv_gemm_uniform(bits, M, N, K, v(x), v(wq), v(s), v(z), v(y), v(0))
+    assert gm(wq=0) == q.ERR_NULL
+    assert gm(bits=3) == q.ERR_UNSUPPORTED
+    assert gm(M=0) == q.ERR_SHAPE
+    assert gm(K=200) == q.ERR_SHAPE
+    assert gm(x=FAKE + 8) == q.ERR_ALIGN
+    assert gm(y=FAKE * 3) == q.ERR_VALUE             # y overlaps the scales
