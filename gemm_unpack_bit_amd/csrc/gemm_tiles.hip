@@ -26,13 +26,16 @@ namespace {
 
 constexpr int XROW = 136;  // staged activation row: 128 halves + 8 of padding (bank spread)
 
-template <int BITS>
+// MI: 16-row activation tiles per wave; the block has 32 MI rows.
+template <int BITS, int MI>
 __global__ void __launch_bounds__(256) gemm_tiles_kernel(UniformArgs a) {
   using TR = Uni<BITS>;
   constexpr int PPD = TR::CPD / 2;
   constexpr int ZPW = 32 / BITS;
   constexpr uint32_t TB = 16u * 128u * BITS / 8;  // tile bytes
-  __shared__ __attribute__((aligned(16))) _Float16 xs[2][64 * XROW];
+  constexpr int BM = 32 * MI;                     // activation rows per block
+  constexpr int XP = BM * 16 / 256;               // 16-byte staging pieces per thread
+  __shared__ __attribute__((aligned(16))) _Float16 xs[2][BM * XROW];
 
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -41,9 +44,9 @@ __global__ void __launch_bounds__(256) gemm_tiles_kernel(UniformArgs a) {
   const int G = K / 128;
   const int NT = (N + 15) / 16;
   const uint32_t zrow = 4u * ((G * BITS + 31) / 32);
-  const int m0 = blockIdx.y * 64;
+  const int m0 = blockIdx.y * BM;
   const int rt0 = blockIdx.x * 4 + 2 * (wave >> 1);  // this wave's first tile-row
-  const int mw = 32 * (wave & 1);                    // this wave's first row of the block
+  const int mw = 16 * MI * (wave & 1);               // this wave's first row of the block
   const uint32_t mg = magic1024x2();
 
   const rsrc_t rw = make_rsrc(a.wq, (uint32_t)NT * G * TB);
@@ -52,17 +55,17 @@ __global__ void __launch_bounds__(256) gemm_tiles_kernel(UniformArgs a) {
   const rsrc_t rx = make_rsrc(a.x, (uint32_t)M * K * 2u);
 
   // activation staging: thread t moves 16-byte pieces t, t + 256, ... of the
-  // block's 64 x 128 tile of group g (rows past M read zeros)
-  auto x_load = [&](int g, u4 (&v)[4]) {
+  // block's BM x 128 tile of group g (rows past M read zeros)
+  auto x_load = [&](int g, u4 (&v)[XP]) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
+    for (int i = 0; i < XP; ++i) {
       const int idx = threadIdx.x + 256 * i, r = idx >> 4, c8 = idx & 15;
       v[i] = bload16(rx, m0 + r < M ? ((uint32_t)(m0 + r) * K + 128u * g + 8u * c8) * 2u : OOB);
     }
   };
-  auto x_store = [&](int b, const u4 (&v)[4]) {
+  auto x_store = [&](int b, const u4 (&v)[XP]) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
+    for (int i = 0; i < XP; ++i) {
       const int idx = threadIdx.x + 256 * i, r = idx >> 4, c8 = idx & 15;
       *reinterpret_cast<u4*>(&xs[b][r * XROW + 8 * c8]) = v[i];
     }
@@ -99,9 +102,9 @@ __global__ void __launch_bounds__(256) gemm_tiles_kernel(UniformArgs a) {
     }
   };
 
-  f4 acc[2][2];
+  f4 acc[MI][2];
 #pragma unroll
-  for (int i = 0; i < 2; ++i)
+  for (int i = 0; i < MI; ++i)
 #pragma unroll
     for (int t = 0; t < 2; ++t) acc[i][t] = f4{0.f, 0.f, 0.f, 0.f};
 
@@ -109,7 +112,7 @@ __global__ void __launch_bounds__(256) gemm_tiles_kernel(UniformArgs a) {
   // group g + 1 waits in registers (stored to the other buffer after the
   // compute) and group g + 2 is being loaded; the barrier waits for LDS
   // traffic only, so those loads stay in flight across it.
-  u4 xv[2][4];
+  u4 xv[2][XP];
   Wst wst[3];
   x_load(0, xv[0]);
   w_load(0, wst[0]);
@@ -118,7 +121,7 @@ __global__ void __launch_bounds__(256) gemm_tiles_kernel(UniformArgs a) {
   x_store(0, xv[0]);
   __syncthreads();
 
-  auto step = [&](int g, int b, u4 (&xnext)[4], u4 (&xlater)[4], const Wst& cur, Wst& later) {
+  auto step = [&](int g, int b, u4 (&xnext)[XP], u4 (&xlater)[XP], const Wst& cur, Wst& later) {
     if (g + 2 < G) {  // (workgroup-uniform)
       x_load(g + 2, xlater);
       w_load(g + 2, later);
@@ -132,7 +135,7 @@ __global__ void __launch_bounds__(256) gemm_tiles_kernel(UniformArgs a) {
       for (int d = 0; d < BITS; ++d) TR::deq(cur.w[t][d], mg, zz, p[t] + d * PPD);
     }
 #pragma unroll
-    for (int i = 0; i < 2; ++i) {
+    for (int i = 0; i < MI; ++i) {
       // A fragments: block row mw + 16 i + n, k 32 kq + 8 s .. + 7 of the group
       const _Float16* xr = &xs[b][(mw + 16 * i + n) * XROW + 32 * kq];
       f4 dd[2] = {f4{0.f, 0.f, 0.f, 0.f}, f4{0.f, 0.f, 0.f, 0.f}};
@@ -167,7 +170,7 @@ __global__ void __launch_bounds__(256) gemm_tiles_kernel(UniformArgs a) {
 
   // lane l holds D[row 4 (l / 16) + r][weight row l % 16] of each 16 x 16 tile
 #pragma unroll
-  for (int i = 0; i < 2; ++i)
+  for (int i = 0; i < MI; ++i)
 #pragma unroll
     for (int t = 0; t < 2; ++t) {
       const int col = 16 * (rt0 + t) + n;
@@ -181,16 +184,23 @@ __global__ void __launch_bounds__(256) gemm_tiles_kernel(UniformArgs a) {
 
 }  // namespace
 
-hipError_t launch_gemm_tiles(const UniformArgs& a, hipStream_t s) {
+template <int MI>
+hipError_t launch_mi(const UniformArgs& a, hipStream_t s) {
   const int NT = (a.N + 15) / 16;
-  const dim3 grid((NT + 3) / 4, (a.M + 63) / 64), block(256);
+  const dim3 grid((NT + 3) / 4, (a.M + 32 * MI - 1) / (32 * MI)), block(256);
   switch (a.bits) {
-    case 2: hipLaunchKernelGGL(gemm_tiles_kernel<2>, grid, block, 0, s, a); break;
-    case 4: hipLaunchKernelGGL(gemm_tiles_kernel<4>, grid, block, 0, s, a); break;
-    case 8: hipLaunchKernelGGL(gemm_tiles_kernel<8>, grid, block, 0, s, a); break;
+    case 2: hipLaunchKernelGGL((gemm_tiles_kernel<2, MI>), grid, block, 0, s, a); break;
+    case 4: hipLaunchKernelGGL((gemm_tiles_kernel<4, MI>), grid, block, 0, s, a); break;
+    case 8: hipLaunchKernelGGL((gemm_tiles_kernel<8, MI>), grid, block, 0, s, a); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();
+}
+
+hipError_t launch_gemm_tiles(const UniformArgs& a, int mi, hipStream_t s) {
+  if (mi == 2) return launch_mi<2>(a, s);
+  if (mi == 4) return launch_mi<4>(a, s);
+  return hipErrorInvalidValue;
 }
 
 }  // namespace qg

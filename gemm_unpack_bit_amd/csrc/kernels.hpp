@@ -101,9 +101,9 @@ size_t codebook_gen_ws_bytes(int M, int N, int K);
 // form with wk (1..4) waves per workgroup (one K part per 256-k chunk)
 hipError_t launch_gemv_codebook_gen(const CodebookGenArgs& a, int ks, hipStream_t s);
 
-// Prefill-size GEMM (gemm_tiles.hip): the uniform format at any M, 64 x 64
-// blocks on the matrix cores
-hipError_t launch_gemm_tiles(const UniformArgs& a, hipStream_t s);
+// Prefill-size GEMM (gemm_tiles.hip): the uniform format at any M on the
+// matrix cores, blocks of 32 mi activation rows (mi = 2, 4) x 64 weight rows
+hipError_t launch_gemm_tiles(const UniformArgs& a, int mi, hipStream_t s);
 
 // Unfused baselines (unfused.hip): eager dequantization to fp16 W [N, K]
 // row-major (uniform b-bit: bits, wq, scales, zeros; LUT4: wq, absmax, lut),

@@ -17,13 +17,15 @@ def _case(seed, M, N, K, bits):
     return c, q.pack(dev(c["codes"]), bits), dev(c["scales"]), q.pack_zeros(dev(c["zeros"]), bits)
 
 
+@pytest.mark.parametrize("mi", ["2", "4"])  # activation tiles per wave (64- or 128-row blocks)
 @pytest.mark.parametrize("force", ["0", "1"])  # "1": the GEMM kernel also for M <= 64
 @pytest.mark.parametrize("bits", [2, 4, 8])
 @pytest.mark.parametrize("M,N,K", [(1, 16, 128), (17, 70, 384), (64, 300, 2048), (100, 1000, 640), (300, 48, 128),
                                    (130, 257, 1152)])
-def test_gemm_small_shapes(bits, M, N, K, force, monkeypatch):
-    say("gemm", bits, M, N, K, force)
+def test_gemm_small_shapes(bits, M, N, K, force, mi, monkeypatch):
+    say("gemm", bits, M, N, K, force, mi)
     monkeypatch.setenv("QGEMV_GEMM_KERNEL", force)
+    monkeypatch.setenv("QGEMV_GEMM_MI", mi)
     c, wq, s, zq = _case(M * 7 + N + K + bits, M, N, K, bits)
     y = host(q.gemm_uniform(dev(c["x"]), wq, s, zq, bits))
     y_ref, A = ref.gemv_uniform(c["x"], c["codes"], c["scales"], c["zeros"])
