@@ -117,6 +117,32 @@ def dequant_lut4(codes, absmax, lut, block=64):
     return L[np.asarray(codes, dtype=np.int64)] * np.repeat(_f64(absmax), block, axis=1)
 
 
+def quantize_activations_int8(x):
+    """Symmetric per-row int8 activations (ADAngel review: arbitrary-precision
+    quantization such as W4A8, activations at 8 bits; the pages fix no
+    scheme, the plainest reading is one symmetric scale per row):
+    s[m] = max_k |x[m, k]| / 127 and q[m, k] = rint(x[m, k] / s[m]) clamped to
+    [-127, 127], both in float32 (the precision that decides the integers);
+    a zero row gets s = 0 and q = 0."""
+    x32 = np.asarray(x).astype(np.float32)
+    amax = np.abs(x32).max(axis=1)
+    s = (amax / np.float32(127.0)).astype(np.float32)
+    safe = np.where(s > 0, s, np.float32(1.0)).astype(np.float32)
+    q = np.rint((x32 / safe[:, None]).astype(np.float32)).clip(-127, 127).astype(np.int8)
+    return q, s
+
+
+def gemv_w4a8(x, codes, scales, zeros, g=128, rows=None):
+    """Padding strategy for W4A8 (ADAngel review, DPR: padding extends the
+    low-bit weight to the activation width, here int4 codes to int8 (q - z)):
+    y[m, n] = s_x[m] * sum_k s_w[n, k // g] * (q[n, k] - z[n, k // g]) * x_q[m, k].
+    Tolerance scale: s_x[m] * sum_k |s_w (q - z) x_q|."""
+    xq, sx = quantize_activations_int8(x)
+    y, A = gemv_uniform(xq, codes, scales, zeros, g, rows=rows)
+    sx64 = sx.astype(np.float64)[:, None]
+    return y * sx64, A * sx64
+
+
 def gemv_lut4(x, codes, absmax, lut, block=64, rows=None):
     x64 = _f64(x)
 

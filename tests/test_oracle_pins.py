@@ -432,3 +432,40 @@ def test_planted_codebook_mistakes_are_caught(monkeypatch, mutant):
     monkeypatch.setattr(ref, "dequant_codebook_additive", mutant)
     with pytest.raises(AssertionError):
         test_codebook_additive_one_hot_worked_example()
+
+
+# ----------------------------------------------------------------------------
+# W4A8 (int8 activations, padding strategy)
+# ----------------------------------------------------------------------------
+def test_int8_activation_quantization_worked_example():
+    """By hand: x = (1, -2, 0.5, fp16(2/127)): s = 2 / 127 (fp32); x / s =
+    (63.5 exactly in fp32, -127, 31.75, 0.99994) -> rint, half to even =
+    (64, -127, 32, 1); a zero row gives s = 0, q = 0."""
+    x = np.zeros((2, 128), np.float16)
+    x[0, :4] = [1.0, -2.0, 0.5, np.float16(2.0 / 127.0)]
+    q, s = ref.quantize_activations_int8(x)
+    assert s[0] == np.float32(2.0) / np.float32(127.0) and s[1] == 0
+    assert q[0, :4].tolist() == [64, -127, 32, 1] and not q[0, 4:].any() and not q[1].any()
+
+
+def test_w4a8_reduces_to_uniform_on_integer_activations():
+    """Activations that are integers with max |x| = 127 quantize to themselves
+    (s = 1), so W4A8 is the uniform GEMV on them."""
+    c = synth.uniform_case(29, 3, 40, 256, 4)
+    x = (np.arange(3 * 256).reshape(3, 256) % 255 - 127).astype(np.float16)
+    y8, A8 = ref.gemv_w4a8(x, c["codes"], c["scales"], c["zeros"])
+    yu, Au = ref.gemv_uniform(x, c["codes"], c["scales"], c["zeros"])
+    assert np.array_equal(y8, yu) and np.array_equal(A8, Au)
+
+
+def test_w4a8_within_quantization_error_of_w4a16():
+    """|y_w4a8 - y_w4a16| <= (s_x / 2) * sum_k |w| (each activation moves by
+    at most half a step), and the bound is not vacuous."""
+    c = synth.uniform_case(30, 4, 64, 512, 4)
+    y8, _ = ref.gemv_w4a8(c["x"], c["codes"], c["scales"], c["zeros"])
+    y16, _ = ref.gemv_uniform(c["x"], c["codes"], c["scales"], c["zeros"])
+    _, sx = ref.quantize_activations_int8(c["x"])
+    wabs = np.abs(ref.dequant_uniform(c["codes"], c["scales"], c["zeros"])).sum(axis=1)
+    bound = sx.astype(np.float64)[:, None] / 2 * wabs[None, :]
+    assert (np.abs(y8 - y16) <= bound + 1e-12).all()
+    assert np.abs(y8 - y16).max() > 0
