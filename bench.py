@@ -281,6 +281,9 @@ VARIANTS = {
     # CodeGEMM notes compare: (m, v, g) = (3, 16, 32) and (2, 8, 64)
     "codebook_m3v16g32_m1": dict(kind="codebook_gen", bits=2, m=1, cb=(3, 16, 32)),
     "codebook_m2v8g64_m1": dict(kind="codebook_gen", bits=2, m=1, cb=(2, 8, 64)),
+    # W4A8 (int8 activations, padding strategy, int8 matrix cores)
+    "w4a8_m1": dict(kind="w4a8", bits=4, m=1),
+    "w4a8_m16": dict(kind="w4a8", bits=4, m=16),
     # prefill: the GEMM path at M = 512 (compute-bound; TFLOP/s reported)
     "w4a16_prefill_m512": dict(kind="gemm", bits=4, m=512),
     # unfused baselines: what fusion buys.  fp16 weights (no quantization),
@@ -354,6 +357,14 @@ def variant_layer(torch, q, dev, kind, bits, m, idx, N, K, cb=None):
         b_sp = 4 * rec.size + 4 * ptr.size + 2 * m * K + 4 * m * N
         parts = {"w4a16": (dense, alg_bytes(N, K, 4, m)), "spmv_tilecoo": (sp, b_sp)}
         nbytes = alg_bytes(N, K, 4, m) + 4 * rec.size + 4 * ptr.size
+    elif kind == "w4a8":
+        c = synth.uniform_case(seed, m, N, K, bits)
+        ws = torch.zeros(q.w4a8_workspace_bytes(m, K), dtype=torch.uint8, device=dev)
+        t = dict(x=up(c["x"]), wq=q.pack(up(c["codes"]), bits), s=up(c["scales"]),
+                 z=q.pack_zeros(up(c["zeros"]), bits))
+        call = lambda t: q.w4a8(t["x"], t["wq"], t["s"], t["z"], ws, out=y)
+        oracle = lambda rows: ref.gemv_w4a8(c["x"], c["codes"], c["scales"], c["zeros"], rows=rows)
+        nbytes = alg_bytes(N, K, bits, m)
     elif kind == "gemm":
         c = synth.uniform_case(seed, m, N, K, bits)
         t = dict(x=up(c["x"]), wq=q.pack(up(c["codes"]), bits), s=up(c["scales"]),

@@ -44,6 +44,8 @@ _SIGS = {
     "qgemv_codebook": (_i, [_i, _i, _i, _vp, _vp, _vp, _vp, _vp, _vp, _sz, _vp]),
     "qgemv_codebook_workspace_bytes": (_sz, [_i, _i, _i]),
     "qgemv_tilecoo_encode": (_i, [_i, _i, ctypes.c_int64, _vp, _vp, _vp, _vp, _vp]),
+    "qgemv_w4a8": (_i, [_i, _i, _i, _vp, _vp, _vp, _vp, _vp, _vp, _sz, _vp]),
+    "qgemv_w4a8_workspace_bytes": (_sz, [_i, _i]),
     "qgemv_gemm_uniform": (_i, [_i, _i, _i, _i, _vp, _vp, _vp, _vp, _vp, _vp]),
     "qgemv_codebook_gen": (_i, [_i, _i, _i, _i, _i, _i, _vp, _vp, _vp, _vp, _vp, _vp, _sz, _vp]),
     "qgemv_codebook_gen_workspace_bytes": (_sz, [_i, _i, _i, _i, _i, _i]),
@@ -451,4 +453,34 @@ def gemm_uniform(x, wq, scales, zeros, bits, out=None):
         _need(out, torch.float16, "out")
     _check("qgemv_gemm_uniform", lib().qgemv_gemm_uniform(bits, M, N, K, _ptr(x), _ptr(wq), _ptr(scales),
                                                           _ptr(zeros), _ptr(out), _stream(x)))
+    return out
+
+
+def w4a8_workspace_bytes(M, K):
+    return int(lib().qgemv_w4a8_workspace_bytes(M, K))
+
+
+def w4a8(x, wq, scales, zeros, ws, out=None):
+    """W4A8 with int8 activations (one symmetric scale per row) on the int8
+    matrix cores.  Arguments as w4a16; ws: a CUDA tensor of at least
+    w4a8_workspace_bytes(M, K) bytes (16-byte aligned), which holds the int8
+    activations [M, K] and then the fp32 row scales after the call."""
+    torch = _torch()
+    _need(x, torch.float16, "x")
+    _need(wq, torch.int32, "wq")
+    _need(scales, torch.float16, "scales")
+    _need(zeros, torch.int32, "zeros")
+    if not isinstance(ws, torch.Tensor) or not ws.is_cuda or not ws.is_contiguous():
+        raise TypeError("ws must be a contiguous CUDA tensor")
+    M, K = x.shape
+    N = scales.shape[0]
+    need = packed_words(4, N, K)
+    if need and wq.numel() != need:
+        raise ValueError("wq does not hold N x K device-layout 4-bit codes")
+    if out is None:
+        out = torch.empty((M, N), dtype=torch.float16, device=x.device)
+    else:
+        _need(out, torch.float16, "out")
+    _check("qgemv_w4a8", lib().qgemv_w4a8(M, N, K, _ptr(x), _ptr(wq), _ptr(scales), _ptr(zeros), _ptr(out),
+                                          _ptr(ws), ws.numel() * ws.element_size(), _stream(x)))
     return out

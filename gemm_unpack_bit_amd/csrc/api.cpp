@@ -175,6 +175,35 @@ int qgemv_uniform(int bits, int path, int M, int N, int K, const uint16_t* x, co
   return hip_status(qg::launch_gemv_tiles(a, tile_cfg(bits, M, N, K, mfma), s));
 }
 
+size_t qgemv_w4a8_workspace_bytes(int M, int K) {
+  if (M < 1 || M > QGEMV_MAX_M || K < QGEMV_GROUP || K % QGEMV_GROUP) return 0;
+  return qg::w4a8_ws_bytes(M, K);
+}
+
+int qgemv_w4a8(int M, int N, int K, const uint16_t* x, const uint32_t* wq, const uint16_t* scales,
+               const uint32_t* zeros, uint16_t* y, void* ws, size_t ws_bytes, qgemv_stream_t stream) {
+  if (!x || !wq || !scales || !zeros || !y) return QGEMV_ERR_NULL;
+  int rc = check_mnk(M, N, K, 4);
+  if (rc) return rc;
+  if (!ws || ws_bytes < qg::w4a8_ws_bytes(M, K)) return QGEMV_ERR_WORKSPACE;
+  if (((uintptr_t)x & 1u) || !aligned16(wq) || ((uintptr_t)scales & 1u) || ((uintptr_t)zeros & 3u) ||
+      ((uintptr_t)y & 1u) || !aligned16(ws))
+    return QGEMV_ERR_ALIGN;
+  const size_t ybytes = (size_t)M * N * 2, G = K / QGEMV_GROUP;
+  const size_t in_b[4] = {(size_t)M * K * 2, words(4, QGEMV_LAYOUT_DEVICE, N, K) * 4, G * N * 2,
+                          words(4, QGEMV_LAYOUT_PLAIN, N, (int)G) * 4};
+  const void* in_p[4] = {x, wq, scales, zeros};
+  for (int i = 0; i < 4; ++i)
+    if (overlaps(y, ybytes, in_p[i], in_b[i]) || overlaps(ws, ws_bytes, in_p[i], in_b[i])) return QGEMV_ERR_VALUE;
+  if (overlaps(ws, ws_bytes, y, ybytes)) return QGEMV_ERR_VALUE;
+  int8_t* xq = reinterpret_cast<int8_t*>(ws);
+  float* sx = reinterpret_cast<float*>(reinterpret_cast<char*>(ws) + ((size_t)M * K + 15) / 16 * 16);
+  qg::W4A8Args a{M, N, K, x, wq, scales, zeros, y, xq, sx};
+  int wk = qg::w4a8_waves(N, K);
+  if (const char* e = std::getenv("QGEMV_W4A8_WK")) wk = std::atoi(e);  // tuning override
+  return hip_status(qg::launch_gemv_w4a8(a, wk, reinterpret_cast<hipStream_t>(stream)));
+}
+
 int qgemv_gemm_uniform(int bits, int M, int N, int K, const uint16_t* x, const uint32_t* wq, const uint16_t* scales,
                        const uint32_t* zeros, uint16_t* y, qgemv_stream_t stream) {
   if (!x || !wq || !scales || !zeros || !y) return QGEMV_ERR_NULL;

@@ -1,0 +1,135 @@
+// W4A8 GEMV with the padding strategy (ADAngel review, DPR: padding extends
+// the low-bit weight to the activation width), on the int8 matrix cores:
+//
+//   x_q[m, k] = rint(x[m, k] / s_x[m]) clamped to [-127, 127],
+//   s_x[m] = max_k |x[m, k]| / 127                        (fp32)
+//   y[m, n]   = s_x[m] * sum_g s_w[n, g] * sum_{k in g} (q[n, k] - z[n, g]) x_q[m, k]
+//
+// Two kernels on the caller's stream:
+//  * quant_rows_kernel: one workgroup per activation row writes x_q (int8)
+//    and s_x (fp32) to the caller's workspace; fp32 correctly rounded
+//    division and round-to-nearest-even, so x_q is the exact integer the
+//    definition gives.
+//  * gemv_w4a8_kernel: a workgroup owns one 16-row tile-row of the 4-bit
+//    tiled device layout; its waves take quant groups round-robin.  A lane's
+//    4 code words hold its row's 32 k of the group; two byte permutes put a
+//    word's 8 codes in k order, one or/subtract/xor turns them into the
+//    signed bytes q - z (no borrow between bytes), and 16 of them are the B
+//    operand of v_mfma_i32_16x16x64_i8 (A: the same 16 k of 16 activation
+//    rows).  The int32 group sums are exact; each is scaled by the lane's
+//    row scale, the waves are added in a fixed order through LDS, and the
+//    row's activation scale is applied last.  Deterministic.
+#include "common.hpp"
+#include "kernels.hpp"
+
+namespace qg {
+namespace {
+
+typedef int v4i __attribute__((ext_vector_type(4)));
+
+__global__ void __launch_bounds__(256) quant_rows_kernel(W4A8Args a) {
+  __shared__ float wmax[4];
+  const int m = blockIdx.x, K = a.K;
+  const uint16_t* xr = a.x + (size_t)m * K;
+  float amax = 0.f;
+  for (int k = threadIdx.x; k < K; k += blockDim.x) amax = fmaxf(amax, fabsf(h2f(xr[k])));
+  // max over the workgroup (exact, any order)
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) amax = fmaxf(amax, __shfl_xor(amax, off, 64));
+  if ((threadIdx.x & 63) == 0) wmax[threadIdx.x >> 6] = amax;
+  __syncthreads();
+  amax = fmaxf(fmaxf(wmax[0], wmax[1]), fmaxf(wmax[2], wmax[3]));
+  const float s = amax / 127.0f;  // correctly rounded fp32 division
+  int8_t* qr = a.xq + (size_t)m * K;
+  for (int k = threadIdx.x; k < K; k += blockDim.x) {
+    const float v = s > 0.f ? rintf(h2f(xr[k]) / s) : 0.f;
+    qr[k] = (int8_t)fminf(fmaxf(v, -127.f), 127.f);
+  }
+  if (threadIdx.x == 0) a.sx[m] = s;
+}
+
+// the 8 codes of a device-layout word in k order, minus the zero point, as
+// signed bytes: fields 0..7 sit at k offsets 0, 2, 4, 6, 1, 3, 5, 7
+__device__ __forceinline__ uint2 codes_minus_z(uint32_t w, uint32_t z4) {
+  const uint32_t lo = w & 0x0F0F0F0Fu;         // bytes: k 0, 4, 1, 5
+  const uint32_t hi = (w >> 4) & 0x0F0F0F0Fu;  // bytes: k 2, 6, 3, 7
+  const uint32_t k03 = __builtin_amdgcn_perm(hi, lo, 0x06040200u);  // k 0, 1, 2, 3
+  const uint32_t k47 = __builtin_amdgcn_perm(hi, lo, 0x07050301u);  // k 4, 5, 6, 7
+  // per byte: (q + 128 - z) stays in [113, 143] (no borrow), then ^ 0x80 = q - z
+  return uint2{((k03 | 0x80808080u) - z4) ^ 0x80808080u, ((k47 | 0x80808080u) - z4) ^ 0x80808080u};
+}
+
+__global__ void __launch_bounds__(1024) gemv_w4a8_kernel(W4A8Args a) {
+  extern __shared__ __attribute__((aligned(16))) float red[];  // [WK][64] float4
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int WK = blockDim.x >> 6;
+  const int n = lane & 15, kq = lane >> 4;
+  const int M = a.M, N = a.N, K = a.K;
+  const int G = K / 128;
+  const int NT = (N + 15) / 16;
+  const int rt = blockIdx.x;
+  const int row = 16 * rt + n;
+  const uint32_t zrow = 4u * ((G * 4 + 31) / 32);
+  const rsrc_t rw = make_rsrc(a.wq, (uint32_t)NT * G * 1024u);
+  const rsrc_t rs = make_rsrc(a.scales, (uint32_t)N * G * 2u);
+  const rsrc_t rz = make_rsrc(a.zeros, (uint32_t)N * zrow);
+  const rsrc_t rx = make_rsrc(a.xq, (uint32_t)M * K);
+  // A: activation row n (rows past M read zeros), the lane's 32 k of a group
+  const uint32_t xo = n < M ? (uint32_t)n * K + 32u * kq : OOB;
+  const bool rv = row < N;
+
+  f4 acc = f4{0.f, 0.f, 0.f, 0.f};
+  for (int g = wave; g < G; g += WK) {  // (wave-uniform)
+    const u4 w = bload16<CPOL_NT>(rw, ((uint32_t)rt * G + g) * 1024u + 16u * lane);
+    const uint16_t sb = bload2(rs, rv ? ((uint32_t)row * G + g) * 2u : OOB);
+    const uint32_t zw = bload4(rz, rv ? (uint32_t)row * zrow + 4u * (uint32_t)(g / 8) : OOB);
+    const u4 x0 = bload16(rx, xo, 128u * g), x1 = bload16(rx, xo, 128u * g + 16u);
+    const uint32_t z4 = ((zw >> (4 * (g % 8))) & 15u) * 0x01010101u;
+    const uint2 b0 = codes_minus_z(w[0], z4), b1 = codes_minus_z(w[1], z4);
+    const uint2 b2 = codes_minus_z(w[2], z4), b3 = codes_minus_z(w[3], z4);
+    // step s: k 32 kq + 16 s .. + 15 on both sides
+    v4i d = {0, 0, 0, 0};
+    d = __builtin_amdgcn_mfma_i32_16x16x64_i8(__builtin_bit_cast(v4i, x0),
+                                              v4i{(int)b0.x, (int)b0.y, (int)b1.x, (int)b1.y}, d, 0, 0, 0);
+    d = __builtin_amdgcn_mfma_i32_16x16x64_i8(__builtin_bit_cast(v4i, x1),
+                                              v4i{(int)b2.x, (int)b2.y, (int)b3.x, (int)b3.y}, d, 0, 0, 0);
+    const float sc = h2f(sb);  // lane l: weight row l % 16
+#pragma unroll
+    for (int i = 0; i < 4; ++i) acc[i] = fmaf(sc, (float)d[i], acc[i]);
+  }
+  // lane l holds D[activation row 4 (l / 16) + i][weight row l % 16]
+  reinterpret_cast<f4*>(red)[wave * 64 + lane] = acc;
+  __syncthreads();
+  for (int e = threadIdx.x; e < 256; e += blockDim.x) {
+    const int i = e & 3, l = e >> 2;
+    const int m = 4 * (l >> 4) + i, col = 16 * rt + (l & 15);
+    if (m >= M || col >= N) continue;
+    float sum = 0.f;
+    for (int w = 0; w < WK; ++w) sum += red[(w * 64 + l) * 4 + i];
+    a.y[(size_t)m * N + col] = f2h(a.sx[m] * sum);
+  }
+}
+
+}  // namespace
+
+size_t w4a8_ws_bytes(int M, int K) { return ((size_t)M * K + 15) / 16 * 16 + (size_t)M * 4; }
+
+// waves per workgroup: as the decode VALU engine's one-group chunks (16 for
+// long K, 4 on wide layers, else 8), at most one per group
+int w4a8_waves(int N, int K) {
+  const int G = K / 128, nt = (N + 15) / 16;
+  int wk = G >= 96 ? 16 : (nt >= 1024 ? 4 : 8);
+  return wk > G ? G : wk;
+}
+
+hipError_t launch_gemv_w4a8(const W4A8Args& a, int wk, hipStream_t s) {
+  if (wk < 1 || wk > 16) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(quant_rows_kernel, dim3(a.M), dim3(256), 0, s, a);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(gemv_w4a8_kernel, dim3((a.N + 15) / 16), dim3(64 * wk), (size_t)wk * 64 * 16, s, a);
+  return hipGetLastError();
+}
+
+}  // namespace qg

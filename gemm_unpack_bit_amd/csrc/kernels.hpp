@@ -101,6 +101,22 @@ size_t codebook_gen_ws_bytes(int M, int N, int K);
 // form with wk (1..4) waves per workgroup (one K part per 256-k chunk)
 hipError_t launch_gemv_codebook_gen(const CodebookGenArgs& a, int ks, hipStream_t s);
 
+// W4A8 with the padding strategy (gemv_w4a8.hip): int8 activations per row
+// in the workspace (xq [M, K], then sx [M] fp32 at a 16-byte boundary)
+struct W4A8Args {
+  int M, N, K;
+  const uint16_t* x;
+  const uint32_t* wq;
+  const uint16_t* scales;
+  const uint32_t* zeros;
+  uint16_t* y;
+  int8_t* xq;
+  float* sx;
+};
+size_t w4a8_ws_bytes(int M, int K);
+int w4a8_waves(int N, int K);
+hipError_t launch_gemv_w4a8(const W4A8Args& a, int wk, hipStream_t s);
+
 // Prefill-size GEMM (gemm_tiles.hip): the uniform format at any M on the
 // matrix cores, blocks of 32 mi activation rows (mi = 2, 4) x 64 weight rows
 hipError_t launch_gemm_tiles(const UniformArgs& a, int mi, hipStream_t s);

@@ -296,6 +296,26 @@ int qgemv_codebook_gen(int M, int N, int K, int ncb, int v, int group, const uin
 size_t qgemv_codebook_gen_workspace_bytes(int M, int N, int K, int ncb, int v, int group);
 
 /* ------------------------------------------------------------------------
+ * W4A8 GEMV with the padding strategy (ADAngel review: arbitrary-precision
+ * quantization such as W4A8; DPR's padding extends the low-bit weights to
+ * the activation width), on the int8 matrix cores:
+ *     s_x[m]  = max_k |x[m, k]| / 127,  x_q = rint(x / s_x) clamped to +-127
+ *               (fp32, round half to even; a zero row gives 0)
+ *     y[m, n] = s_x[m] * sum_k s[n, k/128] * (q[n, k] - z[n, k/128]) * x_q[m, k]
+ * x, wq, scales, zeros, y as qgemv_w4a16 (4-bit uniform format).
+ *   ws [dev] scratch of qgemv_w4a8_workspace_bytes(M, K) bytes, 16-byte
+ *      aligned: the int8 activations [M, K], then the fp32 scales [M] at the
+ *      next 16-byte boundary (left there after the call).  Required
+ *      (QGEMV_ERR_WORKSPACE if NULL or smaller).
+ * Shapes and the other rules as qgemv_w4a16; ws may not overlap an input or
+ * y (QGEMV_ERR_VALUE).  Two kernels on `stream`; deterministic.
+ * ------------------------------------------------------------------------ */
+int qgemv_w4a8(int M, int N, int K, const uint16_t *x, const uint32_t *wq, const uint16_t *scales,
+               const uint32_t *zeros, uint16_t *y, void *ws, size_t ws_bytes, qgemv_stream_t stream);
+/* Workspace bytes of qgemv_w4a8 (0 on bad arguments). */
+size_t qgemv_w4a8_workspace_bytes(int M, int K);
+
+/* ------------------------------------------------------------------------
  * Prefill-size GEMM of the uniform format (any M), the compute-bound regime
  * the decode kernels give way to as the batch grows (QFactory review, "Key
  * observations"; ADAngel review: batch growth turns kernels compute-bound):

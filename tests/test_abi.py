@@ -194,3 +194,16 @@ def test_gemm_validation_without_gpu(L):
     assert gm(K=200) == q.ERR_SHAPE
     assert gm(x=FAKE + 8) == q.ERR_ALIGN
     assert gm(y=FAKE * 3) == q.ERR_VALUE             # y overlaps the scales
+
+
+def test_w4a8_validation_without_gpu(L):
+    v = ctypes.c_void_p
+    wa = lambda M=1, N=64, K=256, x=FAKE, wq=FAKE * 2, s=FAKE * 3, z=FAKE * 4, y=FAKE * 64, ws=FAKE * 128, wsb=1 << 16: \
+        L.qgemv_w4a8(M, N, K, v(x), v(wq), v(s), v(z), v(y), v(ws), wsb, v(0))
+    assert wa(x=0) == q.ERR_NULL
+    assert wa(M=17) == q.ERR_SHAPE
+    assert wa(ws=0) == q.ERR_WORKSPACE
+    assert wa(wsb=16) == q.ERR_WORKSPACE
+    assert wa(ws=FAKE * 128 + 4) == q.ERR_ALIGN
+    assert wa(ws=FAKE * 2) == q.ERR_VALUE            # the workspace overlaps the codes
+    assert L.qgemv_w4a8_workspace_bytes(3, 256) == 3 * 256 + 3 * 4   # int8 rows, then the fp32 scales
