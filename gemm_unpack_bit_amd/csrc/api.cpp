@@ -186,7 +186,7 @@ int qgemv_w4a8(int M, int N, int K, const uint16_t* x, const uint32_t* wq, const
   int rc = check_mnk(M, N, K, 4);
   if (rc) return rc;
   if (!ws || ws_bytes < qg::w4a8_ws_bytes(M, K)) return QGEMV_ERR_WORKSPACE;
-  if (((uintptr_t)x & 1u) || !aligned16(wq) || ((uintptr_t)scales & 1u) || ((uintptr_t)zeros & 3u) ||
+  if (!aligned16(x) || !aligned16(wq) || ((uintptr_t)scales & 1u) || ((uintptr_t)zeros & 3u) ||
       ((uintptr_t)y & 1u) || !aligned16(ws))
     return QGEMV_ERR_ALIGN;
   const size_t ybytes = (size_t)M * N * 2, G = K / QGEMV_GROUP;

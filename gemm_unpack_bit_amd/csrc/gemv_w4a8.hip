@@ -6,12 +6,15 @@
 //   y[m, n]   = s_x[m] * sum_g s_w[n, g] * sum_{k in g} (q[n, k] - z[n, g]) x_q[m, k]
 //
 // Two kernels on the caller's stream:
-//  * quant_rows_kernel: one workgroup per activation row writes x_q (int8)
-//    and s_x (fp32) to the caller's workspace; fp32 correctly rounded
-//    division and round-to-nearest-even, so x_q is the exact integer the
-//    definition gives.
+//  * quant_rows_kernel: writes x_q (int8) and s_x (fp32) to the caller's
+//    workspace; fp32 correctly rounded division and round-to-nearest-even,
+//    so x_q is the exact integer the definition gives.  Each workgroup takes
+//    2048 k of one row: it reads the whole row for the max (exact in any
+//    order, so every workgroup of the row finds the same s_x) and quantizes
+//    its own part, which it already holds in registers.
 //  * gemv_w4a8_kernel: a workgroup owns one 16-row tile-row of the 4-bit
-//    tiled device layout; its waves take quant groups round-robin.  A lane's
+//    tiled device layout; its waves take runs of WU quant groups
+//    round-robin, issuing all of a run's loads before its MFMAs.  A lane's
 //    4 code words hold its row's 32 k of the group; two byte permutes put a
 //    word's 8 codes in k order, one or/subtract/xor turns them into the
 //    signed bytes q - z (no borrow between bytes), and 16 of them are the B
@@ -27,25 +30,64 @@ namespace {
 
 typedef int v4i __attribute__((ext_vector_type(4)));
 
-__global__ void __launch_bounds__(256) quant_rows_kernel(W4A8Args a) {
-  __shared__ float wmax[4];
-  const int m = blockIdx.x, K = a.K;
-  const uint16_t* xr = a.x + (size_t)m * K;
+constexpr int QT = 256;  // threads of the quantization kernel; one 8-k piece each
+constexpr int QU = 4;    // pieces per thread in flight in the max pass
+
+__device__ __forceinline__ float h8_absmax(u4 v) {
+  float r = 0.f;
+#pragma unroll
+  for (int e = 0; e < 4; ++e) r = fmaxf(r, fmaxf(fabsf(h2f((uint16_t)v[e])), fabsf(h2f((uint16_t)(v[e] >> 16)))));
+  return r;
+}
+// int8 code of one activation (s > 0): rint(x / s) clamped, as a byte
+__device__ __forceinline__ uint32_t q8(uint16_t xh, float s) {
+  const float v = fminf(fmaxf(rintf(h2f(xh) / s), -127.f), 127.f);  // correctly rounded fp32 division
+  return (uint32_t)(int)v & 0xFFu;
+}
+
+// grid: (K / 2048 rounded up, M)
+__global__ void __launch_bounds__(QT) quant_rows_kernel(W4A8Args a) {
+  __shared__ float wmax[QT / 64];
+  const int m = blockIdx.y, K = a.K, tid = threadIdx.x;
+  const int np = K / 8;                       // 16-byte pieces of the row
+  const int mine = blockIdx.x * QT + tid;     // the piece this thread quantizes
+  const rsrc_t rx = make_rsrc(a.x + (size_t)m * K, (uint32_t)K * 2u);
+  u4 own = u4{0u, 0u, 0u, 0u};
   float amax = 0.f;
-  for (int k = threadIdx.x; k < K; k += blockDim.x) amax = fmaxf(amax, fabsf(h2f(xr[k])));
+  for (int base = tid; base < np; base += QT * QU) {
+    u4 v[QU];
+#pragma unroll
+    for (int j = 0; j < QU; ++j) {
+      const int p = base + QT * j;
+      v[j] = bload16(rx, p < np ? 16u * p : OOB);  // (past the row: zeros)
+    }
+#pragma unroll
+    for (int j = 0; j < QU; ++j) {
+      amax = fmaxf(amax, h8_absmax(v[j]));
+      if (base + QT * j == mine) own = v[j];
+    }
+  }
   // max over the workgroup (exact, any order)
 #pragma unroll
   for (int off = 32; off > 0; off >>= 1) amax = fmaxf(amax, __shfl_xor(amax, off, 64));
-  if ((threadIdx.x & 63) == 0) wmax[threadIdx.x >> 6] = amax;
+  if ((tid & 63) == 0) wmax[tid >> 6] = amax;
   __syncthreads();
-  amax = fmaxf(fmaxf(wmax[0], wmax[1]), fmaxf(wmax[2], wmax[3]));
+  amax = 0.f;
+#pragma unroll
+  for (int w = 0; w < QT / 64; ++w) amax = fmaxf(amax, wmax[w]);
   const float s = amax / 127.0f;  // correctly rounded fp32 division
-  int8_t* qr = a.xq + (size_t)m * K;
-  for (int k = threadIdx.x; k < K; k += blockDim.x) {
-    const float v = s > 0.f ? rintf(h2f(xr[k]) / s) : 0.f;
-    qr[k] = (int8_t)fminf(fmaxf(v, -127.f), 127.f);
+  if (mine < np) {
+    uint32_t lo = 0u, hi = 0u;
+    if (s > 0.f) {  // a zero row quantizes to zeros
+#pragma unroll
+      for (int e = 0; e < 2; ++e) {
+        lo |= (q8((uint16_t)own[e], s) | q8((uint16_t)(own[e] >> 16), s) << 8) << (16 * e);
+        hi |= (q8((uint16_t)own[2 + e], s) | q8((uint16_t)(own[2 + e] >> 16), s) << 8) << (16 * e);
+      }
+    }
+    *reinterpret_cast<uint2*>(a.xq + (size_t)m * K + 8 * (size_t)mine) = uint2{lo, hi};
   }
-  if (threadIdx.x == 0) a.sx[m] = s;
+  if (blockIdx.x == 0 && tid == 0) a.sx[m] = s;
 }
 
 // the 8 codes of a device-layout word in k order, minus the zero point, as
@@ -58,6 +100,8 @@ __device__ __forceinline__ uint2 codes_minus_z(uint32_t w, uint32_t z4) {
   // per byte: (q + 128 - z) stays in [113, 143] (no borrow), then ^ 0x80 = q - z
   return uint2{((k03 | 0x80808080u) - z4) ^ 0x80808080u, ((k47 | 0x80808080u) - z4) ^ 0x80808080u};
 }
+
+constexpr int WU = 4;  // quant groups per wave whose loads are in flight together
 
 __global__ void __launch_bounds__(1024) gemv_w4a8_kernel(W4A8Args a) {
   extern __shared__ __attribute__((aligned(16))) float red[];  // [WK][64] float4
@@ -79,24 +123,57 @@ __global__ void __launch_bounds__(1024) gemv_w4a8_kernel(W4A8Args a) {
   const uint32_t xo = n < M ? (uint32_t)n * K + 32u * kq : OOB;
   const bool rv = row < N;
 
+  // G a multiple of WU: a run's WU scales are one aligned 8-byte load and its
+  // zero points one word (runs start at multiples of WU = 4, inside one
+  // 8-group zero word); otherwise one load per group.
+  const bool packed = G % WU == 0;
   f4 acc = f4{0.f, 0.f, 0.f, 0.f};
-  for (int g = wave; g < G; g += WK) {  // (wave-uniform)
-    const u4 w = bload16<CPOL_NT>(rw, ((uint32_t)rt * G + g) * 1024u + 16u * lane);
-    const uint16_t sb = bload2(rs, rv ? ((uint32_t)row * G + g) * 2u : OOB);
-    const uint32_t zw = bload4(rz, rv ? (uint32_t)row * zrow + 4u * (uint32_t)(g / 8) : OOB);
-    const u4 x0 = bload16(rx, xo, 128u * g), x1 = bload16(rx, xo, 128u * g + 16u);
-    const uint32_t z4 = ((zw >> (4 * (g % 8))) & 15u) * 0x01010101u;
-    const uint2 b0 = codes_minus_z(w[0], z4), b1 = codes_minus_z(w[1], z4);
-    const uint2 b2 = codes_minus_z(w[2], z4), b3 = codes_minus_z(w[3], z4);
-    // step s: k 32 kq + 16 s .. + 15 on both sides
-    v4i d = {0, 0, 0, 0};
-    d = __builtin_amdgcn_mfma_i32_16x16x64_i8(__builtin_bit_cast(v4i, x0),
-                                              v4i{(int)b0.x, (int)b0.y, (int)b1.x, (int)b1.y}, d, 0, 0, 0);
-    d = __builtin_amdgcn_mfma_i32_16x16x64_i8(__builtin_bit_cast(v4i, x1),
-                                              v4i{(int)b2.x, (int)b2.y, (int)b3.x, (int)b3.y}, d, 0, 0, 0);
-    const float sc = h2f(sb);  // lane l: weight row l % 16
+  for (int g0 = WU * wave; g0 < G; g0 += WU * WK) {  // (wave-uniform)
+    // all loads of the run first; groups past G read zeros (scale 0: no effect)
+    u4 w[WU], x0[WU], x1[WU];
+    uint16_t sb[WU];
+    uint32_t zw[WU];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) acc[i] = fmaf(sc, (float)d[i], acc[i]);
+    for (int u = 0; u < WU; ++u) {
+      const int g = g0 + u;
+      const bool gv = g < G;
+      w[u] = bload16<CPOL_NT>(rw, gv ? ((uint32_t)rt * G + g) * 1024u + 16u * lane : OOB);
+      x0[u] = bload16(rx, gv ? xo : OOB, 128u * g);
+      x1[u] = bload16(rx, gv ? xo : OOB, 128u * g + 16u);
+    }
+    if (packed) {
+      const u2 sv = __builtin_bit_cast(
+          u2, __builtin_amdgcn_raw_buffer_load_b64(rs, rv ? ((uint32_t)row * G + g0) * 2u : OOB, 0, 0));
+      const uint32_t z = bload4(rz, rv ? (uint32_t)row * zrow + 4u * (uint32_t)(g0 / 8) : OOB);
+#pragma unroll
+      for (int u = 0; u < WU; ++u) {
+        sb[u] = (uint16_t)((u < 2 ? sv.x : sv.y) >> (16 * (u & 1)));
+        zw[u] = z;
+      }
+    } else {
+#pragma unroll
+      for (int u = 0; u < WU; ++u) {
+        const int g = g0 + u;
+        const bool gv = g < G;
+        sb[u] = bload2(rs, rv && gv ? ((uint32_t)row * G + g) * 2u : OOB);
+        zw[u] = bload4(rz, rv && gv ? (uint32_t)row * zrow + 4u * (uint32_t)(g / 8) : OOB);
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < WU; ++u) {
+      const uint32_t z4 = ((zw[u] >> (4 * ((g0 + u) % 8))) & 15u) * 0x01010101u;
+      const uint2 b0 = codes_minus_z(w[u][0], z4), b1 = codes_minus_z(w[u][1], z4);
+      const uint2 b2 = codes_minus_z(w[u][2], z4), b3 = codes_minus_z(w[u][3], z4);
+      // step s: k 32 kq + 16 s .. + 15 on both sides
+      v4i d = {0, 0, 0, 0};
+      d = __builtin_amdgcn_mfma_i32_16x16x64_i8(__builtin_bit_cast(v4i, x0[u]),
+                                                v4i{(int)b0.x, (int)b0.y, (int)b1.x, (int)b1.y}, d, 0, 0, 0);
+      d = __builtin_amdgcn_mfma_i32_16x16x64_i8(__builtin_bit_cast(v4i, x1[u]),
+                                                v4i{(int)b2.x, (int)b2.y, (int)b3.x, (int)b3.y}, d, 0, 0, 0);
+      const float sc = h2f(sb[u]);  // lane l: weight row l % 16
+#pragma unroll
+      for (int i = 0; i < 4; ++i) acc[i] = fmaf(sc, (float)d[i], acc[i]);
+    }
   }
   // lane l holds D[activation row 4 (l / 16) + i][weight row l % 16]
   reinterpret_cast<f4*>(red)[wave * 64 + lane] = acc;
@@ -116,16 +193,16 @@ __global__ void __launch_bounds__(1024) gemv_w4a8_kernel(W4A8Args a) {
 size_t w4a8_ws_bytes(int M, int K) { return ((size_t)M * K + 15) / 16 * 16 + (size_t)M * 4; }
 
 // waves per workgroup: as the decode VALU engine's one-group chunks (16 for
-// long K, 4 on wide layers, else 8), at most one per group
+// long K, 4 on wide layers, else 8), at most one per run of WU groups
 int w4a8_waves(int N, int K) {
   const int G = K / 128, nt = (N + 15) / 16;
-  int wk = G >= 96 ? 16 : (nt >= 1024 ? 4 : 8);
-  return wk > G ? G : wk;
+  const int wk = G >= 96 ? 16 : (nt >= 1024 ? 4 : 8), runs = (G + WU - 1) / WU;
+  return wk > runs ? runs : wk;
 }
 
 hipError_t launch_gemv_w4a8(const W4A8Args& a, int wk, hipStream_t s) {
   if (wk < 1 || wk > 16) return hipErrorInvalidValue;
-  hipLaunchKernelGGL(quant_rows_kernel, dim3(a.M), dim3(256), 0, s, a);
+  hipLaunchKernelGGL(quant_rows_kernel, dim3((a.K / 8 + QT - 1) / QT, a.M), dim3(QT), 0, s, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(gemv_w4a8_kernel, dim3((a.N + 15) / 16), dim3(64 * wk), (size_t)wk * 64 * 16, s, a);

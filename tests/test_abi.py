@@ -205,5 +205,6 @@ def test_w4a8_validation_without_gpu(L):
     assert wa(ws=0) == q.ERR_WORKSPACE
     assert wa(wsb=16) == q.ERR_WORKSPACE
     assert wa(ws=FAKE * 128 + 4) == q.ERR_ALIGN
+    assert wa(x=FAKE + 8) == q.ERR_ALIGN
     assert wa(ws=FAKE * 2) == q.ERR_VALUE            # the workspace overlaps the codes
     assert L.qgemv_w4a8_workspace_bytes(3, 256) == 3 * 256 + 3 * 4   # int8 rows, then the fp32 scales

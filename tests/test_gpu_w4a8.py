@@ -26,7 +26,9 @@ def _run(x, c, wk=None, monkeypatch=None):
     return y, xq, sx
 
 
-@pytest.mark.parametrize("M,N,K", [(1, 16, 128), (3, 70, 384), (16, 300, 2048), (5, 1000, 640), (2, 48, 14336)])
+# the quantization takes 2048 k per workgroup: K = 32768 is 16 whole parts, 33024 ends in a short one
+@pytest.mark.parametrize("M,N,K", [(1, 16, 128), (3, 70, 384), (16, 300, 2048), (5, 1000, 640), (2, 48, 14336),
+                                   (1, 24, 32768), (3, 40, 33024)])
 def test_w4a8_matches_oracle_and_quantizes_exactly(M, N, K):
     say("w4a8", M, N, K)
     c = synth.uniform_case(N + K + M, M, N, K, 4)
