@@ -7,6 +7,7 @@
 #include <cstdint>
 #include <cstdio>
 #include <cstdlib>
+#include <cstring>
 
 #include "kernels.hpp"
 
@@ -284,6 +285,20 @@ int qgemv_outlier(int path, int M, int N, int K, const uint16_t* x, const uint32
   qg::UniformArgs a{4, M, N, K, x, wq, scales, zeros, y, tile_ptr, tile_rec, (int)nnz};
   if (path == QGEMV_PATH_AUTO) path = auto_path(4, M, N);
   const bool mfma = path == QGEMV_PATH_MFMA;
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  // Wide layers (N >= 16384) at M >= 4: the fused kernel is held to two
+  // tile-rows per workgroup there, and the dense kernel followed by the
+  // separate sparse kernel is faster (28672 x 4096: 26.1 vs 37.4 us at M = 4,
+  // 69.8 vs 83.3 at M = 16).  QGEMV_OUTLIER_FORM=fused|split forces a form.
+  bool split = M >= 4 && N >= 16384 && K <= QGEMV_SPMV_MAX_K && (long)M * K * 2 + 512 < 1L << 31;
+  if (const char* e = std::getenv("QGEMV_OUTLIER_FORM")) split = std::strcmp(e, "split") == 0;
+  if (split && !std::getenv("QGEMV_OUTLIER_CFG")) {
+    const qg::UniformArgs d{4, M, N, K, x, wq, scales, zeros, y, nullptr, nullptr, 0};
+    const hipError_t e = qg::launch_gemv_tiles(d, tile_cfg(4, M, N, K, mfma), s);
+    if (e != hipSuccess || nnz == 0) return hip_status(e);
+    const qg::SpmvArgs sa{M, N, K, x, tile_ptr, tile_rec, (int)nnz, y};
+    return hip_status(qg::launch_spmv_tilecoo(sa, s));
+  }
   qg::TileCfg c = qg::pick_outlier(M, N, K, mfma);
   if (const char* e = std::getenv("QGEMV_OUTLIER_CFG")) {  // tuning override "tpw,wk[,mt[,v]]"
     int tpw, wk, mt, v;
@@ -296,7 +311,7 @@ int qgemv_outlier(int path, int M, int N, int K, const uint16_t* x, const uint32
     if (n >= 3 && !mfma) c.mt = mt;
     if (n >= 4) c.v = v;
   }
-  return hip_status(qg::launch_gemv_outlier(a, c, reinterpret_cast<hipStream_t>(stream)));
+  return hip_status(qg::launch_gemv_outlier(a, c, s));
 }
 
 size_t qgemv_codebook_workspace_bytes(int M, int N, int K) {

@@ -214,7 +214,9 @@ int qgemv_lut4(int M, int N, int K, const uint16_t *x, const uint32_t *wq,
  * dense engine); tile_ptr and tile_rec 4-byte aligned.  Records are read as
  * given (their validity is the encoder's job; malformed ones give wrong
  * values, never an out-of-bounds access).  Asynchronous, deterministic, no
- * allocation.
+ * allocation.  On wide layers (N >= 16384) at M >= 4 the call runs the dense
+ * kernel and then the sparse kernel of qgemv_spmv_tilecoo, the faster form
+ * there; y is then rounded to fp16 twice (after each kernel).
  * ------------------------------------------------------------------------ */
 int qgemv_outlier(int path, int M, int N, int K, const uint16_t *x, const uint32_t *wq,
                   const uint16_t *scales, const uint32_t *zeros, const uint32_t *tile_ptr,

@@ -149,10 +149,26 @@ def test_outlier_every_launch_shape(monkeypatch, path, M, N, K):
     assert len(ran) >= 8, ran
 
 
+@pytest.mark.parametrize("form", ["fused", "split"])
+@pytest.mark.parametrize("path", [q.PATH_VALU, q.PATH_MFMA])
+@pytest.mark.parametrize("M", [1, 5, 16])
+def test_outlier_both_forms(monkeypatch, form, path, M):
+    """The fused kernel and the dense-then-sparse sequence the call takes on
+    wide layers, each forced through QGEMV_OUTLIER_FORM, on a ragged shape."""
+    N, K = 1000, 2176
+    say("outlier form", form, path, M)
+    c = synth.outlier_case(71 + M, M, N, K, frac=0.01)
+    wq, s, zq, tp, tr = _upload(c, N, K)
+    monkeypatch.setenv("QGEMV_OUTLIER_FORM", form)
+    y = host(q.outlier(dev(c["x"]), wq, s, zq, tp, tr, path))
+    y_ref, A = ref.gemv_outlier(c["x"], c["codes"], c["scales"], c["zeros"], c["o_rows"], c["o_cols"], c["o_vals"])
+    assert_within(y, y_ref, A, f"outlier form={form} M={M} path={path}")
+
+
 # -- the decoder-layer shapes at every batch size (sampled rows): long K with
 # staged batch rows must still fit the launch's LDS
 @pytest.mark.parametrize("N,K,M", [(4096, 14336, 2), (4096, 14336, 4), (4096, 14336, 16), (6144, 4096, 2),
-                                   (28672, 4096, 4), (8192, 28672, 2)])
+                                   (28672, 4096, 4), (28672, 4096, 16), (8192, 28672, 2)])
 def test_outlier_layer_shapes_batched(N, K, M):
     say("outlier layer", N, K, M)
     c = synth.outlier_case(61 + M, M, N, K)
