@@ -56,16 +56,19 @@ def test_w4a8_ties_round_to_even():
 
 
 @pytest.mark.parametrize("wk", [1, 3, 8, 16])
-def test_w4a8_every_wave_count(wk, monkeypatch):
-    M, N, K = 4, 200, 2048
-    say("w4a8 wk", wk)
-    c = synth.uniform_case(7 + wk, M, N, K, 4)
-    y, _, _ = _run(c["x"], c, wk, monkeypatch)
+@pytest.mark.parametrize("M", [1, 4])
+def test_w4a8_every_wave_count(wk, M, monkeypatch):
+    """Every wave count, including runs past the group count and idle waves."""
+    N, K = 200, 2048
+    say("w4a8 wk", wk, M)
+    c = synth.uniform_case(7 + wk + M, M, N, K, 4)
+    y, xq, _ = _run(c["x"], c, wk, monkeypatch)
+    assert np.array_equal(xq, ref.quantize_activations_int8(c["x"])[0])
     y_ref, A = ref.gemv_w4a8(c["x"], c["codes"], c["scales"], c["zeros"])
-    assert_within(y, y_ref, A, f"w4a8 wk={wk}")
+    assert_within(y, y_ref, A, f"w4a8 wk={wk} M={M}")
 
 
-@pytest.mark.parametrize("M,N,K", [(1, 28672, 4096), (4, 4096, 14336)])
+@pytest.mark.parametrize("M,N,K", [(1, 28672, 4096), (1, 4096, 14336), (4, 4096, 14336)])
 def test_w4a8_full_size_sampled(M, N, K):
     say("w4a8 full", M, N, K)
     c = synth.uniform_case(8 + M, M, N, K, 4)
