@@ -22,6 +22,8 @@
 //    rows).  The int32 group sums are exact; each is scaled by the lane's
 //    row scale, the waves are added in a fixed order through LDS, and the
 //    row's activation scale is applied last.  Deterministic.
+#include <cstdlib>
+
 #include "common.hpp"
 #include "kernels.hpp"
 
@@ -103,8 +105,12 @@ __device__ __forceinline__ uint2 codes_minus_z(uint32_t w, uint32_t z4) {
 
 constexpr int WU = 4;  // quant groups per wave whose loads are in flight together
 
+// TR tile-rows per workgroup (1, 2): with 2, each A fragment loaded from L2
+// serves both tile-rows, halving the activation reads (they reach twice the
+// weight bytes at M = 16).
+template <int TR>
 __global__ void __launch_bounds__(1024) gemv_w4a8_kernel(W4A8Args a) {
-  extern __shared__ __attribute__((aligned(16))) float red[];  // [WK][64] float4
+  extern __shared__ __attribute__((aligned(16))) float red[];  // [WK][TR][64] float4
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int WK = blockDim.x >> 6;
@@ -112,8 +118,7 @@ __global__ void __launch_bounds__(1024) gemv_w4a8_kernel(W4A8Args a) {
   const int M = a.M, N = a.N, K = a.K;
   const int G = K / 128;
   const int NT = (N + 15) / 16;
-  const int rt = blockIdx.x;
-  const int row = 16 * rt + n;
+  const int rt0 = blockIdx.x * TR;
   const uint32_t zrow = 4u * ((G * 4 + 31) / 32);
   const rsrc_t rw = make_rsrc(a.wq, (uint32_t)NT * G * 1024u);
   const rsrc_t rs = make_rsrc(a.scales, (uint32_t)N * G * 2u);
@@ -121,69 +126,85 @@ __global__ void __launch_bounds__(1024) gemv_w4a8_kernel(W4A8Args a) {
   const rsrc_t rx = make_rsrc(a.xq, (uint32_t)M * K);
   // A: activation row n (rows past M read zeros), the lane's 32 k of a group
   const uint32_t xo = n < M ? (uint32_t)n * K + 32u * kq : OOB;
-  const bool rv = row < N;
-
   // G a multiple of WU: a run's WU scales are one aligned 8-byte load and its
   // zero points one word (runs start at multiples of WU = 4, inside one
   // 8-group zero word); otherwise one load per group.
   const bool packed = G % WU == 0;
-  f4 acc = f4{0.f, 0.f, 0.f, 0.f};
+
+  f4 acc[TR];
+#pragma unroll
+  for (int t = 0; t < TR; ++t) acc[t] = f4{0.f, 0.f, 0.f, 0.f};
   for (int g0 = WU * wave; g0 < G; g0 += WU * WK) {  // (wave-uniform)
-    // all loads of the run first; groups past G read zeros (scale 0: no effect)
-    u4 w[WU], x0[WU], x1[WU];
-    uint16_t sb[WU];
-    uint32_t zw[WU];
+    // all loads of the run first; groups past G and tile-rows past NT read
+    // zeros (scale 0: no effect)
+    u4 w[TR][WU], x0[WU], x1[WU];
+    uint16_t sb[TR][WU];
+    uint32_t zw[TR][WU];
 #pragma unroll
-    for (int u = 0; u < WU; ++u) {
-      const int g = g0 + u;
-      const bool gv = g < G;
-      w[u] = bload16<CPOL_NT>(rw, gv ? ((uint32_t)rt * G + g) * 1024u + 16u * lane : OOB);
-      x0[u] = bload16(rx, gv ? xo : OOB, 128u * g);
-      x1[u] = bload16(rx, gv ? xo : OOB, 128u * g + 16u);
-    }
-    if (packed) {
-      const u2 sv = __builtin_bit_cast(
-          u2, __builtin_amdgcn_raw_buffer_load_b64(rs, rv ? ((uint32_t)row * G + g0) * 2u : OOB, 0, 0));
-      const uint32_t z = bload4(rz, rv ? (uint32_t)row * zrow + 4u * (uint32_t)(g0 / 8) : OOB);
-#pragma unroll
-      for (int u = 0; u < WU; ++u) {
-        sb[u] = (uint16_t)((u < 2 ? sv.x : sv.y) >> (16 * (u & 1)));
-        zw[u] = z;
-      }
-    } else {
+    for (int t = 0; t < TR; ++t)
 #pragma unroll
       for (int u = 0; u < WU; ++u) {
         const int g = g0 + u;
-        const bool gv = g < G;
-        sb[u] = bload2(rs, rv && gv ? ((uint32_t)row * G + g) * 2u : OOB);
-        zw[u] = bload4(rz, rv && gv ? (uint32_t)row * zrow + 4u * (uint32_t)(g / 8) : OOB);
+        w[t][u] = bload16<CPOL_NT>(rw, g < G && rt0 + t < NT ? ((uint32_t)(rt0 + t) * G + g) * 1024u + 16u * lane
+                                                             : OOB);
+      }
+#pragma unroll
+    for (int u = 0; u < WU; ++u) {
+      const int g = g0 + u;
+      x0[u] = bload16(rx, g < G ? xo : OOB, 128u * g);
+      x1[u] = bload16(rx, g < G ? xo : OOB, 128u * g + 16u);
+    }
+#pragma unroll
+    for (int t = 0; t < TR; ++t) {
+      const int row = 16 * (rt0 + t) + n;
+      const bool rv = row < N;
+      if (packed) {
+        const u2 sv = __builtin_bit_cast(
+            u2, __builtin_amdgcn_raw_buffer_load_b64(rs, rv ? ((uint32_t)row * G + g0) * 2u : OOB, 0, 0));
+        const uint32_t z = bload4(rz, rv ? (uint32_t)row * zrow + 4u * (uint32_t)(g0 / 8) : OOB);
+#pragma unroll
+        for (int u = 0; u < WU; ++u) {
+          sb[t][u] = (uint16_t)((u < 2 ? sv.x : sv.y) >> (16 * (u & 1)));
+          zw[t][u] = z;
+        }
+      } else {
+#pragma unroll
+        for (int u = 0; u < WU; ++u) {
+          const int g = g0 + u;
+          const bool gv = rv && g < G;
+          sb[t][u] = bload2(rs, gv ? ((uint32_t)row * G + g) * 2u : OOB);
+          zw[t][u] = bload4(rz, gv ? (uint32_t)row * zrow + 4u * (uint32_t)(g / 8) : OOB);
+        }
       }
     }
 #pragma unroll
-    for (int u = 0; u < WU; ++u) {
-      const uint32_t z4 = ((zw[u] >> (4 * ((g0 + u) % 8))) & 15u) * 0x01010101u;
-      const uint2 b0 = codes_minus_z(w[u][0], z4), b1 = codes_minus_z(w[u][1], z4);
-      const uint2 b2 = codes_minus_z(w[u][2], z4), b3 = codes_minus_z(w[u][3], z4);
-      // step s: k 32 kq + 16 s .. + 15 on both sides
-      v4i d = {0, 0, 0, 0};
-      d = __builtin_amdgcn_mfma_i32_16x16x64_i8(__builtin_bit_cast(v4i, x0[u]),
-                                                v4i{(int)b0.x, (int)b0.y, (int)b1.x, (int)b1.y}, d, 0, 0, 0);
-      d = __builtin_amdgcn_mfma_i32_16x16x64_i8(__builtin_bit_cast(v4i, x1[u]),
-                                                v4i{(int)b2.x, (int)b2.y, (int)b3.x, (int)b3.y}, d, 0, 0, 0);
-      const float sc = h2f(sb[u]);  // lane l: weight row l % 16
+    for (int u = 0; u < WU; ++u)
 #pragma unroll
-      for (int i = 0; i < 4; ++i) acc[i] = fmaf(sc, (float)d[i], acc[i]);
-    }
+      for (int t = 0; t < TR; ++t) {
+        const uint32_t z4 = ((zw[t][u] >> (4 * ((g0 + u) % 8))) & 15u) * 0x01010101u;
+        const uint2 b0 = codes_minus_z(w[t][u][0], z4), b1 = codes_minus_z(w[t][u][1], z4);
+        const uint2 b2 = codes_minus_z(w[t][u][2], z4), b3 = codes_minus_z(w[t][u][3], z4);
+        // step s: k 32 kq + 16 s .. + 15 on both sides
+        v4i d = {0, 0, 0, 0};
+        d = __builtin_amdgcn_mfma_i32_16x16x64_i8(__builtin_bit_cast(v4i, x0[u]),
+                                                  v4i{(int)b0.x, (int)b0.y, (int)b1.x, (int)b1.y}, d, 0, 0, 0);
+        d = __builtin_amdgcn_mfma_i32_16x16x64_i8(__builtin_bit_cast(v4i, x1[u]),
+                                                  v4i{(int)b2.x, (int)b2.y, (int)b3.x, (int)b3.y}, d, 0, 0, 0);
+        const float sc = h2f(sb[t][u]);  // lane l: weight row l % 16 of tile-row t
+#pragma unroll
+        for (int i = 0; i < 4; ++i) acc[t][i] = fmaf(sc, (float)d[i], acc[t][i]);
+      }
   }
   // lane l holds D[activation row 4 (l / 16) + i][weight row l % 16]
-  reinterpret_cast<f4*>(red)[wave * 64 + lane] = acc;
+#pragma unroll
+  for (int t = 0; t < TR; ++t) reinterpret_cast<f4*>(red)[(wave * TR + t) * 64 + lane] = acc[t];
   __syncthreads();
-  for (int e = threadIdx.x; e < 256; e += blockDim.x) {
-    const int i = e & 3, l = e >> 2;
-    const int m = 4 * (l >> 4) + i, col = 16 * rt + (l & 15);
+  for (int e = threadIdx.x; e < 256 * TR; e += blockDim.x) {
+    const int i = e & 3, l = (e >> 2) & 63, t = e >> 8;
+    const int m = 4 * (l >> 4) + i, col = 16 * (rt0 + t) + (l & 15);
     if (m >= M || col >= N) continue;
     float sum = 0.f;
-    for (int w = 0; w < WK; ++w) sum += red[(w * 64 + l) * 4 + i];
+    for (int w = 0; w < WK; ++w) sum += red[((w * TR + t) * 64 + l) * 4 + i];
     a.y[(size_t)m * N + col] = f2h(a.sx[m] * sum);
   }
 }
@@ -200,12 +221,25 @@ int w4a8_waves(int N, int K) {
   return wk > runs ? runs : wk;
 }
 
+// tile-rows per workgroup: 2 from 9 activation rows on where the grid stays
+// wide (384 tile-rows or more), else 1 (8B layers at M = 16: gate+up 25.0 ->
+// 23.0 us, qkv 11.0 -> 10.5; at M = 8 and on narrower layers 2 is slower)
+int w4a8_tile_rows(int M, int N) { return M > 8 && (N + 15) / 16 >= 384 ? 2 : 1; }
+
 hipError_t launch_gemv_w4a8(const W4A8Args& a, int wk, hipStream_t s) {
   if (wk < 1 || wk > 16) return hipErrorInvalidValue;
+  int tr = w4a8_tile_rows(a.M, a.N);
+  if (const char* e = std::getenv("QGEMV_W4A8_TR")) tr = std::atoi(e);  // tuning override (1, 2)
+  if (tr != 1 && tr != 2) return hipErrorInvalidValue;
   hipLaunchKernelGGL(quant_rows_kernel, dim3((a.K / 8 + QT - 1) / QT, a.M), dim3(QT), 0, s, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(gemv_w4a8_kernel, dim3((a.N + 15) / 16), dim3(64 * wk), (size_t)wk * 64 * 16, s, a);
+  const int NT = (a.N + 15) / 16;
+  const size_t lds = (size_t)wk * tr * 64 * 16;
+  if (tr == 2)
+    hipLaunchKernelGGL(gemv_w4a8_kernel<2>, dim3((NT + 1) / 2), dim3(64 * wk), lds, s, a);
+  else
+    hipLaunchKernelGGL(gemv_w4a8_kernel<1>, dim3(NT), dim3(64 * wk), lds, s, a);
   return hipGetLastError();
 }
 

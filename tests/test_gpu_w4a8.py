@@ -84,3 +84,17 @@ def test_w4a8_deterministic():
     y1, _, _ = _run(c["x"], c)
     y2, _, _ = _run(c["x"], c)
     assert np.array_equal(y1.view(np.uint16), y2.view(np.uint16))
+
+
+@pytest.mark.parametrize("tr", [1, 2])
+@pytest.mark.parametrize("M,N,K", [(1, 1000, 640), (16, 300, 2048), (6, 8200, 1024), (16, 8208, 384)])
+def test_w4a8_tile_rows_per_workgroup(tr, M, N, K, monkeypatch):
+    """One or two tile-rows per workgroup (two share each activation load),
+    forced through QGEMV_W4A8_TR, on odd tile-row counts and ragged rows."""
+    say("w4a8 tr", tr, M, N, K)
+    monkeypatch.setenv("QGEMV_W4A8_TR", str(tr))
+    c = synth.uniform_case(11 * tr + M + N, M, N, K, 4)
+    y, xq, _ = _run(c["x"], c)
+    assert np.array_equal(xq, ref.quantize_activations_int8(c["x"])[0])
+    y_ref, A = ref.gemv_w4a8(c["x"], c["codes"], c["scales"], c["zeros"])
+    assert_within(y, y_ref, A, f"w4a8 tr={tr} M={M} N={N} K={K}")
