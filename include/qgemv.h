@@ -40,7 +40,27 @@
  *   hipError_t is available from qgemv_last_hip_error() (per thread).
  * - Accuracy: every result satisfies |y - y_exact| <= 2e-3 * A + 1e-6 with
  *   A[m, n] = sum_k |x[m,k] * w[n,k]|; accumulation is fp32, output is
- *   rounded to nearest even.
+ *   rounded to nearest even.  (qgemv_w4a8 states y_exact over its int8
+ *   activations, which it computes exactly.)
+ *
+ * Tuning overrides
+ * ----------------
+ * For tests and launch-shape sweeps only; normal use sets none of them.  They
+ * are read from the environment on every call and force a choice the library
+ * otherwise makes itself.  A forced shape the kernels do not support is
+ * rejected with an error status (or, for QGEMV_CODEBOOK_GEN_KS, ignored).
+ *   QGEMV_TILE_CFG="tpw,wk[,mt[,v]]"   uniform kernels (qgemv_w2a16 .. qgemv_uniform)
+ *   QGEMV_OUTLIER_CFG="tpw,wk[,mt[,v]]" qgemv_outlier's fused kernel
+ *   QGEMV_OUTLIER_FORM=fused|split      qgemv_outlier: one kernel, or dense then sparse
+ *   QGEMV_LUT4_CFG="tpw,ng,wk[,mt[,d]]" qgemv_lut4
+ *   QGEMV_CODEBOOK_CFG="kind,wk,..."    qgemv_codebook's kernel and shape
+ *   QGEMV_CODEBOOK_GEN_KS=k             qgemv_codebook_gen: k K parts, or -wk for
+ *                                       the stationary kernel with wk waves
+ *   QGEMV_DENSE_CFG="tpw,s,wk"          qgemv_gemv_f16
+ *   QGEMV_GEMM_KERNEL=1, QGEMV_GEMM_MI  qgemv_gemm_uniform: the GEMM at any M; its
+ *                                       block rows (2 or 4 MFMA tiles per wave)
+ *   QGEMV_W4A8_WK, QGEMV_W4A8_TR        qgemv_w4a8: waves and tile-rows (1, 2) per
+ *                                       workgroup
  */
 #ifndef QGEMV_H
 #define QGEMV_H
