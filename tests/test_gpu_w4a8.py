@@ -68,7 +68,9 @@ def test_w4a8_every_wave_count(wk, M, monkeypatch):
     assert_within(y, y_ref, A, f"w4a8 wk={wk} M={M}")
 
 
-@pytest.mark.parametrize("M,N,K", [(1, 28672, 4096), (1, 4096, 14336), (4, 4096, 14336)])
+# the launch configurations the benchmark times (M = 16 on gate+up and qkv: two tile-rows per workgroup)
+@pytest.mark.parametrize("M,N,K", [(1, 28672, 4096), (1, 4096, 14336), (4, 4096, 14336), (16, 28672, 4096),
+                                   (16, 6144, 4096), (16, 4096, 14336)])
 def test_w4a8_full_size_sampled(M, N, K):
     say("w4a8 full", M, N, K)
     c = synth.uniform_case(8 + M, M, N, K, 4)
