@@ -8,15 +8,16 @@
 // lane's 32 consecutive k of one row in one quant group are exactly the B
 // operand of v_mfma_f32_16x16x32_f16 (as in the decode MFMA engine), so a
 // wave dequantizes its B fragments in registers straight from global memory
-// and exactly ((q - z) in fp16).  The activations of a 64-row block are
+// and exactly ((q - z) in fp16).  The activations of the block's rows are
 // staged in LDS one quant group (128 k) at a time, double-buffered, and
 // shared by the workgroup.
 //
-// Block: 64 activation rows x 64 weight rows (4 tile-rows), 4 waves; wave w
-// computes rows 32 (w & 1) .. + 32 and tile-rows 2 (w >> 1) .. + 2 as 2 x 2
-// MFMA tiles.  Per group each wave runs 16 MFMAs into a group partial and
-// adds it times the lane's row scale (one rounding per group, as the decode
-// kernels).  Deterministic.
+// Block: 32 MI activation rows x 64 weight rows (4 tile-rows), 4 waves; wave
+// w owns tile-row w of the block and every activation row of it, so each
+// weight fragment is dequantized once per workgroup (the four waves each read
+// the A fragments from LDS).  Per group a wave runs 8 MI MFMAs into group
+// partials and adds each times the lane's row scale (one rounding per group,
+// as the decode kernels).  Deterministic.
 #include "common.hpp"
 #include "dequant.hpp"
 #include "kernels.hpp"
@@ -26,9 +27,9 @@ namespace {
 
 constexpr int XROW = 136;  // staged activation row: 128 halves + 8 of padding (bank spread)
 
-// MI: 16-row activation tiles per wave; the block has 32 MI rows.
 template <int BITS, int MI>
 __global__ void __launch_bounds__(256) gemm_tiles_kernel(UniformArgs a) {
+  constexpr int NMI = 2 * MI;  // 16-row activation tiles per wave (all of the block)
   using TR = Uni<BITS>;
   constexpr int PPD = TR::CPD / 2;
   constexpr int ZPW = 32 / BITS;
@@ -45,8 +46,7 @@ __global__ void __launch_bounds__(256) gemm_tiles_kernel(UniformArgs a) {
   const int NT = (N + 15) / 16;
   const uint32_t zrow = 4u * ((G * BITS + 31) / 32);
   const int m0 = blockIdx.y * BM;
-  const int rt0 = blockIdx.x * 4 + 2 * (wave >> 1);  // this wave's first tile-row
-  const int mw = 16 * MI * (wave & 1);               // this wave's first row of the block
+  const int rt = blockIdx.x * 4 + wave;  // this wave's tile-row
   const uint32_t mg = magic1024x2();
 
   const rsrc_t rw = make_rsrc(a.wq, (uint32_t)NT * G * TB);
@@ -70,43 +70,37 @@ __global__ void __launch_bounds__(256) gemm_tiles_kernel(UniformArgs a) {
       *reinterpret_cast<u4*>(&xs[b][r * XROW + 8 * c8]) = v[i];
     }
   };
-  // weights of the wave's 2 tile-rows in group g: codes, scale and zero point
+  // weights of the wave's tile-row in group g: codes, scale and zero point
   struct Wst {
-    uint32_t w[2][BITS];
-    uint16_t s[2];
-    uint32_t z[2];
+    uint32_t w[BITS];
+    uint16_t s;
+    uint32_t z;
   };
+  const bool tv = rt < NT;
+  const int row = 16 * rt + n;
+  const bool rv = tv && row < N;
   auto w_load = [&](int g, Wst& st) {
+    const uint32_t tb = ((uint32_t)rt * G + g) * TB;
+    if constexpr (BITS == 2) {
+      const u2 v = __builtin_bit_cast(
+          u2, __builtin_amdgcn_raw_buffer_load_b64(rw, tv ? tb + 8u * lane : OOB, 0, CPOL_NT));
+      st.w[0] = v.x;
+      st.w[1] = v.y;
+    } else {
 #pragma unroll
-    for (int t = 0; t < 2; ++t) {
-      const int rt = rt0 + t;
-      const bool tv = rt < NT;
-      const uint32_t tb = ((uint32_t)rt * G + g) * TB;
-      if constexpr (BITS == 2) {
-        const u2 v = __builtin_bit_cast(
-            u2, __builtin_amdgcn_raw_buffer_load_b64(rw, tv ? tb + 8u * lane : OOB, 0, CPOL_NT));
-        st.w[t][0] = v.x;
-        st.w[t][1] = v.y;
-      } else {
+      for (int h = 0; h < BITS / 4; ++h) {
+        const u4 v = bload16<CPOL_NT>(rw, tv ? tb + 1024u * h + 16u * lane : OOB);
 #pragma unroll
-        for (int h = 0; h < BITS / 4; ++h) {
-          const u4 v = bload16<CPOL_NT>(rw, tv ? tb + 1024u * h + 16u * lane : OOB);
-#pragma unroll
-          for (int e = 0; e < 4; ++e) st.w[t][4 * h + e] = v[e];
-        }
+        for (int e = 0; e < 4; ++e) st.w[4 * h + e] = v[e];
       }
-      const int row = 16 * rt + n;
-      const bool rv = tv && row < N;
-      st.s[t] = bload2(rs, rv ? ((uint32_t)row * G + g) * 2u : OOB);
-      st.z[t] = bload4(rz, rv ? (uint32_t)row * zrow + 4u * (uint32_t)(g / ZPW) : OOB);
     }
+    st.s = bload2(rs, rv ? ((uint32_t)row * G + g) * 2u : OOB);
+    st.z = bload4(rz, rv ? (uint32_t)row * zrow + 4u * (uint32_t)(g / ZPW) : OOB);
   };
 
-  f4 acc[MI][2];
+  f4 acc[NMI];
 #pragma unroll
-  for (int i = 0; i < MI; ++i)
-#pragma unroll
-    for (int t = 0; t < 2; ++t) acc[i][t] = f4{0.f, 0.f, 0.f, 0.f};
+  for (int i = 0; i < NMI; ++i) acc[i] = f4{0.f, 0.f, 0.f, 0.f};
 
   // Pipeline, distance 2: group g is computed from LDS buffer g % 2 while
   // group g + 1 waits in registers (stored to the other buffer after the
@@ -126,34 +120,25 @@ __global__ void __launch_bounds__(256) gemm_tiles_kernel(UniformArgs a) {
       x_load(g + 2, xlater);
       w_load(g + 2, later);
     }
-    // B fragments: the (q - z) pairs of the lane's 32 k of each tile-row
-    h2 p[2][16];
+    // B fragments: the (q - z) pairs of the lane's 32 k
+    h2 p[16];
+    const typename TR::Z zz = TR::zc((cur.z >> (BITS * (g % ZPW))) & ((1u << BITS) - 1u));
 #pragma unroll
-    for (int t = 0; t < 2; ++t) {
-      const typename TR::Z zz = TR::zc((cur.z[t] >> (BITS * (g % ZPW))) & ((1u << BITS) - 1u));
+    for (int d = 0; d < BITS; ++d) TR::deq(cur.w[d], mg, zz, p + d * PPD);
+    const float sc = h2f(cur.s);  // lane l: weight row l % 16
 #pragma unroll
-      for (int d = 0; d < BITS; ++d) TR::deq(cur.w[t][d], mg, zz, p[t] + d * PPD);
-    }
-#pragma unroll
-    for (int i = 0; i < MI; ++i) {
-      // A fragments: block row mw + 16 i + n, k 32 kq + 8 s .. + 7 of the group
-      const _Float16* xr = &xs[b][(mw + 16 * i + n) * XROW + 32 * kq];
-      f4 dd[2] = {f4{0.f, 0.f, 0.f, 0.f}, f4{0.f, 0.f, 0.f, 0.f}};
+    for (int i = 0; i < NMI; ++i) {
+      // A fragments: block row 16 i + n, k 32 kq + 8 s .. + 7 of the group
+      const _Float16* xr = &xs[b][(16 * i + n) * XROW + 32 * kq];
+      f4 dd = f4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int s = 0; s < 4; ++s) {
         const h8 av = __builtin_bit_cast(h8, *reinterpret_cast<const u4*>(xr + 8 * s));
-#pragma unroll
-        for (int t = 0; t < 2; ++t) {
-          const u4 bv = {as_u32(p[t][4 * s]), as_u32(p[t][4 * s + 1]), as_u32(p[t][4 * s + 2]), as_u32(p[t][4 * s + 3])};
-          dd[t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(av, __builtin_bit_cast(h8, bv), dd[t], 0, 0, 0);
-        }
+        const u4 bv = {as_u32(p[4 * s]), as_u32(p[4 * s + 1]), as_u32(p[4 * s + 2]), as_u32(p[4 * s + 3])};
+        dd = __builtin_amdgcn_mfma_f32_16x16x32_f16(av, __builtin_bit_cast(h8, bv), dd, 0, 0, 0);
       }
 #pragma unroll
-      for (int t = 0; t < 2; ++t) {
-        const float sc = h2f(cur.s[t]);  // lane l: weight row l % 16 of tile-row t
-#pragma unroll
-        for (int r = 0; r < 4; ++r) acc[i][t][r] = fmaf(sc, dd[t][r], acc[i][t][r]);
-      }
+      for (int r = 0; r < 4; ++r) acc[i][r] = fmaf(sc, dd[r], acc[i][r]);
     }
     if (g + 1 < G) x_store(b ^ 1, xnext);
     lds_barrier();  // group g + 1 staged; every wave is done with buffer b
@@ -170,15 +155,11 @@ __global__ void __launch_bounds__(256) gemm_tiles_kernel(UniformArgs a) {
 
   // lane l holds D[row 4 (l / 16) + r][weight row l % 16] of each 16 x 16 tile
 #pragma unroll
-  for (int i = 0; i < MI; ++i)
+  for (int i = 0; i < NMI; ++i)
 #pragma unroll
-    for (int t = 0; t < 2; ++t) {
-      const int col = 16 * (rt0 + t) + n;
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int row = m0 + mw + 16 * i + 4 * kq + r;
-        if (row < M && col < N) a.y[(size_t)row * N + col] = f2h(acc[i][t][r]);
-      }
+    for (int r = 0; r < 4; ++r) {
+      const int m = m0 + 16 * i + 4 * kq + r;
+      if (m < M && row < N) a.y[(size_t)m * N + row] = f2h(acc[i][r]);
     }
 }
 
