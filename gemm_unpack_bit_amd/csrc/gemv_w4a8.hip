@@ -12,8 +12,8 @@
 //    2048 k of one row: it reads the whole row for the max (exact in any
 //    order, so every workgroup of the row finds the same s_x) and quantizes
 //    its own part, which it already holds in registers.
-//  * gemv_w4a8_kernel: a workgroup owns one 16-row tile-row of the 4-bit
-//    tiled device layout; its waves take runs of WU quant groups
+//  * gemv_w4a8_kernel<TR>: a workgroup owns TR (1 or 2) 16-row tile-rows of
+//    the 4-bit tiled device layout; its waves take runs of WU quant groups
 //    round-robin, issuing all of a run's loads before its MFMAs.  A lane's
 //    4 code words hold its row's 32 k of the group; two byte permutes put a
 //    word's 8 codes in k order, one or/subtract/xor turns them into the
