@@ -178,16 +178,7 @@ gemv_tiles_kernel(UniformArgs a) {
   // past K read instead (they add s = 0 times a finite value)
   const int XK = K + 32;
   const int XM = MFMA ? min(M, 16) : MT;  // staged activation rows
-  // IDENT: the W4 VALU engine with staged activations takes each group's
-  // sum through the identity sum (q - z) x = sum (1024 + q) x - (1024 + z) sum x
-  // on the raw magic-OR values (fields at bit 0; 1024 + 16 q and 64 + z for
-  // fields at bit 4), which saves the packed subtract per pair.  The sums of
-  // the activations that meet the two field kinds, per (row, group, k
-  // quarter), are staged after the activations (group G: the zero pad).
-  constexpr bool IDENT = !MFMA && BITS == 4 && XLDS;
-  float2* const xsum = reinterpret_cast<float2*>(reinterpret_cast<char*>(smem) + (size_t)XM * XK * 2);
-  char* const pbase = reinterpret_cast<char*>(smem) +
-                      (XLDS ? (size_t)XM * XK * 2 + (IDENT ? (size_t)XM * (G + 1) * 32 : 0) : 0);
+  char* const pbase = reinterpret_cast<char*>(smem) + (XLDS ? (size_t)XM * XK * 2 : 0);
   const uint32_t psb = PLDS ? (32u * G + 15u) & ~15u : 0u;  // 16 rows x G scales, 16-byte padded
   const uint32_t pzb = PLDS ? 16u * zrow : 0u;                // 16 rows of packed zero points
   const uint16_t* ps = reinterpret_cast<const uint16_t*>(pbase);
@@ -305,37 +296,6 @@ gemv_tiles_kernel(UniformArgs a) {
         zw = gin ? zv : 0u;
       }
       const float sc = h2f(sj);
-      if constexpr (IDENT) {
-        // raw pairs: (1024 + q) for the fields at bit 0 (pairs 0, 2 of each
-        // 8-k run), (1024 + 16 q) for those at bit 4 (pairs 1, 3)
-        h2 p[16];
-#pragma unroll
-        for (int d = 0; d < 4; ++d) {
-          const uint32_t w = st.c[j].w[d], u = w >> 8;
-          p[4 * d] = as_h2(and_or(w, 0x000F000Fu, mg));
-          p[4 * d + 1] = as_h2(and_or(w, 0x00F000F0u, mg));
-          p[4 * d + 2] = as_h2(and_or(u, 0x000F000Fu, mg));
-          p[4 * d + 3] = as_h2(and_or(u, 0x00F000F0u, mg));
-        }
-        const float zf = (float)((zw >> (4 * ((gc0 + j) % ZPW))) & 15u);
-        const bool xin = (SAL && XB == 1) || gc0 + j < G;
-#pragma unroll
-        for (int m = 0; m < MT; ++m) {
-          float lo = 0.f, hi = 0.f;
-#pragma unroll
-          for (int v = 0; v < 4; ++v) {
-            const u4 xv = xs[(m * XK + (xin ? 128 * (gc0 + j) + 32 * kq : K)) / 8 + v];
-            lo = dot2(p[4 * v], as_h2(xv[0]), lo);
-            hi = dot2(p[4 * v + 1], as_h2(xv[1]), hi);
-            lo = dot2(p[4 * v + 2], as_h2(xv[2]), lo);
-            hi = dot2(p[4 * v + 3], as_h2(xv[3]), hi);
-          }
-          const float2 xm = xsum[(m * (G + 1) + (xin ? gc0 + j : G)) * 4 + kq];
-          const float corr = fmaf(1024.f + zf, xm.x, (64.f + zf) * xm.y);
-          accv[t][m] = fmaf(sc, fmaf(hi, 0.0625f, lo) - corr, accv[t][m]);
-        }
-        continue;
-      }
       const typename TR::Z zz = TR::zc((zw >> (BITS * ((gc0 + j) % ZPW))) & ZMASK);
       h2 p[16];  // (q - z) pairs of the lane's 32 consecutive k
 #pragma unroll
@@ -449,27 +409,6 @@ gemv_tiles_kernel(UniformArgs a) {
         vptr[i] = bload4(rtp, ((uint32_t)rt0 * G + i) * 4u);
     }
     lds_barrier();
-    if constexpr (IDENT) {
-      // per (row, group <= G, quarter): the sums of the staged activations at
-      // the pairs that meet bit-0 fields and bit-4 fields
-      const h2 ones = {(_Float16)1.0f, (_Float16)1.0f};
-      const int per = (G + 1) * 4;
-      for (int i = threadIdx.x; i < XM * per; i += blockDim.x) {
-        const int m = i / per, r = i - m * per, g = r >> 2, q = r & 3;
-        const int base = (m * XK + (g < G ? 128 * g + 32 * q : K)) / 8;
-        float lo = 0.f, hi = 0.f;
-#pragma unroll
-        for (int v = 0; v < 4; ++v) {
-          const u4 xv = xs[base + v];
-          lo = dot2(as_h2(xv[0]), ones, lo);
-          hi = dot2(as_h2(xv[1]), ones, hi);
-          lo = dot2(as_h2(xv[2]), ones, lo);
-          hi = dot2(as_h2(xv[3]), ones, hi);
-        }
-        xsum[i] = float2{lo, hi};
-      }
-      lds_barrier();
-    }
   };
   // Outliers (FlashQuant abstract: an fp16 sparse path fused with the
   // low-bit dense one, sharing activations and outputs; Tile-COO records).
@@ -761,8 +700,7 @@ hipError_t launch_t(const UniformArgs& a, const TileCfg& c, hipStream_t s) {
     const dim3 block(64 * c.wk);
     const size_t red = tiles_lds_bytes(MFMA, MT, TPW, c.wk);
     if (red > LDS_MAX || 64 * c.wk > max_threads(NG)) return hipErrorInvalidValue;
-    // (the W4 VALU engine also stages per-group activation sums)
-    const size_t xl = xlds_bytes(MFMA, MT, a.M, a.K) + (!MFMA && BITS == 4 ? (size_t)MT * (a.K / 128 + 1) * 32 : 0);
+    const size_t xl = xlds_bytes(MFMA, MT, a.M, a.K);
     const bool xlds = xl <= XLDS_MAX;
     // (the buffer bounds check drops a 16-byte load that straddles the end of
     // an array, so both arrays must end on a 16-byte boundary: N % 8 == 0 does)
@@ -921,8 +859,7 @@ TileCfg pick_outlier(int M, int N, int K, bool mfma) {
   // halve the waves until the launch's LDS fits (staged activations and
   // quant params, partials, the sparse phase's slots): long K with batch
   // rows staged leaves less room for per-wave scratch
-  const size_t G = K / 128;
-  size_t xl = xlds_bytes(mfma, c.mt, M, K) + (!mfma ? (size_t)c.mt * (G + 1) * 32 : 0);
+  size_t xl = xlds_bytes(mfma, c.mt, M, K);
   if (xl > XLDS_MAX) xl = 0;
   const size_t fixed = xl + params_lds_bytes(4, K);
   while (c.wk > 1 && fixed + tiles_lds_bytes(mfma, c.mt, c.tpw, c.wk) +

@@ -117,6 +117,25 @@ def uniform_case(seed, M, N, K, bits, g=128, s_lo=0.001, s_hi=0.02):
     )
 
 
+def degenerate_codes(seed, zeros, bits, g=128, near=False):
+    """Codes equal to their group's zero point (q == z at every k: the exact
+    product is 0).  With near=True, one code per (row, group), at a uniform
+    position inside the group, is one step away from z (up, or down at the
+    top code), so each group holds exactly one nonzero weight."""
+    zeros = np.asarray(zeros)
+    N, G = zeros.shape
+    out = np.repeat(zeros, g, axis=1).astype(np.uint8)
+    if near:
+        pos = (uniform01(seed, S_OPOS, N * G) * g).astype(np.int64).reshape(N, G)
+        rows = np.arange(N)
+        top = (1 << bits) - 1
+        for j in range(G):
+            k = g * j + pos[:, j]
+            z = out[rows, k].astype(np.int64)
+            out[rows, k] = np.where(z < top, z + 1, z - 1).astype(np.uint8)
+    return out
+
+
 def dense_case(seed, M, N, K, std=0.02):
     """fp16 weight [N, K] ~ N(0, std) (the magnitude of a dequantized weight)
     and activations x ~ N(0, 1): the input of a plain fp16 GEMV."""

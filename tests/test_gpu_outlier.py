@@ -49,6 +49,29 @@ def test_no_outliers_equals_dense_bitwise(path):
     assert np.array_equal(y.view(np.uint16), yd.view(np.uint16))
 
 
+@pytest.mark.parametrize("path", PATHS)
+@pytest.mark.parametrize("N,K", [(256, 1024), (4096, 4096), (28672, 4096)])
+def test_degenerate_dense_part(path, N, K):
+    """Dense codes equal to their zero points (the dense part is exactly 0):
+    with no outliers y = 0 exactly; with outliers y = the sparse product
+    alone, within the bound of that product's A.  Every engine, M = 1, 2, 4."""
+    c = synth.outlier_case(31 + N, 4, N, K)
+    codes = synth.degenerate_codes(32, c["zeros"], 4)
+    wq, zq, s = q.pack(dev(codes), 4), q.pack_zeros(dev(c["zeros"]), 4), dev(c["scales"])
+    ptr0, _ = q.tilecoo_encode(N, K, [], [], [])
+    ptr, rec = q.tilecoo_encode(N, K, c["o_rows"], c["o_cols"], c["o_vals"])
+    t = torch()
+    empty = t.zeros(0, dtype=t.int32, device="cuda")
+    ys, As = ref.gemv_outlier(c["x"], codes, c["scales"], c["zeros"], c["o_rows"], c["o_cols"], c["o_vals"])
+    for M in (1, 2, 4):
+        say("outlier q==z", path, N, K, M)
+        x = dev(c["x"][:M])
+        y0 = host(q.outlier(x, wq, s, zq, dev(ptr0.view(np.int32)), empty, path))
+        assert np.all(y0.astype(np.float64) == 0.0), f"q==z, no outliers, M={M} path={path}"
+        y = host(q.outlier(x, wq, s, zq, dev(ptr.view(np.int32)), dev(rec.view(np.int32)), path))
+        assert_within(y, ys[:M], As[:M], f"q==z plus outliers M={M} N={N} K={K} path={path}")
+
+
 def test_zero_scales_give_pure_sparse_product():
     """s = 0: the dense part vanishes and y = S x exactly up to fp32 summation."""
     say("outlier spmv")
