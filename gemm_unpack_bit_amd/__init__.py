@@ -18,6 +18,9 @@ OK, ERR_NULL, ERR_SHAPE, ERR_ALIGN, ERR_UNSUPPORTED, ERR_WORKSPACE, ERR_VALUE, E
 PATH_AUTO, PATH_VALU, PATH_MFMA = 0, 1, 2
 LAYOUT_PLAIN, LAYOUT_DEVICE, LAYOUT_ROWS64 = 0, 1, 2
 GROUP = 128
+# qgemv_variant (weight formats, for workspace_bytes)
+W2, W4, W8, LUT4, OUTLIER4, CODEBOOK, W4A8 = 2, 4, 8, 16, 17, 18, 19
+LAYOUT_VERSION = 1  # QGEMV_LAYOUT_VERSION of the header this binding follows
 
 _lib = None
 
@@ -29,6 +32,8 @@ _i64 = ctypes.c_int64
 # name -> (restype, argtypes); kept in step with include/qgemv.h
 _SIGS = {
     "qgemv_version": (_i, []),
+    "qgemv_layout_version": (_i, []),
+    "qgemv_workspace_bytes": (_sz, [_i, _i, _i, _i]),
     "qgemv_status_string": (ctypes.c_char_p, [_i]),
     "qgemv_last_hip_error": (_i, []),
     "qgemv_packed_words": (_sz, [_i, _i, _i, _i]),
@@ -112,6 +117,17 @@ def _need(t, dtype, name):
         raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
     if not t.is_contiguous():
         raise ValueError(f"{name} must be contiguous")
+
+
+def layout_version():
+    """Version of the packed formats (packed buffers are valid only for a
+    library reporting the same one)."""
+    return int(lib().qgemv_layout_version())
+
+
+def workspace_bytes(variant, M, N, K):
+    """Scratch bytes the compute call of `variant` (W2 .. W4A8) needs at (M, N, K)."""
+    return int(lib().qgemv_workspace_bytes(variant, M, N, K))
 
 
 def packed_words(bits, rows, cols, layout=LAYOUT_DEVICE):
@@ -213,7 +229,8 @@ def tilecoo_encode(N, K, rows, cols, vals):
     """Host-side Tile-COO encoding of fp16 outliers (numpy in, numpy out).
 
     rows, cols: integer coordinates; vals: fp16 values.  Returns (tile_ptr
-    uint32 [ceil(N/128) * ceil(K/128) + 1], tile_rec uint32 [nnz])."""
+    uint32 [ceil(N/16) * ceil(K/128) + 1]: tiles of 16 rows x 128 k, tile_rec
+    uint32 [nnz])."""
     import numpy as np
 
     rows = np.ascontiguousarray(rows, dtype=np.int32)

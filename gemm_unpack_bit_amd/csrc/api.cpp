@@ -8,8 +8,16 @@
 #include <cstdio>
 #include <cstdlib>
 #include <cstring>
+#include <mutex>
 
 #include "kernels.hpp"
+
+namespace qg {
+const char* tune_env(const char* name) {
+  static const bool on = std::getenv("QGEMV_TUNING") != nullptr;
+  return on ? std::getenv(name) : nullptr;
+}
+}  // namespace qg
 
 namespace {
 
@@ -47,13 +55,22 @@ int check_mnk(int M, int N, int K, int bits) {
   return QGEMV_OK;
 }
 
+// Tuning overrides (QGEMV_*_CFG and the like) are looked up only when
+// QGEMV_TUNING was set at the first call of the process, so normal calls do no
+// environment lookups on the host path; when it is set they are read on every
+// call, so a sweep can change them between calls.
+using qg::tune_env;
+
+// The out-of-range flag of qgemv_pack is one device word: clearing it,
+// packing and reading it back are serialized across host threads.
+std::mutex g_pack_mutex;
+
 // Tuning override of the launch shape: QGEMV_TILE_CFG="tpw,wk[,mt[,v]]"
 // (tile-rows per workgroup, waves per workgroup, batch rows per VALU
-// workgroup, pipeline variant).  Read on
-// every call (cheap) so a tuning sweep can change it between calls.
+// workgroup, pipeline variant).
 qg::TileCfg tile_cfg(int bits, int M, int N, int K, bool mfma) {
   qg::TileCfg c = qg::pick_tiles(bits, M, N, K, mfma);
-  if (const char* e = std::getenv("QGEMV_TILE_CFG")) {
+  if (const char* e = tune_env("QGEMV_TILE_CFG")) {
     int tpw, wk, mt, v;
     const int n = std::sscanf(e, "%d,%d,%d,%d", &tpw, &wk, &mt, &v);
     if (n >= 2) {
@@ -69,7 +86,7 @@ qg::TileCfg tile_cfg(int bits, int M, int N, int K, bool mfma) {
 // Tuning override of the LUT4 launch shape: QGEMV_LUT4_CFG="tpw,ng,wk[,mt[,d]]".
 qg::Lut4Cfg lut4_cfg(int M, int N, int K) {
   qg::Lut4Cfg c = qg::pick_lut4(M, N, K);
-  if (const char* e = std::getenv("QGEMV_LUT4_CFG")) {
+  if (const char* e = tune_env("QGEMV_LUT4_CFG")) {
     int tpw, ng, wk, mt, d;
     const int n = std::sscanf(e, "%d,%d,%d,%d,%d", &tpw, &ng, &wk, &mt, &d);
     if (n >= 3) {
@@ -97,7 +114,22 @@ int auto_path(int bits, int M, int N) {
 
 extern "C" {
 
-int qgemv_version(void) { return 100; }
+int qgemv_version(void) { return 200; }
+
+int qgemv_layout_version(void) { return QGEMV_LAYOUT_VERSION; }
+
+size_t qgemv_workspace_bytes(int variant, int M, int N, int K) {
+  switch (variant) {
+    case QGEMV_W2:
+    case QGEMV_W4:
+    case QGEMV_W8:
+    case QGEMV_LUT4:
+    case QGEMV_OUTLIER4: return 0;
+    case QGEMV_CODEBOOK: return qgemv_codebook_workspace_bytes(M, N, K);
+    case QGEMV_W4A8: return N >= 1 ? qgemv_w4a8_workspace_bytes(M, K) : 0;
+  }
+  return 0;
+}
 
 const char* qgemv_status_string(int status) {
   switch (status) {
@@ -131,6 +163,7 @@ int qgemv_pack(int bits, int layout, int rows, int cols, const uint8_t* codes, u
   if (rows < 0 || cols < 0 || (layout == QGEMV_LAYOUT_DEVICE && cols % QGEMV_GROUP)) return QGEMV_ERR_SHAPE;
   if (overlaps(codes, (size_t)rows * cols, packed, words(bits, layout, rows, cols) * 4)) return QGEMV_ERR_VALUE;
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  std::lock_guard<std::mutex> lock(g_pack_mutex);
   int rc = hip_status(qg::launch_pack(bits, layout, rows, cols, codes, packed, s));
   if (rc) return rc;
   int bad = 0;
@@ -201,7 +234,7 @@ int qgemv_w4a8(int M, int N, int K, const uint16_t* x, const uint32_t* wq, const
   float* sx = reinterpret_cast<float*>(reinterpret_cast<char*>(ws) + ((size_t)M * K + 15) / 16 * 16);
   qg::W4A8Args a{M, N, K, x, wq, scales, zeros, y, xq, sx};
   int wk = qg::w4a8_waves(N, K);
-  if (const char* e = std::getenv("QGEMV_W4A8_WK")) wk = std::atoi(e);  // tuning override
+  if (const char* e = tune_env("QGEMV_W4A8_WK")) wk = std::atoi(e);  // tuning override
   return hip_status(qg::launch_gemv_w4a8(a, wk, reinterpret_cast<hipStream_t>(stream)));
 }
 
@@ -229,7 +262,7 @@ int qgemv_gemm_uniform(int bits, int M, int N, int K, const uint16_t* x, const u
   // decode kernel on each 16-row slice (it streams the weights once per
   // slice, but its grid fills the chip: 101 vs 287 us per step at M = 32);
   // from 65 rows on, the GEMM (faster from about M = 128).
-  const char* force = std::getenv("QGEMV_GEMM_KERNEL");  // tuning override: "1" = the GEMM at any M
+  const char* force = tune_env("QGEMV_GEMM_KERNEL");  // tuning override: "1" = the GEMM at any M
   if (M <= QGEMV_GEMM_SLICE_MAX_M && !(force && force[0] == '1')) {
     for (int m0 = 0; m0 < M; m0 += QGEMV_MAX_M) {
       const int mm = M - m0 < QGEMV_MAX_M ? M - m0 : QGEMV_MAX_M;
@@ -244,7 +277,7 @@ int qgemv_gemm_uniform(int bits, int M, int N, int K, const uint16_t* x, const u
   // MFMA) once they still give about 448 workgroups, else 64-row blocks
   // (sweeps of the 8B layers, M = 128..2048)
   int mi = (long)((N + 63) / 64) * ((M + 127) / 128) >= 448 ? 4 : 2;
-  if (const char* e = std::getenv("QGEMV_GEMM_MI")) mi = std::atoi(e);  // tuning override
+  if (const char* e = tune_env("QGEMV_GEMM_MI")) mi = std::atoi(e);  // tuning override
   return hip_status(qg::launch_gemm_tiles(a, mi, s));
 }
 
@@ -291,8 +324,8 @@ int qgemv_outlier(int path, int M, int N, int K, const uint16_t* x, const uint32
   // separate sparse kernel is faster (28672 x 4096: 26.1 vs 37.4 us at M = 4,
   // 69.8 vs 83.3 at M = 16).  QGEMV_OUTLIER_FORM=fused|split forces a form.
   bool split = M >= 4 && N >= 16384 && K <= QGEMV_SPMV_MAX_K && (long)M * K * 2 + 512 < 1L << 31;
-  if (const char* e = std::getenv("QGEMV_OUTLIER_FORM")) split = std::strcmp(e, "split") == 0;
-  if (split && !std::getenv("QGEMV_OUTLIER_CFG")) {
+  if (const char* e = tune_env("QGEMV_OUTLIER_FORM")) split = std::strcmp(e, "split") == 0;
+  if (split && !tune_env("QGEMV_OUTLIER_CFG")) {
     const qg::UniformArgs d{4, M, N, K, x, wq, scales, zeros, y, nullptr, nullptr, 0};
     const hipError_t e = qg::launch_gemv_tiles(d, tile_cfg(4, M, N, K, mfma), s);
     if (e != hipSuccess || nnz == 0) return hip_status(e);
@@ -300,7 +333,7 @@ int qgemv_outlier(int path, int M, int N, int K, const uint16_t* x, const uint32
     return hip_status(qg::launch_spmv_tilecoo(sa, s));
   }
   qg::TileCfg c = qg::pick_outlier(M, N, K, mfma);
-  if (const char* e = std::getenv("QGEMV_OUTLIER_CFG")) {  // tuning override "tpw,wk[,mt[,v]]"
+  if (const char* e = tune_env("QGEMV_OUTLIER_CFG")) {  // tuning override "tpw,wk[,mt[,v]]"
     int tpw, wk, mt, v;
     const int n = std::sscanf(e, "%d,%d,%d,%d", &tpw, &wk, &mt, &v);
     if (n >= 2) {
@@ -341,7 +374,7 @@ int qgemv_codebook(int M, int N, int K, const uint16_t* x, const uint32_t* codes
     return QGEMV_ERR_VALUE;
   qg::CodebookCfg c = qg::pick_codebook(M, N, K);
   // tuning override: "1,wk,pp,r[,mb]" (stationary) or "0,wk,ks" (sequential)
-  if (const char* e = std::getenv("QGEMV_CODEBOOK_CFG")) {
+  if (const char* e = tune_env("QGEMV_CODEBOOK_CFG")) {
     int kind, wk, p1, p2 = 0, p3 = 1;
     if (std::sscanf(e, "%d,%d,%d,%d,%d", &kind, &wk, &p1, &p2, &p3) >= 3) {
       c.wk = wk;
@@ -399,7 +432,7 @@ int qgemv_codebook_gen(int M, int N, int K, int ncb, int v, int group, const uin
              overlaps(ws, ws_bytes, codebooks, cbytes) || overlaps(ws, ws_bytes, scales, sbytes)))
     return QGEMV_ERR_VALUE;
   int ks = qg::codebook_gen_ks(M, N, K);
-  if (const char* e = std::getenv("QGEMV_CODEBOOK_GEN_KS")) {  // tuning override: K parts, or -wk (stationary)
+  if (const char* e = tune_env("QGEMV_CODEBOOK_GEN_KS")) {  // tuning override: K parts, or -wk (stationary)
     const int k = std::atoi(e);
     if (k >= 1) ks = k < K / 256 ? k : K / 256;
     if (k <= -1 && k >= -4) ks = k;
@@ -483,7 +516,7 @@ int qgemv_gemv_f16(int M, int N, int K, const uint16_t* x, const uint16_t* w, ui
   if (overlaps(y, ybytes, x, (size_t)M * K * 2) || overlaps(y, ybytes, w, (size_t)N * K * 2))
     return QGEMV_ERR_VALUE;
   qg::DenseCfg c = qg::pick_dense(M, N, K);
-  if (const char* e = std::getenv("QGEMV_DENSE_CFG")) {  // tuning override "tpw,s,wk"
+  if (const char* e = tune_env("QGEMV_DENSE_CFG")) {  // tuning override "tpw,s,wk"
     int tpw, st, wk;
     if (std::sscanf(e, "%d,%d,%d", &tpw, &st, &wk) == 3) c = {tpw, st, wk};
   }

@@ -229,7 +229,7 @@ int w4a8_tile_rows(int M, int N) { return M > 8 && (N + 15) / 16 >= 384 ? 2 : 1;
 hipError_t launch_gemv_w4a8(const W4A8Args& a, int wk, hipStream_t s) {
   if (wk < 1 || wk > 16) return hipErrorInvalidValue;
   int tr = w4a8_tile_rows(a.M, a.N);
-  if (const char* e = std::getenv("QGEMV_W4A8_TR")) tr = std::atoi(e);  // tuning override (1, 2)
+  if (const char* e = tune_env("QGEMV_W4A8_TR")) tr = std::atoi(e);  // tuning override (1, 2)
   if (tr != 1 && tr != 2) return hipErrorInvalidValue;
   hipLaunchKernelGGL(quant_rows_kernel, dim3((a.K / 8 + QT - 1) / QT, a.M), dim3(QT), 0, s, a);
   hipError_t e = hipGetLastError();

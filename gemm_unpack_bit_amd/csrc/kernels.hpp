@@ -6,6 +6,10 @@
 
 namespace qg {
 
+// A tuning override from the environment, or NULL: looked up only when
+// QGEMV_TUNING was set at the process's first call (api.cpp).
+const char* tune_env(const char* name);
+
 struct UniformArgs {
   int bits, M, N, K;
   const uint16_t* x;

@@ -46,7 +46,9 @@
  * Tuning overrides
  * ----------------
  * For tests and launch-shape sweeps only; normal use sets none of them.  They
- * are read from the environment on every call and force a choice the library
+ * are read only when QGEMV_TUNING is set in the environment at the library's
+ * first call (checked once per process); then they are read on every call,
+ * so a sweep can change them between calls.  Each forces a choice the library
  * otherwise makes itself.  A forced shape the kernels do not support is
  * rejected with an error status (or, for QGEMV_CODEBOOK_GEN_KS, ignored).
  *   QGEMV_TILE_CFG="tpw,wk[,mt[,v]]"   uniform kernels (qgemv_w2a16 .. qgemv_uniform)
@@ -99,8 +101,35 @@ typedef enum {
 #define QGEMV_LUT4_MAX_K 48000
 #define QGEMV_SPMV_MAX_K 1048576
 
+/* Weight formats (one per compute family), for qgemv_workspace_bytes. */
+typedef enum {
+  QGEMV_W2 = 2,        /* qgemv_w2a16 / qgemv_uniform(2, ...)   */
+  QGEMV_W4 = 4,        /* qgemv_w4a16 / qgemv_uniform(4, ...)   */
+  QGEMV_W8 = 8,        /* qgemv_w8a16 / qgemv_uniform(8, ...)   */
+  QGEMV_LUT4 = 16,     /* qgemv_lut4                            */
+  QGEMV_OUTLIER4 = 17, /* qgemv_outlier                         */
+  QGEMV_CODEBOOK = 18, /* qgemv_codebook                        */
+  QGEMV_W4A8 = 19      /* qgemv_w4a8                            */
+} qgemv_variant;
+
 /* Library version (major*10000 + minor*100 + patch). */
 int qgemv_version(void);
+
+/* Version of every packed format this library reads and writes: the device
+ * and rows-of-64 code layouts, the plain zero-point packing and the Tile-COO
+ * record.  Packed buffers are valid only for a library reporting the same
+ * layout version; keep it beside stored packed weights and repack on a
+ * mismatch. */
+#define QGEMV_LAYOUT_VERSION 1
+int qgemv_layout_version(void);
+
+/* Scratch bytes the compute entry point of `variant` needs (or, for
+ * QGEMV_CODEBOOK, uses to split K) at batch M and an N x K weight: 0 for the
+ * variants that take no workspace (QGEMV_W2/W4/W8, QGEMV_LUT4, QGEMV_OUTLIER4),
+ * qgemv_codebook_workspace_bytes(M, N, K) for QGEMV_CODEBOOK and
+ * qgemv_w4a8_workspace_bytes(M, K) for QGEMV_W4A8.  Also 0 for an unknown
+ * variant or a shape the variant rejects (its call then reports the error). */
+size_t qgemv_workspace_bytes(int variant, int M, int N, int K);
 /* Static string for a status code (never NULL). */
 const char *qgemv_status_string(int status);
 /* hipError_t of the last failed HIP call in this thread (0 if none). */
@@ -146,7 +175,11 @@ size_t qgemv_packed_words(int bits, int layout, int rows, int cols);
 /* codes [dev] uint8 [rows, cols], one code per byte (< 2^bits)
  * packed [dev] uint32 [qgemv_packed_words(bits, layout, rows, cols)]
  * Offline prep: synchronizes `stream`; returns QGEMV_ERR_VALUE (packed
- * contents then unspecified) if any code is >= 2^bits. */
+ * contents then unspecified) if any code is >= 2^bits.  The out-of-range flag
+ * is one device word per GPU: calls from several host threads are serialized
+ * inside the library (each holds a lock from clearing the flag to reading it
+ * back), so concurrent calls on different streams stay correct but do not
+ * overlap. */
 int qgemv_pack(int bits, int layout, int rows, int cols, const uint8_t *codes, uint32_t *packed,
                qgemv_stream_t stream);
 

@@ -55,6 +55,25 @@ def test_host_queries(L):
     assert L.qgemv_last_hip_error() == 0
 
 
+def test_layout_version_and_workspace_query(L):
+    assert L.qgemv_layout_version() == q.LAYOUT_VERSION == 1
+    hdr = open(os.path.join(ROOT, "include", "qgemv.h")).read()
+    assert re.search(r"#define QGEMV_LAYOUT_VERSION 1\b", hdr)
+    # formats that take no workspace
+    for v in (q.W2, q.W4, q.W8, q.LUT4, q.OUTLIER4):
+        assert L.qgemv_workspace_bytes(v, 1, 4096, 4096) == 0
+        assert L.qgemv_workspace_bytes(v, 16, 57344, 8192) == 0
+    # the families with one agree with their own queries
+    for M, N, K in ((1, 4096, 4096), (4, 57344, 8192), (16, 8192, 28672)):
+        assert L.qgemv_workspace_bytes(q.CODEBOOK, M, N, K) == L.qgemv_codebook_workspace_bytes(M, N, K)
+        assert L.qgemv_workspace_bytes(q.W4A8, M, N, K) == L.qgemv_w4a8_workspace_bytes(M, K) > 0
+    # unknown variant, bad shapes
+    assert L.qgemv_workspace_bytes(3, 1, 64, 128) == 0
+    assert L.qgemv_workspace_bytes(q.W4A8, 0, 64, 128) == 0
+    assert L.qgemv_workspace_bytes(q.W4A8, 1, 64, 100) == 0
+    assert L.qgemv_workspace_bytes(q.W4A8, 1, 0, 128) == 0
+
+
 FAKE = 0x1000  # 16-byte aligned, never dereferenced: every call below fails validation first
 
 
