@@ -51,6 +51,7 @@ _SIGS = {
     "qgemv_tilecoo_encode": (_i, [_i, _i, ctypes.c_int64, _vp, _vp, _vp, _vp, _vp]),
     "qgemv_w4a8": (_i, [_i, _i, _i, _vp, _vp, _vp, _vp, _vp, _vp, _sz, _vp]),
     "qgemv_w4a8_workspace_bytes": (_sz, [_i, _i]),
+    "qgemv_w4a8_noalloc": (_i, [_i, _i, _i, _vp, _vp, _vp, _vp, _vp, _vp]),
     "qgemv_gemm_uniform": (_i, [_i, _i, _i, _i, _vp, _vp, _vp, _vp, _vp, _vp]),
     "qgemv_codebook_gen": (_i, [_i, _i, _i, _i, _i, _i, _vp, _vp, _vp, _vp, _vp, _vp, _sz, _vp]),
     "qgemv_codebook_gen_workspace_bytes": (_sz, [_i, _i, _i, _i, _i, _i]),
@@ -500,4 +501,30 @@ def w4a8(x, wq, scales, zeros, ws, out=None):
         _need(out, torch.float16, "out")
     _check("qgemv_w4a8", lib().qgemv_w4a8(M, N, K, _ptr(x), _ptr(wq), _ptr(scales), _ptr(zeros), _ptr(out),
                                           _ptr(ws), ws.numel() * ws.element_size(), _stream(x)))
+    return out
+
+
+W4A8_NOALLOC_MAX_MK = 1 << 20  # QGEMV_W4A8_NOALLOC_MAX_MK
+
+
+def w4a8_noalloc(x, wq, scales, zeros, out=None):
+    """w4a8 without a workspace: the library's own per-GPU scratch holds the
+    int8 activations (M * K <= W4A8_NOALLOC_MAX_MK).  Calls that overlap in
+    time on one GPU race on that scratch."""
+    torch = _torch()
+    _need(x, torch.float16, "x")
+    _need(wq, torch.int32, "wq")
+    _need(scales, torch.float16, "scales")
+    _need(zeros, torch.int32, "zeros")
+    M, K = x.shape
+    N = scales.shape[0]
+    need = packed_words(4, N, K)
+    if need and wq.numel() != need:
+        raise ValueError("wq does not hold N x K device-layout 4-bit codes")
+    if out is None:
+        out = torch.empty((M, N), dtype=torch.float16, device=x.device)
+    else:
+        _need(out, torch.float16, "out")
+    _check("qgemv_w4a8_noalloc", lib().qgemv_w4a8_noalloc(M, N, K, _ptr(x), _ptr(wq), _ptr(scales), _ptr(zeros),
+                                                          _ptr(out), _stream(x)))
     return out

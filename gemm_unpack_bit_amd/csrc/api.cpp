@@ -214,11 +214,13 @@ size_t qgemv_w4a8_workspace_bytes(int M, int K) {
   return qg::w4a8_ws_bytes(M, K);
 }
 
-int qgemv_w4a8(int M, int N, int K, const uint16_t* x, const uint32_t* wq, const uint16_t* scales,
-               const uint32_t* zeros, uint16_t* y, void* ws, size_t ws_bytes, qgemv_stream_t stream) {
-  if (!x || !wq || !scales || !zeros || !y) return QGEMV_ERR_NULL;
-  int rc = check_mnk(M, N, K, 4);
-  if (rc) return rc;
+namespace {
+// qgemv_w4a8 and qgemv_w4a8_noalloc: argument checks (null, shape, workspace,
+// alignment, overlap), then the two kernels with `ws` as the scratch.
+// `ws_checked` = false skips the workspace overlap test (library scratch).
+int w4a8_call(int M, int N, int K, const uint16_t* x, const uint32_t* wq, const uint16_t* scales,
+              const uint32_t* zeros, uint16_t* y, void* ws, size_t ws_bytes, bool ws_checked,
+              qgemv_stream_t stream) {
   if (!ws || ws_bytes < qg::w4a8_ws_bytes(M, K)) return QGEMV_ERR_WORKSPACE;
   if (!aligned16(x) || !aligned16(wq) || ((uintptr_t)scales & 1u) || ((uintptr_t)zeros & 3u) ||
       ((uintptr_t)y & 1u) || !aligned16(ws))
@@ -228,14 +230,36 @@ int qgemv_w4a8(int M, int N, int K, const uint16_t* x, const uint32_t* wq, const
                           words(4, QGEMV_LAYOUT_PLAIN, N, (int)G) * 4};
   const void* in_p[4] = {x, wq, scales, zeros};
   for (int i = 0; i < 4; ++i)
-    if (overlaps(y, ybytes, in_p[i], in_b[i]) || overlaps(ws, ws_bytes, in_p[i], in_b[i])) return QGEMV_ERR_VALUE;
-  if (overlaps(ws, ws_bytes, y, ybytes)) return QGEMV_ERR_VALUE;
+    if (overlaps(y, ybytes, in_p[i], in_b[i]) || (ws_checked && overlaps(ws, ws_bytes, in_p[i], in_b[i])))
+      return QGEMV_ERR_VALUE;
+  if (ws_checked && overlaps(ws, ws_bytes, y, ybytes)) return QGEMV_ERR_VALUE;
   int8_t* xq = reinterpret_cast<int8_t*>(ws);
   float* sx = reinterpret_cast<float*>(reinterpret_cast<char*>(ws) + ((size_t)M * K + 15) / 16 * 16);
   qg::W4A8Args a{M, N, K, x, wq, scales, zeros, y, xq, sx};
   int wk = qg::w4a8_waves(N, K);
   if (const char* e = tune_env("QGEMV_W4A8_WK")) wk = std::atoi(e);  // tuning override
   return hip_status(qg::launch_gemv_w4a8(a, wk, reinterpret_cast<hipStream_t>(stream)));
+}
+}  // namespace
+
+int qgemv_w4a8(int M, int N, int K, const uint16_t* x, const uint32_t* wq, const uint16_t* scales,
+               const uint32_t* zeros, uint16_t* y, void* ws, size_t ws_bytes, qgemv_stream_t stream) {
+  if (!x || !wq || !scales || !zeros || !y) return QGEMV_ERR_NULL;
+  int rc = check_mnk(M, N, K, 4);
+  if (rc) return rc;
+  return w4a8_call(M, N, K, x, wq, scales, zeros, y, ws, ws_bytes, true, stream);
+}
+
+int qgemv_w4a8_noalloc(int M, int N, int K, const uint16_t* x, const uint32_t* wq, const uint16_t* scales,
+                       const uint32_t* zeros, uint16_t* y, qgemv_stream_t stream) {
+  if (!x || !wq || !scales || !zeros || !y) return QGEMV_ERR_NULL;
+  int rc = check_mnk(M, N, K, 4);
+  if (rc) return rc;
+  if ((size_t)M * K > QGEMV_W4A8_NOALLOC_MAX_MK) return QGEMV_ERR_WORKSPACE;
+  void* ws = nullptr;
+  rc = hip_status(qg::w4a8_noalloc_scratch(&ws));
+  if (rc) return rc;
+  return w4a8_call(M, N, K, x, wq, scales, zeros, y, ws, qg::w4a8_noalloc_scratch_bytes(), false, stream);
 }
 
 int qgemv_gemm_uniform(int bits, int M, int N, int K, const uint16_t* x, const uint32_t* wq, const uint16_t* scales,

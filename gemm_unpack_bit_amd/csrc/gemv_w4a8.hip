@@ -23,6 +23,7 @@
 //    row scale, the waves are added in a fixed order through LDS, and the
 //    row's activation scale is applied last.  Deterministic.
 #include <cstdlib>
+#include <mutex>
 
 #include "common.hpp"
 #include "kernels.hpp"
@@ -212,6 +213,40 @@ __global__ void __launch_bounds__(1024) gemv_w4a8_kernel(W4A8Args a) {
 }  // namespace
 
 size_t w4a8_ws_bytes(int M, int K) { return ((size_t)M * K + 15) / 16 * 16 + (size_t)M * 4; }
+
+// Scratch of the entry point that allocates nothing (qgemv_w4a8_noalloc):
+// the int8 activations and fp32 row scales of one call, in a file-scope
+// device array.  Every GPU the library runs on holds its own copy until the
+// process ends; all calls on one GPU share it.  In host code `scratch` names
+// a host-side stand-in, never the device memory: host code uses only the
+// address hipGetSymbolAddress returns for the current device.
+constexpr size_t NOALLOC_SCRATCH_BYTES = W4A8_NOALLOC_MAX_MK + 16 * 4 + 256;
+static __device__ __align__(256) uint8_t scratch[NOALLOC_SCRATCH_BYTES];
+static_assert(NOALLOC_SCRATCH_BYTES >= W4A8_NOALLOC_MAX_MK + 15 + 16 * 4, "room for x_q and s_x at M <= 16");
+
+size_t w4a8_noalloc_scratch_bytes() { return NOALLOC_SCRATCH_BYTES; }
+
+// Device address of `scratch` on the calling thread's current device, looked
+// up once per device (with that device current) and kept.
+hipError_t w4a8_noalloc_scratch(void** ptr) {
+  constexpr int MAX_DEV = 64;
+  static std::mutex mu;
+  static void* addr[MAX_DEV] = {};
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= MAX_DEV) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(mu);
+  if (!addr[dev]) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    if (!p) return hipErrorInvalidSymbol;
+    addr[dev] = p;
+  }
+  *ptr = addr[dev];
+  return hipSuccess;
+}
 
 // waves per workgroup: as the decode VALU engine's one-group chunks (16 for
 // long K, 4 on wide layers, else 8), at most one per run of WU groups

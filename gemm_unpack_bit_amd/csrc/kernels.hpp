@@ -118,6 +118,12 @@ struct W4A8Args {
   float* sx;
 };
 size_t w4a8_ws_bytes(int M, int K);
+// qgemv_w4a8_noalloc: largest M * K its static scratch holds, the scratch's
+// size, and its device address on the current device (looked up once per
+// device)
+constexpr size_t W4A8_NOALLOC_MAX_MK = 1u << 20;
+size_t w4a8_noalloc_scratch_bytes();
+hipError_t w4a8_noalloc_scratch(void** ptr);
 int w4a8_waves(int N, int K);
 hipError_t launch_gemv_w4a8(const W4A8Args& a, int wk, hipStream_t s);
 

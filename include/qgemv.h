@@ -370,6 +370,22 @@ int qgemv_w4a8(int M, int N, int K, const uint16_t *x, const uint32_t *wq, const
 /* Workspace bytes of qgemv_w4a8 (0 on bad arguments). */
 size_t qgemv_w4a8_workspace_bytes(int M, int K);
 
+/* qgemv_w4a8 without a workspace argument, for callers that cannot allocate
+ * device memory (code under stream capture, tight serving loops, harnesses
+ * that forbid allocation): the int8 activations and row scales go to a
+ * scratch array inside the library, one per GPU, held until the process ends
+ * (about 1 MiB each).  The call itself allocates and frees nothing.
+ * M * K <= QGEMV_W4A8_NOALLOC_MAX_MK (QGEMV_ERR_WORKSPACE beyond); other
+ * arguments, checks and results as qgemv_w4a8 (same kernels, same bits).
+ * The calling thread's current device must be the device of `stream` and of
+ * every buffer.  All calls on one GPU share its scratch and each leaves its
+ * x_q and s_x there (every call rewrites what it reads): calls that overlap
+ * in time on one GPU (other streams, other threads) race and must be
+ * serialized by the caller. */
+#define QGEMV_W4A8_NOALLOC_MAX_MK 1048576
+int qgemv_w4a8_noalloc(int M, int N, int K, const uint16_t *x, const uint32_t *wq, const uint16_t *scales,
+                       const uint32_t *zeros, uint16_t *y, qgemv_stream_t stream);
+
 /* ------------------------------------------------------------------------
  * Prefill-size GEMM of the uniform format (any M), the compute-bound regime
  * the decode kernels give way to as the batch grows (QFactory review, "Key

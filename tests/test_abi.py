@@ -227,3 +227,16 @@ def test_w4a8_validation_without_gpu(L):
     assert wa(x=FAKE + 8) == q.ERR_ALIGN
     assert wa(ws=FAKE * 2) == q.ERR_VALUE            # the workspace overlaps the codes
     assert L.qgemv_w4a8_workspace_bytes(3, 256) == 3 * 256 + 3 * 4   # int8 rows, then the fp32 scales
+
+
+def test_w4a8_noalloc_validation_without_gpu(L):
+    """Every check runs before the library looks up its scratch on the device."""
+    v = ctypes.c_void_p
+    na = lambda M=1, N=64, K=256, x=FAKE, wq=FAKE * 2, s=FAKE * 3, z=FAKE * 4, y=FAKE * 64: \
+        L.qgemv_w4a8_noalloc(M, N, K, v(x), v(wq), v(s), v(z), v(y), v(0))
+    assert na(x=0) == q.ERR_NULL
+    assert na(M=17) == q.ERR_SHAPE
+    assert na(K=200) == q.ERR_SHAPE
+    # M * K beyond the scratch the library holds
+    assert na(M=16, K=q.W4A8_NOALLOC_MAX_MK // 16 + 128, y=FAKE * 4096) == q.ERR_WORKSPACE
+    assert na(M=1, K=q.W4A8_NOALLOC_MAX_MK + 128, y=FAKE * 4096) == q.ERR_WORKSPACE
