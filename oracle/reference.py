@@ -143,6 +143,91 @@ def gemv_w4a8(x, codes, scales, zeros, g=128, rows=None):
     return y * sx64, A * sx64
 
 
+def quantize_activations_asym8(x):
+    """Asymmetric per-row int8 activations with an integer zero point, the
+    activation side of a matmul whose two operands both carry zero points
+    (QFactory review, observation 2: A_z1 . B_z2 expanded through all-ones J
+    matrices).  The pages fix no activation scheme; reading taken: one fp32
+    scale and one zero point per row mapping the row's range, widened to
+    contain 0 (so that the zero point stays a signed byte), onto the signed
+    byte range, every decision in fp32:
+        lo, hi = min(min_k x, 0), max(max_k x, 0)
+        s = (hi - lo) / 255,  zx = clamp(-128 - rint(lo / s), -128, 127)
+        q = clamp(rint(x / s) + zx, -128, 127)
+    (a zero row: s = 0, zx = 0, q = 0), and the activation the GEMV uses is
+    s * (q - zx).  Returns (q int8 [M, K], s float32 [M], zx int32 [M])."""
+    x32 = np.asarray(x).astype(np.float32)
+    lo = np.minimum(x32.min(axis=1), np.float32(0.0))
+    hi = np.maximum(x32.max(axis=1), np.float32(0.0))
+    s = ((hi - lo).astype(np.float32) / np.float32(255.0)).astype(np.float32)
+    safe = np.where(s > 0, s, np.float32(1.0)).astype(np.float32)
+    zx = np.where(s > 0, np.clip(-128.0 - np.rint((lo / safe).astype(np.float32)), -128, 127), 0).astype(np.int32)
+    q = (np.rint((x32 / safe[:, None]).astype(np.float32)) + zx[:, None]).clip(-128, 127)
+    q = np.where(s[:, None] > 0, q, 0).astype(np.int8)
+    return q, s, zx
+
+
+def gemv_w4a8_asym(x, codes, scales, zeros, g=128, rows=None):
+    """W4A8 with asymmetric activations, by definition: both operands
+    dequantized, y[m, n] = s_x[m] * sum_k s_w[n, k // g] (q[n, k] - z[n, k // g])
+    (x_q[m, k] - zx[m]).  Tolerance scale: s_x[m] * sum_k |s_w (q - z) (x_q - zx)|."""
+    xq, sx, zx = quantize_activations_asym8(x)
+    xc = xq.astype(np.float64) - zx.astype(np.float64)[:, None]
+    y, A = gemv_uniform(xc, codes, scales, zeros, g, rows=rows)
+    sx64 = sx.astype(np.float64)[:, None]
+    return y * sx64, A * sx64
+
+
+def gemv_w4a8_asym_expanded(x, codes, scales, zeros, g=128):
+    """The same result through the zero-point expansion of each group's
+    integer dot product (QFactory review, observation 2, plain reading):
+        sum_k (q - z)(x_q - zx) = sum_k q x_q - z sum_k x_q - zx sum_k q + g z zx
+    with the raw codes and raw activation bytes, every term an exact integer."""
+    xq, sx, zx = quantize_activations_asym8(x)
+    q = np.asarray(codes).astype(np.int64)
+    xi = xq.astype(np.int64)
+    z = np.asarray(zeros).astype(np.int64)
+    s = _f64(scales)
+    N, K = q.shape
+    M = xi.shape[0]
+    y = np.zeros((M, N))
+    for G in range(K // g):
+        sl = slice(G * g, (G + 1) * g)
+        qx = xi[:, sl] @ q[:, sl].T                      # [M, N] sum q x_q
+        sx_ = xi[:, sl].sum(axis=1)[:, None]             # [M, 1] sum x_q
+        sq = q[:, sl].sum(axis=1)[None, :]               # [1, N] sum q
+        e = qx - z[:, G][None, :] * sx_ - zx[:, None].astype(np.int64) * sq + g * z[:, G][None, :] * zx[:, None]
+        y += s[:, G][None, :] * e.astype(np.float64)
+    return y * sx.astype(np.float64)[:, None]
+
+
+def split_activations_int8(xq):
+    """Split strategy's decomposition (ADAngel review, DPR: operands split by
+    bits, partial products at a narrower width, outputs reconstructed): each
+    int8 activation into a signed high nibble and an unsigned low nibble,
+    x_q = 16 h + l with h in [-8, 7] and l in [0, 15]."""
+    xi = np.asarray(xq).astype(np.int64)
+    h = np.floor_divide(xi, 16)
+    l = xi - 16 * h
+    return h, l
+
+
+def gemv_w4a8_split(x, codes, scales, zeros, g=128, rows=None):
+    """W4A8 by the Split strategy: decomposition of the int8 activations
+    into 4-bit slices (split_activations_int8), a partial product of each
+    slice with the 4-bit weights (q - z), reconstruction
+    P = 16 P_h + P_l per group, then the scales.  The same value as
+    gemv_w4a8 (padding): the decomposition is exact."""
+    xq, sx = quantize_activations_int8(x)
+    h, l = split_activations_int8(xq)
+    yh, Ah = gemv_uniform(h.astype(np.float64), codes, scales, zeros, g, rows=rows)
+    yl, Al = gemv_uniform(l.astype(np.float64), codes, scales, zeros, g, rows=rows)
+    sx64 = sx.astype(np.float64)[:, None]
+    # tolerance scale: that of the reconstructed product
+    _, A = gemv_uniform(xq.astype(np.float64), codes, scales, zeros, g, rows=rows)
+    return (16.0 * yh + yl) * sx64, A * sx64
+
+
 def gemv_lut4(x, codes, absmax, lut, block=64, rows=None):
     x64 = _f64(x)
 

@@ -469,3 +469,103 @@ def test_w4a8_within_quantization_error_of_w4a16():
     bound = sx.astype(np.float64)[:, None] / 2 * wabs[None, :]
     assert (np.abs(y8 - y16) <= bound + 1e-12).all()
     assert np.abs(y8 - y16).max() > 0
+
+
+# ----------------------------------------------------------------------------
+# W4A8 with asymmetric activations (zero points on both operands) and the
+# Split strategy
+# ----------------------------------------------------------------------------
+def test_asym8_quantization_worked_example():
+    """By hand.  Row 0: x = (-3, 5, 0, 1, 0, ...): lo = -3, hi = 5, s = 8/255
+    (fp32); lo/s = -95.625 -> rint -96, zx = -128 + 96 = -32; x/s = (-95.625,
+    159.375, 0, 31.875) -> (-96, 159, 0, 32) + zx = (-128, 127, -32, 0).
+    Row 1, constant 2 (the range widened to [0, 2]): s = 2/255, zx = -128,
+    2/s -> 255, q = 127.  Row 2, zeros: s = 0, zx = 0, q = 0."""
+    x = np.zeros((3, 128), np.float16)
+    x[0, :4] = [-3.0, 5.0, 0.0, 1.0]
+    x[1, :] = 2.0
+    q, s, zx = ref.quantize_activations_asym8(x)
+    assert s[0] == np.float32(8.0) / np.float32(255.0) and s[1] == np.float32(2.0) / np.float32(255.0) and s[2] == 0
+    assert zx.tolist() == [-32, -128, 0]
+    assert q[0, :4].tolist() == [-128, 127, -32, 0] and (q[0, 4:] == -32).all()
+    assert (q[1] == 127).all() and not q[2].any()
+
+
+def test_asym8_expansion_equals_definition():
+    """The zero-point expansion with raw codes and raw activation bytes (every
+    term an exact integer) equals the dequantize-then-multiply definition."""
+    for seed, (M, N, K) in enumerate([(1, 7, 128), (3, 33, 512), (16, 64, 1024)]):
+        c = synth.uniform_case(700 + seed, M, N, K, 4)
+        y, A = ref.gemv_w4a8_asym(c["x"], c["codes"], c["scales"], c["zeros"])
+        ye = ref.gemv_w4a8_asym_expanded(c["x"], c["codes"], c["scales"], c["zeros"])
+        assert np.abs(y - ye).max() <= 1e-12 * max(1.0, A.max())
+
+
+def test_asym8_exact_brute_force():
+    c = synth.uniform_case(710, 2, 3, 256, 4)
+    xq, sx, zx = ref.quantize_activations_asym8(c["x"])
+    y, _ = ref.gemv_w4a8_asym(c["x"], c["codes"], c["scales"], c["zeros"])
+    for m in range(2):
+        for n in range(3):
+            tot = Fraction(0)
+            for k in range(256):
+                w = Fraction(float(c["scales"][n, k // 128])) * (int(c["codes"][n, k]) - int(c["zeros"][n, k // 128]))
+                tot += w * (int(xq[m, k]) - int(zx[m]))
+            assert abs(float(tot * Fraction(float(sx[m]))) - y[m, n]) <= 1e-12 * max(1.0, abs(y[m, n]))
+
+
+def test_asym8_reduces_to_uniform_on_full_range_integers():
+    """Integer activations that span exactly [-128, 127] quantize to
+    themselves (s = 1, zx = 0), so the result is the uniform GEMV on them."""
+    c = synth.uniform_case(720, 3, 40, 256, 4)
+    x = (np.arange(3 * 256).reshape(3, 256) % 256 - 128).astype(np.float16)
+    q, s, zx = ref.quantize_activations_asym8(x)
+    assert (s == 1).all() and (zx == 0).all() and np.array_equal(q.astype(np.float16), x)
+    ya, Aa = ref.gemv_w4a8_asym(x, c["codes"], c["scales"], c["zeros"])
+    yu, Au = ref.gemv_uniform(x, c["codes"], c["scales"], c["zeros"])
+    assert np.array_equal(ya, yu) and np.array_equal(Aa, Au)
+
+
+def test_asym8_within_quantization_error_of_w4a16():
+    """Each activation moves by at most one step s_x (half a step by
+    rounding, plus the clamp at the top of the range), and the bound is not
+    vacuous; an asymmetric row (all positive) uses the range better than the
+    symmetric scheme."""
+    c = synth.uniform_case(730, 4, 64, 512, 4)
+    x = c["x"].astype(np.float64)
+    x[3] = np.abs(x[3]) + 0.5
+    x = x.astype(np.float16)
+    ya, _ = ref.gemv_w4a8_asym(x, c["codes"], c["scales"], c["zeros"])
+    y16, _ = ref.gemv_uniform(x, c["codes"], c["scales"], c["zeros"])
+    _, sx, _ = ref.quantize_activations_asym8(x)
+    wabs = np.abs(ref.dequant_uniform(c["codes"], c["scales"], c["zeros"])).sum(axis=1)
+    assert (np.abs(ya - y16) <= sx.astype(np.float64)[:, None] * wabs[None, :] + 1e-12).all()
+    assert np.abs(ya - y16).max() > 0
+    ys, _ = ref.gemv_w4a8(x, c["codes"], c["scales"], c["zeros"])
+    assert np.abs(ya - y16)[3].max() < np.abs(ys - y16)[3].max()
+
+
+def test_split_decomposition_is_exact():
+    v = np.arange(-128, 128)
+    h, l = ref.split_activations_int8(v)
+    assert np.array_equal(16 * h + l, v)
+    assert h.min() == -8 and h.max() == 7 and l.min() == 0 and l.max() == 15
+
+
+def test_split_equals_padding():
+    for seed, (M, N, K) in enumerate([(1, 9, 128), (5, 40, 640), (16, 32, 2048)]):
+        c = synth.uniform_case(740 + seed, M, N, K, 4)
+        ys, As = ref.gemv_w4a8_split(c["x"], c["codes"], c["scales"], c["zeros"])
+        yp, Ap = ref.gemv_w4a8(c["x"], c["codes"], c["scales"], c["zeros"])
+        assert np.abs(ys - yp).max() <= 1e-12 * max(1.0, Ap.max()) and np.array_equal(As, Ap)
+
+
+def _mut_expansion_sign(x, codes, scales, zeros, g=128):
+    xq, sx, zx = ref.quantize_activations_asym8(x)
+    return ref.gemv_uniform(xq.astype(np.float64) + zx[:, None], codes, scales, zeros, g)[0] * sx.astype(np.float64)[:, None]
+
+
+def test_planted_asym_mistake_is_caught(monkeypatch):
+    monkeypatch.setattr(ref, "gemv_w4a8_asym_expanded", _mut_expansion_sign)
+    with pytest.raises(AssertionError):
+        test_asym8_expansion_equals_definition()
