@@ -13,6 +13,9 @@ Modules
 ``reference``  float64 y_ref and A = sum_k |x_k w_k| for every variant, plus
                alternative evaluation orders (group identity, Psumbook)
 ``exact``      exact rational brute force for tiny shapes (fractions.Fraction)
+``cref``       a plain C implementation of the uniform GEMV (``cref.c``: its
+               own fp16 decoding and bit loop, float64 sums, OpenMP over rows),
+               the form timed as the CPU baseline
 
 Acceptance rule used throughout: ``|y - y_ref| <= 2e-3 * A + 1e-6``.
 
