@@ -19,7 +19,7 @@ PATH_AUTO, PATH_VALU, PATH_MFMA = 0, 1, 2
 LAYOUT_PLAIN, LAYOUT_DEVICE, LAYOUT_ROWS64 = 0, 1, 2
 GROUP = 128
 # qgemv_variant (weight formats, for workspace_bytes)
-W2, W4, W8, LUT4, OUTLIER4, CODEBOOK, W4A8 = 2, 4, 8, 16, 17, 18, 19
+W2, W4, W8, LUT4, OUTLIER4, CODEBOOK, W4A8, W4A8_SPLIT, W4A8_ASYM = 2, 4, 8, 16, 17, 18, 19, 20, 21
 LAYOUT_VERSION = 1  # QGEMV_LAYOUT_VERSION of the header this binding follows
 
 _lib = None
@@ -52,6 +52,11 @@ _SIGS = {
     "qgemv_w4a8": (_i, [_i, _i, _i, _vp, _vp, _vp, _vp, _vp, _vp, _sz, _vp]),
     "qgemv_w4a8_workspace_bytes": (_sz, [_i, _i]),
     "qgemv_w4a8_noalloc": (_i, [_i, _i, _i, _vp, _vp, _vp, _vp, _vp, _vp]),
+    "qgemv_w4a8_split": (_i, [_i, _i, _i, _vp, _vp, _vp, _vp, _vp, _vp, _sz, _vp]),
+    "qgemv_w4a8_split_workspace_bytes": (_sz, [_i, _i]),
+    "qgemv_w4a8_asym": (_i, [_i, _i, _i, _vp, _vp, _vp, _vp, _vp, _vp, _sz, _vp]),
+    "qgemv_w4a8_asym_workspace_bytes": (_sz, [_i, _i]),
+    "qgemv_stream_read": (_i, [_vp, _sz, _vp, _i, _i, _vp]),
     "qgemv_gemm_uniform": (_i, [_i, _i, _i, _i, _vp, _vp, _vp, _vp, _vp, _vp]),
     "qgemv_codebook_gen": (_i, [_i, _i, _i, _i, _i, _i, _vp, _vp, _vp, _vp, _vp, _vp, _sz, _vp]),
     "qgemv_codebook_gen_workspace_bytes": (_sz, [_i, _i, _i, _i, _i, _i]),
@@ -478,7 +483,29 @@ def w4a8_workspace_bytes(M, K):
     return int(lib().qgemv_w4a8_workspace_bytes(M, K))
 
 
-def w4a8(x, wq, scales, zeros, ws, out=None):
+def w4a8_split_workspace_bytes(M, K):
+    return int(lib().qgemv_w4a8_split_workspace_bytes(M, K))
+
+
+def w4a8_asym_workspace_bytes(M, K):
+    return int(lib().qgemv_w4a8_asym_workspace_bytes(M, K))
+
+
+def w4a8_split(x, wq, scales, zeros, ws, out=None):
+    """W4A8 by the split strategy (the int8 activations as two 4-bit slices
+    on the fp8 matrix cores); the same bits as w4a8.  ws: at least
+    w4a8_split_workspace_bytes(M, K) bytes."""
+    return w4a8(x, wq, scales, zeros, ws, out, _fn="qgemv_w4a8_split")
+
+
+def w4a8_asym(x, wq, scales, zeros, ws, out=None):
+    """W4A8 with asymmetric int8 activations (a scale and a zero point per
+    row), zero points of both operands by the expansion.  ws: at least
+    w4a8_asym_workspace_bytes(M, K) bytes."""
+    return w4a8(x, wq, scales, zeros, ws, out, _fn="qgemv_w4a8_asym")
+
+
+def w4a8(x, wq, scales, zeros, ws, out=None, _fn="qgemv_w4a8"):
     """W4A8 with int8 activations (one symmetric scale per row) on the int8
     matrix cores.  Arguments as w4a16; ws: a CUDA tensor of at least
     w4a8_workspace_bytes(M, K) bytes (16-byte aligned), which holds the int8
@@ -499,8 +526,8 @@ def w4a8(x, wq, scales, zeros, ws, out=None):
         out = torch.empty((M, N), dtype=torch.float16, device=x.device)
     else:
         _need(out, torch.float16, "out")
-    _check("qgemv_w4a8", lib().qgemv_w4a8(M, N, K, _ptr(x), _ptr(wq), _ptr(scales), _ptr(zeros), _ptr(out),
-                                          _ptr(ws), ws.numel() * ws.element_size(), _stream(x)))
+    _check(_fn, getattr(lib(), _fn)(M, N, K, _ptr(x), _ptr(wq), _ptr(scales), _ptr(zeros), _ptr(out),
+                                    _ptr(ws), ws.numel() * ws.element_size(), _stream(x)))
     return out
 
 
@@ -528,3 +555,17 @@ def w4a8_noalloc(x, wq, scales, zeros, out=None):
     _check("qgemv_w4a8_noalloc", lib().qgemv_w4a8_noalloc(M, N, K, _ptr(x), _ptr(wq), _ptr(scales), _ptr(zeros),
                                                           _ptr(out), _stream(x)))
     return out
+
+
+def stream_read(buf, sink, nbytes=None, workgroups=1024, threads=512, offset=0):
+    """Measurement: read `nbytes` of the CUDA tensor `buf` from byte `offset`
+    once (qgemv_stream_read); sink: a CUDA tensor of at least 4 bytes."""
+    torch = _torch()
+    if not isinstance(buf, torch.Tensor) or not buf.is_cuda or not buf.is_contiguous():
+        raise TypeError("buf must be a contiguous CUDA tensor")
+    total = buf.numel() * buf.element_size()
+    nbytes = total - offset if nbytes is None else nbytes
+    if offset < 0 or offset + nbytes > total:
+        raise ValueError("range outside buf")
+    _check("qgemv_stream_read", lib().qgemv_stream_read(_vp(buf.data_ptr() + offset), nbytes, _ptr(sink),
+                                                        workgroups, threads, _stream(buf)))

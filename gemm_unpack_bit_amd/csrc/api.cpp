@@ -127,6 +127,8 @@ size_t qgemv_workspace_bytes(int variant, int M, int N, int K) {
     case QGEMV_OUTLIER4: return 0;
     case QGEMV_CODEBOOK: return qgemv_codebook_workspace_bytes(M, N, K);
     case QGEMV_W4A8: return N >= 1 ? qgemv_w4a8_workspace_bytes(M, K) : 0;
+    case QGEMV_W4A8_SPLIT: return N >= 1 ? qgemv_w4a8_split_workspace_bytes(M, K) : 0;
+    case QGEMV_W4A8_ASYM: return N >= 1 ? qgemv_w4a8_asym_workspace_bytes(M, K) : 0;
   }
   return 0;
 }
@@ -215,13 +217,15 @@ size_t qgemv_w4a8_workspace_bytes(int M, int K) {
 }
 
 namespace {
-// qgemv_w4a8 and qgemv_w4a8_noalloc: argument checks (null, shape, workspace,
-// alignment, overlap), then the two kernels with `ws` as the scratch.
-// `ws_checked` = false skips the workspace overlap test (library scratch).
+// qgemv_w4a8 (and its split / asymmetric forms) and qgemv_w4a8_noalloc:
+// argument checks (null, shape, workspace, alignment, overlap), then the two
+// kernels with `ws` as the scratch.  `ws_checked` = false skips the
+// workspace overlap test (library scratch).
 int w4a8_call(int M, int N, int K, const uint16_t* x, const uint32_t* wq, const uint16_t* scales,
               const uint32_t* zeros, uint16_t* y, void* ws, size_t ws_bytes, bool ws_checked,
-              qgemv_stream_t stream) {
-  if (!ws || ws_bytes < qg::w4a8_ws_bytes(M, K)) return QGEMV_ERR_WORKSPACE;
+              qgemv_stream_t stream, int mode = qg::W4A8_PAD) {
+  const qg::W4A8Ws lay = qg::w4a8_ws_layout(mode, M, K);
+  if (!ws || ws_bytes < lay.total) return QGEMV_ERR_WORKSPACE;
   if (!aligned16(x) || !aligned16(wq) || ((uintptr_t)scales & 1u) || ((uintptr_t)zeros & 3u) ||
       ((uintptr_t)y & 1u) || !aligned16(ws))
     return QGEMV_ERR_ALIGN;
@@ -233,9 +237,12 @@ int w4a8_call(int M, int N, int K, const uint16_t* x, const uint32_t* wq, const 
     if (overlaps(y, ybytes, in_p[i], in_b[i]) || (ws_checked && overlaps(ws, ws_bytes, in_p[i], in_b[i])))
       return QGEMV_ERR_VALUE;
   if (ws_checked && overlaps(ws, ws_bytes, y, ybytes)) return QGEMV_ERR_VALUE;
-  int8_t* xq = reinterpret_cast<int8_t*>(ws);
-  float* sx = reinterpret_cast<float*>(reinterpret_cast<char*>(ws) + ((size_t)M * K + 15) / 16 * 16);
-  qg::W4A8Args a{M, N, K, x, wq, scales, zeros, y, xq, sx};
+  char* w = reinterpret_cast<char*>(ws);
+  qg::W4A8Args a{M, N, K, x, wq, scales, zeros, y, reinterpret_cast<int8_t*>(w + lay.xq),
+                 reinterpret_cast<float*>(w + lay.sx), mode,
+                 mode == qg::W4A8_SPLIT ? reinterpret_cast<uint8_t*>(w + lay.xl) : nullptr,
+                 mode == qg::W4A8_ASYM ? reinterpret_cast<int*>(w + lay.zx) : nullptr,
+                 mode == qg::W4A8_ASYM ? reinterpret_cast<int*>(w + lay.xsum) : nullptr};
   int wk = qg::w4a8_waves(N, K);
   if (const char* e = tune_env("QGEMV_W4A8_WK")) wk = std::atoi(e);  // tuning override
   return hip_status(qg::launch_gemv_w4a8(a, wk, reinterpret_cast<hipStream_t>(stream)));
@@ -248,6 +255,32 @@ int qgemv_w4a8(int M, int N, int K, const uint16_t* x, const uint32_t* wq, const
   int rc = check_mnk(M, N, K, 4);
   if (rc) return rc;
   return w4a8_call(M, N, K, x, wq, scales, zeros, y, ws, ws_bytes, true, stream);
+}
+
+size_t qgemv_w4a8_split_workspace_bytes(int M, int K) {
+  if (M < 1 || M > QGEMV_MAX_M || K < QGEMV_GROUP || K % QGEMV_GROUP) return 0;
+  return qg::w4a8_ws_layout(qg::W4A8_SPLIT, M, K).total;
+}
+
+int qgemv_w4a8_split(int M, int N, int K, const uint16_t* x, const uint32_t* wq, const uint16_t* scales,
+                     const uint32_t* zeros, uint16_t* y, void* ws, size_t ws_bytes, qgemv_stream_t stream) {
+  if (!x || !wq || !scales || !zeros || !y) return QGEMV_ERR_NULL;
+  int rc = check_mnk(M, N, K, 4);
+  if (rc) return rc;
+  return w4a8_call(M, N, K, x, wq, scales, zeros, y, ws, ws_bytes, true, stream, qg::W4A8_SPLIT);
+}
+
+size_t qgemv_w4a8_asym_workspace_bytes(int M, int K) {
+  if (M < 1 || M > QGEMV_MAX_M || K < QGEMV_GROUP || K % QGEMV_GROUP) return 0;
+  return qg::w4a8_ws_layout(qg::W4A8_ASYM, M, K).total;
+}
+
+int qgemv_w4a8_asym(int M, int N, int K, const uint16_t* x, const uint32_t* wq, const uint16_t* scales,
+                    const uint32_t* zeros, uint16_t* y, void* ws, size_t ws_bytes, qgemv_stream_t stream) {
+  if (!x || !wq || !scales || !zeros || !y) return QGEMV_ERR_NULL;
+  int rc = check_mnk(M, N, K, 4);
+  if (rc) return rc;
+  return w4a8_call(M, N, K, x, wq, scales, zeros, y, ws, ws_bytes, true, stream, qg::W4A8_ASYM);
 }
 
 int qgemv_w4a8_noalloc(int M, int N, int K, const uint16_t* x, const uint32_t* wq, const uint16_t* scales,
@@ -565,6 +598,19 @@ int qgemv_spmv_tilecoo(int M, int N, int K, const uint16_t* x, const uint32_t* t
   if (nnz == 0) return QGEMV_OK;  // nothing to add
   qg::SpmvArgs a{M, N, K, x, tile_ptr, tile_rec, (int)nnz, y};
   return hip_status(qg::launch_spmv_tilecoo(a, reinterpret_cast<hipStream_t>(stream)));
+}
+
+// ---- measurement ----
+
+int qgemv_stream_read(const void* src, size_t bytes, uint32_t* sink, int workgroups, int threads,
+                      qgemv_stream_t stream) {
+  if (!src || !sink) return QGEMV_ERR_NULL;
+  if (bytes == 0 || bytes % 16 || workgroups < 1 || threads < 64 || threads > 1024 || threads % 64)
+    return QGEMV_ERR_SHAPE;
+  if (!aligned16(src) || ((uintptr_t)sink & 3u)) return QGEMV_ERR_ALIGN;
+  if (overlaps(sink, 4, src, bytes)) return QGEMV_ERR_VALUE;
+  return hip_status(qg::launch_stream_read(src, bytes, sink, workgroups, threads,
+                                           reinterpret_cast<hipStream_t>(stream)));
 }
 
 }  // extern "C"

@@ -92,5 +92,34 @@ struct Uni<2> {
   }
 };
 
+// ---------------------------------------------------------------------------
+// streaming a lane's share of one 16 x 128 tile of the device layout
+// ---------------------------------------------------------------------------
+// One lane's codes of one tile: 32 codes = b words, in <= 2 loads.
+template <int BITS>
+struct LaneCodes {
+  uint32_t w[BITS];
+  // `off` = lane offset inside the tile (VGPR) or OOB, `soff` = tile offset (SGPR)
+  __device__ __forceinline__ void load(rsrc_t r, uint32_t off, uint32_t soff) {
+    if constexpr (BITS == 2) {
+      const u2 v = __builtin_bit_cast(u2, __builtin_amdgcn_raw_buffer_load_b64(r, off, soff, CPOL_NT));
+      w[0] = v[0];
+      w[1] = v[1];
+    } else {
+#pragma unroll
+      for (int h = 0; h < BITS / 4; ++h) {
+        const u4 v = bload16<CPOL_NT>(r, off + 1024u * h, soff);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) w[4 * h + e] = v[e];
+      }
+    }
+  }
+};
+
+// Lane byte offset inside a tile (its first word).
+template <int BITS>
+__device__ __forceinline__ uint32_t lane_off(int lane) {
+  return (uint32_t)lane * 4u * (BITS < 4 ? BITS : 4);
+}
 
 }  // namespace qg

@@ -37,6 +37,8 @@
 //  * Reduction: the four k-quarters of a row are summed across lanes with the
 //    gfx950 permlane swaps, the waves through LDS in a fixed order, so the
 //    result is bitwise deterministic.
+#include <cstdlib>
+
 #include "common.hpp"
 #include "dequant.hpp"
 #include "kernels.hpp"
@@ -46,33 +48,6 @@ namespace {
 
 __device__ __forceinline__ h8 cat4(h2 a, h2 b, h2 c, h2 d) {
   return __builtin_bit_cast(h8, u4{as_u32(a), as_u32(b), as_u32(c), as_u32(d)});
-}
-
-// One lane's codes of one tile: 32 codes = b words, in <= 2 loads.
-template <int BITS>
-struct LaneCodes {
-  uint32_t w[BITS];
-  // `off` = lane offset inside the tile (VGPR) or OOB, `soff` = tile offset (SGPR)
-  __device__ __forceinline__ void load(rsrc_t r, uint32_t off, uint32_t soff) {
-    if constexpr (BITS == 2) {
-      const u2 v = __builtin_bit_cast(u2, __builtin_amdgcn_raw_buffer_load_b64(r, off, soff, CPOL_NT));
-      w[0] = v[0];
-      w[1] = v[1];
-    } else {
-#pragma unroll
-      for (int h = 0; h < BITS / 4; ++h) {
-        const u4 v = bload16<CPOL_NT>(r, off + 1024u * h, soff);
-#pragma unroll
-        for (int e = 0; e < 4; ++e) w[4 * h + e] = v[e];
-      }
-    }
-  }
-};
-
-// Lane byte offset inside a tile (its first word).
-template <int BITS>
-__device__ __forceinline__ uint32_t lane_off(int lane) {
-  return (uint32_t)lane * 4u * (BITS < 4 ? BITS : 4);
 }
 
 // NG consecutive fp16 scales of one row in one load (2*NG-byte aligned).
@@ -701,7 +676,9 @@ hipError_t launch_t(const UniformArgs& a, const TileCfg& c, hipStream_t s) {
     const size_t red = tiles_lds_bytes(MFMA, MT, TPW, c.wk);
     if (red > LDS_MAX || 64 * c.wk > max_threads(NG)) return hipErrorInvalidValue;
     const size_t xl = xlds_bytes(MFMA, MT, a.M, a.K);
-    const bool xlds = xl <= XLDS_MAX;
+    size_t xmax = XLDS_MAX;
+    if (const char* e = tune_env("QGEMV_XLDS_MAX")) xmax = (size_t)std::atol(e);  // tuning override (bytes)
+    const bool xlds = xl <= xmax;
     // (the buffer bounds check drops a 16-byte load that straddles the end of
     // an array, so both arrays must end on a 16-byte boundary: N % 8 == 0 does)
     const size_t G = a.K / 128, zbytes = (size_t)a.N * 4 * ((G * BITS + 31) / 32);

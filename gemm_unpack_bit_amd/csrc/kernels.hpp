@@ -107,6 +107,11 @@ hipError_t launch_gemv_codebook_gen(const CodebookGenArgs& a, int ks, hipStream_
 
 // W4A8 with the padding strategy (gemv_w4a8.hip): int8 activations per row
 // in the workspace (xq [M, K], then sx [M] fp32 at a 16-byte boundary)
+// W4A8 strategies: padding (int8 matrix cores, symmetric activations),
+// split (the int8 activations in two 4-bit slices on the fp8 matrix cores)
+// and asymmetric activations (zero points on both operands, int8 matrix
+// cores on the raw codes, zero-point expansion)
+enum W4A8Mode { W4A8_PAD = 0, W4A8_SPLIT = 1, W4A8_ASYM = 2 };
 struct W4A8Args {
   int M, N, K;
   const uint16_t* x;
@@ -114,9 +119,19 @@ struct W4A8Args {
   const uint16_t* scales;
   const uint32_t* zeros;
   uint16_t* y;
-  int8_t* xq;
-  float* sx;
+  int8_t* xq;   // pad, asym: int8 activations [M, K]; split: 16 h as fp8 [M, K]
+  float* sx;    // activation scales [M]
+  int mode;     // W4A8Mode
+  uint8_t* xl;  // split: the low slices l as fp8 [M, K]
+  int* zx;      // asym: activation zero points [16]
+  int* xsum;    // asym: per-group sums of the int8 activations [K/128][16]
 };
+// workspace layout of each mode: the byte offsets of xq, xl, sx, zx, xsum
+// and the total (unused parts 0)
+struct W4A8Ws {
+  size_t xq, xl, sx, zx, xsum, total;
+};
+W4A8Ws w4a8_ws_layout(int mode, int M, int K);
 size_t w4a8_ws_bytes(int M, int K);
 // qgemv_w4a8_noalloc: largest M * K its static scratch holds, the scratch's
 // size, and its device address on the current device (looked up once per
@@ -172,6 +187,10 @@ size_t spmv_lds_bytes(int K);
 hipError_t launch_spmv_tilecoo(const SpmvArgs& a, hipStream_t s);
 
 // bit packing (layout: 0 plain, 1 device = tiled, see pack.hip)
+// streaming-read probe (measurement): reads `bytes` (a multiple of 16) once
+hipError_t launch_stream_read(const void* src, size_t bytes, uint32_t* sink, int workgroups, int threads,
+                              hipStream_t s);
+
 size_t packed_words(int bits, int layout, int rows, int cols);
 hipError_t launch_pack(int bits, int layout, int rows, int cols, const uint8_t* codes, uint32_t* packed,
                        hipStream_t s);

@@ -109,7 +109,9 @@ typedef enum {
   QGEMV_LUT4 = 16,     /* qgemv_lut4                            */
   QGEMV_OUTLIER4 = 17, /* qgemv_outlier                         */
   QGEMV_CODEBOOK = 18, /* qgemv_codebook                        */
-  QGEMV_W4A8 = 19      /* qgemv_w4a8                            */
+  QGEMV_W4A8 = 19,     /* qgemv_w4a8                            */
+  QGEMV_W4A8_SPLIT = 20, /* qgemv_w4a8_split                    */
+  QGEMV_W4A8_ASYM = 21   /* qgemv_w4a8_asym                     */
 } qgemv_variant;
 
 /* Library version (major*10000 + minor*100 + patch). */
@@ -127,7 +129,8 @@ int qgemv_layout_version(void);
  * QGEMV_CODEBOOK, uses to split K) at batch M and an N x K weight: 0 for the
  * variants that take no workspace (QGEMV_W2/W4/W8, QGEMV_LUT4, QGEMV_OUTLIER4),
  * qgemv_codebook_workspace_bytes(M, N, K) for QGEMV_CODEBOOK and
- * qgemv_w4a8_workspace_bytes(M, K) for QGEMV_W4A8.  Also 0 for an unknown
+ * qgemv_w4a8_workspace_bytes(M, K) for QGEMV_W4A8 (and the split / asym
+ * queries for QGEMV_W4A8_SPLIT / QGEMV_W4A8_ASYM).  Also 0 for an unknown
  * variant or a shape the variant rejects (its call then reports the error). */
 size_t qgemv_workspace_bytes(int variant, int M, int N, int K);
 /* Static string for a status code (never NULL). */
@@ -370,6 +373,46 @@ int qgemv_w4a8(int M, int N, int K, const uint16_t *x, const uint32_t *wq, const
 /* Workspace bytes of qgemv_w4a8 (0 on bad arguments). */
 size_t qgemv_w4a8_workspace_bytes(int M, int K);
 
+/* ------------------------------------------------------------------------
+ * W4A8 by the split strategy (ADAngel review, DPR: decomposition, partial
+ * products, reconstruction; split sits between padding and bit-serial
+ * decomposition): the same int8 activations and the same result as
+ * qgemv_w4a8, with each x_q decomposed as 16 h + l (h in [-8, 7], l in
+ * [0, 15]) and each 4-bit operand pair multiplied on the fp8 matrix cores
+ * (small integers are exact in fp8 e4m3; v_mfma_f32_16x16x128_f8f6f4), the
+ * two partial products added exactly in one fp32 accumulator.  The result is
+ * bit for bit that of qgemv_w4a8.
+ *   ws [dev] scratch of qgemv_w4a8_split_workspace_bytes(M, K) bytes,
+ *      16-byte aligned: the high slices 16 h [M, K] and the low slices l
+ *      [M, K] as fp8 e4m3 bytes, then the fp32 scales [M] (each part at a
+ *      16-byte boundary).  Required (QGEMV_ERR_WORKSPACE if NULL or smaller).
+ * Other arguments and rules as qgemv_w4a8.
+ * ------------------------------------------------------------------------ */
+int qgemv_w4a8_split(int M, int N, int K, const uint16_t *x, const uint32_t *wq, const uint16_t *scales,
+                     const uint32_t *zeros, uint16_t *y, void *ws, size_t ws_bytes, qgemv_stream_t stream);
+size_t qgemv_w4a8_split_workspace_bytes(int M, int K);
+
+/* ------------------------------------------------------------------------
+ * W4A8 with asymmetric activations, zero points on both operands (QFactory
+ * review, observation 2: the matmul of two zero-point operands expanded
+ * through all-ones matrices, so no operand is dequantized element by
+ * element):
+ *     lo = min(min_k x[m, k], 0), hi = max(max_k x[m, k], 0)      (fp32)
+ *     s_x[m] = (hi - lo) / 255, zx[m] = clamp(-128 - rint(lo / s_x), -128, 127)
+ *     x_q[m, k] = clamp(rint(x / s_x) + zx, -128, 127)   (a zero row: all 0)
+ *     y[m, n] = s_x[m] * sum_k s_w[n, k/128] (q - z[n, k/128]) (x_q - zx[m])
+ * evaluated per group as sum q x_q - z sum x_q - zx sum q + 128 z zx on the
+ * int8 matrix cores with the raw codes, every term an exact integer.
+ *   ws [dev] scratch of qgemv_w4a8_asym_workspace_bytes(M, K) bytes, 16-byte
+ *      aligned: x_q [M, K] int8, then s_x fp32 [16], zx int32 [16] and the
+ *      group sums of x_q int32 [K/128][16] (each part at a 16-byte
+ *      boundary).  Required.
+ * Other arguments and rules as qgemv_w4a8.
+ * ------------------------------------------------------------------------ */
+int qgemv_w4a8_asym(int M, int N, int K, const uint16_t *x, const uint32_t *wq, const uint16_t *scales,
+                    const uint32_t *zeros, uint16_t *y, void *ws, size_t ws_bytes, qgemv_stream_t stream);
+size_t qgemv_w4a8_asym_workspace_bytes(int M, int K);
+
 /* qgemv_w4a8 without a workspace argument, for callers that cannot allocate
  * device memory (code under stream capture, tight serving loops, harnesses
  * that forbid allocation): the int8 activations and row scales go to a
@@ -465,6 +508,20 @@ size_t qgemv_tilecoo_ptr_len(int N, int K);
  * or an inf/NaN value, QGEMV_ERR_SHAPE for bad N, K or nnz. */
 int qgemv_tilecoo_encode(int N, int K, int64_t nnz, const int32_t *rows, const int32_t *cols,
                          const uint16_t *val_bits, uint32_t *tile_ptr, uint32_t *tile_rec);
+
+/* ------------------------------------------------------------------------
+ * Measurement: a plain streaming read of a device buffer, the achievable HBM
+ * read bandwidth the GEMV kernels are compared with.  Reads every byte of
+ * src [dev] once with 16-byte non-temporal loads (a wave-wide load is one
+ * contiguous 1 KB burst, as in the weight streams), grid-stride over
+ * `workgroups` x `threads`.  Writes sink[0] [dev] only if the XOR of all the
+ * data equals a fixed improbable pattern (the result is never needed).
+ * bytes a positive multiple of 16, threads a multiple of 64 in [64, 1024],
+ * workgroups >= 1 (QGEMV_ERR_SHAPE); src 16-byte aligned, sink 4-byte
+ * (QGEMV_ERR_ALIGN).  Asynchronous on `stream`.
+ * ------------------------------------------------------------------------ */
+int qgemv_stream_read(const void *src, size_t bytes, uint32_t *sink, int workgroups, int threads,
+                      qgemv_stream_t stream);
 
 #ifdef __cplusplus
 }

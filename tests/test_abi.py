@@ -240,3 +240,21 @@ def test_w4a8_noalloc_validation_without_gpu(L):
     # M * K beyond the scratch the library holds
     assert na(M=16, K=q.W4A8_NOALLOC_MAX_MK // 16 + 128, y=FAKE * 4096) == q.ERR_WORKSPACE
     assert na(M=1, K=q.W4A8_NOALLOC_MAX_MK + 128, y=FAKE * 4096) == q.ERR_WORKSPACE
+
+
+def test_w4a8_split_and_asym_validation_without_gpu(L):
+    v = ctypes.c_void_p
+    for fn, wsq in ((L.qgemv_w4a8_split, L.qgemv_w4a8_split_workspace_bytes),
+                    (L.qgemv_w4a8_asym, L.qgemv_w4a8_asym_workspace_bytes)):
+        call = lambda M=1, N=64, K=256, x=FAKE, ws=FAKE * 128, wsb=1 << 16: \
+            fn(M, N, K, v(x), v(FAKE * 2), v(FAKE * 3), v(FAKE * 4), v(FAKE * 64), v(ws), wsb, v(0))
+        assert call(x=0) == q.ERR_NULL
+        assert call(M=17) == q.ERR_SHAPE
+        assert call(ws=0) == q.ERR_WORKSPACE
+        assert call(wsb=wsq(1, 256) - 1) == q.ERR_WORKSPACE
+        assert call(ws=FAKE * 2) == q.ERR_VALUE
+    # split: two byte planes then the scales; asym: bytes, 16 scales, 16 zero points, [K/128][16] sums
+    assert L.qgemv_w4a8_split_workspace_bytes(3, 256) == 2 * 768 + 12
+    assert L.qgemv_w4a8_asym_workspace_bytes(3, 256) == 768 + 64 + 64 + 2 * 64
+    assert L.qgemv_workspace_bytes(q.W4A8_SPLIT, 3, 64, 256) == L.qgemv_w4a8_split_workspace_bytes(3, 256)
+    assert L.qgemv_workspace_bytes(q.W4A8_ASYM, 3, 64, 256) == L.qgemv_w4a8_asym_workspace_bytes(3, 256)
