@@ -5,9 +5,9 @@ Llama-3-8B decoder layer -- fused QKV (6144x4096), O (4096x4096), fused
 gate+up (28672x4096), down (4096x14336) -- each a W4A16 group-128 asymmetric
 GEMV through the C ABI (qgemv_w4a16).  Inputs are seeded synthetic tensors of
 those shapes (x ~ N(0,1), codes U{0..15}, scales U(0.001,0.02), zeros
-U{0..15}); R rotated copies of every weight tensor (R * bytes >= 1 GiB, above
-the 256 MB Infinity Cache and the 8 x 4 MB L2) make every call read its
-weights from HBM.
+U{0..15}); each layer rotates over R copies of its weight tensors (R * bytes
+>= 1 GiB, above the 256 MB Infinity Cache and the 8 x 4 MB L2), so every call
+reads its weights from HBM.
 
 Timing: W eager warm-up steps; then the GPU is kept busy by a device-side
 sleep while the host enqueues exactly K steps (4K kernel launches) between two
@@ -16,20 +16,28 @@ HIP events on the launch stream, so the measured region holds GPU time only
 aborts).  Synchronized on both sides.  value = algorithmic bytes of the K steps
 / elapsed time.
 
-Printed: ONE JSON line (rank 0).  Extra objects: "roofline" for the dominant
-kernel (gate+up, the largest matrix; average launch duration = a region of K
-back-to-back launches of that layer alone, timed the same way), "cpu_baseline"
-(the float64 CPU oracle on a bounded row sample, host cores), "layers"
-(per-layer us/call, same method), "variants" (W2, W8, W4 at M = 4 and 16,
-LUT4, outliers, codebook on the same four layers, and the codebook on the
-70B-shaped layers at M = 1 and 4: per-layer launch time and algorithmic
-bytes, sampled rows checked against the oracle first; not part of `value`).  roofline.traffic = HBM bytes per launch of
-that kernel from rocprofv3 FETCH_SIZE / WRITE_SIZE (scaled by a device copy of
-known size), read from profiles/; null when the kernel sources changed since.
+Printed: ONE JSON line (rank 0).  Extra objects:
+  roofline      the dominant kernel (gate+up, the largest matrix): average
+                launch duration over K back-to-back launches of that layer alone,
+                timed the same way; against the 8 TB/s HBM peak and against the
+                achievable peak (the best plain streaming read of 4 GiB through
+                qgemv_stream_read); traffic = HBM bytes per launch from rocprofv3
+                FETCH_SIZE / WRITE_SIZE (scaled by a device copy of known size),
+                read from profiles/, null when the kernel sources changed since
+  layers        per-layer us/call, with the streaming read of the same byte
+                count (cache-cold slices) beside it
+  stream_read   the streaming-read measurements
+  variants      W2, W8, W4 at M = 4 and 16, LUT4, outliers, codebooks, W4A8,
+                prefill, unfused baselines on the same layers (sampled rows
+                checked against the oracle first; not part of `value`)
+  skinny_70b    W4 and W2 on the Llama-70B-shaped layers at M = 1, 2, 4, 8, 16
+                on both dot engines (VALU and MFMA): the batch-size crossover
+  cpu_baseline  the plain C float64 oracle on a bounded row sample, one thread
+                and all host cores, CPU model recorded
 
 Profiling helpers (used under rocprofv3):
-  --only LAYER          run only that layer in every step (skips the variants)
-  --no-variants         skip the other variants' measurements
+  --only LAYER          run only that layer in every step (skips the extras)
+  --no-variants         skip the variants and the 70B skinny workload
   --copy-calibration    also time a device copy of known size (for scaling
                         FETCH_SIZE / WRITE_SIZE counters)
   --summarize-trace CSV print per-kernel, per-grid duration statistics of a
@@ -75,14 +83,17 @@ def build_inputs(torch, q, dev):
                            y=torch.empty((M, N), dtype=torch.float16, device=dev),
                            bytes=alg_bytes(N, K)))
     step_bytes = sum(L["bytes"] for L in layers)
-    R = max(2, -(-(1 << 30) // step_bytes))
+    # each layer rotates over its own R copies, R * bytes >= 1 GiB (above the
+    # 256 MB Infinity Cache), so every call -- in a step or timed alone --
+    # reads its weights from HBM
     for L in layers:
-        for _ in range(R - 1):
+        L["R"] = max(2, -(-(1 << 30) // L["bytes"]))
+        for _ in range(L["R"] - 1):
             L["wq"].append(L["wq"][0].clone())
             L["s"].append(L["s"][0].clone())
             L["z"].append(L["z"][0].clone())
     torch.cuda.synchronize()
-    return layers, R, step_bytes
+    return layers, step_bytes
 
 
 def spot_check(q, layers):
@@ -183,6 +194,7 @@ TRAFFIC_FILE = os.path.join(ROOT, "profiles", "gemv_w4a16_gate_up_28672x4096_m1_
 KERNEL_SOURCES = ["gemm_unpack_bit_amd/csrc/gemv_tiles.hip", "gemm_unpack_bit_amd/csrc/dequant.hpp",
                   "gemm_unpack_bit_amd/csrc/common.hpp", "gemm_unpack_bit_amd/csrc/kernels.hpp",
                   "gemm_unpack_bit_amd/csrc/api.cpp"]
+GEMV_KERNELS = ("gemv_tiles_kernel",)
 
 
 def sources_sha256(paths):
@@ -211,7 +223,7 @@ def traffic_from(fetch_csv, write_csv):
             if r["Counter_Name"] != counter:
                 continue
             v = float(r["Counter_Value"])
-            if "gemv_tiles_kernel" in r["Kernel_Name"]:
+            if any(k in r["Kernel_Name"] for k in GEMV_KERNELS):
                 gemv.append(v)
                 names.add((r["Kernel_Name"], r["Grid_Size"], r["Workgroup_Size"]))
             elif "copyBuffer" in r["Kernel_Name"]:
@@ -445,39 +457,151 @@ def measure_variants(torch, q, dev, timer, n):
     return out
 
 
-def cpu_baseline(layers, budget_s=10.0):
-    """The float64 oracle (unpack -> dequantize -> matvec) on the first 1/8 of
-    the rows of every layer, repeated until `budget_s` of wall time."""
+def cpu_model():
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def cpu_baseline(layers, budget_s=8.0):
+    """The plain C oracle (oracle/cref.c: unpack -> dequantize -> float64
+    matvec) on rows [0, N/8) of every layer: single-threaded, then with one
+    thread per host core available to this process, each repeated until
+    about `budget_s` of wall time.  Packing the sample (plain layout) is done
+    once, outside the timed region."""
+    from oracle import cref, formats
+
+    sample = []
+    for L in layers:
+        c, n8 = L["host"], L["N"] // 8
+        packed = (formats.pack_plain(c["codes"][:n8], BITS), formats.pack_plain(c["zeros"][:n8], BITS))
+        sample.append((c, n8, packed, alg_bytes(n8, L["K"])))
+    sample_bytes = sum(sb for *_, sb in sample)
+    cores = len(os.sched_getaffinity(0)) if hasattr(os, "sched_getaffinity") else (os.cpu_count() or 1)
+
+    def timed(threads, budget):
+        reps, t0 = 0, time.perf_counter()
+        while True:
+            for c, n8, packed, _ in sample:
+                cref.gemv_uniform(c["x"], None, c["scales"][:n8], None, BITS, packed=packed, threads=threads)
+            reps += 1
+            el = time.perf_counter() - t0
+            if el >= budget:
+                return reps, el
+
+    r1, e1 = timed(1, budget_s / 2)
+    rn, en = timed(cores, budget_s / 2)
+    step_us = lambda reps, el: el / reps * 8 * 1e6
+    return {
+        "value": round(sample_bytes * rn / en / 1e9, 4),
+        "unit": "GB/s",
+        "cores": int(cores),
+        "kind": "oracle",
+        "sample": f"plain C float64 oracle (oracle/cref.c, OpenMP over rows) on rows [0, N/8) of each of the "
+                  f"4 layers: {rn} passes in {en:.1f} s on {cores} threads, {r1} passes in {e1:.1f} s on one; "
+                  f"extrapolated {step_us(rn, en):.0f} us ({cores} threads) and {step_us(r1, e1):.0f} us "
+                  f"(1 thread) per full 4-layer step",
+        "single_thread_GBps": round(sample_bytes * r1 / e1 / 1e9, 4),
+        "us_per_step": round(step_us(rn, en), 1),
+        "us_per_step_single_thread": round(step_us(r1, e1), 1),
+        "cpu_model": cpu_model(),
+    }
+
+
+# ---------------------------------------------------------------------------
+# achievable peak: a plain streaming read (qgemv_stream_read) of a 4 GiB
+# buffer, the best of a few launch shapes; and reads of each layer's byte
+# count from rotating slices of the same buffer (cache-cold)
+# ---------------------------------------------------------------------------
+READ_SHAPES = [(wg, th) for wg in (256, 512, 1024, 2048, 4096) for th in (256, 512, 1024)]
+
+
+def achievable_peak(torch, q, timer, sizes):
+    GiB = 1 << 30
+    buf = torch.empty(4 * GiB, dtype=torch.uint8, device="cuda")
+    buf.fill_(0x5A)
+    sink = torch.zeros(4, dtype=torch.int32, device="cuda")
+
+    def best_read(nbytes, n):
+        nbytes = nbytes // 16 * 16
+        slices = max(1, (4 * GiB) // nbytes)
+        best = None
+        for wg, th in READ_SHAPES:
+            fn = lambda i, wg=wg, th=th: q.stream_read(buf, sink, nbytes, wg, th, (i % slices) * nbytes)
+            for i in range(2):
+                fn(i)
+            us = timer.region_us(fn, n, host_cost(torch, fn)) / n
+            if best is None or us < best[0]:
+                best = (us, wg, th)
+        return {"bytes": nbytes, "us": round(best[0], 3), "GBps": round(nbytes / best[0] / 1e3, 1),
+                "workgroups": best[1], "threads": best[2]}
+
+    out = {"read_4GiB": best_read(4 * GiB, 3)}
+    out["per_size"] = {name: best_read(nb, 40) for name, nb in sizes.items()}
+    del buf
+    torch.cuda.empty_cache()
+    return out
+
+
+# ---------------------------------------------------------------------------
+# the 70B skinny-GEMM workload: W4 and W2 on the four Llama-70B-shaped layers
+# at M = 1, 2, 4, 8, 16, each on both dot engines (the batch-size crossover)
+# ---------------------------------------------------------------------------
+SKINNY_M = (1, 2, 4, 8, 16)
+
+
+def measure_skinny(torch, q, timer, n):
     from oracle import reference as ref
 
-    try:
-        import threadpoolctl
-
-        info = threadpoolctl.threadpool_info()
-        blas_threads = max([i.get("num_threads", 1) for i in info] or [1])
-    except Exception:  # pragma: no cover
-        blas_threads = os.cpu_count() or 1
-    sample_bytes = 0
-    t0 = time.perf_counter()
-    reps = 0
-    while True:
-        for L in layers:
-            c = L["host"]
-            rows = np.arange(L["N"] // 8)
-            ref.gemv_uniform(c["x"], c["codes"], c["scales"], c["zeros"], rows=rows)
-            sample_bytes += alg_bytes(len(rows), L["K"])
-        reps += 1
-        el = time.perf_counter() - t0
-        if el >= budget_s:
-            break
-    return {
-        "value": round(sample_bytes / el / 1e9, 4),
-        "unit": "GB/s",
-        "cores": int(blas_threads),
-        "kind": "oracle",
-        "sample": f"float64 oracle (numpy) on rows [0, N/8) of each of the 4 layers, {reps} passes in "
-                  f"{el:.1f} s; extrapolated {el / reps * 8 * 1e6:.0f} us per full 4-layer step",
-    }
+    up = lambda a: torch.from_numpy(np.ascontiguousarray(a)).cuda()
+    out = {}
+    for bits in (4, 2):
+        per_m = {M: {"valu": 0.0, "mfma": 0.0, "bytes": 0, "layers": {}} for M in SKINNY_M}
+        for idx, (name, (N, K)) in enumerate(synth.LLAMA_70B_LAYERS.items()):
+            c = synth.uniform_case(synth.seed_for(3, idx), 16, N, K, bits)
+            t0 = dict(wq=q.pack(up(c["codes"]), bits), s=up(c["scales"]), z=q.pack_zeros(up(c["zeros"]), bits))
+            x16 = up(c["x"])
+            rows = np.linspace(0, N - 1, 8).astype(np.int64)
+            y_ref, A = ref.gemv_uniform(c["x"], c["codes"], c["scales"], c["zeros"], rows=rows)
+            for path in (q.PATH_VALU, q.PATH_MFMA):
+                for M in (1, 16):
+                    y = q.uniform(x16[:M], t0["wq"], t0["s"], t0["z"], bits, path).cpu().numpy()
+                    if not ref.within_tolerance(y[:, rows], y_ref[:M], A[:M]).all():
+                        raise SystemExit(f"bench: skinny W{bits} {name} M={M} path={path} outside tolerance")
+            R = max(2, -(-(1 << 30) // alg_bytes(N, K, bits, 0)))
+            copies = [t0] + [{k: a.clone() for k, a in t0.items()} for _ in range(R - 1)]
+            for M in SKINNY_M:
+                x = x16[:M].contiguous()
+                y = torch.empty((M, N), dtype=torch.float16, device="cuda")
+                rec = {}
+                for eng, path in (("valu", q.PATH_VALU), ("mfma", q.PATH_MFMA)):
+                    fn = lambda i, path=path: q.uniform(x, copies[i % R]["wq"], copies[i % R]["s"],
+                                                        copies[i % R]["z"], bits, path, out=y)
+                    for i in range(4):
+                        fn(i)
+                    us = timer.region_us(fn, n, host_cost(torch, fn)) / n
+                    rec[eng] = round(us, 3)
+                    per_m[M][eng] += us
+                nb = alg_bytes(N, K, bits, M)
+                per_m[M]["bytes"] += nb
+                rec["GBps_best"] = round(nb / min(rec["valu"], rec["mfma"]) / 1e3, 1)
+                per_m[M]["layers"][name] = rec
+            del copies, t0
+            torch.cuda.empty_cache()
+        res = {}
+        for M, v in per_m.items():
+            auto = "valu" if M <= 1 else "mfma"  # the engine the library picks (qgemv_uniform, PATH_AUTO)
+            res[f"m{M}"] = {"auto_engine": auto, "us_per_step_valu": round(v["valu"], 3),
+                            "us_per_step_mfma": round(v["mfma"], 3), "bytes": v["bytes"],
+                            "GBps_auto": round(v["bytes"] / v[auto] / 1e3, 1),
+                            "pct_peak_auto": round(v["bytes"] / v[auto] / 1e3 / PEAK_HBM_GBS * 100, 1),
+                            "faster_engine": "valu" if v["valu"] < v["mfma"] else "mfma", "layers": v["layers"]}
+        out[f"w{bits}a16"] = res
+    return out
 
 
 def main():
@@ -509,7 +633,7 @@ def main():
 
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     dev = torch.device("cuda:0")
-    layers, R, step_bytes = build_inputs(torch, q, dev)
+    layers, step_bytes = build_inputs(torch, q, dev)
 
     run = [L for L in layers if args.only in (None, L["name"])]
     if not run:
@@ -519,8 +643,8 @@ def main():
         step_bytes = sum(L["bytes"] for L in run)
 
     def step(i):
-        r = i % R
         for L in run:
+            r = i % L["R"]
             q.w4a16(L["x"], L["wq"][r], L["s"][r], L["z"][r], out=L["y"])
 
     for i in range(args.warmup):
@@ -543,7 +667,7 @@ def main():
     per_layer = {}
     for L in run:
         def one(i, L=L):
-            r = i % R
+            r = i % L["R"]
             q.w4a16(L["x"], L["wq"][r], L["s"][r], L["z"][r], out=L["y"])
 
         us = timer.region_us(one, K, host_cost(torch, one)) / K
@@ -555,6 +679,13 @@ def main():
     dom = max(run, key=lambda L: L["bytes"])
     dom_us = per_layer[dom["name"]]["us_per_call"]
     achieved = dom["bytes"] / dom_us / 1e3
+    peak = None
+    if not args.only:
+        peak = achievable_peak(torch, q, timer, {L["name"]: L["bytes"] for L in run})
+        for L in run:
+            rd = peak["per_size"][L["name"]]
+            per_layer[L["name"]]["stream_read_us"] = rd["us"]
+            per_layer[L["name"]]["vs_stream_read"] = round(rd["us"] / per_layer[L["name"]]["us_per_call"], 3)
 
     out = {
         "metric": METRIC,
@@ -572,7 +703,8 @@ def main():
         "config": {
             "workload": "Llama-3-8B decoder-layer linear GEMVs (qkv 6144x4096, o 4096x4096, gate_up 28672x4096, "
                         "down 4096x14336), W4A16 asymmetric g128, M=1, cache-cold rotated weights",
-            "batch_m": M, "bits": BITS, "group": G, "rotated_copies": R, "step_bytes": step_bytes,
+            "batch_m": M, "bits": BITS, "group": G, "rotated_copies": {L["name"]: L["R"] for L in layers},
+            "step_bytes": step_bytes,
             "us_per_step": round(ms_per_step * 1000, 3), "pct_peak": round(value / PEAK_HBM_GBS * 100, 2),
             "timing": "GPU-time region of back-to-back launches behind a device sleep"
                       + (" (host-bound: numbers unreliable)" if Timer.host_bound else ""),
@@ -590,8 +722,17 @@ def main():
         },
         "layers": per_layer,
     }
+    if peak:
+        ap = peak["read_4GiB"]["GBps"]
+        out["roofline"]["achievable_peak"] = ap
+        out["roofline"]["frac_achievable"] = round(achieved / ap, 4)
+        out["roofline"]["achievable_peak_from"] = (
+            f"qgemv_stream_read of a 4 GiB buffer, best of {len(READ_SHAPES)} launch shapes "
+            f"({peak['read_4GiB']['workgroups']} x {peak['read_4GiB']['threads']})")
+        out["stream_read"] = peak
     if not (args.no_variants or args.only):
         out["variants"] = measure_variants(torch, q, dev, timer, max(20, min(K, 100)))
+        out["skinny_70b"] = measure_skinny(torch, q, timer, max(20, min(K, 60)))
     if not args.no_cpu:
         out["cpu_baseline"] = cpu_baseline(layers)
     print(json.dumps(out), flush=True)
