@@ -114,6 +114,17 @@ __device__ __forceinline__ void reduce_waves(const float* red, int OUT, int WK, 
   }
 }
 
+// i / d for 0 <= i < 2^22 and 1 <= d < 2^22, exact, with inv = 1.0f / d:
+// the float estimate is off by at most one below 2^23, and one correction
+// each way fixes it (a few full-rate VALU ops instead of an integer
+// division sequence).
+__device__ __forceinline__ int div_small(int i, int d, float inv) {
+  int q = (int)((float)i * inv);
+  q -= __mul24(q, d) > i ? 1 : 0;
+  q += __mul24(q + 1, d) <= i ? 1 : 0;
+  return q;
+}
+
 // Workgroup barrier that orders LDS only: each wave waits for its own LDS
 // operations (lgkmcnt 0) and meets the others at s_barrier, while its global
 // loads stay in flight.  __syncthreads() would also wait for every vector

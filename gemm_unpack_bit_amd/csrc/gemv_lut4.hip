@@ -209,7 +209,9 @@ __global__ void __launch_bounds__(512, MT == 1 ? 4 : 2) gemv_lut4_kernel(Lut4Arg
 #pragma unroll
     for (int u = 0; u < 4; ++u) {
       const int i = i0 + u * blockDim.x;
-      const int m = i / X8, k8 = i - m * X8;
+      // row of vector i (MT rows; i >= n16 loads nothing)
+      const int m = MT == 1 ? 0 : (i >= X8 ? 1 : 0);
+      const int k8 = i - m * X8;
       v[u] = bload16(rx, i < n16 && m0 + m < M && k8 < K / 8 ? ((uint32_t)(m0 + m) * K + 8u * k8) * 2u : OOB);
     }
   };

@@ -319,11 +319,14 @@ gemv_tiles_kernel(UniformArgs a) {
   // weights behind them (loads complete in order); the barrier waits for LDS
   // traffic only, leaving the weight stages in flight.
   const int X8 = XK / 8, n16 = XM * X8;
+  const float x8inv = 1.0f / (float)X8;
   auto x_pass = [&](int i0, u4* v) {
 #pragma unroll
     for (int u = 0; u < 4; ++u) {
       const int i = i0 + u * blockDim.x;
-      const int m = i / X8, k8 = i - m * X8;
+      // row of vector i (VALU: MT rows, known here; i >= n16 loads nothing)
+      const int m = MFMA ? div_small(i, X8, x8inv) : (MT == 1 ? 0 : (i >= X8 ? 1 : 0));
+      const int k8 = i - m * X8;
       v[u] = bload16(rx, i < n16 && m0 + m < M && k8 < K / 8 ? ((uint32_t)(m0 + m) * K + 8u * k8) * 2u : OOB);
     }
   };
