@@ -296,6 +296,11 @@ VARIANTS = {
     # W4A8 (int8 activations, padding strategy, int8 matrix cores)
     "w4a8_m1": dict(kind="w4a8", bits=4, m=1),
     "w4a8_m16": dict(kind="w4a8", bits=4, m=16),
+    # W4A8 by the split strategy (fp8 matrix cores) and with asymmetric activations
+    "w4a8_split_m1": dict(kind="w4a8_split", bits=4, m=1),
+    "w4a8_split_m16": dict(kind="w4a8_split", bits=4, m=16),
+    "w4a8_asym_m1": dict(kind="w4a8_asym", bits=4, m=1),
+    "w4a8_asym_m16": dict(kind="w4a8_asym", bits=4, m=16),
     # prefill: the GEMM path at M = 512 (compute-bound; TFLOP/s reported)
     "w4a16_prefill_m512": dict(kind="gemm", bits=4, m=512),
     # unfused baselines: what fusion buys.  fp16 weights (no quantization),
@@ -369,13 +374,16 @@ def variant_layer(torch, q, dev, kind, bits, m, idx, N, K, cb=None):
         b_sp = 4 * rec.size + 4 * ptr.size + 2 * m * K + 4 * m * N
         parts = {"w4a16": (dense, alg_bytes(N, K, 4, m)), "spmv_tilecoo": (sp, b_sp)}
         nbytes = alg_bytes(N, K, 4, m) + 4 * rec.size + 4 * ptr.size
-    elif kind == "w4a8":
+    elif kind in ("w4a8", "w4a8_split", "w4a8_asym"):
         c = synth.uniform_case(seed, m, N, K, bits)
-        ws = torch.zeros(q.w4a8_workspace_bytes(m, K), dtype=torch.uint8, device=dev)
+        fn, wsb, ofn = {"w4a8": (q.w4a8, q.w4a8_workspace_bytes, ref.gemv_w4a8),
+                        "w4a8_split": (q.w4a8_split, q.w4a8_split_workspace_bytes, ref.gemv_w4a8_split),
+                        "w4a8_asym": (q.w4a8_asym, q.w4a8_asym_workspace_bytes, ref.gemv_w4a8_asym)}[kind]
+        ws = torch.zeros(wsb(m, K), dtype=torch.uint8, device=dev)
         t = dict(x=up(c["x"]), wq=q.pack(up(c["codes"]), bits), s=up(c["scales"]),
                  z=q.pack_zeros(up(c["zeros"]), bits))
-        call = lambda t: q.w4a8(t["x"], t["wq"], t["s"], t["z"], ws, out=y)
-        oracle = lambda rows: ref.gemv_w4a8(c["x"], c["codes"], c["scales"], c["zeros"], rows=rows)
+        call = lambda t: fn(t["x"], t["wq"], t["s"], t["z"], ws, out=y)
+        oracle = lambda rows: ofn(c["x"], c["codes"], c["scales"], c["zeros"], rows=rows)
         nbytes = alg_bytes(N, K, bits, m)
     elif kind == "gemm":
         c = synth.uniform_case(seed, m, N, K, bits)
@@ -455,6 +463,28 @@ def measure_variants(torch, q, dev, timer, n):
         out[vname] = {"m": v["m"], "layers": layers, "us_per_step": round(total_us, 3),
                       "GBps": round(total_bytes / total_us / 1e3, 1)}
     return out
+
+
+def profile_variant(torch, q, dev, vname, only, calls):
+    """Run one entry of the variants table (one layer with `only`) `calls`
+    times on cache-cold copies, for counter collection; prints one line."""
+    v = VARIANTS[vname]
+    shapes = synth.LLAMA_70B_LAYERS if v.get("layers") == "70b" else synth.LLAMA3_8B_LAYERS
+    done = []
+    for idx, (name, (N, K)) in enumerate(shapes.items()):
+        if only and name != only:
+            continue
+        t, call, _, _, nbytes, _ = variant_layer(torch, q, dev, v["kind"], v["bits"], v["m"], idx, N, K, v.get("cb"))
+        R = max(2, -(-(1 << 30) // nbytes))
+        copies = [t] + [{k: (a.clone() if k not in ("x", "lut", "cb") else a) for k, a in t.items()}
+                        for _ in range(R - 1)]
+        for i in range(calls):
+            call(copies[i % R])
+        torch.cuda.synchronize()
+        done.append({"layer": name, "N": N, "K": K, "bytes_per_call": nbytes, "calls": calls})
+        del copies, t
+        torch.cuda.empty_cache()
+    print(json.dumps({"profile_variant": vname, "m": v["m"], "layers": done}), flush=True)
 
 
 def cpu_model():
@@ -612,6 +642,9 @@ def main():
     ap.add_argument("--no-cpu", action="store_true", help="skip the cpu_baseline leg")
     ap.add_argument("--no-variants", action="store_true", help="skip the other variants' measurements")
     ap.add_argument("--only", default=None, help="run only this layer (profiling)")
+    ap.add_argument("--variant", default=None,
+                    help="profiling: run only this entry of the variants table (with --only: one layer), "
+                         "--steps calls per layer, and exit")
     ap.add_argument("--copy-calibration", action="store_true")
     ap.add_argument("--summarize-trace", default=None)
     ap.add_argument("--traffic-from", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"), default=None)
@@ -633,6 +666,9 @@ def main():
 
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     dev = torch.device("cuda:0")
+    if args.variant:
+        profile_variant(torch, q, dev, args.variant, args.only, args.steps)
+        return
     layers, step_bytes = build_inputs(torch, q, dev)
 
     run = [L for L in layers if args.only in (None, L["name"])]
