@@ -330,10 +330,10 @@ int qgemv_gemm_uniform(int bits, int M, int N, int K, const uint16_t* x, const u
     return QGEMV_OK;
   }
   qg::UniformArgs a{bits, M, N, K, x, wq, scales, zeros, y};
-  // 128-row blocks (4 activation tiles per wave, half the dequantization per
-  // MFMA) once they still give about 448 workgroups, else 64-row blocks
-  // (sweeps of the 8B layers, M = 128..2048)
-  int mi = (long)((N + 63) / 64) * ((M + 127) / 128) >= 448 ? 4 : 2;
+  // 64-row blocks (half the dequantization per MFMA) once they give at least
+  // 160 workgroups of 256 weight rows, else 32-row blocks (sweeps of the 8B
+  // and 70B layers, M = 128..2048)
+  int mi = (long)((N + 255) / 256) * ((M + 63) / 64) >= 160 ? 4 : 2;
   if (const char* e = tune_env("QGEMV_GEMM_MI")) mi = std::atoi(e);  // tuning override
   return hip_status(qg::launch_gemm_tiles(a, mi, s));
 }

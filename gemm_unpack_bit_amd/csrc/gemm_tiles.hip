@@ -10,14 +10,24 @@
 // wave dequantizes its B fragments in registers straight from global memory
 // and exactly ((q - z) in fp16).  The activations of the block's rows are
 // staged in LDS one quant group (128 k) at a time, double-buffered, and
-// shared by the workgroup.
+// shared by the workgroup; they go straight from global memory into LDS
+// (16-byte buffer loads with an LDS destination), so they occupy no
+// registers on the way.
 //
-// Block: 32 MI activation rows x 64 weight rows (4 tile-rows), 4 waves; wave
-// w owns tile-row w of the block and every activation row of it, so each
-// weight fragment is dequantized once per workgroup (the four waves each read
-// the A fragments from LDS).  Per group a wave runs 8 MI MFMAs into group
-// partials and adds each times the lane's row scale (one rounding per group,
-// as the decode kernels).  Deterministic.
+// Block: 16 NMT activation rows x 256 weight rows (16 tile-rows), 4 waves.
+// Wave w owns tile-rows 4w .. 4w + 3 and every activation row of the block:
+// each weight fragment is dequantized once per workgroup, and each
+// activation fragment read from LDS feeds four MFMAs (one per tile-row), so
+// the LDS reads per MFMA are a quarter of a one-tile-row-per-wave split
+// (which would ask for about twice the LDS bandwidth the matrix cores can
+// use).  Per group a wave runs 16 NMT MFMAs into group partials and adds
+// each times its row's scale (one rounding per group, as the decode
+// kernels).  Deterministic.
+//
+// Block order: workgroups go to the eight XCDs round robin, so consecutive
+// ids are renumbered to give each XCD a contiguous range of blocks, with the
+// activation blocks of one weight slice adjacent: the XCD's L2 serves that
+// slice's weights to all of them.
 #include "common.hpp"
 #include "dequant.hpp"
 #include "kernels.hpp"
@@ -25,18 +35,32 @@
 namespace qg {
 namespace {
 
-constexpr int XROW = 136;  // staged activation row: 128 halves + 8 of padding (bank spread)
+constexpr int NNT = 4;     // tile-rows per wave
+constexpr int NXCD = 8;
 
-template <int BITS, int MI>
-__global__ void __launch_bounds__(256) gemm_tiles_kernel(UniformArgs a) {
-  constexpr int NMI = 2 * MI;  // 16-row activation tiles per wave (all of the block)
+__device__ __forceinline__ h8 cat4(h2 a, h2 b, h2 c, h2 d) {
+  return __builtin_bit_cast(h8, u4{as_u32(a), as_u32(b), as_u32(c), as_u32(d)});
+}
+
+template <int BITS, int NMT>
+__global__ void __launch_bounds__(256, 2) gemm_tiles_kernel(UniformArgs a, int nmb, int nnb) {
   using TR = Uni<BITS>;
   constexpr int PPD = TR::CPD / 2;
   constexpr int ZPW = 32 / BITS;
+  constexpr uint32_t ZMASK = (1u << BITS) - 1u;
   constexpr uint32_t TB = 16u * 128u * BITS / 8;  // tile bytes
-  constexpr int BM = 32 * MI;                     // activation rows per block
-  constexpr int XP = BM * 16 / 256;               // 16-byte staging pieces per thread
-  __shared__ __attribute__((aligned(16))) _Float16 xs[2][BM * XROW];
+  constexpr int BM = 16 * NMT;                    // activation rows per block
+  // staged activations: [buffer][row][16 pieces of 8 halves], piece c of row
+  // r holding k 8 (c ^ (r % 16)) .. + 7 of the group: a row is 256 bytes,
+  // so without the swizzle the 16 rows of an A fragment read would all hit
+  // the same banks
+  __shared__ __attribute__((aligned(16))) _Float16 xs[2][BM * 128];
+
+  // (a workgroup past the last block leaves before any barrier)
+  const int total = nmb * nnb, per = (total + NXCD - 1) / NXCD;
+  const int L = (int)(blockIdx.x % NXCD) * per + (int)(blockIdx.x / NXCD);
+  if (L >= total) return;
+  const int mb = L % nmb, nb = L / nmb;
 
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -45,142 +69,166 @@ __global__ void __launch_bounds__(256) gemm_tiles_kernel(UniformArgs a) {
   const int G = K / 128;
   const int NT = (N + 15) / 16;
   const uint32_t zrow = 4u * ((G * BITS + 31) / 32);
-  const int m0 = blockIdx.y * BM;
-  const int rt = blockIdx.x * 4 + wave;  // this wave's tile-row
+  const int m0 = mb * BM;
+  const int rt0 = nb * 4 * NNT + wave * NNT;  // this wave's first tile-row
   const uint32_t mg = magic1024x2();
+  const uint32_t lw = lane_off<BITS>(lane);
 
   const rsrc_t rw = make_rsrc(a.wq, (uint32_t)NT * G * TB);
   const rsrc_t rz = make_rsrc(a.zeros, (uint32_t)N * zrow);
   const rsrc_t rs = make_rsrc(a.scales, (uint32_t)N * G * 2u);
   const rsrc_t rx = make_rsrc(a.x, (uint32_t)M * K * 2u);
 
-  // activation staging: thread t moves 16-byte pieces t, t + 256, ... of the
-  // block's BM x 128 tile of group g (rows past M read zeros)
-  auto x_load = [&](int g, u4 (&v)[XP]) {
+  // Every load below is unconditional and takes its group (and block-row
+  // step) in the scalar offset: rows past M or N and tile-rows past the last
+  // fall outside their buffer and read zeros; the stage loaded past the last
+  // group is never used.
+  //
+  // activation staging: wave w fills rows 4 (4 j + w) .. + 3 of the block
+  // (j < NMT), one 1 KB load each: lane l writes piece l % 16 of row
+  // 4 (4 j + w) + l / 16, i.e. k 8 ((l % 16) ^ (row % 16)) .. + 7.
+  const int xr0 = 4 * wave + (lane >> 4);  // the lane's row for j = 0 (row % 16 is the same for every j)
+  const uint32_t xbase = ((uint32_t)(m0 + xr0) * K + 8u * (uint32_t)((lane & 15) ^ xr0)) * 2u;
+  auto x_issue = [&](int g, int b) {
 #pragma unroll
-    for (int i = 0; i < XP; ++i) {
-      const int idx = threadIdx.x + 256 * i, r = idx >> 4, c8 = idx & 15;
-      v[i] = bload16(rx, m0 + r < M ? ((uint32_t)(m0 + r) * K + 128u * g + 8u * c8) * 2u : OOB);
-    }
+    for (int j = 0; j < NMT; ++j)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rx, (__attribute__((address_space(3))) void*)&xs[b][(4 * j + wave) * 512],
+                                               16, xbase, 32u * (uint32_t)K * j + 256u * g, 0, 0);
   };
-  auto x_store = [&](int b, const u4 (&v)[XP]) {
-#pragma unroll
-    for (int i = 0; i < XP; ++i) {
-      const int idx = threadIdx.x + 256 * i, r = idx >> 4, c8 = idx & 15;
-      *reinterpret_cast<u4*>(&xs[b][r * XROW + 8 * c8]) = v[i];
-    }
-  };
-  // weights of the wave's tile-row in group g: codes, scale and zero point
+  // the wave's weights in group g: codes, scale and zero point of lane row n
+  // of each of its tile-rows
   struct Wst {
-    uint32_t w[BITS];
-    uint16_t s;
-    uint32_t z;
+    LaneCodes<BITS> c[NNT];
+    uint16_t s[NNT];
+    uint32_t z[NNT];
   };
-  const bool tv = rt < NT;
-  const int row = 16 * rt + n;
-  const bool rv = tv && row < N;
+  const uint32_t soff_n = 2u * (uint32_t)G * n, zoff_n = zrow * n;
   auto w_load = [&](int g, Wst& st) {
-    const uint32_t tb = ((uint32_t)rt * G + g) * TB;
-    if constexpr (BITS == 2) {
-      const u2 v = __builtin_bit_cast(
-          u2, __builtin_amdgcn_raw_buffer_load_b64(rw, tv ? tb + 8u * lane : OOB, 0, CPOL_NT));
-      st.w[0] = v.x;
-      st.w[1] = v.y;
-    } else {
 #pragma unroll
-      for (int h = 0; h < BITS / 4; ++h) {
-        const u4 v = bload16<CPOL_NT>(rw, tv ? tb + 1024u * h + 16u * lane : OOB);
-#pragma unroll
-        for (int e = 0; e < 4; ++e) st.w[4 * h + e] = v[e];
-      }
+    for (int t = 0; t < NNT; ++t) {
+      const uint32_t rt = (uint32_t)(rt0 + t);
+      st.c[t].load(rw, lw, (rt * G + g) * TB);
+      st.s[t] = bload2(rs, soff_n, 32u * G * rt + 2u * g);
+      st.z[t] = bload4(rz, zoff_n, 16u * zrow * rt + 4u * (uint32_t)(g / ZPW));
     }
-    st.s = bload2(rs, rv ? ((uint32_t)row * G + g) * 2u : OOB);
-    st.z = bload4(rz, rv ? (uint32_t)row * zrow + 4u * (uint32_t)(g / ZPW) : OOB);
   };
 
-  f4 acc[NMI];
+  f4 acc[NMT][NNT];
 #pragma unroll
-  for (int i = 0; i < NMI; ++i) acc[i] = f4{0.f, 0.f, 0.f, 0.f};
+  for (int i = 0; i < NMT; ++i)
+#pragma unroll
+    for (int t = 0; t < NNT; ++t) acc[i][t] = f4{0.f, 0.f, 0.f, 0.f};
 
-  // Pipeline, distance 2: group g is computed from LDS buffer g % 2 while
-  // group g + 1 waits in registers (stored to the other buffer after the
-  // compute) and group g + 2 is being loaded; the barrier waits for LDS
-  // traffic only, so those loads stay in flight across it.
-  u4 xv[2][XP];
-  Wst wst[3];
-  x_load(0, xv[0]);
-  w_load(0, wst[0]);
-  x_load(1, xv[1]);  // (with one group: other data in bounds, never used)
-  w_load(1, wst[1]);
-  x_store(0, xv[0]);
-  __syncthreads();
-
-  auto step = [&](int g, int b, u4 (&xnext)[XP], u4 (&xlater)[XP], const Wst& cur, Wst& later) {
-    if (g + 2 < G) {  // (workgroup-uniform)
-      x_load(g + 2, xlater);
-      w_load(g + 2, later);
+  auto compute = [&](int g, int b, const Wst& st) {
+    // B fragments: the (q - z) pairs of the lane's 32 k in each tile-row
+    h2 p[NNT][16];
+    float sc[NNT];
+#pragma unroll
+    for (int t = 0; t < NNT; ++t) {
+      const typename TR::Z zz = TR::zc((st.z[t] >> (BITS * (g % ZPW))) & ZMASK);
+#pragma unroll
+      for (int d = 0; d < BITS; ++d) TR::deq(st.c[t].w[d], mg, zz, p[t] + d * PPD);
+      sc[t] = h2f(st.s[t]);
     }
-    // B fragments: the (q - z) pairs of the lane's 32 k
-    h2 p[16];
-    const typename TR::Z zz = TR::zc((cur.z >> (BITS * (g % ZPW))) & ((1u << BITS) - 1u));
 #pragma unroll
-    for (int d = 0; d < BITS; ++d) TR::deq(cur.w[d], mg, zz, p + d * PPD);
-    const float sc = h2f(cur.s);  // lane l: weight row l % 16
-#pragma unroll
-    for (int i = 0; i < NMI; ++i) {
+    for (int i = 0; i < NMT; ++i) {
       // A fragments: block row 16 i + n, k 32 kq + 8 s .. + 7 of the group
-      const _Float16* xr = &xs[b][(16 * i + n) * XROW + 32 * kq];
-      f4 dd = f4{0.f, 0.f, 0.f, 0.f};
+      const u4* xr = reinterpret_cast<const u4*>(&xs[b][(16 * i + n) * 128]);
+      u4 av[4];
 #pragma unroll
-      for (int s = 0; s < 4; ++s) {
-        const h8 av = __builtin_bit_cast(h8, *reinterpret_cast<const u4*>(xr + 8 * s));
-        const u4 bv = {as_u32(p[4 * s]), as_u32(p[4 * s + 1]), as_u32(p[4 * s + 2]), as_u32(p[4 * s + 3])};
-        dd = __builtin_amdgcn_mfma_f32_16x16x32_f16(av, __builtin_bit_cast(h8, bv), dd, 0, 0, 0);
-      }
+      for (int s = 0; s < 4; ++s) av[s] = xr[(4 * kq + s) ^ n];
+      f4 dd[NNT];
 #pragma unroll
-      for (int r = 0; r < 4; ++r) acc[i][r] = fmaf(sc, dd[r], acc[i][r]);
+      for (int t = 0; t < NNT; ++t) dd[t] = f4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int s = 0; s < 4; ++s)
+#pragma unroll
+        for (int t = 0; t < NNT; ++t)
+          dd[t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(h8, av[s]),
+                                                         cat4(p[t][4 * s], p[t][4 * s + 1], p[t][4 * s + 2],
+                                                              p[t][4 * s + 3]),
+                                                         dd[t], 0, 0, 0);
+#pragma unroll
+      for (int t = 0; t < NNT; ++t)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) acc[i][t][r] = fmaf(sc[t], dd[t][r], acc[i][t][r]);
     }
-    if (g + 1 < G) x_store(b ^ 1, xnext);
-    lds_barrier();  // group g + 1 staged; every wave is done with buffer b
   };
-  // six groups per iteration so the register stages are named statically
-  for (int g = 0; g < G; g += 6) {
-    step(g, 0, xv[1], xv[0], wst[0], wst[2]);
-    if (g + 1 < G) step(g + 1, 1, xv[0], xv[1], wst[1], wst[0]);
-    if (g + 2 < G) step(g + 2, 0, xv[1], xv[0], wst[2], wst[1]);
-    if (g + 3 < G) step(g + 3, 1, xv[0], xv[1], wst[0], wst[2]);
-    if (g + 4 < G) step(g + 4, 0, xv[1], xv[0], wst[1], wst[0]);
-    if (g + 5 < G) step(g + 5, 1, xv[0], xv[1], wst[2], wst[1]);
+
+  // Pipeline: group g is computed from LDS buffer g % 2 and register stage
+  // g % 2.  At the start of a step the activations of group g + 1 go into the
+  // other buffer (every wave is past group g - 1, its last reader), then the
+  // weights of group g + 1 into the other register stage; at its end the
+  // wave waits for its activation loads only (loads complete in order), and
+  // the barrier for every wave's.  Loads past the last group read zeros.
+  // WLOADS: the vector memory instructions of one w_load.
+  constexpr int WLOADS = NNT * ((BITS == 8 ? 2 : 1) + 2);
+  static_assert(WLOADS < 64, "vmcnt range");
+  constexpr int VMW = (WLOADS & 15) | (0x7 << 4) | (0xF << 8) | ((WLOADS >> 4) << 14);  // s_waitcnt vmcnt(WLOADS)
+  Wst wst[2];
+  x_issue(0, 0);
+  __builtin_amdgcn_sched_barrier(0);
+  w_load(0, wst[0]);
+  __builtin_amdgcn_sched_barrier(0);
+  __builtin_amdgcn_s_waitcnt(VMW);
+  lds_barrier();
+
+  // (the scheduling barriers keep the loads at the start of the step, in
+  // this order, where the compiler would sink them to the end to save
+  // registers)
+  auto step = [&](int g, int b, const Wst& cur, Wst& next) {
+    x_issue(g + 1, b ^ 1);
+    __builtin_amdgcn_sched_barrier(0);
+    w_load(g + 1, next);
+    __builtin_amdgcn_sched_barrier(0);
+    compute(g, b, cur);
+    __builtin_amdgcn_s_waitcnt(VMW);  // this wave's activation loads of group g + 1
+    lds_barrier();
+  };
+  // two groups per iteration so the register stages are named statically
+  for (int g = 0; g < G; g += 2) {
+    step(g, 0, wst[0], wst[1]);
+    if (g + 1 < G) step(g + 1, 1, wst[1], wst[0]);
   }
 
   // lane l holds D[row 4 (l / 16) + r][weight row l % 16] of each 16 x 16 tile
 #pragma unroll
-  for (int i = 0; i < NMI; ++i)
+  for (int i = 0; i < NMT; ++i)
 #pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const int m = m0 + 16 * i + 4 * kq + r;
-      if (m < M && row < N) a.y[(size_t)m * N + row] = f2h(acc[i][r]);
-    }
+    for (int t = 0; t < NNT; ++t)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int m = m0 + 16 * i + 4 * kq + r;
+        const int row = 16 * (rt0 + t) + n;
+        if (m < M && row < N) a.y[(size_t)m * N + row] = f2h(acc[i][t][r]);
+      }
 }
 
 }  // namespace
 
-template <int MI>
-hipError_t launch_mi(const UniformArgs& a, hipStream_t s) {
+template <int BITS, int NMT>
+hipError_t launch_bm(const UniformArgs& a, hipStream_t s) {
   const int NT = (a.N + 15) / 16;
-  const dim3 grid((NT + 3) / 4, (a.M + 32 * MI - 1) / (32 * MI)), block(256);
-  switch (a.bits) {
-    case 2: hipLaunchKernelGGL((gemm_tiles_kernel<2, MI>), grid, block, 0, s, a); break;
-    case 4: hipLaunchKernelGGL((gemm_tiles_kernel<4, MI>), grid, block, 0, s, a); break;
-    case 8: hipLaunchKernelGGL((gemm_tiles_kernel<8, MI>), grid, block, 0, s, a); break;
-    default: return hipErrorInvalidValue;
-  }
+  const int nmb = (a.M + 16 * NMT - 1) / (16 * NMT);
+  const int nnb = (NT + 4 * NNT - 1) / (4 * NNT);
+  const long total = (long)nmb * nnb;
+  const long grid = (total + NXCD - 1) / NXCD * NXCD;
+  if (grid > 0x7FFFFFFFL) return hipErrorInvalidValue;
+  hipLaunchKernelGGL((gemm_tiles_kernel<BITS, NMT>), dim3((unsigned)grid), dim3(256), 0, s, a, nmb, nnb);
   return hipGetLastError();
 }
 
+// mi: 16-row activation tiles per block (2: 32-row blocks, 4: 64-row
+// blocks).  8-bit weights take 32-row blocks either way: two register
+// stages of their codes and the partials of 64 rows do not fit the 256
+// registers of two waves per SIMD.
 hipError_t launch_gemm_tiles(const UniformArgs& a, int mi, hipStream_t s) {
-  if (mi == 2) return launch_mi<2>(a, s);
-  if (mi == 4) return launch_mi<4>(a, s);
+  if (mi != 2 && mi != 4) return hipErrorInvalidValue;
+  switch (a.bits) {
+    case 2: return mi == 4 ? launch_bm<2, 4>(a, s) : launch_bm<2, 2>(a, s);
+    case 4: return mi == 4 ? launch_bm<4, 4>(a, s) : launch_bm<4, 2>(a, s);
+    case 8: return launch_bm<8, 2>(a, s);
+  }
   return hipErrorInvalidValue;
 }
 

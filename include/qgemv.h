@@ -60,7 +60,7 @@
  *                                       the stationary kernel with wk waves
  *   QGEMV_DENSE_CFG="tpw,s,wk"          qgemv_gemv_f16
  *   QGEMV_GEMM_KERNEL=1, QGEMV_GEMM_MI  qgemv_gemm_uniform: the GEMM at any M; its
- *                                       block rows (2 or 4 MFMA tiles per wave)
+ *                                       block rows (2 or 4 16-row MFMA tiles)
  *   QGEMV_W4A8_WK, QGEMV_W4A8_TR        qgemv_w4a8: waves and tile-rows (1, 2) per
  *                                       workgroup
  */
@@ -438,8 +438,8 @@ int qgemv_w4a8_noalloc(int M, int N, int K, const uint16_t *x, const uint32_t *w
  * M >= 1 with M*K*2 and M*N*2 below 2^31, N >= 1, K a positive multiple of
  * 128 (QGEMV_ERR_SHAPE); alignment and overlap rules as qgemv_uniform.
  * Up to 64 rows: the decode kernel on each 16-row slice of x; beyond: a
- * GEMM on the matrix cores, 64 x 64 output blocks, fp32 accumulation with
- * one scale per group.  Asynchronous, deterministic.
+ * GEMM on the matrix cores, 32- or 64-row x 256-column output blocks, fp32
+ * accumulation with one scale per group.  Asynchronous, deterministic.
  * ------------------------------------------------------------------------ */
 int qgemv_gemm_uniform(int bits, int M, int N, int K, const uint16_t *x, const uint32_t *wq,
                        const uint16_t *scales, const uint32_t *zeros, uint16_t *y,
