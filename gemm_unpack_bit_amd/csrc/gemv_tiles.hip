@@ -104,11 +104,11 @@ constexpr int max_threads(int ng) { return ng == 1 ? 1024 : 512; }
 // zeros: those rows of the product are never stored.
 // SP: also add the Tile-COO fp16 outliers of the workgroup's rows (outlier
 // variant): see sparse_compute below.
-// PLDS (one tile-row of one-group chunks): the workgroup's 16 rows of scales
-// and of packed zero points are two contiguous blocks; they are staged in LDS
-// with coalesced 16-byte loads, so a chunk costs one weight load per lane
-// instead of three (per-lane scale and zero loads touch 16 rows' cache lines
-// for every 1 KB of codes).
+// PLDS: the workgroup's 16 TPW rows of scales and of packed zero points are
+// two contiguous blocks; they are staged in LDS with coalesced 16-byte loads,
+// so a chunk costs one weight load per lane and tile instead of three
+// (per-lane scale and zero loads touch 16 rows' cache lines for every 1 KB
+// of codes).
 template <int BITS, bool MFMA, int MT, int NG, int D, int TPW, bool SAL, bool XLDS, bool SP, bool PLDS>
 __global__ void __launch_bounds__(max_threads(NG)) __attribute__((amdgpu_waves_per_eu(waves_per_simd(NG))))
 gemv_tiles_kernel(UniformArgs a) {
@@ -124,9 +124,8 @@ gemv_tiles_kernel(UniformArgs a) {
   static_assert(!DEEP || (XLDS && NG == 1), "the deep chunk ring keeps no activations in registers");
   static_assert(ZPW % NG == 0, "a chunk's zero points share one word");
 
-  static_assert(!PLDS || (TPW == 1 && NG == 1), "staged quant params: one tile-row, one-group chunks");
   // LDS: [staged activations: XM x K halves, XLDS only] [staged scales and
-  // zero points of the tile-row, PLDS only] then the per-wave partials: VALU
+  // zero points of the TPW tile-rows, PLDS only] then the per-wave partials: VALU
   // [WK][TPW][MT][16] floats, MFMA [WK][TPW][64] float4
   extern __shared__ __attribute__((aligned(16))) float smem[];
 
@@ -154,8 +153,8 @@ gemv_tiles_kernel(UniformArgs a) {
   const int XK = K + 32;
   const int XM = MFMA ? min(M, 16) : MT;  // staged activation rows
   char* const pbase = reinterpret_cast<char*>(smem) + (XLDS ? (size_t)XM * XK * 2 : 0);
-  const uint32_t psb = PLDS ? (32u * G + 15u) & ~15u : 0u;  // 16 rows x G scales, 16-byte padded
-  const uint32_t pzb = PLDS ? 16u * zrow : 0u;                // 16 rows of packed zero points
+  const uint32_t psb = PLDS ? (32u * TPW * G + 15u) & ~15u : 0u;  // 16 TPW rows x G scales, 16-byte padded
+  const uint32_t pzb = PLDS ? 16u * TPW * zrow : 0u;                // 16 TPW rows of packed zero points
   const uint16_t* ps = reinterpret_cast<const uint16_t*>(pbase);
   const uint32_t* pz = reinterpret_cast<const uint32_t*>(pbase + psb);
   float* red = reinterpret_cast<float*>(pbase + psb + pzb);
@@ -265,8 +264,8 @@ gemv_tiles_kernel(UniformArgs a) {
         // a condition would become a branch inside the pipelined loop
         const bool gin = gc0 + j < G;
         const int g = min(gc0 + j, G - 1);
-        const uint16_t sv = ps[n * G + g];
-        const uint32_t zv = pz[n * (int)(zrow / 4) + g / ZPW];
+        const uint16_t sv = ps[(16 * t + n) * G + g];
+        const uint32_t zv = pz[(16 * t + n) * (int)(zrow / 4) + g / ZPW];
         sj = gin ? sv : (uint16_t)0;
         zw = gin ? zv : 0u;
       }
@@ -331,8 +330,8 @@ gemv_tiles_kernel(UniformArgs a) {
     }
   };
   u4 xfirst[XLDS ? 4 : 1];
-  // quant params of the tile-row: scale vectors [0, psb / 16), then zero
-  // point vectors; rows past N read zeros
+  // quant params of the TPW tile-rows: scale vectors [0, psb / 16), then
+  // zero point vectors; rows past N read zeros
   const int np16 = (int)((psb + pzb) / 16);
   auto p_pass = [&](int i) -> u4 {
     const uint32_t sv = psb / 16u;
@@ -522,7 +521,7 @@ gemv_tiles_kernel(UniformArgs a) {
 #pragma unroll
     for (int t = 0; t < D - 1; ++t) load_stage(t, c, ring[t]);
     load_x(c, 0);
-    if constexpr (XLDS || SP) stage_x();
+    if constexpr (XLDS || PLDS || SP) stage_x();
     sparse_issue();
     for (; c < NC; c += WK) {
 #pragma unroll
@@ -645,11 +644,11 @@ hipError_t launch_k(const UniformArgs& a, dim3 grid, dim3 block, size_t lds, hip
   return hipGetLastError();
 }
 
-// staged quant params of one tile-row (PLDS): 16 rows of G fp16 scales,
-// 16-byte padded, then 16 rows of packed zero points
-size_t params_lds_bytes(int bits, int K) {
+// staged quant params of tpw tile-rows (PLDS): 16 tpw rows of G fp16 scales,
+// 16-byte padded, then 16 tpw rows of packed zero points
+size_t params_lds_bytes(int bits, int K, int tpw) {
   const size_t G = K / 128;
-  return (32 * G + 15) / 16 * 16 + 16 * 4 * ((G * bits + 31) / 32);
+  return (32 * tpw * G + 15) / 16 * 16 + 16 * tpw * 4 * ((G * bits + 31) / 32);
 }
 
 template <int BITS, bool MFMA, int MT, int NG, int D, int TPW, bool XL, bool SP>
@@ -660,6 +659,15 @@ hipError_t launch_p(const UniformArgs& a, bool sal, bool plds, dim3 grid, dim3 b
     return plds ? launch_k<BITS, MFMA, MT, NG, D, TPW, true, XL, SP, true>(a, grid, block, lds, s)
                 : launch_k<BITS, MFMA, MT, NG, D, TPW, true, XL, SP, false>(a, grid, block, lds, s);
   } else {
+    // Staged quant params with several tile-rows: on the matrix-core engine
+    // (sweeps of the 8B and 70B layers: 6-17% faster at M = 4..16; on the
+    // VALU engine at M = 1 its several-group chunks already take one scale
+    // load per tile, and staging measured up to 20% slower), and where the
+    // kernel still fits its registers (8 tile-rows of one-group chunks or of
+    // 2-bit codes spill).
+    constexpr bool PLDS_OK = MFMA && !(TPW == 8 && (NG == 1 || BITS == 2));
+    if constexpr (PLDS_OK)
+      if (sal && plds) return launch_k<BITS, MFMA, MT, NG, D, TPW, true, XL, SP, true>(a, grid, block, lds, s);
     return sal ? launch_k<BITS, MFMA, MT, NG, D, TPW, true, XL, SP, false>(a, grid, block, lds, s)
                : launch_k<BITS, MFMA, MT, NG, D, TPW, false, XL, SP, false>(a, grid, block, lds, s);
   }
@@ -685,11 +693,12 @@ hipError_t launch_t(const UniformArgs& a, const TileCfg& c, hipStream_t s) {
     // (the buffer bounds check drops a 16-byte load that straddles the end of
     // an array, so both arrays must end on a 16-byte boundary: N % 8 == 0 does)
     const size_t G = a.K / 128, zbytes = (size_t)a.N * 4 * ((G * BITS + 31) / 32);
-    const bool plds = TPW == 1 && NG == 1 && reinterpret_cast<uintptr_t>(a.scales) % 16 == 0 &&
-                      reinterpret_cast<uintptr_t>(a.zeros) % 16 == 0 && (size_t)a.N * G * 2 % 16 == 0 &&
-                      zbytes % 16 == 0;
-    const size_t lds = (xlds ? xl : 0) + (plds ? params_lds_bytes(BITS, a.K) : 0) + red +
-                       (SP ? sparse_lds_bytes(MFMA, MT, c.wk, TPW, a.K, a.M) : 0);
+    bool plds = reinterpret_cast<uintptr_t>(a.scales) % 16 == 0 && reinterpret_cast<uintptr_t>(a.zeros) % 16 == 0 &&
+                (size_t)a.N * G * 2 % 16 == 0 && zbytes % 16 == 0;
+    if (const char* e = tune_env("QGEMV_PLDS")) plds = plds && e[0] == '1';  // tuning override
+    const size_t rest = (xlds ? xl : 0) + red + (SP ? sparse_lds_bytes(MFMA, MT, c.wk, TPW, a.K, a.M) : 0);
+    if (rest + params_lds_bytes(BITS, a.K, TPW) > LDS_ALL) plds = false;  // (long K: stage nothing)
+    const size_t lds = rest + (plds ? params_lds_bytes(BITS, a.K, TPW) : 0);
     if (lds > LDS_ALL) return hipErrorInvalidValue;
     // chunk scales in one load: whole chunks and a 2*NG-byte aligned base
     const bool sal = (a.K / 128) % NG == 0 && reinterpret_cast<uintptr_t>(a.scales) % (2 * NG) == 0;
@@ -750,16 +759,17 @@ hipError_t launch_b(const UniformArgs& a, const TileCfg& c, hipStream_t s) {
 
 // Launch shape per engine and layer shape, fitted to full sweeps on MI355X
 // over the Llama-3-8B / 70B decode layers (cache-cold weights, W2/W4/W8,
-// M = 1..16; within 2% of the per-shape best in total):
+// M = 1..16; within 2-3% of the per-shape best in total):
 //  * VALU (batch 1): one tile-row per workgroup with staged quant params and
 //    one-group chunks -- 16 waves for long K, 4 when the grid is already wide,
 //    a 4-deep chunk ring for the shortest K -- except the widest layers and
 //    4-bit layers of 384-512 tile-rows, which take two tile-rows and
 //    four-group chunks;
-//  * MFMA (batch >= 2): one tile-row for narrow layers; more tile-rows per
-//    workgroup as the batch and the width grow (longer reuse of each staged
-//    activation fragment), 8 tile-rows with half chunks for the widest 4-bit
-//    layers at M >= 8.
+//  * MFMA (batch >= 2), 2- and 4-bit codes: one tile-row for narrow layers
+//    (at most 256 tile-rows); otherwise 2 or 4 tile-rows of one-group chunks
+//    with staged quant params (16 waves up to M = 4, fewer as the batch
+//    grows), and 8 tile-rows with half chunks for the widest 4-bit layers at
+//    M >= 9.  8-bit codes keep the earlier fit (several-group chunks).
 TileCfg pick_tiles(int bits, int M, int N, int K, bool mfma) {
   TileCfg c;
   c.mfma = mfma;
@@ -778,24 +788,46 @@ TileCfg pick_tiles(int bits, int M, int N, int K, bool mfma) {
       const int wk = G >= 96 ? 16 : (nt >= 1024 ? 4 : 8);
       set(1, wk, wk <= 8 && (nt <= 256 || nt >= 1024) ? 4 : 3);
     }
-  } else if (M >= 8 && nt >= 1536 && bits != 2) {
-    if (bits == 4) set(8, 8, 1);        // half chunks keep 8 tile-rows of stages in registers
-    else if (M >= 9) set(8, 8, 0);
-    else set(4, 4, 0);
+  } else if (nt <= 256) {  // narrow layers: one tile-row per workgroup
+    if (M <= 2) set(1, 16, 3);
+    else if (M <= 4) set(1, G >= 96 ? 8 : 16, 3);
+    else set(1, M <= 8 ? 8 : 4, 3);
+  } else if (bits == 8) {
+    if (M >= 8 && nt >= 1536) {
+      if (M >= 9) set(8, 8, 0);
+      else set(4, 4, 0);
+    } else if (M <= 2) {
+      if (nt >= 2048 || G >= 128) set(2, 8, 0);
+      else set(1, nt >= 1024 ? 4 : 8, 3);
+    } else if (M <= 4) {
+      if (nt >= 1536) set(4, nt >= 2048 ? 4 : 8, 0);
+      else if (G >= 128) set(2, 8, 0);
+      else set(1, 8, 3);
+    } else {
+      if (nt >= 1536) set(4, 4, 0);
+      else if (nt >= 640) set(4, 8, 0);
+      else set(2, M <= 8 ? 8 : 4, 0);
+    }
   } else if (M <= 2) {
-    if (nt >= 2048 || (nt > 256 && G >= 128)) set(2, 8, 0);
-    else if (nt <= 256) set(1, 16, 3);
+    if (nt >= 2048 || G >= 128) set(2, 16, 3);
+    else if (bits == 2 && nt >= 1024) set(2, 8, 3);
     else set(1, nt >= 1024 ? 4 : 8, 3);
   } else if (M <= 4) {
-    if (nt >= 1536) set(4, nt >= 2048 ? 4 : 8, 0);
-    else if (nt <= 256) set(1, G >= 96 ? 8 : 16, 3);
-    else if (G >= 128) set(2, 8, 0);
-    else set(1, 8, 3);
+    if (nt >= 2048) set(bits == 4 ? 2 : 4, 8, 3);
+    else if (nt >= 1024) set(4, 8, 3);
+    else if (nt >= 640 && G < 128) set(4, 16, 3);
+    else set(2, 16, 3);
   } else {
-    if (nt <= 256) set(1, M <= 8 ? 8 : 4, 3);
-    else if (nt >= 1536) set(4, 4, 0);
-    else if (nt >= 640) set(4, 8, 0);
-    else set(2, M <= 8 ? 8 : 4, 0);
+    if (nt >= 1536) {
+      if (bits == 4 && M >= 9) set(8, nt >= 2048 ? 4 : 8, 1);  // half chunks keep 8 tile-rows of stages in registers
+      else set(4, 8, 3);
+    } else if (nt >= 640 && G < 128) {
+      set(4, 16, 3);
+    } else if (G >= 128) {
+      set(2, M >= 9 ? 8 : 16, 3);
+    } else {
+      set(2, 8, 3);
+    }
   }
   // never more waves than chunks of groups
   const int ng = chunk_groups(bits, mfma, c.mt, c.v);
@@ -833,6 +865,7 @@ TileCfg pick_outlier(int M, int N, int K, bool mfma) {
   } else {
     c.tpw = 2;
     c.v = 0;
+    if (c.wk > 8) c.wk = 8;  // (several-group chunks: at most 512 threads)
     const int nc = (K / 128 + chunk_groups(4, mfma, c.mt, 0) - 1) / chunk_groups(4, mfma, c.mt, 0);
     if (c.wk > nc) c.wk = nc;
   }
@@ -841,7 +874,7 @@ TileCfg pick_outlier(int M, int N, int K, bool mfma) {
   // rows staged leaves less room for per-wave scratch
   size_t xl = xlds_bytes(mfma, c.mt, M, K);
   if (xl > XLDS_MAX) xl = 0;
-  const size_t fixed = xl + params_lds_bytes(4, K);
+  const size_t fixed = xl + params_lds_bytes(4, K, c.tpw);
   while (c.wk > 1 && fixed + tiles_lds_bytes(mfma, c.mt, c.tpw, c.wk) +
                              sparse_lds_bytes(mfma, c.mt, c.wk, c.tpw, K, M) > LDS_ALL)
     c.wk = (c.wk + 1) / 2;

@@ -52,6 +52,11 @@
  * otherwise makes itself.  A forced shape the kernels do not support is
  * rejected with an error status (or, for QGEMV_CODEBOOK_GEN_KS, ignored).
  *   QGEMV_TILE_CFG="tpw,wk[,mt[,v]]"   uniform kernels (qgemv_w2a16 .. qgemv_uniform)
+ *   QGEMV_XLDS_MAX=bytes                uniform kernels: largest activation block
+ *                                       staged in LDS (above it, per-wave loads)
+ *   QGEMV_PLDS=0|1                      uniform kernels: stage the workgroup's scales
+ *                                       and zero points in LDS (1, the default where
+ *                                       aligned and they fit) or load them per lane
  *   QGEMV_OUTLIER_CFG="tpw,wk[,mt[,v]]" qgemv_outlier's fused kernel
  *   QGEMV_OUTLIER_FORM=fused|split      qgemv_outlier: one kernel, or dense then sparse
  *   QGEMV_LUT4_CFG="tpw,ng,wk[,mt[,d]]" qgemv_lut4
