@@ -119,39 +119,42 @@ __global__ void __launch_bounds__(256, 2) gemm_tiles_kernel(UniformArgs a, int n
 #pragma unroll
     for (int t = 0; t < NNT; ++t) acc[i][t] = f4{0.f, 0.f, 0.f, 0.f};
 
+  // Tile-row-major: the A fragments of every activation tile are read once
+  // (NMT x 4 registers of 16 bytes), then each tile-row's MFMAs run while the
+  // next tile-row's B fragments are dequantized (independent work, so the
+  // VALU and the matrix core overlap inside the wave).
   auto compute = [&](int g, int b, const Wst& st) {
-    // B fragments: the (q - z) pairs of the lane's 32 k in each tile-row
-    h2 p[NNT][16];
-    float sc[NNT];
-#pragma unroll
-    for (int t = 0; t < NNT; ++t) {
-      const typename TR::Z zz = TR::zc((st.z[t] >> (BITS * (g % ZPW))) & ZMASK);
-#pragma unroll
-      for (int d = 0; d < BITS; ++d) TR::deq(st.c[t].w[d], mg, zz, p[t] + d * PPD);
-      sc[t] = h2f(st.s[t]);
-    }
+    u4 av[NMT][4];
 #pragma unroll
     for (int i = 0; i < NMT; ++i) {
-      // A fragments: block row 16 i + n, k 32 kq + 8 s .. + 7 of the group
+      // block row 16 i + n, k 32 kq + 8 s .. + 7 of the group
       const u4* xr = reinterpret_cast<const u4*>(&xs[b][(16 * i + n) * 128]);
-      u4 av[4];
 #pragma unroll
-      for (int s = 0; s < 4; ++s) av[s] = xr[(4 * kq + s) ^ n];
-      f4 dd[NNT];
+      for (int s = 0; s < 4; ++s) av[i][s] = xr[(4 * kq + s) ^ n];
+    }
+    // B fragments: the (q - z) pairs of the lane's 32 k in tile-row t
+    auto deq_t = [&](int t, h2 (&p)[16]) {
+      const typename TR::Z zz = TR::zc((st.z[t] >> (BITS * (g % ZPW))) & ZMASK);
 #pragma unroll
-      for (int t = 0; t < NNT; ++t) dd[t] = f4{0.f, 0.f, 0.f, 0.f};
+      for (int d = 0; d < BITS; ++d) TR::deq(st.c[t].w[d], mg, zz, p + d * PPD);
+    };
+    h2 p[2][16];
+    deq_t(0, p[0]);
 #pragma unroll
-      for (int s = 0; s < 4; ++s)
+    for (int t = 0; t < NNT; ++t) {
+      if (t + 1 < NNT) deq_t(t + 1, p[(t + 1) & 1]);
+      const float sc = h2f(st.s[t]);
 #pragma unroll
-        for (int t = 0; t < NNT; ++t)
-          dd[t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(h8, av[s]),
-                                                         cat4(p[t][4 * s], p[t][4 * s + 1], p[t][4 * s + 2],
-                                                              p[t][4 * s + 3]),
-                                                         dd[t], 0, 0, 0);
+      for (int i = 0; i < NMT; ++i) {
+        f4 dd = f4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int t = 0; t < NNT; ++t)
+        for (int s = 0; s < 4; ++s)
+          dd = __builtin_amdgcn_mfma_f32_16x16x32_f16(
+              __builtin_bit_cast(h8, av[i][s]),
+              cat4(p[t & 1][4 * s], p[t & 1][4 * s + 1], p[t & 1][4 * s + 2], p[t & 1][4 * s + 3]), dd, 0, 0, 0);
 #pragma unroll
-        for (int r = 0; r < 4; ++r) acc[i][t][r] = fmaf(sc[t], dd[t][r], acc[i][t][r]);
+        for (int r = 0; r < 4; ++r) acc[i][t][r] = fmaf(sc, dd[r], acc[i][t][r]);
+      }
     }
   };
 
