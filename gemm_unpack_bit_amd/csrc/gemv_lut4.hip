@@ -74,10 +74,14 @@ __device__ __forceinline__ void load_block_scales(rsrc_t r, uint32_t rowoff, uin
 // 4*NG-byte aligned, so a chunk's scales are one load.
 template <int MT, int NG, int TPW, int D, bool SAL>
 __global__ void __launch_bounds__(512, MT == 1 ? 4 : 2) gemv_lut4_kernel(Lut4Args a) {
-  // LDS: [pair table 64 KB][activations MT x XK halves, 8-k runs permuted
-  // (xarea_bytes)][partials]
+  // LDS: the pair table (64 KB, static: its address is a compile-time
+  // constant, so a lookup's address is the v_perm result itself, with no add
+  // of a dynamic base), then dynamic [activations MT x XK halves, 8-k runs
+  // permuted (xarea_bytes)][partials]
+  __shared__ __attribute__((aligned(16))) uint32_t ltab[TABLE_BYTES / 4];
   extern __shared__ __attribute__((aligned(16))) uint32_t lsm[];
   char* const lds = reinterpret_cast<char*>(lsm);
+  const char* const tab = reinterpret_cast<const char*>(ltab);
 
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -94,7 +98,7 @@ __global__ void __launch_bounds__(512, MT == 1 ? 4 : 2) gemv_lut4_kernel(Lut4Arg
   int rt0 = blockIdx.x * TPW;             // the current row group's first tile-row
   const int XK = K + 32;  // staged row stride (halves): K, then a zero pad
   const uint32_t lane4 = 4u * lane;
-  float* const red = reinterpret_cast<float*>(lds + TABLE_BYTES + xarea_bytes(MT, K));
+  float* const red = reinterpret_cast<float*>(lds + xarea_bytes(MT, K));
 
   const rsrc_t rw = make_rsrc(a.wq, (uint32_t)NT * G * 1024u);
   const rsrc_t ra = make_rsrc(a.absmax, (uint32_t)N * KB * 2u);
@@ -142,7 +146,7 @@ __global__ void __launch_bounds__(512, MT == 1 ? 4 : 2) gemv_lut4_kernel(Lut4Arg
     const int gc0 = c * NG;
     const bool xin = (SAL && TPW >= 2) || gc0 + j < G;
     const uint32_t xk = xin ? 128u * (gc0 + j) + 32u * kq : (uint32_t)K;
-    return *reinterpret_cast<const u4*>(lds + TABLE_BYTES + ((uint32_t)m * XK + xk + 8u * d) * 2u);
+    return *reinterpret_cast<const u4*>(lds + ((uint32_t)m * XK + xk + 8u * d) * 2u);
   };
   auto load_xc = [&](int c) {
     if constexpr (XREG) {
@@ -171,7 +175,7 @@ __global__ void __launch_bounds__(512, MT == 1 ? 4 : 2) gemv_lut4_kernel(Lut4Arg
         for (int jb = 0; jb < 4; ++jb) {
           // (code byte jb << 8) | 4 lane: entry jb of this lane's table copy
           const uint32_t addr = __builtin_amdgcn_perm(w, lane4, 0x0C0C0000u | ((4u + jb) << 8));
-          const h2 pr = as_h2(*reinterpret_cast<const uint32_t*>(lds + addr));
+          const h2 pr = as_h2(*reinterpret_cast<const uint32_t*>(tab + addr));
 #pragma unroll
           for (int m = 0; m < MT; ++m) part[m] = dot2(pr, as_h2(xv[m][jb]), part[m]);
         }
@@ -221,20 +225,20 @@ __global__ void __launch_bounds__(512, MT == 1 ? 4 : 2) gemv_lut4_kernel(Lut4Arg
 
   // pair table: 256 pair values, then 64 lane-major copies of each
   {
-    uint32_t* pairs = reinterpret_cast<uint32_t*>(lds + TABLE_BYTES);  // scratch in the x area
+    uint32_t* pairs = reinterpret_cast<uint32_t*>(lds);  // scratch in the x area
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       const int e = threadIdx.x + j * (int)blockDim.x;
       if (e < 256) pairs[e] = tlo[j] | (thi[j] << 16);
     }
     lds_barrier();
-    for (int i = threadIdx.x; i < 256 * TABLE_COPIES; i += blockDim.x) lsm[i] = pairs[i / TABLE_COPIES];
+    for (int i = threadIdx.x; i < 256 * TABLE_COPIES; i += blockDim.x) ltab[i] = pairs[i / TABLE_COPIES];
     lds_barrier();  // (LDS only: the weight prefetch stays in flight)
   }
   // activations of rows m0 .. m0 + MT - 1; each 8-k run stored as
   // (x0,x2),(x4,x6),(x1,x3),(x5,x7); the 4 pad runs per row read zeros
   {
-    u4* xw = reinterpret_cast<u4*>(lds + TABLE_BYTES);
+    u4* xw = reinterpret_cast<u4*>(lds);
     auto put = [&](int i0, const u4* v) {
 #pragma unroll
       for (int u = 0; u < 4; ++u) {
@@ -325,16 +329,18 @@ hipError_t launch_l(const Lut4Args& a, const Lut4Cfg& c, hipStream_t s) {
   const int NRG = (NT + TPW - 1) / TPW;
   const int MY = (a.M + MT - 1) / MT;
   const dim3 block(64 * c.wk);
-  const size_t lds = lut4_lds_bytes(MT, TPW, c.wk, a.K);
-  if (lds > LUT4_LDS_LIMIT) return hipErrorInvalidValue;
+  const size_t total = lut4_lds_bytes(MT, TPW, c.wk, a.K);
+  if (total > LUT4_LDS_LIMIT) return hipErrorInvalidValue;
+  const size_t lds = total - TABLE_BYTES;  // dynamic part (the table is static)
   const bool sal = (a.K / 128) % NG == 0 && reinterpret_cast<uintptr_t>(a.absmax) % (4 * NG) == 0;
-  static bool raised = false;  // every launch needs more than the default 64 KB of dynamic LDS
+  static bool raised = false;  // one-time opt-in to the whole LDS beside the static table
   if (!raised) {
+    const int dmax = (int)(LUT4_LDS_LIMIT - TABLE_BYTES);
     hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&gemv_lut4_kernel<MT, NG, TPW, D, true>),
-                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)LUT4_LDS_LIMIT);
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, dmax);
     if (e == hipSuccess)
       e = hipFuncSetAttribute(reinterpret_cast<const void*>(&gemv_lut4_kernel<MT, NG, TPW, D, false>),
-                              hipFuncAttributeMaxDynamicSharedMemorySize, (int)LUT4_LDS_LIMIT);
+                              hipFuncAttributeMaxDynamicSharedMemorySize, dmax);
     if (e != hipSuccess) return e;
     raised = true;
   }
