@@ -656,8 +656,8 @@ def main():
         traffic_from(*args.traffic_from)
         return
     if args.gpus != 1:
-        print(f"bench.py: this build runs on one GPU; --gpus {args.gpus} is not supported "
-              "(the GEMV is measured on one GPU's share; see the sharding notes)", file=sys.stderr)
+        print(f"bench.py: the GEMV runs and is measured on one GPU; --gpus {args.gpus} is not supported "
+              "(a multi-GPU run would give each GPU its own slice of the weight rows)", file=sys.stderr)
         sys.exit(2)
 
     import torch

@@ -120,9 +120,9 @@ __global__ void __launch_bounds__(256, 2) gemm_tiles_kernel(UniformArgs a, int n
     for (int t = 0; t < NNT; ++t) acc[i][t] = f4{0.f, 0.f, 0.f, 0.f};
 
   // Tile-row-major: the A fragments of every activation tile are read once
-  // (NMT x 4 registers of 16 bytes), then each tile-row's MFMAs run while the
-  // next tile-row's B fragments are dequantized (independent work, so the
-  // VALU and the matrix core overlap inside the wave).
+  // (NMT x 4 registers of 16 bytes), then each tile-row's MFMAs are issued
+  // interleaved with the dequantization of the next tile-row (independent
+  // work the compiler schedules between the MFMAs).
   auto compute = [&](int g, int b, const Wst& st) {
     u4 av[NMT][4];
 #pragma unroll
