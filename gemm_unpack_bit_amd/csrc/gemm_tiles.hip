@@ -42,7 +42,11 @@ __device__ __forceinline__ h8 cat4(h2 a, h2 b, h2 c, h2 d) {
   return __builtin_bit_cast(h8, u4{as_u32(a), as_u32(b), as_u32(c), as_u32(d)});
 }
 
-template <int BITS, int NMT>
+// QS: K/128 is a multiple of 8 and the quant params are 16-byte aligned: a
+// block's 256 rows of scales and zero-point words are staged in LDS 8 groups
+// at a time with coalesced 16-byte loads (one row per thread), instead of
+// per-lane loads that touch 16 rows' cache lines for each tile-row and group.
+template <int BITS, int NMT, bool QS>
 __global__ void __launch_bounds__(256, 2) gemm_tiles_kernel(UniformArgs a, int nmb, int nnb) {
   using TR = Uni<BITS>;
   constexpr int PPD = TR::CPD / 2;
@@ -55,6 +59,11 @@ __global__ void __launch_bounds__(256, 2) gemm_tiles_kernel(UniformArgs a, int n
   // so without the swizzle the 16 rows of an A fragment read would all hit
   // the same banks
   __shared__ __attribute__((aligned(16))) _Float16 xs[2][BM * 128];
+  // staged quant params of an 8-group chunk, two buffers: [row][8] scales and
+  // [row][ZW] zero-point words (the words holding the chunk's groups)
+  constexpr int ZW = BITS == 8 ? 2 : 1;
+  __shared__ __attribute__((aligned(16))) uint16_t qs_s[2][QS ? 256 * 8 : 8];
+  __shared__ __attribute__((aligned(16))) uint32_t qs_z[2][QS ? 256 * ZW : 4];
 
   // (a workgroup past the last block leaves before any barrier)
   const int total = nmb * nnb, per = (total + NXCD - 1) / NXCD;
@@ -99,8 +108,8 @@ __global__ void __launch_bounds__(256, 2) gemm_tiles_kernel(UniformArgs a, int n
   // of each of its tile-rows
   struct Wst {
     LaneCodes<BITS> c[NNT];
-    uint16_t s[NNT];
-    uint32_t z[NNT];
+    uint16_t s[QS ? 1 : NNT];
+    uint32_t z[QS ? 1 : NNT];
   };
   const uint32_t soff_n = 2u * (uint32_t)G * n, zoff_n = zrow * n;
   auto w_load = [&](int g, Wst& st) {
@@ -108,9 +117,25 @@ __global__ void __launch_bounds__(256, 2) gemm_tiles_kernel(UniformArgs a, int n
     for (int t = 0; t < NNT; ++t) {
       const uint32_t rt = (uint32_t)(rt0 + t);
       st.c[t].load(rw, lw, (rt * G + g) * TB);
-      st.s[t] = bload2(rs, soff_n, 32u * G * rt + 2u * g);
-      st.z[t] = bload4(rz, zoff_n, 16u * zrow * rt + 4u * (uint32_t)(g / ZPW));
+      if constexpr (!QS) {
+        st.s[t] = bload2(rs, soff_n, 32u * G * rt + 2u * g);
+        st.z[t] = bload4(rz, zoff_n, 16u * zrow * rt + 4u * (uint32_t)(g / ZPW));
+      }
     }
+  };
+  // the staged quant params of chunk c (groups 8c .. 8c + 7): thread t loads
+  // block row t's 8 scales and its zero-point words
+  const uint32_t qrow = (uint32_t)nb * 256u + threadIdx.x;
+  const uint32_t qs_v = qrow * (uint32_t)G * 2u, qz_v = qrow * zrow;
+  auto q_issue = [&](int c, u4& sv, uint32_t (&zv)[ZW]) {
+    sv = bload16(rs, qs_v, 16u * (uint32_t)c);
+#pragma unroll
+    for (int e = 0; e < ZW; ++e) zv[e] = bload4(rz, qz_v, 4u * ((uint32_t)(8 * c) / ZPW + e));
+  };
+  auto q_store = [&](int b, const u4& sv, const uint32_t (&zv)[ZW]) {
+    *reinterpret_cast<u4*>(&qs_s[b][threadIdx.x * 8]) = sv;
+#pragma unroll
+    for (int e = 0; e < ZW; ++e) qs_z[b][threadIdx.x * ZW + e] = zv[e];
   };
 
   f4 acc[NMT][NNT];
@@ -133,8 +158,19 @@ __global__ void __launch_bounds__(256, 2) gemm_tiles_kernel(UniformArgs a, int n
       for (int s = 0; s < 4; ++s) av[i][s] = xr[(4 * kq + s) ^ n];
     }
     // B fragments: the (q - z) pairs of the lane's 32 k in tile-row t
+    // quant params of tile-row t in group g: the lane's row, from the staged
+    // chunk or from the stage's own loads
+    const int cb = (g >> 3) & 1, lr0 = 16 * wave * NNT + n;
+    auto zword = [&](int t) -> uint32_t {
+      if constexpr (QS) return qs_z[cb][(lr0 + 16 * t) * ZW + ((g & 7) * BITS) / 32];
+      else return st.z[t];
+    };
+    auto scale = [&](int t) -> uint16_t {
+      if constexpr (QS) return qs_s[cb][(lr0 + 16 * t) * 8 + (g & 7)];
+      else return st.s[t];
+    };
     auto deq_t = [&](int t, h2 (&p)[16]) {
-      const typename TR::Z zz = TR::zc((st.z[t] >> (BITS * (g % ZPW))) & ZMASK);
+      const typename TR::Z zz = TR::zc((zword(t) >> (BITS * (g % ZPW))) & ZMASK);
 #pragma unroll
       for (int d = 0; d < BITS; ++d) TR::deq(st.c[t].w[d], mg, zz, p + d * PPD);
     };
@@ -143,7 +179,7 @@ __global__ void __launch_bounds__(256, 2) gemm_tiles_kernel(UniformArgs a, int n
 #pragma unroll
     for (int t = 0; t < NNT; ++t) {
       if (t + 1 < NNT) deq_t(t + 1, p[(t + 1) & 1]);
-      const float sc = h2f(st.s[t]);
+      const float sc = h2f(scale(t));
 #pragma unroll
       for (int i = 0; i < NMT; ++i) {
         f4 dd = f4{0.f, 0.f, 0.f, 0.f};
@@ -165,10 +201,16 @@ __global__ void __launch_bounds__(256, 2) gemm_tiles_kernel(UniformArgs a, int n
   // wave waits for its activation loads only (loads complete in order), and
   // the barrier for every wave's.  Loads past the last group read zeros.
   // WLOADS: the vector memory instructions of one w_load.
-  constexpr int WLOADS = NNT * ((BITS == 8 ? 2 : 1) + 2);
+  constexpr int WLOADS = NNT * ((BITS == 8 ? 2 : 1) + (QS ? 0 : 2));
   static_assert(WLOADS < 64, "vmcnt range");
   constexpr int VMW = (WLOADS & 15) | (0x7 << 4) | (0xF << 8) | ((WLOADS >> 4) << 14);  // s_waitcnt vmcnt(WLOADS)
   Wst wst[2];
+  u4 qsv;
+  uint32_t qzv[ZW];
+  if constexpr (QS) {
+    q_issue(0, qsv, qzv);
+    q_store(0, qsv, qzv);  // (waits for these loads only)
+  }
   x_issue(0, 0);
   __builtin_amdgcn_sched_barrier(0);
   w_load(0, wst[0]);
@@ -180,11 +222,20 @@ __global__ void __launch_bounds__(256, 2) gemm_tiles_kernel(UniformArgs a, int n
   // this order, where the compiler would sink them to the end to save
   // registers)
   auto step = [&](int g, int b, const Wst& cur, Wst& next) {
+    // the last step of a chunk also stages the next chunk's quant params
+    // (into the other buffer: its previous chunk was last read a whole
+    // chunk ago, before several barriers)
+    const bool qnext = QS && (g & 7) == 7 && g + 1 < G;
+    if constexpr (QS)
+      if (qnext) q_issue((g + 1) >> 3, qsv, qzv);
+    __builtin_amdgcn_sched_barrier(0);
     x_issue(g + 1, b ^ 1);
     __builtin_amdgcn_sched_barrier(0);
     w_load(g + 1, next);
     __builtin_amdgcn_sched_barrier(0);
     compute(g, b, cur);
+    if constexpr (QS)
+      if (qnext) q_store(((g + 1) >> 3) & 1, qsv, qzv);
     __builtin_amdgcn_s_waitcnt(VMW);  // this wave's activation loads of group g + 1
     lds_barrier();
   };
@@ -217,7 +268,11 @@ hipError_t launch_bm(const UniformArgs& a, hipStream_t s) {
   const long total = (long)nmb * nnb;
   const long grid = (total + NXCD - 1) / NXCD * NXCD;
   if (grid > 0x7FFFFFFFL) return hipErrorInvalidValue;
-  hipLaunchKernelGGL((gemm_tiles_kernel<BITS, NMT>), dim3((unsigned)grid), dim3(256), 0, s, a, nmb, nnb);
+  const bool qs = (a.K / 128) % 8 == 0 && reinterpret_cast<uintptr_t>(a.scales) % 16 == 0;
+  if (qs)
+    hipLaunchKernelGGL((gemm_tiles_kernel<BITS, NMT, true>), dim3((unsigned)grid), dim3(256), 0, s, a, nmb, nnb);
+  else
+    hipLaunchKernelGGL((gemm_tiles_kernel<BITS, NMT, false>), dim3((unsigned)grid), dim3(256), 0, s, a, nmb, nnb);
   return hipGetLastError();
 }
 
