@@ -4,6 +4,7 @@
 
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <cstdint>
 #include <cstdio>
 #include <cstdlib>
@@ -81,6 +82,52 @@ qg::TileCfg tile_cfg(int bits, int M, int N, int K, bool mfma) {
     if (n >= 4) c.v = v;
   }
   return c;
+}
+
+// Workgroups of the prefill GEMM with 16 mi-row x 64 nt-column blocks.
+long gemm_wgs(int M, int N, int mi, int nt) {
+  return (long)((M + 16 * mi - 1) / (16 * mi)) * (((N + 15) / 16 + 4 * nt - 1) / (4 * nt));
+}
+
+// Prefill GEMM block (sweeps of the 8B and 70B layers, M = 32..2048, W2 /
+// W4 / W8): the largest block that still gives enough workgroups to keep
+// two per CU busy.  64 x 256 needs at least 320 (a narrower grid leaves one
+// wave per SIMD with its loads, dequantization and MFMAs in series), 64 x
+// 128 at least 384, else 32 x 128 (the most workgroups).  64-row blocks
+// only where they pad M by at most a quarter more than 32-row blocks.
+// 8-bit weights have 32-row blocks only: 32 x 256 from 512 workgroups, else
+// 32 x 128.
+void gemm_block(int bits, int M, int N, int& mi, int& nt) {
+  const bool m64 = (M + 63) / 64 * 64 * 4 <= (M + 31) / 32 * 32 * 5;
+  if (bits == 8) {
+    mi = 2;
+    nt = gemm_wgs(M, N, 2, 4) >= 512 ? 4 : 2;
+  } else if (m64 && gemm_wgs(M, N, 4, 4) >= 320) {
+    mi = 4, nt = 4;
+  } else if (m64 && gemm_wgs(M, N, 4, 2) >= 384) {
+    mi = 4, nt = 2;
+  } else {
+    mi = 2, nt = 2;
+  }
+}
+
+// 17..64 rows: the 16-row slices of the decode kernel or the GEMM.  A slice
+// streams the weights once, in about max(0.15 G + 2, weight bytes / 3.5
+// TB/s) us (its per-workgroup group loop or HBM); the GEMM's few workgroups
+// each run the whole K loop, about 0.7 G us per 512 workgroups.  Fitted to
+// the 8B layers at M = 32..80 (W4): the slices win on the long-K down layer
+// up to M = 64, the GEMM on the wide gate+up layer from M = 32 and on the
+// 4096-k layers at M = 64.
+bool prefer_slices(int bits, int M, int N, int K) {
+  if (M <= QGEMV_MAX_M) return true;
+  if (M > QGEMV_GEMM_SLICE_MAX_M) return false;
+  const int G = K / QGEMV_GROUP;
+  const double wbytes = (double)N * K * bits / 8;
+  const double t16 = std::max(0.15 * G + 2.0, wbytes / 3.5e6);
+  int mi, nt;
+  gemm_block(bits, M, N, mi, nt);
+  const double rounds = std::max(1.0, (double)gemm_wgs(M, N, mi, nt) / 512.0);
+  return (double)((M + QGEMV_MAX_M - 1) / QGEMV_MAX_M) * t16 <= 0.7 * G * rounds;
 }
 
 // Tuning override of the LUT4 launch shape: QGEMV_LUT4_CFG="tpw,ng,wk[,mt[,d]]".
@@ -315,12 +362,14 @@ int qgemv_gemm_uniform(int bits, int M, int N, int K, const uint16_t* x, const u
       overlaps(y, ybytes, zeros, words(bits, QGEMV_LAYOUT_PLAIN, N, G) * 4))
     return QGEMV_ERR_VALUE;
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
-  // Batch-size policy (sweeps of the 8B layers, W4): up to 64 rows, the
-  // decode kernel on each 16-row slice (it streams the weights once per
-  // slice, but its grid fills the chip: 101 vs 287 us per step at M = 32);
-  // from 65 rows on, the GEMM (faster from about M = 128).
-  const char* force = tune_env("QGEMV_GEMM_KERNEL");  // tuning override: "1" = the GEMM at any M
-  if (M <= QGEMV_GEMM_SLICE_MAX_M && !(force && force[0] == '1')) {
+  // Batch-size policy.  Up to 16 rows, the decode kernel; up to 64 rows,
+  // whichever of the decode kernel on each 16-row slice and the GEMM the
+  // cost model below prefers; beyond, the GEMM.
+  const char* force = tune_env("QGEMV_GEMM_KERNEL");  // tuning override: "1" GEMM, "2" slices (M <= 64)
+  const bool slices = force && force[0] == '1'   ? false
+                      : force && force[0] == '2' ? M <= QGEMV_GEMM_SLICE_MAX_M
+                                                 : prefer_slices(bits, M, N, K);
+  if (slices) {
     for (int m0 = 0; m0 < M; m0 += QGEMV_MAX_M) {
       const int mm = M - m0 < QGEMV_MAX_M ? M - m0 : QGEMV_MAX_M;
       qg::UniformArgs a{bits, mm, N, K, x + (size_t)m0 * K, wq, scales, zeros, y + (size_t)m0 * N};
@@ -330,12 +379,11 @@ int qgemv_gemm_uniform(int bits, int M, int N, int K, const uint16_t* x, const u
     return QGEMV_OK;
   }
   qg::UniformArgs a{bits, M, N, K, x, wq, scales, zeros, y};
-  // 64-row blocks (half the dequantization per MFMA) once they give at least
-  // 160 workgroups of 256 weight rows, else 32-row blocks (sweeps of the 8B
-  // and 70B layers, M = 128..2048)
-  int mi = (long)((N + 255) / 256) * ((M + 63) / 64) >= 160 ? 4 : 2;
-  if (const char* e = tune_env("QGEMV_GEMM_MI")) mi = std::atoi(e);  // tuning override
-  return hip_status(qg::launch_gemm_tiles(a, mi, s));
+  int mi, nt;
+  gemm_block(bits, M, N, mi, nt);
+  if (const char* e = tune_env("QGEMV_GEMM_MI")) mi = std::atoi(e);  // tuning overrides
+  if (const char* e = tune_env("QGEMV_GEMM_NT")) nt = std::atoi(e);
+  return hip_status(qg::launch_gemm_tiles(a, mi, nt, s));
 }
 
 int qgemv_w2a16(int M, int N, int K, const uint16_t* x, const uint32_t* wq, const uint16_t* scales,

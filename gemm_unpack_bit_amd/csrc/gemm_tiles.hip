@@ -14,15 +14,18 @@
 // (16-byte buffer loads with an LDS destination), so they occupy no
 // registers on the way.
 //
-// Block: 16 NMT activation rows x 256 weight rows (16 tile-rows), 4 waves.
-// Wave w owns tile-rows 4w .. 4w + 3 and every activation row of the block:
-// each weight fragment is dequantized once per workgroup, and each
-// activation fragment read from LDS feeds four MFMAs (one per tile-row), so
-// the LDS reads per MFMA are a quarter of a one-tile-row-per-wave split
-// (which would ask for about twice the LDS bandwidth the matrix cores can
-// use).  Per group a wave runs 16 NMT MFMAs into group partials and adds
-// each times its row's scale (one rounding per group, as the decode
-// kernels).  Deterministic.
+// Block: 16 NMT activation rows x 64 NNT weight rows (4 NNT tile-rows), 4
+// waves.  Wave w owns tile-rows NNT w .. NNT w + NNT - 1 and every
+// activation row of the block: each weight fragment is dequantized once per
+// workgroup, and each activation fragment read from LDS feeds NNT MFMAs (one
+// per tile-row).  NNT = 4 (256 weight rows) quarters the LDS reads per MFMA
+// of a one-tile-row-per-wave split (which would ask for about twice the LDS
+// bandwidth the matrix cores can use); NNT = 2 (128 weight rows) doubles
+// the workgroups of a narrow layer, where 256-row blocks leave one wave per
+// SIMD with nothing to overlap its loads, dequantization and MFMAs.  Per
+// group a wave runs 4 NMT NNT MFMAs into group partials and adds each times
+// its row's scale (one rounding per group, as the decode kernels).
+// Deterministic.
 //
 // Block order: workgroups go to the eight XCDs round robin, so consecutive
 // ids are renumbered to give each XCD a contiguous range of blocks, with the
@@ -35,7 +38,6 @@
 namespace qg {
 namespace {
 
-constexpr int NNT = 4;     // tile-rows per wave
 constexpr int NXCD = 8;
 
 __device__ __forceinline__ h8 cat4(h2 a, h2 b, h2 c, h2 d) {
@@ -43,10 +45,11 @@ __device__ __forceinline__ h8 cat4(h2 a, h2 b, h2 c, h2 d) {
 }
 
 // QS: K/128 is a multiple of 8 and the quant params are 16-byte aligned: a
-// block's 256 rows of scales and zero-point words are staged in LDS 8 groups
-// at a time with coalesced 16-byte loads (one row per thread), instead of
-// per-lane loads that touch 16 rows' cache lines for each tile-row and group.
-template <int BITS, int NMT, bool QS>
+// block's 64 NNT rows of scales and zero-point words are staged in LDS 8
+// groups at a time with coalesced 16-byte loads (one row per thread of the
+// first NNT waves), instead of per-lane loads that touch 16 rows' cache
+// lines for each tile-row and group.
+template <int BITS, int NMT, int NNT, bool QS>
 __global__ void __launch_bounds__(256, 2) gemm_tiles_kernel(UniformArgs a, int nmb, int nnb) {
   using TR = Uni<BITS>;
   constexpr int PPD = TR::CPD / 2;
@@ -62,8 +65,9 @@ __global__ void __launch_bounds__(256, 2) gemm_tiles_kernel(UniformArgs a, int n
   // staged quant params of an 8-group chunk, two buffers: [row][8] scales and
   // [row][ZW] zero-point words (the words holding the chunk's groups)
   constexpr int ZW = BITS == 8 ? 2 : 1;
-  __shared__ __attribute__((aligned(16))) uint16_t qs_s[2][QS ? 256 * 8 : 8];
-  __shared__ __attribute__((aligned(16))) uint32_t qs_z[2][QS ? 256 * ZW : 4];
+  constexpr int BN = 64 * NNT;  // weight rows per block
+  __shared__ __attribute__((aligned(16))) uint16_t qs_s[2][QS ? BN * 8 : 8];
+  __shared__ __attribute__((aligned(16))) uint32_t qs_z[2][QS ? BN * ZW : 4];
 
   // (a workgroup past the last block leaves before any barrier)
   const int total = nmb * nnb, per = (total + NXCD - 1) / NXCD;
@@ -123,16 +127,20 @@ __global__ void __launch_bounds__(256, 2) gemm_tiles_kernel(UniformArgs a, int n
       }
     }
   };
-  // the staged quant params of chunk c (groups 8c .. 8c + 7): thread t loads
-  // block row t's 8 scales and its zero-point words
-  const uint32_t qrow = (uint32_t)nb * 256u + threadIdx.x;
+  // the staged quant params of chunk c (groups 8c .. 8c + 7): thread t < BN
+  // loads block row t's 8 scales and its zero-point words (with NNT = 2 the
+  // last two waves stage nothing: a wave-uniform branch)
+  const bool qwave = wave < NNT;
+  const uint32_t qrow = (uint32_t)nb * BN + threadIdx.x;
   const uint32_t qs_v = qrow * (uint32_t)G * 2u, qz_v = qrow * zrow;
   auto q_issue = [&](int c, u4& sv, uint32_t (&zv)[ZW]) {
+    if (!qwave) return;
     sv = bload16(rs, qs_v, 16u * (uint32_t)c);
 #pragma unroll
     for (int e = 0; e < ZW; ++e) zv[e] = bload4(rz, qz_v, 4u * ((uint32_t)(8 * c) / ZPW + e));
   };
   auto q_store = [&](int b, const u4& sv, const uint32_t (&zv)[ZW]) {
+    if (!qwave) return;
     *reinterpret_cast<u4*>(&qs_s[b][threadIdx.x * 8]) = sv;
 #pragma unroll
     for (int e = 0; e < ZW; ++e) qs_z[b][threadIdx.x * ZW + e] = zv[e];
@@ -260,7 +268,7 @@ __global__ void __launch_bounds__(256, 2) gemm_tiles_kernel(UniformArgs a, int n
 
 }  // namespace
 
-template <int BITS, int NMT>
+template <int BITS, int NMT, int NNT>
 hipError_t launch_bm(const UniformArgs& a, hipStream_t s) {
   const int NT = (a.N + 15) / 16;
   const int nmb = (a.M + 16 * NMT - 1) / (16 * NMT);
@@ -270,22 +278,30 @@ hipError_t launch_bm(const UniformArgs& a, hipStream_t s) {
   if (grid > 0x7FFFFFFFL) return hipErrorInvalidValue;
   const bool qs = (a.K / 128) % 8 == 0 && reinterpret_cast<uintptr_t>(a.scales) % 16 == 0;
   if (qs)
-    hipLaunchKernelGGL((gemm_tiles_kernel<BITS, NMT, true>), dim3((unsigned)grid), dim3(256), 0, s, a, nmb, nnb);
+    hipLaunchKernelGGL((gemm_tiles_kernel<BITS, NMT, NNT, true>), dim3((unsigned)grid), dim3(256), 0, s, a, nmb, nnb);
   else
-    hipLaunchKernelGGL((gemm_tiles_kernel<BITS, NMT, false>), dim3((unsigned)grid), dim3(256), 0, s, a, nmb, nnb);
+    hipLaunchKernelGGL((gemm_tiles_kernel<BITS, NMT, NNT, false>), dim3((unsigned)grid), dim3(256), 0, s, a, nmb, nnb);
   return hipGetLastError();
 }
 
 // mi: 16-row activation tiles per block (2: 32-row blocks, 4: 64-row
+// blocks); nt: tile-rows per wave (4: 256-column blocks, 2: 128-column
 // blocks).  8-bit weights take 32-row blocks either way: two register
 // stages of their codes and the partials of 64 rows do not fit the 256
 // registers of two waves per SIMD.
-hipError_t launch_gemm_tiles(const UniformArgs& a, int mi, hipStream_t s) {
-  if (mi != 2 && mi != 4) return hipErrorInvalidValue;
+template <int BITS>
+hipError_t launch_bits(const UniformArgs& a, int mi, int nt, hipStream_t s) {
+  if constexpr (BITS != 8)
+    if (mi == 4) return nt == 4 ? launch_bm<BITS, 4, 4>(a, s) : launch_bm<BITS, 4, 2>(a, s);
+  return nt == 4 ? launch_bm<BITS, 2, 4>(a, s) : launch_bm<BITS, 2, 2>(a, s);
+}
+
+hipError_t launch_gemm_tiles(const UniformArgs& a, int mi, int nt, hipStream_t s) {
+  if ((mi != 2 && mi != 4) || (nt != 2 && nt != 4)) return hipErrorInvalidValue;
   switch (a.bits) {
-    case 2: return mi == 4 ? launch_bm<2, 4>(a, s) : launch_bm<2, 2>(a, s);
-    case 4: return mi == 4 ? launch_bm<4, 4>(a, s) : launch_bm<4, 2>(a, s);
-    case 8: return launch_bm<8, 2>(a, s);
+    case 2: return launch_bits<2>(a, mi, nt, s);
+    case 4: return launch_bits<4>(a, mi, nt, s);
+    case 8: return launch_bits<8>(a, mi, nt, s);
   }
   return hipErrorInvalidValue;
 }

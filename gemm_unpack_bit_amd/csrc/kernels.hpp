@@ -143,8 +143,9 @@ int w4a8_waves(int N, int K);
 hipError_t launch_gemv_w4a8(const W4A8Args& a, int wk, hipStream_t s);
 
 // Prefill-size GEMM (gemm_tiles.hip): the uniform format at any M on the
-// matrix cores, blocks of 32 mi activation rows (mi = 2, 4) x 64 weight rows
-hipError_t launch_gemm_tiles(const UniformArgs& a, int mi, hipStream_t s);
+// matrix cores, blocks of 16 mi activation rows (mi = 2, 4) x 64 nt weight
+// rows (nt = 2, 4)
+hipError_t launch_gemm_tiles(const UniformArgs& a, int mi, int nt, hipStream_t s);
 
 // Unfused baselines (unfused.hip): eager dequantization to fp16 W [N, K]
 // row-major (uniform b-bit: bits, wq, scales, zeros; LUT4: wq, absmax, lut),

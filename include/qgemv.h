@@ -64,8 +64,13 @@
  *   QGEMV_CODEBOOK_GEN_KS=k             qgemv_codebook_gen: k K parts, or -wk for
  *                                       the stationary kernel with wk waves
  *   QGEMV_DENSE_CFG="tpw,s,wk"          qgemv_gemv_f16
- *   QGEMV_GEMM_KERNEL=1, QGEMV_GEMM_MI  qgemv_gemm_uniform: the GEMM at any M; its
- *                                       block rows (2 or 4 16-row MFMA tiles)
+ *   QGEMV_GEMM_KERNEL=1|2               qgemv_gemm_uniform: the GEMM at any M (1), or
+ *                                       16-row slices of the decode kernel up to
+ *                                       M = 64 (2)
+ *   QGEMV_GEMM_MI, QGEMV_GEMM_NT        qgemv_gemm_uniform's GEMM block: 2 or 4
+ *                                       16-row MFMA tiles of x by 2 or 4 16-row
+ *                                       tile-rows of W per wave (32 or 64 x 128
+ *                                       or 256)
  *   QGEMV_W4A8_WK, QGEMV_W4A8_TR        qgemv_w4a8: waves and tile-rows (1, 2) per
  *                                       workgroup
  */
@@ -442,9 +447,11 @@ int qgemv_w4a8_noalloc(int M, int N, int K, const uint16_t *x, const uint32_t *w
  * Other arguments as qgemv_uniform (bits 2, 4, 8; the same packed weights).
  * M >= 1 with M*K*2 and M*N*2 below 2^31, N >= 1, K a positive multiple of
  * 128 (QGEMV_ERR_SHAPE); alignment and overlap rules as qgemv_uniform.
- * Up to 64 rows: the decode kernel on each 16-row slice of x; beyond: a
- * GEMM on the matrix cores, 32- or 64-row x 256-column output blocks, fp32
- * accumulation with one scale per group.  Asynchronous, deterministic.
+ * Up to 16 rows: the decode kernel; 17 to 64: the decode kernel on each
+ * 16-row slice of x or the GEMM, by a cost model of the two; beyond: a
+ * GEMM on the matrix cores, 32- or 64-row x 128- or 256-column output
+ * blocks, fp32 accumulation with one scale per group.  Asynchronous,
+ * deterministic.
  * ------------------------------------------------------------------------ */
 int qgemv_gemm_uniform(int bits, int M, int N, int K, const uint16_t *x, const uint32_t *wq,
                        const uint16_t *scales, const uint32_t *zeros, uint16_t *y,

@@ -17,15 +17,18 @@ def _case(seed, M, N, K, bits):
     return c, q.pack(dev(c["codes"]), bits), dev(c["scales"]), q.pack_zeros(dev(c["zeros"]), bits)
 
 
-@pytest.mark.parametrize("mi", ["2", "4"])  # activation tiles per wave (64- or 128-row blocks)
+# block shapes: (activation tiles, tile-rows per wave) = 32 or 64 activation
+# rows x 256 or 128 weight rows
+@pytest.mark.parametrize("mi,nt", [("2", "4"), ("4", "4"), ("2", "2"), ("4", "2")])
 @pytest.mark.parametrize("force", ["0", "1"])  # "1": the GEMM kernel also for M <= 64
 @pytest.mark.parametrize("bits", [2, 4, 8])
 @pytest.mark.parametrize("M,N,K", [(1, 16, 128), (17, 70, 384), (64, 300, 2048), (100, 1000, 640), (300, 48, 128),
-                                   (130, 257, 1152)])
-def test_gemm_small_shapes(bits, M, N, K, force, mi, monkeypatch):
-    say("gemm", bits, M, N, K, force, mi)
+                                   (130, 257, 1152), (96, 200, 1024)])
+def test_gemm_small_shapes(bits, M, N, K, force, mi, nt, monkeypatch):
+    say("gemm", bits, M, N, K, force, mi, nt)
     monkeypatch.setenv("QGEMV_GEMM_KERNEL", force)
     monkeypatch.setenv("QGEMV_GEMM_MI", mi)
+    monkeypatch.setenv("QGEMV_GEMM_NT", nt)
     c, wq, s, zq = _case(M * 7 + N + K + bits, M, N, K, bits)
     y = host(q.gemm_uniform(dev(c["x"]), wq, s, zq, bits))
     y_ref, A = ref.gemv_uniform(c["x"], c["codes"], c["scales"], c["zeros"])
@@ -46,7 +49,7 @@ def test_gemm_agrees_with_gemv_and_is_deterministic():
     assert_within(yv, y_ref, A, "gemv")
 
 
-@pytest.mark.parametrize("M,N,K", [(512, 4096, 4096), (200, 4096, 14336)])
+@pytest.mark.parametrize("M,N,K", [(512, 4096, 4096), (200, 4096, 14336), (512, 4096, 14336)])
 def test_gemm_full_size_sampled(M, N, K):
     say("gemm full", M, N, K)
     c, wq, s, zq = _case(6 + M, M, N, K, 4)
