@@ -32,6 +32,9 @@
 //  * Streaming, pipeline, work split and reduction follow the uniform kernel:
 //    branch-free non-temporal tile loads through a D-slot register ring,
 //    permlane quarter sums, LDS wave sums in fixed order (deterministic).
+//  * Block scales: per lane with its codes, or (one batch row, workgroups
+//    that walk several row groups) staged in LDS a row group ahead with
+//    coalesced loads.
 #include <algorithm>
 
 #include "common.hpp"
@@ -73,12 +76,19 @@ __device__ __forceinline__ void load_block_scales(rsrc_t r, uint32_t rowoff, uin
 // rows per workgroup; with one tile-row, D chunks per wave in a ring (D - 1
 // loads ahead).  SAL: K/128 is a multiple of NG and the block scales are
 // 4*NG-byte aligned, so a chunk's scales are one load.
-template <int MT, int NG, int TPW, int D, bool SAL>
+// BS (one tile-row, one-group chunks): a row group's block scales (16 rows
+// x K/64, one contiguous block of the [N, K/64] array) are staged in LDS
+// with coalesced 4-byte loads (at most two per thread), issued a whole row
+// group ahead; per-lane scale loads would touch 16 rows' cache lines for
+// every 1 KB tile of codes.
+template <int MT, int NG, int TPW, int D, bool SAL, bool BS>
 __global__ void __launch_bounds__(MT == 1 ? 1024 : 512, MT == 1 ? 4 : 2) gemv_lut4_kernel(Lut4Args a) {
+  static_assert(!BS || (SAL && NG == 1 && TPW == 1), "staged block scales: one tile-row, one-group chunks");
   // LDS: the pair table (64 KB, static: its address is a compile-time
   // constant, so a lookup's address is the v_perm result itself, with no add
   // of a dynamic base), then dynamic [activations MT x XK halves, 8-k runs
-  // permuted (xarea_bytes)][partials]
+  // permuted (xarea_bytes)][partials][BS: two buffers of 16 rows x SW words
+  // of block-scale pairs]
   __shared__ __attribute__((aligned(16))) uint32_t ltab[TABLE_BYTES / 4];
   extern __shared__ __attribute__((aligned(16))) uint32_t lsm[];
   char* const lds = reinterpret_cast<char*>(lsm);
@@ -100,6 +110,11 @@ __global__ void __launch_bounds__(MT == 1 ? 1024 : 512, MT == 1 ? 4 : 2) gemv_lu
   const int XK = K + 32;  // staged row stride (halves): K, then a zero pad
   const uint32_t lane4 = 4u * lane;
   float* const red = reinterpret_cast<float*>(lds + xarea_bytes(MT, K));
+  // staged block scales (BS): word g of row r holds the scales of group g
+  // (64-blocks 2g, 2g + 1); SW is odd, so the 16 rows of one read fall on
+  // distinct banks
+  const int SW = G | 1;
+  uint32_t* const sbuf = reinterpret_cast<uint32_t*>(lds + xarea_bytes(MT, K) + (size_t)WK * TPW * MT * 64);
 
   const rsrc_t rw = make_rsrc(a.wq, (uint32_t)NT * G * 1024u);
   const rsrc_t ra = make_rsrc(a.absmax, (uint32_t)N * KB * 2u);
@@ -126,6 +141,7 @@ __global__ void __launch_bounds__(MT == 1 ? 1024 : 512, MT == 1 ? 4 : 2) gemv_lu
       const uint32_t sw = __builtin_amdgcn_readfirstlane(ok ? ((uint32_t)rt * G + gc0 + j) * 1024u : 0u);
       st.c[j] = bload16<CPOL_NT>(rw, ok ? 16u * lane : OOB, sw);
     }
+    if constexpr (BS) return;  // block scales come from LDS
     const uint32_t ss = __builtin_amdgcn_readfirstlane(cv ? 4u * gc0 : 0u);
     if constexpr (SAL) {
       load_block_scales<NG>(ra, rv ? row * (uint32_t)KB * 2u : OOB, ss, kq >> 1, st.s);
@@ -160,6 +176,7 @@ __global__ void __launch_bounds__(MT == 1 ? 1024 : 512, MT == 1 ? 4 : 2) gemv_lu
     }
   };
 
+  int sb = 0;  // the staged block-scale buffer of the current row group (BS)
   auto compute = [&](int t, int c, const St& st) {
 #pragma unroll
     for (int j = 0; j < NG; ++j) {
@@ -181,7 +198,14 @@ __global__ void __launch_bounds__(MT == 1 ? 1024 : 512, MT == 1 ? 4 : 2) gemv_lu
           for (int m = 0; m < MT; ++m) part[m] = dot2(pr, as_h2(xv[m][jb]), part[m]);
         }
       }
-      const float sc = h2f(st.s[j]);
+      float sc;
+      if constexpr (BS) {
+        // the lane's 64-block of group c: half kq / 2 of word c of row n
+        const uint32_t wv = sbuf[(sb * 16 + n) * SW + c];
+        sc = h2f((uint16_t)(wv >> (16 * (kq >> 1))));
+      } else {
+        sc = h2f(st.s[j]);
+      }
 #pragma unroll
       for (int m = 0; m < MT; ++m) acc[t][m] = fmaf(sc, part[m], acc[t][m]);
     }
@@ -196,6 +220,33 @@ __global__ void __launch_bounds__(MT == 1 ? 1024 : 512, MT == 1 ? 4 : 2) gemv_lu
     } else {
 #pragma unroll
       for (int k = 0; k + 1 < R; ++k) load_stage(0, wave + k * WK, ring[k]);
+    }
+  };
+  // BS: words i = threadIdx.x + e blockDim.x (e < 2) of tile-row rt's block
+  // scales (16 G words; tile-rows past the last and rows past N read zeros),
+  // and their stores into buffer b (row i / G, word i % G)
+  // (the second word only where the workgroup has fewer threads than words:
+  // a uniform branch; the LDS word offsets are the same for every row group)
+  using BSv = uint32_t[2];
+  const bool bs2 = BS && (int)blockDim.x < 16 * G;
+  int bsoff[2];
+#pragma unroll
+  for (int e = 0; e < 2; ++e) {
+    const int i = threadIdx.x + e * (int)blockDim.x;
+    const int r = i / G;
+    bsoff[e] = BS && i < 16 * G ? r * SW + (i - r * G) : -1;
+  }
+  auto bs_issue = [&](int rt, BSv& v) {
+    if constexpr (BS) {
+      const uint32_t so = __builtin_amdgcn_readfirstlane(rt < NT ? (uint32_t)rt * 64u * (uint32_t)G : 0u);
+      v[0] = bload4(ra, rt < NT && bsoff[0] >= 0 ? 4u * threadIdx.x : OOB, so);
+      if (bs2) v[1] = bload4(ra, rt < NT && bsoff[1] >= 0 ? 4u * (threadIdx.x + blockDim.x) : OOB, so);
+    }
+  };
+  auto bs_store = [&](int b, const BSv& v) {
+    if constexpr (BS) {
+      if (bsoff[0] >= 0) sbuf[b * 16 * SW + bsoff[0]] = v[0];
+      if (bs2 && bsoff[1] >= 0) sbuf[b * 16 * SW + bsoff[1]] = v[1];
     }
   };
   // Start-up loads, in the order they are needed: the table entries, then the
@@ -222,6 +273,8 @@ __global__ void __launch_bounds__(MT == 1 ? 1024 : 512, MT == 1 ? 4 : 2) gemv_lu
   };
   u4 xfirst[4];
   x_pass(threadIdx.x, xfirst);
+  BSv bsfirst;
+  bs_issue(rt0, bsfirst);
   prologue();  // weights in flight while the tables fill
 
   // pair table: 256 pair values, then 64 lane-major copies of each
@@ -256,6 +309,7 @@ __global__ void __launch_bounds__(MT == 1 ? 1024 : 512, MT == 1 ? 4 : 2) gemv_lu
       x_pass(i0, v);
       put(i0, v);
     }
+    bs_store(0, bsfirst);
     lds_barrier();
   }
 
@@ -263,6 +317,8 @@ __global__ void __launch_bounds__(MT == 1 ? 1024 : 512, MT == 1 ? 4 : 2) gemv_lu
   // rg = blockIdx.x, blockIdx.x + gridDim.x, ...  The next group's first
   // chunks are issued before this group's reduction.
   for (int rg = blockIdx.x; rg < NRG; rg += gridDim.x) {
+  BSv bsnext;
+  bs_issue((rg + (int)gridDim.x) * TPW, bsnext);  // the next row group's block scales
 #pragma unroll
   for (int t = 0; t < TPW; ++t)
 #pragma unroll
@@ -308,6 +364,7 @@ __global__ void __launch_bounds__(MT == 1 ? 1024 : 512, MT == 1 ? 4 : 2) gemv_lu
       const float v = quarter_sum(acc[t][m]);
       if (lane < 16) red[((wave * TPW + t) * MT + m) * 16 + lane] = v;
     }
+  bs_store(sb ^ 1, bsnext);  // (its last reader was the group before this one)
   lds_barrier();  // LDS only: the next group's loads stay in flight
   reduce_waves(red, TPW * MT * 16, WK, [&](int e, float sum) {
     const int r = e & 15, m = (e >> 4) % MT, t = (e >> 4) / MT;
@@ -315,6 +372,7 @@ __global__ void __launch_bounds__(MT == 1 ? 1024 : 512, MT == 1 ? 4 : 2) gemv_lu
     if (m0 + m < M && row < N) a.y[(size_t)(m0 + m) * N + row] = f2h(sum);
   });
   lds_barrier();  // the partial area is written again by the next group
+  sb ^= 1;
   }
 }
 
@@ -324,53 +382,93 @@ size_t lut4_lds_bytes(int mt, int tpw, int wk, int K) {
   return TABLE_BYTES + xarea_bytes(mt, K) + (size_t)wk * tpw * mt * 16 * 4;
 }
 
+// staged block scales (BS): two buffers of 16 rows x (G | 1) words
+size_t lut4_bs_bytes(int K) { return 2u * 16u * 4u * (size_t)((K / 128) | 1); }
+
+// kernel per scale mode: 0 per-group scale loads, 1 one aligned load per
+// chunk (SAL), 2 staged block scales (BS)
+template <int MT, int NG, int TPW, int D>
+const void* lut4_kernel(int mode) {
+  if constexpr (NG == 1 && TPW == 1)
+    if (mode == 2) return reinterpret_cast<const void*>(&gemv_lut4_kernel<MT, NG, TPW, D, true, true>);
+  return mode ? reinterpret_cast<const void*>(&gemv_lut4_kernel<MT, NG, TPW, D, true, false>)
+              : reinterpret_cast<const void*>(&gemv_lut4_kernel<MT, NG, TPW, D, false, false>);
+}
+
 template <int MT, int NG, int TPW, int D>
 hipError_t launch_l(const Lut4Args& a, const Lut4Cfg& c, hipStream_t s) {
   const int NT = (a.N + 15) / 16;
   const int NRG = (NT + TPW - 1) / TPW;
   const int MY = (a.M + MT - 1) / MT;
+  const int G = a.K / 128;
   const dim3 block(64 * c.wk);
   const size_t total = lut4_lds_bytes(MT, TPW, c.wk, a.K);
   if (total > LUT4_LDS_LIMIT) return hipErrorInvalidValue;
-  const size_t lds = total - TABLE_BYTES;  // dynamic part (the table is static)
-  const bool sal = (a.K / 128) % NG == 0 && reinterpret_cast<uintptr_t>(a.absmax) % (4 * NG) == 0;
+  const bool sal = G % NG == 0 && reinterpret_cast<uintptr_t>(a.absmax) % (4 * NG) == 0;
   static bool raised = false;  // one-time opt-in to the whole LDS beside the static table
   if (!raised) {
     const int dmax = (int)(LUT4_LDS_LIMIT - TABLE_BYTES);
-    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&gemv_lut4_kernel<MT, NG, TPW, D, true>),
-                                       hipFuncAttributeMaxDynamicSharedMemorySize, dmax);
-    if (e == hipSuccess)
-      e = hipFuncSetAttribute(reinterpret_cast<const void*>(&gemv_lut4_kernel<MT, NG, TPW, D, false>),
-                              hipFuncAttributeMaxDynamicSharedMemorySize, dmax);
-    if (e != hipSuccess) return e;
+    for (int m = 0; m < 3; ++m) {
+      const hipError_t e = hipFuncSetAttribute(lut4_kernel<MT, NG, TPW, D>(m), hipFuncAttributeMaxDynamicSharedMemorySize, dmax);
+      if (e != hipSuccess) return e;
+    }
     raised = true;
   }
   // persistent grid: no more workgroups than are resident at once (each
   // builds its table once and walks row groups).  Residency per CU is asked
-  // once per (alignment, waves, LDS size) and remembered.
-  static int occ[2][17];
-  static size_t occ_lds[2][17];
+  // once per (scale mode, waves, LDS size) and remembered.
+  static int occ[3][17];
+  static size_t occ_lds[3][17];
   int dev = 0, cus = 0;
   hipError_t e0 = hipGetDevice(&dev);
   if (e0 == hipSuccess) e0 = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
-  if (e0 == hipSuccess && occ_lds[sal][c.wk] != lds) {
-    int per_cu = 0;
-    e0 = hipOccupancyMaxActiveBlocksPerMultiprocessor(
-        &per_cu, sal ? reinterpret_cast<const void*>(&gemv_lut4_kernel<MT, NG, TPW, D, true>)
-                     : reinterpret_cast<const void*>(&gemv_lut4_kernel<MT, NG, TPW, D, false>),
-        (int)block.x, lds);
-    if (e0 == hipSuccess) {
-      occ[sal][c.wk] = std::max(per_cu, 1);
-      occ_lds[sal][c.wk] = lds;
+  if (e0 != hipSuccess) return e0;
+  auto slots_of = [&](int mode, size_t lds, long& slots) -> hipError_t {
+    if (occ_lds[mode][c.wk] != lds) {
+      int per_cu = 0;
+      const hipError_t e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, lut4_kernel<MT, NG, TPW, D>(mode),
+                                                                        (int)block.x, lds);
+      if (e != hipSuccess) return e;
+      occ[mode][c.wk] = std::max(per_cu, 1);
+      occ_lds[mode][c.wk] = lds;
+    }
+    slots = std::max(1L, (long)cus * occ[mode][c.wk] / MY);
+    return hipSuccess;
+  };
+  // Staged block scales: one batch row, one tile-row of one-group chunks, at
+  // most two words per thread (16 G <= 2 threads), room in LDS, and at least
+  // two row groups per workgroup (sweeps of the 8B and 70B layers: 70B
+  // gate+up at M = 1 54.3 -> 50.2 us, q 14.4 -> 13.7; with one row group
+  // per workgroup, or at M = 2, staging cost up to 6%).
+  int mode = sal ? 1 : 0;
+  size_t lds = total - TABLE_BYTES;  // dynamic part (the table is static)
+  long slots = 0;
+  bool bs = MT == 1 && NG == 1 && TPW == 1 && sal && 8 * G <= (int)block.x &&
+            total + lut4_bs_bytes(a.K) <= LUT4_LDS_LIMIT;
+  if (const char* e = tune_env("QGEMV_LUT4_BS")) bs = bs && e[0] != '0';  // tuning override ("0": off)
+  if (bs) {
+    e0 = slots_of(2, lds + lut4_bs_bytes(a.K), slots);
+    if (e0 != hipSuccess) return e0;
+    const char* force = tune_env("QGEMV_LUT4_BS");
+    if (NRG >= 2 * slots || (force && force[0] == '2')) {  // ("2": regardless of the row groups)
+      mode = 2;
+      lds += lut4_bs_bytes(a.K);
     }
   }
-  if (e0 != hipSuccess) return e0;
-  const long slots = std::max(1L, (long)cus * occ[sal][c.wk] / MY);
+  if (mode != 2) {
+    e0 = slots_of(mode, lds, slots);
+    if (e0 != hipSuccess) return e0;
+  }
   const dim3 grid((unsigned)std::min<long>(NRG, slots), MY);
-  if (sal)
-    hipLaunchKernelGGL((gemv_lut4_kernel<MT, NG, TPW, D, true>), grid, block, lds, s, a);
+  if constexpr (NG == 1 && TPW == 1)
+    if (mode == 2) {
+      hipLaunchKernelGGL((gemv_lut4_kernel<MT, NG, TPW, D, true, true>), grid, block, lds, s, a);
+      return hipGetLastError();
+    }
+  if (mode == 1)
+    hipLaunchKernelGGL((gemv_lut4_kernel<MT, NG, TPW, D, true, false>), grid, block, lds, s, a);
   else
-    hipLaunchKernelGGL((gemv_lut4_kernel<MT, NG, TPW, D, false>), grid, block, lds, s, a);
+    hipLaunchKernelGGL((gemv_lut4_kernel<MT, NG, TPW, D, false, false>), grid, block, lds, s, a);
   return hipGetLastError();
 }
 

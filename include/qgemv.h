@@ -60,6 +60,9 @@
  *   QGEMV_OUTLIER_CFG="tpw,wk[,mt[,v]]" qgemv_outlier's fused kernel
  *   QGEMV_OUTLIER_FORM=fused|split      qgemv_outlier: one kernel, or dense then sparse
  *   QGEMV_LUT4_CFG="tpw,ng,wk[,mt[,d]]" qgemv_lut4
+ *   QGEMV_LUT4_BS=0|2                   qgemv_lut4: never stage the block scales in
+ *                                       LDS (0), or stage them wherever the shape
+ *                                       allows (2)
  *   QGEMV_CODEBOOK_CFG="kind,wk,..."    qgemv_codebook's kernel and shape
  *   QGEMV_CODEBOOK_GEN_KS=k             qgemv_codebook_gen: k K parts, or -wk for
  *                                       the stationary kernel with wk waves

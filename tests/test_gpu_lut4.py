@@ -45,10 +45,25 @@ def test_lut4_every_launch_shape(monkeypatch, M, N, K):
     cfgs = [(1, ng, wk, mt, d) for ng in (1, 2) for wk in (1, 3, 8) for mt in (1, 2) for d in (2, 4, 8)
             if not (ng == 2 and d == 8)]
     cfgs += [(2, 4, wk, mt, 2) for wk in (1, 3, 8) for mt in (1, 2)]
-    for cfg in cfgs:
-        monkeypatch.setenv("QGEMV_LUT4_CFG", ",".join(map(str, cfg)))
-        y = host(q.lut4(x, wq, a, lut))
-        assert_within(y, y_ref, A, f"lut4 M={M} N={N} K={K} cfg={cfg}")
+    for bs in ("2", "0"):  # one tile-row of one-group chunks: block scales staged in LDS or loaded per lane
+        monkeypatch.setenv("QGEMV_LUT4_BS", bs)
+        for cfg in cfgs:
+            monkeypatch.setenv("QGEMV_LUT4_CFG", ",".join(map(str, cfg)))
+            y = host(q.lut4(x, wq, a, lut))
+            assert_within(y, y_ref, A, f"lut4 M={M} N={N} K={K} cfg={cfg} bs={bs}")
+
+
+@pytest.mark.parametrize("M,N,K", [(1, 33000, 384), (1, 40008, 1024), (2, 20000, 512)])
+def test_lut4_many_row_groups_every_row(M, N, K):
+    """More row groups than resident workgroups, so each workgroup walks
+    several and stages the next group's block scales while it computes the
+    current one; a ragged last tile-row; every row checked."""
+    say("lut4 many row groups", M, N, K)
+    c = synth.lut4_case(N + K + 3 * M, M, N, K)
+    wq, a, lut = _upload(c)
+    y = host(q.lut4(dev(c["x"]), wq, a, lut))
+    y_ref, A = ref.gemv_lut4(c["x"], c["codes"], c["absmax"], c["lut"])
+    assert_within(y, y_ref, A, f"lut4 M={M} N={N} K={K}")
 
 
 def test_lut4_one_hot_is_exact():
