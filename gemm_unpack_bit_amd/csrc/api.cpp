@@ -90,21 +90,20 @@ long gemm_wgs(int M, int N, int mi, int nt) {
 }
 
 // Prefill GEMM block (sweeps of the 8B and 70B layers, M = 32..2048, W2 /
-// W4 / W8): the largest block that still gives enough workgroups to keep
-// two per CU busy.  64 x 256 needs at least 320 (a narrower grid leaves one
-// wave per SIMD with its loads, dequantization and MFMAs in series), 64 x
-// 128 at least 384, else 32 x 128 (the most workgroups).  64-row blocks
-// only where they pad M by at most a quarter more than 32-row blocks.
-// 8-bit weights have 32-row blocks only: 32 x 256 from 512 workgroups, else
-// 32 x 128.
+// W4 / W8): the largest block that still gives enough workgroups.  64 x 256
+// needs at least 384 (a narrower grid leaves one wave per SIMD with its
+// loads, dequantization and MFMAs in series), 64 x 128 at least 192, else
+// 32 x 128 (the most workgroups).  64-row blocks only where they pad M by
+// at most a quarter more than 32-row blocks.  8-bit weights have 32-row
+// blocks only: 32 x 256 from 512 workgroups, else 32 x 128.
 void gemm_block(int bits, int M, int N, int& mi, int& nt) {
   const bool m64 = (M + 63) / 64 * 64 * 4 <= (M + 31) / 32 * 32 * 5;
   if (bits == 8) {
     mi = 2;
     nt = gemm_wgs(M, N, 2, 4) >= 512 ? 4 : 2;
-  } else if (m64 && gemm_wgs(M, N, 4, 4) >= 320) {
+  } else if (m64 && gemm_wgs(M, N, 4, 4) >= 384) {
     mi = 4, nt = 4;
-  } else if (m64 && gemm_wgs(M, N, 4, 2) >= 384) {
+  } else if (m64 && gemm_wgs(M, N, 4, 2) >= 192) {
     mi = 4, nt = 2;
   } else {
     mi = 2, nt = 2;

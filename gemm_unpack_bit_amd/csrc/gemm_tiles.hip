@@ -61,7 +61,12 @@ __global__ void __launch_bounds__(256, 2) gemm_tiles_kernel(UniformArgs a, int n
   // r holding k 8 (c ^ (r % 16)) .. + 7 of the group: a row is 256 bytes,
   // so without the swizzle the 16 rows of an A fragment read would all hit
   // the same banks
-  __shared__ __attribute__((aligned(16))) _Float16 xs[2][BM * 128];
+  // (two separate arrays, selected by a compile-time buffer index: the
+  // compiler then knows that reading one never waits for loads into the
+  // other)
+  __shared__ __attribute__((aligned(16))) _Float16 xs0[BM * 128];
+  __shared__ __attribute__((aligned(16))) _Float16 xs1[BM * 128];
+  auto xbuf = [&](int b) -> _Float16* { return b ? xs1 : xs0; };
   // staged quant params of an 8-group chunk, two buffers: [row][8] scales and
   // [row][ZW] zero-point words (the words holding the chunk's groups)
   constexpr int ZW = BITS == 8 ? 2 : 1;
@@ -105,7 +110,7 @@ __global__ void __launch_bounds__(256, 2) gemm_tiles_kernel(UniformArgs a, int n
   auto x_issue = [&](int g, int b) {
 #pragma unroll
     for (int j = 0; j < NMT; ++j)
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(rx, (__attribute__((address_space(3))) void*)&xs[b][(4 * j + wave) * 512],
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rx, (__attribute__((address_space(3))) void*)&xbuf(b)[(4 * j + wave) * 512],
                                                16, xbase, 32u * (uint32_t)K * j + 256u * g, 0, 0);
   };
   // the wave's weights in group g: codes, scale and zero point of lane row n
@@ -161,7 +166,7 @@ __global__ void __launch_bounds__(256, 2) gemm_tiles_kernel(UniformArgs a, int n
 #pragma unroll
     for (int i = 0; i < NMT; ++i) {
       // block row 16 i + n, k 32 kq + 8 s .. + 7 of the group
-      const u4* xr = reinterpret_cast<const u4*>(&xs[b][(16 * i + n) * 128]);
+      const u4* xr = reinterpret_cast<const u4*>(&xbuf(b)[(16 * i + n) * 128]);
 #pragma unroll
       for (int s = 0; s < 4; ++s) av[i][s] = xr[(4 * kq + s) ^ n];
     }
