@@ -109,7 +109,16 @@ constexpr int max_threads(int ng) { return ng == 1 ? 1024 : 512; }
 // so a chunk costs one weight load per lane and tile instead of three
 // (per-lane scale and zero loads touch 16 rows' cache lines for every 1 KB
 // of codes).
-template <int BITS, bool MFMA, int MT, int NG, int D, int TPW, bool SAL, bool XLDS, bool SP, bool PLDS>
+// XD (MFMA, activations too large to stage whole, one-group chunks of
+// several tile-rows): each wave streams its chunks' activation blocks (the
+// batch rows x 128 k) through a two-slot LDS ring with 16-byte loads straight
+// into LDS, a chunk ahead.  Such a load covers 4 rows x 256 contiguous bytes
+// (8 cache lines); the per-lane A-fragment loads it replaces touch 32 lines
+// each.  A chunk's A fragments and quant params are read from LDS before the
+// next chunk's load is issued, so the wait for a slot's load is never a
+// wait for the one behind it.
+template <int BITS, bool MFMA, int MT, int NG, int D, int TPW, bool SAL, bool XLDS, bool SP, bool PLDS,
+          bool XD = false>
 __global__ void __launch_bounds__(max_threads(NG)) __attribute__((amdgpu_waves_per_eu(waves_per_simd(NG))))
 gemv_tiles_kernel(UniformArgs a) {
   using TR = Uni<BITS>;
@@ -123,6 +132,7 @@ gemv_tiles_kernel(UniformArgs a) {
   static_assert(TPW % D == 0 || (TPW == 1 && D == 2) || DEEP, "a chunk's stages fill the ring evenly");
   static_assert(!DEEP || (XLDS && NG == 1), "the deep chunk ring keeps no activations in registers");
   static_assert(ZPW % NG == 0, "a chunk's zero points share one word");
+  static_assert(!XD || (MFMA && !XLDS && !SP && NG == 1 && TPW >= D), "the activation ring: MFMA, one-group chunks");
 
   // LDS: [staged activations: XM x K halves, XLDS only] [staged scales and
   // zero points of the TPW tile-rows, PLDS only] then the per-wave partials: VALU
@@ -152,12 +162,20 @@ gemv_tiles_kernel(UniformArgs a) {
   // past K read instead (they add s = 0 times a finite value)
   const int XK = K + 32;
   const int XM = MFMA ? min(M, 16) : MT;  // staged activation rows
-  char* const pbase = reinterpret_cast<char*>(smem) + (XLDS ? (size_t)XM * XK * 2 : 0);
+  // XD: the activation ring first (per wave two slots of XMR rows x 256
+  // bytes, XMR = the batch rows rounded up to 4), which the partials reuse
+  // after the loop
+  const int XMR = (min(M, 16) + 3) & ~3;
+  const uint32_t xslot = 256u * XMR;
+  const size_t ringb = !XD ? 0
+                      : (size_t)WK * 2 * xslot > (size_t)WK * TPW * 64 * 16 ? (size_t)WK * 2 * xslot
+                                                                            : (size_t)WK * TPW * 64 * 16;
+  char* const pbase = reinterpret_cast<char*>(smem) + (XLDS ? (size_t)XM * XK * 2 : ringb);
   const uint32_t psb = PLDS ? (32u * TPW * G + 15u) & ~15u : 0u;  // 16 TPW rows x G scales, 16-byte padded
   const uint32_t pzb = PLDS ? 16u * TPW * zrow : 0u;                // 16 TPW rows of packed zero points
   const uint16_t* ps = reinterpret_cast<const uint16_t*>(pbase);
   const uint32_t* pz = reinterpret_cast<const uint32_t*>(pbase + psb);
-  float* red = reinterpret_cast<float*>(pbase + psb + pzb);
+  float* red = XD ? smem : reinterpret_cast<float*>(pbase + psb + pzb);
   const u4* xs = reinterpret_cast<const u4*>(smem);
 
   // outlier variant (SP): LDS after the partials (see sparse_lds_bytes), per
@@ -231,7 +249,7 @@ gemv_tiles_kernel(UniformArgs a) {
   constexpr int XB = TPW < D ? 2 : 1;
   u4 xr[XLDS ? 1 : XB][XLDS ? 1 : NG][XR][4];
   auto load_x = [&](int c, int b) {
-    if constexpr (XLDS) return;
+    if constexpr (XLDS || XD) return;
     const int gc0 = c * NG;
 #pragma unroll
     for (int j = 0; j < NG; ++j) {
@@ -241,6 +259,55 @@ gemv_tiles_kernel(UniformArgs a) {
       for (int r = 0; r < XR; ++r)
 #pragma unroll
         for (int v = 0; v < 4; ++v) xr[XLDS ? 0 : b][XLDS ? 0 : j][r][v] = bload16(rx, ok ? xoff[r] + 16u * v : OOB, sx);
+    }
+  };
+
+  // XD: the current chunk's quant params, read from LDS with its A fragments
+  uint16_t xd_s[XD && PLDS ? TPW : 1];
+  uint32_t xd_z[XD && PLDS ? TPW : 1];
+  // XD: activation block of chunk c (group c) into ring slot `slot`: load j
+  // covers rows 4 j .. 4 j + 3, lane l writing piece l % 16 of row
+  // 4 j + l / 16, which holds k-piece (l % 16) ^ row (the swizzle keeps the
+  // 16 rows of an A-fragment read on distinct banks); rows past M and chunks
+  // past the last read zeros
+  // (offsets formed at issue: kept in registers across the loop they would
+  // cost occupancy)
+  auto xd_issue = [&](int c, int slot) {
+    if constexpr (XD) {
+      const uint32_t so = __builtin_amdgcn_readfirstlane(c < G ? 256u * (uint32_t)c : 0u);
+      char* dst = reinterpret_cast<char*>(smem) + (size_t)(wave * 2 + slot) * xslot;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int row = 4 * j + kq;
+        if (4 * j < XMR)  // (wave-uniform)
+          __builtin_amdgcn_raw_ptr_buffer_load_lds(
+              rx, (__attribute__((address_space(3))) void*)(dst + 1024 * j), 16,
+              row < M && c < G ? ((uint32_t)row * K + 8u * (uint32_t)(n ^ row)) * 2u : OOB, so, 0, 0);
+      }
+    }
+  };
+  // XD: the A fragments of the chunk in `slot` (batch row n, or row XMR - 1
+  // for n >= XMR: those result rows are never stored) into the activation
+  // registers, and its quant params (read once per chunk: read per tile-row
+  // from LDS instead, they measured up to 20% slower)
+  auto xd_read = [&](int c, int slot) {
+    if constexpr (XD) {
+      const int row = min(n, XMR - 1);
+      const u4* xb = reinterpret_cast<const u4*>(reinterpret_cast<const char*>(smem) +
+                                                 (size_t)(wave * 2 + slot) * xslot + 256u * row);
+#pragma unroll
+      for (int s4 = 0; s4 < 4; ++s4) xr[0][0][0][s4] = xb[(4 * kq + s4) ^ row];
+      if constexpr (PLDS) {
+        const bool gin = c < G;
+        const int g = min(c, G - 1);
+#pragma unroll
+        for (int t = 0; t < TPW; ++t) {
+          const uint16_t sv = ps[(16 * t + n) * G + g];
+          const uint32_t zv = pz[(16 * t + n) * (int)(zrow / 4) + g / ZPW];
+          xd_s[t] = gin ? sv : (uint16_t)0;
+          xd_z[t] = gin ? zv : 0u;
+        }
+      }
     }
   };
 
@@ -260,14 +327,19 @@ gemv_tiles_kernel(UniformArgs a) {
       uint32_t zw = st.z;
       uint16_t sj = st.s[j];
       if constexpr (PLDS) {  // (a chunk past the last: scale 0, zero point 0)
-        // unconditional reads at a clamped group, then a select: a read under
-        // a condition would become a branch inside the pipelined loop
-        const bool gin = gc0 + j < G;
-        const int g = min(gc0 + j, G - 1);
-        const uint16_t sv = ps[(16 * t + n) * G + g];
-        const uint32_t zv = pz[(16 * t + n) * (int)(zrow / 4) + g / ZPW];
-        sj = gin ? sv : (uint16_t)0;
-        zw = gin ? zv : 0u;
+        if constexpr (XD) {
+          sj = xd_s[t];
+          zw = xd_z[t];
+        } else {
+          // unconditional reads at a clamped group, then a select: a read
+          // under a condition would become a branch inside the pipelined loop
+          const bool gin = gc0 + j < G;
+          const int g = min(gc0 + j, G - 1);
+          const uint16_t sv = ps[(16 * t + n) * G + g];
+          const uint32_t zv = pz[(16 * t + n) * (int)(zrow / 4) + g / ZPW];
+          sj = gin ? sv : (uint16_t)0;
+          zw = gin ? zv : 0u;
+        }
       }
       const float sc = h2f(sj);
       const typename TR::Z zz = TR::zc((zw >> (BITS * ((gc0 + j) % ZPW))) & ZMASK);
@@ -521,9 +593,31 @@ gemv_tiles_kernel(UniformArgs a) {
 #pragma unroll
     for (int t = 0; t < D - 1; ++t) load_stage(t, c, ring[t]);
     load_x(c, 0);
+    xd_issue(c, 0);
     if constexpr (XLDS || PLDS || SP) stage_x();
     sparse_issue();
+    int xsl = 0;  // XD: ring slot of chunk c
+    // XD: the compiler does not order reads of a ring slot after the loads
+    // into it, so the waits are explicit.  Before the loop: everything (the
+    // first slot, the first stages).  At the top of each chunk: its slot's
+    // loads, which the previous chunk's TPW weight stages followed (loads
+    // complete in order; the scheduling barriers keep the issue order).  The
+    // next chunk's loads go into the other slot, read (into registers) a
+    // chunk ago.
+    constexpr int XLPS = (BITS == 8 ? 2 : 1) + (PLDS ? 0 : 2);  // vector memory instructions per stage
+    constexpr int XW = TPW * XLPS;
+    static_assert(XW < 64, "vmcnt range");
+    constexpr int XVMW = (XW & 15) | (0x7 << 4) | (0xF << 8) | ((XW >> 4) << 14);  // s_waitcnt vmcnt(XW)
+    if constexpr (XD) __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
     for (; c < NC; c += WK) {
+      if constexpr (XD) {
+        __builtin_amdgcn_sched_barrier(0);
+        __builtin_amdgcn_s_waitcnt(XVMW);
+        xd_read(c, xsl);
+        __builtin_amdgcn_sched_barrier(0);
+        xd_issue(c + WK, xsl ^ 1);
+        __builtin_amdgcn_sched_barrier(0);
+      }
 #pragma unroll
       for (int t = 0; t < TPW; ++t) {
         const int ta = t + D - 1;  // stage to issue (slot of the stage unpacked last)
@@ -537,6 +631,7 @@ gemv_tiles_kernel(UniformArgs a) {
         __builtin_amdgcn_sched_barrier(0);
       }
       load_x(c + WK, 0);
+      xsl ^= 1;
     }
   } else if constexpr (DEEP) {
     // one tile-row, D chunks in flight: chunk c + i WK sits in slot i % D
@@ -578,6 +673,12 @@ gemv_tiles_kernel(UniformArgs a) {
   sparse_compute();
 
   if constexpr (MFMA) {
+    if constexpr (XD) {
+      // the partials reuse the activation ring: every load into it has
+      // landed and every wave is past its last read
+      __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
+      __syncthreads();
+    }
     // lane l holds result rows m = 4 (l / 16) + i of weight row l % 16
     f4* r4 = reinterpret_cast<f4*>(red);
 #pragma unroll
@@ -628,9 +729,10 @@ size_t sparse_lds_bytes(bool mfma, int mt, int wk, int tpw, int K, int M) {
 
 constexpr size_t LDS_ALL = 160 * 1024;  // gfx950 LDS per workgroup
 
-template <int BITS, bool MFMA, int MT, int NG, int D, int TPW, bool SAL, bool XLDS, bool SP, bool PLDS>
+template <int BITS, bool MFMA, int MT, int NG, int D, int TPW, bool SAL, bool XLDS, bool SP, bool PLDS,
+          bool XD = false>
 hipError_t launch_k(const UniformArgs& a, dim3 grid, dim3 block, size_t lds, hipStream_t s) {
-  auto kern = &gemv_tiles_kernel<BITS, MFMA, MT, NG, D, TPW, SAL, XLDS, SP, PLDS>;
+  auto kern = &gemv_tiles_kernel<BITS, MFMA, MT, NG, D, TPW, SAL, XLDS, SP, PLDS, XD>;
   if (lds > 64 * 1024) {
     static bool raised = false;  // one-time opt-in above the default dynamic LDS limit
     if (!raised) {
@@ -652,7 +754,19 @@ size_t params_lds_bytes(int bits, int K, int tpw) {
 }
 
 template <int BITS, bool MFMA, int MT, int NG, int D, int TPW, bool XL, bool SP>
-hipError_t launch_p(const UniformArgs& a, bool sal, bool plds, dim3 grid, dim3 block, size_t lds, hipStream_t s) {
+hipError_t launch_p(const UniformArgs& a, bool sal, bool plds, bool xd, dim3 grid, dim3 block, size_t lds,
+                    hipStream_t s) {
+  // the activation ring (XD): the matrix-core engine with activations not
+  // staged whole, one-group chunks of several tile-rows, no outliers
+  constexpr bool XD_OK = MFMA && !XL && !SP && NG == 1 && TPW >= D && TPW >= 2 && TPW <= 4 && !(BITS == 8 && TPW == 4);
+  if constexpr (XD_OK) {
+    if (xd) {
+      if (!sal) return hipErrorInvalidValue;
+      return plds ? launch_k<BITS, MFMA, MT, NG, D, TPW, true, XL, SP, true, true>(a, grid, block, lds, s)
+                  : launch_k<BITS, MFMA, MT, NG, D, TPW, true, XL, SP, false, true>(a, grid, block, lds, s);
+    }
+  }
+  if (xd) return hipErrorInvalidValue;
   if constexpr (TPW == 1 && NG == 1) {
     // one-group chunks: a group's scale is always one whole, aligned load
     if (!sal) return hipErrorInvalidValue;
@@ -696,18 +810,32 @@ hipError_t launch_t(const UniformArgs& a, const TileCfg& c, hipStream_t s) {
     bool plds = reinterpret_cast<uintptr_t>(a.scales) % 16 == 0 && reinterpret_cast<uintptr_t>(a.zeros) % 16 == 0 &&
                 (size_t)a.N * G * 2 % 16 == 0 && zbytes % 16 == 0;
     if (const char* e = tune_env("QGEMV_PLDS")) plds = plds && e[0] == '1';  // tuning override
-    const size_t rest = (xlds ? xl : 0) + red + (SP ? sparse_lds_bytes(MFMA, MT, c.wk, TPW, a.K, a.M) : 0);
+    // chunk scales in one load: whole chunks and a 2*NG-byte aligned base
+    const bool sal = (a.K / 128) % NG == 0 && reinterpret_cast<uintptr_t>(a.scales) % (2 * NG) == 0;
+    // the activation ring (matrix cores, activations not staged whole): per
+    // wave two slots of the batch rows (rounded up to 4) x 256 bytes, which
+    // the partials reuse after the loop
+    // (the wider variants would spill).  Used where it measured faster
+    // (sweeps of the 8B and 70B layers, M = 2..16): long K (K/128 >= 128:
+    // 70B down at M = 8 28.9 -> 24.6 us, M = 16 36.7 -> 33.3) or M >= 13 (70B
+    // q at M = 16 17.5 -> 15.7); at M = 4..8 with K = 4096..8192 it cost up
+    // to 11%.
+    bool xd = MFMA && !xlds && !SP && NG == 1 && TPW >= D && TPW >= 2 && TPW <= 4 && !(BITS == 8 && TPW == 4) && sal;
+    bool xd_rule = a.K / 128 >= 128 || a.M >= 13;
+    if (const char* e = tune_env("QGEMV_XDMA")) xd_rule = e[0] == '2' || (e[0] == '1' && xd_rule);  // tuning override
+    xd = xd && xd_rule;
+    const size_t ring = (size_t)c.wk * 2 * 256 * ((std::min(a.M, 16) + 3) & ~3);
+    const size_t rest = xd ? std::max(ring, red)
+                           : (xlds ? xl : 0) + red + (SP ? sparse_lds_bytes(MFMA, MT, c.wk, TPW, a.K, a.M) : 0);
     if (rest + params_lds_bytes(BITS, a.K, TPW) > LDS_ALL) plds = false;  // (long K: stage nothing)
     const size_t lds = rest + (plds ? params_lds_bytes(BITS, a.K, TPW) : 0);
     if (lds > LDS_ALL) return hipErrorInvalidValue;
-    // chunk scales in one load: whole chunks and a 2*NG-byte aligned base
-    const bool sal = (a.K / 128) % NG == 0 && reinterpret_cast<uintptr_t>(a.scales) % (2 * NG) == 0;
     if constexpr (DEEP) {
       if (!xlds) return hipErrorInvalidValue;  // the deep ring reads activations from LDS only
-      return launch_p<BITS, MFMA, MT, NG, D, TPW, true, SP>(a, sal, plds, grid, block, lds, s);
+      return launch_p<BITS, MFMA, MT, NG, D, TPW, true, SP>(a, sal, plds, false, grid, block, lds, s);
     } else {
-      if (xlds) return launch_p<BITS, MFMA, MT, NG, D, TPW, true, SP>(a, sal, plds, grid, block, lds, s);
-      return launch_p<BITS, MFMA, MT, NG, D, TPW, false, SP>(a, sal, plds, grid, block, lds, s);
+      if (xlds) return launch_p<BITS, MFMA, MT, NG, D, TPW, true, SP>(a, sal, plds, false, grid, block, lds, s);
+      return launch_p<BITS, MFMA, MT, NG, D, TPW, false, SP>(a, sal, plds, xd, grid, block, lds, s);
     }
   }
 }

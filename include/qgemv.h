@@ -57,6 +57,10 @@
  *   QGEMV_PLDS=0|1                      uniform kernels: stage the workgroup's scales
  *                                       and zero points in LDS (1, the default where
  *                                       aligned and they fit) or load them per lane
+ *   QGEMV_XDMA=0|1|2                    matrix-core uniform kernel with activations not
+ *                                       staged whole: per-wave LDS ring of activation
+ *                                       blocks off (0), where it measured faster (1,
+ *                                       the default), wherever the shape allows (2)
  *   QGEMV_OUTLIER_CFG="tpw,wk[,mt[,v]]" qgemv_outlier's fused kernel
  *   QGEMV_OUTLIER_FORM=fused|split      qgemv_outlier: one kernel, or dense then sparse
  *   QGEMV_LUT4_CFG="tpw,ng,wk[,mt[,d]]" qgemv_lut4

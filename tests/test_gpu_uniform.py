@@ -112,6 +112,34 @@ def test_every_launch_shape(monkeypatch, bits, N, K, path, M):
         assert any(r.startswith("1,") and r.endswith(",4") for r in ran), ran
 
 
+@pytest.mark.parametrize("bits", [2, 4, 8])
+@pytest.mark.parametrize("M", [2, 5, 8, 13, 16])
+def test_activation_ring_launch_shapes(monkeypatch, bits, M):
+    """Matrix-core engine with the activations not staged whole: each wave
+    streams its chunks' activation blocks through a two-slot LDS ring (on and
+    off), with staged or per-lane quant params, several tile-rows and wave
+    counts; a ragged N, an odd K/128 and batch rows that are not a multiple
+    of 4."""
+    N, K = 300, 2176
+    say("activation ring", bits, M, N, K)
+    c = synth.uniform_case(N + K + bits + M, M, N, K, bits)
+    wq = q.pack(dev(c["codes"]), bits)
+    zq = q.pack_zeros(dev(c["zeros"]), bits)
+    x, s = dev(c["x"]), dev(c["scales"])
+    y_ref, A = ref.gemv_uniform(c["x"], c["codes"], c["scales"], c["zeros"])
+    monkeypatch.setenv("QGEMV_XLDS_MAX", "0")  # activations never staged whole
+    for xd in ("2", "0"):  # the ring forced on, and off
+        monkeypatch.setenv("QGEMV_XDMA", xd)
+        for plds in ("1", "0"):
+            monkeypatch.setenv("QGEMV_PLDS", plds)
+            for tpw in (2, 4):
+                for wk in (1, 4, 16):
+                    cfg = f"{tpw},{wk},1,3"
+                    monkeypatch.setenv("QGEMV_TILE_CFG", cfg)
+                    y = host(q.uniform(x, wq, s, zq, bits, q.PATH_MFMA))
+                    assert_within(y, y_ref, A, f"W{bits} M={M} cfg={cfg} xd={xd} plds={plds}")
+
+
 # ----------------------------------------------------------------------------
 # exact special cases
 # ----------------------------------------------------------------------------
