@@ -112,21 +112,22 @@ void gemm_block(int bits, int M, int N, int& mi, int& nt) {
 
 // 17..64 rows: the 16-row slices of the decode kernel or the GEMM.  A slice
 // streams the weights once, in about max(0.15 G + 2, weight bytes / 3.5
-// TB/s) us (its per-workgroup group loop or HBM); the GEMM's few workgroups
-// each run the whole K loop, about 0.7 G us per 512 workgroups.  Fitted to
-// the 8B layers at M = 32..80 (W4): the slices win on the long-K down layer
-// up to M = 64, the GEMM on the wide gate+up layer from M = 32 and on the
-// 4096-k layers at M = 64.
+// TB/s) us (its per-workgroup group loop, or HBM; 2-bit codes priced as
+// 4-bit ones: their unpack, not their bytes, bounds them); the GEMM's few
+// workgroups each run the whole K loop, about 0.58 G us per 320
+// workgroups.  Fitted to the 8B and 70B layers at M = 24..64 (W2 / W4 /
+// W8): the GEMM takes the wide gate+up layers from M = 17, the 4096-k
+// layers from M = 48 and every layer at M = 64.
 bool prefer_slices(int bits, int M, int N, int K) {
   if (M <= QGEMV_MAX_M) return true;
   if (M > QGEMV_GEMM_SLICE_MAX_M) return false;
   const int G = K / QGEMV_GROUP;
-  const double wbytes = (double)N * K * bits / 8;
+  const double wbytes = (double)N * K * (bits < 4 ? 4 : bits) / 8;
   const double t16 = std::max(0.15 * G + 2.0, wbytes / 3.5e6);
   int mi, nt;
   gemm_block(bits, M, N, mi, nt);
-  const double rounds = std::max(1.0, (double)gemm_wgs(M, N, mi, nt) / 512.0);
-  return (double)((M + QGEMV_MAX_M - 1) / QGEMV_MAX_M) * t16 <= 0.7 * G * rounds;
+  const double rounds = std::max(1.0, (double)gemm_wgs(M, N, mi, nt) / 320.0);
+  return (double)((M + QGEMV_MAX_M - 1) / QGEMV_MAX_M) * t16 <= 0.58 * G * rounds;
 }
 
 // Tuning override of the LUT4 launch shape: QGEMV_LUT4_CFG="tpw,ng,wk[,mt[,d]]".
