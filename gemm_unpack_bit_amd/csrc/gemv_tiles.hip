@@ -815,16 +815,12 @@ hipError_t launch_t(const UniformArgs& a, const TileCfg& c, hipStream_t s) {
     // the activation ring (matrix cores, activations not staged whole): per
     // wave two slots of the batch rows (rounded up to 4) x 256 bytes, which
     // the partials reuse after the loop
-    // (the wider variants would spill).  Used where it measured faster
-    // (sweeps of the 8B and 70B layers, M = 2..16): long K (K/128 >= 128:
-    // 70B down at M = 8 28.9 -> 24.6 us, M = 9 32.4 -> 25.8) or M >= 12
-    // (with 16 waves of two tile-rows at M = 16: 70B down 33.4 -> 30.6, o
-    // 12.1 -> 11.4, 8B down 17.2 -> 15.9); at M = 4..9 with K = 4096..8192
-    // it cost up to 11%.
+    // (the wider variants would spill).  Used where the launch shape asks for
+    // it (pick_tiles: where it measured faster).
     bool xd = MFMA && !xlds && !SP && NG == 1 && TPW >= D && TPW >= 2 && TPW <= 4 && !(BITS == 8 && TPW == 4) && sal;
-    bool xd_rule = a.K / 128 >= 128 || a.M >= 12;
-    if (const char* e = tune_env("QGEMV_XDMA")) xd_rule = e[0] == '2' || (e[0] == '1' && xd_rule);  // tuning override
-    xd = xd && xd_rule;
+    bool xd_want = c.xd;
+    if (const char* e = tune_env("QGEMV_XDMA")) xd_want = e[0] == '2' || (e[0] == '1' && xd_want);  // tuning override
+    xd = xd && xd_want;
     const size_t ring = (size_t)c.wk * 2 * 256 * ((std::min(a.M, 16) + 3) & ~3);
     const size_t rest = xd ? std::max(ring, red)
                            : (xlds ? xl : 0) + red + (SP ? sparse_lds_bytes(MFMA, MT, c.wk, TPW, a.K, a.M) : 0);
@@ -895,12 +891,16 @@ hipError_t launch_b(const UniformArgs& a, const TileCfg& c, hipStream_t s) {
 //    4-bit layers of 384-512 tile-rows, which take two tile-rows and
 //    four-group chunks;
 //  * MFMA (batch >= 2), 2- and 4-bit codes: one tile-row for narrow layers
-//    (at most 256 tile-rows; two for long K from M = 12); otherwise 2 or 4
-//    tile-rows of one-group chunks with staged quant params (16 waves up to
-//    M = 4, for long K, and from M = 12, where the activation ring frees
-//    the registers the wide workgroups need; else 8), and 8 tile-rows
-//    with half chunks for the widest 4-bit layers at M >= 9.  8-bit codes
-//    keep the earlier fit (several-group chunks).
+//    (at most 256 tile-rows; 16 waves at M = 5..7 for K < 12288; two
+//    tile-rows for long K from M = 12); otherwise 2 or 4 tile-rows of
+//    one-group chunks with staged quant params (16 waves up to M = 6, for
+//    K >= 8192 and from M = 12, where the activation ring frees the
+//    registers the wide workgroups need; else 8), two tile-rows with the
+//    ring for the widest layers at M = 5..8, and 8 tile-rows with half
+//    chunks for the widest 4-bit layers at M >= 9.  8-bit codes keep the
+//    earlier fit (several-group chunks).
+//  * The activation ring (matrix cores, activations not staged whole) for
+//    K >= 16384, from M = 12, and for the shapes that set it above.
 TileCfg pick_tiles(int bits, int M, int N, int K, bool mfma) {
   TileCfg c;
   c.mfma = mfma;
@@ -923,6 +923,7 @@ TileCfg pick_tiles(int bits, int M, int N, int K, bool mfma) {
     if (M <= 2) set(1, 16, 3);
     else if (M <= 4) set(1, G >= 96 ? 8 : 16, 3);
     else if (M >= 12 && G >= 96 && bits != 8) set(2, 16, 3);  // (long K: two tile-rows, the activation ring)
+    else if (M <= 7 && G < 96 && bits != 8) set(1, 16, 3);
     else set(1, M <= 8 ? 8 : 4, 3);
   } else if (bits == 8) {
     if (M >= 8 && nt >= 1536) {
@@ -952,13 +953,19 @@ TileCfg pick_tiles(int bits, int M, int N, int K, bool mfma) {
   } else {
     if (nt >= 1536) {
       if (bits == 4 && M >= 9) set(8, nt >= 2048 ? 4 : 8, 1);  // half chunks keep 8 tile-rows of stages in registers
+      else if (M <= 8 && nt >= 2048) set(2, 4, 3), c.xd = true;
       else set(4, 8, 3);
     } else if (nt >= 640 && G < 128) {
       set(4, 16, 3);
+    } else if (M <= 8 && G >= 64) {
+      set(2, 16, 3), c.xd = true;
     } else {
-      set(2, G >= 128 || M >= 12 ? 16 : 8, 3);
+      set(2, G >= 128 || M >= 12 || M <= 6 ? 16 : 8, 3);
     }
   }
+  // the activation ring (where the shape and the activations allow it):
+  // long K, or from M = 12, or as set above
+  if (mfma && (G >= 128 || M >= 12)) c.xd = true;
   // never more waves than chunks of groups
   const int ng = chunk_groups(bits, mfma, c.mt, c.v);
   const int nc = (G + ng - 1) / ng;

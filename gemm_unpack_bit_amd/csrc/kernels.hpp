@@ -33,6 +33,7 @@ struct UniformArgs {
 struct TileCfg {
   bool mfma;
   int mt, tpw, wk, v;
+  bool xd = false;  // matrix-core engine, activations not staged whole: the per-wave activation ring
 };
 
 TileCfg pick_tiles(int bits, int M, int N, int K, bool mfma);
