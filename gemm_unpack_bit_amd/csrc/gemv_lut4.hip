@@ -286,7 +286,13 @@ __global__ void __launch_bounds__(MT == 1 ? 1024 : 512, MT == 1 ? 4 : 2) gemv_lu
       if (e < 256) pairs[e] = tlo[j] | (thi[j] << 16);
     }
     lds_barrier();
-    for (int i = threadIdx.x; i < 256 * TABLE_COPIES; i += blockDim.x) ltab[i] = pairs[i / TABLE_COPIES];
+    // 16 bytes (four copies of one pair) per write: piece i holds copies
+    // 4 (i % 16) .. + 3 of entry i / 16
+    constexpr int PIECES = 256 * TABLE_COPIES / 4;
+    for (int i = threadIdx.x; i < PIECES; i += blockDim.x) {
+      const uint32_t v = pairs[i / (TABLE_COPIES / 4)];
+      reinterpret_cast<u4*>(ltab)[i] = u4{v, v, v, v};
+    }
     lds_barrier();  // (LDS only: the weight prefetch stays in flight)
   }
   // activations of rows m0 .. m0 + MT - 1; each 8-k run stored as
