@@ -90,23 +90,32 @@ long gemm_wgs(int M, int N, int mi, int nt) {
 }
 
 // Prefill GEMM block (sweeps of the 8B and 70B layers, M = 32..2048, W2 /
-// W4 / W8): the largest block that still gives enough workgroups.  64 x 256
-// needs at least 384 (a narrower grid leaves one wave per SIMD with its
-// loads, dequantization and MFMAs in series), 64 x 128 at least 192, else
-// 32 x 128 (the most workgroups).  64-row blocks only where they pad M by
-// at most a quarter more than 32-row blocks.  8-bit weights have 32-row
-// blocks only: 32 x 256 from 512 workgroups, else 32 x 128.
-void gemm_block(int bits, int M, int N, int& mi, int& nt) {
+// W4 / W8): the largest block that still gives enough workgroups, and on a
+// thin grid two K halves per workgroup (twice the waves, same workgroups).
+// 64 x 256 needs at least 400 workgroups (a narrower grid leaves one wave
+// per SIMD with its loads, dequantization and MFMAs in series), 64 x 128 at
+// least 384 with all of K, or 144 to 256 with two K halves (their 8-wave
+// workgroups run one per CU, so more than 256 leave a tail: 70B q at M = 256
+// 81.6 vs 71.2 us), else 32 x 128 (two K halves below 512).  64-row blocks only where they pad M by at most a quarter more
+// than 32-row blocks.  8-bit weights have 32-row blocks only: 32 x 256 from
+// 448 workgroups, else 32 x 128, with two K halves below 640.  (Two K
+// halves need K/128 even; the caller falls back to one.)
+void gemm_block(int bits, int M, int N, int& mi, int& nt, int& kh) {
   const bool m64 = (M + 63) / 64 * 64 * 4 <= (M + 31) / 32 * 32 * 5;
+  kh = 1;
   if (bits == 8) {
     mi = 2;
-    nt = gemm_wgs(M, N, 2, 4) >= 512 ? 4 : 2;
-  } else if (m64 && gemm_wgs(M, N, 4, 4) >= 384) {
+    nt = gemm_wgs(M, N, 2, 4) >= 448 ? 4 : 2;
+    if (nt == 2 && gemm_wgs(M, N, 2, 2) < 640) kh = 2;
+  } else if (m64 && gemm_wgs(M, N, 4, 4) >= 400) {
     mi = 4, nt = 4;
-  } else if (m64 && gemm_wgs(M, N, 4, 2) >= 192) {
+  } else if (m64 && gemm_wgs(M, N, 4, 2) >= 384) {
     mi = 4, nt = 2;
+  } else if (m64 && gemm_wgs(M, N, 4, 2) >= 144 && gemm_wgs(M, N, 4, 2) <= 256) {
+    mi = 4, nt = 2, kh = 2;  // (8-wave workgroups run one per CU: at most one round)
   } else {
     mi = 2, nt = 2;
+    kh = gemm_wgs(M, N, 2, 2) < 512 ? 2 : 1;
   }
 }
 
@@ -114,20 +123,20 @@ void gemm_block(int bits, int M, int N, int& mi, int& nt) {
 // streams the weights once, in about max(0.15 G + 2, weight bytes / 3.5
 // TB/s) us (its per-workgroup group loop, or HBM; 2-bit codes priced as
 // 4-bit ones: their unpack, not their bytes, bounds them); the GEMM's few
-// workgroups each run the whole K loop, about 0.58 G us per 320
+// workgroups (two K halves each) run the K loop, about 0.44 G us per 320
 // workgroups.  Fitted to the 8B and 70B layers at M = 24..64 (W2 / W4 /
-// W8): the GEMM takes the wide gate+up layers from M = 17, the 4096-k
-// layers from M = 48 and every layer at M = 64.
+// W8): the GEMM takes the wide gate+up layers from M = 17 and the others
+// from M = 48.
 bool prefer_slices(int bits, int M, int N, int K) {
   if (M <= QGEMV_MAX_M) return true;
   if (M > QGEMV_GEMM_SLICE_MAX_M) return false;
   const int G = K / QGEMV_GROUP;
   const double wbytes = (double)N * K * (bits < 4 ? 4 : bits) / 8;
   const double t16 = std::max(0.15 * G + 2.0, wbytes / 3.5e6);
-  int mi, nt;
-  gemm_block(bits, M, N, mi, nt);
+  int mi, nt, kh;
+  gemm_block(bits, M, N, mi, nt, kh);
   const double rounds = std::max(1.0, (double)gemm_wgs(M, N, mi, nt) / 320.0);
-  return (double)((M + QGEMV_MAX_M - 1) / QGEMV_MAX_M) * t16 <= 0.58 * G * rounds;
+  return (double)((M + QGEMV_MAX_M - 1) / QGEMV_MAX_M) * t16 <= 0.44 * G * rounds;
 }
 
 // Tuning override of the LUT4 launch shape: QGEMV_LUT4_CFG="tpw,ng,wk[,mt[,d]]".
@@ -379,11 +388,13 @@ int qgemv_gemm_uniform(int bits, int M, int N, int K, const uint16_t* x, const u
     return QGEMV_OK;
   }
   qg::UniformArgs a{bits, M, N, K, x, wq, scales, zeros, y};
-  int mi, nt;
-  gemm_block(bits, M, N, mi, nt);
+  int mi, nt, kh;
+  gemm_block(bits, M, N, mi, nt, kh);
   if (const char* e = tune_env("QGEMV_GEMM_MI")) mi = std::atoi(e);  // tuning overrides
   if (const char* e = tune_env("QGEMV_GEMM_NT")) nt = std::atoi(e);
-  return hip_status(qg::launch_gemm_tiles(a, mi, nt, s));
+  if (const char* e = tune_env("QGEMV_GEMM_KH")) kh = std::atoi(e);
+  if (kh == 2 && (nt != 2 || G % 2)) kh = 1;  // (two K halves: 128-column blocks, K/128 even)
+  return hip_status(qg::launch_gemm_tiles(a, mi, nt, kh, s));
 }
 
 int qgemv_w2a16(int M, int N, int K, const uint16_t* x, const uint32_t* wq, const uint16_t* scales,

@@ -49,8 +49,14 @@ __device__ __forceinline__ h8 cat4(h2 a, h2 b, h2 c, h2 d) {
 // groups at a time with coalesced 16-byte loads (one row per thread of the
 // first NNT waves), instead of per-lane loads that touch 16 rows' cache
 // lines for each tile-row and group.
-template <int BITS, int NMT, int NNT, bool QS>
-__global__ void __launch_bounds__(256, 2) gemm_tiles_kernel(UniformArgs a, int nmb, int nnb) {
+// KH: K halves per workgroup (1 or 2).  With 2, the workgroup has 8 waves:
+// waves 4 h .. 4 h + 3 take the groups g = 2 s + h of the block (the same
+// tile-rows and activation rows for both halves), each half with its own
+// activation buffers; at the end the second half's partials go through LDS
+// and the first half adds them in a fixed order.  A narrow layer then keeps
+// two waves per SIMD with half the workgroups.
+template <int BITS, int NMT, int NNT, bool QS, int KH>
+__global__ void __launch_bounds__(256 * KH, 2 / KH) gemm_tiles_kernel(UniformArgs a, int nmb, int nnb) {
   using TR = Uni<BITS>;
   constexpr int PPD = TR::CPD / 2;
   constexpr int ZPW = 32 / BITS;
@@ -64,8 +70,9 @@ __global__ void __launch_bounds__(256, 2) gemm_tiles_kernel(UniformArgs a, int n
   // (two separate arrays, selected by a compile-time buffer index: the
   // compiler then knows that reading one never waits for loads into the
   // other)
-  __shared__ __attribute__((aligned(16))) _Float16 xs0[BM * 128];
-  __shared__ __attribute__((aligned(16))) _Float16 xs1[BM * 128];
+  // (KH halves: half h uses rows [h BM, h BM + BM) of each buffer)
+  __shared__ __attribute__((aligned(16))) _Float16 xs0[KH * BM * 128];
+  __shared__ __attribute__((aligned(16))) _Float16 xs1[KH * BM * 128];
   auto xbuf = [&](int b) -> _Float16* { return b ? xs1 : xs0; };
   // staged quant params of an 8-group chunk, two buffers: [row][8] scales and
   // [row][ZW] zero-point words (the words holding the chunk's groups)
@@ -81,7 +88,9 @@ __global__ void __launch_bounds__(256, 2) gemm_tiles_kernel(UniformArgs a, int n
   const int mb = L % nmb, nb = L / nmb;
 
   const int lane = threadIdx.x & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int wid = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int half = KH == 1 ? 0 : wid >> 2;  // this wave's K half
+  const int wave = KH == 1 ? wid : wid & 3;  // its place among the 4 waves of the half
   const int n = lane & 15, kq = lane >> 4;
   const int M = a.M, N = a.N, K = a.K;
   const int G = K / 128;
@@ -110,7 +119,7 @@ __global__ void __launch_bounds__(256, 2) gemm_tiles_kernel(UniformArgs a, int n
   auto x_issue = [&](int g, int b) {
 #pragma unroll
     for (int j = 0; j < NMT; ++j)
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(rx, (__attribute__((address_space(3))) void*)&xbuf(b)[(4 * j + wave) * 512],
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rx, (__attribute__((address_space(3))) void*)&xbuf(b)[(half * 4 * NMT + 4 * j + wave) * 512],
                                                16, xbase, 32u * (uint32_t)K * j + 256u * g, 0, 0);
   };
   // the wave's weights in group g: codes, scale and zero point of lane row n
@@ -135,7 +144,7 @@ __global__ void __launch_bounds__(256, 2) gemm_tiles_kernel(UniformArgs a, int n
   // the staged quant params of chunk c (groups 8c .. 8c + 7): thread t < BN
   // loads block row t's 8 scales and its zero-point words (with NNT = 2 the
   // last two waves stage nothing: a wave-uniform branch)
-  const bool qwave = wave < NNT;
+  const bool qwave = wid < NNT;
   const uint32_t qrow = (uint32_t)nb * BN + threadIdx.x;
   const uint32_t qs_v = qrow * (uint32_t)G * 2u, qz_v = qrow * zrow;
   auto q_issue = [&](int c, u4& sv, uint32_t (&zv)[ZW]) {
@@ -166,7 +175,7 @@ __global__ void __launch_bounds__(256, 2) gemm_tiles_kernel(UniformArgs a, int n
 #pragma unroll
     for (int i = 0; i < NMT; ++i) {
       // block row 16 i + n, k 32 kq + 8 s .. + 7 of the group
-      const u4* xr = reinterpret_cast<const u4*>(&xbuf(b)[(16 * i + n) * 128]);
+      const u4* xr = reinterpret_cast<const u4*>(&xbuf(b)[(half * BM + 16 * i + n) * 128]);
 #pragma unroll
       for (int s = 0; s < 4; ++s) av[i][s] = xr[(4 * kq + s) ^ n];
     }
@@ -224,9 +233,9 @@ __global__ void __launch_bounds__(256, 2) gemm_tiles_kernel(UniformArgs a, int n
     q_issue(0, qsv, qzv);
     q_store(0, qsv, qzv);  // (waits for these loads only)
   }
-  x_issue(0, 0);
+  x_issue(half, 0);
   __builtin_amdgcn_sched_barrier(0);
-  w_load(0, wst[0]);
+  w_load(half, wst[0]);
   __builtin_amdgcn_sched_barrier(0);
   __builtin_amdgcn_s_waitcnt(VMW);
   lds_barrier();
@@ -237,25 +246,53 @@ __global__ void __launch_bounds__(256, 2) gemm_tiles_kernel(UniformArgs a, int n
   auto step = [&](int g, int b, const Wst& cur, Wst& next) {
     // the last step of a chunk also stages the next chunk's quant params
     // (into the other buffer: its previous chunk was last read a whole
-    // chunk ago, before several barriers)
-    const bool qnext = QS && (g & 7) == 7 && g + 1 < G;
+    // chunk ago, before several barriers); with two K halves a step covers
+    // groups g - half and g - half + 1, which share a chunk (8 | K/128)
+    const int gn = g - half + KH;  // the first group of the next step
+    const bool qnext = QS && (gn & 7) == 0 && gn < G;
     if constexpr (QS)
-      if (qnext) q_issue((g + 1) >> 3, qsv, qzv);
+      if (qnext) q_issue(gn >> 3, qsv, qzv);
     __builtin_amdgcn_sched_barrier(0);
-    x_issue(g + 1, b ^ 1);
+    x_issue(g + KH, b ^ 1);
     __builtin_amdgcn_sched_barrier(0);
-    w_load(g + 1, next);
+    w_load(g + KH, next);
     __builtin_amdgcn_sched_barrier(0);
     compute(g, b, cur);
     if constexpr (QS)
-      if (qnext) q_store(((g + 1) >> 3) & 1, qsv, qzv);
+      if (qnext) q_store((gn >> 3) & 1, qsv, qzv);
     __builtin_amdgcn_s_waitcnt(VMW);  // this wave's activation loads of group g + 1
     lds_barrier();
   };
   // two groups per iteration so the register stages are named statically
-  for (int g = 0; g < G; g += 2) {
-    step(g, 0, wst[0], wst[1]);
-    if (g + 1 < G) step(g + 1, 1, wst[1], wst[0]);
+  // (every wave runs the same number of steps; a half's group past the last
+  // reads zeros)
+  const int S = (G + KH - 1) / KH;
+  for (int st = 0; st < S; st += 2) {
+    step(KH * st + half, 0, wst[0], wst[1]);
+    if (st + 1 < S) step(KH * (st + 1) + half, 1, wst[1], wst[0]);
+  }
+  if constexpr (KH == 2) {
+    // the second half's partials into LDS (over the activation buffers:
+    // every load into them has landed and every read is done, the last
+    // step ended with a barrier), then added by the first half
+    float* red = reinterpret_cast<float*>(xs0);
+    constexpr int NV = NMT * NNT * 4;
+    if (half == 1) {
+#pragma unroll
+      for (int i = 0; i < NMT; ++i)
+#pragma unroll
+        for (int t = 0; t < NNT; ++t)
+#pragma unroll
+          for (int r = 0; r < 4; ++r) red[((wave * NV) + (i * NNT + t) * 4 + r) * 64 + lane] = acc[i][t][r];
+    }
+    lds_barrier();
+    if (half == 1) return;
+#pragma unroll
+    for (int i = 0; i < NMT; ++i)
+#pragma unroll
+      for (int t = 0; t < NNT; ++t)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) acc[i][t][r] += red[((wave * NV) + (i * NNT + t) * 4 + r) * 64 + lane];
   }
 
   // lane l holds D[row 4 (l / 16) + r][weight row l % 16] of each 16 x 16 tile
@@ -273,7 +310,7 @@ __global__ void __launch_bounds__(256, 2) gemm_tiles_kernel(UniformArgs a, int n
 
 }  // namespace
 
-template <int BITS, int NMT, int NNT>
+template <int BITS, int NMT, int NNT, int KH = 1>
 hipError_t launch_bm(const UniformArgs& a, hipStream_t s) {
   const int NT = (a.N + 15) / 16;
   const int nmb = (a.M + 16 * NMT - 1) / (16 * NMT);
@@ -283,9 +320,9 @@ hipError_t launch_bm(const UniformArgs& a, hipStream_t s) {
   if (grid > 0x7FFFFFFFL) return hipErrorInvalidValue;
   const bool qs = (a.K / 128) % 8 == 0 && reinterpret_cast<uintptr_t>(a.scales) % 16 == 0;
   if (qs)
-    hipLaunchKernelGGL((gemm_tiles_kernel<BITS, NMT, NNT, true>), dim3((unsigned)grid), dim3(256), 0, s, a, nmb, nnb);
+    hipLaunchKernelGGL((gemm_tiles_kernel<BITS, NMT, NNT, true, KH>), dim3((unsigned)grid), dim3(256 * KH), 0, s, a, nmb, nnb);
   else
-    hipLaunchKernelGGL((gemm_tiles_kernel<BITS, NMT, NNT, false>), dim3((unsigned)grid), dim3(256), 0, s, a, nmb, nnb);
+    hipLaunchKernelGGL((gemm_tiles_kernel<BITS, NMT, NNT, false, KH>), dim3((unsigned)grid), dim3(256 * KH), 0, s, a, nmb, nnb);
   return hipGetLastError();
 }
 
@@ -295,18 +332,24 @@ hipError_t launch_bm(const UniformArgs& a, hipStream_t s) {
 // stages of their codes and the partials of 64 rows do not fit the 256
 // registers of two waves per SIMD.
 template <int BITS>
-hipError_t launch_bits(const UniformArgs& a, int mi, int nt, hipStream_t s) {
+hipError_t launch_bits(const UniformArgs& a, int mi, int nt, int kh, hipStream_t s) {
+  if (kh == 2) {  // (two K halves: the 128-column blocks)
+    if (nt != 2) return hipErrorInvalidValue;
+    if constexpr (BITS != 8)
+      if (mi == 4) return launch_bm<BITS, 4, 2, 2>(a, s);
+    return launch_bm<BITS, 2, 2, 2>(a, s);
+  }
   if constexpr (BITS != 8)
     if (mi == 4) return nt == 4 ? launch_bm<BITS, 4, 4>(a, s) : launch_bm<BITS, 4, 2>(a, s);
   return nt == 4 ? launch_bm<BITS, 2, 4>(a, s) : launch_bm<BITS, 2, 2>(a, s);
 }
 
-hipError_t launch_gemm_tiles(const UniformArgs& a, int mi, int nt, hipStream_t s) {
-  if ((mi != 2 && mi != 4) || (nt != 2 && nt != 4)) return hipErrorInvalidValue;
+hipError_t launch_gemm_tiles(const UniformArgs& a, int mi, int nt, int kh, hipStream_t s) {
+  if ((mi != 2 && mi != 4) || (nt != 2 && nt != 4) || (kh != 1 && kh != 2)) return hipErrorInvalidValue;
   switch (a.bits) {
-    case 2: return launch_bits<2>(a, mi, nt, s);
-    case 4: return launch_bits<4>(a, mi, nt, s);
-    case 8: return launch_bits<8>(a, mi, nt, s);
+    case 2: return launch_bits<2>(a, mi, nt, kh, s);
+    case 4: return launch_bits<4>(a, mi, nt, kh, s);
+    case 8: return launch_bits<8>(a, mi, nt, kh, s);
   }
   return hipErrorInvalidValue;
 }

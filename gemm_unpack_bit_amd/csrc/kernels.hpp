@@ -145,8 +145,9 @@ hipError_t launch_gemv_w4a8(const W4A8Args& a, int wk, hipStream_t s);
 
 // Prefill-size GEMM (gemm_tiles.hip): the uniform format at any M on the
 // matrix cores, blocks of 16 mi activation rows (mi = 2, 4) x 64 nt weight
-// rows (nt = 2, 4)
-hipError_t launch_gemm_tiles(const UniformArgs& a, int mi, int nt, hipStream_t s);
+// rows (nt = 2, 4), K split in kh halves inside the workgroup (kh = 2: nt = 2
+// and K/128 even only)
+hipError_t launch_gemm_tiles(const UniformArgs& a, int mi, int nt, int kh, hipStream_t s);
 
 // Unfused baselines (unfused.hip): eager dequantization to fp16 W [N, K]
 // row-major (uniform b-bit: bits, wq, scales, zeros; LUT4: wq, absmax, lut),

@@ -17,18 +17,22 @@ def _case(seed, M, N, K, bits):
     return c, q.pack(dev(c["codes"]), bits), dev(c["scales"]), q.pack_zeros(dev(c["zeros"]), bits)
 
 
-# block shapes: (activation tiles, tile-rows per wave) = 32 or 64 activation
-# rows x 256 or 128 weight rows
-@pytest.mark.parametrize("mi,nt", [("2", "4"), ("4", "4"), ("2", "2"), ("4", "2")])
+# block shapes: (activation tiles, tile-rows per wave, K halves per
+# workgroup) = 32 or 64 activation rows x 256 or 128 weight rows, all of K or
+# two interleaved halves of it (128-column blocks and K/128 even only: the
+# other shapes run one half)
+@pytest.mark.parametrize("mi,nt,kh", [("2", "4", "1"), ("4", "4", "1"), ("2", "2", "1"), ("4", "2", "1"),
+                                      ("2", "2", "2"), ("4", "2", "2")])
 @pytest.mark.parametrize("force", ["0", "1"])  # "1": the GEMM kernel also for M <= 64
 @pytest.mark.parametrize("bits", [2, 4, 8])
 @pytest.mark.parametrize("M,N,K", [(1, 16, 128), (17, 70, 384), (64, 300, 2048), (100, 1000, 640), (300, 48, 128),
-                                   (130, 257, 1152), (96, 200, 1024)])
-def test_gemm_small_shapes(bits, M, N, K, force, mi, nt, monkeypatch):
-    say("gemm", bits, M, N, K, force, mi, nt)
+                                   (130, 257, 1152), (96, 200, 1024), (40, 130, 256)])
+def test_gemm_small_shapes(bits, M, N, K, force, mi, nt, kh, monkeypatch):
+    say("gemm", bits, M, N, K, force, mi, nt, kh)
     monkeypatch.setenv("QGEMV_GEMM_KERNEL", force)
     monkeypatch.setenv("QGEMV_GEMM_MI", mi)
     monkeypatch.setenv("QGEMV_GEMM_NT", nt)
+    monkeypatch.setenv("QGEMV_GEMM_KH", kh)
     c, wq, s, zq = _case(M * 7 + N + K + bits, M, N, K, bits)
     y = host(q.gemm_uniform(dev(c["x"]), wq, s, zq, bits))
     y_ref, A = ref.gemv_uniform(c["x"], c["codes"], c["scales"], c["zeros"])
@@ -49,9 +53,11 @@ def test_gemm_agrees_with_gemv_and_is_deterministic():
     assert_within(yv, y_ref, A, "gemv")
 
 
+@pytest.mark.parametrize("kh", ["1", "2"])
 @pytest.mark.parametrize("M,N,K", [(512, 4096, 4096), (200, 4096, 14336), (512, 4096, 14336)])
-def test_gemm_full_size_sampled(M, N, K):
-    say("gemm full", M, N, K)
+def test_gemm_full_size_sampled(M, N, K, kh, monkeypatch):
+    say("gemm full", M, N, K, kh)
+    monkeypatch.setenv("QGEMV_GEMM_KH", kh)
     c, wq, s, zq = _case(6 + M, M, N, K, 4)
     y = host(q.gemm_uniform(dev(c["x"]), wq, s, zq, 4))
     rows = sample_rows(N)
