@@ -15,7 +15,8 @@
 // registers on the way.
 //
 // Block: 16 NMT activation rows x 64 NNT weight rows (4 NNT tile-rows), 4
-// waves.  Wave w owns tile-rows NNT w .. NNT w + NNT - 1 and every
+// waves per K half (one or two halves, KH).  Wave w of a half owns
+// tile-rows NNT w .. NNT w + NNT - 1 and every
 // activation row of the block: each weight fragment is dequantized once per
 // workgroup, and each activation fragment read from LDS feeds NNT MFMAs (one
 // per tile-row).  NNT = 4 (256 weight rows) quarters the LDS reads per MFMA
@@ -24,7 +25,8 @@
 // the workgroups of a narrow layer, where 256-row blocks leave one wave per
 // SIMD with nothing to overlap its loads, dequantization and MFMAs.  Per
 // group a wave runs 4 NMT NNT MFMAs into group partials and adds each times
-// its row's scale (one rounding per group, as the decode kernels).
+// its row's scale (one rounding per group, as the decode kernels).  With
+// two K halves the halves' partials are added in a fixed order at the end.
 // Deterministic.
 //
 // Block order: workgroups go to the eight XCDs round robin, so consecutive
