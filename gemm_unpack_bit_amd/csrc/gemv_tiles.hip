@@ -38,6 +38,7 @@
 //    gfx950 permlane swaps, the waves through LDS in a fixed order, so the
 //    result is bitwise deterministic.
 #include <cstdlib>
+#include <type_traits>
 
 #include "common.hpp"
 #include "dequant.hpp"
@@ -556,14 +557,51 @@ gemv_tiles_kernel(UniformArgs a) {
     }
     wave_fence();  // (the slot is rewritten by the next batch)
   };
+  // A wave's first batch runs early in the dense loop, right after the
+  // first chunk's next stage loads are issued: the batches (in LDS) were the
+  // last loads before those, so an exact vmcnt waits for them and no more,
+  // and the batch is worked through while the weight stages are in flight
+  // (run after the loop, its latency adds to every workgroup's).  Its other
+  // batches, and a wave's with no chunk, still run after the loop: more
+  // sparse work inside the loop would hold back the weight stream.  Only the
+  // VALU engine at one batch row with at most three stages in flight does
+  // so: with the matrix core's 16 row sums per lane, or a fourth stage's
+  // registers, the sums held across the loop no longer fit the register
+  // budget and spill.
+  constexpr bool SP_EARLY = SP && !MFMA && MT == 1 && D <= 3;
+  int sp_i = 0;  // the wave's next batch (wave-uniform)
+  auto sparse_zero = [&]() {
+#pragma unroll
+    for (int t = 0; t < TPW; ++t)
+#pragma unroll
+      for (int i = 0; i < SR; ++i) sacc[t][i] = 0.f;
+  };
+  // in a loop's first chunk, after N vector memory instructions issued
+  // behind the batch loads
+  auto sparse_early = [&](auto n) {
+    if constexpr (SP_EARLY) {
+      constexpr int N = decltype(n)::value;
+      static_assert(N < 64, "vmcnt range");
+      if (sp_i == 0) {
+        __builtin_amdgcn_sched_barrier(0);
+        __builtin_amdgcn_s_waitcnt((N & 15) | (0x7 << 4) | (0xF << 8) | ((N >> 4) << 14));  // vmcnt(N)
+        sparse_zero();
+        const uint32_t b0 = vbeg + 64u * wave;
+        if (b0 < vend) sparse_batch(vrec[lane], b0 + lane);
+        sp_i = 1;
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    }
+  };
   auto sparse_compute = [&]() {
     if constexpr (SP) {
-      __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): the batches are in LDS (issued long before)
-#pragma unroll
-      for (int t = 0; t < TPW; ++t)
-#pragma unroll
-        for (int i = 0; i < SR; ++i) sacc[t][i] = 0.f;
-      for (int i = 0;; ++i) {  // wave-uniform
+      if (sp_i == 0) {
+        __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): the batches are in LDS (issued long before)
+        sparse_zero();
+      }
+      // (after an early batch the others are in LDS too: their loads came
+      // before the ones the early wait covered)
+      for (int i = sp_i;; ++i) {  // wave-uniform
         const uint32_t b0 = vbeg + 64u * (wave + WK * i);
         if (b0 >= vend) break;
         const uint32_t idx = b0 + lane;
@@ -587,6 +625,9 @@ gemv_tiles_kernel(UniformArgs a) {
     }
   };
 
+  // vector memory instructions of one load_stage, and of one load_x
+  constexpr int SLD = NG * (BITS == 8 ? 2 : 1) + (PLDS ? 0 : (SAL ? 1 : NG) + 1);
+  constexpr int XLD = XLDS || XD ? 0 : NG * XR * 4;
   stage_x_issue();
   // (a wave with no chunk at all, c >= NC, reads zeros: no branch here)
   if constexpr (XB == 1) {
@@ -626,6 +667,7 @@ gemv_tiles_kernel(UniformArgs a) {
         } else {
           load_stage(ta - TPW, c + WK, ring[ta % D]);  // next chunk (zeros past the last); same slot
         }
+        if (t == 0) sparse_early(std::integral_constant<int, SLD>{});
         __builtin_amdgcn_sched_barrier(0);
         compute(t, c, ring[t % D], 0);
         __builtin_amdgcn_sched_barrier(0);
@@ -644,6 +686,7 @@ gemv_tiles_kernel(UniformArgs a) {
 #pragma unroll
       for (int i = 0; i < D; ++i) {
         load_stage(0, c + (i + D - 1) * WK, ring[(i + D - 1) % D]);
+        if (i == 0) sparse_early(std::integral_constant<int, SLD>{});
         __builtin_amdgcn_sched_barrier(0);
         compute(0, c + i * WK, ring[i], 0);
         __builtin_amdgcn_sched_barrier(0);
@@ -659,6 +702,7 @@ gemv_tiles_kernel(UniformArgs a) {
     for (; c < NC; c += 2 * WK) {
       load_stage(0, c + WK, ring[1]);
       load_x(c + WK, 1);
+      sparse_early(std::integral_constant<int, SLD + XLD>{});
       __builtin_amdgcn_sched_barrier(0);
       compute(0, c, ring[0], 0);
       __builtin_amdgcn_sched_barrier(0);
