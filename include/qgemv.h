@@ -78,6 +78,11 @@
  *                                       16-row MFMA tiles of x by 2 or 4 16-row
  *                                       tile-rows of W per wave (32 or 64 x 128
  *                                       or 256)
+ *   QGEMV_GEMM_KH=1|2                   qgemv_gemm_uniform's GEMM: K in one pass (1)
+ *                                       or in two halves taken by the two halves
+ *                                       of a 512-thread workgroup (2; only with
+ *                                       2 tile-rows per wave and K/128 even,
+ *                                       else 1)
  *   QGEMV_W4A8_WK, QGEMV_W4A8_TR        qgemv_w4a8: waves and tile-rows (1, 2) per
  *                                       workgroup
  */
