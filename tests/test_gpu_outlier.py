@@ -172,6 +172,37 @@ def test_outlier_every_launch_shape(monkeypatch, path, M, N, K):
     assert len(ran) >= 8, ran
 
 
+@pytest.mark.parametrize("xlds,plds", [("", "1"), ("0", "1"), ("", "0"), ("0", "0")])
+@pytest.mark.parametrize("N,K", [(300, 2176), (64, 4096), (272, 33024)])
+def test_outlier_early_batch_every_staging(monkeypatch, xlds, plds, N, K):
+    """The VALU engine at one batch row runs a wave's first record batch
+    inside the dense loop, behind a wait whose count depends on the loads a
+    stage issues: activations staged in LDS or loaded per chunk, quant params
+    staged or loaded per lane.  Every combination, every launch shape, with
+    enough records per tile-row that waves hold several batches (K = 33024:
+    activations too long to stage)."""
+    say("outlier early batch", xlds, plds, N, K)
+    c = synth.outlier_case(N + K + 7, 1, N, K, frac=0.02)
+    wq, s, zq, tp, tr = _upload(c, N, K)
+    x = dev(c["x"])
+    y_ref, A = ref.gemv_outlier(c["x"], c["codes"], c["scales"], c["zeros"], c["o_rows"], c["o_cols"], c["o_vals"])
+    if xlds:
+        monkeypatch.setenv("QGEMV_XLDS_MAX", xlds)
+    monkeypatch.setenv("QGEMV_PLDS", plds)
+    ran = []
+    for tpw, v in ((1, 3), (2, 0)):
+        for wk in (1, 4, 16):
+            cfg = f"{tpw},{wk},1,{v}"
+            monkeypatch.setenv("QGEMV_OUTLIER_CFG", cfg)
+            try:
+                y = host(q.outlier(x, wq, s, zq, tp, tr, q.PATH_VALU))
+            except q.QgemvError:
+                continue
+            assert_within(y, y_ref, A, f"outlier early batch N={N} K={K} cfg={cfg} xlds={xlds} plds={plds}")
+            ran.append(cfg)
+    assert len(ran) >= 4, ran
+
+
 @pytest.mark.parametrize("form", ["fused", "split"])
 @pytest.mark.parametrize("path", [q.PATH_VALU, q.PATH_MFMA])
 @pytest.mark.parametrize("M", [1, 5, 16])
