@@ -22,6 +22,15 @@ __device__ __forceinline__ float dot2(h2 a, h2 b, float c) {
   return __builtin_amdgcn_fdot2(a, b, c, false);
 }
 
+// a.lo*b.lo + a.hi*b.hi into a fresh fp32: the VOP3 form with an
+// inline-constant 0 accumulator (the builtin with a 0 accumulator becomes
+// the tied-accumulator form and a v_mov of 0 before it)
+__device__ __forceinline__ float dot2_first(h2 a, h2 b) {
+  float d;
+  asm("v_dot2_f32_f16 %0, %1, %2, 0" : "=v"(d) : "v"(a), "v"(b));
+  return d;
+}
+
 __device__ __forceinline__ h2 fma2(h2 a, h2 b, h2 c) { return __builtin_elementwise_fma(a, b, c); }
 
 __device__ __forceinline__ float h2f(uint16_t bits) {

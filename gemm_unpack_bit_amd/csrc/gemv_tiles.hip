@@ -367,9 +367,12 @@ gemv_tiles_kernel(UniformArgs a) {
           for (int v = 0; v < 4; ++v) {
             // x[m0 + m][128 (gc0 + j) + 32 kq + 8 v .. + 8], or the zero pad
             const bool xin = (SAL && XB == 1) || gc0 + j < G;
-            const u4 xv = XLDS ? xs[(m * XK + (xin ? 128 * (gc0 + j) + 32 * kq : K)) / 8 + v] : xr[b][j][m][v];
+            // (unsigned: every term is non-negative, so the division is a shift)
+            const u4 xv = XLDS ? xs[((uint32_t)(m * XK) + (xin ? 128u * (uint32_t)(gc0 + j) + 32u * kq : (uint32_t)K)) / 8u + v]
+                               : xr[b][j][m][v];
 #pragma unroll
-            for (int e = 0; e < 4; ++e) part = dot2(p[4 * v + e], as_h2(xv[e]), part);
+            for (int e = 0; e < 4; ++e)
+              part = v == 0 && e == 0 ? dot2_first(p[0], as_h2(xv[0])) : dot2(p[4 * v + e], as_h2(xv[e]), part);
           }
           accv[t][m] = fmaf(sc, part, accv[t][m]);
         }
