@@ -118,8 +118,13 @@ constexpr int max_threads(int ng) { return ng == 1 ? 1024 : 512; }
 // each.  A chunk's A fragments and quant params are read from LDS before the
 // next chunk's load is issued, so the wait for a slot's load is never a
 // wait for the one behind it.
+// FULL (the deep chunk ring of the VALU engine, no outliers): K/128 is a
+// multiple of the ring depth times the waves, so every chunk a wave unpacks
+// inside its loop lies inside K and the selects for chunks past the last
+// (activation pad, zero point, scale) drop out; the loads issued ahead past
+// the last chunk still read zeros.
 template <int BITS, bool MFMA, int MT, int NG, int D, int TPW, bool SAL, bool XLDS, bool SP, bool PLDS,
-          bool XD = false>
+          bool XD = false, bool FULL = false>
 __global__ void __launch_bounds__(max_threads(NG)) __attribute__((amdgpu_waves_per_eu(waves_per_simd(NG))))
 gemv_tiles_kernel(UniformArgs a) {
   using TR = Uni<BITS>;
@@ -134,6 +139,7 @@ gemv_tiles_kernel(UniformArgs a) {
   static_assert(!DEEP || (XLDS && NG == 1), "the deep chunk ring keeps no activations in registers");
   static_assert(ZPW % NG == 0, "a chunk's zero points share one word");
   static_assert(!XD || (MFMA && !XLDS && !SP && NG == 1 && TPW >= D), "the activation ring: MFMA, one-group chunks");
+  static_assert(!FULL || (DEEP && !MFMA && !SP), "whole chunk rounds: the deep ring of the VALU engine");
 
   // LDS: [staged activations: XM x K halves, XLDS only] [staged scales and
   // zero points of the TPW tile-rows, PLDS only] then the per-wave partials: VALU
@@ -334,7 +340,7 @@ gemv_tiles_kernel(UniformArgs a) {
         } else {
           // unconditional reads at a clamped group, then a select: a read
           // under a condition would become a branch inside the pipelined loop
-          const bool gin = gc0 + j < G;
+          const bool gin = FULL || gc0 + j < G;
           const int g = min(gc0 + j, G - 1);
           const uint16_t sv = ps[(16 * t + n) * G + g];
           const uint32_t zv = pz[(16 * t + n) * (int)(zrow / 4) + g / ZPW];
@@ -366,7 +372,7 @@ gemv_tiles_kernel(UniformArgs a) {
 #pragma unroll
           for (int v = 0; v < 4; ++v) {
             // x[m0 + m][128 (gc0 + j) + 32 kq + 8 v .. + 8], or the zero pad
-            const bool xin = (SAL && XB == 1) || gc0 + j < G;
+            const bool xin = FULL || (SAL && XB == 1) || gc0 + j < G;
             // (unsigned: every term is non-negative, so the division is a shift)
             const u4 xv = XLDS ? xs[((uint32_t)(m * XK) + (xin ? 128u * (uint32_t)(gc0 + j) + 32u * kq : (uint32_t)K)) / 8u + v]
                                : xr[b][j][m][v];
@@ -777,9 +783,9 @@ size_t sparse_lds_bytes(bool mfma, int mt, int wk, int tpw, int K, int M) {
 constexpr size_t LDS_ALL = 160 * 1024;  // gfx950 LDS per workgroup
 
 template <int BITS, bool MFMA, int MT, int NG, int D, int TPW, bool SAL, bool XLDS, bool SP, bool PLDS,
-          bool XD = false>
+          bool XD = false, bool FULL = false>
 hipError_t launch_k(const UniformArgs& a, dim3 grid, dim3 block, size_t lds, hipStream_t s) {
-  auto kern = &gemv_tiles_kernel<BITS, MFMA, MT, NG, D, TPW, SAL, XLDS, SP, PLDS, XD>;
+  auto kern = &gemv_tiles_kernel<BITS, MFMA, MT, NG, D, TPW, SAL, XLDS, SP, PLDS, XD, FULL>;
   if (lds > 64 * 1024) {
     static bool raised = false;  // one-time opt-in above the default dynamic LDS limit
     if (!raised) {
@@ -802,7 +808,7 @@ size_t params_lds_bytes(int bits, int K, int tpw) {
 
 template <int BITS, bool MFMA, int MT, int NG, int D, int TPW, bool XL, bool SP>
 hipError_t launch_p(const UniformArgs& a, bool sal, bool plds, bool xd, dim3 grid, dim3 block, size_t lds,
-                    hipStream_t s) {
+                    hipStream_t s, bool full = false) {
   // the activation ring (XD): the matrix-core engine with activations not
   // staged whole, one-group chunks of several tile-rows, no outliers
   constexpr bool XD_OK = MFMA && !XL && !SP && NG == 1 && TPW >= D && TPW >= 2 && TPW <= 4 && !(BITS == 8 && TPW == 4);
@@ -817,6 +823,11 @@ hipError_t launch_p(const UniformArgs& a, bool sal, bool plds, bool xd, dim3 gri
   if constexpr (TPW == 1 && NG == 1) {
     // one-group chunks: a group's scale is always one whole, aligned load
     if (!sal) return hipErrorInvalidValue;
+    if constexpr (D > 2 && !MFMA && !SP) {
+      if (full)
+        return plds ? launch_k<BITS, MFMA, MT, NG, D, TPW, true, XL, SP, true, false, true>(a, grid, block, lds, s)
+                    : launch_k<BITS, MFMA, MT, NG, D, TPW, true, XL, SP, false, false, true>(a, grid, block, lds, s);
+    }
     return plds ? launch_k<BITS, MFMA, MT, NG, D, TPW, true, XL, SP, true>(a, grid, block, lds, s)
                 : launch_k<BITS, MFMA, MT, NG, D, TPW, true, XL, SP, false>(a, grid, block, lds, s);
   } else {
@@ -876,7 +887,11 @@ hipError_t launch_t(const UniformArgs& a, const TileCfg& c, hipStream_t s) {
     if (lds > LDS_ALL) return hipErrorInvalidValue;
     if constexpr (DEEP) {
       if (!xlds) return hipErrorInvalidValue;  // the deep ring reads activations from LDS only
-      return launch_p<BITS, MFMA, MT, NG, D, TPW, true, SP>(a, sal, plds, false, grid, block, lds, s);
+      // every wave's chunks fill whole rounds of the ring
+      const int nc = (int)(a.K / 128 + NG - 1) / NG;
+      bool full = nc % (D * c.wk) == 0;
+      if (const char* e = tune_env("QGEMV_FULL_ROUNDS")) full = full && e[0] == '1';  // tuning override
+      return launch_p<BITS, MFMA, MT, NG, D, TPW, true, SP>(a, sal, plds, false, grid, block, lds, s, full);
     } else {
       if (xlds) return launch_p<BITS, MFMA, MT, NG, D, TPW, true, SP>(a, sal, plds, false, grid, block, lds, s);
       return launch_p<BITS, MFMA, MT, NG, D, TPW, false, SP>(a, sal, plds, xd, grid, block, lds, s);

@@ -57,6 +57,10 @@
  *   QGEMV_PLDS=0|1                      uniform kernels: stage the workgroup's scales
  *                                       and zero points in LDS (1, the default where
  *                                       aligned and they fit) or load them per lane
+ *   QGEMV_FULL_ROUNDS=0|1               uniform VALU kernels with the deep chunk ring:
+ *                                       when K/128 fills whole rounds of the ring, a
+ *                                       kernel without the past-the-last-chunk selects
+ *                                       (1, the default) or the general one (0)
  *   QGEMV_XDMA=0|1|2                    matrix-core uniform kernel with activations not
  *                                       staged whole: per-wave LDS ring of activation
  *                                       blocks off (0), where it measured faster (1,
