@@ -162,6 +162,10 @@ gemv_tiles_kernel(UniformArgs a) {
   const uint32_t lw = lane_off<BITS>(lane);
 
   const rsrc_t rw = make_rsrc(a.wq, (uint32_t)NT * G * TB);
+  // the deep rings select a chunk past the last by its descriptor (an empty
+  // one: every load reads zeros), a scalar select, instead of by a vector
+  // select of the lane offset per chunk
+  const rsrc_t rw0 = make_rsrc(a.wq, 0u);
   const rsrc_t rz = make_rsrc(a.zeros, (uint32_t)N * zrow);
   const rsrc_t rs = make_rsrc(a.scales, (uint32_t)N * G * 2u);
   const rsrc_t rx = make_rsrc(a.x, (uint32_t)M * K * 2u);
@@ -237,7 +241,10 @@ gemv_tiles_kernel(UniformArgs a) {
     for (int j = 0; j < NG; ++j) {
       const bool ok = tv && (SAL ? cv : gc0 + j < G);
       const uint32_t sw = __builtin_amdgcn_readfirstlane(ok ? ((uint32_t)rt * G + gc0 + j) * TB : 0u);
-      st.c[j].load(rw, ok ? lw : OOB, sw);
+      if constexpr (DEEP)
+        st.c[j].load(ok ? rw : rw0, lw, sw);
+      else
+        st.c[j].load(rw, ok ? lw : OOB, sw);
     }
     if constexpr (PLDS) return;  // quant params come from LDS
     const uint32_t ss = __builtin_amdgcn_readfirstlane(cv ? 2u * gc0 : 0u);
