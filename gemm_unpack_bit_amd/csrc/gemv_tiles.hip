@@ -118,8 +118,9 @@ constexpr int max_threads(int ng) { return ng == 1 ? 1024 : 512; }
 // each.  A chunk's A fragments and quant params are read from LDS before the
 // next chunk's load is issued, so the wait for a slot's load is never a
 // wait for the one behind it.
-// FULL (the deep chunk ring of the VALU engine, no outliers): K/128 is a
-// multiple of the ring depth times the waves, so every chunk a wave unpacks
+// FULL (one tile-row of one-group chunks on the VALU engine, no outliers):
+// K/128 is a multiple of the ring depth times the waves (a round of the
+// two-stage loop is two chunks per wave), so every chunk a wave unpacks
 // inside its loop lies inside K and the selects for chunks past the last
 // (activation pad, zero point, scale) drop out; the loads issued ahead past
 // the last chunk still read zeros.
@@ -139,7 +140,7 @@ gemv_tiles_kernel(UniformArgs a) {
   static_assert(!DEEP || (XLDS && NG == 1), "the deep chunk ring keeps no activations in registers");
   static_assert(ZPW % NG == 0, "a chunk's zero points share one word");
   static_assert(!XD || (MFMA && !XLDS && !SP && NG == 1 && TPW >= D), "the activation ring: MFMA, one-group chunks");
-  static_assert(!FULL || (DEEP && !MFMA && !SP), "whole chunk rounds: the deep ring of the VALU engine");
+  static_assert(!FULL || (TPW == 1 && NG == 1 && !MFMA && !SP), "whole chunk rounds: one tile-row, VALU");
 
   // LDS: [staged activations: XM x K halves, XLDS only] [staged scales and
   // zero points of the TPW tile-rows, PLDS only] then the per-wave partials: VALU
@@ -830,7 +831,7 @@ hipError_t launch_p(const UniformArgs& a, bool sal, bool plds, bool xd, dim3 gri
   if constexpr (TPW == 1 && NG == 1) {
     // one-group chunks: a group's scale is always one whole, aligned load
     if (!sal) return hipErrorInvalidValue;
-    if constexpr (D > 2 && !MFMA && !SP) {
+    if constexpr (!MFMA && !SP) {
       if (full)
         return plds ? launch_k<BITS, MFMA, MT, NG, D, TPW, true, XL, SP, true, false, true>(a, grid, block, lds, s)
                     : launch_k<BITS, MFMA, MT, NG, D, TPW, true, XL, SP, false, false, true>(a, grid, block, lds, s);
@@ -900,7 +901,13 @@ hipError_t launch_t(const UniformArgs& a, const TileCfg& c, hipStream_t s) {
       if (const char* e = tune_env("QGEMV_FULL_ROUNDS")) full = full && e[0] == '1';  // tuning override
       return launch_p<BITS, MFMA, MT, NG, D, TPW, true, SP>(a, sal, plds, false, grid, block, lds, s, full);
     } else {
-      if (xlds) return launch_p<BITS, MFMA, MT, NG, D, TPW, true, SP>(a, sal, plds, false, grid, block, lds, s);
+      if (xlds) {
+        // one tile-row, two stages: whole rounds as for the deep rings
+        const int nc = (int)(a.K / 128 + NG - 1) / NG;
+        bool full = TPW == 1 && nc % (D * c.wk) == 0;
+        if (const char* e = tune_env("QGEMV_FULL_ROUNDS")) full = full && e[0] == '1';  // tuning override
+        return launch_p<BITS, MFMA, MT, NG, D, TPW, true, SP>(a, sal, plds, false, grid, block, lds, s, full);
+      }
       return launch_p<BITS, MFMA, MT, NG, D, TPW, false, SP>(a, sal, plds, xd, grid, block, lds, s);
     }
   }

@@ -114,13 +114,15 @@ def test_every_launch_shape(monkeypatch, bits, N, K, path, M):
 
 @pytest.mark.parametrize("bits", [2, 4, 8])
 @pytest.mark.parametrize("N,K,cfg", [(28672, 4096, None), (4096, 4096, None), (300, 2048, "1,4,1,4"),
-                                     (1000, 4096, "1,8,2,4"), (260, 2048, "1,2,1,5")])
+                                     (1000, 4096, "1,8,2,4"), (260, 2048, "1,2,1,5"), (10240, 8192, None),
+                                     (1000, 4096, "1,8,1,3"), (300, 2048, "1,4,2,3")])
 def test_whole_ring_rounds_kernel_equals_general(monkeypatch, bits, N, K, cfg):
-    """Where K/128 fills whole rounds of the deep chunk ring, the kernel
-    without the past-the-last-chunk selects runs (QGEMV_FULL_ROUNDS=1, the
-    default); it must give the general kernel's y bit for bit (8B gate+up
-    and o as picked, and forced shapes with one and two batch rows and the
-    8-deep ring), inside the oracle's bound on sampled rows."""
+    """Where K/128 fills whole rounds of a one-tile-row chunk ring, the
+    kernel without the past-the-last-chunk selects runs
+    (QGEMV_FULL_ROUNDS=1, the default); it must give the general kernel's y
+    bit for bit (8B gate+up and o and 70B q as picked, and forced shapes:
+    the 4- and 8-deep rings and the two-stage loop, one and two batch
+    rows), inside the oracle's bound on sampled rows."""
     if bits == 8 and cfg and cfg.endswith(",5"):
         pytest.skip("the 8-deep ring holds 8-bit stages only by spilling: no such kernel")
     M = 2 if cfg and cfg.split(",")[2] == "2" else 1
