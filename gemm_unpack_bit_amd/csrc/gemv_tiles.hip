@@ -348,7 +348,9 @@ gemv_tiles_kernel(UniformArgs a) {
         } else {
           // unconditional reads at a clamped group, then a select: a read
           // under a condition would become a branch inside the pipelined loop
-          const bool gin = FULL || gc0 + j < G;
+          // (the several-tile-row loop, XB = 1, computes only chunks below
+          // NC, and whole ones when SAL: no select there, as for xin)
+          const bool gin = FULL || (SAL && XB == 1) || gc0 + j < G;
           const int g = min(gc0 + j, G - 1);
           const uint16_t sv = ps[(16 * t + n) * G + g];
           const uint32_t zv = pz[(16 * t + n) * (int)(zrow / 4) + g / ZPW];
