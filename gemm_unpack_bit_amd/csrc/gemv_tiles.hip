@@ -118,7 +118,7 @@ constexpr int max_threads(int ng) { return ng == 1 ? 1024 : 512; }
 // each.  A chunk's A fragments and quant params are read from LDS before the
 // next chunk's load is issued, so the wait for a slot's load is never a
 // wait for the one behind it.
-// FULL (one tile-row of one-group chunks, either engine, no outliers):
+// FULL (one tile-row of one-group chunks, either engine):
 // K/128 is a multiple of the ring depth times the waves (a round of the
 // two-stage loop is two chunks per wave), so every chunk a wave unpacks
 // inside its loop lies inside K and the selects for chunks past the last
@@ -140,7 +140,7 @@ gemv_tiles_kernel(UniformArgs a) {
   static_assert(!DEEP || (XLDS && NG == 1), "the deep chunk ring keeps no activations in registers");
   static_assert(ZPW % NG == 0, "a chunk's zero points share one word");
   static_assert(!XD || (MFMA && !XLDS && !SP && NG == 1 && TPW >= D), "the activation ring: MFMA, one-group chunks");
-  static_assert(!FULL || (TPW == 1 && NG == 1 && !SP), "whole chunk rounds: one tile-row of one-group chunks");
+  static_assert(!FULL || (TPW == 1 && NG == 1), "whole chunk rounds: one tile-row of one-group chunks");
 
   // LDS: [staged activations: XM x K halves, XLDS only] [staged scales and
   // zero points of the TPW tile-rows, PLDS only] then the per-wave partials: VALU
@@ -833,7 +833,7 @@ hipError_t launch_p(const UniformArgs& a, bool sal, bool plds, bool xd, dim3 gri
   if constexpr (TPW == 1 && NG == 1) {
     // one-group chunks: a group's scale is always one whole, aligned load
     if (!sal) return hipErrorInvalidValue;
-    if constexpr (!SP) {
+    {
       if (full)
         return plds ? launch_k<BITS, MFMA, MT, NG, D, TPW, true, XL, SP, true, false, true>(a, grid, block, lds, s)
                     : launch_k<BITS, MFMA, MT, NG, D, TPW, true, XL, SP, false, false, true>(a, grid, block, lds, s);

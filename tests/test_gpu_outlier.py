@@ -232,3 +232,20 @@ def test_outlier_layer_shapes_batched(N, K, M):
     y_ref, A = ref.gemv_outlier(c["x"], c["codes"], c["scales"], c["zeros"], c["o_rows"], c["o_cols"], c["o_vals"],
                                 rows=rows)
     assert_within(y[:, rows], y_ref, A, f"outlier M={M} N={N} K={K}")
+
+
+@pytest.mark.parametrize("path", [q.PATH_VALU, q.PATH_MFMA])
+@pytest.mark.parametrize("N,K,M", [(4096, 4096, 1), (28672, 4096, 1), (10240, 8192, 1), (4096, 4096, 2)])
+def test_whole_ring_rounds_kernel_equals_general(monkeypatch, path, N, K, M):
+    """The fused outlier kernel where K/128 fills whole rounds of its chunk
+    ring (QGEMV_FULL_ROUNDS=1, the default) against the general kernel:
+    the same y bit for bit."""
+    c = synth.outlier_case(800 + N + M, M, N, K)
+    wq, s, zq, tp, tr = _upload(c, N, K)
+    x = dev(c["x"])
+    ys = {}
+    for full in ("0", "1"):
+        say("outlier full rounds", full, path, N, K, M)
+        monkeypatch.setenv("QGEMV_FULL_ROUNDS", full)
+        ys[full] = host(q.outlier(x, wq, s, zq, tp, tr, path))
+    assert np.array_equal(ys["0"].view(np.uint16), ys["1"].view(np.uint16))
