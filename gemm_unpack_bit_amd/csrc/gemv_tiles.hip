@@ -146,6 +146,19 @@ gemv_tiles_kernel(UniformArgs a) {
   // zero points of the TPW tile-rows, PLDS only] then the per-wave partials: VALU
   // [WK][TPW][MT][16] floats, MFMA [WK][TPW][64] float4
   extern __shared__ __attribute__((aligned(16))) float smem[];
+  // Z2T (2-bit codes, kernels that pass the staging barrier before their
+  // loop): the five zero-point constants of each z in 0..3, built once per
+  // workgroup (32 bytes per z), so a group reads them instead of building
+  // them from its zero point (a multiply-add and five shift-ors per group)
+  constexpr bool Z2T = BITS == 2 && (XLDS || PLDS || SP);
+  __shared__ __attribute__((aligned(16))) uint32_t z2tab[Z2T ? 32 : 4];
+  if constexpr (Z2T) {
+    if (threadIdx.x < 4) {
+      const typename TR::Z zt = TR::zc(threadIdx.x);
+#pragma unroll
+      for (int k = 0; k < 5; ++k) z2tab[8 * threadIdx.x + k] = as_u32(zt.c[k]);
+    }
+  }
 
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -359,7 +372,19 @@ gemv_tiles_kernel(UniformArgs a) {
         }
       }
       const float sc = h2f(sj);
-      const typename TR::Z zz = TR::zc((zw >> (BITS * ((gc0 + j) % ZPW))) & ZMASK);
+      const uint32_t zq = (zw >> (BITS * ((gc0 + j) % ZPW))) & ZMASK;
+      const typename TR::Z zz = [&] {
+        if constexpr (Z2T) {
+          typename TR::Z r;
+          const u4 e = *reinterpret_cast<const u4*>(&z2tab[8 * zq]);
+#pragma unroll
+          for (int k = 0; k < 4; ++k) r.c[k] = as_h2(e[k]);
+          r.c[4] = as_h2(z2tab[8 * zq + 4]);
+          return r;
+        } else {
+          return TR::zc(zq);
+        }
+      }();
       h2 p[16];  // (q - z) pairs of the lane's 32 consecutive k
 #pragma unroll
       for (int d = 0; d < BITS; ++d) TR::deq(st.c[j].w[d], mg, zz, p + d * PPD);
@@ -791,16 +816,20 @@ size_t sparse_lds_bytes(bool mfma, int mt, int wk, int tpw, int K, int M) {
 }
 
 constexpr size_t LDS_ALL = 160 * 1024;  // gfx950 LDS per workgroup
+// static LDS of the kernel beside its dynamic share (the 2-bit zero-point
+// constant table, Z2T): counted in both limits below
+constexpr size_t z2t_lds(int bits) { return bits == 2 ? 128 : 0; }
 
 template <int BITS, bool MFMA, int MT, int NG, int D, int TPW, bool SAL, bool XLDS, bool SP, bool PLDS,
           bool XD = false, bool FULL = false>
 hipError_t launch_k(const UniformArgs& a, dim3 grid, dim3 block, size_t lds, hipStream_t s) {
   auto kern = &gemv_tiles_kernel<BITS, MFMA, MT, NG, D, TPW, SAL, XLDS, SP, PLDS, XD, FULL>;
-  if (lds > 64 * 1024) {
+  if (lds + z2t_lds(BITS) > 64 * 1024) {
     static bool raised = false;  // one-time opt-in above the default dynamic LDS limit
     if (!raised) {
       hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
-                                         hipFuncAttributeMaxDynamicSharedMemorySize, (int)LDS_ALL);
+                                         hipFuncAttributeMaxDynamicSharedMemorySize,
+                                         (int)(LDS_ALL - z2t_lds(BITS)));
       if (e != hipSuccess) return e;
       raised = true;
     }
@@ -892,9 +921,10 @@ hipError_t launch_t(const UniformArgs& a, const TileCfg& c, hipStream_t s) {
     const size_t ring = (size_t)c.wk * 2 * 256 * ((std::min(a.M, 16) + 3) & ~3);
     const size_t rest = xd ? std::max(ring, red)
                            : (xlds ? xl : 0) + red + (SP ? sparse_lds_bytes(MFMA, MT, c.wk, TPW, a.K, a.M) : 0);
-    if (rest + params_lds_bytes(BITS, a.K, TPW) > LDS_ALL) plds = false;  // (long K: stage nothing)
+    const size_t lds_all = LDS_ALL - z2t_lds(BITS);
+    if (rest + params_lds_bytes(BITS, a.K, TPW) > lds_all) plds = false;  // (long K: stage nothing)
     const size_t lds = rest + (plds ? params_lds_bytes(BITS, a.K, TPW) : 0);
-    if (lds > LDS_ALL) return hipErrorInvalidValue;
+    if (lds > lds_all) return hipErrorInvalidValue;
     if constexpr (DEEP) {
       if (!xlds) return hipErrorInvalidValue;  // the deep ring reads activations from LDS only
       // every wave's chunks fill whole rounds of the ring
